@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the ray-driven projector pair on one MI355X.
+
+A step is one SIRT iteration on the 512^3 parallel3d dual-axis workload (C4:
+280 views, 512 x 512 detector): the forward projection with the residual
+epilogue (ct_sirt_residual) and the brick-binned adjoint with the update
+epilogue (ct_sirt_update), i.e. every hot-path kernel of the iteration.  The
+SIRT weights are computed once before timing.  Inputs live in HBM before the
+timed region starts.
+
+Printed value: ray-voxel intersections per second over the step (each
+intersection is visited once by A and once by A^T, so 2 * nnz per step),
+in G/s; ms_per_step is the time of one SIRT iteration.  --workload c5 instead
+times A + A^T (ct_project + ct_backproject) on the 512^3 jittered circular
+cone (720 views, 1024 x 768).
+
+Roofline: algorithmic HBM bytes of the dominant kernel per launch divided by
+its average duration (HIP events on the launch stream), against 8 TB/s.
+CPU baseline: the float64 oracle on a bounded sample of views, same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12
+
+
+def _kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("ct_kernels.hip", "ct_abi.hip", "ct_geometry.cpp"):
+        with open(os.path.join(ROOT, "ray_driven_projector_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str, workload: str, per_launch_bytes_unused=None):
+    """HBM bytes per launch measured by rocprofv3 counters, if a summary taken on
+    the current kernel sources is committed under profiles/; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        if d.get("source_hash") != _kernel_source_hash():
+            return None
+        return float(d["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(wl, n_views_sample: int):
+    """Float64 oracle on the first views of the workload (A then A^T)."""
+    import numpy as np
+
+    import oracle
+    from ray_driven_projector_amd import workloads as W
+
+    if wl.config == 4:
+        half = wl.n_views // 2
+        k = max(1, n_views_sample // 2)
+        views = list(range(half - k // 2, half - k // 2 + k)) + list(range(2 * half - k, 2 * half))
+    else:
+        views = list(range(n_views_sample))
+    sub = wl.subset_views(views)
+    og = oracle.Geometry.from_workload(sub)
+    x = W.make_phantom(wl)
+    nt = oracle.default_threads()
+    t0 = time.perf_counter()
+    sino, nnz, _ = oracle.project(og, x, nthreads=nt, with_counts=True)
+    t1 = time.perf_counter()
+    oracle.backproject(og, sino, nthreads=nt)
+    t2 = time.perf_counter()
+    rate = 2 * nnz / (t2 - t0) / 1e9
+    return {"value": rate, "unit": "G ray-voxel intersections/s", "cores": nt, "kind": "oracle",
+            "sample": f"{len(views)} of {wl.n_views} views of the same workload: A then A^T, "
+                      f"{nnz} intersections each; A {t1 - t0:.2f} s, A^T {t2 - t1:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=["c4", "c5"], default="c4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-views", type=int, default=16)
+    ap.add_argument("--extra", action="store_true", help="also time A, A^T and atomic A^T alone")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py: this build targets one GPU; the multi-GPU sharding of the path is "
+              "described in DESIGN.md and not run. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ray_driven_projector_amd as rdp
+    from ray_driven_projector_amd import workloads as W
+
+    if not os.path.exists(rdp.LIB_PATH):
+        from ray_driven_projector_amd import build as b
+        b.build()
+    torch.cuda.set_device(0)
+    cfg = 4 if args.workload == "c4" else 5
+    wl = W.make_workload(cfg)
+    print(f"# workload: {wl.name}", file=sys.stderr, flush=True)
+    phantom = W.make_phantom(wl)
+    g = rdp.Geometry.from_workload(wl)
+    stream = torch.cuda.current_stream()
+    x_true = torch.from_numpy(phantom).cuda()
+    y = torch.empty(g.sino_shape, device="cuda")
+    rdp.ct_project(g, x_true, y)                     # synthetic measurement
+    nnz = rdp.ct_count_intersections(g)
+    M, N = wl.n_rays, wl.n_voxels
+    print(f"# nnz={nnz} rays={M} voxels={N}", file=sys.stderr, flush=True)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    if cfg == 4:
+        rinv = torch.empty(g.sino_shape, device="cuda")
+        cinv = torch.empty(g.vol_shape, device="cuda")
+        rdp.ct_sirt_weights(g, rinv, cinv)
+        x = torch.zeros(g.vol_shape, device="cuda")
+        work = torch.empty(g.sino_shape, device="cuda")
+        names = ("sirt_residual", "sirt_update")
+        bytes_per = {"sirt_residual": 4 * nnz + 12 * M, "sirt_update": 4 * nnz + 4 * M + 12 * N}
+        kern_names = {"sirt_residual": "ray_kernel<1, false>", "sirt_update": "brick_kernel<16, 16, 16, 256, 1>"}
+
+        def step(evs):
+            evs[0].record(stream)
+            rdp.ct_sirt_residual(g, x, y, rinv, work, stream)
+            evs[1].record(stream)
+            rdp.ct_sirt_update(g, work, cinv, 1.0, x, stream)
+            evs[2].record(stream)
+    else:
+        xs = x_true
+        sino = torch.empty(g.sino_shape, device="cuda")
+        vol = torch.empty(g.vol_shape, device="cuda")
+        names = ("project", "backproject")
+        bytes_per = {"project": 4 * nnz + 4 * M, "backproject": 4 * nnz + 4 * M + 4 * N}
+        kern_names = {"project": "ray_kernel<0, false>", "backproject": "brick_kernel<16, 16, 16, 256, 0>"}
+
+        def step(evs):
+            evs[0].record(stream)
+            rdp.ct_project(g, xs, sino, stream)
+            evs[1].record(stream)
+            rdp.ct_backproject(g, y, vol, stream)
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step([ev(), ev(), ev()])
+    torch.cuda.synchronize()
+    all_evs = [[ev(), ev(), ev()] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(all_evs[k])
+        print(f"# step {k} enqueued", file=sys.stderr, flush=True) if k == 0 else None
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms = {names[0]: [], names[1]: []}
+    for e in all_evs:
+        k_ms[names[0]].append(e[0].elapsed_time(e[1]))
+        k_ms[names[1]].append(e[1].elapsed_time(e[2]))
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    avg = {k: float(np.mean(v)) for k, v in k_ms.items()}
+    dom = max(avg, key=avg.get)
+    achieved = bytes_per[dom] / (avg[dom] * 1e-3)
+    value = 2 * nnz / (ms_step * 1e-3) / 1e9
+
+    extra = {}
+    if args.extra:
+        out_s = torch.empty(g.sino_shape, device="cuda")
+        out_v = torch.empty(g.vol_shape, device="cuda")
+        for name, fn, a, b in (("A", rdp.ct_project, x_true, out_s), ("AT", rdp.ct_backproject, y, out_v),
+                               ("AT_atomic", rdp.ct_backproject_atomic, y, out_v)):
+            fn(g, a, b, stream)
+            ts = []
+            for _ in range(3 if name != "AT_atomic" else 1):
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                fn(g, a, b, stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            extra[f"{name}_ms"] = float(np.median(ts))
+            extra[f"{name}_G_intersections_per_s"] = nnz / (np.median(ts) * 1e-3) / 1e9
+
+    res = {
+        "metric": "G ray-voxel intersections/s for A and A^T; ms per SIRT iteration at 512^3",
+        "value": round(value, 3),
+        "unit": "G ray-voxel intersections/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (wl.name + (", one SIRT iteration (A with residual + A^T with update)"
+                                    if cfg == 4 else ", A + A^T")),
+            "volume": list(wl.vol_shape), "views": wl.n_views, "detector": list(wl.det_shape),
+            "intersections_per_pass": nnz, "rays": M, "voxels": N,
+        },
+        "ms_per_sirt_iteration": round(ms_step, 3) if cfg == 4 else None,
+        "kernel_ms": {k: round(v, 3) for k, v in avg.items()},
+        "roofline": {
+            "bound": "hbm", "kernel": kern_names[dom], "achieved": round(achieved / 1e9, 1),
+            "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
+            "traffic": _traffic(dom, args.workload),
+            "algorithmic_bytes_per_launch": bytes_per[dom],
+        },
+    }
+    res.update(extra)
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_views)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * ctproj.h -- C ABI of the MI355X (gfx950) ray-driven projector pair.
+ *
+ * The library computes, for an arbitrary per-view acquisition geometry,
+ *
+ *   A    : the cell-constant Siddon forward projector.  Entry a_ij is the
+ *          length of ray i inside voxel j, so (A x)_i is the line integral of
+ *          the piecewise-constant volume along ray i (diffct documentation,
+ *          "Differentiable analytical reconstruction"; one ray per detector
+ *          pixel, no detector-area integration: "Trajectories and Geometry" >
+ *          "Parameterized detector surfaces").
+ *   A^T  : its matched adjoint (backprojection), the exact transpose of A
+ *          (diffct documentation, Projector.backproject: "Apply the matched
+ *          adjoint"; Quickstart: "matched adjoint A^T", "not an inverse").
+ *   SIRT : x <- x + relax * C A^T R (y - A x) with R = 1/(A 1) per ray and
+ *          C = 1/(A^T 1) per voxel, each 0 where the sum is 0 (the pages name
+ *          a SIRT solver -- diffct "API Reference" > "Numerical Solvers",
+ *          ASTRA SIRT3D_CUDA in the electron-tomography article -- without
+ *          printing its formula; this is the standard form).
+ *
+ * Conventions (diffct documentation, "Trajectories and Geometry" >
+ * "Trajectory format"):
+ *   - Cartesian (x, y, z) coordinates, origin at the volume centre, one length
+ *     unit for positions and spacings.
+ *   - Volume: float32, C-contiguous (D, H, W), i.e. index ((z*H)+y)*W+x.
+ *     2D beams use D = 1 (dz is then ignored).
+ *   - Sinogram: float32, C-contiguous (views, U, V), V fastest.  2D: V = 1.
+ *   - Flat-detector pixel (u, v) centre:
+ *       det_center + (u - (U-1)/2) du det_u + (v - (V-1)/2) dv det_v.
+ *   - fan/cone rays are the segment from the source to the pixel centre;
+ *     parallel and parallel3d rays are infinite lines through the pixel
+ *     (Projector class reference: "its infinite ray lines pass through
+ *     detector pixels").
+ *   - Voxels are half-open boxes [lo + k s, lo + (k+1) s): a ray lying exactly
+ *     on a lattice plane belongs to the higher-index cell.
+ *
+ * Ownership and threading:
+ *   - Every float* argument of the compute calls is a DEVICE pointer owned by
+ *     the caller (e.g. a torch tensor's data_ptr()).  The library never frees
+ *     or retains them.
+ *   - A geometry handle is owned by the library from ct_geom_create until
+ *     ct_geom_destroy.  It is immutable after creation; concurrent calls on
+ *     different streams with the same handle are safe.
+ *   - Every compute call is asynchronous and ordered on the caller's stream
+ *     (a hipStream_t passed as void*; NULL is the legacy default stream).
+ *   - Compute calls allocate nothing: all device memory they touch is the
+ *     caller's buffers plus the handle's own tables.
+ *
+ * Errors: every call returns a ct_status_t.  Host-side validation happens
+ * before anything is enqueued; on error nothing was launched.  A launch
+ * failure reported by the HIP runtime is returned as CT_E_HIP.  No C++
+ * exception crosses this interface.  ct_last_error() gives a message for the
+ * most recent failing call on the calling thread.
+ */
+#ifndef CTPROJ_H
+#define CTPROJ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ct_geom_s *ct_geom_t;     /* opaque, library-owned */
+typedef void *ct_stream_t;               /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+    CT_PARALLEL2D = 0,   /* rows: ray_dir, det_origin (= detector centre), det_u   */
+    CT_FAN2D = 1,        /* rows: src_pos, det_center, det_u                       */
+    CT_CONE = 2,         /* rows: src_pos, det_center, det_u, det_v                */
+    CT_PARALLEL3D = 3    /* rows: ray_dir, det_center, det_u, det_v                */
+} ct_beam_t;
+
+typedef enum {
+    CT_OK = 0,
+    CT_E_NULL = 1,       /* a required pointer is NULL                              */
+    CT_E_SHAPE = 2,      /* a size is zero/negative or inconsistent with the beam  */
+    CT_E_NONFINITE = 3,  /* a frame value or spacing is NaN or infinite            */
+    CT_E_FRAME = 4,      /* axes not unit / not orthogonal, ray tangent to the
+                            detector, source on the detector plane or at its centre */
+    CT_E_RANGE = 5,      /* geometry too far from the volume, or sizes beyond the
+                            library's limits                                        */
+    CT_E_ALIAS = 6,      /* an output buffer overlaps another buffer of the call    */
+    CT_E_NOMEM = 7,      /* device allocation of the handle's tables failed         */
+    CT_E_HIP = 8,        /* the HIP runtime reported an error                       */
+    CT_E_ARG = 9         /* invalid enum value, handle, spacing or scalar argument  */
+} ct_status_t;
+
+typedef struct {
+    int32_t beam;               /* ct_beam_t */
+    int32_t reserved;           /* must be 0 */
+    int64_t n_views;            /* >= 1 */
+    int64_t vol_shape[3];       /* (D, H, W); 2D beams: D = 1 */
+    double voxel_spacing[3];    /* (dz, dy, dx) > 0; 2D: dz ignored */
+    int64_t det_shape[2];       /* (U, V); 2D beams: V = 1 */
+    double det_spacing[2];      /* (du, dv) > 0; 2D: dv ignored */
+    const double *frames;       /* HOST pointer, n_views x 12 float64, row-major:
+                                   a(3) c(3) e_u(3) e_v(3) in (x, y, z) order, with
+                                   a = src_pos (fan, cone) or ray_dir (parallel,
+                                   parallel3d), c = detector centre.  2D beams: all
+                                   z components 0, e_v ignored.  Copied at create. */
+} ct_geom_desc_t;
+
+/*
+ * Frame validation only (host, float64, no device work).  Rules follow diffct
+ * "Trajectories and Geometry" > "Custom acquisition example": finite values,
+ * the same nonzero view count, unit direction axes, ray_dir orthogonal to
+ * det_u (2D parallel), det_u orthogonal to det_v (3D), parallel3d rays not
+ * tangent to the detector plane, fan/cone source not at the detector centre
+ * and not viewing the detector edge-on, the nearer of source and detector
+ * centre within 1e6 voxel spacings of the origin and both within 1e15.
+ * Tolerances: |norm - 1| <= 1e-6, |dot| <= 1e-6, |ray . normal| > 1e-6.
+ * Library limits: D*H*W < 2^30, views*U*V < 2^31, each extent < 2^20, voxel
+ * spacings in [1e-10, 1e10] within a ratio of 1e6 of each other.
+ */
+ct_status_t ct_geom_validate(const ct_geom_desc_t *desc);
+
+/* Validate, precompute the per-view float64 ray table, allocate and upload it
+ * to the current HIP device (synchronous).  *out receives the handle. */
+ct_status_t ct_geom_create(const ct_geom_desc_t *desc, ct_geom_t *out);
+
+/* Free the handle and its device tables.  NULL is accepted.  The caller must
+ * make sure no work using the handle is still pending. */
+ct_status_t ct_geom_destroy(ct_geom_t g);
+
+/* Host copy of the per-view ray table (n_views x CT_VIEW_TABLE_STRIDE doubles),
+ * for inspection.  Works without a device: it may be called on a handle made by
+ * ct_geom_create, or with desc != NULL and g == NULL to compute it on the host. */
+#define CT_VIEW_TABLE_STRIDE 40
+ct_status_t ct_geom_view_table(ct_geom_t g, const ct_geom_desc_t *desc, double *out);
+
+/* Forward projection A: sino[view][u][v] = sum_j a_ij vol[j].
+ * vol: device (D,H,W) float32; sino: device (views,U,V) float32.
+ * Every ray is written, missed rays as 0 (diffct "Large Volumes and Chunked
+ * Execution" > "Resident layouts and accumulation": forward kernels overwrite
+ * each ray, including missed rays).  vol and sino must not overlap. */
+ct_status_t ct_project(ct_geom_t g, const float *vol, float *sino, ct_stream_t stream);
+
+/* Matched adjoint A^T: vol[j] = sum_i a_ij sino[i]; every voxel is overwritten.
+ * Volume bricks accumulate their rays in on-chip memory (LDS) and are each
+ * written once, with no global atomics.  The LDS adds of different waves
+ * interleave freely, so the float32 summation order, and with it the last bits
+ * of the result, can differ between runs (the diffct documentation notes the
+ * same of its atomic adjoint in "Example results").  sino and vol must not
+ * overlap. */
+ct_status_t ct_backproject(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream);
+
+/* The same A^T by one lane per ray with global float atomics (a measured
+ * baseline; float32 summation order varies between runs, as the diffct
+ * documentation notes for its atomic adjoint in "Example results"). */
+ct_status_t ct_backproject_atomic(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream);
+
+/* SIRT weights (once per geometry): row_inv[i] = 1/(A 1)_i, col_inv[j] =
+ * 1/(A^T 1)_j, each 0 where the sum is 0.  row_inv: (views,U,V); col_inv:
+ * (D,H,W); device float32, non-overlapping. */
+ct_status_t ct_sirt_weights(ct_geom_t g, float *row_inv, float *col_inv, ct_stream_t stream);
+
+/* First half of a SIRT iteration: work_sino = row_inv * (y - A x). */
+ct_status_t ct_sirt_residual(ct_geom_t g, const float *x, const float *y, const float *row_inv,
+                             float *work_sino, ct_stream_t stream);
+
+/* Second half: x += relax * col_inv * A^T work_sino (x read and written in place). */
+ct_status_t ct_sirt_update(ct_geom_t g, const float *work_sino, const float *col_inv, float relax,
+                           float *x, ct_stream_t stream);
+
+/* One SIRT iteration = ct_sirt_residual then ct_sirt_update, stream-ordered.
+ * work_sino is caller scratch of sinogram size; relax must be finite. */
+ct_status_t ct_sirt_step(ct_geom_t g, float *x, const float *y, const float *row_inv,
+                         const float *col_inv, float relax, float *work_sino, ct_stream_t stream);
+
+/* Ray-voxel intersections: the number of (ray, voxel) pairs the traversal
+ * visits, i.e. per ray the number of lattice-plane crossings inside the volume
+ * plus one, from the float64 entry and exit cells.  This equals the number of
+ * pairs with positive length except where a ray crosses two planes at exactly
+ * the same point.  per_ray (device uint32, sinogram-shaped) may be NULL; if
+ * non-NULL it receives each ray's count.  *total (host) receives the sum; this
+ * call synchronises the stream. */
+ct_status_t ct_count_intersections(ct_geom_t g, uint32_t *per_ray, uint64_t *total,
+                                   ct_stream_t stream);
+
+/* Message of the most recent failing call on this thread ("" if none). */
+const char *ct_last_error(void);
+
+/* Library version string. */
+const char *ct_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CTPROJ_H */

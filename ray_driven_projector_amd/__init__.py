@@ -1,0 +1,247 @@
+"""Python binding of libctproj, the gfx950 ray-driven projector pair.
+
+The functions here carry the C ABI's names (include/ctproj.h) and only marshal
+arguments: torch tensors are checked (device, dtype, contiguity, shape) and
+their device pointers and the current HIP stream are handed to the library.
+Every step of the computation runs in the library's HIP kernels.  If the
+built library is missing, the first call raises; there is no fallback.
+
+Geometry: ``Geometry`` wraps a ``ct_geom_t`` handle made from a beam type,
+shapes and per-view frames (see ``workloads.py`` for the frame layout).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libctproj.so")
+
+CT_OK, CT_E_NULL, CT_E_SHAPE, CT_E_NONFINITE, CT_E_FRAME, CT_E_RANGE, CT_E_ALIAS, \
+    CT_E_NOMEM, CT_E_HIP, CT_E_ARG = range(10)
+STATUS_NAMES = {0: "CT_OK", 1: "CT_E_NULL", 2: "CT_E_SHAPE", 3: "CT_E_NONFINITE",
+                4: "CT_E_FRAME", 5: "CT_E_RANGE", 6: "CT_E_ALIAS", 7: "CT_E_NOMEM",
+                8: "CT_E_HIP", 9: "CT_E_ARG"}
+CT_PARALLEL2D, CT_FAN2D, CT_CONE, CT_PARALLEL3D = range(4)
+CT_VIEW_TABLE_STRIDE = 40
+
+# every symbol declared in include/ctproj.h
+EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_destroy", "ct_geom_view_table",
+           "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_sirt_weights",
+           "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_count_intersections",
+           "ct_last_error", "ct_version"]
+
+
+class CtError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class GeomDesc(ctypes.Structure):
+    _fields_ = [("beam", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n_views", ctypes.c_int64),
+                ("vol_shape", ctypes.c_int64 * 3), ("voxel_spacing", ctypes.c_double * 3),
+                ("det_shape", ctypes.c_int64 * 2), ("det_spacing", ctypes.c_double * 2),
+                ("frames", ctypes.POINTER(ctypes.c_double))]
+
+
+_lib = None
+
+
+def lib():
+    """Load libctproj.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run ray_driven_projector_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P, c = ctypes.POINTER, ctypes
+        vp = c.c_void_p
+        st = c.c_int
+        L.ct_geom_validate.argtypes = [P(GeomDesc)]
+        L.ct_geom_create.argtypes = [P(GeomDesc), P(vp)]
+        L.ct_geom_destroy.argtypes = [vp]
+        L.ct_geom_view_table.argtypes = [vp, P(GeomDesc), P(c.c_double)]
+        L.ct_project.argtypes = [vp, vp, vp, vp]
+        L.ct_backproject.argtypes = [vp, vp, vp, vp]
+        L.ct_backproject_atomic.argtypes = [vp, vp, vp, vp]
+        L.ct_sirt_weights.argtypes = [vp, vp, vp, vp]
+        L.ct_sirt_residual.argtypes = [vp, vp, vp, vp, vp, vp]
+        L.ct_sirt_update.argtypes = [vp, vp, vp, c.c_float, vp, vp]
+        L.ct_sirt_step.argtypes = [vp, vp, vp, vp, vp, c.c_float, vp, vp]
+        L.ct_count_intersections.argtypes = [vp, vp, P(c.c_uint64), vp]
+        for name in EXPORTS[:-2]:
+            getattr(L, name).restype = st
+        L.ct_last_error.restype = c.c_char_p
+        L.ct_last_error.argtypes = []
+        L.ct_version.restype = c.c_char_p
+        L.ct_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != CT_OK:
+        raise CtError(status, lib().ct_last_error().decode())
+
+
+def make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames):
+    """Build a ct_geom_desc_t; returns (desc, frames_array) -- keep both alive."""
+    fr = np.ascontiguousarray(frames, dtype=np.float64)
+    if fr.ndim != 2 or fr.shape[1] != 12:
+        raise ValueError("frames must be (n_views, 12)")
+    d = GeomDesc()
+    d.beam = int(beam)
+    d.reserved = 0
+    d.n_views = fr.shape[0]
+    for k in range(3):
+        d.vol_shape[k] = int(vol_shape[k])
+        d.voxel_spacing[k] = float(voxel_spacing[k])
+    for k in range(2):
+        d.det_shape[k] = int(det_shape[k])
+        d.det_spacing[k] = float(det_spacing[k])
+    d.frames = fr.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    return d, fr
+
+
+def ct_geom_validate(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames) -> int:
+    """Host-only frame validation; returns the ct_status_t code."""
+    d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
+    return int(lib().ct_geom_validate(ctypes.byref(d)))
+
+
+def ct_geom_view_table(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames):
+    """Host-computed per-view ray table (n_views x 40 float64)."""
+    d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
+    out = np.zeros((fr.shape[0], CT_VIEW_TABLE_STRIDE), dtype=np.float64)
+    _check(lib().ct_geom_view_table(None, ctypes.byref(d),
+                                    out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    return out
+
+
+def last_error() -> str:
+    return lib().ct_last_error().decode()
+
+
+class Geometry:
+    """A ct_geom_t handle (device tables on the current HIP device)."""
+
+    def __init__(self, beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames):
+        d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
+        h = ctypes.c_void_p()
+        _check(lib().ct_geom_create(ctypes.byref(d), ctypes.byref(h)))
+        self._h = h
+        self.beam = int(beam)
+        self.vol_shape = tuple(int(x) for x in vol_shape)
+        self.sino_shape = (fr.shape[0], int(det_shape[0]), int(det_shape[1]))
+
+    @classmethod
+    def from_workload(cls, wl) -> "Geometry":
+        return cls(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing, wl.frames)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().ct_geom_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):  # pragma: no cover - best effort
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _ptr(t, shape, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def ct_project(g: Geometry, vol, sino, stream=None):
+    """sino <- A vol (overwrites every ray)."""
+    _check(lib().ct_project(g.handle, _ptr(vol, g.vol_shape, "vol"),
+                            _ptr(sino, g.sino_shape, "sino"), _stream(stream)))
+    return sino
+
+
+def ct_backproject(g: Geometry, sino, vol, stream=None):
+    """vol <- A^T sino (brick-binned, overwrites every voxel)."""
+    _check(lib().ct_backproject(g.handle, _ptr(sino, g.sino_shape, "sino"),
+                                _ptr(vol, g.vol_shape, "vol"), _stream(stream)))
+    return vol
+
+
+def ct_backproject_atomic(g: Geometry, sino, vol, stream=None):
+    """vol <- A^T sino (one lane per ray, global float atomics)."""
+    _check(lib().ct_backproject_atomic(g.handle, _ptr(sino, g.sino_shape, "sino"),
+                                       _ptr(vol, g.vol_shape, "vol"), _stream(stream)))
+    return vol
+
+
+def ct_sirt_weights(g: Geometry, row_inv, col_inv, stream=None):
+    _check(lib().ct_sirt_weights(g.handle, _ptr(row_inv, g.sino_shape, "row_inv"),
+                                 _ptr(col_inv, g.vol_shape, "col_inv"), _stream(stream)))
+    return row_inv, col_inv
+
+
+def ct_sirt_residual(g: Geometry, x, y, row_inv, work_sino, stream=None):
+    _check(lib().ct_sirt_residual(g.handle, _ptr(x, g.vol_shape, "x"), _ptr(y, g.sino_shape, "y"),
+                                  _ptr(row_inv, g.sino_shape, "row_inv"),
+                                  _ptr(work_sino, g.sino_shape, "work_sino"), _stream(stream)))
+    return work_sino
+
+
+def ct_sirt_update(g: Geometry, work_sino, col_inv, relax, x, stream=None):
+    _check(lib().ct_sirt_update(g.handle, _ptr(work_sino, g.sino_shape, "work_sino"),
+                                _ptr(col_inv, g.vol_shape, "col_inv"), float(relax),
+                                _ptr(x, g.vol_shape, "x"), _stream(stream)))
+    return x
+
+
+def ct_sirt_step(g: Geometry, x, y, row_inv, col_inv, relax, work_sino, stream=None):
+    _check(lib().ct_sirt_step(g.handle, _ptr(x, g.vol_shape, "x"), _ptr(y, g.sino_shape, "y"),
+                              _ptr(row_inv, g.sino_shape, "row_inv"),
+                              _ptr(col_inv, g.vol_shape, "col_inv"), float(relax),
+                              _ptr(work_sino, g.sino_shape, "work_sino"), _stream(stream)))
+    return x
+
+
+def ct_count_intersections(g: Geometry, per_ray=None, stream=None) -> int:
+    """Number of (ray, voxel) pairs with positive float32 length (syncs the stream)."""
+    import torch
+    total = ctypes.c_uint64(0)
+    p = ctypes.c_void_p(0)
+    if per_ray is not None:
+        if per_ray.dtype not in (torch.int32, torch.uint32) or not per_ray.is_cuda \
+                or not per_ray.is_contiguous() or tuple(per_ray.shape) != tuple(g.sino_shape):
+            raise ValueError("per_ray must be a contiguous int32 device tensor of sinogram shape")
+        p = ctypes.c_void_p(per_ray.data_ptr())
+    _check(lib().ct_count_intersections(g.handle, p, ctypes.byref(total), _stream(stream)))
+    return int(total.value)
+
+
+def version() -> str:
+    return lib().ct_version().decode()

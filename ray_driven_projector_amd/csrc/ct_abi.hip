@@ -1,0 +1,314 @@
+// ct_abi.hip -- the extern "C" entry points declared in include/ctproj.h.
+//
+// Each call validates its arguments on the host (null pointers, handle,
+// overlapping buffers) before anything is enqueued, then launches on the
+// caller's stream.  Buffer aliasing is rejected as the diffct Projector class
+// reference describes for project_into ("Known overlapping/read-only outputs
+// are rejected before execution").
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "ct_internal.h"
+#include "ct_launch.h"
+
+namespace ctp {
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+void set_error(const char *msg) {
+    std::snprintf(g_err, sizeof g_err, "%s", msg ? msg : "");
+}
+
+}  // namespace ctp
+
+using namespace ctp;
+
+struct ct_geom_s {
+    uint64_t magic;
+    GeomHost host;
+    std::vector<double> table;          // host copy of the view table
+    double *d_views = nullptr;          // device view table
+    unsigned long long *d_total = nullptr;  // device counter for ct_count_intersections
+    int device = 0;
+};
+
+namespace {
+
+constexpr uint64_t kMagic = 0x43545052'4F4A3031ull;  // "CTPROJ01"
+
+ct_status_t fail(ct_status_t st, const char *msg) {
+    set_error(msg);
+    return st;
+}
+
+ct_status_t hip_fail(hipError_t e, const char *where) {
+    char buf[400];
+    std::snprintf(buf, sizeof buf, "%s: %s", where, hipGetErrorString(e));
+    set_error(buf);
+    return CT_E_HIP;
+}
+
+bool valid(ct_geom_t g) { return g && g->magic == kMagic; }
+
+LaunchGeom lg(ct_geom_t g) {
+    LaunchGeom l;
+    l.views = g->d_views;
+    l.W = (int)g->host.W;
+    l.H = (int)g->host.H;
+    l.D = (int)g->host.D;
+    l.U = (int)g->host.U;
+    l.V = (int)g->host.V;
+    l.n_views = (int)g->host.n_views;
+    l.spx = g->host.sx;
+    l.spy = g->host.sy;
+    l.spz = g->host.sz;
+    l.two_d = g->host.is2d;
+    return l;
+}
+
+size_t vol_bytes(ct_geom_t g) { return (size_t)g->host.D * g->host.H * g->host.W * sizeof(float); }
+size_t sino_bytes(ct_geom_t g) {
+    return (size_t)g->host.n_views * g->host.U * g->host.V * sizeof(float);
+}
+
+struct Span {
+    const void *p;
+    size_t n;
+};
+bool overlap(Span a, Span b) {
+    const char *a0 = (const char *)a.p, *b0 = (const char *)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+struct Arg {
+    Span span;
+    bool output;
+};
+
+// Every output must overlap no other buffer of the call (inputs may share memory).
+ct_status_t check_alias(std::initializer_list<Arg> args) {
+    const Arg *v = args.begin();
+    const size_t n = args.size();
+    for (size_t i = 0; i < n; ++i)
+        for (size_t j = i + 1; j < n; ++j)
+            if ((v[i].output || v[j].output) && overlap(v[i].span, v[j].span))
+                return fail(CT_E_ALIAS, "an output buffer overlaps another buffer of the call");
+    return CT_OK;
+}
+
+ct_status_t launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return hip_fail(e, what);
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ensure_device(ct_geom_t g) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != g->device) return fail(CT_E_ARG, "current HIP device differs from the handle's device");
+    return CT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ct_last_error(void) { return g_err; }
+
+const char *ct_version(void) { return "ctproj 0.1 gfx950"; }
+
+ct_status_t ct_geom_validate(const ct_geom_desc_t *desc) {
+    const char *why = "";
+    ct_status_t st = validate_desc(desc, nullptr, &why);
+    if (st != CT_OK) return fail(st, why);
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_geom_view_table(ct_geom_t g, const ct_geom_desc_t *desc, double *out) {
+    if (!out) return fail(CT_E_NULL, "output pointer is NULL");
+    if (g) {
+        if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+        std::memcpy(out, g->table.data(), g->table.size() * sizeof(double));
+        set_error("");
+        return CT_OK;
+    }
+    GeomHost h;
+    const char *why = "";
+    ct_status_t st = validate_desc(desc, &h, &why);
+    if (st != CT_OK) return fail(st, why);
+    build_view_table(desc, h, out);
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_geom_create(const ct_geom_desc_t *desc, ct_geom_t *out) {
+    if (!out) return fail(CT_E_NULL, "output handle pointer is NULL");
+    *out = nullptr;
+    GeomHost h;
+    const char *why = "";
+    ct_status_t st = validate_desc(desc, &h, &why);
+    if (st != CT_OK) return fail(st, why);
+    ct_geom_s *g = new (std::nothrow) ct_geom_s();
+    if (!g) return fail(CT_E_NOMEM, "host allocation failed");
+    g->magic = kMagic;
+    g->host = h;
+    try {
+        g->table.assign((size_t)h.n_views * CT_VIEW_TABLE_STRIDE, 0.0);
+    } catch (...) {
+        delete g;
+        return fail(CT_E_NOMEM, "host allocation failed");
+    }
+    build_view_table(desc, h, g->table.data());
+    hipError_t e = hipGetDevice(&g->device);
+    if (e != hipSuccess) {
+        delete g;
+        return hip_fail(e, "hipGetDevice");
+    }
+    size_t nb = g->table.size() * sizeof(double);
+    e = hipMalloc((void **)&g->d_views, nb);
+    if (e != hipSuccess) {
+        delete g;
+        (void)hipGetLastError();
+        return fail(CT_E_NOMEM, "hipMalloc of the view table failed");
+    }
+    e = hipMalloc((void **)&g->d_total, sizeof(unsigned long long));
+    if (e != hipSuccess) {
+        (void)hipFree(g->d_views);
+        delete g;
+        (void)hipGetLastError();
+        return fail(CT_E_NOMEM, "hipMalloc of the counter failed");
+    }
+    e = hipMemcpy(g->d_views, g->table.data(), nb, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(g->d_views);
+        (void)hipFree(g->d_total);
+        delete g;
+        return hip_fail(e, "hipMemcpy of the view table");
+    }
+    *out = g;
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_geom_destroy(ct_geom_t g) {
+    if (!g) return CT_OK;
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    g->magic = 0;
+    if (g->d_views) (void)hipFree(g->d_views);
+    if (g->d_total) (void)hipFree(g->d_total);
+    delete g;
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_project(ct_geom_t g, const float *vol, float *sino, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!vol || !sino) return fail(CT_E_NULL, "vol and sino must be non-NULL");
+    Span V{vol, vol_bytes(g)}, S{sino, sino_bytes(g)};
+    ct_status_t st = check_alias({{V, false}, {S, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    return launched(launch_project(lg(g), vol, sino, (hipStream_t)stream), "ct_project launch");
+}
+
+ct_status_t ct_backproject(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!vol || !sino) return fail(CT_E_NULL, "vol and sino must be non-NULL");
+    Span V{vol, vol_bytes(g)}, S{sino, sino_bytes(g)};
+    ct_status_t st = check_alias({{V, true}, {S, false}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    return launched(launch_backproject(lg(g), sino, vol, (hipStream_t)stream), "ct_backproject launch");
+}
+
+ct_status_t ct_backproject_atomic(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!vol || !sino) return fail(CT_E_NULL, "vol and sino must be non-NULL");
+    Span V{vol, vol_bytes(g)}, S{sino, sino_bytes(g)};
+    ct_status_t st = check_alias({{V, true}, {S, false}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    return launched(launch_backproject_atomic(lg(g), sino, vol, (hipStream_t)stream),
+                    "ct_backproject_atomic launch");
+}
+
+ct_status_t ct_sirt_weights(ct_geom_t g, float *row_inv, float *col_inv, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!row_inv || !col_inv) return fail(CT_E_NULL, "row_inv and col_inv must be non-NULL");
+    Span R{row_inv, sino_bytes(g)}, C{col_inv, vol_bytes(g)};
+    ct_status_t st = check_alias({{R, true}, {C, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    hipError_t e = launch_rowinv(lg(g), row_inv, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ct_sirt_weights row launch");
+    return launched(launch_colinv(lg(g), col_inv, (hipStream_t)stream), "ct_sirt_weights column launch");
+}
+
+ct_status_t ct_sirt_residual(ct_geom_t g, const float *x, const float *y, const float *row_inv,
+                             float *work_sino, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!x || !y || !row_inv || !work_sino) return fail(CT_E_NULL, "a buffer pointer is NULL");
+    Span X{x, vol_bytes(g)}, Y{y, sino_bytes(g)}, R{row_inv, sino_bytes(g)}, E{work_sino, sino_bytes(g)};
+    ct_status_t st = check_alias({{X, false}, {Y, false}, {R, false}, {E, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    return launched(launch_residual(lg(g), x, y, row_inv, work_sino, (hipStream_t)stream),
+                    "ct_sirt_residual launch");
+}
+
+ct_status_t ct_sirt_update(ct_geom_t g, const float *work_sino, const float *col_inv, float relax,
+                           float *x, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!x || !work_sino || !col_inv) return fail(CT_E_NULL, "a buffer pointer is NULL");
+    if (!std::isfinite(relax)) return fail(CT_E_ARG, "relax must be finite");
+    Span X{x, vol_bytes(g)}, E{work_sino, sino_bytes(g)}, C{col_inv, vol_bytes(g)};
+    ct_status_t st = check_alias({{X, true}, {E, false}, {C, false}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    return launched(launch_sirt_update(lg(g), work_sino, col_inv, relax, x, (hipStream_t)stream),
+                    "ct_sirt_update launch");
+}
+
+ct_status_t ct_sirt_step(ct_geom_t g, float *x, const float *y, const float *row_inv,
+                         const float *col_inv, float relax, float *work_sino, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!x || !y || !row_inv || !col_inv || !work_sino) return fail(CT_E_NULL, "a buffer pointer is NULL");
+    if (!std::isfinite(relax)) return fail(CT_E_ARG, "relax must be finite");
+    Span X{x, vol_bytes(g)}, Y{y, sino_bytes(g)}, R{row_inv, sino_bytes(g)}, C{col_inv, vol_bytes(g)},
+        E{work_sino, sino_bytes(g)};
+    ct_status_t st = check_alias({{X, true}, {Y, false}, {R, false}, {C, false}, {E, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    hipError_t e = launch_residual(lg(g), x, y, row_inv, work_sino, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ct_sirt_step residual launch");
+    return launched(launch_sirt_update(lg(g), work_sino, col_inv, relax, x, (hipStream_t)stream),
+                    "ct_sirt_step update launch");
+}
+
+ct_status_t ct_count_intersections(ct_geom_t g, uint32_t *per_ray, uint64_t *total, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!total) return fail(CT_E_NULL, "total must be non-NULL");
+    ct_status_t st = ensure_device(g);
+    if (st != CT_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_count(lg(g), per_ray, g->d_total, s);
+    if (e != hipSuccess) return hip_fail(e, "ct_count_intersections launch");
+    unsigned long long host = 0;
+    e = hipMemcpyAsync(&host, g->d_total, sizeof host, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "ct_count_intersections copy");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "ct_count_intersections sync");
+    *total = (uint64_t)host;
+    set_error("");
+    return CT_OK;
+}
+
+}  // extern "C"

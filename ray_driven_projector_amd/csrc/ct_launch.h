@@ -1,0 +1,32 @@
+// ct_launch.h -- launchers implemented in ct_kernels.hip, used by ct_abi.hip.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace ctp {
+
+struct LaunchGeom {
+    const double *views;  // device view table
+    int W, H, D, U, V, n_views;
+    double spx, spy, spz;  // voxel spacing (x, y, z)
+    bool two_d;
+};
+
+hipError_t launch_fill(float *p, size_t n, float v, hipStream_t s);
+hipError_t launch_project(const LaunchGeom &g, const float *vol, float *sino, hipStream_t s);
+hipError_t launch_residual(const LaunchGeom &g, const float *x, const float *y, const float *rinv,
+                           float *e, hipStream_t s);
+hipError_t launch_rowinv(const LaunchGeom &g, float *rinv, hipStream_t s);
+hipError_t launch_count(const LaunchGeom &g, uint32_t *per_ray, unsigned long long *total,
+                        hipStream_t s);
+hipError_t launch_backproject_atomic(const LaunchGeom &g, const float *sino, float *vol,
+                                     hipStream_t s);
+hipError_t launch_backproject(const LaunchGeom &g, const float *sino, float *vol, hipStream_t s);
+hipError_t launch_sirt_update(const LaunchGeom &g, const float *e, const float *cinv, float relax,
+                              float *x, hipStream_t s);
+hipError_t launch_colinv(const LaunchGeom &g, float *cinv, hipStream_t s);
+
+}  // namespace ctp
