@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-views", type=int, default=16)
     ap.add_argument("--extra", action="store_true", help="also time A, A^T and atomic A^T alone")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy first (reference kernel for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -112,6 +114,12 @@ def main():
         from ray_driven_projector_amd import build as b
         b.build()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = 4 if args.workload == "c4" else 5
     wl = W.make_workload(cfg)
     print(f"# workload: {wl.name}", file=sys.stderr, flush=True)
@@ -134,7 +142,7 @@ def main():
         work = torch.empty(g.sino_shape, device="cuda")
         names = ("sirt_residual", "sirt_update")
         bytes_per = {"sirt_residual": 4 * nnz + 12 * M, "sirt_update": 4 * nnz + 4 * M + 12 * N}
-        kern_names = {"sirt_residual": "ray_kernel<1, false>", "sirt_update": "brick_kernel<16, 16, 16, 256, 1>"}
+        kern_names = {"sirt_residual": "ray_kernel<1, false>", "sirt_update": "brick_kernel<32, 16, 16, 512, 1>"}
 
         def step(evs):
             evs[0].record(stream)
@@ -148,7 +156,7 @@ def main():
         vol = torch.empty(g.vol_shape, device="cuda")
         names = ("project", "backproject")
         bytes_per = {"project": 4 * nnz + 4 * M, "backproject": 4 * nnz + 4 * M + 4 * N}
-        kern_names = {"project": "ray_kernel<0, false>", "backproject": "brick_kernel<16, 16, 16, 256, 0>"}
+        kern_names = {"project": "ray_kernel<0, false>", "backproject": "brick_kernel<32, 16, 16, 512, 0>"}
 
         def step(evs):
             evs[0].record(stream)

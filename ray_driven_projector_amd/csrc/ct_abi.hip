@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -36,6 +37,8 @@ struct ct_geom_s {
     double *d_views = nullptr;          // device view table
     unsigned long long *d_total = nullptr;  // device counter for ct_count_intersections
     int device = 0;
+    int fwd_lg_tv = 2;                  // forward wave patch 16 u x 4 v
+    int brick_shape = 2;                // adjoint bricks of 32 x 16 x 16
 };
 
 namespace {
@@ -69,6 +72,8 @@ LaunchGeom lg(ct_geom_t g) {
     l.spy = g->host.sy;
     l.spz = g->host.sz;
     l.two_d = g->host.is2d;
+    l.fwd_lg_tv = g->fwd_lg_tv;
+    l.brick_shape = g->brick_shape;
     return l;
 }
 
@@ -100,6 +105,23 @@ ct_status_t check_alias(std::initializer_list<Arg> args) {
             if ((v[i].output || v[j].output) && overlap(v[i].span, v[j].span))
                 return fail(CT_E_ALIAS, "an output buffer overlaps another buffer of the call");
     return CT_OK;
+}
+
+// Launch shapes.  CTPROJ_FWD_LGTV (0..6) and CTPROJ_BRICK (0..2) override the
+// defaults for tuning sweeps; both only change the work decomposition.
+// Defaults measured on 512^3 cone and parallel3d workloads: 16 x 4 pixel patches
+// per wave for the forward gather, 32 x 16 x 16 voxel bricks for the adjoint.
+void choose_tiles(ct_geom_s *g) {
+    g->fwd_lg_tv = 2;
+    g->brick_shape = 2;
+    if (const char *e = std::getenv("CTPROJ_FWD_LGTV")) {
+        const int v = std::atoi(e);
+        if (v >= 0 && v <= 6) g->fwd_lg_tv = v;
+    }
+    if (const char *e = std::getenv("CTPROJ_BRICK")) {
+        const int v = std::atoi(e);
+        if (v >= 0 && v <= 2) g->brick_shape = v;
+    }
 }
 
 ct_status_t launched(hipError_t e, const char *what) {
@@ -167,6 +189,7 @@ ct_status_t ct_geom_create(const ct_geom_desc_t *desc, ct_geom_t *out) {
         return fail(CT_E_NOMEM, "host allocation failed");
     }
     build_view_table(desc, h, g->table.data());
+    choose_tiles(g);
     hipError_t e = hipGetDevice(&g->device);
     if (e != hipSuccess) {
         delete g;

@@ -7,16 +7,22 @@
 // axes, so the ray's parameter interval inside the volume is cut at each plane
 // crossing and each piece lies in exactly one cell.
 //
-// Numerics.  Per ray, the clip against the box, the first and last cell and the
-// number of plane crossings per axis are computed in float64.  The walk itself
-// runs in float32 on the physical distance measured from the ray's entry point:
-// the m-th crossing of axis a sits at fma(m, q_a, l0_a) (q_a = length per cell
-// along a, l0_a = distance to the first crossing), recomputed rather than
-// accumulated so its error stays at one rounding.  The walk ends at
-//   l_end = min(chord, min_a fma(N_a, q_a, l0_a)),
-// evaluated with the same float32 expression as the crossings; since that
-// expression is monotone in m, any crossing taken before l_end is one of the
-// N_a real crossings of its axis, so cell indices never leave the volume.
+// Walk.  The pieces of a ray are enumerated by an integer fixed-point walk: the
+// positions of the next crossing on each axis are unsigned 32-bit multiples of a
+// per-walk unit (about 1e-9 of the walk's length).  The m-th crossing of axis a is
+// l0_a + m q_a, formed by exact (saturating) integer adds, so nothing drifts; the
+// walk ends at
+//   l_end = min(chord, min_a (l0_a + N_a q_a)),
+// N_a being the number of planes of axis a crossed inside the interval (from
+// float64 or float32 entry/exit cells).  Any crossing taken before l_end is
+// therefore one of the N_a real crossings of its axis, so cell indices never leave
+// the volume or the brick, whatever the rounding of the set-up.
+//
+// Precision.  The forward gather sets each ray up in float64 and re-bases the walk
+// every kChunk cells of the major axis, so every piece length is resolved to
+// better than 1e-5 of a cell.  The brick adjoint sets each ray up in float32 in
+// brick-local coordinates (positions within tens of voxels).  The atomic adjoint
+// keeps a float64 walk.
 //
 // Layout.  Volume (D,H,W) float32, sinogram (views,U,V) float32, V fastest.
 #include <hip/hip_runtime.h>
@@ -51,9 +57,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+// Out-of-range offsets (including negative ones, seen as huge unsigned values)
+// read 0 through a buffer resource.
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
 }
+
+__device__ __forceinline__ uint32_t umin3(uint32_t a, uint32_t b, uint32_t c) { return min(min(a, b), c); }
+
+// Wave-uniform values: keep them in scalar registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uni(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+// Non-negative float64 to fixed point, saturating.
+__device__ __forceinline__ uint32_t fix64(double x) {
+    return (uint32_t)fmin(x + 0.5, 4294967295.0);
+}
+
+// Non-negative float32 to fixed point, saturating (INF -> 0xFFFFFFFF).
+__device__ __forceinline__ uint32_t fix32(float x) { return (uint32_t)fminf(x, 4294967040.f); }
+
+// l0 + n q, saturating at 0xFFFFFFFF.
+__device__ __forceinline__ uint32_t last_plus_one(uint32_t l0, uint32_t n, uint32_t q) {
+    const unsigned long long t = (unsigned long long)n * q + l0;
+    return (t >> 32) ? 0xFFFFFFFFu : (uint32_t)t;
+}
+
+// ---------------------------------------------------------------------------
+// float64 ray set-up
+// ---------------------------------------------------------------------------
 
 // One axis of the slab clip in voxel coordinates: box [0, n) on this axis.
 __device__ __forceinline__ void clip_axis(double o, double d, double n, double &tin, double &tout,
@@ -93,130 +127,9 @@ __device__ __forceinline__ void axis_cells(double o, double d, double tin, doubl
     dist = d > 0.0 ? (double)(ce + 1) - e : (d < 0.0 ? e - (double)ce : 0.0);
 }
 
-// Walk state of one ray (T = float for the gathers, double where every single
-// piece length must be exact to float64 rounding).
-template <class T>
-struct Walk {
-    int idx;            // element index of the current cell
-    int stx, sty, stz;  // signed element strides
-    int ncross;         // plane crossings inside the interval (all axes)
-    T l0x, l0y, l0z;
-    T qx, qy, qz;
-    T lend;
-};
-
-__device__ __forceinline__ float t_fma(float a, float b, float c) { return fmaf(a, b, c); }
-__device__ __forceinline__ double t_fma(double a, double b, double c) { return fma(a, b, c); }
-__device__ __forceinline__ float t_min(float a, float b) { return fminf(a, b); }
-__device__ __forceinline__ double t_min(double a, double b) { return fmin(a, b); }
-template <class T> __device__ __forceinline__ T t_inf();
-template <> __device__ __forceinline__ float t_inf<float>() { return __builtin_huge_valf(); }
-template <> __device__ __forceinline__ double t_inf<double>() { return __builtin_huge_val(); }
-
-// Build the walk of the ray o + t d (voxel coordinates) through the box
-// [0,nx) x [0,ny) x [0,nz), t in [tmin, tmax]; element strides (1, sy, sz).
-// Returns false if the ray misses the box.  chord receives the physical length.
-template <class T>
-__device__ __forceinline__ bool make_walk(double ox, double oy, double oz, double dx, double dy,
-                                          double dz, double tmin, double tmax, int nx, int ny,
-                                          int nz, int sy, int sz, double spx, double spy,
-                                          double spz, Walk<T> &w, float &chord) {
-    // A component below 2^-40 of the largest moves the ray by less than 1e-12 of
-    // its length along that axis: treat the ray as parallel to those planes, which
-    // keeps every per-axis step length finite in float32.
-    {
-        const double dm = fmax(fabs(dx), fmax(fabs(dy), fabs(dz))) * 0x1p-40;
-        if (fabs(dx) < dm) dx = 0.0;
-        if (fabs(dy) < dm) dy = 0.0;
-        if (fabs(dz) < dm) dz = 0.0;
-    }
-    double tin = tmin, tout = tmax;
-    bool hit = true;
-    clip_axis(ox, dx, (double)nx, tin, tout, hit);
-    clip_axis(oy, dy, (double)ny, tin, tout, hit);
-    clip_axis(oz, dz, (double)nz, tin, tout, hit);
-    hit = hit && (tout > tin);
-    if (!hit) return false;
-    int cx, cy, cz, nxc, nyc, nzc;
-    double ddx, ddy, ddz;
-    axis_cells(ox, dx, tin, tout, nx, cx, nxc, ddx);
-    axis_cells(oy, dy, tin, tout, ny, cy, nyc, ddy);
-    axis_cells(oz, dz, tin, tout, nz, cz, nzc, ddz);
-    double px = dx * spx, py = dy * spy, pz = dz * spz;
-    double L = sqrt(px * px + py * py + pz * pz);
-    w.idx = (cz * ny + cy) * nx + cx;
-    w.ncross = nxc + nyc + nzc;
-    w.stx = dx > 0.0 ? 1 : -1;
-    w.sty = dy > 0.0 ? sy : -sy;
-    w.stz = dz > 0.0 ? sz : -sz;
-    const T ch = (T)((tout - tin) * L);
-    T lend = ch;
-    if (dx != 0.0) {
-        double q = L / fabs(dx);
-        w.qx = (T)q;
-        w.l0x = (T)(ddx * q);
-        lend = t_min(lend, t_fma((T)nxc, w.qx, w.l0x));
-    } else {
-        w.qx = (T)0;
-        w.l0x = t_inf<T>();
-    }
-    if (dy != 0.0) {
-        double q = L / fabs(dy);
-        w.qy = (T)q;
-        w.l0y = (T)(ddy * q);
-        lend = t_min(lend, t_fma((T)nyc, w.qy, w.l0y));
-    } else {
-        w.qy = (T)0;
-        w.l0y = t_inf<T>();
-    }
-    if (dz != 0.0) {
-        double q = L / fabs(dz);
-        w.qz = (T)q;
-        w.l0z = (T)(ddz * q);
-        lend = t_min(lend, t_fma((T)nzc, w.qz, w.l0z));
-    } else {
-        w.qz = (T)0;
-        w.l0z = t_inf<T>();
-    }
-    w.lend = lend;
-    chord = (float)ch;
-    return true;
-}
-
-// Visit every (cell, length) piece of the walk in order; f(idx, len).
-template <class T, class F>
-__device__ __forceinline__ void walk(const Walk<T> &w, F &&f) {
-    int idx = w.idx;
-    T lc = (T)0;
-    T mx = (T)0, my = (T)0, mz = (T)0;
-    T lx = w.l0x, ly = w.l0y, lz = w.l0z;
-    const T lend = w.lend;
-    for (;;) {
-        const T tmin = t_min(t_min(lx, ly), lz);
-        const T tn = t_min(tmin, lend);
-        f(idx, tn - lc);
-        if (!(tmin < lend)) break;  // also leaves on NaN
-        lc = tn;
-        if (lx == tmin) {
-            idx += w.stx;
-            mx += (T)1;
-            lx = t_fma(mx, w.qx, w.l0x);
-        }
-        if (ly == tmin) {
-            idx += w.sty;
-            my += (T)1;
-            ly = t_fma(my, w.qy, w.l0y);
-        }
-        if (lz == tmin) {
-            idx += w.stz;
-            mz += (T)1;
-            lz = t_fma(mz, w.qz, w.l0z);
-        }
-    }
-}
-
-// Ray set-up shared by the gathers: drop negligible direction components, clip
-// to the volume box in float64.  Returns false on a miss.
+// Drop direction components below 2^-40 of the largest (they move the ray by
+// less than 1e-12 of its length along that axis: the ray is then parallel to
+// those planes), and clip to the volume box.  Returns false on a miss.
 __device__ __forceinline__ bool clip_ray(double ox, double oy, double oz, double &dx, double &dy,
                                          double &dz, double tmin, double tmax, int nx, int ny,
                                          int nz, double &tin, double &tout) {
@@ -232,6 +145,135 @@ __device__ __forceinline__ bool clip_ray(double ox, double oy, double oz, double
     clip_axis(oz, dz, (double)nz, tin, tout, hit);
     return hit && (tout > tin);
 }
+
+// ---------------------------------------------------------------------------
+// float64 walk (atomic adjoint) -- same plan as the integer walk, in doubles
+// ---------------------------------------------------------------------------
+
+struct DWalk {
+    int idx;            // element index of the current cell
+    int stx, sty, stz;  // signed element strides
+    int ncross;         // plane crossings inside the interval (all axes)
+    double l0x, l0y, l0z, qx, qy, qz, lend;
+};
+
+__device__ __forceinline__ void daxis(double d, double L, int n, double dist, double &q,
+                                      double &l0, double &lend) {
+    if (d != 0.0) {
+        q = L / fabs(d);
+        l0 = dist * q;
+        lend = fmin(lend, fma((double)n, q, l0));
+    } else {
+        q = 0.0;
+        l0 = __builtin_huge_val();
+    }
+}
+
+__device__ __forceinline__ bool make_dwalk(double ox, double oy, double oz, double dx, double dy,
+                                           double dz, double tmin, double tmax, int nx, int ny,
+                                           int nz, double spx, double spy, double spz, DWalk &w,
+                                           double &chord) {
+    double tin, tout;
+    if (!clip_ray(ox, oy, oz, dx, dy, dz, tmin, tmax, nx, ny, nz, tin, tout)) return false;
+    int cx, cy, cz, nxc, nyc, nzc;
+    double ddx, ddy, ddz;
+    axis_cells(ox, dx, tin, tout, nx, cx, nxc, ddx);
+    axis_cells(oy, dy, tin, tout, ny, cy, nyc, ddy);
+    axis_cells(oz, dz, tin, tout, nz, cz, nzc, ddz);
+    const double px = dx * spx, py = dy * spy, pz = dz * spz;
+    const double L = sqrt(px * px + py * py + pz * pz);
+    w.idx = (cz * ny + cy) * nx + cx;
+    w.ncross = nxc + nyc + nzc;
+    w.stx = dx > 0.0 ? 1 : -1;
+    w.sty = dy > 0.0 ? nx : -nx;
+    w.stz = dz > 0.0 ? nx * ny : -nx * ny;
+    chord = (tout - tin) * L;
+    w.lend = chord;
+    daxis(dx, L, nxc, ddx, w.qx, w.l0x, w.lend);
+    daxis(dy, L, nyc, ddy, w.qy, w.l0y, w.lend);
+    daxis(dz, L, nzc, ddz, w.qz, w.l0z, w.lend);
+    return true;
+}
+
+template <class F>
+__device__ __forceinline__ void dwalk(const DWalk &w, F &&f) {
+    int idx = w.idx;
+    double lc = 0.0, mx = 0.0, my = 0.0, mz = 0.0;
+    double lx = w.l0x, ly = w.l0y, lz = w.l0z;
+    for (;;) {
+        const double tmin = fmin(fmin(lx, ly), lz);
+        const double tn = fmin(tmin, w.lend);
+        f(idx, tn - lc);
+        if (!(tmin < w.lend)) break;  // also leaves on NaN
+        lc = tn;
+        if (lx == tmin) { idx += w.stx; mx += 1.0; lx = fma(mx, w.qx, w.l0x); }
+        if (ly == tmin) { idx += w.sty; my += 1.0; ly = fma(my, w.qy, w.l0y); }
+        if (lz == tmin) { idx += w.stz; mz += 1.0; lz = fma(mz, w.qz, w.l0z); }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// integer walk
+// ---------------------------------------------------------------------------
+
+struct IWalk {
+    uint32_t idx;           // byte offset of the current cell
+    uint32_t stx, sty, stz; // byte strides (two's complement for negative steps)
+    uint32_t lx, ly, lz;    // next crossing per axis (0xFFFFFFFF: none)
+    uint32_t qx, qy, qz;    // crossing spacing per axis
+    uint32_t lend;          // end of the walk
+};
+
+// One step of the gather walk: advance past the current piece, returning its
+// length and the byte offset of the next cell.
+struct GStep {
+    uint32_t seg;
+    bool last;
+};
+__device__ __forceinline__ GStep gstep(const IWalk &w, uint32_t &idx, uint32_t &lc, uint32_t &lx,
+                                       uint32_t &ly, uint32_t &lz) {
+    const uint32_t tmin = umin3(lx, ly, lz);
+    const uint32_t tn = min(tmin, w.lend);
+    const bool bx = lx == tmin, by = ly == tmin, bz = lz == tmin;
+    lx = __builtin_elementwise_add_sat(lx, bx ? w.qx : 0u);
+    ly = __builtin_elementwise_add_sat(ly, by ? w.qy : 0u);
+    lz = __builtin_elementwise_add_sat(lz, bz ? w.qz : 0u);
+    idx += (bx ? w.stx : 0u) + (by ? w.sty : 0u) + (bz ? w.stz : 0u);
+    GStep g{tn - lc, tmin >= w.lend};
+    lc = tn;
+    return g;
+}
+
+// Sum of length * value over the walk, in walk units.  The cell offsets do not
+// depend on the loaded values, so the load of the next cell is issued before the
+// current product is formed; the loop is unrolled by two so the two value
+// registers swap roles without a copy (a copy would wait for the newer load).
+// The load after the last piece may fall outside the volume; the buffer
+// resource returns 0 there and the value is unused.
+__device__ __forceinline__ float iwalk_gather(const IWalk &w, __amdgpu_buffer_rsrc_t rs) {
+    uint32_t idx = w.idx;
+    uint32_t lc = 0, lx = w.lx, ly = w.ly, lz = w.lz;
+    float acc = 0.f;
+    float va = load_f32(rs, idx);
+    for (;;) {
+        const GStep s0 = gstep(w, idx, lc, lx, ly, lz);
+        const float vb = load_f32(rs, idx);
+        acc = fmaf((float)s0.seg, va, acc);
+        if (s0.last) break;
+        const GStep s1 = gstep(w, idx, lc, lx, ly, lz);
+        va = load_f32(rs, idx);
+        acc = fmaf((float)s1.seg, vb, acc);
+        if (s1.last) break;
+    }
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+// forward: float64 set-up, integer walk re-based per chunk
+// ---------------------------------------------------------------------------
+
+// Cells of the major axis covered by one chunk of the walk.
+constexpr int kChunk = 64;
 
 // Cells of one axis for a chunk of the ray.  On the major axis the chunk's first
 // cell and cell count are known exactly; a chunk after the first starts on a
@@ -253,18 +295,25 @@ __device__ __forceinline__ void chunk_axis(double o, double d, double ta, double
     }
 }
 
-// Cells of the major axis covered by one chunk of the float32 walk.  Positions
-// inside a chunk stay below 64 * sqrt(3) cell lengths, where float32 resolves
-// better than 1e-5 of a cell.
-constexpr int kChunk = 64;
+__device__ __forceinline__ void fix_axis(double d, double L, double S, int ncr, double dist,
+                                         uint32_t &l0, uint32_t &q, uint32_t &lend) {
+    if (d != 0.0) {
+        const double qS = (L / fabs(d)) * S;
+        q = fix64(qS);
+        l0 = fix64(dist * qS);
+        lend = min(lend, last_plus_one(l0, (uint32_t)ncr, q));
+    } else {
+        q = 0u;
+        l0 = 0xFFFFFFFFu;
+    }
+}
 
-// Visit the pieces of the ray o + t d, t in [tin, tout] (inside the box), with
-// the float32 walk re-based at every kChunk cells of the major axis.
-template <class F>
-__device__ __forceinline__ void walk_chunked(double ox, double oy, double oz, double dx, double dy,
+// Line integral of the ray o + t d, t in [tin, tout] (inside the box), with the
+// walk re-based every kChunk cells of the major axis.
+__device__ __forceinline__ float project_ray(double ox, double oy, double oz, double dx, double dy,
                                              double dz, double tin, double tout, int nx, int ny,
-                                             int nz, int sy, int sz, double spx, double spy,
-                                             double spz, F &&f) {
+                                             int nz, double spx, double spy, double spz,
+                                             __amdgpu_buffer_rsrc_t rs) {
     const double px = dx * spx, py = dy * spy, pz = dz * spz;
     const double L = sqrt(px * px + py * py + pz * pz);
     const double ax = fabs(dx), ay = fabs(dy), az = fabs(dz);
@@ -280,9 +329,8 @@ __device__ __forceinline__ void walk_chunked(double ox, double oy, double oz, do
     cout = min(max(cout, 0), nM - 1);
     const int ncell = max((cout - cin) * sgn, 0) + 1;
     const int nch = (ncell + kChunk - 1) / kChunk;
-    const float qx = dx != 0.0 ? (float)(L / ax) : 0.f;
-    const float qy = dy != 0.0 ? (float)(L / ay) : 0.f;
-    const float qz = dz != 0.0 ? (float)(L / az) : 0.f;
+    const uint32_t sy = (uint32_t)nx * 4u, sz = (uint32_t)nx * (uint32_t)ny * 4u;
+    float total = 0.f;
     double ta = tin;
     for (int ch = 0; ch < nch; ++ch) {
         const int first = cin + sgn * ch * kChunk;
@@ -297,26 +345,21 @@ __device__ __forceinline__ void walk_chunked(double ox, double oy, double oz, do
         chunk_axis(ox, dx, ta, tb, nx, M == 0, first, cells, ch == 0, cx, nxc, ddx);
         chunk_axis(oy, dy, ta, tb, ny, M == 1, first, cells, ch == 0, cy, nyc, ddy);
         chunk_axis(oz, dz, ta, tb, nz, M == 2, first, cells, ch == 0, cz, nzc, ddz);
-        Walk<float> w;
-        w.idx = (cz * ny + cy) * nx + cx;
-        w.ncross = nxc + nyc + nzc;
-        w.stx = dx > 0.0 ? 1 : -1;
-        w.sty = dy > 0.0 ? sy : -sy;
-        w.stz = dz > 0.0 ? sz : -sz;
-        float lend = (float)((tb - ta) * L);
-        w.qx = qx;
-        w.qy = qy;
-        w.qz = qz;
-        w.l0x = dx != 0.0 ? (float)(ddx * (L / ax)) : CT_INF;
-        w.l0y = dy != 0.0 ? (float)(ddy * (L / ay)) : CT_INF;
-        w.l0z = dz != 0.0 ? (float)(ddz * (L / az)) : CT_INF;
-        if (dx != 0.0) lend = fminf(lend, fmaf((float)nxc, qx, w.l0x));
-        if (dy != 0.0) lend = fminf(lend, fmaf((float)nyc, qy, w.l0y));
-        if (dz != 0.0) lend = fminf(lend, fmaf((float)nzc, qz, w.l0z));
-        w.lend = lend;
-        walk(w, f);
+        const double chord = (tb - ta) * L;
+        const double S = 0x1p30 / chord;   // walk units per length unit
+        IWalk w;
+        w.idx = (((uint32_t)cz * (uint32_t)ny + (uint32_t)cy) * (uint32_t)nx + (uint32_t)cx) * 4u;
+        w.stx = dx > 0.0 ? 4u : (uint32_t)-4;
+        w.sty = dy > 0.0 ? sy : 0u - sy;
+        w.stz = dz > 0.0 ? sz : 0u - sz;
+        w.lend = 1u << 30;
+        fix_axis(dx, L, S, nxc, ddx, w.lx, w.qx, w.lend);
+        fix_axis(dy, L, S, nyc, ddy, w.ly, w.qy, w.lend);
+        fix_axis(dz, L, S, nzc, ddz, w.lz, w.qz, w.lend);
+        total = fmaf(iwalk_gather(w, rs), (float)(chord * 0x1p-30), total);
         ta = tb;
     }
+    return total;
 }
 
 // ---------------------------------------------------------------------------
@@ -335,15 +378,17 @@ struct RayArgs {
     unsigned long long *total; // RM_COUNT
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
+    int lg_tv;                 // wave patch: (64 >> lg_tv) u  x  (1 << lg_tv) v
     int n_utiles, n_vtiles, n_blocks;
     uint32_t vol_bytes;
 };
 
-// Tiles: 3D 16(u) x 16(v) per 256-thread block, each wave an 8 x 8 patch, so
-// the 64 rays of a wave form a tight bundle that touches few cache lines per
-// step.  2D: 256 consecutive u per block.  Block order: v-band outermost, then
-// view, then u tile, so all views of one detector band (one slab of the volume
-// for cone/parallel3d orbits) run together while that slab is cache-resident.
+// Tiles: each wave takes a patch of 64 neighbouring pixels, so its rays form a
+// tight bundle that touches few cache lines per step; a 256-thread block is a
+// 2 x 2 arrangement of patches.  2D: 256 consecutive u per block.  Block order:
+// v-band outermost, then view, then u tile, so all views of one detector band
+// (one slab of the volume for cone/parallel3d orbits) run close together while
+// that slab is cache-resident.
 template <int MODE, bool TWO_D>
 __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
     const int blk = xcd_remap(blockIdx.x, a.n_blocks);
@@ -357,8 +402,9 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
         u = ut * 256 + threadIdx.x;
         v = 0;
     } else {
-        u = ut * 16 + (wv & 1) * 8 + (lane >> 3);
-        v = band * 16 + (wv >> 1) * 8 + (lane & 7);
+        const int tv = 1 << a.lg_tv, tu = 64 >> a.lg_tv;
+        u = ut * 2 * tu + (wv & 1) * tu + (lane >> a.lg_tv);
+        v = band * 2 * tv + (wv >> 1) * tv + (lane & (tv - 1));
     }
     const bool active = (u < a.U) && (v < a.V);
     uint32_t my_count = 0;
@@ -372,44 +418,43 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
         double dy = vw[VT_D00 + 1] + fu * vw[VT_DU + 1] + fv * vw[VT_DV + 1];
         double dz = vw[VT_D00 + 2] + fu * vw[VT_DU + 2] + fv * vw[VT_DV + 2];
         const size_t ray = ((size_t)view * a.U + u) * a.V + v;
-        using WT = typename std::conditional<MODE == RM_ATOMIC_BP, double, float>::type;
-        Walk<WT> w;
-        float chord = 0.f;
-        bool hit = false;
-        if (MODE != RM_PROJECT && MODE != RM_RESIDUAL)
-            hit = make_walk<WT>(ox, oy, oz, dx, dy, dz, vw[VT_TMIN], vw[VT_TMAX], a.W, a.H, a.D, a.W,
-                                a.W * a.H, a.spx, a.spy, a.spz, w, chord);
         if (MODE == RM_PROJECT || MODE == RM_RESIDUAL) {
             float acc = 0.f;
             double tin, tout;
             if (clip_ray(ox, oy, oz, dx, dy, dz, vw[VT_TMIN], vw[VT_TMAX], a.W, a.H, a.D, tin, tout)) {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.vol, a.vol_bytes);
-                walk_chunked(ox, oy, oz, dx, dy, dz, tin, tout, a.W, a.H, a.D, a.W, a.W * a.H, a.spx,
-                             a.spy, a.spz,
-                             [&](int idx, float len) { acc = fmaf(len, load_f32(rs, idx * 4), acc); });
+                acc = project_ray(ox, oy, oz, dx, dy, dz, tin, tout, a.W, a.H, a.D, a.spx, a.spy,
+                                  a.spz, rs);
             }
             if (MODE == RM_PROJECT) {
                 a.out[ray] = acc;
             } else {
                 a.out[ray] = a.rinv[ray] * (a.sino[ray] - acc);
             }
-        } else if (MODE == RM_ROWINV) {
-            // (A 1)_i is the ray's chord through the whole volume
-            float r = (hit && chord > 0.f) ? 1.0f / chord : 0.f;
-            a.out[ray] = isfinite(r) ? r : 0.f;
-        } else if (MODE == RM_COUNT) {
-            // cells visited = plane crossings + 1, from the float64 entry and exit
-            // cells (each crossing starts a new cell; exact ties would add empty ones)
-            const uint32_t c = hit ? (uint32_t)(w.ncross + 1) : 0u;
-            if (a.counts) a.counts[ray] = c;
-            my_count = c;
-        } else if (MODE == RM_ATOMIC_BP) {
-            const float y = a.sino[ray];
-            if (hit && y != 0.f) {
-                float *vol = a.out;
-                walk(w, [&](int idx, WT len) {
-                    if (len > (WT)0) atomicAdd(vol + idx, (float)len * y);
-                });
+        } else {
+            DWalk w;
+            double chord = 0.0;
+            const bool hit = make_dwalk(ox, oy, oz, dx, dy, dz, vw[VT_TMIN], vw[VT_TMAX], a.W, a.H,
+                                        a.D, a.spx, a.spy, a.spz, w, chord);
+            if (MODE == RM_ROWINV) {
+                // (A 1)_i is the ray's chord through the whole volume
+                const float ch = (float)chord;
+                const float r = (hit && ch > 0.f) ? 1.0f / ch : 0.f;
+                a.out[ray] = isfinite(r) ? r : 0.f;
+            } else if (MODE == RM_COUNT) {
+                // cells visited = plane crossings + 1, from the float64 entry and exit
+                // cells (each crossing starts a new cell; exact ties would add empty ones)
+                const uint32_t c = hit ? (uint32_t)(w.ncross + 1) : 0u;
+                if (a.counts) a.counts[ray] = c;
+                my_count = c;
+            } else if (MODE == RM_ATOMIC_BP) {
+                const float y = a.sino[ray];
+                if (hit && y != 0.f) {
+                    float *vol = a.out;
+                    dwalk(w, [&](int idx, double len) {
+                        if (len > 0.0) atomicAdd(vol + idx, (float)len * y);
+                    });
+                }
             }
         }
     }
@@ -437,7 +482,8 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
 // (u, v)'s ray meets that plane is affine in (u, v), so it is formed in float32
 // from a float64 anchor at the footprint's first pixel plus small integer offsets;
 // positions inside the walk then stay within tens of voxels of the brick and keep
-// float32 resolution near 1e-6 voxel.
+// float32 resolution near 1e-6 voxel.  Negative directions are mirrored so every
+// axis is walked upwards in the set-up arithmetic.
 
 enum BrickMode : int { BM_BACKPROJECT = 0, BM_SIRT_UPDATE = 1, BM_COLINV = 2 };
 
@@ -452,15 +498,126 @@ struct BrickArgs {
     int nbx, nby, nbz, n_blocks;
 };
 
+// Clip one (mirrored, non-negative) axis: o' in brick coordinates, a = |d|,
+// inv = 1/a (INF for a = 0), extent e.  A ray with a = 0 is inside iff 0 <= o' < e.
+__device__ __forceinline__ void bclip(float o, float a, float inv, float e, float &lo, float &hi) {
+    if (a > 0.f) {
+        lo = -o * inv;
+        hi = (e - o) * inv;
+    } else {
+        const bool in = (o >= 0.f) && (o < e);
+        lo = in ? -3e38f : 3e38f;
+        hi = -lo;
+    }
+}
+
+// Entry cell, crossing count and fixed-point crossing plan of one mirrored axis.
+__device__ __forceinline__ void baxis(float o, float a, float inv, float tin, float tout, int e,
+                                      float LS, int &ce, uint32_t &ncr, uint32_t &l0, uint32_t &q) {
+    const float E = fmaf(tin, a, o), X = fmaf(tout, a, o);
+    ce = min(max((int)floorf(E), 0), e - 1);
+    const int cx = min(max((int)ceilf(X) - 1, 0), e - 1);
+    ncr = (uint32_t)max(cx - ce, 0);
+    const float qf = LS * inv;                 // walk units per cell along this axis
+    q = fix32(qf);
+    l0 = fix32(((float)(ce + 1) - E) * qf);
+}
+
+// Footprint of the brick [x0, x0+ex) x [y0, y0+ey) x [z0, z0+ez) on the detector of
+// one view: the bounding box of its 8 projected corners (lane & 7 projects corner
+// lane & 7; lanes reduce in groups of 8).  Returns false if no pixel can see it.
+struct Footprint {
+    int u0, u1, v0, v1;
+};
+__device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int x0, int y0, int z0,
+                                                int ex, int ey, int ez, int U, int V, bool two_d,
+                                                Footprint &f) {
+    const int c = lane & 7;
+    const double X = (c & 1) ? x0 + ex : x0;
+    const double Y = (c & 2) ? y0 + ey : y0;
+    const double Z = (c & 4) ? z0 + ez : z0;
+    const double rx = X - vw[VT_O00 + 0], ry = Y - vw[VT_O00 + 1], rz = Z - vw[VT_O00 + 2];
+    const double al = vw[VT_MINV + 0] * rx + vw[VT_MINV + 1] * ry + vw[VT_MINV + 2] * rz;
+    const double be = vw[VT_MINV + 3] * rx + vw[VT_MINV + 4] * ry + vw[VT_MINV + 5] * rz;
+    const double ga = vw[VT_MINV + 6] * rx + vw[VT_MINV + 7] * ry + vw[VT_MINV + 8] * rz;
+    const bool persp = vw[VT_PERSP] != 0.0;
+    float cu, cvv;
+    int bad = 0;
+    if (persp) {
+        // a corner at or behind the source: every pixel may see the brick
+        bad = !(al > 1e-9);
+        cu = bad ? 0.f : (float)(be / al);
+        cvv = bad ? 0.f : (float)(ga / al);
+    } else {
+        cu = (float)be;
+        cvv = (float)ga;
+    }
+    float umin = cu, umax = cu, vmin = cvv, vmax = cvv;
+    for (int off = 1; off < 8; off <<= 1) {
+        umin = fminf(umin, __shfl_xor(umin, off));
+        umax = fmaxf(umax, __shfl_xor(umax, off));
+        vmin = fminf(vmin, __shfl_xor(vmin, off));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+        bad |= __shfl_xor(bad, off);
+    }
+    umin = uni(umin); umax = uni(umax); vmin = uni(vmin); vmax = uni(vmax);
+    bad = uni(bad);
+    if (bad) {
+        f.u0 = 0; f.u1 = U - 1; f.v0 = 0; f.v1 = V - 1;
+    } else {
+        // guard the float conversions against far-away projections
+        umin = fmaxf(umin, -1.f); umax = fminf(umax, (float)U);
+        vmin = fmaxf(vmin, -1.f); vmax = fminf(vmax, (float)V);
+        f.u0 = max(0, (int)ceilf(umin - 1e-3f));
+        f.u1 = min(U - 1, (int)floorf(umax + 1e-3f));
+        f.v0 = max(0, (int)ceilf(vmin - 1e-3f));
+        f.v1 = min(V - 1, (int)floorf(vmax + 1e-3f));
+    }
+    if (two_d) { f.v0 = 0; f.v1 = 0; }
+    return f.u0 <= f.u1 && f.v0 <= f.v1;
+}
+
+// Footprint ray r (v fastest) -> offsets (iu, iv) from the footprint's corner.
+__device__ __forceinline__ void decode_ray(int r, int nfv, float inv_nfv, int &iu, int &iv) {
+    iu = (int)(((float)r + 0.5f) * inv_nfv);
+    iv = r - iu * nfv;
+    if (iv < 0) { iu -= 1; iv += nfv; } else if (iv >= nfv) { iu += 1; iv -= nfv; }
+}
+
+// LDS scatter into 64-bit fixed point: lds[cell] += round(length * ys) for every
+// piece, ys being the value per walk unit already multiplied by the brick's
+// fixed-point scale (so each term stays below 2^30 in magnitude).  Float
+// atomic adds in LDS run some 30x slower than integer ones on this chip, hence the
+// integer accumulator.
+__device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long long *lds, float ys) {
+    uint32_t idx = w.idx;
+    uint32_t lc = 0, lx = w.lx, ly = w.ly, lz = w.lz;
+    const uint32_t lend = w.lend;
+    for (;;) {
+        const uint32_t tmin = umin3(lx, ly, lz);
+        const uint32_t tn = min(tmin, lend);
+        const int t = (int)__builtin_rintf((float)(tn - lc) * ys);
+        const unsigned long long v = (unsigned long long)(long long)t;
+        atomicAdd((unsigned long long *)((char *)lds + idx), v);
+        if (tmin >= lend) break;
+        lc = tn;
+        const bool bx = lx == tmin, by = ly == tmin, bz = lz == tmin;
+        lx = __builtin_elementwise_add_sat(lx, bx ? w.qx : 0u);
+        ly = __builtin_elementwise_add_sat(ly, by ? w.qy : 0u);
+        lz = __builtin_elementwise_add_sat(lz, bz ? w.qz : 0u);
+        idx += (bx ? w.stx : 0u) + (by ? w.sty : 0u) + (bz ? w.stz : 0u);
+    }
+}
+
 template <int BX, int BY, int BZ, int NT, int MODE>
 __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
-    constexpr int LSY = BX + 1;           // padded LDS strides: rays of a wave that
-    constexpr int LSZ = LSY * BY + 1;     // differ only in y or z hit different banks
-    constexpr int LN = LSZ * BZ;
+    constexpr int LSY = BX + 1;           // padded LDS strides (elements): rays of a
+    constexpr int LSZ = LSY * BY + 1;     // wave that differ only in y or z hit
+    constexpr int LN = LSZ * BZ;          // different banks
     constexpr int NWAVES = NT / 64;
-    __shared__ float acc[LN];
-    for (int i = threadIdx.x; i < LN; i += NT) acc[i] = 0.f;
-    __syncthreads();
+    __shared__ unsigned long long acc[LN];
+    __shared__ float wave_max[NWAVES];
+    for (int i = threadIdx.x; i < LN; i += NT) acc[i] = 0ull;
 
     const int blk = xcd_remap(blockIdx.x, a.n_blocks);
     const int bxi = blk % a.nbx;
@@ -469,61 +626,55 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
     const int x0 = bxi * BX, y0 = byi * BY, z0 = bzi * BZ;
     const int ex = min(BX, a.W - x0), ey = min(BY, a.H - y0), ez = min(BZ, a.D - z0);
     const double cbx = x0 + 0.5 * ex, cby = y0 + 0.5 * ey, cbz = z0 + 0.5 * ez;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = uni((int)(threadIdx.x >> 6));
     const bool two_d = (a.D == 1 && a.V == 1);
+    const float fex = (float)ex, fey = (float)ey, fez = (float)ez;
+    const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
 
+    // ---- pass 1: largest |y| over the rays that can meet this brick ----
+    float ymax = 1.f;
+    if (MODE != BM_COLINV) {
+        float m = 0.f;
+        for (int view = wv; view < a.n_views; view += NWAVES) {
+            const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
+            Footprint f;
+            if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d, f)) continue;
+            const int nfv = f.v1 - f.v0 + 1, nrays = (f.u1 - f.u0 + 1) * nfv;
+            const float inv_nfv = 1.0f / (float)nfv;
+            const float *ysrc = a.sino + ((size_t)view * a.U + f.u0) * a.V + f.v0;
+            for (int r = lane; r < nrays; r += 64) {
+                int iu, iv;
+                decode_ray(r, nfv, inv_nfv, iu, iv);
+                m = fmaxf(m, fabsf(ysrc[(size_t)iu * a.V + iv]));
+            }
+        }
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (lane == 0) wave_max[wv] = m;
+        __syncthreads();
+        ymax = 0.f;
+        for (int k = 0; k < NWAVES; ++k) ymax = fmaxf(ymax, wave_max[k]);
+    } else {
+        __syncthreads();
+    }
+    // Fixed-point scale: one piece is at most a voxel diagonal long, so every
+    // term length * |y| * scale stays below 2^30.
+    const float diag = sqrtf(spx * spx + spy * spy + spz * spz);
+    const float bound = diag * ymax;
+    const float scale = bound > 0.f ? ldexpf(1.f, (int)floorf(30.f - log2f(bound))) : 1.f;
+
+    // ---- pass 2: walk every footprint ray through the brick ----
     for (int view = wv; view < a.n_views; view += NWAVES) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
-        // ---- footprint: project corner (lane & 7) of the brick ----
-        const int c = lane & 7;
-        const double X = (c & 1) ? x0 + ex : x0;
-        const double Y = (c & 2) ? y0 + ey : y0;
-        const double Z = (c & 4) ? z0 + ez : z0;
-        const double rx = X - vw[VT_O00 + 0], ry = Y - vw[VT_O00 + 1], rz = Z - vw[VT_O00 + 2];
-        const double al = vw[VT_MINV + 0] * rx + vw[VT_MINV + 1] * ry + vw[VT_MINV + 2] * rz;
-        const double be = vw[VT_MINV + 3] * rx + vw[VT_MINV + 4] * ry + vw[VT_MINV + 5] * rz;
-        const double ga = vw[VT_MINV + 6] * rx + vw[VT_MINV + 7] * ry + vw[VT_MINV + 8] * rz;
-        const bool persp = vw[VT_PERSP] != 0.0;
-        float cu, cvv;
-        int bad = 0;
-        if (persp) {
-            bad = !(al > 1e-9);
-            cu = bad ? 0.f : (float)(be / al);
-            cvv = bad ? 0.f : (float)(ga / al);
-        } else {
-            cu = (float)be;
-            cvv = (float)ga;
-        }
-        float umin = cu, umax = cu, vmin = cvv, vmax = cvv;
-        for (int off = 1; off < 8; off <<= 1) {
-            umin = fminf(umin, __shfl_xor(umin, off));
-            umax = fmaxf(umax, __shfl_xor(umax, off));
-            vmin = fminf(vmin, __shfl_xor(vmin, off));
-            vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-            bad |= __shfl_xor(bad, off);
-        }
-        int u0, u1, v0, v1;
-        if (bad) {
-            u0 = 0; u1 = a.U - 1; v0 = 0; v1 = a.V - 1;
-        } else {
-            // guard the float conversions against far-away projections
-            umin = fmaxf(umin, -1.f); umax = fminf(umax, (float)a.U);
-            vmin = fmaxf(vmin, -1.f); vmax = fminf(vmax, (float)a.V);
-            u0 = max(0, (int)ceilf(umin - 1e-3f));
-            u1 = min(a.U - 1, (int)floorf(umax + 1e-3f));
-            v0 = max(0, (int)ceilf(vmin - 1e-3f));
-            v1 = min(a.V - 1, (int)floorf(vmax + 1e-3f));
-        }
-        if (two_d) { v0 = 0; v1 = 0; }
-        if (u0 > u1 || v0 > v1) continue;
-        const int nfu = u1 - u0 + 1, nfv = v1 - v0 + 1;
-        const int nrays = nfu * nfv;
+        Footprint f;
+        if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d, f)) continue;
+        const int u0 = f.u0, v0 = f.v0;
+        const int nfv = f.v1 - f.v0 + 1;
+        const int nrays = (f.u1 - f.u0 + 1) * nfv;
         const float inv_nfv = 1.0f / (float)nfv;
 
         // ---- per (view, brick) ray parametrisation, anchored at (u0, v0) ----
         const double nx_ = vw[VT_N + 0], ny_ = vw[VT_N + 1], nz_ = vw[VT_N + 2];
         const double fu0 = u0, fv0 = v0;
-        // origin and direction of the anchor pixel's ray
         const double aox = vw[VT_O00 + 0] + fu0 * vw[VT_OU + 0] + fv0 * vw[VT_OV + 0];
         const double aoy = vw[VT_O00 + 1] + fu0 * vw[VT_OU + 1] + fv0 * vw[VT_OV + 1];
         const double aoz = vw[VT_O00 + 2] + fu0 * vw[VT_OU + 2] + fv0 * vw[VT_OV + 2];
@@ -533,34 +684,40 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
         // Dir . N is the same for every pixel of a flat detector
         const double tb = ((cbx - aox) * nx_ + (cby - aoy) * ny_ + (cbz - aoz) * nz_) /
                           (adx * nx_ + ady * ny_ + adz * nz_);
-        const float A0x = (float)(aox + tb * adx - x0);
-        const float A0y = (float)(aoy + tb * ady - y0);
-        const float A0z = (float)(aoz + tb * adz - z0);
-        const float Aux = (float)(vw[VT_OU + 0] + tb * vw[VT_DU + 0]);
-        const float Auy = (float)(vw[VT_OU + 1] + tb * vw[VT_DU + 1]);
-        const float Auz = (float)(vw[VT_OU + 2] + tb * vw[VT_DU + 2]);
-        const float Avx = (float)(vw[VT_OV + 0] + tb * vw[VT_DV + 0]);
-        const float Avy = (float)(vw[VT_OV + 1] + tb * vw[VT_DV + 1]);
-        const float Avz = (float)(vw[VT_OV + 2] + tb * vw[VT_DV + 2]);
-        const float Dx = (float)adx, Dy = (float)ady, Dz = (float)adz;
-        const float DUx = (float)vw[VT_DU + 0], DUy = (float)vw[VT_DU + 1], DUz = (float)vw[VT_DU + 2];
-        const float DVx = (float)vw[VT_DV + 0], DVy = (float)vw[VT_DV + 1], DVz = (float)vw[VT_DV + 2];
-        const float t0 = (float)(vw[VT_TMIN] - tb), t1 = (float)(vw[VT_TMAX] - tb);
-        const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
-        const float fex = (float)ex, fey = (float)ey, fez = (float)ez;
+        const float A0x = uni((float)(aox + tb * adx - x0));
+        const float A0y = uni((float)(aoy + tb * ady - y0));
+        const float A0z = uni((float)(aoz + tb * adz - z0));
+        const float Aux = uni((float)(vw[VT_OU + 0] + tb * vw[VT_DU + 0]));
+        const float Auy = uni((float)(vw[VT_OU + 1] + tb * vw[VT_DU + 1]));
+        const float Auz = uni((float)(vw[VT_OU + 2] + tb * vw[VT_DU + 2]));
+        const float Avx = uni((float)(vw[VT_OV + 0] + tb * vw[VT_DV + 0]));
+        const float Avy = uni((float)(vw[VT_OV + 1] + tb * vw[VT_DV + 1]));
+        const float Avz = uni((float)(vw[VT_OV + 2] + tb * vw[VT_DV + 2]));
+        const float Dx = uni((float)adx), Dy = uni((float)ady), Dz = uni((float)adz);
+        const float DUx = uni((float)vw[VT_DU + 0]), DUy = uni((float)vw[VT_DU + 1]);
+        const float DUz = uni((float)vw[VT_DU + 2]);
+        const float DVx = uni((float)vw[VT_DV + 0]), DVy = uni((float)vw[VT_DV + 1]);
+        const float DVz = uni((float)vw[VT_DV + 2]);
+        const float t0 = uni((float)(vw[VT_TMIN] - tb)), t1 = uni((float)(vw[VT_TMAX] - tb));
         const float *ysrc = a.sino + ((size_t)view * a.U + u0) * a.V + v0;
 
+        // the sinogram value of the lane's next ray is loaded one ray ahead
+        float ynext = 1.f;
+        if (MODE != BM_COLINV && lane < nrays) {
+            int iu, iv;
+            decode_ray(lane, nfv, inv_nfv, iu, iv);
+            ynext = ysrc[(size_t)iu * a.V + iv];
+        }
         for (int r = lane; r < nrays; r += 64) {
-            int iu = (int)(((float)r + 0.5f) * inv_nfv);
-            int iv = r - iu * nfv;
-            if (iv < 0) { iu -= 1; iv += nfv; } else if (iv >= nfv) { iu += 1; iv -= nfv; }
-            float yv;
-            if (MODE == BM_COLINV) {
-                yv = 1.f;
-            } else {
-                yv = ysrc[(size_t)iu * a.V + iv];
-                if (yv == 0.f) continue;
+            const float yv = ynext;
+            if (MODE != BM_COLINV && r + 64 < nrays) {
+                int iu, iv;
+                decode_ray(r + 64, nfv, inv_nfv, iu, iv);
+                ynext = ysrc[(size_t)iu * a.V + iv];
             }
+            if (yv == 0.f) continue;
+            int iu, iv;
+            decode_ray(r, nfv, inv_nfv, iu, iv);
             const float fu = (float)iu, fv = (float)iv;
             const float ox = fmaf(fv, Avx, fmaf(fu, Aux, A0x));
             const float oy = fmaf(fv, Avy, fmaf(fu, Auy, A0y));
@@ -574,85 +731,54 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
                 if (fabsf(dy) < dm) dy = 0.f;
                 if (fabsf(dz) < dm) dz = 0.f;
             }
-            // clip to the brick [0,ex) x [0,ey) x [0,ez) and to [t0, t1]
-            float tin = t0, tout = t1;
-            bool hit = true;
-            float ix_ = 0.f, iy_ = 0.f, iz_ = 0.f;
-            if (dx != 0.f) {
-                ix_ = 1.0f / dx;
-                float a0 = -ox * ix_, a1 = (fex - ox) * ix_;
-                tin = fmaxf(tin, fminf(a0, a1));
-                tout = fminf(tout, fmaxf(a0, a1));
-            } else {
-                hit = hit && ox >= 0.f && ox < fex;
-            }
-            if (dy != 0.f) {
-                iy_ = 1.0f / dy;
-                float a0 = -oy * iy_, a1 = (fey - oy) * iy_;
-                tin = fmaxf(tin, fminf(a0, a1));
-                tout = fminf(tout, fmaxf(a0, a1));
-            } else {
-                hit = hit && oy >= 0.f && oy < fey;
-            }
-            if (dz != 0.f) {
-                iz_ = 1.0f / dz;
-                float a0 = -oz * iz_, a1 = (fez - oz) * iz_;
-                tin = fmaxf(tin, fminf(a0, a1));
-                tout = fminf(tout, fmaxf(a0, a1));
-            } else {
-                hit = hit && oz >= 0.f && oz < fez;
-            }
-            if (!(hit && tout > tin)) continue;
-            // entry / exit cells and crossing counts per axis
+            // mirror negative directions: walk every axis upwards
+            const float mx = dx < 0.f ? fex - ox : ox, axx = fabsf(dx);
+            const float my = dy < 0.f ? fey - oy : oy, ayy = fabsf(dy);
+            const float mz = dz < 0.f ? fez - oz : oz, azz = fabsf(dz);
+            const float ix = __builtin_amdgcn_rcpf(axx);
+            const float iy = __builtin_amdgcn_rcpf(ayy);
+            const float iz = __builtin_amdgcn_rcpf(azz);
+            float lox, hix, loy, hiy, loz, hiz;
+            bclip(mx, axx, ix, fex, lox, hix);
+            bclip(my, ayy, iy, fey, loy, hiy);
+            bclip(mz, azz, iz, fez, loz, hiz);
+            const float tin = fmaxf(fmaxf(fmaxf(lox, loy), loz), t0);
+            const float tout = fminf(fminf(fminf(hix, hiy), hiz), t1);
+            if (!(tin < tout)) continue;
             const float px = dx * spx, py = dy * spy, pz = dz * spz;
-            const float L = sqrtf(px * px + py * py + pz * pz);
-            int cx, cy, cz, nxc, nyc, nzc;
-            float l0x, l0y, l0z, qx, qy, qz;
-            float lend = (tout - tin) * L;
-            auto axis = [&](float o, float d, float inv, int n, int &c0, int &ncr, float &l0,
-                            float &q) {
-                const float e = fmaf(tin, d, o), xx = fmaf(tout, d, o);
-                int ce, ce2;
-                if (d > 0.f) { ce = (int)floorf(e); ce2 = (int)ceilf(xx) - 1; }
-                else if (d < 0.f) { ce = (int)ceilf(e) - 1; ce2 = (int)floorf(xx); }
-                else { ce = (int)floorf(e); ce2 = ce; }
-                ce = min(max(ce, 0), n - 1);
-                ce2 = min(max(ce2, 0), n - 1);
-                c0 = ce;
-                if (d != 0.f) {
-                    ncr = d > 0.f ? max(ce2 - ce, 0) : max(ce - ce2, 0);
-                    q = L * fabsf(inv);
-                    const float dist = d > 0.f ? (float)(ce + 1) - e : e - (float)ce;
-                    l0 = dist * q;
-                    lend = fminf(lend, fmaf((float)ncr, q, l0));
-                } else {
-                    ncr = 0;
-                    q = 0.f;
-                    l0 = CT_INF;
-                }
-            };
-            axis(ox, dx, ix_, ex, cx, nxc, l0x, qx);
-            axis(oy, dy, iy_, ey, cy, nyc, l0y, qy);
-            axis(oz, dz, iz_, ez, cz, nzc, l0z, qz);
-            Walk<float> w;
-            w.idx = cz * LSZ + cy * LSY + cx;
-            w.stx = dx > 0.f ? 1 : -1;
-            w.sty = dy > 0.f ? LSY : -LSY;
-            w.stz = dz > 0.f ? LSZ : -LSZ;
-            w.l0x = l0x; w.l0y = l0y; w.l0z = l0z;
-            w.qx = qx; w.qy = qy; w.qz = qz;
+            const float L = __builtin_amdgcn_sqrtf(px * px + py * py + pz * pz);
+            const float chord = (tout - tin) * L;
+            const float S = 0x1p30f * __builtin_amdgcn_rcpf(chord);   // walk units per length
+            const float LS = L * S;
+            int cx, cy, cz;
+            uint32_t nxc, nyc, nzc;
+            IWalk w;
+            baxis(mx, axx, ix, tin, tout, ex, LS, cx, nxc, w.lx, w.qx);
+            baxis(my, ayy, iy, tin, tout, ey, LS, cy, nyc, w.ly, w.qy);
+            baxis(mz, azz, iz, tin, tout, ez, LS, cz, nzc, w.lz, w.qz);
+            uint32_t lend = 1u << 30;
+            lend = min(lend, last_plus_one(w.lx, nxc, w.qx));
+            lend = min(lend, last_plus_one(w.ly, nyc, w.qy));
+            lend = min(lend, last_plus_one(w.lz, nzc, w.qz));
             w.lend = lend;
-            walk(w, [&](int idx, float len) {
-                if (len > 0.f) atomicAdd(&acc[idx], len * yv);
-            });
+            // back to real cell indices and signed strides
+            const int rcx = dx < 0.f ? ex - 1 - cx : cx;
+            const int rcy = dy < 0.f ? ey - 1 - cy : cy;
+            const int rcz = dz < 0.f ? ez - 1 - cz : cz;
+            w.idx = (uint32_t)((rcz * LSZ + rcy * LSY + rcx) * 8);
+            w.stx = dx < 0.f ? (uint32_t)-8 : 8u;
+            w.sty = dy < 0.f ? (uint32_t)(-8 * LSY) : (uint32_t)(8 * LSY);
+            w.stz = dz < 0.f ? (uint32_t)(-8 * LSZ) : (uint32_t)(8 * LSZ);
+            iwalk_scatter_fix(w, acc, yv * scale * (chord * 0x1p-30f));
         }
     }
     __syncthreads();
+    const float inv_scale = 1.0f / scale;
     for (int i = threadIdx.x; i < BX * BY * BZ; i += NT) {
         const int lx = i % BX, ly = (i / BX) % BY, lz = i / (BX * BY);
         if (lx < ex && ly < ey && lz < ez) {
             const size_t g = ((size_t)(z0 + lz) * a.H + (y0 + ly)) * a.W + (x0 + lx);
-            const float val = acc[lz * LSZ + ly * LSY + lx];
+            const float val = (float)(long long)acc[lz * LSZ + ly * LSY + lx] * inv_scale;
             if (MODE == BM_BACKPROJECT) {
                 a.vol[g] = val;
             } else if (MODE == BM_SIRT_UPDATE) {
@@ -683,11 +809,14 @@ static RayArgs ray_args(const LaunchGeom &g) {
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
     if (g.two_d) {
+        a.lg_tv = 0;
         a.n_utiles = (g.U + 255) / 256;
         a.n_vtiles = 1;
     } else {
-        a.n_utiles = (g.U + 15) / 16;
-        a.n_vtiles = (g.V + 15) / 16;
+        a.lg_tv = g.fwd_lg_tv;
+        const int tv = 1 << a.lg_tv, tu = 64 >> a.lg_tv;
+        a.n_utiles = (g.U + 2 * tu - 1) / (2 * tu);
+        a.n_vtiles = (g.V + 2 * tv - 1) / (2 * tv);
     }
     a.n_blocks = a.n_utiles * a.n_vtiles * g.n_views;
     a.vol_bytes = (uint32_t)((size_t)g.W * g.H * g.D * 4);
@@ -755,7 +884,15 @@ hipError_t launch_backproject_atomic(const LaunchGeom &g, const float *sino, flo
     return launch_ray<RM_ATOMIC_BP>(g, a, s);
 }
 
-// Brick shapes: 3D 16 x 16 x 16 voxels with 4 waves; 2D 64 x 64 pixels with 4 waves.
+template <int BX, int BY, int BZ, int NT, int MODE>
+static void launch_brick_shape(BrickArgs &a, const LaunchGeom &g, hipStream_t s) {
+    a.nbx = (g.W + BX - 1) / BX;
+    a.nby = (g.H + BY - 1) / BY;
+    a.nbz = (g.D + BZ - 1) / BZ;
+    a.n_blocks = a.nbx * a.nby * a.nbz;
+    hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE>), dim3(a.n_blocks), dim3(NT), 0, s, a);
+}
+
 template <int MODE>
 static hipError_t launch_brick(const LaunchGeom &g, const float *sino, float *vol,
                                const float *cinv, float relax, hipStream_t s) {
@@ -768,15 +905,13 @@ static hipError_t launch_brick(const LaunchGeom &g, const float *sino, float *vo
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
     if (g.two_d) {
-        constexpr int BX = 64, BY = 64, BZ = 1, NT = 256;
-        a.nbx = (g.W + BX - 1) / BX; a.nby = (g.H + BY - 1) / BY; a.nbz = 1;
-        a.n_blocks = a.nbx * a.nby * a.nbz;
-        hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE>), dim3(a.n_blocks), dim3(NT), 0, s, a);
+        launch_brick_shape<64, 64, 1, 256, MODE>(a, g, s);
+    } else if (g.brick_shape == 1) {
+        launch_brick_shape<32, 32, 16, 512, MODE>(a, g, s);
+    } else if (g.brick_shape == 2) {
+        launch_brick_shape<32, 16, 16, 512, MODE>(a, g, s);
     } else {
-        constexpr int BX = 16, BY = 16, BZ = 16, NT = 256;
-        a.nbx = (g.W + BX - 1) / BX; a.nby = (g.H + BY - 1) / BY; a.nbz = (g.D + BZ - 1) / BZ;
-        a.n_blocks = a.nbx * a.nby * a.nbz;
-        hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE>), dim3(a.n_blocks), dim3(NT), 0, s, a);
+        launch_brick_shape<16, 16, 16, 256, MODE>(a, g, s);
     }
     return hipGetLastError();
 }
