@@ -58,18 +58,13 @@ def _traffic(kernel: str, workload: str, per_launch_bytes_unused=None):
 
 
 def cpu_baseline(wl, n_views_sample: int):
-    """Float64 oracle on the first views of the workload (A then A^T)."""
+    """Float64 oracle on evenly spaced views of the workload (A then A^T)."""
     import numpy as np
 
     import oracle
     from ray_driven_projector_amd import workloads as W
 
-    if wl.config == 4:
-        half = wl.n_views // 2
-        k = max(1, n_views_sample // 2)
-        views = list(range(half - k // 2, half - k // 2 + k)) + list(range(2 * half - k, 2 * half))
-    else:
-        views = list(range(n_views_sample))
+    views = sorted(set(int(round(v)) for v in np.linspace(0, wl.n_views - 1, n_views_sample)))
     sub = wl.subset_views(views)
     og = oracle.Geometry.from_workload(sub)
     x = W.make_phantom(wl)
