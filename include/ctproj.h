@@ -39,12 +39,18 @@
  *     the caller (e.g. a torch tensor's data_ptr()).  The library never frees
  *     or retains them.
  *   - A geometry handle is owned by the library from ct_geom_create until
- *     ct_geom_destroy.  It is immutable after creation; concurrent calls on
- *     different streams with the same handle are safe.
+ *     ct_geom_destroy.  Besides its per-view tables it may hold up to two
+ *     volume-sized float32 buffers: copies of the volume in y- or z-fastest
+ *     order that the forward projector reads for views whose detector axes run
+ *     along y or z (ct_geom_create allocates only those some view needs).  The
+ *     forward calls (ct_project, ct_sirt_residual, ct_sirt_step) write these
+ *     copies, so such calls on one handle must not overlap in time; use one
+ *     handle per stream for concurrent forward projections.  All other calls
+ *     only read the handle.
  *   - Every compute call is asynchronous and ordered on the caller's stream
  *     (a hipStream_t passed as void*; NULL is the legacy default stream).
  *   - Compute calls allocate nothing: all device memory they touch is the
- *     caller's buffers plus the handle's own tables.
+ *     caller's buffers plus the handle's own buffers.
  *
  * Errors: every call returns a ct_status_t.  Host-side validation happens
  * before anything is enqueued; on error nothing was launched.  A launch
@@ -133,7 +139,8 @@ ct_status_t ct_geom_view_table(ct_geom_t g, const ct_geom_desc_t *desc, double *
  * vol: device (D,H,W) float32; sino: device (views,U,V) float32.
  * Every ray is written, missed rays as 0 (diffct "Large Volumes and Chunked
  * Execution" > "Resident layouts and accumulation": forward kernels overwrite
- * each ray, including missed rays).  vol and sino must not overlap. */
+ * each ray, including missed rays).  vol and sino must not overlap; vol must
+ * hold finite values (a non-finite voxel may spread to rays that pass near it). */
 ct_status_t ct_project(ct_geom_t g, const float *vol, float *sino, ct_stream_t stream);
 
 /* Matched adjoint A^T: vol[j] = sum_i a_ij sino[i]; every voxel is overwritten.

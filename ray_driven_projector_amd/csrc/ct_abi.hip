@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -37,8 +38,9 @@ struct ct_geom_s {
     double *d_views = nullptr;          // device view table
     unsigned long long *d_total = nullptr;  // device counter for ct_count_intersections
     int device = 0;
-    int fwd_lg_tv = 2;                  // forward wave patch 16 u x 4 v
     int brick_shape = 2;                // adjoint bricks of 32 x 16 x 16
+    float *d_vol_yf = nullptr;          // y-fastest volume copy read by some views' gathers
+    float *d_vol_zf = nullptr;          // z-fastest volume copy read by some views' gathers
 };
 
 namespace {
@@ -72,8 +74,9 @@ LaunchGeom lg(ct_geom_t g) {
     l.spy = g->host.sy;
     l.spz = g->host.sz;
     l.two_d = g->host.is2d;
-    l.fwd_lg_tv = g->fwd_lg_tv;
     l.brick_shape = g->brick_shape;
+    l.vol_yf = g->d_vol_yf;
+    l.vol_zf = g->d_vol_zf;
     return l;
 }
 
@@ -107,20 +110,28 @@ ct_status_t check_alias(std::initializer_list<Arg> args) {
     return CT_OK;
 }
 
-// Launch shapes.  CTPROJ_FWD_LGTV (0..6) and CTPROJ_BRICK (0..2) override the
-// defaults for tuning sweeps; both only change the work decomposition.
-// Defaults measured on 512^3 cone and parallel3d workloads: 16 x 4 pixel patches
-// per wave for the forward gather, 32 x 16 x 16 voxel bricks for the adjoint.
+// Launch shapes.  CTPROJ_BRICK (0..2) overrides the adjoint brick shape and
+// CTPROJ_FWD_LAYOUT=x keeps every forward gather on the caller's x-fastest volume;
+// both only change the work decomposition (used for tuning comparisons).
+// Defaults measured on 512^3 cone and parallel3d workloads: 32 x 16 x 16 bricks.
 void choose_tiles(ct_geom_s *g) {
-    g->fwd_lg_tv = 2;
     g->brick_shape = 2;
-    if (const char *e = std::getenv("CTPROJ_FWD_LGTV")) {
-        const int v = std::atoi(e);
-        if (v >= 0 && v <= 6) g->fwd_lg_tv = v;
-    }
     if (const char *e = std::getenv("CTPROJ_BRICK")) {
         const int v = std::atoi(e);
         if (v >= 0 && v <= 2) g->brick_shape = v;
+    }
+    const char *lay = std::getenv("CTPROJ_FWD_LAYOUT");
+    if (lay && lay[0] == 'x') {
+        for (int64_t k = 0; k < g->host.n_views; ++k) {
+            double *t = g->table.data() + k * CT_VIEW_TABLE_STRIDE;
+            const double su[3] = {t[VT_OU] + t[VT_DU], t[VT_OU + 1] + t[VT_DU + 1], t[VT_OU + 2] + t[VT_DU + 2]};
+            const double sv[3] = {t[VT_OV] + t[VT_DV], t[VT_OV + 1] + t[VT_DV + 1], t[VT_OV + 2] + t[VT_DV + 2]};
+            const double nu = std::sqrt(su[0] * su[0] + su[1] * su[1] + su[2] * su[2]);
+            const double nv = std::sqrt(sv[0] * sv[0] + sv[1] * sv[1] + sv[2] * sv[2]);
+            const double au = nu > 0 ? std::fabs(su[0]) / nu : 0.0, av = nv > 0 ? std::fabs(sv[0]) / nv : 0.0;
+            t[VT_LAYOUT] = 0.0;
+            t[VT_PATCH] = (g->host.is2d || au >= av) ? 0.0 : 1.0;
+        }
     }
 }
 
@@ -216,6 +227,23 @@ ct_status_t ct_geom_create(const ct_geom_desc_t *desc, ct_geom_t *out) {
         delete g;
         return hip_fail(e, "hipMemcpy of the view table");
     }
+    // volume copies in other axis orders, for the views whose gathers read them
+    bool need_y = false, need_z = false;
+    for (int64_t k = 0; k < h.n_views; ++k) {
+        const double lay = g->table[(size_t)k * CT_VIEW_TABLE_STRIDE + VT_LAYOUT];
+        need_y = need_y || lay == 1.0;
+        need_z = need_z || lay == 2.0;
+    }
+    const size_t vbytes = (size_t)h.D * h.H * h.W * sizeof(float);
+    if ((need_y && hipMalloc((void **)&g->d_vol_yf, vbytes) != hipSuccess) ||
+        (need_z && hipMalloc((void **)&g->d_vol_zf, vbytes) != hipSuccess)) {
+        (void)hipGetLastError();
+        if (g->d_vol_yf) (void)hipFree(g->d_vol_yf);
+        (void)hipFree(g->d_views);
+        (void)hipFree(g->d_total);
+        delete g;
+        return fail(CT_E_NOMEM, "hipMalloc of a volume layout copy failed");
+    }
     *out = g;
     set_error("");
     return CT_OK;
@@ -227,6 +255,8 @@ ct_status_t ct_geom_destroy(ct_geom_t g) {
     g->magic = 0;
     if (g->d_views) (void)hipFree(g->d_views);
     if (g->d_total) (void)hipFree(g->d_total);
+    if (g->d_vol_yf) (void)hipFree(g->d_vol_yf);
+    if (g->d_vol_zf) (void)hipFree(g->d_vol_zf);
     delete g;
     set_error("");
     return CT_OK;

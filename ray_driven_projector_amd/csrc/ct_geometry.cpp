@@ -159,6 +159,53 @@ bool invert3(const double m[9], double inv[9]) {
 
 }  // namespace
 
+// Forward gather layout per view.  The 16-wide side of a wave's pixel patch runs
+// along one detector axis; the gather reads the volume copy whose contiguous axis
+// carries the largest share of that axis's pixel step, so neighbouring lanes read
+// neighbouring words.  score[a][p] = |step_p . e_a| / |step_p|.  A copy that only
+// a few views would use (each needs its own transposed volume) is given up for the
+// best copy already in use when that is at least 95% as well aligned.  2D beams
+// have one detector axis and keep the caller's x-fastest layout.
+static void choose_layouts(const GeomHost &g, double *table) {
+    if (g.is2d) return;
+    const int64_t n = g.n_views;
+    auto score = [&](const double *t, int a, int p) {
+        const double *o = t + (p == 0 ? VT_OU : VT_OV), *d = t + (p == 0 ? VT_DU : VT_DV);
+        const double st[3] = {o[0] + d[0], o[1] + d[1], o[2] + d[2]};
+        const double nn = std::sqrt(st[0] * st[0] + st[1] * st[1] + st[2] * st[2]);
+        return nn > 0 ? std::fabs(st[a]) / nn : 0.0;
+    };
+    int64_t use[3] = {0, 0, 0};
+    for (int64_t k = 0; k < n; ++k) {
+        double *t = table + k * CT_VIEW_TABLE_STRIDE;
+        double best = -1.0;
+        int la = 0, pa = 0;
+        for (int p = 0; p < 2; ++p)
+            for (int a = 0; a < 3; ++a)
+                if (score(t, a, p) > best + 1e-9) { best = score(t, a, p); la = a; pa = p; }
+        t[VT_LAYOUT] = la;
+        t[VT_PATCH] = pa;
+        use[la]++;
+    }
+    for (int64_t k = 0; k < n; ++k) {
+        double *t = table + k * CT_VIEW_TABLE_STRIDE;
+        const int la = (int)t[VT_LAYOUT];
+        if (use[la] * 16 >= n) continue;
+        const double own = score(t, la, (int)t[VT_PATCH]);
+        double best = -1.0;
+        int ba = -1, bp = 0;
+        for (int a = 0; a < 3; ++a) {
+            if (a == la || use[a] * 16 < n) continue;
+            for (int p = 0; p < 2; ++p)
+                if (score(t, a, p) > best) { best = score(t, a, p); ba = a; bp = p; }
+        }
+        if (ba >= 0 && best >= 0.95 * own) {
+            t[VT_LAYOUT] = ba;
+            t[VT_PATCH] = bp;
+        }
+    }
+}
+
 void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *table) {
     const bool parallel = (g.beam == CT_PARALLEL2D || g.beam == CT_PARALLEL3D);
     const V3 s = {g.sx, g.sy, g.sz};
@@ -211,7 +258,11 @@ void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *tab
         double inv[9];
         if (!invert3(m, inv)) std::memset(inv, 0, sizeof inv);  // unreachable after validation
         for (int q = 0; q < 9; ++q) t[VT_MINV + q] = inv[q];
+        // Forward gather layout: chosen for all views by choose_layouts.
+        t[VT_LAYOUT] = 0.0;
+        t[VT_PATCH] = 0.0;
     }
+    choose_layouts(g, table);
 }
 
 }  // namespace ctp

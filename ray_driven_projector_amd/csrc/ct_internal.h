@@ -21,6 +21,10 @@
 //   parallel              : u = beta, v = gamma
 // 2D geometries put the detector normal in the third column so MINV exists; the
 // v coordinate is then meaningless and ignored.
+//
+// LAYOUT / PATCH: the forward projector gathers from the volume copy whose
+// contiguous axis lies closest to the detector direction along which a wave's
+// 16-wide pixel patch runs, so neighbouring lanes read neighbouring words.
 #pragma once
 
 #include <cstdint>
@@ -41,7 +45,9 @@ enum ViewSlot : int {
     VT_N = 20,
     VT_PERSP = 23,
     VT_MINV = 24,   // 9 values, row-major
-    VT_END = 33
+    VT_LAYOUT = 33, // volume copy the forward gathers from: 0 x-, 1 y-, 2 z-fastest
+    VT_PATCH = 34,  // forward wave patch: 0 = 16 u x 4 v, 1 = 4 u x 16 v
+    VT_END = 35
 };
 static_assert(VT_END <= CT_VIEW_TABLE_STRIDE, "view table overflow");
 

@@ -245,25 +245,30 @@ __device__ __forceinline__ GStep gstep(const IWalk &w, uint32_t &idx, uint32_t &
 }
 
 // Sum of length * value over the walk, in walk units.  The cell offsets do not
-// depend on the loaded values, so the load of the next cell is issued before the
-// current product is formed; the loop is unrolled by two so the two value
-// registers swap roles without a copy (a copy would wait for the newer load).
-// The load after the last piece may fall outside the volume; the buffer
-// resource returns 0 there and the value is unused.
+// depend on the loaded values, so the walk runs ahead of the arithmetic: each
+// iteration generates four pieces and has their four gathers in flight before
+// the first product is formed.  Steps generated past the end of the walk have
+// zero length (their cells may lie outside the volume; the buffer resource reads
+// 0 there, and in-volume values are finite, so they add nothing).
 __device__ __forceinline__ float iwalk_gather(const IWalk &w, __amdgpu_buffer_rsrc_t rs) {
     uint32_t idx = w.idx;
     uint32_t lc = 0, lx = w.lx, ly = w.ly, lz = w.lz;
     float acc = 0.f;
-    float va = load_f32(rs, idx);
+    float v0 = load_f32(rs, idx);
     for (;;) {
         const GStep s0 = gstep(w, idx, lc, lx, ly, lz);
-        const float vb = load_f32(rs, idx);
-        acc = fmaf((float)s0.seg, va, acc);
-        if (s0.last) break;
+        const float v1 = load_f32(rs, idx);
         const GStep s1 = gstep(w, idx, lc, lx, ly, lz);
-        va = load_f32(rs, idx);
-        acc = fmaf((float)s1.seg, vb, acc);
-        if (s1.last) break;
+        const float v2 = load_f32(rs, idx);
+        const GStep s2 = gstep(w, idx, lc, lx, ly, lz);
+        const float v3 = load_f32(rs, idx);
+        const GStep s3 = gstep(w, idx, lc, lx, ly, lz);
+        acc = fmaf((float)s0.seg, v0, acc);
+        acc = fmaf((float)s1.seg, v1, acc);
+        acc = fmaf((float)s2.seg, v2, acc);
+        v0 = load_f32(rs, idx);
+        acc = fmaf((float)s3.seg, v3, acc);
+        if (s0.last || s1.last || s2.last || s3.last) break;
     }
     return acc;
 }
@@ -313,6 +318,7 @@ __device__ __forceinline__ void fix_axis(double d, double L, double S, int ncr, 
 __device__ __forceinline__ float project_ray(double ox, double oy, double oz, double dx, double dy,
                                              double dz, double tin, double tout, int nx, int ny,
                                              int nz, double spx, double spy, double spz,
+                                             uint32_t ex, uint32_t ey, uint32_t ez,
                                              __amdgpu_buffer_rsrc_t rs) {
     const double px = dx * spx, py = dy * spy, pz = dz * spz;
     const double L = sqrt(px * px + py * py + pz * pz);
@@ -329,7 +335,8 @@ __device__ __forceinline__ float project_ray(double ox, double oy, double oz, do
     cout = min(max(cout, 0), nM - 1);
     const int ncell = max((cout - cin) * sgn, 0) + 1;
     const int nch = (ncell + kChunk - 1) / kChunk;
-    const uint32_t sy = (uint32_t)nx * 4u, sz = (uint32_t)nx * (uint32_t)ny * 4u;
+    // (ex, ey, ez): element strides of x, y, z in the volume copy being read
+    const uint32_t sx = ex * 4u, sy = ey * 4u, sz = ez * 4u;
     float total = 0.f;
     double ta = tin;
     for (int ch = 0; ch < nch; ++ch) {
@@ -348,8 +355,8 @@ __device__ __forceinline__ float project_ray(double ox, double oy, double oz, do
         const double chord = (tb - ta) * L;
         const double S = 0x1p30 / chord;   // walk units per length unit
         IWalk w;
-        w.idx = (((uint32_t)cz * (uint32_t)ny + (uint32_t)cy) * (uint32_t)nx + (uint32_t)cx) * 4u;
-        w.stx = dx > 0.0 ? 4u : (uint32_t)-4;
+        w.idx = (uint32_t)cx * sx + (uint32_t)cy * sy + (uint32_t)cz * sz;
+        w.stx = dx > 0.0 ? sx : 0u - sx;
         w.sty = dy > 0.0 ? sy : 0u - sy;
         w.stz = dz > 0.0 ? sz : 0u - sz;
         w.lend = 1u << 30;
@@ -370,7 +377,9 @@ enum RayMode : int { RM_PROJECT = 0, RM_RESIDUAL = 1, RM_ROWINV = 2, RM_COUNT = 
 
 struct RayArgs {
     const double *views;
-    const float *vol;          // RM_PROJECT, RM_RESIDUAL
+    const float *vol;          // RM_PROJECT, RM_RESIDUAL: the caller's x-fastest volume
+    const float *vol_yf;       // y-fastest copy ((z*W + x)*H + y), if a view reads it
+    const float *vol_zf;       // z-fastest copy ((x*H + y)*D + z), if a view reads it
     float *out;                // sinogram-shaped output; RM_ATOMIC_BP: the volume
     const float *sino;         // RM_RESIDUAL: y; RM_ATOMIC_BP: the sinogram
     const float *rinv;         // RM_RESIDUAL
@@ -378,17 +387,17 @@ struct RayArgs {
     unsigned long long *total; // RM_COUNT
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
-    int lg_tv;                 // wave patch: (64 >> lg_tv) u  x  (1 << lg_tv) v
     int n_utiles, n_vtiles, n_blocks;
     uint32_t vol_bytes;
 };
 
-// Tiles: each wave takes a patch of 64 neighbouring pixels, so its rays form a
-// tight bundle that touches few cache lines per step; a 256-thread block is a
-// 2 x 2 arrangement of patches.  2D: 256 consecutive u per block.  Block order:
-// v-band outermost, then view, then u tile, so all views of one detector band
-// (one slab of the volume for cone/parallel3d orbits) run close together while
-// that slab is cache-resident.
+// Tiles: a 256-thread block takes 16 x 16 pixels of one view; each wave takes a
+// 16 x 4 (or 4 x 16) patch whose 16-wide side runs along the detector axis that
+// the view's volume copy stores contiguously, so the 64 rays of a wave read few
+// cache lines per step.  2D: 256 consecutive u per block.  Block order: v-band
+// outermost, then view, then u tile, so all views of one detector band (one slab
+// of the volume for cone/parallel3d orbits) run close together while that slab is
+// cache-resident.
 template <int MODE, bool TWO_D>
 __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
     const int blk = xcd_remap(blockIdx.x, a.n_blocks);
@@ -402,9 +411,14 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
         u = ut * 256 + threadIdx.x;
         v = 0;
     } else {
-        const int tv = 1 << a.lg_tv, tu = 64 >> a.lg_tv;
-        u = ut * 2 * tu + (wv & 1) * tu + (lane >> a.lg_tv);
-        v = band * 2 * tv + (wv >> 1) * tv + (lane & (tv - 1));
+        const double *vw0 = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
+        if (vw0[VT_PATCH] == 0.0) {   // 16 u x 4 v per wave
+            u = ut * 16 + (lane & 15);
+            v = band * 16 + wv * 4 + (lane >> 4);
+        } else {                      // 4 u x 16 v per wave
+            u = ut * 16 + wv * 4 + (lane >> 4);
+            v = band * 16 + (lane & 15);
+        }
     }
     const bool active = (u < a.U) && (v < a.V);
     uint32_t my_count = 0;
@@ -422,9 +436,15 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
             float acc = 0.f;
             double tin, tout;
             if (clip_ray(ox, oy, oz, dx, dy, dz, vw[VT_TMIN], vw[VT_TMAX], a.W, a.H, a.D, tin, tout)) {
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.vol, a.vol_bytes);
+                const int layout = TWO_D ? 0 : (int)vw[VT_LAYOUT];
+                const uint32_t W = a.W, H = a.H, D = a.D;
+                const float *src = layout == 0 ? a.vol : (layout == 1 ? a.vol_yf : a.vol_zf);
+                const uint32_t ex = layout == 0 ? 1u : (layout == 1 ? H : H * D);
+                const uint32_t ey = layout == 0 ? W : (layout == 1 ? 1u : D);
+                const uint32_t ez = layout == 0 ? W * H : (layout == 1 ? W * H : 1u);
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, a.vol_bytes);
                 acc = project_ray(ox, oy, oz, dx, dy, dz, tin, tout, a.W, a.H, a.D, a.spx, a.spy,
-                                  a.spz, rs);
+                                  a.spz, ex, ey, ez, rs);
             }
             if (MODE == RM_PROJECT) {
                 a.out[ray] = acc;
@@ -584,7 +604,7 @@ __device__ __forceinline__ void decode_ray(int r, int nfv, float inv_nfv, int &i
     if (iv < 0) { iu -= 1; iv += nfv; } else if (iv >= nfv) { iu += 1; iv -= nfv; }
 }
 
-// LDS scatter into 64-bit fixed point: lds[cell] += round(length * ys) for every
+// LDS scatter into 64-bit fixed point: lds[cell] += trunc(length * ys) for every
 // piece, ys being the value per walk unit already multiplied by the brick's
 // fixed-point scale (so each term stays below 2^30 in magnitude).  Float
 // atomic adds in LDS run some 30x slower than integer ones on this chip, hence the
@@ -596,7 +616,7 @@ __device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long 
     for (;;) {
         const uint32_t tmin = umin3(lx, ly, lz);
         const uint32_t tn = min(tmin, lend);
-        const int t = (int)__builtin_rintf((float)(tn - lc) * ys);
+        const int t = (int)((float)(tn - lc) * ys);   // truncation: |bias| < 1 unit per term
         const unsigned long long v = (unsigned long long)(long long)t;
         atomicAdd((unsigned long long *)((char *)lds + idx), v);
         if (tmin >= lend) break;
@@ -791,6 +811,27 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
     }
 }
 
+// out[a + b*tb + o*to] = in[a*sa + b + o*so]: one 32 x 32 tile of a 2D transpose
+// per block (reads contiguous along b, writes contiguous along a) for each outer
+// index o.  Builds the y- and z-fastest volume copies.
+__global__ __launch_bounds__(256) void transpose_kernel(const float *__restrict__ in,
+                                                        float *__restrict__ out, int A, int B,
+                                                        size_t sa, size_t so, size_t tb, size_t to) {
+    __shared__ float tile[32][33];
+    const int b0 = blockIdx.x * 32, a0 = blockIdx.y * 32;
+    const size_t o = blockIdx.z;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int k = ty; k < 32; k += 8) {
+        const int aa = a0 + k, bb = b0 + tx;
+        if (aa < A && bb < B) tile[k][tx] = in[(size_t)aa * sa + bb + o * so];
+    }
+    __syncthreads();
+    for (int k = ty; k < 32; k += 8) {
+        const int bb = b0 + k, aa = a0 + tx;
+        if (aa < A && bb < B) out[aa + (size_t)bb * tb + o * to] = tile[tx][k];
+    }
+}
+
 __global__ void fill_kernel(float *p, size_t n, float v) {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -809,14 +850,11 @@ static RayArgs ray_args(const LaunchGeom &g) {
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
     if (g.two_d) {
-        a.lg_tv = 0;
         a.n_utiles = (g.U + 255) / 256;
         a.n_vtiles = 1;
     } else {
-        a.lg_tv = g.fwd_lg_tv;
-        const int tv = 1 << a.lg_tv, tu = 64 >> a.lg_tv;
-        a.n_utiles = (g.U + 2 * tu - 1) / (2 * tu);
-        a.n_vtiles = (g.V + 2 * tv - 1) / (2 * tv);
+        a.n_utiles = (g.U + 15) / 16;
+        a.n_vtiles = (g.V + 15) / 16;
     }
     a.n_blocks = a.n_utiles * a.n_vtiles * g.n_views;
     a.vol_bytes = (uint32_t)((size_t)g.W * g.H * g.D * 4);
@@ -840,16 +878,42 @@ hipError_t launch_fill(float *p, size_t n, float v, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Build the y- and z-fastest copies of the volume that the views' gathers use.
+static hipError_t stage_layouts(const LaunchGeom &g, const float *vol, RayArgs &a, hipStream_t s) {
+    a.vol_yf = g.vol_yf;
+    a.vol_zf = g.vol_zf;
+    const size_t W = g.W, H = g.H, D = g.D;
+    if (g.vol_yf) {   // (z, x, y): per z slice, transpose (y, x) -> (x, y)
+        dim3 grid((unsigned)((W + 31) / 32), (unsigned)((H + 31) / 32), (unsigned)D);
+        hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, vol, g.vol_yf, (int)H, (int)W,
+                           W, W * H, H, W * H);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (g.vol_zf) {   // (x, y, z): per y row, transpose (z, x) -> (x, z)
+        dim3 grid((unsigned)((W + 31) / 32), (unsigned)((D + 31) / 32), (unsigned)H);
+        hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, vol, g.vol_zf, (int)D, (int)W,
+                           W * H, W, H * D, D);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_project(const LaunchGeom &g, const float *vol, float *sino, hipStream_t s) {
     RayArgs a = ray_args(g);
     a.vol = vol;
     a.out = sino;
+    const hipError_t e = stage_layouts(g, vol, a, s);
+    if (e != hipSuccess) return e;
     return launch_ray<RM_PROJECT>(g, a, s);
 }
 
 hipError_t launch_residual(const LaunchGeom &g, const float *x, const float *y, const float *rinv,
                            float *e, hipStream_t s) {
     RayArgs a = ray_args(g);
+    const hipError_t er = stage_layouts(g, x, a, s);
+    if (er != hipSuccess) return er;
     a.vol = x;
     a.sino = y;
     a.rinv = rinv;

@@ -13,8 +13,9 @@ struct LaunchGeom {
     int W, H, D, U, V, n_views;
     double spx, spy, spz;  // voxel spacing (x, y, z)
     bool two_d;
-    int fwd_lg_tv;         // forward wave patch: (64 >> lg) u x (1 << lg) v pixels
     int brick_shape;       // adjoint brick: 0 = 16^3, 1 = 32x32x16, 2 = 32x16x16
+    float *vol_yf;         // handle-owned y-fastest volume copy, or null if no view reads it
+    float *vol_zf;         // handle-owned z-fastest volume copy, or null if no view reads it
 };
 
 hipError_t launch_fill(float *p, size_t n, float v, hipStream_t s);
