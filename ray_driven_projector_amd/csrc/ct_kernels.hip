@@ -531,16 +531,18 @@ __device__ __forceinline__ void bclip(float o, float a, float inv, float e, floa
     }
 }
 
-// Entry cell, crossing count and fixed-point crossing plan of one mirrored axis.
-__device__ __forceinline__ void baxis(float o, float a, float inv, float tin, float tout, int e,
-                                      float LS, int &ce, uint32_t &ncr, uint32_t &l0, uint32_t &q) {
+// Crossing plan of one mirrored (non-negative direction) axis for the walk from
+// tin to tout: entry cell, number of planes crossed, and the fixed-point position
+// of the first crossing.  qf = walk units per cell along the axis (INF if the ray
+// does not move along it, which leaves the axis with no crossing).
+__device__ __forceinline__ void baxis(float o, float a, float tin, float tout, float e, float qf,
+                                      int &ce, uint32_t &ncr, uint32_t &l0) {
     const float E = fmaf(tin, a, o), X = fmaf(tout, a, o);
-    ce = min(max((int)floorf(E), 0), e - 1);
-    const int cx = min(max((int)ceilf(X) - 1, 0), e - 1);
-    ncr = (uint32_t)max(cx - ce, 0);
-    const float qf = LS * inv;                 // walk units per cell along this axis
-    q = fix32(qf);
-    l0 = fix32(((float)(ce + 1) - E) * qf);
+    const float fe = __builtin_amdgcn_fmed3f(floorf(E), 0.f, e - 1.f);
+    const float fx = __builtin_amdgcn_fmed3f(ceilf(X) - 1.f, 0.f, e - 1.f);
+    ce = (int)fe;
+    ncr = (uint32_t)fmaxf(fx - fe, 0.f);
+    l0 = fix32((fe + 1.f - E) * qf);
 }
 
 // Footprint of the brick [x0, x0+ex) x [y0, y0+ey) x [z0, z0+ez) on the detector of
@@ -597,35 +599,187 @@ __device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int 
     return f.u0 <= f.u1 && f.v0 <= f.v1;
 }
 
-// Footprint ray r (v fastest) -> offsets (iu, iv) from the footprint's corner.
-__device__ __forceinline__ void decode_ray(int r, int nfv, float inv_nfv, int &iu, int &iv) {
-    iu = (int)(((float)r + 0.5f) * inv_nfv);
-    iv = r - iu * nfv;
-    if (iv < 0) { iu -= 1; iv += nfv; } else if (iv >= nfv) { iu += 1; iv -= nfv; }
-}
-
 // LDS scatter into 64-bit fixed point: lds[cell] += trunc(length * ys) for every
 // piece, ys being the value per walk unit already multiplied by the brick's
 // fixed-point scale (so each term stays below 2^30 in magnitude).  Float
 // atomic adds in LDS run some 30x slower than integer ones on this chip, hence the
-// integer accumulator.
+// integer accumulator.  Unrolled by two so the piece start needs no register copy.
+struct SStep {
+    uint32_t tn;
+    bool last;
+};
+__device__ __forceinline__ SStep sstep(const IWalk &w, unsigned long long *lds, float ys, uint32_t &idx,
+                                       uint32_t lc, uint32_t &lx, uint32_t &ly, uint32_t &lz) {
+    const uint32_t tmin = umin3(lx, ly, lz);
+    const uint32_t tn = min(tmin, w.lend);
+    const int t = (int)((float)(tn - lc) * ys);   // truncation: |bias| < 1 unit per term
+    atomicAdd((unsigned long long *)((char *)lds + idx), (unsigned long long)(long long)t);
+    const bool bx = lx == tmin, by = ly == tmin, bz = lz == tmin;
+    lx = __builtin_elementwise_add_sat(lx, bx ? w.qx : 0u);
+    ly = __builtin_elementwise_add_sat(ly, by ? w.qy : 0u);
+    lz = __builtin_elementwise_add_sat(lz, bz ? w.qz : 0u);
+    idx += (bx ? w.stx : 0u) + (by ? w.sty : 0u) + (bz ? w.stz : 0u);
+    return SStep{tn, tmin >= w.lend};
+}
 __device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long long *lds, float ys) {
     uint32_t idx = w.idx;
-    uint32_t lc = 0, lx = w.lx, ly = w.ly, lz = w.lz;
-    const uint32_t lend = w.lend;
+    uint32_t lx = w.lx, ly = w.ly, lz = w.lz;
+    uint32_t lc = 0;
     for (;;) {
-        const uint32_t tmin = umin3(lx, ly, lz);
-        const uint32_t tn = min(tmin, lend);
-        const int t = (int)((float)(tn - lc) * ys);   // truncation: |bias| < 1 unit per term
-        const unsigned long long v = (unsigned long long)(long long)t;
-        atomicAdd((unsigned long long *)((char *)lds + idx), v);
-        if (tmin >= lend) break;
-        lc = tn;
-        const bool bx = lx == tmin, by = ly == tmin, bz = lz == tmin;
-        lx = __builtin_elementwise_add_sat(lx, bx ? w.qx : 0u);
-        ly = __builtin_elementwise_add_sat(ly, by ? w.qy : 0u);
-        lz = __builtin_elementwise_add_sat(lz, bz ? w.qz : 0u);
-        idx += (bx ? w.stx : 0u) + (by ? w.sty : 0u) + (bz ? w.stz : 0u);
+        const SStep a = sstep(w, lds, ys, idx, lc, lx, ly, lz);
+        if (a.last) break;
+        const SStep b = sstep(w, lds, ys, idx, a.tn, lx, ly, lz);
+        if (b.last) break;
+        lc = b.tn;
+    }
+}
+
+// Walk every ray of one view's footprint through the brick.  PERSP: fan/cone
+// rays (direction per ray); otherwise parallel rays, whose direction and
+// everything derived from it are the same for the whole footprint and kept in
+// scalar registers.  S = walk units per length unit (the same for the brick);
+// ys_scale = fixed-point scale / S.
+template <int LSY, int LSZ, int MODE, bool PERSP>
+__device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw, int view,
+                                           const Footprint &f, bool two_d, int lane, int x0, int y0,
+                                           int z0, int ex, int ey, int ez, double cbx, double cby,
+                                           double cbz, float S, float ys_scale,
+                                           unsigned long long *acc) {
+    const float fex = (float)ex, fey = (float)ey, fez = (float)ez;
+    const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
+    const int u0 = f.u0, v0 = f.v0;
+    const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
+    const bool ufast = !two_d && vw[VT_PATCH] == 0.0;
+    const int nf = ufast ? nfu : nfv;
+
+    // ---- per (view, brick) ray parametrisation, anchored at (u0, v0) ----
+    const double nx_ = vw[VT_N + 0], ny_ = vw[VT_N + 1], nz_ = vw[VT_N + 2];
+    const double fu0 = u0, fv0 = v0;
+    const double aox = vw[VT_O00 + 0] + fu0 * vw[VT_OU + 0] + fv0 * vw[VT_OV + 0];
+    const double aoy = vw[VT_O00 + 1] + fu0 * vw[VT_OU + 1] + fv0 * vw[VT_OV + 1];
+    const double aoz = vw[VT_O00 + 2] + fu0 * vw[VT_OU + 2] + fv0 * vw[VT_OV + 2];
+    const double adx = vw[VT_D00 + 0] + fu0 * vw[VT_DU + 0] + fv0 * vw[VT_DV + 0];
+    const double ady = vw[VT_D00 + 1] + fu0 * vw[VT_DU + 1] + fv0 * vw[VT_DV + 1];
+    const double adz = vw[VT_D00 + 2] + fu0 * vw[VT_DU + 2] + fv0 * vw[VT_DV + 2];
+    // Dir . N is the same for every pixel of a flat detector
+    const double tb = ((cbx - aox) * nx_ + (cby - aoy) * ny_ + (cbz - aoz) * nz_) /
+                      (adx * nx_ + ady * ny_ + adz * nz_);
+    const float A0x = uni((float)(aox + tb * adx - x0));
+    const float A0y = uni((float)(aoy + tb * ady - y0));
+    const float A0z = uni((float)(aoz + tb * adz - z0));
+    const float Aux = uni((float)(vw[VT_OU + 0] + tb * vw[VT_DU + 0]));
+    const float Auy = uni((float)(vw[VT_OU + 1] + tb * vw[VT_DU + 1]));
+    const float Auz = uni((float)(vw[VT_OU + 2] + tb * vw[VT_DU + 2]));
+    const float Avx = uni((float)(vw[VT_OV + 0] + tb * vw[VT_DV + 0]));
+    const float Avy = uni((float)(vw[VT_OV + 1] + tb * vw[VT_DV + 1]));
+    const float Avz = uni((float)(vw[VT_OV + 2] + tb * vw[VT_DV + 2]));
+    const float Dx = uni((float)adx), Dy = uni((float)ady), Dz = uni((float)adz);
+    const float DUx = uni((float)vw[VT_DU + 0]), DUy = uni((float)vw[VT_DU + 1]);
+    const float DUz = uni((float)vw[VT_DU + 2]);
+    const float DVx = uni((float)vw[VT_DV + 0]), DVy = uni((float)vw[VT_DV + 1]);
+    const float DVz = uni((float)vw[VT_DV + 2]);
+    const float t0 = uni((float)(vw[VT_TMIN] - tb)), t1 = uni((float)(vw[VT_TMAX] - tb));
+    const float *ysrc = a.sino + ((size_t)view * a.U + u0) * a.V + v0;
+
+    // parallel rays: direction-derived quantities once per footprint
+    float pdx = Dx, pdy = Dy, pdz = Dz;
+    float pix = 0.f, piy = 0.f, piz = 0.f, pqx = 0.f, pqy = 0.f, pqz = 0.f, pLS = 0.f;
+    if (!PERSP) {
+        const float dm = fmaxf(fabsf(pdx), fmaxf(fabsf(pdy), fabsf(pdz))) * 0x1p-40f;
+        if (fabsf(pdx) < dm) pdx = 0.f;
+        if (fabsf(pdy) < dm) pdy = 0.f;
+        if (fabsf(pdz) < dm) pdz = 0.f;
+        pix = __builtin_amdgcn_rcpf(fabsf(pdx));
+        piy = __builtin_amdgcn_rcpf(fabsf(pdy));
+        piz = __builtin_amdgcn_rcpf(fabsf(pdz));
+        const float L = sqrtf(pdx * spx * pdx * spx + pdy * spy * pdy * spy + pdz * spz * pdz * spz);
+        pLS = uni(L * S);
+        pqx = uni(L * S * pix);
+        pqy = uni(L * S * piy);
+        pqz = uni(L * S * piz);
+    }
+
+    // footprint position of ray r, advanced by 64 rays per round
+    const int step_slow = 64 / nf, step_fast = 64 - step_slow * nf;
+    int slow = lane / nf, fast = lane - (lane / nf) * nf;
+    float ynext = 1.f;
+    if (MODE != BM_COLINV && lane < nrays) {
+        const int iu = ufast ? fast : slow, iv = ufast ? slow : fast;
+        ynext = ysrc[(size_t)iu * a.V + iv];
+    }
+    for (int r = lane; r < nrays; r += 64) {
+        const int cf = fast, cs = slow;
+        fast += step_fast;
+        slow += step_slow;
+        if (fast >= nf) { fast -= nf; slow += 1; }
+        const float yv = ynext;
+        if (MODE != BM_COLINV && r + 64 < nrays) {
+            const int iu = ufast ? fast : slow, iv = ufast ? slow : fast;
+            ynext = ysrc[(size_t)iu * a.V + iv];
+        }
+        if (yv == 0.f) continue;
+        const float fu = (float)(ufast ? cf : cs), fv = (float)(ufast ? cs : cf);
+        const float ox = fmaf(fv, Avx, fmaf(fu, Aux, A0x));
+        const float oy = fmaf(fv, Avy, fmaf(fu, Auy, A0y));
+        const float oz = fmaf(fv, Avz, fmaf(fu, Auz, A0z));
+        float dx = pdx, dy = pdy, dz = pdz;
+        if (PERSP) {
+            dx = fmaf(fv, DVx, fmaf(fu, DUx, Dx));
+            dy = fmaf(fv, DVy, fmaf(fu, DUy, Dy));
+            dz = fmaf(fv, DVz, fmaf(fu, DUz, Dz));
+            const float dm = fmaxf(fabsf(dx), fmaxf(fabsf(dy), fabsf(dz))) * 0x1p-40f;
+            if (fabsf(dx) < dm) dx = 0.f;
+            if (fabsf(dy) < dm) dy = 0.f;
+            if (fabsf(dz) < dm) dz = 0.f;
+        }
+        // mirror negative directions: walk every axis upwards
+        const float mx = dx < 0.f ? fex - ox : ox, axx = fabsf(dx);
+        const float my = dy < 0.f ? fey - oy : oy, ayy = fabsf(dy);
+        const float mz = dz < 0.f ? fez - oz : oz, azz = fabsf(dz);
+        const float ix = PERSP ? __builtin_amdgcn_rcpf(axx) : pix;
+        const float iy = PERSP ? __builtin_amdgcn_rcpf(ayy) : piy;
+        const float iz = PERSP ? __builtin_amdgcn_rcpf(azz) : piz;
+        float lox, hix, loy, hiy, loz, hiz;
+        bclip(mx, axx, ix, fex, lox, hix);
+        bclip(my, ayy, iy, fey, loy, hiy);
+        bclip(mz, azz, iz, fez, loz, hiz);
+        const float tin = fmaxf(fmaxf(fmaxf(lox, loy), loz), t0);
+        const float tout = fminf(fminf(fminf(hix, hiy), hiz), t1);
+        if (!(tin < tout)) continue;
+        float qx = pqx, qy = pqy, qz = pqz;
+        float LS = pLS;
+        if (PERSP) {
+            const float px = dx * spx, py = dy * spy, pz = dz * spz;
+            LS = __builtin_amdgcn_sqrtf(px * px + py * py + pz * pz) * S;
+            qx = LS * ix;
+            qy = LS * iy;
+            qz = LS * iz;
+        }
+        int cx, cy, cz;
+        uint32_t nxc, nyc, nzc;
+        IWalk w;
+        baxis(mx, axx, tin, tout, fex, qx, cx, nxc, w.lx);
+        baxis(my, ayy, tin, tout, fey, qy, cy, nyc, w.ly);
+        baxis(mz, azz, tin, tout, fez, qz, cz, nzc, w.lz);
+        w.qx = fix32(qx);
+        w.qy = fix32(qy);
+        w.qz = fix32(qz);
+        // the walk ends at the ray's own end (a segment may stop inside the brick)
+        // or one plane past the last crossing of an axis, whichever comes first
+        uint32_t lend = fix32((tout - tin) * LS);
+        lend = min(lend, last_plus_one(w.lx, nxc, w.qx));
+        lend = min(lend, last_plus_one(w.ly, nyc, w.qy));
+        lend = min(lend, last_plus_one(w.lz, nzc, w.qz));
+        w.lend = lend;
+        // back to real cell indices and signed strides
+        const int rcx = dx < 0.f ? ex - 1 - cx : cx;
+        const int rcy = dy < 0.f ? ey - 1 - cy : cy;
+        const int rcz = dz < 0.f ? ez - 1 - cz : cz;
+        w.idx = (uint32_t)((rcz * LSZ + rcy * LSY + rcx) * 8);
+        w.stx = dx < 0.f ? (uint32_t)-8 : 8u;
+        w.sty = dy < 0.f ? (uint32_t)(-8 * LSY) : (uint32_t)(8 * LSY);
+        w.stz = dz < 0.f ? (uint32_t)(-8 * LSZ) : (uint32_t)(8 * LSZ);
+        iwalk_scatter_fix(w, acc, yv * ys_scale);
     }
 }
 
@@ -648,7 +802,6 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
     const double cbx = x0 + 0.5 * ex, cby = y0 + 0.5 * ey, cbz = z0 + 0.5 * ez;
     const int lane = threadIdx.x & 63, wv = uni((int)(threadIdx.x >> 6));
     const bool two_d = (a.D == 1 && a.V == 1);
-    const float fex = (float)ex, fey = (float)ey, fez = (float)ez;
     const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
 
     // ---- pass 1: largest |y| over the rays that can meet this brick ----
@@ -659,13 +812,15 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
             const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
             Footprint f;
             if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d, f)) continue;
-            const int nfv = f.v1 - f.v0 + 1, nrays = (f.u1 - f.u0 + 1) * nfv;
-            const float inv_nfv = 1.0f / (float)nfv;
+            const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
             const float *ysrc = a.sino + ((size_t)view * a.U + f.u0) * a.V + f.v0;
+            const int step_slow = 64 / nfv, step_fast = 64 - step_slow * nfv;
+            int iu = lane / nfv, iv = lane - (lane / nfv) * nfv;
             for (int r = lane; r < nrays; r += 64) {
-                int iu, iv;
-                decode_ray(r, nfv, inv_nfv, iu, iv);
                 m = fmaxf(m, fabsf(ysrc[(size_t)iu * a.V + iv]));
+                iv += step_fast;
+                iu += step_slow;
+                if (iv >= nfv) { iv -= nfv; iu += 1; }
             }
         }
         for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -683,114 +838,21 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
     const float scale = bound > 0.f ? ldexpf(1.f, (int)floorf(30.f - log2f(bound))) : 1.f;
 
     // ---- pass 2: walk every footprint ray through the brick ----
+    // walk units: 2^30 per brick diagonal, the longest possible chord
+    const float bdiag = sqrtf((float)ex * spx * (float)ex * spx + (float)ey * spy * (float)ey * spy +
+                              (float)ez * spz * (float)ez * spz);
+    const float S = 0x1p30f / bdiag;
+    const float ys_scale = scale / S;
     for (int view = wv; view < a.n_views; view += NWAVES) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
         Footprint f;
         if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d, f)) continue;
-        const int u0 = f.u0, v0 = f.v0;
-        const int nfv = f.v1 - f.v0 + 1;
-        const int nrays = (f.u1 - f.u0 + 1) * nfv;
-        const float inv_nfv = 1.0f / (float)nfv;
-
-        // ---- per (view, brick) ray parametrisation, anchored at (u0, v0) ----
-        const double nx_ = vw[VT_N + 0], ny_ = vw[VT_N + 1], nz_ = vw[VT_N + 2];
-        const double fu0 = u0, fv0 = v0;
-        const double aox = vw[VT_O00 + 0] + fu0 * vw[VT_OU + 0] + fv0 * vw[VT_OV + 0];
-        const double aoy = vw[VT_O00 + 1] + fu0 * vw[VT_OU + 1] + fv0 * vw[VT_OV + 1];
-        const double aoz = vw[VT_O00 + 2] + fu0 * vw[VT_OU + 2] + fv0 * vw[VT_OV + 2];
-        const double adx = vw[VT_D00 + 0] + fu0 * vw[VT_DU + 0] + fv0 * vw[VT_DV + 0];
-        const double ady = vw[VT_D00 + 1] + fu0 * vw[VT_DU + 1] + fv0 * vw[VT_DV + 1];
-        const double adz = vw[VT_D00 + 2] + fu0 * vw[VT_DU + 2] + fv0 * vw[VT_DV + 2];
-        // Dir . N is the same for every pixel of a flat detector
-        const double tb = ((cbx - aox) * nx_ + (cby - aoy) * ny_ + (cbz - aoz) * nz_) /
-                          (adx * nx_ + ady * ny_ + adz * nz_);
-        const float A0x = uni((float)(aox + tb * adx - x0));
-        const float A0y = uni((float)(aoy + tb * ady - y0));
-        const float A0z = uni((float)(aoz + tb * adz - z0));
-        const float Aux = uni((float)(vw[VT_OU + 0] + tb * vw[VT_DU + 0]));
-        const float Auy = uni((float)(vw[VT_OU + 1] + tb * vw[VT_DU + 1]));
-        const float Auz = uni((float)(vw[VT_OU + 2] + tb * vw[VT_DU + 2]));
-        const float Avx = uni((float)(vw[VT_OV + 0] + tb * vw[VT_DV + 0]));
-        const float Avy = uni((float)(vw[VT_OV + 1] + tb * vw[VT_DV + 1]));
-        const float Avz = uni((float)(vw[VT_OV + 2] + tb * vw[VT_DV + 2]));
-        const float Dx = uni((float)adx), Dy = uni((float)ady), Dz = uni((float)adz);
-        const float DUx = uni((float)vw[VT_DU + 0]), DUy = uni((float)vw[VT_DU + 1]);
-        const float DUz = uni((float)vw[VT_DU + 2]);
-        const float DVx = uni((float)vw[VT_DV + 0]), DVy = uni((float)vw[VT_DV + 1]);
-        const float DVz = uni((float)vw[VT_DV + 2]);
-        const float t0 = uni((float)(vw[VT_TMIN] - tb)), t1 = uni((float)(vw[VT_TMAX] - tb));
-        const float *ysrc = a.sino + ((size_t)view * a.U + u0) * a.V + v0;
-
-        // the sinogram value of the lane's next ray is loaded one ray ahead
-        float ynext = 1.f;
-        if (MODE != BM_COLINV && lane < nrays) {
-            int iu, iv;
-            decode_ray(lane, nfv, inv_nfv, iu, iv);
-            ynext = ysrc[(size_t)iu * a.V + iv];
-        }
-        for (int r = lane; r < nrays; r += 64) {
-            const float yv = ynext;
-            if (MODE != BM_COLINV && r + 64 < nrays) {
-                int iu, iv;
-                decode_ray(r + 64, nfv, inv_nfv, iu, iv);
-                ynext = ysrc[(size_t)iu * a.V + iv];
-            }
-            if (yv == 0.f) continue;
-            int iu, iv;
-            decode_ray(r, nfv, inv_nfv, iu, iv);
-            const float fu = (float)iu, fv = (float)iv;
-            const float ox = fmaf(fv, Avx, fmaf(fu, Aux, A0x));
-            const float oy = fmaf(fv, Avy, fmaf(fu, Auy, A0y));
-            const float oz = fmaf(fv, Avz, fmaf(fu, Auz, A0z));
-            float dx = fmaf(fv, DVx, fmaf(fu, DUx, Dx));
-            float dy = fmaf(fv, DVy, fmaf(fu, DUy, Dy));
-            float dz = fmaf(fv, DVz, fmaf(fu, DUz, Dz));
-            {
-                const float dm = fmaxf(fabsf(dx), fmaxf(fabsf(dy), fabsf(dz))) * 0x1p-40f;
-                if (fabsf(dx) < dm) dx = 0.f;
-                if (fabsf(dy) < dm) dy = 0.f;
-                if (fabsf(dz) < dm) dz = 0.f;
-            }
-            // mirror negative directions: walk every axis upwards
-            const float mx = dx < 0.f ? fex - ox : ox, axx = fabsf(dx);
-            const float my = dy < 0.f ? fey - oy : oy, ayy = fabsf(dy);
-            const float mz = dz < 0.f ? fez - oz : oz, azz = fabsf(dz);
-            const float ix = __builtin_amdgcn_rcpf(axx);
-            const float iy = __builtin_amdgcn_rcpf(ayy);
-            const float iz = __builtin_amdgcn_rcpf(azz);
-            float lox, hix, loy, hiy, loz, hiz;
-            bclip(mx, axx, ix, fex, lox, hix);
-            bclip(my, ayy, iy, fey, loy, hiy);
-            bclip(mz, azz, iz, fez, loz, hiz);
-            const float tin = fmaxf(fmaxf(fmaxf(lox, loy), loz), t0);
-            const float tout = fminf(fminf(fminf(hix, hiy), hiz), t1);
-            if (!(tin < tout)) continue;
-            const float px = dx * spx, py = dy * spy, pz = dz * spz;
-            const float L = __builtin_amdgcn_sqrtf(px * px + py * py + pz * pz);
-            const float chord = (tout - tin) * L;
-            const float S = 0x1p30f * __builtin_amdgcn_rcpf(chord);   // walk units per length
-            const float LS = L * S;
-            int cx, cy, cz;
-            uint32_t nxc, nyc, nzc;
-            IWalk w;
-            baxis(mx, axx, ix, tin, tout, ex, LS, cx, nxc, w.lx, w.qx);
-            baxis(my, ayy, iy, tin, tout, ey, LS, cy, nyc, w.ly, w.qy);
-            baxis(mz, azz, iz, tin, tout, ez, LS, cz, nzc, w.lz, w.qz);
-            uint32_t lend = 1u << 30;
-            lend = min(lend, last_plus_one(w.lx, nxc, w.qx));
-            lend = min(lend, last_plus_one(w.ly, nyc, w.qy));
-            lend = min(lend, last_plus_one(w.lz, nzc, w.qz));
-            w.lend = lend;
-            // back to real cell indices and signed strides
-            const int rcx = dx < 0.f ? ex - 1 - cx : cx;
-            const int rcy = dy < 0.f ? ey - 1 - cy : cy;
-            const int rcz = dz < 0.f ? ez - 1 - cz : cz;
-            w.idx = (uint32_t)((rcz * LSZ + rcy * LSY + rcx) * 8);
-            w.stx = dx < 0.f ? (uint32_t)-8 : 8u;
-            w.sty = dy < 0.f ? (uint32_t)(-8 * LSY) : (uint32_t)(8 * LSY);
-            w.stz = dz < 0.f ? (uint32_t)(-8 * LSZ) : (uint32_t)(8 * LSZ);
-            iwalk_scatter_fix(w, acc, yv * scale * (chord * 0x1p-30f));
-        }
+        if (vw[VT_PERSP] != 0.0)
+            brick_rays<LSY, LSZ, MODE, true>(a, vw, view, f, two_d, lane, x0, y0, z0, ex, ey, ez, cbx,
+                                             cby, cbz, S, ys_scale, acc);
+        else
+            brick_rays<LSY, LSZ, MODE, false>(a, vw, view, f, two_d, lane, x0, y0, z0, ex, ey, ez, cbx,
+                                              cby, cbz, S, ys_scale, acc);
     }
     __syncthreads();
     const float inv_scale = 1.0f / scale;
@@ -971,7 +1033,7 @@ static hipError_t launch_brick(const LaunchGeom &g, const float *sino, float *vo
     if (g.two_d) {
         launch_brick_shape<64, 64, 1, 256, MODE>(a, g, s);
     } else if (g.brick_shape == 1) {
-        launch_brick_shape<32, 32, 16, 512, MODE>(a, g, s);
+        launch_brick_shape<32, 32, 16, 1024, MODE>(a, g, s);
     } else if (g.brick_shape == 2) {
         launch_brick_shape<32, 16, 16, 512, MODE>(a, g, s);
     } else {
