@@ -145,11 +145,12 @@ ct_status_t ct_project(ct_geom_t g, const float *vol, float *sino, ct_stream_t s
 
 /* Matched adjoint A^T: vol[j] = sum_i a_ij sino[i]; every voxel is overwritten.
  * Volume bricks accumulate their rays in on-chip memory (LDS) and are each
- * written once, with no global atomics.  The LDS adds of different waves
- * interleave freely, so the float32 summation order, and with it the last bits
- * of the result, can differ between runs (the diffct documentation notes the
- * same of its atomic adjoint in "Example results").  sino and vol must not
- * overlap. */
+ * written once, with no global atomics.  Each term is an exact product of a
+ * fixed-point piece length and a fixed-point ray value, summed in 64-bit
+ * integers, so the result is bit-for-bit the same on every run (unlike an
+ * adjoint built on float atomics: the diffct documentation notes run-to-run
+ * differences of its atomic adjoint in "Example results").  sino must hold
+ * finite values; sino and vol must not overlap. */
 ct_status_t ct_backproject(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream);
 
 /* The same A^T by one lane per ray with global float atomics (a measured

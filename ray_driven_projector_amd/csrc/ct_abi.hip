@@ -110,7 +110,7 @@ ct_status_t check_alias(std::initializer_list<Arg> args) {
     return CT_OK;
 }
 
-// Launch shapes.  CTPROJ_BRICK (0..2) overrides the adjoint brick shape and
+// Launch shapes.  CTPROJ_BRICK (0..4) overrides the adjoint brick shape and
 // CTPROJ_FWD_LAYOUT=x keeps every forward gather on the caller's x-fastest volume;
 // both only change the work decomposition (used for tuning comparisons).
 // Defaults measured on 512^3 cone and parallel3d workloads: 32 x 16 x 16 bricks.
@@ -118,7 +118,7 @@ void choose_tiles(ct_geom_s *g) {
     g->brick_shape = 2;
     if (const char *e = std::getenv("CTPROJ_BRICK")) {
         const int v = std::atoi(e);
-        if (v >= 0 && v <= 2) g->brick_shape = v;
+        if (v >= 0 && v <= 4) g->brick_shape = v;
     }
     const char *lay = std::getenv("CTPROJ_FWD_LAYOUT");
     if (lay && lay[0] == 'x') {

@@ -9,7 +9,8 @@
 //
 // Walk.  The pieces of a ray are enumerated by an integer fixed-point walk: the
 // positions of the next crossing on each axis are unsigned 32-bit multiples of a
-// per-walk unit (about 1e-9 of the walk's length).  The m-th crossing of axis a is
+// walk unit (forward: about 1e-9 of the walk's length; brick adjoint: just under
+// 2^-23 of a voxel diagonal).  The m-th crossing of axis a is
 // l0_a + m q_a, formed by exact (saturating) integer adds, so nothing drifts; the
 // walk ends at
 //   l_end = min(chord, min_a (l0_a + N_a q_a)),
@@ -21,8 +22,9 @@
 // Precision.  The forward gather sets each ray up in float64 and re-bases the walk
 // every kChunk cells of the major axis, so every piece length is resolved to
 // better than 1e-5 of a cell.  The brick adjoint sets each ray up in float32 in
-// brick-local coordinates (positions within tens of voxels).  The atomic adjoint
-// keeps a float64 walk.
+// brick-local coordinates (positions within tens of voxels) and sums exact
+// integer products, so its result does not depend on the order of the adds.
+// The atomic adjoint keeps a float64 walk.
 //
 // Layout.  Volume (D,H,W) float32, sinogram (views,U,V) float32, V fastest.
 #include <hip/hip_runtime.h>
@@ -599,51 +601,62 @@ __device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int 
     return f.u0 <= f.u1 && f.v0 <= f.v1;
 }
 
-// LDS scatter into 64-bit fixed point: lds[cell] += trunc(length * ys) for every
-// piece, ys being the value per walk unit already multiplied by the brick's
-// fixed-point scale (so each term stays below 2^30 in magnitude).  Float
-// atomic adds in LDS run some 30x slower than integer ones on this chip, hence the
-// integer accumulator.  Unrolled by two so the piece start needs no register copy.
-struct SStep {
-    uint32_t tn;
-    bool last;
-};
-__device__ __forceinline__ SStep sstep(const IWalk &w, unsigned long long *lds, float ys, uint32_t &idx,
-                                       uint32_t lc, uint32_t &lx, uint32_t &ly, uint32_t &lz) {
-    const uint32_t tmin = umin3(lx, ly, lz);
-    const uint32_t tn = min(tmin, w.lend);
-    const int t = (int)((float)(tn - lc) * ys);   // truncation: |bias| < 1 unit per term
-    atomicAdd((unsigned long long *)((char *)lds + idx), (unsigned long long)(long long)t);
-    const bool bx = lx == tmin, by = ly == tmin, bz = lz == tmin;
+// LDS scatter into 64-bit fixed point: lds[cell] += length * Y for every piece,
+// length in walk units and Y the ray's value in fixed point, both below 2^23 in
+// magnitude, so the product is formed exactly by the 24-bit multiplier
+// (v_mul_i32_i24 / v_mul_hi_i32_i24) and the integer sums do not depend on the
+// order of the adds.  Float atomic adds in LDS run some 30x slower than integer
+// ones on this chip, hence the integer accumulator.
+constexpr float kPieceUnits = 8323072.f;   // 2^23 - 2^16
+__device__ __forceinline__ unsigned long long mul24_64(uint32_t len, int y) {
+    const int a = (int)(len << 8) >> 8, b = (y << 8) >> 8;   // 24-bit operands
+    return (unsigned long long)((long long)a * (long long)b);
+}
+__device__ __forceinline__ void lds_add(unsigned long long *lds, uint32_t byte_off,
+                                        unsigned long long v) {
+    atomicAdd((unsigned long long *)((char *)lds + byte_off), v);
+}
+// Move past the crossing at t: every axis whose next crossing is t steps on.
+__device__ __forceinline__ void sadvance(const IWalk &w, uint32_t t, uint32_t &idx, uint32_t &lx,
+                                         uint32_t &ly, uint32_t &lz) {
+    const bool bx = lx == t, by = ly == t, bz = lz == t;
     lx = __builtin_elementwise_add_sat(lx, bx ? w.qx : 0u);
     ly = __builtin_elementwise_add_sat(ly, by ? w.qy : 0u);
     lz = __builtin_elementwise_add_sat(lz, bz ? w.qz : 0u);
     idx += (bx ? w.stx : 0u) + (by ? w.sty : 0u) + (bz ? w.stz : 0u);
-    return SStep{tn, tmin >= w.lend};
 }
-__device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long long *lds, float ys) {
+// Two pieces per iteration with one exit test: the loop is entered only while the
+// next event t lies before l_end, so the first piece of an iteration is whole;
+// the second is cut at l_end.  A cell is only written before a crossing at or
+// past l_end has been taken, so every offset stays inside the brick.
+__device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long long *lds, int Y) {
     uint32_t idx = w.idx;
     uint32_t lx = w.lx, ly = w.ly, lz = w.lz;
-    uint32_t lc = 0;
-    for (;;) {
-        const SStep a = sstep(w, lds, ys, idx, lc, lx, ly, lz);
-        if (a.last) break;
-        const SStep b = sstep(w, lds, ys, idx, a.tn, lx, ly, lz);
-        if (b.last) break;
-        lc = b.tn;
+    uint32_t lc = 0, t = umin3(lx, ly, lz);
+    while (t < w.lend) {
+        lds_add(lds, idx, mul24_64(t - lc, Y));
+        sadvance(w, t, idx, lx, ly, lz);
+        lc = t;
+        t = umin3(lx, ly, lz);
+        const uint32_t tn = min(t, w.lend);
+        lds_add(lds, idx, mul24_64(tn - lc, Y));
+        sadvance(w, t, idx, lx, ly, lz);
+        lc = tn;
+        t = umin3(lx, ly, lz);
     }
+    if (lc < w.lend) lds_add(lds, idx, mul24_64(w.lend - lc, Y));
 }
 
 // Walk every ray of one view's footprint through the brick.  PERSP: fan/cone
 // rays (direction per ray); otherwise parallel rays, whose direction and
 // everything derived from it are the same for the whole footprint and kept in
-// scalar registers.  S = walk units per length unit (the same for the brick);
-// ys_scale = fixed-point scale / S.
+// scalar registers.  S = walk units per length unit (the same for every ray);
+// yscale = power-of-two fixed-point scale of the ray values of this brick.
 template <int LSY, int LSZ, int MODE, bool PERSP>
 __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw, int view,
                                            const Footprint &f, bool two_d, int lane, int x0, int y0,
                                            int z0, int ex, int ey, int ez, double cbx, double cby,
-                                           double cbz, float S, float ys_scale,
+                                           double cbz, float S, float yscale,
                                            unsigned long long *acc) {
     const float fex = (float)ex, fey = (float)ey, fez = (float)ez;
     const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
@@ -779,7 +792,8 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         w.stx = dx < 0.f ? (uint32_t)-8 : 8u;
         w.sty = dy < 0.f ? (uint32_t)(-8 * LSY) : (uint32_t)(8 * LSY);
         w.stz = dz < 0.f ? (uint32_t)(-8 * LSZ) : (uint32_t)(8 * LSZ);
-        iwalk_scatter_fix(w, acc, yv * ys_scale);
+        const int Y = (int)rintf(__builtin_amdgcn_fmed3f(yv * yscale, -8388607.f, 8388607.f));
+        iwalk_scatter_fix(w, acc, Y);
     }
 }
 
@@ -831,36 +845,33 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
     } else {
         __syncthreads();
     }
-    // Fixed-point scale: one piece is at most a voxel diagonal long, so every
-    // term length * |y| * scale stays below 2^30.
-    const float diag = sqrtf(spx * spx + spy * spy + spz * spz);
-    const float bound = diag * ymax;
-    const float scale = bound > 0.f ? ldexpf(1.f, (int)floorf(30.f - log2f(bound))) : 1.f;
+    // Ray values in fixed point: |y| * yscale < 2^23 for every ray of the brick.
+    const float yscale = ymax > 0.f ? ldexpf(1.f, 22 - ilogbf(ymax)) : 1.f;
 
     // ---- pass 2: walk every footprint ray through the brick ----
-    // walk units: 2^30 per brick diagonal, the longest possible chord
-    const float bdiag = sqrtf((float)ex * spx * (float)ex * spx + (float)ey * spy * (float)ey * spy +
-                              (float)ez * spz * (float)ez * spz);
-    const float S = 0x1p30f / bdiag;
-    const float ys_scale = scale / S;
+    // Walk units: just under 2^23 per voxel diagonal.  A piece never exceeds the
+    // ray's crossing length of one cell along its major axis, which is at most
+    // the voxel diagonal, so piece lengths fit the 24-bit multiplier.
+    const float vdiag = two_d ? sqrtf(spx * spx + spy * spy) : sqrtf(spx * spx + spy * spy + spz * spz);
+    const float S = kPieceUnits / vdiag;
     for (int view = wv; view < a.n_views; view += NWAVES) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
         Footprint f;
         if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d, f)) continue;
         if (vw[VT_PERSP] != 0.0)
             brick_rays<LSY, LSZ, MODE, true>(a, vw, view, f, two_d, lane, x0, y0, z0, ex, ey, ez, cbx,
-                                             cby, cbz, S, ys_scale, acc);
+                                             cby, cbz, S, yscale, acc);
         else
             brick_rays<LSY, LSZ, MODE, false>(a, vw, view, f, two_d, lane, x0, y0, z0, ex, ey, ez, cbx,
-                                              cby, cbz, S, ys_scale, acc);
+                                              cby, cbz, S, yscale, acc);
     }
     __syncthreads();
-    const float inv_scale = 1.0f / scale;
+    const double inv_scale = 1.0 / ((double)S * (double)yscale);
     for (int i = threadIdx.x; i < BX * BY * BZ; i += NT) {
         const int lx = i % BX, ly = (i / BX) % BY, lz = i / (BX * BY);
         if (lx < ex && ly < ey && lz < ez) {
             const size_t g = ((size_t)(z0 + lz) * a.H + (y0 + ly)) * a.W + (x0 + lx);
-            const float val = (float)(long long)acc[lz * LSZ + ly * LSY + lx] * inv_scale;
+            const float val = (float)((double)(long long)acc[lz * LSZ + ly * LSY + lx] * inv_scale);
             if (MODE == BM_BACKPROJECT) {
                 a.vol[g] = val;
             } else if (MODE == BM_SIRT_UPDATE) {
@@ -1036,6 +1047,10 @@ static hipError_t launch_brick(const LaunchGeom &g, const float *sino, float *vo
         launch_brick_shape<32, 32, 16, 1024, MODE>(a, g, s);
     } else if (g.brick_shape == 2) {
         launch_brick_shape<32, 16, 16, 512, MODE>(a, g, s);
+    } else if (g.brick_shape == 3) {
+        launch_brick_shape<32, 16, 32, 1024, MODE>(a, g, s);
+    } else if (g.brick_shape == 4) {
+        launch_brick_shape<32, 32, 8, 512, MODE>(a, g, s);
     } else {
         launch_brick_shape<16, 16, 16, 256, MODE>(a, g, s);
     }
