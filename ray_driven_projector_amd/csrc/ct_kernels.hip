@@ -520,31 +520,36 @@ struct BrickArgs {
     int nbx, nby, nbz, n_blocks;
 };
 
-// Clip one (mirrored, non-negative) axis: o' in brick coordinates, a = |d|,
-// inv = 1/a (INF for a = 0), extent e.  A ray with a = 0 is inside iff 0 <= o' < e.
-__device__ __forceinline__ void bclip(float o, float a, float inv, float e, float &lo, float &hi) {
-    if (a > 0.f) {
-        lo = -o * inv;
-        hi = (e - o) * inv;
-    } else {
-        const bool in = (o >= 0.f) && (o < e);
-        lo = in ? -3e38f : 3e38f;
-        hi = -lo;
+// Slab clip of an axis the ray does not move along (a = 0): the ray is inside
+// for every t iff 0 <= o < e.  Replaces (o, 1/a) by stand-ins for which the
+// general formulas lo = -o/a, hi = (e - o)/a give an unbounded interval (inside)
+// or an empty one (outside).
+__device__ __forceinline__ void bclip_zero(float o, float a, float e, float &co, float &cinv) {
+    if (a == 0.f) {
+        co = (o >= 0.f && o < e) ? 0.5f * e : -1.f;
+        cinv = 1e35f;
     }
 }
 
-// Crossing plan of one mirrored (non-negative direction) axis for the walk from
-// tin to tout: entry cell, number of planes crossed, and the fixed-point position
-// of the first crossing.  qf = walk units per cell along the axis (INF if the ray
-// does not move along it, which leaves the axis with no crossing).
-__device__ __forceinline__ void baxis(float o, float a, float tin, float tout, float e, float qf,
-                                      int &ce, uint32_t &ncr, uint32_t &l0) {
-    const float E = fmaf(tin, a, o), X = fmaf(tout, a, o);
-    const float fe = __builtin_amdgcn_fmed3f(floorf(E), 0.f, e - 1.f);
-    const float fx = __builtin_amdgcn_fmed3f(ceilf(X) - 1.f, 0.f, e - 1.f);
-    ce = (int)fe;
-    ncr = (uint32_t)fmaxf(fx - fe, 0.f);
-    l0 = fix32((fe + 1.f - E) * qf);
+// Non-negative float32 to fixed point with the convert's own saturation
+// (values from 2^32 up and INF give 0xFFFFFFFF, negative values 0).
+__device__ __forceinline__ uint32_t sat_u32(float x) {
+    uint32_t r;
+    asm("v_cvt_u32_f32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
+// Crossing plan of one mirrored (non-negative direction) axis of extent e for a
+// walk entering at tin: entry cell fe (float), the fixed-point position l0 of
+// the first crossing, and far = the position of the crossing of the brick's far
+// face, l0 + (e - 1 - fe) q, saturating.  A walk that ends at or before far takes
+// at most e - 1 - fe crossings of this axis, so it never leaves the brick.
+__device__ __forceinline__ void baxis(float o, float a, float tin, float em1, float qf, uint32_t q,
+                                      float &fe, uint32_t &l0, uint32_t &far) {
+    const float E = fmaf(tin, a, o);
+    fe = __builtin_amdgcn_fmed3f(floorf(E), 0.f, em1);
+    l0 = sat_u32((fe + 1.f - E) * qf);
+    far = last_plus_one(l0, sat_u32(em1 - fe), q);
 }
 
 // Footprint of the brick [x0, x0+ex) x [y0, y0+ey) x [z0, z0+ez) on the detector of
@@ -648,21 +653,22 @@ __device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long 
 }
 
 // Walk every ray of one view's footprint through the brick.  PERSP: fan/cone
-// rays (direction per ray); otherwise parallel rays, whose direction and
-// everything derived from it are the same for the whole footprint and kept in
-// scalar registers.  S = walk units per length unit (the same for every ray);
-// yscale = power-of-two fixed-point scale of the ray values of this brick.
-template <int LSY, int LSZ, int MODE, bool PERSP>
+// rays (direction per ray); otherwise parallel rays, whose direction and all
+// that is derived from it are the same for the whole footprint and computed
+// once, outside the ray loop.  TWO_D: single-slice bricks of a 2D geometry,
+// whose rays lie in the slice (z is neither clipped nor walked).  S = walk units
+// per length unit; yscale = power-of-two fixed-point scale of the ray values.
+template <int LSY, int LSZ, int MODE, bool PERSP, bool TWO_D>
 __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw, int view,
-                                           const Footprint &f, bool two_d, int lane, int x0, int y0,
-                                           int z0, int ex, int ey, int ez, double cbx, double cby,
+                                           const Footprint &f, int lane, int x0, int y0, int z0,
+                                           int ex, int ey, int ez, double cbx, double cby,
                                            double cbz, float S, float yscale,
                                            unsigned long long *acc) {
     const float fex = (float)ex, fey = (float)ey, fez = (float)ez;
     const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
     const int u0 = f.u0, v0 = f.v0;
     const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
-    const bool ufast = !two_d && vw[VT_PATCH] == 0.0;
+    const bool ufast = !TWO_D && vw[VT_PATCH] == 0.0;
     const int nf = ufast ? nfu : nfv;
 
     // ---- per (view, brick) ray parametrisation, anchored at (u0, v0) ----
@@ -677,121 +683,112 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     // Dir . N is the same for every pixel of a flat detector
     const double tb = ((cbx - aox) * nx_ + (cby - aoy) * ny_ + (cbz - aoz) * nz_) /
                       (adx * nx_ + ady * ny_ + adz * nz_);
+    // per-pixel steps along the footprint's fast (f) and slow (s) axes
+    const int pf = ufast ? VT_OU : VT_OV, ps = ufast ? VT_OV : VT_OU;
+    const int qf_ = ufast ? VT_DU : VT_DV, qs_ = ufast ? VT_DV : VT_DU;
     const float A0x = uni((float)(aox + tb * adx - x0));
     const float A0y = uni((float)(aoy + tb * ady - y0));
     const float A0z = uni((float)(aoz + tb * adz - z0));
-    const float Aux = uni((float)(vw[VT_OU + 0] + tb * vw[VT_DU + 0]));
-    const float Auy = uni((float)(vw[VT_OU + 1] + tb * vw[VT_DU + 1]));
-    const float Auz = uni((float)(vw[VT_OU + 2] + tb * vw[VT_DU + 2]));
-    const float Avx = uni((float)(vw[VT_OV + 0] + tb * vw[VT_DV + 0]));
-    const float Avy = uni((float)(vw[VT_OV + 1] + tb * vw[VT_DV + 1]));
-    const float Avz = uni((float)(vw[VT_OV + 2] + tb * vw[VT_DV + 2]));
+    const float Afx = uni((float)(vw[pf + 0] + tb * vw[qf_ + 0]));
+    const float Afy = uni((float)(vw[pf + 1] + tb * vw[qf_ + 1]));
+    const float Afz = uni((float)(vw[pf + 2] + tb * vw[qf_ + 2]));
+    const float Asx = uni((float)(vw[ps + 0] + tb * vw[qs_ + 0]));
+    const float Asy = uni((float)(vw[ps + 1] + tb * vw[qs_ + 1]));
+    const float Asz = uni((float)(vw[ps + 2] + tb * vw[qs_ + 2]));
     const float Dx = uni((float)adx), Dy = uni((float)ady), Dz = uni((float)adz);
-    const float DUx = uni((float)vw[VT_DU + 0]), DUy = uni((float)vw[VT_DU + 1]);
-    const float DUz = uni((float)vw[VT_DU + 2]);
-    const float DVx = uni((float)vw[VT_DV + 0]), DVy = uni((float)vw[VT_DV + 1]);
-    const float DVz = uni((float)vw[VT_DV + 2]);
+    const float DFx = uni((float)vw[qf_ + 0]), DFy = uni((float)vw[qf_ + 1]);
+    const float DFz = uni((float)vw[qf_ + 2]);
+    const float DSx = uni((float)vw[qs_ + 0]), DSy = uni((float)vw[qs_ + 1]);
+    const float DSz = uni((float)vw[qs_ + 2]);
     const float t0 = uni((float)(vw[VT_TMIN] - tb)), t1 = uni((float)(vw[VT_TMAX] - tb));
     const float *ysrc = a.sino + ((size_t)view * a.U + u0) * a.V + v0;
+    const uint32_t yfs = ufast ? a.V : 1, yss = ufast ? 1 : a.V;   // sinogram strides, fast / slow
 
-    // parallel rays: direction-derived quantities once per footprint
-    float pdx = Dx, pdy = Dy, pdz = Dz;
-    float pix = 0.f, piy = 0.f, piz = 0.f, pqx = 0.f, pqy = 0.f, pqz = 0.f, pLS = 0.f;
-    if (!PERSP) {
-        const float dm = fmaxf(fabsf(pdx), fmaxf(fabsf(pdy), fabsf(pdz))) * 0x1p-40f;
-        if (fabsf(pdx) < dm) pdx = 0.f;
-        if (fabsf(pdy) < dm) pdy = 0.f;
-        if (fabsf(pdz) < dm) pdz = 0.f;
-        pix = __builtin_amdgcn_rcpf(fabsf(pdx));
-        piy = __builtin_amdgcn_rcpf(fabsf(pdy));
-        piz = __builtin_amdgcn_rcpf(fabsf(pdz));
-        const float L = sqrtf(pdx * spx * pdx * spx + pdy * spy * pdy * spy + pdz * spz * pdz * spz);
-        pLS = uni(L * S);
-        pqx = uni(L * S * pix);
-        pqy = uni(L * S * piy);
-        pqz = uni(L * S * piz);
-    }
-
-    // footprint position of ray r, advanced by 64 rays per round
+    // footprint position of ray r (fast index ff, slow index fs, sinogram offset
+    // yo), advanced by 64 rays per round
     const int step_slow = 64 / nf, step_fast = 64 - step_slow * nf;
-    int slow = lane / nf, fast = lane - (lane / nf) * nf;
+    const uint32_t yo_step = step_fast * yfs + step_slow * yss, yo_wrap = yss - nf * yfs;
+    const float fnf = (float)nf, fstep_fast = (float)step_fast, fstep_slow = (float)step_slow;
+    const int ls = lane / nf, lf = lane - ls * nf;
+    float ff = (float)lf, fs = (float)ls;
+    uint32_t yo = lf * yfs + ls * yss;
     float ynext = 1.f;
-    if (MODE != BM_COLINV && lane < nrays) {
-        const int iu = ufast ? fast : slow, iv = ufast ? slow : fast;
-        ynext = ysrc[(size_t)iu * a.V + iv];
-    }
+    if (MODE != BM_COLINV && lane < nrays) ynext = ysrc[yo];
     for (int r = lane; r < nrays; r += 64) {
-        const int cf = fast, cs = slow;
-        fast += step_fast;
-        slow += step_slow;
-        if (fast >= nf) { fast -= nf; slow += 1; }
+        const float cf = ff, cs = fs;
+        ff += fstep_fast;
+        fs += fstep_slow;
+        yo += yo_step;
+        if (ff >= fnf) { ff -= fnf; fs += 1.f; yo += yo_wrap; }
         const float yv = ynext;
-        if (MODE != BM_COLINV && r + 64 < nrays) {
-            const int iu = ufast ? fast : slow, iv = ufast ? slow : fast;
-            ynext = ysrc[(size_t)iu * a.V + iv];
-        }
+        if (MODE != BM_COLINV && r + 64 < nrays) ynext = ysrc[yo];
         if (yv == 0.f) continue;
-        const float fu = (float)(ufast ? cf : cs), fv = (float)(ufast ? cs : cf);
-        const float ox = fmaf(fv, Avx, fmaf(fu, Aux, A0x));
-        const float oy = fmaf(fv, Avy, fmaf(fu, Auy, A0y));
-        const float oz = fmaf(fv, Avz, fmaf(fu, Auz, A0z));
-        float dx = pdx, dy = pdy, dz = pdz;
+        const float ox = fmaf(cs, Asx, fmaf(cf, Afx, A0x));
+        const float oy = fmaf(cs, Asy, fmaf(cf, Afy, A0y));
+        const float oz = TWO_D ? A0z : fmaf(cs, Asz, fmaf(cf, Afz, A0z));
+        float dx = Dx, dy = Dy, dz = Dz;
         if (PERSP) {
-            dx = fmaf(fv, DVx, fmaf(fu, DUx, Dx));
-            dy = fmaf(fv, DVy, fmaf(fu, DUy, Dy));
-            dz = fmaf(fv, DVz, fmaf(fu, DUz, Dz));
-            const float dm = fmaxf(fabsf(dx), fmaxf(fabsf(dy), fabsf(dz))) * 0x1p-40f;
+            dx = fmaf(cs, DSx, fmaf(cf, DFx, Dx));
+            dy = fmaf(cs, DSy, fmaf(cf, DFy, Dy));
+            if (!TWO_D) dz = fmaf(cs, DSz, fmaf(cf, DFz, Dz));
+        }
+        if (TWO_D) dz = 0.f;
+        // Components below 2^-40 of the largest count as zero.  Waves without
+        // any (nearly all of them) take the short clip below.
+        const float dm = fmaxf(fabsf(dx), fmaxf(fabsf(dy), fabsf(dz))) * 0x1p-40f;
+        const float amin = TWO_D ? fminf(fabsf(dx), fabsf(dy))
+                                 : fminf(fabsf(dx), fminf(fabsf(dy), fabsf(dz)));
+        const bool slow = __builtin_amdgcn_ballot_w64(amin < dm) != 0;   // wave-uniform
+        if (slow) {
             if (fabsf(dx) < dm) dx = 0.f;
             if (fabsf(dy) < dm) dy = 0.f;
-            if (fabsf(dz) < dm) dz = 0.f;
+            if (!TWO_D && fabsf(dz) < dm) dz = 0.f;
         }
         // mirror negative directions: walk every axis upwards
-        const float mx = dx < 0.f ? fex - ox : ox, axx = fabsf(dx);
-        const float my = dy < 0.f ? fey - oy : oy, ayy = fabsf(dy);
-        const float mz = dz < 0.f ? fez - oz : oz, azz = fabsf(dz);
-        const float ix = PERSP ? __builtin_amdgcn_rcpf(axx) : pix;
-        const float iy = PERSP ? __builtin_amdgcn_rcpf(ayy) : piy;
-        const float iz = PERSP ? __builtin_amdgcn_rcpf(azz) : piz;
-        float lox, hix, loy, hiy, loz, hiz;
-        bclip(mx, axx, ix, fex, lox, hix);
-        bclip(my, ayy, iy, fey, loy, hiy);
-        bclip(mz, azz, iz, fez, loz, hiz);
+        const bool nx = dx < 0.f, ny = dy < 0.f, nz = dz < 0.f;
+        const float mx = nx ? fex - ox : ox, axx = fabsf(dx);
+        const float my = ny ? fey - oy : oy, ayy = fabsf(dy);
+        const float mz = nz ? fez - oz : oz, azz = fabsf(dz);
+        const float ix = __builtin_amdgcn_rcpf(axx);
+        const float iy = __builtin_amdgcn_rcpf(ayy);
+        const float iz = TWO_D ? 0.f : __builtin_amdgcn_rcpf(azz);
+        // slab clip: lo = -m / a, hi = (e - m) / a
+        float cx = mx, cy = my, cz = mz, cix = ix, ciy = iy, ciz = iz;
+        if (slow) {
+            bclip_zero(mx, axx, fex, cx, cix);
+            bclip_zero(my, ayy, fey, cy, ciy);
+            if (!TWO_D) bclip_zero(mz, azz, fez, cz, ciz);
+        }
+        const float lox = -cx * cix, hix = fmaf(fex, cix, lox);
+        const float loy = -cy * ciy, hiy = fmaf(fey, ciy, loy);
+        const float loz = TWO_D ? -3e38f : -cz * ciz, hiz = TWO_D ? 3e38f : fmaf(fez, ciz, loz);
         const float tin = fmaxf(fmaxf(fmaxf(lox, loy), loz), t0);
         const float tout = fminf(fminf(fminf(hix, hiy), hiz), t1);
         if (!(tin < tout)) continue;
-        float qx = pqx, qy = pqy, qz = pqz;
-        float LS = pLS;
-        if (PERSP) {
-            const float px = dx * spx, py = dy * spy, pz = dz * spz;
-            LS = __builtin_amdgcn_sqrtf(px * px + py * py + pz * pz) * S;
-            qx = LS * ix;
-            qy = LS * iy;
-            qz = LS * iz;
-        }
-        int cx, cy, cz;
-        uint32_t nxc, nyc, nzc;
+        const float px = dx * spx, py = dy * spy, pz = dz * spz;
+        const float LS = __builtin_amdgcn_sqrtf(px * px + py * py + pz * pz) * S;
+        const float qfx = LS * ix, qfy = LS * iy, qfz = LS * iz;
         IWalk w;
-        baxis(mx, axx, tin, tout, fex, qx, cx, nxc, w.lx);
-        baxis(my, ayy, tin, tout, fey, qy, cy, nyc, w.ly);
-        baxis(mz, azz, tin, tout, fez, qz, cz, nzc, w.lz);
-        w.qx = fix32(qx);
-        w.qy = fix32(qy);
-        w.qz = fix32(qz);
-        // the walk ends at the ray's own end (a segment may stop inside the brick)
-        // or one plane past the last crossing of an axis, whichever comes first
-        uint32_t lend = fix32((tout - tin) * LS);
-        lend = min(lend, last_plus_one(w.lx, nxc, w.qx));
-        lend = min(lend, last_plus_one(w.ly, nyc, w.qy));
-        lend = min(lend, last_plus_one(w.lz, nzc, w.qz));
-        w.lend = lend;
-        // back to real cell indices and signed strides
-        const int rcx = dx < 0.f ? ex - 1 - cx : cx;
-        const int rcy = dy < 0.f ? ey - 1 - cy : cy;
-        const int rcz = dz < 0.f ? ez - 1 - cz : cz;
-        w.idx = (uint32_t)((rcz * LSZ + rcy * LSY + rcx) * 8);
-        w.stx = dx < 0.f ? (uint32_t)-8 : 8u;
-        w.sty = dy < 0.f ? (uint32_t)(-8 * LSY) : (uint32_t)(8 * LSY);
-        w.stz = dz < 0.f ? (uint32_t)(-8 * LSZ) : (uint32_t)(8 * LSZ);
+        w.qx = sat_u32(qfx);
+        w.qy = sat_u32(qfy);
+        w.qz = TWO_D ? 0xFFFFFFFFu : sat_u32(qfz);
+        float fcx, fcy, fcz = 0.f;
+        uint32_t farx, fary, farz = 0xFFFFFFFFu;
+        baxis(mx, axx, tin, fex - 1.f, qfx, w.qx, fcx, w.lx, farx);
+        baxis(my, ayy, tin, fey - 1.f, qfy, w.qy, fcy, w.ly, fary);
+        if (!TWO_D) baxis(mz, azz, tin, fez - 1.f, qfz, w.qz, fcz, w.lz, farz);
+        else w.lz = 0xFFFFFFFFu;
+        // the walk ends at the ray's own end (a segment may stop inside the
+        // brick) or at the first far-face crossing, whichever comes first
+        w.lend = min(sat_u32((tout - tin) * LS), min(min(farx, fary), farz));
+        // back to real cell indices (exact small integers in float) and strides
+        const float rcx = nx ? fex - 1.f - fcx : fcx;
+        const float rcy = ny ? fey - 1.f - fcy : fcy;
+        const float rcz = nz ? fez - 1.f - fcz : fcz;
+        w.idx = (uint32_t)fmaf(rcz, (float)(8 * LSZ), fmaf(rcy, (float)(8 * LSY), rcx * 8.f));
+        w.stx = nx ? (uint32_t)-8 : 8u;
+        w.sty = ny ? (uint32_t)(-8 * LSY) : (uint32_t)(8 * LSY);
+        w.stz = TWO_D ? 0u : (nz ? (uint32_t)(-8 * LSZ) : (uint32_t)(8 * LSZ));
         const int Y = (int)rintf(__builtin_amdgcn_fmed3f(yv * yscale, -8388607.f, 8388607.f));
         iwalk_scatter_fix(w, acc, Y);
     }
@@ -815,7 +812,8 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
     const int ex = min(BX, a.W - x0), ey = min(BY, a.H - y0), ez = min(BZ, a.D - z0);
     const double cbx = x0 + 0.5 * ex, cby = y0 + 0.5 * ey, cbz = z0 + 0.5 * ez;
     const int lane = threadIdx.x & 63, wv = uni((int)(threadIdx.x >> 6));
-    const bool two_d = (a.D == 1 && a.V == 1);
+    constexpr bool TWO_D = BZ == 1;   // single-slice bricks serve the 2D beams only
+    const bool two_d = TWO_D;
     const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
 
     // ---- pass 1: largest |y| over the rays that can meet this brick ----
@@ -859,11 +857,11 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
         Footprint f;
         if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d, f)) continue;
         if (vw[VT_PERSP] != 0.0)
-            brick_rays<LSY, LSZ, MODE, true>(a, vw, view, f, two_d, lane, x0, y0, z0, ex, ey, ez, cbx,
-                                             cby, cbz, S, yscale, acc);
+            brick_rays<LSY, LSZ, MODE, true, TWO_D>(a, vw, view, f, lane, x0, y0, z0, ex, ey, ez, cbx,
+                                                    cby, cbz, S, yscale, acc);
         else
-            brick_rays<LSY, LSZ, MODE, false>(a, vw, view, f, two_d, lane, x0, y0, z0, ex, ey, ez, cbx,
-                                              cby, cbz, S, yscale, acc);
+            brick_rays<LSY, LSZ, MODE, false, TWO_D>(a, vw, view, f, lane, x0, y0, z0, ex, ey, ez,
+                                                     cbx, cby, cbz, S, yscale, acc);
     }
     __syncthreads();
     const double inv_scale = 1.0 / ((double)S * (double)yscale);
