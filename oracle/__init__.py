@@ -212,3 +212,46 @@ def sirt(g: Geometry, y, x0=None, n_iter: int = 1, relax: float = 1.0,
         e = R * (y - project(g, x, nthreads))
         x = x + relax * C * backproject(g, e, nthreads)
     return x
+
+
+# ----------------------------------------------------------------------------
+# CGLS.  The pages ship a CGLS solver and time it per iteration ("Performance";
+# "API Reference" > "Numerical Solvers"), keeping x, s, p and r, q with float64
+# norms ("Large Volumes and Chunked Execution" > "Runnable iterative
+# reconstruction"), but print no formula.  This is the standard conjugate
+# gradient method on the normal equations A^T A x = A^T y in its least-squares
+# form (Hestenes-Stiefel / Bjorck):
+#     r = y - A x,  s = A^T r,  p = s,  gamma = ||s||^2
+#     repeat:  q = A p;  alpha = gamma / ||q||^2;  x += alpha p;  r -= alpha q;
+#              s = A^T r;  gamma' = ||s||^2;  beta = gamma' / gamma;
+#              p = s + beta p;  gamma = gamma'
+# with alpha = 0 when q = 0 and beta = 0 when gamma = 0.
+# ----------------------------------------------------------------------------
+
+def cgls(g: Geometry, y, x0=None, n_iter: int = 1, nthreads: int | None = None):
+    """Returns (x, hist): hist holds per iteration alpha, beta, gamma (after the
+    step), qq = ||q||^2 and rr = ||r||^2 (after the step), plus the start's
+    gamma0 and rr0."""
+    y = _as64(y).reshape(g.sino_shape)
+    x = np.zeros(g.vol_shape) if x0 is None else _as64(x0).reshape(g.vol_shape).copy()
+    r = y - project(g, x, nthreads)
+    s = backproject(g, r, nthreads)
+    p = s.copy()
+    gamma = float(np.sum(s * s))
+    hist = {"gamma0": gamma, "rr0": float(np.sum(r * r)),
+            "alpha": [], "beta": [], "gamma": [], "qq": [], "rr": []}
+    for _ in range(n_iter):
+        q = project(g, p, nthreads)
+        qq = float(np.sum(q * q))
+        alpha = gamma / qq if qq > 0 else 0.0
+        x = x + alpha * p
+        r = r - alpha * q
+        s = backproject(g, r, nthreads)
+        gnew = float(np.sum(s * s))
+        beta = gnew / gamma if gamma > 0 else 0.0
+        p = s + beta * p
+        gamma = gnew
+        for k, v in (("alpha", alpha), ("beta", beta), ("gamma", gamma), ("qq", qq),
+                     ("rr", float(np.sum(r * r)))):
+            hist[k].append(v)
+    return x, hist

@@ -337,3 +337,62 @@ def test_sirt_weighted_residual_is_non_increasing():
         assert cur <= prev * (1 + 1e-12)
         prev = cur
         x = oracle.sirt(g, y, x0=x, n_iter=1, weights=(R, C))
+
+
+# ---------------------------------------------------------------------------
+# CGLS
+# ---------------------------------------------------------------------------
+
+def _cgls_problem(seed=3):
+    wl = _tiny(W.BEAM_FAN2D, seed, vol=(1, 5, 5), det=(12, 1), views=9)
+    g = oracle.Geometry.from_workload(wl)
+    A = oracle.brute_matrix(g)
+    assert np.linalg.matrix_rank(A) == A.shape[1]   # full column rank: unique LS solution
+    rng = np.random.default_rng(seed)
+    y = rng.uniform(0, 1, wl.sino_shape)            # inconsistent data
+    return wl, g, A, y
+
+
+def test_cgls_reaches_the_least_squares_solution():
+    # In exact arithmetic CGLS reaches the LS solution within N (= unknowns) steps.
+    wl, g, A, y = _cgls_problem()
+    xs = np.linalg.lstsq(A, y.ravel(), rcond=None)[0]
+    n = A.shape[1]
+    x, hist = oracle.cgls(g, y, n_iter=n + 5)
+    np.testing.assert_allclose(x.ravel(), xs, rtol=0, atol=1e-8 * np.abs(xs).max())
+    assert hist["gamma"][-1] <= 1e-18 * hist["gamma0"]
+
+
+def test_cgls_iterates_minimise_over_the_krylov_space():
+    # x_k = argmin ||y - A x|| over x0 + span{s0, (A^T A) s0, ..., (A^T A)^(k-1) s0},
+    # s0 = A^T (y - A x0): solved directly with a dense basis and lstsq.
+    wl, g, A, y = _cgls_problem(5)
+    rng = np.random.default_rng(7)
+    for x0 in (None, rng.uniform(0, 1, wl.vol_shape)):
+        x0v = np.zeros(A.shape[1]) if x0 is None else x0.ravel()
+        s0 = A.T @ (y.ravel() - A @ x0v)
+        basis = [s0]
+        for _ in range(3):
+            basis.append(A.T @ (A @ basis[-1]))
+        for k in (1, 2, 3, 4):
+            B = np.stack(basis[:k], axis=1)
+            c = np.linalg.lstsq(A @ B, y.ravel() - A @ x0v, rcond=None)[0]
+            xr = x0v + B @ c
+            xk, _ = oracle.cgls(g, y, x0=x0, n_iter=k)
+            np.testing.assert_allclose(xk.ravel(), xr, rtol=0, atol=1e-9 * np.abs(xr).max())
+
+
+def test_cgls_residual_recurrence_and_monotone_norm():
+    wl = W.make_workload(2, scale=8)
+    g = oracle.Geometry.from_workload(wl)
+    y = oracle.project(g, W.make_phantom(wl)) + 0.01 * np.random.default_rng(2).standard_normal(g.sino_shape)
+    x, hist = oracle.cgls(g, y, n_iter=6)
+    rr = [hist["rr0"]] + hist["rr"]
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(rr, rr[1:]))
+    # ||r_{k+1}||^2 = ||r_k||^2 - alpha_k gamma_k (gamma before the step)
+    gam = [hist["gamma0"]] + hist["gamma"]
+    for k in range(6):
+        assert abs(rr[k + 1] - (rr[k] - hist["alpha"][k] * gam[k])) <= 1e-9 * rr[0]
+    # the recurrence-updated residual is the true residual
+    r = y - oracle.project(g, x)
+    assert abs(float(np.sum(r * r)) - rr[-1]) <= 1e-9 * rr[0]
