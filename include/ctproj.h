@@ -61,6 +61,7 @@
 #ifndef CTPROJ_H
 #define CTPROJ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -175,6 +176,40 @@ ct_status_t ct_sirt_update(ct_geom_t g, const float *work_sino, const float *col
  * work_sino is caller scratch of sinogram size; relax must be finite. */
 ct_status_t ct_sirt_step(ct_geom_t g, float *x, const float *y, const float *row_inv,
                          const float *col_inv, float relax, float *work_sino, ct_stream_t stream);
+
+/* ---- CGLS: conjugate gradients on the least-squares problem min ||A x - y||_2 ----
+ * The solver the diffct documentation benchmarks ("Performance": time per CGLS
+ * iteration at 512^3) and ships ("API Reference" > "Numerical Solvers": cgls);
+ * its state is x, s, p (volume-shaped) and r, q (sinogram-shaped) with float64
+ * norms ("Large Volumes and Chunked Execution" > "Runnable iterative
+ * reconstruction").  The pages give no formula; the standard recurrence is:
+ *   start:  r = y - A x,  s = A^T r,  p = s,  gamma = ||s||^2
+ *   step:   q = A p,  alpha = gamma / ||q||^2,  x += alpha p,  r -= alpha q,
+ *           s = A^T r,  beta = ||s||^2 / gamma,  gamma = ||s||^2,  p = s + beta p
+ * (alpha = 0 when ||q|| = 0 and beta = 0 when gamma = 0, so a converged state
+ * stays put).  Vectors are float32; the norms are float64 sums in a fixed order
+ * and the scalars stay in the caller's workspace on the device, so a step
+ * needs no host round trip and its result is the same on every run.  Every
+ * buffer is device memory; none may overlap another of the call. */
+
+/* Bytes of device workspace (8-byte aligned) that ct_cgls_init/ct_cgls_step
+ * need for this geometry: 256 bytes of scalars plus one float64 per block of
+ * the largest launch. */
+ct_status_t ct_cgls_workspace_size(ct_geom_t g, size_t *bytes);
+
+/* Start: r = y - A x (x is the caller's initial volume, e.g. zeros), s = A^T r,
+ * p = s, and the scalars in work.  y, r: (views,U,V); x, s, p: (D,H,W). */
+ct_status_t ct_cgls_init(ct_geom_t g, const float *y, const float *x, float *r, float *s, float *p,
+                         void *work, ct_stream_t stream);
+
+/* One iteration, updating x, r, s, p, q and the scalars in work in place. */
+ct_status_t ct_cgls_step(ct_geom_t g, float *x, float *r, float *s, float *p, float *q, void *work,
+                         ct_stream_t stream);
+
+/* Copy the scalars to the host (synchronises the stream): out[0] = gamma =
+ * ||A^T r||^2, out[1] = alpha and out[2] = beta of the last step, out[3] =
+ * ||q||^2 of the last step, out[4] = ||r||^2. */
+ct_status_t ct_cgls_scalars(ct_geom_t g, const void *work, double out[5], ct_stream_t stream);
 
 /* Ray-voxel intersections: the number of (ray, voxel) pairs the traversal
  * visits, i.e. per ray the number of lattice-plane crossings inside the volume

@@ -30,7 +30,8 @@ CT_VIEW_TABLE_STRIDE = 40
 # every symbol declared in include/ctproj.h
 EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_destroy", "ct_geom_view_table",
            "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_sirt_weights",
-           "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_count_intersections",
+           "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_cgls_workspace_size",
+           "ct_cgls_init", "ct_cgls_step", "ct_cgls_scalars", "ct_count_intersections",
            "ct_last_error", "ct_version"]
 
 
@@ -72,6 +73,10 @@ def lib():
         L.ct_sirt_residual.argtypes = [vp, vp, vp, vp, vp, vp]
         L.ct_sirt_update.argtypes = [vp, vp, vp, c.c_float, vp, vp]
         L.ct_sirt_step.argtypes = [vp, vp, vp, vp, vp, c.c_float, vp, vp]
+        L.ct_cgls_workspace_size.argtypes = [vp, P(c.c_size_t)]
+        L.ct_cgls_init.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        L.ct_cgls_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        L.ct_cgls_scalars.argtypes = [vp, vp, P(c.c_double), vp]
         L.ct_count_intersections.argtypes = [vp, vp, P(c.c_uint64), vp]
         for name in EXPORTS[:-2]:
             getattr(L, name).restype = st
@@ -227,6 +232,43 @@ def ct_sirt_step(g: Geometry, x, y, row_inv, col_inv, relax, work_sino, stream=N
                               _ptr(col_inv, g.vol_shape, "col_inv"), float(relax),
                               _ptr(work_sino, g.sino_shape, "work_sino"), _stream(stream)))
     return x
+
+
+def ct_cgls_workspace_size(g: Geometry) -> int:
+    """Bytes of device workspace the CGLS calls need for this geometry."""
+    n = ctypes.c_size_t(0)
+    _check(lib().ct_cgls_workspace_size(g.handle, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _work_ptr(g: Geometry, work):
+    import torch
+    if not isinstance(work, torch.Tensor) or not work.is_cuda or not work.is_contiguous():
+        raise ValueError("work must be a contiguous device tensor")
+    if work.numel() * work.element_size() < ct_cgls_workspace_size(g):
+        raise ValueError("work is smaller than ct_cgls_workspace_size(g)")
+    return ctypes.c_void_p(work.data_ptr())
+
+
+def ct_cgls_init(g: Geometry, y, x, r, s, p, work, stream=None):
+    """CGLS start: r = y - A x, s = A^T r, p = s, scalars into work."""
+    _check(lib().ct_cgls_init(g.handle, _ptr(y, g.sino_shape, "y"), _ptr(x, g.vol_shape, "x"),
+                              _ptr(r, g.sino_shape, "r"), _ptr(s, g.vol_shape, "s"),
+                              _ptr(p, g.vol_shape, "p"), _work_ptr(g, work), _stream(stream)))
+
+
+def ct_cgls_step(g: Geometry, x, r, s, p, q, work, stream=None):
+    """One CGLS iteration on (x, r, s, p, q, work), in place."""
+    _check(lib().ct_cgls_step(g.handle, _ptr(x, g.vol_shape, "x"), _ptr(r, g.sino_shape, "r"),
+                              _ptr(s, g.vol_shape, "s"), _ptr(p, g.vol_shape, "p"),
+                              _ptr(q, g.sino_shape, "q"), _work_ptr(g, work), _stream(stream)))
+
+
+def ct_cgls_scalars(g: Geometry, work, stream=None) -> dict:
+    """gamma = ||A^T r||^2, alpha, beta, qq = ||q||^2 and rr = ||r||^2 (syncs the stream)."""
+    out = (ctypes.c_double * 5)()
+    _check(lib().ct_cgls_scalars(g.handle, _work_ptr(g, work), out, _stream(stream)))
+    return dict(zip(("gamma", "alpha", "beta", "qq", "rr"), list(out)))
 
 
 def ct_count_intersections(g: Geometry, per_ray=None, stream=None) -> int:

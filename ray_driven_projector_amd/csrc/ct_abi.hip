@@ -7,6 +7,7 @@
 // are rejected before execution").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cmath>
 #include <cstdlib>
@@ -344,6 +345,80 @@ ct_status_t ct_sirt_step(ct_geom_t g, float *x, const float *y, const float *row
     if (e != hipSuccess) return hip_fail(e, "ct_sirt_step residual launch");
     return launched(launch_sirt_update(lg(g), work_sino, col_inv, relax, x, (hipStream_t)stream),
                     "ct_sirt_step update launch");
+}
+
+// ---- CGLS ----
+
+static size_t cgls_partials(ct_geom_t g) {
+    const LaunchGeom l = lg(g);
+    size_t n = cgls_ray_blocks(l);
+    n = std::max(n, cgls_brick_blocks(l));
+    n = std::max(n, (size_t)kCglsVecBlocks);
+    return n;
+}
+
+ct_status_t ct_cgls_workspace_size(ct_geom_t g, size_t *bytes) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!bytes) return fail(CT_E_NULL, "bytes must be non-NULL");
+    *bytes = sizeof(double) * (kCglsStateDoubles + cgls_partials(g));
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_cgls_init(ct_geom_t g, const float *y, const float *x, float *r, float *s, float *p,
+                         void *work, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!y || !x || !r || !s || !p || !work) return fail(CT_E_NULL, "a buffer pointer is NULL");
+    if (((uintptr_t)work & 7u) != 0) return fail(CT_E_ARG, "work must be 8-byte aligned");
+    size_t wb = 0;
+    ct_cgls_workspace_size(g, &wb);
+    Span Y{y, sino_bytes(g)}, X{x, vol_bytes(g)}, R{r, sino_bytes(g)}, S{s, vol_bytes(g)},
+        P{p, vol_bytes(g)}, Wk{work, wb};
+    ct_status_t st = check_alias({{Y, false}, {X, false}, {R, true}, {S, true}, {P, true}, {Wk, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    double *state = (double *)work;
+    return launched(launch_cgls_init(lg(g), y, x, r, s, p, state, state + kCglsStateDoubles,
+                                     (hipStream_t)stream),
+                    "ct_cgls_init launch");
+}
+
+ct_status_t ct_cgls_step(ct_geom_t g, float *x, float *r, float *s, float *p, float *q, void *work,
+                         ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!x || !r || !s || !p || !q || !work) return fail(CT_E_NULL, "a buffer pointer is NULL");
+    if (((uintptr_t)work & 7u) != 0) return fail(CT_E_ARG, "work must be 8-byte aligned");
+    size_t wb = 0;
+    ct_cgls_workspace_size(g, &wb);
+    Span X{x, vol_bytes(g)}, R{r, sino_bytes(g)}, S{s, vol_bytes(g)}, P{p, vol_bytes(g)},
+        Q{q, sino_bytes(g)}, Wk{work, wb};
+    ct_status_t st = check_alias({{X, true}, {R, true}, {S, true}, {P, true}, {Q, true}, {Wk, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    double *state = (double *)work;
+    return launched(launch_cgls_step(lg(g), x, r, s, p, q, state, state + kCglsStateDoubles,
+                                     (hipStream_t)stream),
+                    "ct_cgls_step launch");
+}
+
+ct_status_t ct_cgls_scalars(ct_geom_t g, const void *work, double *out, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!work || !out) return fail(CT_E_NULL, "work and out must be non-NULL");
+    ct_status_t st = ensure_device(g);
+    if (st != CT_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    double host[kCglsStateDoubles];
+    hipError_t e = hipMemcpyAsync(host, work, sizeof host, hipMemcpyDeviceToHost, hs);
+    if (e != hipSuccess) return hip_fail(e, "ct_cgls_scalars copy");
+    e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return hip_fail(e, "ct_cgls_scalars sync");
+    out[0] = host[CS_GAMMA];
+    out[1] = host[CS_ALPHA];
+    out[2] = host[CS_BETA];
+    out[3] = host[CS_QQ];
+    out[4] = host[CS_RR];
+    set_error("");
+    return CT_OK;
 }
 
 ct_status_t ct_count_intersections(ct_geom_t g, uint32_t *per_ray, uint64_t *total, ct_stream_t stream) {

@@ -375,7 +375,12 @@ __device__ __forceinline__ float project_ray(double ox, double oy, double oz, do
 // ray-driven kernels (forward, SIRT residual, row sums, counting, atomic A^T)
 // ---------------------------------------------------------------------------
 
-enum RayMode : int { RM_PROJECT = 0, RM_RESIDUAL = 1, RM_ROWINV = 2, RM_COUNT = 3, RM_ATOMIC_BP = 4 };
+// RM_PROJECT_SQ: A p plus per-block sums of squares; RM_CGLS_R0: y - A x plus
+// per-block sums of squares (the CGLS start).
+enum RayMode : int {
+    RM_PROJECT = 0, RM_RESIDUAL = 1, RM_ROWINV = 2, RM_COUNT = 3, RM_ATOMIC_BP = 4,
+    RM_PROJECT_SQ = 5, RM_CGLS_R0 = 6
+};
 
 struct RayArgs {
     const double *views;
@@ -387,6 +392,7 @@ struct RayArgs {
     const float *rinv;         // RM_RESIDUAL
     uint32_t *counts;          // RM_COUNT (nullable)
     unsigned long long *total; // RM_COUNT
+    double *partial;           // RM_PROJECT_SQ, RM_CGLS_R0: one sum of squares per block
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
     int n_utiles, n_vtiles, n_blocks;
@@ -424,6 +430,9 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
     }
     const bool active = (u < a.U) && (v < a.V);
     uint32_t my_count = 0;
+    constexpr bool kFwd = MODE == RM_PROJECT || MODE == RM_RESIDUAL || MODE == RM_PROJECT_SQ ||
+                          MODE == RM_CGLS_R0;
+    double my_sq = 0.0;
     if (active) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
         const double fu = (double)u, fv = (double)v;
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
         double dy = vw[VT_D00 + 1] + fu * vw[VT_DU + 1] + fv * vw[VT_DV + 1];
         double dz = vw[VT_D00 + 2] + fu * vw[VT_DU + 2] + fv * vw[VT_DV + 2];
         const size_t ray = ((size_t)view * a.U + u) * a.V + v;
-        if (MODE == RM_PROJECT || MODE == RM_RESIDUAL) {
+        if (kFwd) {
             float acc = 0.f;
             double tin, tout;
             if (clip_ray(ox, oy, oz, dx, dy, dz, vw[VT_TMIN], vw[VT_TMAX], a.W, a.H, a.D, tin, tout)) {
@@ -448,8 +457,13 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
                 acc = project_ray(ox, oy, oz, dx, dy, dz, tin, tout, a.W, a.H, a.D, a.spx, a.spy,
                                   a.spz, ex, ey, ez, rs);
             }
-            if (MODE == RM_PROJECT) {
+            if (MODE == RM_PROJECT || MODE == RM_PROJECT_SQ) {
                 a.out[ray] = acc;
+                if (MODE == RM_PROJECT_SQ) my_sq = (double)acc * acc;
+            } else if (MODE == RM_CGLS_R0) {
+                const float r = a.sino[ray] - acc;
+                a.out[ray] = r;
+                my_sq = (double)r * r;
             } else {
                 a.out[ray] = a.rinv[ray] * (a.sino[ray] - acc);
             }
@@ -486,6 +500,15 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
         for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
         if (lane == 0 && c) atomicAdd(a.total, c);
     }
+    if (MODE == RM_PROJECT_SQ || MODE == RM_CGLS_R0) {
+        // fixed-order block sum (float64), one partial per block
+        __shared__ double wsum[4];
+        double q = my_sq;
+        for (int off = 32; off > 0; off >>= 1) q += __shfl_xor(q, off);
+        if (lane == 0) wsum[wv] = q;
+        __syncthreads();
+        if (threadIdx.x == 0) a.partial[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -497,17 +520,21 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
 // wave projects the brick's 8 corners onto the detector (their bounding box holds
 // every pixel whose ray meets the brick), then walks each of those rays through the
 // brick only, adding length * y into LDS.  After all views the brick is written
-// once: no global atomics (the order of the LDS adds still varies between runs).
+// once: no global atomics, and the integer LDS sums do not depend on the order of
+// the adds.
 //
 // Each ray is re-expressed per (view, brick) around the plane through the brick
 // centre parallel to the detector: for a flat detector the point where pixel
 // (u, v)'s ray meets that plane is affine in (u, v), so it is formed in float32
-// from a float64 anchor at the footprint's first pixel plus small integer offsets;
-// positions inside the walk then stay within tens of voxels of the brick and keep
-// float32 resolution near 1e-6 voxel.  Negative directions are mirrored so every
-// axis is walked upwards in the set-up arithmetic.
+// from a float64 anchor at the footprint's centre pixel plus small integer
+// offsets; positions are taken relative to the brick centre, so they stay within
+// about half a brick diagonal and keep float32 resolution near 1e-6 voxel.
+// Negative directions are mirrored about the brick centre so every axis is
+// walked upwards in the set-up arithmetic.
 
-enum BrickMode : int { BM_BACKPROJECT = 0, BM_SIRT_UPDATE = 1, BM_COLINV = 2 };
+// BM_CGLS: s = A^T r written out, per-brick sums of s^2, and optionally
+// x += alpha p (alpha read from the CGLS state) and p = s (the start).
+enum BrickMode : int { BM_BACKPROJECT = 0, BM_SIRT_UPDATE = 1, BM_COLINV = 2, BM_CGLS = 3 };
 
 struct BrickArgs {
     const double *views;
@@ -515,18 +542,23 @@ struct BrickArgs {
     float *vol;               // output (BM_SIRT_UPDATE: x, read-modify-write; BM_COLINV: col_inv)
     const float *cinv;        // BM_SIRT_UPDATE
     float relax;
+    float *x_upd;             // BM_CGLS: x += alpha p_old (nullable)
+    const float *p_old;       // BM_CGLS, with x_upd
+    float *p_copy;            // BM_CGLS: p = s (nullable)
+    const double *state;      // BM_CGLS: CGLS scalars (alpha)
+    double *partial;          // BM_CGLS: one sum of s^2 per brick
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
     int nbx, nby, nbz, n_blocks;
 };
 
-// Slab clip of an axis the ray does not move along (a = 0): the ray is inside
-// for every t iff 0 <= o < e.  Replaces (o, 1/a) by stand-ins for which the
-// general formulas lo = -o/a, hi = (e - o)/a give an unbounded interval (inside)
-// or an empty one (outside).
-__device__ __forceinline__ void bclip_zero(float o, float a, float e, float &co, float &cinv) {
+// Slab clip of an axis the ray does not move along (a = 0), in brick-centred
+// coordinates: the ray is inside for every t iff -h <= o < h.  Replaces (o, 1/a)
+// by stand-ins for which the general formulas lo = (-h - o)/a, hi = lo + 2h/a
+// give an unbounded interval (inside) or an empty one (outside).
+__device__ __forceinline__ void bclip_zero(float o, float a, float h, float &co, float &cinv) {
     if (a == 0.f) {
-        co = (o >= 0.f && o < e) ? 0.5f * e : -1.f;
+        co = (o >= -h && o < h) ? 0.f : -h - 1.f;
         cinv = 1e35f;
     }
 }
@@ -539,17 +571,32 @@ __device__ __forceinline__ uint32_t sat_u32(float x) {
     return r;
 }
 
-// Crossing plan of one mirrored (non-negative direction) axis of extent e for a
-// walk entering at tin: entry cell fe (float), the fixed-point position l0 of
-// the first crossing, and far = the position of the crossing of the brick's far
-// face, l0 + (e - 1 - fe) q, saturating.  A walk that ends at or before far takes
-// at most e - 1 - fe crossings of this axis, so it never leaves the brick.
-__device__ __forceinline__ void baxis(float o, float a, float tin, float em1, float qf, uint32_t q,
-                                      float &fe, uint32_t &l0, uint32_t &far) {
-    const float E = fmaf(tin, a, o);
-    fe = __builtin_amdgcn_fmed3f(floorf(E), 0.f, em1);
-    l0 = sat_u32((fe + 1.f - E) * qf);
+// Crossing plan of one mirrored (non-negative direction) axis of extent e =
+// 2h, in brick-centred coordinates, for a walk entering at tin: entry cell fe
+// (float), the fixed-point position l0 of the first crossing, and far = the
+// position of the crossing of the brick's far face, l0 + (e - 1 - fe) q,
+// saturating.  A walk that ends at or before far takes at most e - 1 - fe
+// crossings of this axis, so it never leaves the brick.
+__device__ __forceinline__ void baxis(float o, float a, float tin, float h, float em1, float qf,
+                                      uint32_t q, float &fe, uint32_t &l0, uint32_t &far) {
+    const float E = fmaf(tin, a, o);   // entry coordinate, centred
+    fe = __builtin_amdgcn_fmed3f(floorf(E + h), 0.f, em1);
+    l0 = sat_u32(((fe + 1.f - h) - E) * qf);
     far = last_plus_one(l0, sat_u32(em1 - fe), q);
+}
+
+// Block sum of one float64 per thread in a fixed order; the result is valid in
+// thread 0.  wsum: one slot per wave.
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double *wsum) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (lane == 0) wsum[wv] = v;
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x == 0)
+        for (int k = 0; k < NT / 64; ++k) t += wsum[k];
+    return t;
 }
 
 // Footprint of the brick [x0, x0+ex) x [y0, y0+ey) x [z0, z0+ez) on the detector of
@@ -665,15 +712,19 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
                                            double cbz, float S, float yscale,
                                            unsigned long long *acc) {
     const float fex = (float)ex, fey = (float)ey, fez = (float)ez;
+    const float hx = 0.5f * fex, hy = 0.5f * fey, hz = 0.5f * fez;
     const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
     const int u0 = f.u0, v0 = f.v0;
     const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
     const bool ufast = !TWO_D && vw[VT_PATCH] == 0.0;
     const int nf = ufast ? nfu : nfv;
 
-    // ---- per (view, brick) ray parametrisation, anchored at (u0, v0) ----
+    // ---- per (view, brick) ray parametrisation, anchored at the footprint's
+    // centre pixel (u0 + cu, v0 + cv), so pixel offsets stay within half the
+    // footprint; positions are relative to the brick centre ----
+    const int cu = nfu / 2, cv = nfv / 2;
     const double nx_ = vw[VT_N + 0], ny_ = vw[VT_N + 1], nz_ = vw[VT_N + 2];
-    const double fu0 = u0, fv0 = v0;
+    const double fu0 = u0 + cu, fv0 = v0 + cv;
     const double aox = vw[VT_O00 + 0] + fu0 * vw[VT_OU + 0] + fv0 * vw[VT_OV + 0];
     const double aoy = vw[VT_O00 + 1] + fu0 * vw[VT_OU + 1] + fv0 * vw[VT_OV + 1];
     const double aoz = vw[VT_O00 + 2] + fu0 * vw[VT_OU + 2] + fv0 * vw[VT_OV + 2];
@@ -686,9 +737,9 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     // per-pixel steps along the footprint's fast (f) and slow (s) axes
     const int pf = ufast ? VT_OU : VT_OV, ps = ufast ? VT_OV : VT_OU;
     const int qf_ = ufast ? VT_DU : VT_DV, qs_ = ufast ? VT_DV : VT_DU;
-    const float A0x = uni((float)(aox + tb * adx - x0));
-    const float A0y = uni((float)(aoy + tb * ady - y0));
-    const float A0z = uni((float)(aoz + tb * adz - z0));
+    const float A0x = uni((float)(aox + tb * adx - cbx));
+    const float A0y = uni((float)(aoy + tb * ady - cby));
+    const float A0z = uni((float)(aoz + tb * adz - cbz));
     const float Afx = uni((float)(vw[pf + 0] + tb * vw[qf_ + 0]));
     const float Afy = uni((float)(vw[pf + 1] + tb * vw[qf_ + 1]));
     const float Afz = uni((float)(vw[pf + 2] + tb * vw[qf_ + 2]));
@@ -704,13 +755,15 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     const float *ysrc = a.sino + ((size_t)view * a.U + u0) * a.V + v0;
     const uint32_t yfs = ufast ? a.V : 1, yss = ufast ? 1 : a.V;   // sinogram strides, fast / slow
 
-    // footprint position of ray r (fast index ff, slow index fs, sinogram offset
-    // yo), advanced by 64 rays per round
+    // footprint position of ray r (fast and slow offsets ff, fs from the anchor,
+    // sinogram offset yo from (u0, v0)), advanced by 64 rays per round
     const int step_slow = 64 / nf, step_fast = 64 - step_slow * nf;
     const uint32_t yo_step = step_fast * yfs + step_slow * yss, yo_wrap = yss - nf * yfs;
-    const float fnf = (float)nf, fstep_fast = (float)step_fast, fstep_slow = (float)step_slow;
+    const float af = (float)(ufast ? cu : cv), as_ = (float)(ufast ? cv : cu);
+    const float fnf = (float)nf, fend = fnf - af;
+    const float fstep_fast = (float)step_fast, fstep_slow = (float)step_slow;
     const int ls = lane / nf, lf = lane - ls * nf;
-    float ff = (float)lf, fs = (float)ls;
+    float ff = (float)lf - af, fs = (float)ls - as_;
     uint32_t yo = lf * yfs + ls * yss;
     float ynext = 1.f;
     if (MODE != BM_COLINV && lane < nrays) ynext = ysrc[yo];
@@ -719,7 +772,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         ff += fstep_fast;
         fs += fstep_slow;
         yo += yo_step;
-        if (ff >= fnf) { ff -= fnf; fs += 1.f; yo += yo_wrap; }
+        if (ff >= fend) { ff -= fnf; fs += 1.f; yo += yo_wrap; }
         const float yv = ynext;
         if (MODE != BM_COLINV && r + 64 < nrays) ynext = ysrc[yo];
         if (yv == 0.f) continue;
@@ -744,24 +797,25 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
             if (fabsf(dy) < dm) dy = 0.f;
             if (!TWO_D && fabsf(dz) < dm) dz = 0.f;
         }
-        // mirror negative directions: walk every axis upwards
+        // mirror negative directions about the brick centre: walk every axis upwards
         const bool nx = dx < 0.f, ny = dy < 0.f, nz = dz < 0.f;
-        const float mx = nx ? fex - ox : ox, axx = fabsf(dx);
-        const float my = ny ? fey - oy : oy, ayy = fabsf(dy);
-        const float mz = nz ? fez - oz : oz, azz = fabsf(dz);
+        const float mx = nx ? -ox : ox, axx = fabsf(dx);
+        const float my = ny ? -oy : oy, ayy = fabsf(dy);
+        const float mz = nz ? -oz : oz, azz = fabsf(dz);
         const float ix = __builtin_amdgcn_rcpf(axx);
         const float iy = __builtin_amdgcn_rcpf(ayy);
         const float iz = TWO_D ? 0.f : __builtin_amdgcn_rcpf(azz);
-        // slab clip: lo = -m / a, hi = (e - m) / a
+        // slab clip: lo = (-h - m) / a, hi = (h - m) / a
         float cx = mx, cy = my, cz = mz, cix = ix, ciy = iy, ciz = iz;
         if (slow) {
-            bclip_zero(mx, axx, fex, cx, cix);
-            bclip_zero(my, ayy, fey, cy, ciy);
-            if (!TWO_D) bclip_zero(mz, azz, fez, cz, ciz);
+            bclip_zero(mx, axx, hx, cx, cix);
+            bclip_zero(my, ayy, hy, cy, ciy);
+            if (!TWO_D) bclip_zero(mz, azz, hz, cz, ciz);
         }
-        const float lox = -cx * cix, hix = fmaf(fex, cix, lox);
-        const float loy = -cy * ciy, hiy = fmaf(fey, ciy, loy);
-        const float loz = TWO_D ? -3e38f : -cz * ciz, hiz = TWO_D ? 3e38f : fmaf(fez, ciz, loz);
+        const float lox = (-hx - cx) * cix, hix = fmaf(fex, cix, lox);
+        const float loy = (-hy - cy) * ciy, hiy = fmaf(fey, ciy, loy);
+        const float loz = TWO_D ? -3e38f : (-hz - cz) * ciz;
+        const float hiz = TWO_D ? 3e38f : fmaf(fez, ciz, loz);
         const float tin = fmaxf(fmaxf(fmaxf(lox, loy), loz), t0);
         const float tout = fminf(fminf(fminf(hix, hiy), hiz), t1);
         if (!(tin < tout)) continue;
@@ -774,9 +828,9 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         w.qz = TWO_D ? 0xFFFFFFFFu : sat_u32(qfz);
         float fcx, fcy, fcz = 0.f;
         uint32_t farx, fary, farz = 0xFFFFFFFFu;
-        baxis(mx, axx, tin, fex - 1.f, qfx, w.qx, fcx, w.lx, farx);
-        baxis(my, ayy, tin, fey - 1.f, qfy, w.qy, fcy, w.ly, fary);
-        if (!TWO_D) baxis(mz, azz, tin, fez - 1.f, qfz, w.qz, fcz, w.lz, farz);
+        baxis(mx, axx, tin, hx, fex - 1.f, qfx, w.qx, fcx, w.lx, farx);
+        baxis(my, ayy, tin, hy, fey - 1.f, qfy, w.qy, fcy, w.ly, fary);
+        if (!TWO_D) baxis(mz, azz, tin, hz, fez - 1.f, qfz, w.qz, fcz, w.lz, farz);
         else w.lz = 0xFFFFFFFFu;
         // the walk ends at the ray's own end (a segment may stop inside the
         // brick) or at the first far-face crossing, whichever comes first
@@ -865,6 +919,8 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
     }
     __syncthreads();
     const double inv_scale = 1.0 / ((double)S * (double)yscale);
+    const float alpha = (MODE == BM_CGLS && a.x_upd) ? (float)a.state[CS_ALPHA] : 0.f;
+    double sq = 0.0;
     for (int i = threadIdx.x; i < BX * BY * BZ; i += NT) {
         const int lx = i % BX, ly = (i / BX) % BY, lz = i / (BX * BY);
         if (lx < ex && ly < ey && lz < ez) {
@@ -874,11 +930,22 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
                 a.vol[g] = val;
             } else if (MODE == BM_SIRT_UPDATE) {
                 a.vol[g] = fmaf(a.relax * a.cinv[g], val, a.vol[g]);
+            } else if (MODE == BM_CGLS) {
+                a.vol[g] = val;
+                sq += (double)val * val;
+                if (a.p_copy) a.p_copy[g] = val;
+                if (a.x_upd) a.x_upd[g] = fmaf(alpha, a.p_old[g], a.x_upd[g]);
             } else {
                 const float r = val > 0.f ? 1.0f / val : 0.f;
                 a.vol[g] = isfinite(r) ? r : 0.f;
             }
         }
+    }
+    if (MODE == BM_CGLS) {
+        // fixed-order block sum (float64), one partial per brick
+        __shared__ double wsq[NWAVES];
+        const double t = block_sum<NT>(sq, wsq);
+        if (threadIdx.x == 0) a.partial[blockIdx.x] = t;
     }
 }
 
@@ -910,6 +977,94 @@ __global__ void fill_kernel(float *p, size_t n, float v) {
 }
 
 __global__ void zero_u64_kernel(unsigned long long *p) { *p = 0ull; }
+
+// ---------------------------------------------------------------------------
+// CGLS vector steps (diffct docs, "Large Volumes and Chunked Execution" >
+// "Runnable iterative reconstruction": state x, s, p and r, q, float64 norms).
+// Scalars live in device memory, so an iteration needs no host round trip.
+// ---------------------------------------------------------------------------
+
+// Sum the per-block partials (fixed order) and derive the scalars of one step:
+//   CO_RR    rr = ||r||^2
+//   CO_INIT  gamma = ||s||^2
+//   CO_ALPHA qq = ||q||^2, alpha = gamma / qq (0 if qq = 0)
+//   CO_BETA  beta = ||s||^2 / gamma (0 if gamma = 0), then gamma = ||s||^2
+__global__ __launch_bounds__(1024) void cgls_finalize_kernel(const double *__restrict__ partial, int n,
+                                                             double *state, int op) {
+    __shared__ double wsum[16];
+    double v = 0.0;
+    for (int i = threadIdx.x; i < n; i += 1024) v += partial[i];
+    const double t = block_sum<1024>(v, wsum);
+    if (threadIdx.x == 0) {
+        if (op == CO_RR) {
+            state[CS_RR] = t;
+        } else if (op == CO_INIT) {
+            state[CS_GAMMA] = t;
+            state[CS_ALPHA] = 0.0;
+            state[CS_BETA] = 0.0;
+        } else if (op == CO_ALPHA) {
+            state[CS_QQ] = t;
+            state[CS_ALPHA] = t > 0.0 ? state[CS_GAMMA] / t : 0.0;
+        } else {
+            const double g = state[CS_GAMMA];
+            state[CS_BETA] = g > 0.0 ? t / g : 0.0;
+            state[CS_GAMMA] = t;
+        }
+    }
+}
+
+// r -= alpha q, with per-block sums of the new r^2.
+__global__ __launch_bounds__(256) void cgls_update_r_kernel(float *__restrict__ r,
+                                                            const float *__restrict__ q, size_t n,
+                                                            bool vec, const double *state,
+                                                            double *partial) {
+    __shared__ double wsum[4];
+    const float alpha = (float)state[CS_ALPHA];
+    const size_t n4 = vec ? n / 4 : 0;   // vec: both buffers 16-byte aligned
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    double sq = 0.0;
+    float4 *r4 = reinterpret_cast<float4 *>(r);
+    const float4 *q4 = reinterpret_cast<const float4 *>(q);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 a = r4[i];
+        const float4 b = q4[i];
+        a.x = fmaf(-alpha, b.x, a.x);
+        a.y = fmaf(-alpha, b.y, a.y);
+        a.z = fmaf(-alpha, b.z, a.z);
+        a.w = fmaf(-alpha, b.w, a.w);
+        r4[i] = a;
+        sq += ((double)a.x * a.x + (double)a.y * a.y) + ((double)a.z * a.z + (double)a.w * a.w);
+    }
+    for (size_t i = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float v = fmaf(-alpha, q[i], r[i]);
+        r[i] = v;
+        sq += (double)v * v;
+    }
+    const double t = block_sum<256>(sq, wsum);
+    if (threadIdx.x == 0) partial[blockIdx.x] = t;
+}
+
+// p = s + beta p.
+__global__ __launch_bounds__(256) void cgls_update_p_kernel(float *__restrict__ p,
+                                                            const float *__restrict__ s, size_t n,
+                                                            bool vec, const double *state) {
+    const float beta = (float)state[CS_BETA];
+    const size_t n4 = vec ? n / 4 : 0;   // vec: both buffers 16-byte aligned
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    float4 *p4 = reinterpret_cast<float4 *>(p);
+    const float4 *s4 = reinterpret_cast<const float4 *>(s);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 a = p4[i];
+        const float4 b = s4[i];
+        a.x = fmaf(beta, a.x, b.x);
+        a.y = fmaf(beta, a.y, b.y);
+        a.z = fmaf(beta, a.z, b.z);
+        a.w = fmaf(beta, a.w, b.w);
+        p4[i] = a;
+    }
+    for (size_t i = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        p[i] = fmaf(beta, p[i], s[i]);
+}
 
 // ---------------------------------------------------------------------------
 // launchers
@@ -1029,14 +1184,8 @@ static void launch_brick_shape(BrickArgs &a, const LaunchGeom &g, hipStream_t s)
 }
 
 template <int MODE>
-static hipError_t launch_brick(const LaunchGeom &g, const float *sino, float *vol,
-                               const float *cinv, float relax, hipStream_t s) {
-    BrickArgs a{};
+static hipError_t launch_brick_args(const LaunchGeom &g, BrickArgs a, hipStream_t s) {
     a.views = g.views;
-    a.sino = sino;
-    a.vol = vol;
-    a.cinv = cinv;
-    a.relax = relax;
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
     if (g.two_d) {
@@ -1055,6 +1204,17 @@ static hipError_t launch_brick(const LaunchGeom &g, const float *sino, float *vo
     return hipGetLastError();
 }
 
+template <int MODE>
+static hipError_t launch_brick(const LaunchGeom &g, const float *sino, float *vol,
+                               const float *cinv, float relax, hipStream_t s) {
+    BrickArgs a{};
+    a.sino = sino;
+    a.vol = vol;
+    a.cinv = cinv;
+    a.relax = relax;
+    return launch_brick_args<MODE>(g, a, s);
+}
+
 hipError_t launch_backproject(const LaunchGeom &g, const float *sino, float *vol, hipStream_t s) {
     return launch_brick<BM_BACKPROJECT>(g, sino, vol, nullptr, 0.f, s);
 }
@@ -1066,6 +1226,86 @@ hipError_t launch_sirt_update(const LaunchGeom &g, const float *e, const float *
 
 hipError_t launch_colinv(const LaunchGeom &g, float *cinv, hipStream_t s) {
     return launch_brick<BM_COLINV>(g, nullptr, cinv, nullptr, 0.f, s);
+}
+
+// ---- CGLS ----
+
+size_t cgls_ray_blocks(const LaunchGeom &g) { return (size_t)ray_args(g).n_blocks; }
+
+size_t cgls_brick_blocks(const LaunchGeom &g) {
+    int bx = 16, by = 16, bz = 16;
+    if (g.two_d) { bx = 64; by = 64; bz = 1; }
+    else if (g.brick_shape == 1) { bx = 32; by = 32; bz = 16; }
+    else if (g.brick_shape == 2) { bx = 32; by = 16; bz = 16; }
+    else if (g.brick_shape == 3) { bx = 32; by = 16; bz = 32; }
+    else if (g.brick_shape == 4) { bx = 32; by = 32; bz = 8; }
+    return (size_t)((g.W + bx - 1) / bx) * ((g.H + by - 1) / by) * ((g.D + bz - 1) / bz);
+}
+
+static hipError_t cgls_finalize(const double *partial, size_t n, double *state, int op, hipStream_t s) {
+    hipLaunchKernelGGL(cgls_finalize_kernel, dim3(1), dim3(1024), 0, s, partial, (int)n, state, op);
+    return hipGetLastError();
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+hipError_t launch_cgls_init(const LaunchGeom &g, const float *y, const float *x, float *r, float *sv,
+                            float *p, double *state, double *partial, hipStream_t s) {
+    // r = y - A x, rr = ||r||^2
+    RayArgs ra = ray_args(g);
+    hipError_t e = stage_layouts(g, x, ra, s);
+    if (e != hipSuccess) return e;
+    ra.vol = x;
+    ra.sino = y;
+    ra.out = r;
+    ra.partial = partial;
+    if ((e = launch_ray<RM_CGLS_R0>(g, ra, s)) != hipSuccess) return e;
+    if ((e = cgls_finalize(partial, (size_t)ra.n_blocks, state, CO_RR, s)) != hipSuccess) return e;
+    // s = A^T r, p = s, gamma = ||s||^2
+    BrickArgs b{};
+    b.sino = r;
+    b.vol = sv;
+    b.p_copy = p;
+    b.state = state;
+    b.partial = partial;
+    if ((e = launch_brick_args<BM_CGLS>(g, b, s)) != hipSuccess) return e;
+    return cgls_finalize(partial, cgls_brick_blocks(g), state, CO_INIT, s);
+}
+
+hipError_t launch_cgls_step(const LaunchGeom &g, float *x, float *r, float *sv, float *p, float *q,
+                            double *state, double *partial, hipStream_t s) {
+    // q = A p, alpha = gamma / ||q||^2
+    RayArgs ra = ray_args(g);
+    hipError_t e = stage_layouts(g, p, ra, s);
+    if (e != hipSuccess) return e;
+    ra.vol = p;
+    ra.out = q;
+    ra.partial = partial;
+    if ((e = launch_ray<RM_PROJECT_SQ>(g, ra, s)) != hipSuccess) return e;
+    if ((e = cgls_finalize(partial, (size_t)ra.n_blocks, state, CO_ALPHA, s)) != hipSuccess) return e;
+    // r -= alpha q, rr = ||r||^2
+    const size_t m = (size_t)g.n_views * g.U * g.V;
+    const bool vr = aligned16(r) && aligned16(q);
+    hipLaunchKernelGGL(cgls_update_r_kernel, dim3(kCglsVecBlocks), dim3(256), 0, s, r, q, m, vr,
+                       (const double *)state, partial);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = cgls_finalize(partial, kCglsVecBlocks, state, CO_RR, s)) != hipSuccess) return e;
+    // s = A^T r and x += alpha p (old p) in the brick write-out; beta, gamma
+    BrickArgs b{};
+    b.sino = r;
+    b.vol = sv;
+    b.x_upd = x;
+    b.p_old = p;
+    b.state = state;
+    b.partial = partial;
+    if ((e = launch_brick_args<BM_CGLS>(g, b, s)) != hipSuccess) return e;
+    if ((e = cgls_finalize(partial, cgls_brick_blocks(g), state, CO_BETA, s)) != hipSuccess) return e;
+    // p = s + beta p
+    const size_t n = (size_t)g.W * g.H * g.D;
+    const bool vp = aligned16(p) && aligned16(sv);
+    hipLaunchKernelGGL(cgls_update_p_kernel, dim3(kCglsVecBlocks), dim3(256), 0, s, p,
+                       (const float *)sv, n, vp, (const double *)state);
+    return hipGetLastError();
 }
 
 }  // namespace ctp

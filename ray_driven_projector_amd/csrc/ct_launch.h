@@ -33,4 +33,17 @@ hipError_t launch_sirt_update(const LaunchGeom &g, const float *e, const float *
                               float *x, hipStream_t s);
 hipError_t launch_colinv(const LaunchGeom &g, float *cinv, hipStream_t s);
 
+// CGLS.  Workspace: kCglsStateDoubles scalars, then one float64 partial per
+// block of the largest launch (forward blocks, bricks or kCglsVecBlocks).
+enum CglsSlot : int { CS_GAMMA = 0, CS_ALPHA = 1, CS_BETA = 2, CS_QQ = 3, CS_RR = 4 };
+enum CglsOp : int { CO_RR = 0, CO_INIT = 1, CO_ALPHA = 2, CO_BETA = 3 };
+constexpr int kCglsStateDoubles = 32;   // 256 bytes
+constexpr unsigned kCglsVecBlocks = 4096;
+size_t cgls_ray_blocks(const LaunchGeom &g);
+size_t cgls_brick_blocks(const LaunchGeom &g);
+hipError_t launch_cgls_init(const LaunchGeom &g, const float *y, const float *x, float *r, float *s,
+                            float *p, double *state, double *partial, hipStream_t st);
+hipError_t launch_cgls_step(const LaunchGeom &g, float *x, float *r, float *s, float *p, float *q,
+                            double *state, double *partial, hipStream_t st);
+
 }  // namespace ctp
