@@ -14,7 +14,10 @@ in G/s; ms_per_step is the time of one SIRT iteration.  --workload c5 instead
 times A + A^T (ct_project + ct_backproject) on the 512^3 jittered circular
 cone (720 views, 1024 x 768); its A^T input is a dense seeded sinogram (every
 ray nonzero), since rays whose value is 0 add nothing and are skipped by the
-adjoint, which would make a sparse sinogram look faster.
+adjoint, which would make a sparse sinogram look faster.  --workload c4cgls /
+c5cgls time CGLS iterations (ct_cgls_step: A p with ||q||^2, r -= alpha q,
+A^T r with ||s||^2 and x += alpha p, p = s + beta p) on the same workloads
+from y = A phantom, after ct_cgls_init.
 
 Roofline: algorithmic HBM bytes of the dominant kernel per launch divided by
 its average duration (HIP events on the launch stream), against 8 TB/s.
@@ -91,7 +94,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["c4", "c5"], default="c4")
+    ap.add_argument("--workload", choices=["c4", "c5", "c4cgls", "c5cgls"], default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-views", type=int, default=16)
     ap.add_argument("--extra", action="store_true", help="also time A, A^T and atomic A^T alone")
@@ -121,7 +124,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cfg = 4 if args.workload == "c4" else 5
+    cfg = 4 if args.workload.startswith("c4") else 5
+    cgls = args.workload.endswith("cgls")
     wl = W.make_workload(cfg)
     print(f"# workload: {wl.name}", file=sys.stderr, flush=True)
     phantom = W.make_phantom(wl)
@@ -135,7 +139,26 @@ def main():
     print(f"# nnz={nnz} rays={M} voxels={N}", file=sys.stderr, flush=True)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    if cfg == 4:
+    if cgls:
+        x = torch.zeros(g.vol_shape, device="cuda")
+        r = torch.empty(g.sino_shape, device="cuda")
+        q = torch.empty(g.sino_shape, device="cuda")
+        s_ = torch.empty(g.vol_shape, device="cuda")
+        p_ = torch.empty(g.vol_shape, device="cuda")
+        work = torch.empty(rdp.ct_cgls_workspace_size(g), dtype=torch.uint8, device="cuda")
+        rdp.ct_cgls_init(g, y, x, r, s_, p_, work, stream)
+        names = ("cgls_step", "none")
+        # forward (A p, ||q||^2) + r update + adjoint (A^T r, ||s||^2, x update) + p update
+        bytes_per = {"cgls_step": (4 * nnz + 4 * M) + 12 * M + (4 * nnz + 4 * M + 16 * N) + 12 * N,
+                     "none": 0}
+        kern_names = {"cgls_step": "one CGLS iteration (all kernels)", "none": ""}
+
+        def step(evs):
+            evs[0].record(stream)
+            rdp.ct_cgls_step(g, x, r, s_, p_, q, work, stream)
+            evs[1].record(stream)
+            evs[2].record(stream)
+    elif cfg == 4:
         rinv = torch.empty(g.sino_shape, device="cuda")
         cinv = torch.empty(g.vol_shape, device="cuda")
         rdp.ct_sirt_weights(g, rinv, cinv)
@@ -186,6 +209,8 @@ def main():
         k_ms[names[1]].append(e[1].elapsed_time(e[2]))
     ms_step = (t1 - t0) * 1e3 / args.steps
     avg = {k: float(np.mean(v)) for k, v in k_ms.items()}
+    if cgls:
+        avg.pop("none")
     dom = max(avg, key=avg.get)
     achieved = bytes_per[dom] / (avg[dom] * 1e-3)
     value = 2 * nnz / (ms_step * 1e-3) / 1e9
@@ -222,12 +247,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": (wl.name + (", one SIRT iteration (A with residual + A^T with update)"
+            "workload": (wl.name + (", one CGLS iteration (from y = A phantom)" if cgls else
+                                    ", one SIRT iteration (A with residual + A^T with update)"
                                     if cfg == 4 else ", A + A^T")),
             "volume": list(wl.vol_shape), "views": wl.n_views, "detector": list(wl.det_shape),
             "intersections_per_pass": nnz, "rays": M, "voxels": N,
         },
-        "ms_per_sirt_iteration": round(ms_step, 3) if cfg == 4 else None,
+        "ms_per_sirt_iteration": round(ms_step, 3) if (cfg == 4 and not cgls) else None,
+        "ms_per_cgls_iteration": round(ms_step, 3) if cgls else None,
         "kernel_ms": {k: round(v, 3) for k, v in avg.items()},
         "roofline": {
             "bound": "hbm", "kernel": kern_names[dom], "achieved": round(achieved / 1e9, 1),
