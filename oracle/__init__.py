@@ -204,13 +204,22 @@ def sirt_weights(g: Geometry, nthreads: int | None = None):
 
 
 def sirt(g: Geometry, y, x0=None, n_iter: int = 1, relax: float = 1.0,
-         weights=None, nthreads: int | None = None) -> np.ndarray:
+         weights=None, nthreads: int | None = None, lo: float = -np.inf, hi: float = np.inf,
+         mask=None) -> np.ndarray:
+    """SIRT; with lo/hi/mask the bounded, masked variant of the ASTRA options
+    printed in the ASTRA guide (MinConstraint, MaxConstraint, ReconstructionMask):
+    after each update x is clipped to [lo, hi], and voxels where mask == 0 keep
+    their previous value."""
     y = _as64(y).reshape(g.sino_shape)
     x = np.zeros(g.vol_shape) if x0 is None else _as64(x0).reshape(g.vol_shape).copy()
     R, C = weights if weights is not None else sirt_weights(g, nthreads)
     for _ in range(n_iter):
         e = R * (y - project(g, x, nthreads))
-        x = x + relax * C * backproject(g, e, nthreads)
+        xn = x + relax * C * backproject(g, e, nthreads)
+        xn = np.clip(xn, lo, hi)
+        if mask is not None:
+            xn = np.where(np.asarray(mask).reshape(g.vol_shape) != 0, xn, x)
+        x = xn
     return x
 
 

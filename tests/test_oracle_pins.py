@@ -396,3 +396,33 @@ def test_cgls_residual_recurrence_and_monotone_norm():
     # the recurrence-updated residual is the true residual
     r = y - oracle.project(g, x)
     assert abs(float(np.sum(r * r)) - rr[-1]) <= 1e-9 * rr[0]
+
+
+def test_bounded_masked_sirt_dense_iteration_and_invariants():
+    # the bounded, masked update against a dense-matrix iteration (A from the
+    # per-cell brute-force chords), plus the invariants it must keep
+    wl = _tiny(W.BEAM_FAN2D, 11, vol=(1, 12, 12), det=(20, 1), views=10)
+    g = oracle.Geometry.from_workload(wl)
+    A = oracle.brute_matrix(g)
+    rs, cs = A.sum(1), A.sum(0)
+    R = np.where(rs > 0, 1 / np.where(rs > 0, rs, 1), 0)
+    C = np.where(cs > 0, 1 / np.where(cs > 0, cs, 1), 0)
+    rng = np.random.default_rng(4)
+    yb = rng.uniform(0, 3, wl.sino_shape).ravel()
+    mask = (rng.uniform(size=wl.vol_shape) < 0.7).astype(np.uint8)
+    x0 = rng.uniform(0, 0.5, wl.vol_shape)
+    xd = x0.ravel().copy()
+    for _ in range(4):
+        xn = np.clip(xd + 0.8 * C * (A.T @ (R * (yb - A @ xd))), 0.1, 0.6)
+        xd = np.where(mask.ravel() != 0, xn, xd)
+    xo = oracle.sirt(g, yb, x0=x0, n_iter=4, relax=0.8, lo=0.1, hi=0.6, mask=mask)
+    np.testing.assert_allclose(xo.ravel(), xd, rtol=1e-11, atol=1e-12)
+    # invariants: masked-out voxels keep x0, updated voxels lie in the bounds, and
+    # the bounds are active somewhere
+    assert np.array_equal(xo[mask == 0], x0[mask == 0])
+    upd = xo[mask != 0]
+    assert upd.min() >= 0.1 and upd.max() <= 0.6
+    assert np.any(upd == 0.1) or np.any(upd == 0.6)
+    # unbounded and unmasked: the plain iteration
+    np.testing.assert_array_equal(oracle.sirt(g, yb, x0=x0, n_iter=2),
+                                  oracle.sirt(g, yb, x0=x0, n_iter=2, lo=-np.inf, hi=np.inf, mask=None))
