@@ -177,6 +177,23 @@ ct_status_t ct_sirt_update(ct_geom_t g, const float *work_sino, const float *col
 ct_status_t ct_sirt_step(ct_geom_t g, float *x, const float *y, const float *row_inv,
                          const float *col_inv, float relax, float *work_sino, ct_stream_t stream);
 
+/* Bounded and masked SIRT (the box constraints and reconstruction mask of the
+ * ASTRA SART/SIRT options printed in the ASTRA guide: MinConstraint,
+ * MaxConstraint, ReconstructionMask).  The update becomes
+ *   x_j <- min(max(x_j + relax * col_inv_j * (A^T work_sino)_j, lo), hi)
+ * for voxels with mask[j] != 0, while voxels with mask[j] == 0 keep their value
+ * (mask: device uint8, volume-shaped, or NULL for all voxels).  lo <= hi; either
+ * may be infinite.  A brick with no masked voxel is skipped entirely. */
+ct_status_t ct_sirt_update_bounded(ct_geom_t g, const float *work_sino, const float *col_inv,
+                                   float relax, float lo, float hi, const uint8_t *mask, float *x,
+                                   ct_stream_t stream);
+
+/* One bounded/masked SIRT iteration: ct_sirt_residual then
+ * ct_sirt_update_bounded, stream-ordered. */
+ct_status_t ct_sirt_step_bounded(ct_geom_t g, float *x, const float *y, const float *row_inv,
+                                 const float *col_inv, float relax, float lo, float hi,
+                                 const uint8_t *mask, float *work_sino, ct_stream_t stream);
+
 /* ---- CGLS: conjugate gradients on the least-squares problem min ||A x - y||_2 ----
  * The solver the diffct documentation benchmarks ("Performance": time per CGLS
  * iteration at 512^3) and ships ("API Reference" > "Numerical Solvers": cgls);

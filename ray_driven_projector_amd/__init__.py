@@ -30,7 +30,8 @@ CT_VIEW_TABLE_STRIDE = 40
 # every symbol declared in include/ctproj.h
 EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_destroy", "ct_geom_view_table",
            "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_sirt_weights",
-           "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_cgls_workspace_size",
+           "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_sirt_update_bounded",
+           "ct_sirt_step_bounded", "ct_cgls_workspace_size",
            "ct_cgls_init", "ct_cgls_step", "ct_cgls_scalars", "ct_count_intersections",
            "ct_last_error", "ct_version"]
 
@@ -73,6 +74,9 @@ def lib():
         L.ct_sirt_residual.argtypes = [vp, vp, vp, vp, vp, vp]
         L.ct_sirt_update.argtypes = [vp, vp, vp, c.c_float, vp, vp]
         L.ct_sirt_step.argtypes = [vp, vp, vp, vp, vp, c.c_float, vp, vp]
+        L.ct_sirt_update_bounded.argtypes = [vp, vp, vp, c.c_float, c.c_float, c.c_float, vp, vp, vp]
+        L.ct_sirt_step_bounded.argtypes = [vp, vp, vp, vp, vp, c.c_float, c.c_float, c.c_float, vp,
+                                           vp, vp]
         L.ct_cgls_workspace_size.argtypes = [vp, P(c.c_size_t)]
         L.ct_cgls_init.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.ct_cgls_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
@@ -231,6 +235,35 @@ def ct_sirt_step(g: Geometry, x, y, row_inv, col_inv, relax, work_sino, stream=N
                               _ptr(row_inv, g.sino_shape, "row_inv"),
                               _ptr(col_inv, g.vol_shape, "col_inv"), float(relax),
                               _ptr(work_sino, g.sino_shape, "work_sino"), _stream(stream)))
+    return x
+
+
+def _mask_ptr(g: Geometry, mask):
+    import torch
+    if mask is None:
+        return ctypes.c_void_p(0)
+    if not isinstance(mask, torch.Tensor) or not mask.is_cuda or mask.dtype != torch.uint8 \
+            or not mask.is_contiguous() or tuple(mask.shape) != tuple(g.vol_shape):
+        raise ValueError("mask must be a contiguous uint8 device tensor of volume shape")
+    return ctypes.c_void_p(mask.data_ptr())
+
+
+def ct_sirt_update_bounded(g: Geometry, work_sino, col_inv, relax, lo, hi, mask, x, stream=None):
+    """x <- clamp(x + relax * col_inv * A^T work_sino, lo, hi) where mask != 0."""
+    _check(lib().ct_sirt_update_bounded(g.handle, _ptr(work_sino, g.sino_shape, "work_sino"),
+                                        _ptr(col_inv, g.vol_shape, "col_inv"), float(relax),
+                                        float(lo), float(hi), _mask_ptr(g, mask),
+                                        _ptr(x, g.vol_shape, "x"), _stream(stream)))
+    return x
+
+
+def ct_sirt_step_bounded(g: Geometry, x, y, row_inv, col_inv, relax, lo, hi, mask, work_sino,
+                         stream=None):
+    _check(lib().ct_sirt_step_bounded(g.handle, _ptr(x, g.vol_shape, "x"), _ptr(y, g.sino_shape, "y"),
+                                      _ptr(row_inv, g.sino_shape, "row_inv"),
+                                      _ptr(col_inv, g.vol_shape, "col_inv"), float(relax), float(lo),
+                                      float(hi), _mask_ptr(g, mask),
+                                      _ptr(work_sino, g.sino_shape, "work_sino"), _stream(stream)))
     return x
 
 

@@ -331,6 +331,46 @@ ct_status_t ct_sirt_update(ct_geom_t g, const float *work_sino, const float *col
                     "ct_sirt_update launch");
 }
 
+ct_status_t ct_sirt_update_bounded(ct_geom_t g, const float *work_sino, const float *col_inv,
+                                  float relax, float lo, float hi, const uint8_t *mask, float *x,
+                                  ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!x || !work_sino || !col_inv) return fail(CT_E_NULL, "a buffer pointer is NULL");
+    if (!std::isfinite(relax)) return fail(CT_E_ARG, "relax must be finite");
+    if (std::isnan(lo) || std::isnan(hi) || !(lo <= hi)) return fail(CT_E_ARG, "bounds must satisfy lo <= hi");
+    const size_t nvox = vol_bytes(g) / sizeof(float);
+    Span X{x, vol_bytes(g)}, E{work_sino, sino_bytes(g)}, C{col_inv, vol_bytes(g)}, M{mask, nvox};
+    ct_status_t st = check_alias({{X, true}, {E, false}, {C, false}});
+    if (st == CT_OK && mask) st = check_alias({{X, true}, {M, false}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    return launched(launch_sirt_update_bounded(lg(g), work_sino, col_inv, relax, lo, hi, mask, x,
+                                               (hipStream_t)stream),
+                    "ct_sirt_update_bounded launch");
+}
+
+ct_status_t ct_sirt_step_bounded(ct_geom_t g, float *x, const float *y, const float *row_inv,
+                                 const float *col_inv, float relax, float lo, float hi,
+                                 const uint8_t *mask, float *work_sino, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!x || !y || !row_inv || !col_inv || !work_sino) return fail(CT_E_NULL, "a buffer pointer is NULL");
+    if (!std::isfinite(relax)) return fail(CT_E_ARG, "relax must be finite");
+    if (std::isnan(lo) || std::isnan(hi) || !(lo <= hi)) return fail(CT_E_ARG, "bounds must satisfy lo <= hi");
+    const size_t nvox = vol_bytes(g) / sizeof(float);
+    Span X{x, vol_bytes(g)}, Y{y, sino_bytes(g)}, R{row_inv, sino_bytes(g)}, C{col_inv, vol_bytes(g)},
+        E{work_sino, sino_bytes(g)};
+    Span M{mask, nvox};
+    ct_status_t st = check_alias({{X, true}, {Y, false}, {R, false}, {C, false}, {E, true}});
+    if (st == CT_OK && mask) st = check_alias({{X, true}, {E, true}, {M, false}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    hipError_t e = launch_residual(lg(g), x, y, row_inv, work_sino, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ct_sirt_step_bounded residual launch");
+    return launched(launch_sirt_update_bounded(lg(g), work_sino, col_inv, relax, lo, hi, mask, x,
+                                               (hipStream_t)stream),
+                    "ct_sirt_step_bounded update launch");
+}
+
 ct_status_t ct_sirt_step(ct_geom_t g, float *x, const float *y, const float *row_inv,
                          const float *col_inv, float relax, float *work_sino, ct_stream_t stream) {
     if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");

@@ -542,6 +542,9 @@ struct BrickArgs {
     float *vol;               // output (BM_SIRT_UPDATE: x, read-modify-write; BM_COLINV: col_inv)
     const float *cinv;        // BM_SIRT_UPDATE
     float relax;
+    bool bounded;             // BM_SIRT_UPDATE: clamp the updated x to [lo, hi]
+    float lo, hi;
+    const uint8_t *mask;      // BM_SIRT_UPDATE: update only voxels with mask != 0 (nullable)
     float *x_upd;             // BM_CGLS: x += alpha p_old (nullable)
     const float *p_old;       // BM_CGLS, with x_upd
     float *p_copy;            // BM_CGLS: p = s (nullable)
@@ -867,6 +870,16 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
     const double cbx = x0 + 0.5 * ex, cby = y0 + 0.5 * ey, cbz = z0 + 0.5 * ez;
     const int lane = threadIdx.x & 63, wv = uni((int)(threadIdx.x >> 6));
     constexpr bool TWO_D = BZ == 1;   // single-slice bricks serve the 2D beams only
+    if (MODE == BM_SIRT_UPDATE && a.mask) {
+        // a brick with no voxel to update does no work at all
+        int any = 0;
+        for (int i = threadIdx.x; i < BX * BY * BZ; i += NT) {
+            const int lx = i % BX, ly = (i / BX) % BY, lz = i / (BX * BY);
+            if (lx < ex && ly < ey && lz < ez)
+                any |= a.mask[((size_t)(z0 + lz) * a.H + (y0 + ly)) * a.W + (x0 + lx)] != 0;
+        }
+        if (!__syncthreads_or(any)) return;
+    }
     const bool two_d = TWO_D;
     const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
 
@@ -929,7 +942,11 @@ __global__ __launch_bounds__(NT) void brick_kernel(BrickArgs a) {
             if (MODE == BM_BACKPROJECT) {
                 a.vol[g] = val;
             } else if (MODE == BM_SIRT_UPDATE) {
-                a.vol[g] = fmaf(a.relax * a.cinv[g], val, a.vol[g]);
+                if (!a.mask || a.mask[g]) {
+                    float v = fmaf(a.relax * a.cinv[g], val, a.vol[g]);
+                    if (a.bounded) v = fminf(fmaxf(v, a.lo), a.hi);
+                    a.vol[g] = v;
+                }
             } else if (MODE == BM_CGLS) {
                 a.vol[g] = val;
                 sq += (double)val * val;
@@ -1222,6 +1239,21 @@ hipError_t launch_backproject(const LaunchGeom &g, const float *sino, float *vol
 hipError_t launch_sirt_update(const LaunchGeom &g, const float *e, const float *cinv, float relax,
                               float *x, hipStream_t s) {
     return launch_brick<BM_SIRT_UPDATE>(g, e, x, cinv, relax, s);
+}
+
+hipError_t launch_sirt_update_bounded(const LaunchGeom &g, const float *e, const float *cinv,
+                                      float relax, float lo, float hi, const uint8_t *mask, float *x,
+                                      hipStream_t s) {
+    BrickArgs a{};
+    a.sino = e;
+    a.vol = x;
+    a.cinv = cinv;
+    a.relax = relax;
+    a.bounded = true;
+    a.lo = lo;
+    a.hi = hi;
+    a.mask = mask;
+    return launch_brick_args<BM_SIRT_UPDATE>(g, a, s);
 }
 
 hipError_t launch_colinv(const LaunchGeom &g, float *cinv, hipStream_t s) {

@@ -32,6 +32,9 @@ hipError_t launch_backproject(const LaunchGeom &g, const float *sino, float *vol
 hipError_t launch_sirt_update(const LaunchGeom &g, const float *e, const float *cinv, float relax,
                               float *x, hipStream_t s);
 hipError_t launch_colinv(const LaunchGeom &g, float *cinv, hipStream_t s);
+hipError_t launch_sirt_update_bounded(const LaunchGeom &g, const float *e, const float *cinv,
+                                      float relax, float lo, float hi, const uint8_t *mask, float *x,
+                                      hipStream_t s);
 
 // CGLS.  Workspace: kCglsStateDoubles scalars, then one float64 partial per
 // block of the largest launch (forward blocks, bricks or kCglsVecBlocks).

@@ -180,6 +180,44 @@ def test_sirt_c2_ten_iterations():
     assert e <= TOL
 
 
+def test_bounded_masked_sirt_c2_ten_iterations():
+    """Box constraints and a reconstruction mask (a disc, so whole corner bricks
+    are skipped), with bounds that are active on both sides."""
+    p, phantom = full_pair(2)
+    y = oracle.project(p.og, phantom).astype(np.float32)
+    R, C = oracle.sirt_weights(p.og)
+    _, H, Wd = p.wl.vol_shape
+    yy, xx = np.mgrid[0:H, 0:Wd]
+    mask = (((yy + 0.5 - H / 2) ** 2 + (xx + 0.5 - Wd / 2) ** 2) < 200.0 ** 2).astype(np.uint8)
+    mask = mask.reshape(p.wl.vol_shape)
+    x0 = np.full(p.wl.vol_shape, 0.05, np.float32)
+    lo, hi = 0.02, 0.6
+    xo = oracle.sirt(p.og, y, x0=x0, n_iter=10, relax=1.0, weights=(R, C), lo=lo, hi=hi, mask=mask)
+    assert np.any(xo[mask != 0] == lo) and np.any(xo[mask != 0] == hi)
+    g = p.g
+    rinv = torch.empty(g.sino_shape, device="cuda")
+    cinv = torch.empty(g.vol_shape, device="cuda")
+    rdp.ct_sirt_weights(g, rinv, cinv)
+    x = dev(x0)
+    yd, md = dev(y), torch.from_numpy(mask).cuda()
+    work = torch.empty(g.sino_shape, device="cuda")
+    for _ in range(10):
+        rdp.ct_sirt_step_bounded(g, x, yd, rinv, cinv, 1.0, lo, hi, md, work)
+    xg = host(x)
+    assert np.array_equal(xg[mask == 0], x0[mask == 0].astype(np.float64))
+    e = rel_l2(xg, xo)
+    say(f"C2 bounded masked SIRT x10 rel_l2 = {e:.3e}")
+    assert e <= TOL
+    # no bounds, no mask: the same bits as the plain step
+    xa, xb = dev(x0), dev(x0)
+    rdp.ct_sirt_step(g, xa, yd, rinv, cinv, 1.0, work)
+    rdp.ct_sirt_step_bounded(g, xb, yd, rinv, cinv, 1.0, -math.inf, math.inf, None, work)
+    assert torch.equal(xa, xb)
+    with pytest.raises(rdp.CtError) as ei:
+        rdp.ct_sirt_step_bounded(g, x, yd, rinv, cinv, 1.0, 1.0, 0.0, md, work)
+    assert ei.value.status == rdp.CT_E_ARG
+
+
 def _sample_rays(wl, n, seed):
     rng = np.random.default_rng(seed)
     return np.unique(rng.integers(0, wl.n_rays, n)).astype(np.int64)
@@ -294,8 +332,10 @@ def test_full_size_adjoint_sampled_columns(config):
 
 def test_sirt_step_c4_matches_composition():
     """One SIRT iteration at 512^3 from x0 = 0 with a sparse measurement: the
-    exact iterate is C * A^T (R * y), with R from the oracle's chords of the
-    sampled rays and C checked on sampled voxels."""
+    exact iterate is C * A^T (R * y).  R on the sampled rays and C on sampled
+    voxels come from the oracle's chords and column sums; A^T of the sparse
+    weighted residual from the oracle in full.  The plain step and the bounded,
+    masked step are both checked."""
     wl = W.make_workload(4)
     p = Pair(wl)
     g = p.g
@@ -310,22 +350,39 @@ def test_sirt_step_c4_matches_composition():
     y = np.zeros(wl.n_rays, dtype=np.float32)
     y[ids] = 1.0 + (np.arange(len(ids)) % 7).astype(np.float32)
     y = y.reshape(wl.sino_shape)
-    x = torch.zeros(g.vol_shape, device="cuda")
-    work = torch.empty(g.sino_shape, device="cuda")
-    rdp.ct_sirt_step(g, x, dev(y), rinv, cinv, 1.0, work)
     e_ref = np.zeros(wl.n_rays)
     e_ref[ids] = R_s * y.ravel()[ids]
-    bt = oracle.backproject(p.og, e_ref.reshape(wl.sino_shape))
-    xg = host(x)
-    cg = host(cinv)
-    # compare x / C on voxels the sampled rays touch (C itself is checked below)
-    mask = bt > 0
-    assert rel_l2(xg[mask], (cg * bt)[mask]) <= TOL
+    bt = oracle.backproject(p.og, e_ref.reshape(wl.sino_shape)).ravel()
+    support = np.flatnonzero(bt > 0)
     rng = np.random.default_rng(3)
-    js = [int(j) for j in rng.choice(np.flatnonzero(mask.ravel()), 3, replace=False)]
+    js = [int(j) for j in rng.choice(support, 4, replace=False)]
     cs = np.array([oracle.column_dot(p.og, j, np.ones(wl.sino_shape)) for j in js])
-    assert rel_l2(cg.ravel()[js], 1 / cs) <= TOL
-
+    x_ref = bt[js] / cs
+    assert rel_l2(host(cinv).ravel()[js], 1 / cs) <= TOL
+    work = torch.empty(g.sino_shape, device="cuda")
+    x = torch.zeros(g.vol_shape, device="cuda")
+    rdp.ct_sirt_step(g, x, dev(y), rinv, cinv, 1.0, work)
+    xg = host(x).ravel()
+    say(f"C4 SIRT step sampled voxels gpu {xg[js]} oracle {x_ref}")
+    assert rel_l2(xg[js], x_ref) <= TOL
+    # voxels that no measured ray crosses with positive length stay (nearly) 0:
+    # a ray grazing a voxel edge may leave a piece of rounding length there
+    assert np.abs(xg[bt == 0]).max() <= 1e-5 * np.abs(xg).max()
+    # bounded and masked: the mask keeps two of the four sampled voxels, the
+    # upper bound cuts the larger of them
+    mask = np.zeros(wl.n_voxels, np.uint8)
+    keep = sorted(js, key=lambda j: x_ref[js.index(j)])[2:]
+    mask[keep] = 1
+    mask[support[: len(support) // 2]] = 1
+    hi = float(np.mean([x_ref[js.index(j)] for j in keep]))
+    xb = torch.zeros(g.vol_shape, device="cuda")
+    rdp.ct_sirt_step_bounded(g, xb, dev(y), rinv, cinv, 1.0, 0.0, hi,
+                             torch.from_numpy(mask.reshape(wl.vol_shape)).cuda(), work)
+    xbg = host(xb).ravel()
+    exp = np.array([min(x_ref[k], hi) if mask[j] else 0.0 for k, j in enumerate(js)])
+    say(f"C4 bounded masked step gpu {xbg[js]} expected {exp}")
+    assert rel_l2(xbg[js], exp) <= TOL
+    assert not np.any(xbg[mask == 0])
 
 # ---------------------------------------------------------------------------
 # edge cases
