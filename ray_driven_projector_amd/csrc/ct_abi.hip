@@ -40,6 +40,7 @@ struct ct_geom_s {
     unsigned long long *d_total = nullptr;  // device counter for ct_count_intersections
     int device = 0;
     int brick_shape = 2;                // adjoint bricks of 32 x 16 x 16
+    int fwd_order = 5;                  // forward block order: 2 x 2 tile groups, views inside
     float *d_vol_yf = nullptr;          // y-fastest volume copy read by some views' gathers
     float *d_vol_zf = nullptr;          // z-fastest volume copy read by some views' gathers
 };
@@ -76,6 +77,7 @@ LaunchGeom lg(ct_geom_t g) {
     l.spz = g->host.sz;
     l.two_d = g->host.is2d;
     l.brick_shape = g->brick_shape;
+    l.fwd_order = g->fwd_order;
     l.vol_yf = g->d_vol_yf;
     l.vol_zf = g->d_vol_zf;
     return l;
@@ -111,15 +113,22 @@ ct_status_t check_alias(std::initializer_list<Arg> args) {
     return CT_OK;
 }
 
-// Launch shapes.  CTPROJ_BRICK (0..4) overrides the adjoint brick shape and
+// Launch shapes.  CTPROJ_BRICK (0..4) overrides the adjoint brick shape,
+// CTPROJ_FWD_ORDER (0..7) the forward block order, and
 // CTPROJ_FWD_LAYOUT=x keeps every forward gather on the caller's x-fastest volume;
 // both only change the work decomposition (used for tuning comparisons).
-// Defaults measured on 512^3 cone and parallel3d workloads: 32 x 16 x 16 bricks.
+// Defaults measured on 512^3 cone and parallel3d workloads: 32 x 16 x 16 bricks,
+// forward order 5 (groups of 2 x 2 pixel tiles, every view of a group in turn).
 void choose_tiles(ct_geom_s *g) {
     g->brick_shape = 2;
     if (const char *e = std::getenv("CTPROJ_BRICK")) {
         const int v = std::atoi(e);
         if (v >= 0 && v <= 4) g->brick_shape = v;
+    }
+    g->fwd_order = 5;
+    if (const char *e = std::getenv("CTPROJ_FWD_ORDER")) {
+        const int v = std::atoi(e);
+        if (v >= 0 && v <= 7) g->fwd_order = v;
     }
     const char *lay = std::getenv("CTPROJ_FWD_LAYOUT");
     if (lay && lay[0] == 'x') {
