@@ -232,15 +232,25 @@ struct GStep {
     uint32_t seg;
     bool last;
 };
+// Exactly one axis steps per call, the first of x, y, z whose next crossing is
+// the minimum; where planes are crossed at the same point the next call takes
+// the other axis after a piece of length 0.
 __device__ __forceinline__ GStep gstep(const IWalk &w, uint32_t &idx, uint32_t &lc, uint32_t &lx,
                                        uint32_t &ly, uint32_t &lz) {
+    const uint32_t qx = w.qx, qy = w.qy, qz = w.qz, sx = w.stx, sy = w.sty, sz = w.stz;
     const uint32_t tmin = umin3(lx, ly, lz);
     const uint32_t tn = min(tmin, w.lend);
-    const bool bx = lx == tmin, by = ly == tmin, bz = lz == tmin;
-    lx = __builtin_elementwise_add_sat(lx, bx ? w.qx : 0u);
-    ly = __builtin_elementwise_add_sat(ly, by ? w.qy : 0u);
-    lz = __builtin_elementwise_add_sat(lz, bz ? w.qz : 0u);
-    idx += (bx ? w.stx : 0u) + (by ? w.sty : 0u) + (bz ? w.stz : 0u);
+    const bool bx = lx == tmin;
+    const bool by = !bx && ly == tmin;
+    const bool bz = !bx && !by;
+    const uint32_t nx = __builtin_elementwise_add_sat(lx, qx);
+    const uint32_t ny = __builtin_elementwise_add_sat(ly, qy);
+    const uint32_t nz = __builtin_elementwise_add_sat(lz, qz);
+    const uint32_t syz = by ? sy : sz;
+    lx = bx ? nx : lx;
+    ly = by ? ny : ly;
+    lz = bz ? nz : lz;
+    idx += bx ? sx : syz;
     GStep g{tn - lc, tmin >= w.lend};
     lc = tn;
     return g;
@@ -703,35 +713,48 @@ __device__ __forceinline__ void lds_add(unsigned long long *lds, uint32_t byte_o
                                         unsigned long long v) {
     atomicAdd((unsigned long long *)((char *)lds + byte_off), v);
 }
-// Move past the crossing at t: every axis whose next crossing is t steps on.
-__device__ __forceinline__ void sadvance(const IWalk &w, uint32_t t, uint32_t &idx, uint32_t &lx,
-                                         uint32_t &ly, uint32_t &lz) {
-    const bool bx = lx == t, by = ly == t, bz = lz == t;
-    lx = __builtin_elementwise_add_sat(lx, bx ? w.qx : 0u);
-    ly = __builtin_elementwise_add_sat(ly, by ? w.qy : 0u);
-    lz = __builtin_elementwise_add_sat(lz, bz ? w.qz : 0u);
-    idx += (bx ? w.stx : 0u) + (by ? w.sty : 0u) + (bz ? w.stz : 0u);
+// Move past the crossing at t = min(lx, ly, lz): exactly one axis steps, the
+// first of x, y, z whose next crossing is t.  Where two planes are crossed at
+// the same point the other axis steps on the next call, after a piece of
+// length 0 (it adds nothing; its cell, one step along the first axis, lies in
+// the brick because that crossing was a real one).
+__device__ __forceinline__ void sadvance(uint32_t qx, uint32_t qy, uint32_t qz, uint32_t sx,
+                                         uint32_t sy, uint32_t sz, uint32_t t, uint32_t &idx,
+                                         uint32_t &lx, uint32_t &ly, uint32_t &lz) {
+    const bool bx = lx == t;
+    const bool by = !bx && ly == t;
+    const bool bz = !bx && !by;
+    const uint32_t nx = __builtin_elementwise_add_sat(lx, qx);
+    const uint32_t ny = __builtin_elementwise_add_sat(ly, qy);
+    const uint32_t nz = __builtin_elementwise_add_sat(lz, qz);
+    const uint32_t syz = by ? sy : sz;   // values, not field addresses: no table in memory
+    lx = bx ? nx : lx;
+    ly = by ? ny : ly;
+    lz = bz ? nz : lz;
+    idx += bx ? sx : syz;
 }
 // Two pieces per iteration with one exit test: the loop is entered only while the
 // next event t lies before l_end, so the first piece of an iteration is whole;
 // the second is cut at l_end.  A cell is only written before a crossing at or
 // past l_end has been taken, so every offset stays inside the brick.
 __device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long long *lds, int Y) {
+    const uint32_t qx = w.qx, qy = w.qy, qz = w.qz, sx = w.stx, sy = w.sty, sz = w.stz;
+    const uint32_t lend = w.lend;
     uint32_t idx = w.idx;
     uint32_t lx = w.lx, ly = w.ly, lz = w.lz;
     uint32_t lc = 0, t = umin3(lx, ly, lz);
-    while (t < w.lend) {
+    while (t < lend) {
         lds_add(lds, idx, mul24_64(t - lc, Y));
-        sadvance(w, t, idx, lx, ly, lz);
+        sadvance(qx, qy, qz, sx, sy, sz, t, idx, lx, ly, lz);
         lc = t;
         t = umin3(lx, ly, lz);
-        const uint32_t tn = min(t, w.lend);
+        const uint32_t tn = min(t, lend);
         lds_add(lds, idx, mul24_64(tn - lc, Y));
-        sadvance(w, t, idx, lx, ly, lz);
+        sadvance(qx, qy, qz, sx, sy, sz, t, idx, lx, ly, lz);
         lc = tn;
         t = umin3(lx, ly, lz);
     }
-    if (lc < w.lend) lds_add(lds, idx, mul24_64(w.lend - lc, Y));
+    if (lc < lend) lds_add(lds, idx, mul24_64(lend - lc, Y));
 }
 
 // Walk every ray of one view's footprint through the brick.  PERSP: fan/cone
