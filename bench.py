@@ -166,7 +166,7 @@ def main():
         work = torch.empty(g.sino_shape, device="cuda")
         names = ("sirt_residual", "sirt_update")
         bytes_per = {"sirt_residual": 4 * nnz + 12 * M, "sirt_update": 4 * nnz + 4 * M + 12 * N}
-        kern_names = {"sirt_residual": "ray_kernel<1, false>", "sirt_update": "brick_kernel<32, 16, 16, 512, 1>"}
+        kern_names = {"sirt_residual": "ray_kernel<1, false>", "sirt_update": "brick_kernel<16, 16, 32, 512, 1>"}
 
         def step(evs):
             evs[0].record(stream)
@@ -183,7 +183,7 @@ def main():
         vol = torch.empty(g.vol_shape, device="cuda")
         names = ("project", "backproject")
         bytes_per = {"project": 4 * nnz + 4 * M, "backproject": 4 * nnz + 4 * M + 4 * N}
-        kern_names = {"project": "ray_kernel<0, false>", "backproject": "brick_kernel<32, 16, 16, 512, 0>"}
+        kern_names = {"project": "ray_kernel<0, false>", "backproject": "brick_kernel<16, 16, 32, 512, 0>"}
 
         def step(evs):
             evs[0].record(stream)

@@ -39,7 +39,7 @@ struct ct_geom_s {
     double *d_views = nullptr;          // device view table
     unsigned long long *d_total = nullptr;  // device counter for ct_count_intersections
     int device = 0;
-    int brick_shape = 2;                // adjoint bricks of 32 x 16 x 16
+    int brick_shape = 5;                // adjoint bricks of 16 x 16 x 32
     int fwd_order = 5;                  // forward block order: 2 x 2 tile groups, views inside
     float *d_vol_yf = nullptr;          // y-fastest volume copy read by some views' gathers
     float *d_vol_zf = nullptr;          // z-fastest volume copy read by some views' gathers
@@ -113,17 +113,17 @@ ct_status_t check_alias(std::initializer_list<Arg> args) {
     return CT_OK;
 }
 
-// Launch shapes.  CTPROJ_BRICK (0..4) overrides the adjoint brick shape,
+// Launch shapes.  CTPROJ_BRICK (0..6) overrides the adjoint brick shape,
 // CTPROJ_FWD_ORDER (0..7) the forward block order, and
 // CTPROJ_FWD_LAYOUT=x keeps every forward gather on the caller's x-fastest volume;
 // both only change the work decomposition (used for tuning comparisons).
-// Defaults measured on 512^3 cone and parallel3d workloads: 32 x 16 x 16 bricks,
+// Defaults measured on 512^3 cone and parallel3d workloads: 16 x 16 x 32 bricks,
 // forward order 5 (groups of 2 x 2 pixel tiles, every view of a group in turn).
 void choose_tiles(ct_geom_s *g) {
-    g->brick_shape = 2;
+    g->brick_shape = 5;
     if (const char *e = std::getenv("CTPROJ_BRICK")) {
         const int v = std::atoi(e);
-        if (v >= 0 && v <= 4) g->brick_shape = v;
+        if (v >= 0 && v <= 6) g->brick_shape = v;
     }
     g->fwd_order = 5;
     if (const char *e = std::getenv("CTPROJ_FWD_ORDER")) {

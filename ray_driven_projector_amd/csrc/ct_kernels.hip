@@ -1274,6 +1274,10 @@ static hipError_t launch_brick_args(const LaunchGeom &g, BrickArgs a, hipStream_
         launch_brick_shape<32, 16, 32, 1024, MODE>(a, g, s);
     } else if (g.brick_shape == 4) {
         launch_brick_shape<32, 32, 8, 512, MODE>(a, g, s);
+    } else if (g.brick_shape == 5) {
+        launch_brick_shape<16, 16, 32, 512, MODE>(a, g, s);
+    } else if (g.brick_shape == 6) {
+        launch_brick_shape<16, 16, 64, 1024, MODE>(a, g, s);
     } else {
         launch_brick_shape<16, 16, 16, 256, MODE>(a, g, s);
     }
@@ -1330,6 +1334,8 @@ size_t cgls_brick_blocks(const LaunchGeom &g) {
     else if (g.brick_shape == 2) { bx = 32; by = 16; bz = 16; }
     else if (g.brick_shape == 3) { bx = 32; by = 16; bz = 32; }
     else if (g.brick_shape == 4) { bx = 32; by = 32; bz = 8; }
+    else if (g.brick_shape == 5) { bx = 16; by = 16; bz = 32; }
+    else if (g.brick_shape == 6) { bx = 16; by = 16; bz = 64; }
     return (size_t)((g.W + bx - 1) / bx) * ((g.H + by - 1) / by) * ((g.D + bz - 1) / bz);
 }
 

@@ -14,7 +14,8 @@ struct LaunchGeom {
     double spx, spy, spz;  // voxel spacing (x, y, z)
     bool two_d;
     int brick_shape;       // adjoint brick: 0 = 16^3, 1 = 32x32x16, 2 = 32x16x16,
-                           // 3 = 32x16x32, 4 = 32x32x8 (x by y by z)
+                           // 3 = 32x16x32, 4 = 32x32x8, 5 = 16x16x32, 6 = 16x16x64
+                           // (x by y by z)
     int fwd_order;         // forward block order (see RayArgs::order)
     float *vol_yf;         // handle-owned y-fastest volume copy, or null if no view reads it
     float *vol_zf;         // handle-owned z-fastest volume copy, or null if no view reads it
