@@ -43,7 +43,8 @@ class _Geom(ctypes.Structure):
                 ("sz", ctypes.c_double), ("sy", ctypes.c_double), ("sx", ctypes.c_double),
                 ("nu", ctypes.c_int64), ("nv", ctypes.c_int64),
                 ("su", ctypes.c_double), ("sv", ctypes.c_double),
-                ("frames", ctypes.POINTER(ctypes.c_double))]
+                ("frames", ctypes.POINTER(ctypes.c_double)),
+                ("offsets", ctypes.POINTER(ctypes.c_double)), ("offsets_per_view", ctypes.c_int)]
 
 
 class _Ray(ctypes.Structure):
@@ -96,9 +97,12 @@ def _iptr(a: np.ndarray):
 
 
 class Geometry:
-    """Oracle geometry: shapes + frames (n_views x 12 float64)."""
+    """Oracle geometry: shapes + frames (n_views x 12 float64), and optionally a
+    detector surface: per-pixel offsets (o_u, o_v, o_n) of shape (U, V, 3), or
+    (views, U, V, 3) per view (2D: V = 1)."""
 
-    def __init__(self, beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames):
+    def __init__(self, beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames,
+                 offsets=None):
         self.frames = np.ascontiguousarray(frames, dtype=np.float64)
         d, h, w = (int(x) for x in vol_shape)
         dz, dy, dx = (float(x) for x in voxel_spacing)
@@ -106,12 +110,25 @@ class Geometry:
         du, dv = (float(x) for x in det_spacing)
         self.vol_shape = (d, h, w)
         self.sino_shape = (self.frames.shape[0], nu, nv)
+        per_view = 0
+        self.offsets = None
+        optr = ctypes.POINTER(ctypes.c_double)()
+        if offsets is not None:
+            self.offsets = np.ascontiguousarray(offsets, dtype=np.float64)
+            if self.offsets.shape == (nu, nv, 3):
+                per_view = 0
+            elif self.offsets.shape == (self.frames.shape[0], nu, nv, 3):
+                per_view = 1
+            else:
+                raise ValueError("offsets must be (U, V, 3) or (views, U, V, 3)")
+            optr = _dptr(self.offsets)
         self._g = _Geom(int(beam), self.frames.shape[0], d, h, w, dz, dy, dx, nu, nv, du, dv,
-                        _dptr(self.frames))
+                        _dptr(self.frames), optr, per_view)
 
     @classmethod
     def from_workload(cls, wl) -> "Geometry":
-        return cls(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing, wl.frames)
+        return cls(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing, wl.frames,
+                   getattr(wl, "offsets", None))
 
     @property
     def n_rays(self) -> int:

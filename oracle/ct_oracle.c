@@ -57,11 +57,29 @@ void ora_ray_of(const ora_geom *g, int64_t view, int64_t u, int64_t v, ora_ray *
     const double *f = g->frames + 12 * view;
     const double *a = f, *c = f + 3, *eu = f + 6, *ev = f + 9;
     int three_d = (g->beam == ORA_CONE || g->beam == ORA_PARALLEL3D);
-    double ou = ((double)u - 0.5 * (double)(g->nu - 1)) * g->su;
-    double ov = three_d ? ((double)v - 0.5 * (double)(g->nv - 1)) * g->sv : 0.0;
     double p[3];
-    for (int k = 0; k < 3; ++k)
-        p[k] = c[k] + ou * eu[k] + (three_d ? ov * ev[k] : 0.0);
+    if (g->offsets) {
+        /* surface point: c + o_u e_u + o_v e_v + o_n n */
+        const double *o = g->offsets + 3 * ((g->offsets_per_view ? view * g->nu * g->nv : 0)
+                                            + u * g->nv + v);
+        double n[3];
+        if (three_d) {
+            n[0] = eu[1] * ev[2] - eu[2] * ev[1];
+            n[1] = eu[2] * ev[0] - eu[0] * ev[2];
+            n[2] = eu[0] * ev[1] - eu[1] * ev[0];
+        } else {
+            n[0] = eu[1];
+            n[1] = -eu[0];
+            n[2] = 0.0;
+        }
+        for (int k = 0; k < 3; ++k)
+            p[k] = c[k] + o[0] * eu[k] + (three_d ? o[1] * ev[k] : 0.0) + o[2] * n[k];
+    } else {
+        double ou = ((double)u - 0.5 * (double)(g->nu - 1)) * g->su;
+        double ov = three_d ? ((double)v - 0.5 * (double)(g->nv - 1)) * g->sv : 0.0;
+        for (int k = 0; k < 3; ++k)
+            p[k] = c[k] + ou * eu[k] + (three_d ? ov * ev[k] : 0.0);
+    }
     if (is_parallel(g->beam)) {
         for (int k = 0; k < 3; ++k) { r->o[k] = p[k]; r->d[k] = a[k]; }
         r->tmin = -INFINITY;

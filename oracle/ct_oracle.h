@@ -38,6 +38,14 @@ typedef struct {
     int64_t nu, nv;          /* detector (U, V); 2D: nv = 1 */
     double su, sv;           /* detector spacing (du, dv) */
     const double *frames;    /* n_views x 12: a(3) c(3) e_u(3) e_v(3), x,y,z order */
+    /* Parameterized detector surface (NULL: flat detector).  Per pixel the local
+     * offsets (o_u, o_v, o_n), shape (U, V, 3), or (views, U, V, 3) when
+     * offsets_per_view != 0; the pixel's world point is
+     *   c + o_u e_u + o_v e_v + o_n n,  n = e_u x e_v (3D), (e_u_y, -e_u_x, 0) (2D)
+     * (diffct documentation, "Trajectories and Geometry" > "Parameterized
+     * detector surfaces"). */
+    const double *offsets;
+    int offsets_per_view;
 } ora_geom;
 
 typedef struct {
@@ -46,7 +54,8 @@ typedef struct {
     double tmin, tmax;       /* parameter range of the ray */
 } ora_ray;
 
-/* Ray through pixel (u, v) of a view: flat-detector pixel-centre formula. */
+/* Ray through pixel (u, v) of a view: flat-detector pixel-centre formula, or
+ * the surface point of the pixel when the geometry has surface offsets. */
 void ora_ray_of(const ora_geom *g, int64_t view, int64_t u, int64_t v, ora_ray *r);
 
 /* Length of the ray inside the half-open box [lo, hi) (slab method). */

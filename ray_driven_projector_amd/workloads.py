@@ -83,6 +83,7 @@ class Workload:
     frames: np.ndarray          # (n_views, 12) float64
     config: int = 0
     meta: dict = field(default_factory=dict)
+    offsets: np.ndarray | None = None   # detector surface: (U, V, 3) or (views, U, V, 3)
 
     @property
     def n_views(self) -> int:
@@ -103,9 +104,37 @@ class Workload:
 
     def subset_views(self, views) -> "Workload":
         views = np.asarray(views, dtype=np.int64)
+        off = self.offsets
+        if off is not None and off.ndim == 4:
+            off = np.ascontiguousarray(off[views])
         return Workload(self.name + f"[{len(views)} views]", self.beam, self.vol_shape,
                         self.voxel_spacing, self.det_shape, self.det_spacing,
-                        np.ascontiguousarray(self.frames[views]), self.config, dict(self.meta))
+                        np.ascontiguousarray(self.frames[views]), self.config, dict(self.meta), off)
+
+
+def cylinder_offsets(det_shape, det_spacing, radius: float, two_d: bool = False) -> np.ndarray:
+    """Per-pixel local offsets (o_u, o_v, o_n) of a cylindrical detector: the
+    pixel at physical detector coordinates (u, v) sits at angle u / radius on a
+    cylinder of that radius whose axis is e_v, bending towards the source
+    (negative normal offsets), after the diffct documentation's example
+    ("Trajectories and Geometry" > "Parameterized detector surfaces").  A radius
+    equal to the source-detector distance centres the cylinder on the source.
+    Shape (U, V, 3); 2D: V = 1 and o_v = 0."""
+    nu, nv = int(det_shape[0]), int(det_shape[1])
+    du, dv = float(det_spacing[0]), float(det_spacing[1])
+    u = (np.arange(nu) - 0.5 * (nu - 1)) * du
+    v = np.zeros(1) if two_d else (np.arange(nv) - 0.5 * (nv - 1)) * dv
+    uu, vv = np.meshgrid(u, v, indexing="ij")
+    ang = uu / radius
+    return np.ascontiguousarray(np.stack((radius * np.sin(ang), vv, radius * (np.cos(ang) - 1.0)),
+                                         axis=-1), dtype=np.float64)
+
+
+def with_surface(wl: "Workload", offsets: np.ndarray, label: str) -> "Workload":
+    """The same acquisition with a parameterized detector surface."""
+    return Workload(wl.name + f", {label} detector", wl.beam, wl.vol_shape, wl.voxel_spacing,
+                    wl.det_shape, wl.det_spacing, wl.frames, wl.config, dict(wl.meta),
+                    np.ascontiguousarray(offsets, dtype=np.float64))
 
 
 def _frames(a, c, eu, ev) -> np.ndarray:

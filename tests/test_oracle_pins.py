@@ -426,3 +426,55 @@ def test_bounded_masked_sirt_dense_iteration_and_invariants():
     # unbounded and unmasked: the plain iteration
     np.testing.assert_array_equal(oracle.sirt(g, yb, x0=x0, n_iter=2),
                                   oracle.sirt(g, yb, x0=x0, n_iter=2, lo=-np.inf, hi=np.inf, mask=None))
+
+
+# ---------------------------------------------------------------------------
+# parameterized detector surfaces
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("beam", ALL_BEAMS)
+def test_flat_surface_offsets_reproduce_the_flat_detector(beam):
+    wl = _tiny(beam, 21, vol=(4, 5, 6), det=(7, 5), views=4)
+    U, V = wl.det_shape
+    du, dv = wl.det_spacing
+    two_d = beam in (W.BEAM_PARALLEL2D, W.BEAM_FAN2D)
+    u = (np.arange(U) - 0.5 * (U - 1)) * du
+    v = np.zeros(1) if two_d else (np.arange(V) - 0.5 * (V - 1)) * dv
+    uu, vv = np.meshgrid(u, v, indexing="ij")
+    off = np.stack((uu, vv, np.zeros_like(uu)), axis=-1)
+    g0 = oracle.Geometry.from_workload(wl)
+    g1 = oracle.Geometry.from_workload(W.with_surface(wl, off, "flat"))
+    x = np.random.default_rng(beam).uniform(0, 1, wl.vol_shape)
+    np.testing.assert_array_equal(oracle.project(g0, x), oracle.project(g1, x))
+
+
+@pytest.mark.parametrize("two_d", [False, True])
+def test_source_centred_cylinder_geometry(two_d):
+    """A cylinder of radius sdd centred on the source (the documentation's
+    example with negative normal offsets): every pixel ray, from the source,
+    has in-plane length sdd at angle u/sdd from the central ray (the detector
+    normal, pointing away from the source), and its e_v component is v."""
+    sid, sdd = 30.0, 50.0
+    if two_d:
+        wl = W.tiny_workload(W.BEAM_FAN2D, (1, 6, 6), (9, 1), 5, 31, sid=sid, sdd=sdd)
+    else:
+        wl = W.tiny_workload(W.BEAM_CONE, (5, 6, 6), (9, 7), 5, 31, sid=sid, sdd=sdd)
+    off = W.cylinder_offsets(wl.det_shape, wl.det_spacing, sdd, two_d=two_d)
+    g = oracle.Geometry.from_workload(W.with_surface(wl, off, "cylinder"))
+    U, V = wl.det_shape
+    du, dv = wl.det_spacing
+    for view in range(wl.n_views):
+        f = wl.frames[view]
+        s, c, eu, ev = f[0:3], f[3:6], f[6:9], f[9:12]
+        n = (c - s) / np.linalg.norm(c - s)            # away from the source
+        for iu in range(U):
+            for iv in range(V):
+                o, d, tmin, tmax = g.ray(view, iu, iv)
+                np.testing.assert_allclose(o, s, rtol=0, atol=1e-12)
+                assert (tmin, tmax) == (0.0, 1.0)
+                up = (iu - 0.5 * (U - 1)) * du
+                vp = 0.0 if two_d else (iv - 0.5 * (V - 1)) * dv
+                assert abs(d @ ev - vp) < 1e-9 if not two_d else True
+                dn, du_ = d @ n, d @ eu
+                assert abs(math.hypot(dn, du_) - sdd) < 1e-9
+                assert abs(math.atan2(du_, dn) - up / sdd) < 1e-12
