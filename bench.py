@@ -17,7 +17,9 @@ ray nonzero), since rays whose value is 0 add nothing and are skipped by the
 adjoint, which would make a sparse sinogram look faster.  --workload c4cgls /
 c5cgls time CGLS iterations (ct_cgls_step: A p with ||q||^2, r -= alpha q,
 A^T r with ||s||^2 and x += alpha p, p = s + beta p) on the same workloads
-from y = A phantom, after ct_cgls_init.
+from y = A phantom, after ct_cgls_init.  --workload c5cyl times A + A^T on C5's
+acquisition with a cylindrical detector centred on the source (radius 1500,
+the parameterized-surface path).
 
 Roofline: algorithmic HBM bytes of the dominant kernel per launch divided by
 its average duration (HIP events on the launch stream), against 8 TB/s.
@@ -94,7 +96,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["c4", "c5", "c4cgls", "c5cgls"], default="c4")
+    ap.add_argument("--workload", choices=["c4", "c5", "c4cgls", "c5cgls", "c5cyl"], default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-views", type=int, default=16)
     ap.add_argument("--extra", action="store_true", help="also time A, A^T and atomic A^T alone")
@@ -127,6 +129,8 @@ def main():
     cfg = 4 if args.workload.startswith("c4") else 5
     cgls = args.workload.endswith("cgls")
     wl = W.make_workload(cfg)
+    if args.workload == "c5cyl":
+        wl = W.with_surface(wl, W.cylinder_offsets(wl.det_shape, wl.det_spacing, 1500.0), "cylindrical")
     print(f"# workload: {wl.name}", file=sys.stderr, flush=True)
     phantom = W.make_phantom(wl)
     g = rdp.Geometry.from_workload(wl)
@@ -166,7 +170,8 @@ def main():
         work = torch.empty(g.sino_shape, device="cuda")
         names = ("sirt_residual", "sirt_update")
         bytes_per = {"sirt_residual": 4 * nnz + 12 * M, "sirt_update": 4 * nnz + 4 * M + 12 * N}
-        kern_names = {"sirt_residual": "ray_kernel<1, false>", "sirt_update": "brick_kernel<16, 16, 32, 512, 1>"}
+        kern_names = {"sirt_residual": "ray_kernel<1, false, false>",
+                      "sirt_update": "brick_kernel<16, 16, 32, 512, 1, false>"}
 
         def step(evs):
             evs[0].record(stream)
@@ -183,7 +188,9 @@ def main():
         vol = torch.empty(g.vol_shape, device="cuda")
         names = ("project", "backproject")
         bytes_per = {"project": 4 * nnz + 4 * M, "backproject": 4 * nnz + 4 * M + 4 * N}
-        kern_names = {"project": "ray_kernel<0, false>", "backproject": "brick_kernel<16, 16, 32, 512, 0>"}
+        sf = "true" if wl.offsets is not None else "false"
+        kern_names = {"project": f"ray_kernel<0, false, {sf}>",
+                      "backproject": f"brick_kernel<16, 16, 32, 512, 0, {sf}>"}
 
         def step(evs):
             evs[0].record(stream)

@@ -126,6 +126,24 @@ ct_status_t ct_geom_validate(const ct_geom_desc_t *desc);
  * to the current HIP device (synchronous).  *out receives the handle. */
 ct_status_t ct_geom_create(const ct_geom_desc_t *desc, ct_geom_t *out);
 
+/* Create a geometry whose detector is a parameterized surface (diffct
+ * documentation, "Trajectories and Geometry" > "Parameterized detector
+ * surfaces"): pixel (u, v) of view k sits at the world point
+ *   c + o_u e_u + o_v e_v + o_n n,   n = e_u x e_v  (2D: (e_u_y, -e_u_x, 0)),
+ * with (c, e_u, e_v) the view's frame and (o_u, o_v, o_n) the pixel's local
+ * offsets in physical units.  offsets: HOST float64, row-major (U, V, 3), shared
+ * by every view (per_view = 0), or (n_views, U, V, 3) (per_view != 0); 2D beams
+ * use V = 1 and need o_v = 0.  Rays are built exactly as for the flat detector
+ * with the surface point in place of the flat pixel centre (fan/cone: from the
+ * source to the point; parallel: through the point along the ray direction),
+ * so project/backproject keep the matched Siddon model, one ray per pixel.
+ * The flat-detector frame checks of ct_geom_create apply; in addition offsets
+ * must be finite and every fan/cone pixel must lie in front of the source
+ * (CT_E_FRAME).  The handle also keeps the offsets (float64) and per-view
+ * footprint bounds on the device.  Synchronous, like ct_geom_create. */
+ct_status_t ct_geom_create_surface(const ct_geom_desc_t *desc, const double *offsets, int per_view,
+                                   ct_geom_t *out);
+
 /* Free the handle and its device tables.  NULL is accepted.  The caller must
  * make sure no work using the handle is still pending. */
 ct_status_t ct_geom_destroy(ct_geom_t g);
@@ -133,7 +151,7 @@ ct_status_t ct_geom_destroy(ct_geom_t g);
 /* Host copy of the per-view ray table (n_views x CT_VIEW_TABLE_STRIDE doubles),
  * for inspection.  Works without a device: it may be called on a handle made by
  * ct_geom_create, or with desc != NULL and g == NULL to compute it on the host. */
-#define CT_VIEW_TABLE_STRIDE 40
+#define CT_VIEW_TABLE_STRIDE 48
 ct_status_t ct_geom_view_table(ct_geom_t g, const ct_geom_desc_t *desc, double *out);
 
 /* Forward projection A: sino[view][u][v] = sum_j a_ij vol[j].

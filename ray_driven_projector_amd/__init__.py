@@ -25,10 +25,11 @@ STATUS_NAMES = {0: "CT_OK", 1: "CT_E_NULL", 2: "CT_E_SHAPE", 3: "CT_E_NONFINITE"
                 4: "CT_E_FRAME", 5: "CT_E_RANGE", 6: "CT_E_ALIAS", 7: "CT_E_NOMEM",
                 8: "CT_E_HIP", 9: "CT_E_ARG"}
 CT_PARALLEL2D, CT_FAN2D, CT_CONE, CT_PARALLEL3D = range(4)
-CT_VIEW_TABLE_STRIDE = 40
+CT_VIEW_TABLE_STRIDE = 48
 
 # every symbol declared in include/ctproj.h
-EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_destroy", "ct_geom_view_table",
+EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_geom_destroy",
+           "ct_geom_view_table",
            "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_sirt_weights",
            "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_sirt_update_bounded",
            "ct_sirt_step_bounded", "ct_cgls_workspace_size",
@@ -65,6 +66,7 @@ def lib():
         st = c.c_int
         L.ct_geom_validate.argtypes = [P(GeomDesc)]
         L.ct_geom_create.argtypes = [P(GeomDesc), P(vp)]
+        L.ct_geom_create_surface.argtypes = [P(GeomDesc), P(c.c_double), c.c_int, P(vp)]
         L.ct_geom_destroy.argtypes = [vp]
         L.ct_geom_view_table.argtypes = [vp, P(GeomDesc), P(c.c_double)]
         L.ct_project.argtypes = [vp, vp, vp, vp]
@@ -136,12 +138,28 @@ def last_error() -> str:
 
 
 class Geometry:
-    """A ct_geom_t handle (device tables on the current HIP device)."""
+    """A ct_geom_t handle (device tables on the current HIP device).  offsets:
+    optional detector surface, float64 (U, V, 3) or (views, U, V, 3)
+    (ct_geom_create_surface)."""
 
-    def __init__(self, beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames):
+    def __init__(self, beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames,
+                 offsets=None):
         d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
         h = ctypes.c_void_p()
-        _check(lib().ct_geom_create(ctypes.byref(d), ctypes.byref(h)))
+        if offsets is None:
+            _check(lib().ct_geom_create(ctypes.byref(d), ctypes.byref(h)))
+        else:
+            off = np.ascontiguousarray(offsets, dtype=np.float64)
+            nu, nv = int(det_shape[0]), int(det_shape[1])
+            if off.shape == (nu, nv, 3):
+                per_view = 0
+            elif off.shape == (fr.shape[0], nu, nv, 3):
+                per_view = 1
+            else:
+                raise ValueError("offsets must be (U, V, 3) or (views, U, V, 3)")
+            _check(lib().ct_geom_create_surface(ctypes.byref(d),
+                                                off.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                                per_view, ctypes.byref(h)))
         self._h = h
         self.beam = int(beam)
         self.vol_shape = tuple(int(x) for x in vol_shape)
@@ -149,7 +167,8 @@ class Geometry:
 
     @classmethod
     def from_workload(cls, wl) -> "Geometry":
-        return cls(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing, wl.frames)
+        return cls(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing, wl.frames,
+                   getattr(wl, "offsets", None))
 
     @property
     def handle(self):

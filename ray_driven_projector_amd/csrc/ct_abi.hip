@@ -43,6 +43,9 @@ struct ct_geom_s {
     int fwd_order = 5;                  // forward block order: 2 x 2 tile groups, views inside
     float *d_vol_yf = nullptr;          // y-fastest volume copy read by some views' gathers
     float *d_vol_zf = nullptr;          // z-fastest volume copy read by some views' gathers
+    double *d_off = nullptr;            // detector surface offsets (float64), or null: flat
+    int surf_per_view = 0;
+    float *d_env = nullptr;             // per-view footprint envelopes of the surface
 };
 
 namespace {
@@ -80,6 +83,9 @@ LaunchGeom lg(ct_geom_t g) {
     l.fwd_order = g->fwd_order;
     l.vol_yf = g->d_vol_yf;
     l.vol_zf = g->d_vol_zf;
+    l.surf_off = g->d_off;
+    l.surf_per_view = g->surf_per_view;
+    l.surf_env = g->d_env;
     return l;
 }
 
@@ -192,13 +198,30 @@ ct_status_t ct_geom_view_table(ct_geom_t g, const ct_geom_desc_t *desc, double *
     return CT_OK;
 }
 
-ct_status_t ct_geom_create(const ct_geom_desc_t *desc, ct_geom_t *out) {
+static void free_handle(ct_geom_s *g) {
+    if (g->d_views) (void)hipFree(g->d_views);
+    if (g->d_total) (void)hipFree(g->d_total);
+    if (g->d_vol_yf) (void)hipFree(g->d_vol_yf);
+    if (g->d_vol_zf) (void)hipFree(g->d_vol_zf);
+    if (g->d_off) (void)hipFree(g->d_off);
+    if (g->d_env) (void)hipFree(g->d_env);
+    delete g;
+}
+
+static ct_status_t create_impl(const ct_geom_desc_t *desc, const double *offsets, int per_view,
+                               ct_geom_t *out) {
     if (!out) return fail(CT_E_NULL, "output handle pointer is NULL");
     *out = nullptr;
     GeomHost h;
     const char *why = "";
     ct_status_t st = validate_desc(desc, &h, &why);
     if (st != CT_OK) return fail(st, why);
+    const size_t n_off = offsets ? (size_t)(per_view ? h.n_views : 1) * h.U * h.V * 3 : 0;
+    for (size_t i = 0; i < n_off; ++i) {
+        if (!std::isfinite(offsets[i])) return fail(CT_E_NONFINITE, "surface offset not finite");
+        if (h.is2d && i % 3 == 1 && offsets[i] != 0.0)
+            return fail(CT_E_ARG, "2D surface offsets need o_v = 0");
+    }
     ct_geom_s *g = new (std::nothrow) ct_geom_s();
     if (!g) return fail(CT_E_NOMEM, "host allocation failed");
     g->magic = kMagic;
@@ -248,26 +271,53 @@ ct_status_t ct_geom_create(const ct_geom_desc_t *desc, ct_geom_t *out) {
     if ((need_y && hipMalloc((void **)&g->d_vol_yf, vbytes) != hipSuccess) ||
         (need_z && hipMalloc((void **)&g->d_vol_zf, vbytes) != hipSuccess)) {
         (void)hipGetLastError();
-        if (g->d_vol_yf) (void)hipFree(g->d_vol_yf);
-        (void)hipFree(g->d_views);
-        (void)hipFree(g->d_total);
-        delete g;
+        free_handle(g);
         return fail(CT_E_NOMEM, "hipMalloc of a volume layout copy failed");
+    }
+    if (offsets) {
+        // surface offsets, then the per-view footprint envelopes (synchronous)
+        g->surf_per_view = per_view ? 1 : 0;
+        const size_t env_bytes =
+            (size_t)h.n_views * surface_env_floats((int)h.U, (int)h.V) * sizeof(float);
+        if (hipMalloc((void **)&g->d_off, n_off * sizeof(double)) != hipSuccess ||
+            hipMalloc((void **)&g->d_env, env_bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            free_handle(g);
+            return fail(CT_E_NOMEM, "hipMalloc of the detector surface failed");
+        }
+        e = hipMemcpy(g->d_off, offsets, n_off * sizeof(double), hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = launch_surface_env(lg(g), g->d_total, nullptr);
+        unsigned long long bad = 0;
+        if (e == hipSuccess) e = hipMemcpy(&bad, g->d_total, sizeof bad, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) {
+            free_handle(g);
+            return hip_fail(e, "detector surface set-up");
+        }
+        if (bad) {
+            free_handle(g);
+            return fail(CT_E_FRAME, "a surface pixel is not in front of the source");
+        }
     }
     *out = g;
     set_error("");
     return CT_OK;
 }
 
+ct_status_t ct_geom_create(const ct_geom_desc_t *desc, ct_geom_t *out) {
+    return create_impl(desc, nullptr, 0, out);
+}
+
+ct_status_t ct_geom_create_surface(const ct_geom_desc_t *desc, const double *offsets, int per_view,
+                                   ct_geom_t *out) {
+    if (!offsets) return fail(CT_E_NULL, "offsets must be non-NULL");
+    return create_impl(desc, offsets, per_view, out);
+}
+
 ct_status_t ct_geom_destroy(ct_geom_t g) {
     if (!g) return CT_OK;
     if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
     g->magic = 0;
-    if (g->d_views) (void)hipFree(g->d_views);
-    if (g->d_total) (void)hipFree(g->d_total);
-    if (g->d_vol_yf) (void)hipFree(g->d_vol_yf);
-    if (g->d_vol_zf) (void)hipFree(g->d_vol_zf);
-    delete g;
+    free_handle(g);
     set_error("");
     return CT_OK;
 }

@@ -261,6 +261,11 @@ void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *tab
         // Forward gather layout: chosen for all views by choose_layouts.
         t[VT_LAYOUT] = 0.0;
         t[VT_PATCH] = 0.0;
+        // detector frame for parameterized surfaces
+        put(t + VT_C, to_vox_point(c));
+        put(t + VT_EU, to_vox_vec(eu));
+        put(t + VT_EV, to_vox_vec(ev));
+        put(t + VT_EN, to_vox_vec(n));
     }
     choose_layouts(g, table);
 }

@@ -22,6 +22,8 @@
 // 2D geometries put the detector normal in the third column so MINV exists; the
 // v coordinate is then meaningless and ignored.
 //
+// C / EU / EV / EN: the detector frame, for parameterized detector surfaces.
+//
 // LAYOUT / PATCH: the forward projector gathers from the volume copy whose
 // contiguous axis lies closest to the detector direction along which a wave's
 // 16-wide pixel patch runs, so neighbouring lanes read neighbouring words.
@@ -47,7 +49,11 @@ enum ViewSlot : int {
     VT_MINV = 24,   // 9 values, row-major
     VT_LAYOUT = 33, // volume copy the forward gathers from: 0 x-, 1 y-, 2 z-fastest
     VT_PATCH = 34,  // forward wave patch: 0 = 16 u x 4 v, 1 = 4 u x 16 v
-    VT_END = 35
+    VT_C = 35,      // detector centre (point)
+    VT_EU = 38,     // e_u, e_v and the normal n as voxel-coordinate vectors (e / s):
+    VT_EV = 41,     // a surface pixel with local offsets (o_u, o_v, o_n) sits at
+    VT_EN = 44,     // C + o_u EU + o_v EV + o_n EN
+    VT_END = 47
 };
 static_assert(VT_END <= CT_VIEW_TABLE_STRIDE, "view table overflow");
 

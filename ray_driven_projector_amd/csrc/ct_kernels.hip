@@ -215,6 +215,147 @@ __device__ __forceinline__ void dwalk(const DWalk &w, F &&f) {
 }
 
 // ---------------------------------------------------------------------------
+// parameterized detector surfaces
+// ---------------------------------------------------------------------------
+
+// Per-pixel local offsets (o_u, o_v, o_n) of a detector surface, shared by the
+// views (U, V, 3) or per view (views, U, V, 3), float64.
+struct Surface {
+    const double *off;   // null: flat detector
+    int per_view;
+};
+
+// Voxel-coordinate point of pixel (u, v) on the surface of a view:
+// C + o_u EU + o_v EV + o_n EN.
+__device__ __forceinline__ void surface_point(const double *vw, const Surface &sf, int view, int u,
+                                              int v, int U, int V, double &px, double &py,
+                                              double &pz) {
+    const double *o = sf.off + 3 * ((sf.per_view ? (size_t)view * U * V : 0) + (size_t)u * V + v);
+    const double ou = o[0], ov = o[1], on = o[2];
+    px = vw[VT_C + 0] + ou * vw[VT_EU + 0] + ov * vw[VT_EV + 0] + on * vw[VT_EN + 0];
+    py = vw[VT_C + 1] + ou * vw[VT_EU + 1] + ov * vw[VT_EV + 1] + on * vw[VT_EN + 1];
+    pz = vw[VT_C + 2] + ou * vw[VT_EU + 2] + ov * vw[VT_EV + 2] + on * vw[VT_EN + 2];
+}
+
+// Ray of pixel (u, v): origin and direction in voxel coordinates (flat detector:
+// the affine table; surface: the source or the pixel's surface point).
+__device__ __forceinline__ void pixel_ray(const double *vw, const Surface &sf, int view, int u, int v,
+                                          int U, int V, double &ox, double &oy, double &oz,
+                                          double &dx, double &dy, double &dz) {
+    if (!sf.off) {
+        const double fu = (double)u, fv = (double)v;
+        ox = vw[VT_O00 + 0] + fu * vw[VT_OU + 0] + fv * vw[VT_OV + 0];
+        oy = vw[VT_O00 + 1] + fu * vw[VT_OU + 1] + fv * vw[VT_OV + 1];
+        oz = vw[VT_O00 + 2] + fu * vw[VT_OU + 2] + fv * vw[VT_OV + 2];
+        dx = vw[VT_D00 + 0] + fu * vw[VT_DU + 0] + fv * vw[VT_DV + 0];
+        dy = vw[VT_D00 + 1] + fu * vw[VT_DU + 1] + fv * vw[VT_DV + 1];
+        dz = vw[VT_D00 + 2] + fu * vw[VT_DU + 2] + fv * vw[VT_DV + 2];
+        return;
+    }
+    double px, py, pz;
+    surface_point(vw, sf, view, u, v, U, V, px, py, pz);
+    if (vw[VT_PERSP] != 0.0) {   // from the source to the surface point
+        ox = vw[VT_O00 + 0]; oy = vw[VT_O00 + 1]; oz = vw[VT_O00 + 2];
+        dx = px - ox; dy = py - oy; dz = pz - oz;
+    } else {                     // through the surface point along the ray direction
+        ox = px; oy = py; oz = pz;
+        dx = vw[VT_D00 + 0]; dy = vw[VT_D00 + 1]; dz = vw[VT_D00 + 2];
+    }
+}
+
+// Where each surface pixel's ray crosses the flat detector plane, in flat pixel
+// units (the coordinates the brick footprints are computed in), reduced per view
+// to monotone envelopes.  Per view, env_size(U, V) floats:
+//   colmin[U], colmax[U]               over all v, for each column u
+//   then per tile of kEnvTile columns:  rowmin[V], rowmax[V] over the tile's columns
+// with the max arrays made running maxima and the min arrays running minima from
+// the right.  A brick whose flat footprint is [a, b] x [c, d] can only be seen by
+// columns u with colmax[u] >= a and colmin[u] <= b, and, within a column tile,
+// by rows v with rowmax[v] >= c and rowmin[v] <= d: index ranges found by binary
+// search.  Per-tile rows keep the v range tight where the surface's flat v
+// depends on u (a cylinder's does, by 1 / cos of the fan angle).
+constexpr int kEnvTile = 16;
+__host__ __device__ inline size_t env_size(int U, int V) {
+    return 2 * (size_t)U + (size_t)((U + kEnvTile - 1) / kEnvTile) * 2 * V;
+}
+__global__ __launch_bounds__(256) void surface_env_kernel(const double *views, Surface sf, int U,
+                                                          int V, float *env,
+                                                          unsigned long long *bad) {
+    const int view = blockIdx.x;
+    const double *vw = views + (size_t)view * CT_VIEW_TABLE_STRIDE;
+    float *e = env + (size_t)view * env_size(U, V);
+    const int nt = (U + kEnvTile - 1) / kEnvTile;
+    const bool persp = vw[VT_PERSP] != 0.0;
+    auto flat = [&](int u, int v, float &fu, float &fv) {
+        double px, py, pz;
+        surface_point(vw, sf, view, u, v, U, V, px, py, pz);
+        const double rx = px - vw[VT_O00 + 0], ry = py - vw[VT_O00 + 1], rz = pz - vw[VT_O00 + 2];
+        const double al = vw[VT_MINV + 0] * rx + vw[VT_MINV + 1] * ry + vw[VT_MINV + 2] * rz;
+        const double be = vw[VT_MINV + 3] * rx + vw[VT_MINV + 4] * ry + vw[VT_MINV + 5] * rz;
+        const double ga = vw[VT_MINV + 6] * rx + vw[VT_MINV + 7] * ry + vw[VT_MINV + 8] * rz;
+        // a fan/cone pixel must lie in front of the source (its ray crosses the
+        // flat detector plane at a positive parameter)
+        if (persp && !(al > 1e-9)) atomicOr(bad, 1ull);
+        fu = (float)(persp ? be / al : be);
+        fv = (float)(persp ? ga / al : ga);
+    };
+    for (int u = threadIdx.x; u < U; u += 256) {
+        float lo = 3e38f, hi = -3e38f;
+        for (int v = 0; v < V; ++v) {
+            float fu, fv;
+            flat(u, v, fu, fv);
+            lo = fminf(lo, fu);
+            hi = fmaxf(hi, fu);
+        }
+        e[u] = lo;
+        e[U + u] = hi;
+    }
+    for (int k = threadIdx.x; k < nt * V; k += 256) {
+        const int t = k / V, v = k - t * V;
+        float lo = 3e38f, hi = -3e38f;
+        for (int u = t * kEnvTile; u < min(U, (t + 1) * kEnvTile); ++u) {
+            float fu, fv;
+            flat(u, v, fu, fv);
+            lo = fminf(lo, fv);
+            hi = fmaxf(hi, fv);
+        }
+        float *r = e + 2 * U + (size_t)t * 2 * V;
+        r[v] = lo;
+        r[V + v] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int u = 1; u < U; ++u) e[U + u] = fmaxf(e[U + u], e[U + u - 1]);
+        for (int u = U - 2; u >= 0; --u) e[u] = fminf(e[u], e[u + 1]);
+    }
+    for (int t = threadIdx.x; t < nt; t += 256) {
+        float *r = e + 2 * U + (size_t)t * 2 * V;
+        for (int v = 1; v < V; ++v) r[V + v] = fmaxf(r[V + v], r[V + v - 1]);
+        for (int v = V - 2; v >= 0; --v) r[v] = fminf(r[v], r[v + 1]);
+    }
+}
+
+// First index i in [0, n) with a[i] >= x (n if none); a non-decreasing,
+// wave-uniform arguments.
+__device__ __forceinline__ int first_ge(const float *a, int n, float x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] >= x) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+// First index i in [0, n) with a[i] > x (n if none).
+__device__ __forceinline__ int first_gt(const float *a, int n, float x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] > x) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
 // integer walk
 // ---------------------------------------------------------------------------
 
@@ -403,6 +544,7 @@ struct RayArgs {
     uint32_t *counts;          // RM_COUNT (nullable)
     unsigned long long *total; // RM_COUNT
     double *partial;           // RM_PROJECT_SQ, RM_CGLS_R0: one sum of squares per block
+    Surface surf;              // detector surface (off == null: flat)
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
     int n_utiles, n_vtiles, n_blocks;
@@ -420,7 +562,8 @@ struct RayArgs {
 // neighbouring views; their rays cross the same voxels at nearly the same time
 // and the gathers hit in L2 (this order cut the 512^3 forward times by a
 // quarter against v-band, view, u-tile).
-template <int MODE, bool TWO_D>
+// SURF: parameterized detector surface (rays from the offsets table).
+template <int MODE, bool TWO_D, bool SURF>
 __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
     const int blk = xcd_remap(blockIdx.x, a.n_blocks);
     int ut, view, band;
@@ -477,13 +620,9 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
     double my_sq = 0.0;
     if (active) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
-        const double fu = (double)u, fv = (double)v;
-        double ox = vw[VT_O00 + 0] + fu * vw[VT_OU + 0] + fv * vw[VT_OV + 0];
-        double oy = vw[VT_O00 + 1] + fu * vw[VT_OU + 1] + fv * vw[VT_OV + 1];
-        double oz = vw[VT_O00 + 2] + fu * vw[VT_OU + 2] + fv * vw[VT_OV + 2];
-        double dx = vw[VT_D00 + 0] + fu * vw[VT_DU + 0] + fv * vw[VT_DV + 0];
-        double dy = vw[VT_D00 + 1] + fu * vw[VT_DU + 1] + fv * vw[VT_DV + 1];
-        double dz = vw[VT_D00 + 2] + fu * vw[VT_DU + 2] + fv * vw[VT_DV + 2];
+        double ox, oy, oz, dx, dy, dz;
+        pixel_ray(vw, SURF ? a.surf : Surface{nullptr, 0}, view, u, v, a.U, a.V, ox, oy, oz, dx, dy,
+                  dz);
         const size_t ray = ((size_t)view * a.U + u) * a.V + v;
         if (kFwd) {
             float acc = 0.f;
@@ -592,6 +731,8 @@ struct BrickArgs {
     float *p_copy;            // BM_CGLS: p = s (nullable)
     const double *state;      // BM_CGLS: CGLS scalars (alpha)
     double *partial;          // BM_CGLS: one sum of s^2 per brick
+    Surface surf;             // detector surface (off == null: flat)
+    const float *env;         // surface: per-view footprint envelopes
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
     int nbx, nby, nbz, n_blocks;
@@ -652,7 +793,7 @@ struct Footprint {
 };
 __device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int x0, int y0, int z0,
                                                 int ex, int ey, int ez, int U, int V, bool two_d,
-                                                Footprint &f) {
+                                                const float *env, Footprint &f) {
     const int c = lane & 7;
     const double X = (c & 1) ? x0 + ex : x0;
     const double Y = (c & 2) ? y0 + ey : y0;
@@ -685,6 +826,21 @@ __device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int 
     bad = uni(bad);
     if (bad) {
         f.u0 = 0; f.u1 = U - 1; f.v0 = 0; f.v1 = V - 1;
+    } else if (env) {
+        // detector surface: the pixel ranges whose flat-plane crossings can fall in
+        // the box (monotone envelopes; a margin for their float32 rounding)
+        const float m = 1e-2f;
+        f.u0 = first_ge(env + U, U, umin - m);
+        f.u1 = first_gt(env, U, umax + m) - 1;
+        f.v0 = V;
+        f.v1 = -1;
+        if (f.u0 <= f.u1) {
+            for (int t = f.u0 / kEnvTile; t <= f.u1 / kEnvTile; ++t) {
+                const float *r = env + 2 * U + (size_t)t * 2 * V;
+                f.v0 = min(f.v0, first_ge(r + V, V, vmin - m));
+                f.v1 = max(f.v1, first_gt(r, V, vmax + m) - 1);
+            }
+        }
     } else {
         // guard the float conversions against far-away projections
         umin = fmaxf(umin, -1.f); umax = fminf(umax, (float)U);
@@ -763,7 +919,7 @@ __device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long 
 // once, outside the ray loop.  TWO_D: single-slice bricks of a 2D geometry,
 // whose rays lie in the slice (z is neither clipped nor walked).  S = walk units
 // per length unit; yscale = power-of-two fixed-point scale of the ray values.
-template <int LSY, int LSZ, int MODE, bool PERSP, bool TWO_D>
+template <int LSY, int LSZ, int MODE, bool PERSP, bool TWO_D, bool SURF>
 __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw, int view,
                                            const Footprint &f, int lane, int x0, int y0, int z0,
                                            int ex, int ey, int ez, double cbx, double cby,
@@ -782,6 +938,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     // footprint; positions are relative to the brick centre ----
     const int cu = nfu / 2, cv = nfv / 2;
     const double nx_ = vw[VT_N + 0], ny_ = vw[VT_N + 1], nz_ = vw[VT_N + 2];
+    const float fnx = (float)nx_, fny = (float)ny_, fnz = (float)nz_;
     const double fu0 = u0 + cu, fv0 = v0 + cv;
     const double aox = vw[VT_O00 + 0] + fu0 * vw[VT_OU + 0] + fv0 * vw[VT_OV + 0];
     const double aoy = vw[VT_O00 + 1] + fu0 * vw[VT_OU + 1] + fv0 * vw[VT_OV + 1];
@@ -809,7 +966,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     const float DFz = uni((float)vw[qf_ + 2]);
     const float DSx = uni((float)vw[qs_ + 0]), DSy = uni((float)vw[qs_ + 1]);
     const float DSz = uni((float)vw[qs_ + 2]);
-    const float t0 = uni((float)(vw[VT_TMIN] - tb)), t1 = uni((float)(vw[VT_TMAX] - tb));
+    const float tv0 = uni((float)(vw[VT_TMIN] - tb)), tv1 = uni((float)(vw[VT_TMAX] - tb));
     const float *ysrc = a.sino + ((size_t)view * a.U + u0) * a.V + v0;
     const uint32_t yfs = ufast ? a.V : 1, yss = ufast ? 1 : a.V;   // sinogram strides, fast / slow
 
@@ -825,25 +982,83 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     uint32_t yo = lf * yfs + ls * yss;
     float ynext = 1.f;
     if (MODE != BM_COLINV && lane < nrays) ynext = ysrc[yo];
+    // surface: the frame in registers, and each ray's offsets fetched one round
+    // ahead like its value (a surface pixel shares the sinogram's pixel index)
+    double sCx = 0, sCy = 0, sCz = 0, sUx = 0, sUy = 0, sUz = 0, sVx = 0, sVy = 0, sVz = 0;
+    double sNx = 0, sNy = 0, sNz = 0, sDx = 0, sDy = 0, sDz = 0;
+    const double *ob = nullptr;
+    double o0n = 0, o1n = 0, o2n = 0;
+    if (SURF) {
+        sCx = vw[VT_C + 0]; sCy = vw[VT_C + 1]; sCz = vw[VT_C + 2];
+        sUx = vw[VT_EU + 0]; sUy = vw[VT_EU + 1]; sUz = vw[VT_EU + 2];
+        sVx = vw[VT_EV + 0]; sVy = vw[VT_EV + 1]; sVz = vw[VT_EV + 2];
+        sNx = vw[VT_EN + 0]; sNy = vw[VT_EN + 1]; sNz = vw[VT_EN + 2];
+        sDx = vw[VT_D00 + 0]; sDy = vw[VT_D00 + 1]; sDz = vw[VT_D00 + 2];
+        if (PERSP) {   // offsets relative to the source: P - S = (C - S) + o . E
+            sCx -= vw[VT_O00 + 0]; sCy -= vw[VT_O00 + 1]; sCz -= vw[VT_O00 + 2];
+        }
+        ob = a.surf.off + 3 * ((a.surf.per_view ? (size_t)view * a.U * a.V : 0) +
+                               (size_t)u0 * a.V + v0);
+        if (lane < nrays) { o0n = ob[3 * yo]; o1n = ob[3 * yo + 1]; o2n = ob[3 * yo + 2]; }
+    }
     for (int r = lane; r < nrays; r += 64) {
         const float cf = ff, cs = fs;
         ff += fstep_fast;
         fs += fstep_slow;
         yo += yo_step;
         if (ff >= fend) { ff -= fnf; fs += 1.f; yo += yo_wrap; }
+        // take this ray's prefetched values before issuing the next ray's loads, so
+        // the wait covers only loads issued a round earlier
         const float yv = ynext;
-        if (MODE != BM_COLINV && r + 64 < nrays) ynext = ysrc[yo];
-        if (yv == 0.f) continue;
-        const float ox = fmaf(cs, Asx, fmaf(cf, Afx, A0x));
-        const float oy = fmaf(cs, Asy, fmaf(cf, Afy, A0y));
-        const float oz = TWO_D ? A0z : fmaf(cs, Asz, fmaf(cf, Afz, A0z));
-        float dx = Dx, dy = Dy, dz = Dz;
-        if (PERSP) {
-            dx = fmaf(cs, DSx, fmaf(cf, DFx, Dx));
-            dy = fmaf(cs, DSy, fmaf(cf, DFy, Dy));
-            if (!TWO_D) dz = fmaf(cs, DSz, fmaf(cf, DFz, Dz));
+        const double o0 = o0n, o1 = o1n, o2 = o2n;
+        if (r + 64 < nrays) {
+            if (MODE != BM_COLINV) ynext = ysrc[yo];
+            if (SURF) { o0n = ob[3 * yo]; o1n = ob[3 * yo + 1]; o2n = ob[3 * yo + 2]; }
         }
-        if (TWO_D) dz = 0.f;
+        if (yv == 0.f) continue;
+        float ox, oy, oz, dx, dy, dz, t0, t1;
+        if (SURF) {
+            // surface pixel: the ray from the table, re-expressed in float64 around
+            // the plane through the brick centre parallel to the flat detector
+            // (any parameter near the plane will do: the origin is then formed in
+            // float64 exactly on the ray for that parameter, so the crossing
+            // parameter itself is computed in float32)
+            const double px = sCx + o0 * sUx + o1 * sVx + o2 * sNx;
+            const double py = sCy + o0 * sUy + o1 * sVy + o2 * sNy;
+            const double pz = sCz + o0 * sUz + o1 * sVz + o2 * sNz;
+            double rdx, rdy, rdz, bx_, by_, bz_;   // direction; origin relative to the brick centre
+            if (PERSP) {
+                rdx = px; rdy = py; rdz = pz;
+                bx_ = vw[VT_O00 + 0] - cbx; by_ = vw[VT_O00 + 1] - cby; bz_ = vw[VT_O00 + 2] - cbz;
+            } else {
+                rdx = sDx; rdy = sDy; rdz = sDz;
+                bx_ = px - cbx; by_ = py - cby; bz_ = pz - cbz;
+            }
+            const float num = -((float)bx_ * fnx + (float)by_ * fny + (float)bz_ * fnz);
+            const float den = (float)rdx * fnx + (float)rdy * fny + (float)rdz * fnz;
+            const double tr = (double)(num * __builtin_amdgcn_rcpf(den));
+            ox = (float)fma(tr, rdx, bx_);
+            oy = (float)fma(tr, rdy, by_);
+            oz = TWO_D ? A0z : (float)fma(tr, rdz, bz_);
+            dx = (float)rdx;
+            dy = (float)rdy;
+            dz = TWO_D ? 0.f : (float)rdz;
+            t0 = (float)(vw[VT_TMIN] - tr);
+            t1 = (float)(vw[VT_TMAX] - tr);
+        } else {
+            ox = fmaf(cs, Asx, fmaf(cf, Afx, A0x));
+            oy = fmaf(cs, Asy, fmaf(cf, Afy, A0y));
+            oz = TWO_D ? A0z : fmaf(cs, Asz, fmaf(cf, Afz, A0z));
+            dx = Dx; dy = Dy; dz = Dz;
+            if (PERSP) {
+                dx = fmaf(cs, DSx, fmaf(cf, DFx, Dx));
+                dy = fmaf(cs, DSy, fmaf(cf, DFy, Dy));
+                if (!TWO_D) dz = fmaf(cs, DSz, fmaf(cf, DFz, Dz));
+            }
+            if (TWO_D) dz = 0.f;
+            t0 = tv0;
+            t1 = tv1;
+        }
         // Components below 2^-40 of the largest count as zero.  Waves without
         // any (nearly all of them) take the short clip below.
         const float dm = fmaxf(fabsf(dx), fmaxf(fabsf(dy), fabsf(dz))) * 0x1p-40f;
@@ -906,9 +1121,10 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     }
 }
 
-template <int BX, int BY, int BZ, int NT, int MODE>
 // Two 512-thread workgroups (or four of 256, one of 1024) share a CU through
 // their LDS, i.e. 4 waves per SIMD; the register budget is held to that.
+// SURF: parameterized detector surface (per-pixel rays from the offsets table).
+template <int BX, int BY, int BZ, int NT, int MODE, bool SURF>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void brick_kernel(
     BrickArgs a) {
     constexpr int LSY = BX + 1;           // padded LDS strides (elements): rays of a
@@ -948,7 +1164,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
         for (int view = wv; view < a.n_views; view += NWAVES) {
             const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
             Footprint f;
-            if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d, f)) continue;
+            if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d,
+                                 a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f))
+                continue;
             const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
             const float *ysrc = a.sino + ((size_t)view * a.U + f.u0) * a.V + f.v0;
             const int step_slow = 64 / nfv, step_fast = 64 - step_slow * nfv;
@@ -980,13 +1198,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     for (int view = wv; view < a.n_views; view += NWAVES) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
         Footprint f;
-        if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d, f)) continue;
+        if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d,
+                             a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f))
+            continue;
         if (vw[VT_PERSP] != 0.0)
-            brick_rays<LSY, LSZ, MODE, true, TWO_D>(a, vw, view, f, lane, x0, y0, z0, ex, ey, ez, cbx,
-                                                    cby, cbz, S, yscale, acc);
+            brick_rays<LSY, LSZ, MODE, true, TWO_D, SURF>(a, vw, view, f, lane, x0, y0, z0, ex, ey,
+                                                          ez, cbx, cby, cbz, S, yscale, acc);
         else
-            brick_rays<LSY, LSZ, MODE, false, TWO_D>(a, vw, view, f, lane, x0, y0, z0, ex, ey, ez,
-                                                     cbx, cby, cbz, S, yscale, acc);
+            brick_rays<LSY, LSZ, MODE, false, TWO_D, SURF>(a, vw, view, f, lane, x0, y0, z0, ex, ey,
+                                                           ez, cbx, cby, cbz, S, yscale, acc);
     }
     __syncthreads();
     const double inv_scale = 1.0 / ((double)S * (double)yscale);
@@ -1148,6 +1368,7 @@ __global__ __launch_bounds__(256) void cgls_update_p_kernel(float *__restrict__ 
 static RayArgs ray_args(const LaunchGeom &g) {
     RayArgs a{};
     a.order = g.fwd_order;
+    a.surf = Surface{g.surf_off, g.surf_per_view};
     a.views = g.views;
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
@@ -1165,10 +1386,14 @@ static RayArgs ray_args(const LaunchGeom &g) {
 
 template <int MODE>
 static hipError_t launch_ray(const LaunchGeom &g, RayArgs a, hipStream_t s) {
-    if (g.two_d)
-        hipLaunchKernelGGL((ray_kernel<MODE, true>), dim3(a.n_blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((ray_kernel<MODE, false>), dim3(a.n_blocks), dim3(256), 0, s, a);
+    const dim3 grid(a.n_blocks), block(256);
+    if (g.two_d) {
+        if (a.surf.off) hipLaunchKernelGGL((ray_kernel<MODE, true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((ray_kernel<MODE, true, false>), grid, block, 0, s, a);
+    } else {
+        if (a.surf.off) hipLaunchKernelGGL((ray_kernel<MODE, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((ray_kernel<MODE, false, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -1256,12 +1481,19 @@ static void launch_brick_shape(BrickArgs &a, const LaunchGeom &g, hipStream_t s)
     a.nby = (g.H + BY - 1) / BY;
     a.nbz = (g.D + BZ - 1) / BZ;
     a.n_blocks = a.nbx * a.nby * a.nbz;
-    hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE>), dim3(a.n_blocks), dim3(NT), 0, s, a);
+    if (a.surf.off)
+        hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, true>), dim3(a.n_blocks), dim3(NT), 0, s,
+                           a);
+    else
+        hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, false>), dim3(a.n_blocks), dim3(NT), 0,
+                           s, a);
 }
 
 template <int MODE>
 static hipError_t launch_brick_args(const LaunchGeom &g, BrickArgs a, hipStream_t s) {
     a.views = g.views;
+    a.surf = Surface{g.surf_off, g.surf_per_view};
+    a.env = g.surf_env;
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
     if (g.two_d) {
@@ -1321,6 +1553,15 @@ hipError_t launch_sirt_update_bounded(const LaunchGeom &g, const float *e, const
 
 hipError_t launch_colinv(const LaunchGeom &g, float *cinv, hipStream_t s) {
     return launch_brick<BM_COLINV>(g, nullptr, cinv, nullptr, 0.f, s);
+}
+
+size_t surface_env_floats(int U, int V) { return env_size(U, V); }
+
+hipError_t launch_surface_env(const LaunchGeom &g, unsigned long long *bad, hipStream_t s) {
+    hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, bad);
+    hipLaunchKernelGGL(surface_env_kernel, dim3(g.n_views), dim3(256), 0, s, g.views,
+                       Surface{g.surf_off, g.surf_per_view}, g.U, g.V, g.surf_env, bad);
+    return hipGetLastError();
 }
 
 // ---- CGLS ----

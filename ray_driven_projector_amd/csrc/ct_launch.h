@@ -17,6 +17,9 @@ struct LaunchGeom {
                            // 3 = 32x16x32, 4 = 32x32x8, 5 = 16x16x32, 6 = 16x16x64
                            // (x by y by z)
     int fwd_order;         // forward block order (see RayArgs::order)
+    const double *surf_off; // detector surface offsets (device float64), or null: flat
+    int surf_per_view;      // offsets given per view
+    float *surf_env;        // per-view footprint envelopes of the surface (device)
     float *vol_yf;         // handle-owned y-fastest volume copy, or null if no view reads it
     float *vol_zf;         // handle-owned z-fastest volume copy, or null if no view reads it
 };
@@ -34,6 +37,11 @@ hipError_t launch_backproject(const LaunchGeom &g, const float *sino, float *vol
 hipError_t launch_sirt_update(const LaunchGeom &g, const float *e, const float *cinv, float relax,
                               float *x, hipStream_t s);
 hipError_t launch_colinv(const LaunchGeom &g, float *cinv, hipStream_t s);
+// Per-view footprint envelopes of a detector surface (once, at geometry creation).
+// bad (device) receives nonzero if a fan/cone surface pixel is not in front of
+// the source.
+hipError_t launch_surface_env(const LaunchGeom &g, unsigned long long *bad, hipStream_t s);
+size_t surface_env_floats(int U, int V);   // per view
 hipError_t launch_sirt_update_bounded(const LaunchGeom &g, const float *e, const float *cinv,
                                       float relax, float lo, float hi, const uint8_t *mask, float *x,
                                       hipStream_t s);
