@@ -177,6 +177,42 @@ ct_status_t ct_backproject(ct_geom_t g, const float *sino, float *vol, ct_stream
  * documentation notes for its atomic adjoint in "Example results"). */
 ct_status_t ct_backproject_atomic(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream);
 
+/* ---- Regions and view batches (chunked execution) ----
+ * The diffct documentation ("Large Volumes and Chunked Execution" > "Resident
+ * layouts and accumulation") splits large problems into volume tiles and view
+ * batches: projection adds the disjoint tile integrals, the adjoint accumulates
+ * each tile over the view batches, tiles keep the global lattice so cells on
+ * internal boundaries keep their owner.  These two calls are those building
+ * blocks.  A region is a box of voxel indices inside the volume; its buffer is a
+ * contiguous (nz, ny, nx) float32 array holding just that box.  A view batch is
+ * the views [view_begin, view_end) of the handle; its sinogram buffer is
+ * (view_end - view_begin, U, V).  Summing ct_project_region over disjoint regions
+ * that cover the volume gives ct_project (up to float32 summation order), and
+ * ct_backproject_region over view batches, accumulated, gives the region of
+ * ct_backproject.
+ * Errors: CT_E_SHAPE if the box is empty or leaves the volume or the view range is
+ * empty or leaves [0, n_views) (checked first, so empty buffers may be NULL);
+ * CT_E_NULL for a NULL buffer; CT_E_ALIAS if the two buffers overlap. */
+typedef struct {
+    int64_t z0, y0, x0;   /* first voxel of the box (z, y, x) */
+    int64_t nz, ny, nx;   /* its extents, >= 1, inside the volume */
+} ct_region_t;
+
+/* sino_batch (+)= A restricted to the region's voxels, for the batch's views.
+ * accumulate = 0 overwrites every ray of the batch (rays missing the region get
+ * 0); accumulate != 0 adds to what sino_batch holds.  Device buffers; they must
+ * not overlap.  Forward calls on one handle must not overlap in time. */
+ct_status_t ct_project_region(ct_geom_t g, const float *vol_region, ct_region_t region,
+                              int64_t view_begin, int64_t view_end, float *sino_batch, int accumulate,
+                              ct_stream_t stream);
+
+/* vol_region (+)= A^T of the batch's rays, restricted to the region.
+ * accumulate = 0 overwrites every voxel of the region; != 0 adds (the brick
+ * adjoint, bit-reproducible per call). */
+ct_status_t ct_backproject_region(ct_geom_t g, const float *sino_batch, int64_t view_begin,
+                                  int64_t view_end, ct_region_t region, float *vol_region,
+                                  int accumulate, ct_stream_t stream);
+
 /* SIRT weights (once per geometry): row_inv[i] = 1/(A 1)_i, col_inv[j] =
  * 1/(A^T 1)_j, each 0 where the sum is 0.  row_inv: (views,U,V); col_inv:
  * (D,H,W); device float32, non-overlapping. */

@@ -30,7 +30,8 @@ CT_VIEW_TABLE_STRIDE = 48
 # every symbol declared in include/ctproj.h
 EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_geom_destroy",
            "ct_geom_view_table",
-           "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_sirt_weights",
+           "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_project_region",
+           "ct_backproject_region", "ct_sirt_weights",
            "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_sirt_update_bounded",
            "ct_sirt_step_bounded", "ct_cgls_workspace_size",
            "ct_cgls_init", "ct_cgls_step", "ct_cgls_scalars", "ct_count_intersections",
@@ -49,6 +50,11 @@ class GeomDesc(ctypes.Structure):
                 ("vol_shape", ctypes.c_int64 * 3), ("voxel_spacing", ctypes.c_double * 3),
                 ("det_shape", ctypes.c_int64 * 2), ("det_spacing", ctypes.c_double * 2),
                 ("frames", ctypes.POINTER(ctypes.c_double))]
+
+
+class Region(ctypes.Structure):
+    _fields_ = [("z0", ctypes.c_int64), ("y0", ctypes.c_int64), ("x0", ctypes.c_int64),
+                ("nz", ctypes.c_int64), ("ny", ctypes.c_int64), ("nx", ctypes.c_int64)]
 
 
 _lib = None
@@ -72,6 +78,8 @@ def lib():
         L.ct_project.argtypes = [vp, vp, vp, vp]
         L.ct_backproject.argtypes = [vp, vp, vp, vp]
         L.ct_backproject_atomic.argtypes = [vp, vp, vp, vp]
+        L.ct_project_region.argtypes = [vp, vp, Region, c.c_int64, c.c_int64, vp, c.c_int, vp]
+        L.ct_backproject_region.argtypes = [vp, vp, c.c_int64, c.c_int64, Region, vp, c.c_int, vp]
         L.ct_sirt_weights.argtypes = [vp, vp, vp, vp]
         L.ct_sirt_residual.argtypes = [vp, vp, vp, vp, vp, vp]
         L.ct_sirt_update.argtypes = [vp, vp, vp, c.c_float, vp, vp]
@@ -220,6 +228,32 @@ def ct_backproject(g: Geometry, sino, vol, stream=None):
     _check(lib().ct_backproject(g.handle, _ptr(sino, g.sino_shape, "sino"),
                                 _ptr(vol, g.vol_shape, "vol"), _stream(stream)))
     return vol
+
+
+def ct_project_region(g: Geometry, vol_region, region, view_begin, view_end, sino_batch,
+                      accumulate=False, stream=None):
+    """sino_batch (+)= A of the region's voxels for views [view_begin, view_end).
+    region = (z0, y0, x0, nz, ny, nx)."""
+    z0, y0, x0, nz, ny, nx = (int(v) for v in region)
+    r = Region(z0, y0, x0, nz, ny, nx)
+    _check(lib().ct_project_region(g.handle, _ptr(vol_region, (nz, ny, nx), "vol_region"), r,
+                                   int(view_begin), int(view_end),
+                                   _ptr(sino_batch, (int(view_end) - int(view_begin),) + g.sino_shape[1:],
+                                        "sino_batch"), int(bool(accumulate)), _stream(stream)))
+    return sino_batch
+
+
+def ct_backproject_region(g: Geometry, sino_batch, view_begin, view_end, region, vol_region,
+                          accumulate=False, stream=None):
+    """vol_region (+)= A^T of the batch's rays restricted to the region."""
+    z0, y0, x0, nz, ny, nx = (int(v) for v in region)
+    r = Region(z0, y0, x0, nz, ny, nx)
+    _check(lib().ct_backproject_region(g.handle,
+                                       _ptr(sino_batch, (int(view_end) - int(view_begin),) + g.sino_shape[1:],
+                                            "sino_batch"), int(view_begin), int(view_end), r,
+                                       _ptr(vol_region, (nz, ny, nx), "vol_region"),
+                                       int(bool(accumulate)), _stream(stream)))
+    return vol_region
 
 
 def ct_backproject_atomic(g: Geometry, sino, vol, stream=None):

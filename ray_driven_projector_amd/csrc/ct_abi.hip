@@ -67,7 +67,7 @@ ct_status_t hip_fail(hipError_t e, const char *where) {
 bool valid(ct_geom_t g) { return g && g->magic == kMagic; }
 
 LaunchGeom lg(ct_geom_t g) {
-    LaunchGeom l;
+    LaunchGeom l{};
     l.views = g->d_views;
     l.W = (int)g->host.W;
     l.H = (int)g->host.H;
@@ -87,6 +87,33 @@ LaunchGeom lg(ct_geom_t g) {
     l.surf_per_view = g->surf_per_view;
     l.surf_env = g->d_env;
     return l;
+}
+
+// Launch geometry for a region of the volume and a batch of views: the buffer
+// holds the region only, the sinogram buffer the batch only.
+LaunchGeom lg_region(ct_geom_t g, const ct_region_t &r, int64_t vb, int64_t ve, bool accumulate) {
+    LaunchGeom l = lg(g);
+    l.W = (int)r.nx;
+    l.H = (int)r.ny;
+    l.D = (int)r.nz;
+    l.offx = (int)r.x0;
+    l.offy = (int)r.y0;
+    l.offz = (int)r.z0;
+    l.accumulate = accumulate ? 1 : 0;
+    l.views = g->d_views + (size_t)vb * CT_VIEW_TABLE_STRIDE;
+    l.n_views = (int)(ve - vb);
+    if (g->d_off && g->surf_per_view) l.surf_off = g->d_off + (size_t)vb * g->host.U * g->host.V * 3;
+    if (g->d_env) l.surf_env = g->d_env + (size_t)vb * surface_env_floats((int)g->host.U, (int)g->host.V);
+    return l;
+}
+
+ct_status_t check_region(ct_geom_t g, const ct_region_t &r, int64_t vb, int64_t ve) {
+    const GeomHost &h = g->host;
+    if (r.nz < 1 || r.ny < 1 || r.nx < 1 || r.z0 < 0 || r.y0 < 0 || r.x0 < 0 || r.z0 + r.nz > h.D ||
+        r.y0 + r.ny > h.H || r.x0 + r.nx > h.W)
+        return fail(CT_E_SHAPE, "region is empty or not inside the volume");
+    if (vb < 0 || ve > h.n_views || vb >= ve) return fail(CT_E_SHAPE, "view range is empty or out of range");
+    return CT_OK;
 }
 
 size_t vol_bytes(ct_geom_t g) { return (size_t)g->host.D * g->host.H * g->host.W * sizeof(float); }
@@ -340,6 +367,40 @@ ct_status_t ct_backproject(ct_geom_t g, const float *sino, float *vol, ct_stream
     if (st != CT_OK) return st;
     if ((st = ensure_device(g)) != CT_OK) return st;
     return launched(launch_backproject(lg(g), sino, vol, (hipStream_t)stream), "ct_backproject launch");
+}
+
+ct_status_t ct_project_region(ct_geom_t g, const float *vol_region, ct_region_t region,
+                              int64_t view_begin, int64_t view_end, float *sino_batch, int accumulate,
+                              ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    ct_status_t st = check_region(g, region, view_begin, view_end);
+    if (st != CT_OK) return st;
+    if (!vol_region || !sino_batch) return fail(CT_E_NULL, "buffers must be non-NULL");
+    const size_t vb = (size_t)region.nz * region.ny * region.nx * sizeof(float);
+    const size_t sb = (size_t)(view_end - view_begin) * g->host.U * g->host.V * sizeof(float);
+    st = check_alias({{Span{vol_region, vb}, false}, {Span{sino_batch, sb}, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    return launched(launch_project(lg_region(g, region, view_begin, view_end, accumulate != 0),
+                                   vol_region, sino_batch, (hipStream_t)stream),
+                    "ct_project_region launch");
+}
+
+ct_status_t ct_backproject_region(ct_geom_t g, const float *sino_batch, int64_t view_begin,
+                                  int64_t view_end, ct_region_t region, float *vol_region,
+                                  int accumulate, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    ct_status_t st = check_region(g, region, view_begin, view_end);
+    if (st != CT_OK) return st;
+    if (!vol_region || !sino_batch) return fail(CT_E_NULL, "buffers must be non-NULL");
+    const size_t vb = (size_t)region.nz * region.ny * region.nx * sizeof(float);
+    const size_t sb = (size_t)(view_end - view_begin) * g->host.U * g->host.V * sizeof(float);
+    st = check_alias({{Span{vol_region, vb}, true}, {Span{sino_batch, sb}, false}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    return launched(launch_backproject(lg_region(g, region, view_begin, view_end, accumulate != 0),
+                                       sino_batch, vol_region, (hipStream_t)stream),
+                    "ct_backproject_region launch");
 }
 
 ct_status_t ct_backproject_atomic(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream) {

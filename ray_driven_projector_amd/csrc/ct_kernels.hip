@@ -545,6 +545,8 @@ struct RayArgs {
     unsigned long long *total; // RM_COUNT
     double *partial;           // RM_PROJECT_SQ, RM_CGLS_R0: one sum of squares per block
     Surface surf;              // detector surface (off == null: flat)
+    int offx, offy, offz;      // voxel index of the volume buffer's first voxel (a region)
+    int accumulate;            // RM_PROJECT: add to the sinogram instead of writing it
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
     int n_utiles, n_vtiles, n_blocks;
@@ -623,6 +625,9 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
         double ox, oy, oz, dx, dy, dz;
         pixel_ray(vw, SURF ? a.surf : Surface{nullptr, 0}, view, u, v, a.U, a.V, ox, oy, oz, dx, dy,
                   dz);
+        ox -= a.offx;   // into the coordinates of the volume buffer (a region of the lattice)
+        oy -= a.offy;
+        oz -= a.offz;
         const size_t ray = ((size_t)view * a.U + u) * a.V + v;
         if (kFwd) {
             float acc = 0.f;
@@ -639,6 +644,7 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
                                   a.spz, ex, ey, ez, rs);
             }
             if (MODE == RM_PROJECT || MODE == RM_PROJECT_SQ) {
+                if (MODE == RM_PROJECT && a.accumulate) acc += a.out[ray];
                 a.out[ray] = acc;
                 if (MODE == RM_PROJECT_SQ) my_sq = (double)acc * acc;
             } else if (MODE == RM_CGLS_R0) {
@@ -733,6 +739,8 @@ struct BrickArgs {
     double *partial;          // BM_CGLS: one sum of s^2 per brick
     Surface surf;             // detector surface (off == null: flat)
     const float *env;         // surface: per-view footprint envelopes
+    int offx, offy, offz;     // voxel index of the volume buffer's first voxel (a region)
+    int accumulate;           // BM_BACKPROJECT: add to the volume instead of writing it
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
     int nbx, nby, nbz, n_blocks;
@@ -1139,9 +1147,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     const int bxi = blk % a.nbx;
     const int byi = (blk / a.nbx) % a.nby;
     const int bzi = blk / (a.nbx * a.nby);
-    const int x0 = bxi * BX, y0 = byi * BY, z0 = bzi * BZ;
+    const int x0 = bxi * BX, y0 = byi * BY, z0 = bzi * BZ;   // within the volume buffer
     const int ex = min(BX, a.W - x0), ey = min(BY, a.H - y0), ez = min(BZ, a.D - z0);
-    const double cbx = x0 + 0.5 * ex, cby = y0 + 0.5 * ey, cbz = z0 + 0.5 * ez;
+    const int gx0 = x0 + a.offx, gy0 = y0 + a.offy, gz0 = z0 + a.offz;   // on the lattice
+    const double cbx = gx0 + 0.5 * ex, cby = gy0 + 0.5 * ey, cbz = gz0 + 0.5 * ez;
     const int lane = threadIdx.x & 63, wv = uni((int)(threadIdx.x >> 6));
     constexpr bool TWO_D = BZ == 1;   // single-slice bricks serve the 2D beams only
     if (MODE == BM_SIRT_UPDATE && a.mask) {
@@ -1164,7 +1173,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
         for (int view = wv; view < a.n_views; view += NWAVES) {
             const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
             Footprint f;
-            if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d,
+            if (!brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
                                  a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f))
                 continue;
             const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
@@ -1198,7 +1207,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     for (int view = wv; view < a.n_views; view += NWAVES) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
         Footprint f;
-        if (!brick_footprint(vw, lane, x0, y0, z0, ex, ey, ez, a.U, a.V, two_d,
+        if (!brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
                              a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f))
             continue;
         if (vw[VT_PERSP] != 0.0)
@@ -1218,7 +1227,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
             const size_t g = ((size_t)(z0 + lz) * a.H + (y0 + ly)) * a.W + (x0 + lx);
             const float val = (float)((double)(long long)acc[lz * LSZ + ly * LSY + lx] * inv_scale);
             if (MODE == BM_BACKPROJECT) {
-                a.vol[g] = val;
+                a.vol[g] = a.accumulate ? a.vol[g] + val : val;
             } else if (MODE == BM_SIRT_UPDATE) {
                 if (!a.mask || a.mask[g]) {
                     float v = fmaf(a.relax * a.cinv[g], val, a.vol[g]);
@@ -1368,6 +1377,8 @@ __global__ __launch_bounds__(256) void cgls_update_p_kernel(float *__restrict__ 
 static RayArgs ray_args(const LaunchGeom &g) {
     RayArgs a{};
     a.order = g.fwd_order;
+    a.offx = g.offx; a.offy = g.offy; a.offz = g.offz;
+    a.accumulate = g.accumulate;
     a.surf = Surface{g.surf_off, g.surf_per_view};
     a.views = g.views;
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
@@ -1492,6 +1503,8 @@ static void launch_brick_shape(BrickArgs &a, const LaunchGeom &g, hipStream_t s)
 template <int MODE>
 static hipError_t launch_brick_args(const LaunchGeom &g, BrickArgs a, hipStream_t s) {
     a.views = g.views;
+    a.offx = g.offx; a.offy = g.offy; a.offz = g.offz;
+    a.accumulate = g.accumulate;
     a.surf = Surface{g.surf_off, g.surf_per_view};
     a.env = g.surf_env;
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;

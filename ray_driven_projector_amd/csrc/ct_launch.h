@@ -17,6 +17,8 @@ struct LaunchGeom {
                            // 3 = 32x16x32, 4 = 32x32x8, 5 = 16x16x32, 6 = 16x16x64
                            // (x by y by z)
     int fwd_order;         // forward block order (see RayArgs::order)
+    int offx, offy, offz;  // region launches: voxel index of the buffer's first voxel
+    int accumulate;        // region launches: add to the output instead of writing it
     const double *surf_off; // detector surface offsets (device float64), or null: flat
     int surf_per_view;      // offsets given per view
     float *surf_env;        // per-view footprint envelopes of the surface (device)
