@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-views", type=int, default=16)
     ap.add_argument("--extra", action="store_true", help="also time A, A^T and atomic A^T alone")
+    ap.add_argument("--host-stream", type=int, nargs=2, metavar=("SLAB", "BATCH_VIEWS"),
+                    help="also time A and A^T with volume and sinogram in pinned host memory "
+                         "(PCIe-inclusive; reported apart from value)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -271,6 +274,27 @@ def main():
         },
     }
     res.update(extra)
+    if args.host_stream:
+        nz, nb = args.host_stream
+        hx = torch.from_numpy(phantom).pin_memory()
+        hy = y.cpu().pin_memory()
+        hs = torch.empty(g.sino_shape, pin_memory=True)
+        hv = torch.empty(g.vol_shape, pin_memory=True)
+        hres = {"plan": {"slab": nz, "batch_views": nb, "axis": "auto"}, "host_memory": "pinned"}
+        for name, fn, a, b in (("A", rdp.ct_project_host, hx, hs), ("AT", rdp.ct_backproject_host, hy, hv)):
+            fn(g, a, b, nz, nb, stream=stream)
+            ts = []
+            for _ in range(3):
+                t = time.perf_counter()
+                fn(g, a, b, nz, nb, stream=stream)
+                ts.append((time.perf_counter() - t) * 1e3)
+            hres[f"{name}_ms"] = round(float(np.median(ts)), 2)
+        n_bt = -(-wl.n_views // nb)
+        vb, sb = 4 * N, 4 * M
+        n_sl_a = -(-wl.vol_shape[0] // nz)   # the adjoint slabs along z; the forward's
+        hres["pcie_bytes"] = {"A": vb * n_bt + sb,   # axis is the library's choice
+                              "AT": sb * (n_sl_a if n_bt > 1 else 1) + vb}
+        res["host_stream"] = hres
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_views)

@@ -43,14 +43,18 @@
  *     volume-sized float32 buffers: copies of the volume in y- or z-fastest
  *     order that the forward projector reads for views whose detector axes run
  *     along y or z (ct_geom_create allocates only those some view needs).  The
- *     forward calls (ct_project, ct_sirt_residual, ct_sirt_step) write these
- *     copies, so such calls on one handle must not overlap in time; use one
- *     handle per stream for concurrent forward projections.  All other calls
- *     only read the handle.
+ *     forward calls (ct_project, ct_project_region, ct_sirt_residual,
+ *     ct_sirt_step*, ct_cgls_*) write these copies, so such calls on one handle
+ *     must not overlap in time; use one handle per stream for concurrent
+ *     forward projections.  All other calls only read the handle.
  *   - Every compute call is asynchronous and ordered on the caller's stream
  *     (a hipStream_t passed as void*; NULL is the legacy default stream).
  *   - Compute calls allocate nothing: all device memory they touch is the
- *     caller's buffers plus the handle's own buffers.
+ *     caller's buffers plus the handle's own buffers.  Two exceptions, both for
+ *     problems larger than one buffer: on a lattice of >= 2^30 voxels the
+ *     volume copies are allocated by the first ct_project_region at that
+ *     region's size (and grown when a later region is larger), and the
+ *     host-streaming calls allocate and free their own device staging.
  *
  * Errors: every call returns a ct_status_t.  Host-side validation happens
  * before anything is enqueued; on error nothing was launched.  A launch
@@ -117,8 +121,11 @@ typedef struct {
  * and not viewing the detector edge-on, the nearer of source and detector
  * centre within 1e6 voxel spacings of the origin and both within 1e15.
  * Tolerances: |norm - 1| <= 1e-6, |dot| <= 1e-6, |ray . normal| > 1e-6.
- * Library limits: D*H*W < 2^30, views*U*V < 2^31, each extent < 2^20, voxel
- * spacings in [1e-10, 1e10] within a ratio of 1e6 of each other.
+ * Library limits: each extent < 2^20, voxel spacings in [1e-10, 1e10] within a
+ * ratio of 1e6 of each other.  Calls that take the whole volume or sinogram as
+ * one device buffer further need D*H*W < 2^30 and views*U*V < 2^31 (else
+ * CT_E_RANGE); larger problems go through the region and host-streaming calls,
+ * whose device buffers obey the same two bounds.
  */
 ct_status_t ct_geom_validate(const ct_geom_desc_t *desc);
 
@@ -212,6 +219,48 @@ ct_status_t ct_project_region(ct_geom_t g, const float *vol_region, ct_region_t 
 ct_status_t ct_backproject_region(ct_geom_t g, const float *sino_batch, int64_t view_begin,
                                   int64_t view_end, ct_region_t region, float *vol_region,
                                   int accumulate, ct_stream_t stream);
+
+/* ---- Host streaming (volumes and sinograms in host memory) ----
+ * The out-of-core pattern of the diffct documentation ("Large Volumes and
+ * Chunked Execution"): the data stay in host memory and pass through the
+ * device in slabs of the volume and batches of views, built on the region
+ * calls above, with uploads, kernels and downloads on three streams of their
+ * own so transfers overlap the kernels.  A^T runs slabs outer, batches inner
+ * (each slab accumulates every batch on the device, then is downloaded); A
+ * runs batches outer, slabs inner.  With one batch (batch_views >= n_views)
+ * the sinogram is uploaded once; with one slab the volume is.
+ * Slab axis: z slabs are contiguous in host memory; y and x slabs are copied
+ * as pitched 2D blocks.  The forward is slow on slabs whose faces are normal
+ * to the detector rows' direction e_v (the rays of one wave enter such a face
+ * at widely spread points): with axis = -1 the forward slabs along z unless
+ * e_v leans mostly on z (e.g. a circular cone orbit about z), else along the
+ * one of y and x that e_v leans on least; the adjoint slabs along z (y in 2D).
+ *
+ * sino_host: (n_views, U, V) float32, vol_host: (D, H, W) float32, both HOST
+ * memory owned by the caller; allocated with hipHostMalloc the copies run
+ * asynchronously, pageable memory works with staged copies.  The calls are
+ * synchronous: they first wait for the work queued on `stream`, and return
+ * when the output is in host memory.  Device memory allocated and freed per
+ * call: A^T: (1 or 2) x slab voxels + (1 or 2) x batch_views*U*V floats (two
+ * buffers only when there is more than one slab / batch); A likewise.  The
+ * handle's forward volume copies are grown to the slab size if smaller.
+ * The A^T result is bit-reproducible for a given plan.
+ *
+ * Errors: CT_E_ARG if a plan size is < 1; CT_E_RANGE if a slab has >= 2^30
+ * voxels or a batch >= 2^31 rays; CT_E_ALIAS if the host buffers overlap;
+ * CT_E_NOMEM if staging cannot be allocated; CT_E_HIP for copy or launch
+ * failures (the output is then incomplete). */
+typedef struct {
+    int64_t slab;          /* planes per device slab along `axis` (>= 1; clamped to the extent) */
+    int64_t batch_views;   /* views per device batch (>= 1; clamped to n_views) */
+    int32_t axis;          /* slab normal: 0 = z, 1 = y, 2 = x, -1 = chosen by the library */
+    int32_t reserved;      /* must be 0 */
+} ct_stream_plan_t;
+
+ct_status_t ct_backproject_host(ct_geom_t g, const float *sino_host, float *vol_host,
+                                ct_stream_plan_t plan, ct_stream_t stream);
+ct_status_t ct_project_host(ct_geom_t g, const float *vol_host, float *sino_host,
+                            ct_stream_plan_t plan, ct_stream_t stream);
 
 /* SIRT weights (once per geometry): row_inv[i] = 1/(A 1)_i, col_inv[j] =
  * 1/(A^T 1)_j, each 0 where the sum is 0.  row_inv: (views,U,V); col_inv:

@@ -31,7 +31,7 @@ CT_VIEW_TABLE_STRIDE = 48
 EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_geom_destroy",
            "ct_geom_view_table",
            "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_project_region",
-           "ct_backproject_region", "ct_sirt_weights",
+           "ct_backproject_region", "ct_project_host", "ct_backproject_host", "ct_sirt_weights",
            "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_sirt_update_bounded",
            "ct_sirt_step_bounded", "ct_cgls_workspace_size",
            "ct_cgls_init", "ct_cgls_step", "ct_cgls_scalars", "ct_count_intersections",
@@ -57,6 +57,14 @@ class Region(ctypes.Structure):
                 ("nz", ctypes.c_int64), ("ny", ctypes.c_int64), ("nx", ctypes.c_int64)]
 
 
+class StreamPlan(ctypes.Structure):
+    _fields_ = [("slab", ctypes.c_int64), ("batch_views", ctypes.c_int64),
+                ("axis", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+AXES = {"auto": -1, "z": 0, "y": 1, "x": 2}
+
+
 _lib = None
 
 
@@ -80,6 +88,8 @@ def lib():
         L.ct_backproject_atomic.argtypes = [vp, vp, vp, vp]
         L.ct_project_region.argtypes = [vp, vp, Region, c.c_int64, c.c_int64, vp, c.c_int, vp]
         L.ct_backproject_region.argtypes = [vp, vp, c.c_int64, c.c_int64, Region, vp, c.c_int, vp]
+        L.ct_project_host.argtypes = [vp, vp, vp, StreamPlan, vp]
+        L.ct_backproject_host.argtypes = [vp, vp, vp, StreamPlan, vp]
         L.ct_sirt_weights.argtypes = [vp, vp, vp, vp]
         L.ct_sirt_residual.argtypes = [vp, vp, vp, vp, vp, vp]
         L.ct_sirt_update.argtypes = [vp, vp, vp, c.c_float, vp, vp]
@@ -254,6 +264,45 @@ def ct_backproject_region(g: Geometry, sino_batch, view_begin, view_end, region,
                                        _ptr(vol_region, (nz, ny, nx), "vol_region"),
                                        int(bool(accumulate)), _stream(stream)))
     return vol_region
+
+
+def _host_ptr(t, shape, name, writable):
+    """Host buffer (a CPU torch tensor, pinned or not, or a numpy array)."""
+    import torch
+    if isinstance(t, np.ndarray):
+        if t.dtype != np.float32 or not t.flags.c_contiguous or (writable and not t.flags.writeable):
+            raise ValueError(f"{name} must be a writable C-contiguous float32 array" if writable
+                             else f"{name} must be a C-contiguous float32 array")
+        p = t.ctypes.data
+    elif isinstance(t, torch.Tensor):
+        if t.is_cuda:
+            raise ValueError(f"{name} must be a host (cpu) tensor")
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor")
+        p = t.data_ptr()
+    else:
+        raise TypeError(f"{name} must be a torch tensor or a numpy array")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(p)
+
+
+def ct_backproject_host(g: Geometry, sino, vol, slab, batch_views, axis="auto", stream=None):
+    """vol = A^T sino with both in host memory, streamed through the device in
+    slabs of `slab` planes along `axis` ("z", "y", "x" or "auto") and batches
+    of batch_views views."""
+    plan = StreamPlan(int(slab), int(batch_views), AXES[axis] if isinstance(axis, str) else int(axis), 0)
+    _check(lib().ct_backproject_host(g.handle, _host_ptr(sino, g.sino_shape, "sino", False),
+                                     _host_ptr(vol, g.vol_shape, "vol", True), plan, _stream(stream)))
+    return vol
+
+
+def ct_project_host(g: Geometry, vol, sino, slab, batch_views, axis="auto", stream=None):
+    """sino = A vol with both in host memory (slabs and view batches)."""
+    plan = StreamPlan(int(slab), int(batch_views), AXES[axis] if isinstance(axis, str) else int(axis), 0)
+    _check(lib().ct_project_host(g.handle, _host_ptr(vol, g.vol_shape, "vol", False),
+                                 _host_ptr(sino, g.sino_shape, "sino", True), plan, _stream(stream)))
+    return sino
 
 
 def ct_backproject_atomic(g: Geometry, sino, vol, stream=None):

@@ -43,6 +43,8 @@ struct ct_geom_s {
     int fwd_order = 5;                  // forward block order: 2 x 2 tile groups, views inside
     float *d_vol_yf = nullptr;          // y-fastest volume copy read by some views' gathers
     float *d_vol_zf = nullptr;          // z-fastest volume copy read by some views' gathers
+    bool need_yf = false, need_zf = false;  // some view reads that copy
+    size_t layout_cap = 0;              // voxels the copies hold (allocated on first use)
     double *d_off = nullptr;            // detector surface offsets (float64), or null: flat
     int surf_per_view = 0;
     float *d_env = nullptr;             // per-view footprint envelopes of the surface
@@ -51,6 +53,12 @@ struct ct_geom_s {
 namespace {
 
 constexpr uint64_t kMagic = 0x43545052'4F4A3031ull;  // "CTPROJ01"
+
+// Whole-volume calls address the volume and the sinogram as single buffers:
+// fewer than 2^30 voxels (32-bit byte offsets in the gathers) and 2^31 rays.
+// Larger lattices are reached through the region and host-streaming calls.
+constexpr int64_t kMaxBufferVoxels = int64_t(1) << 30;
+constexpr int64_t kMaxBufferRays = int64_t(1) << 31;
 
 ct_status_t fail(ct_status_t st, const char *msg) {
     set_error(msg);
@@ -83,6 +91,8 @@ LaunchGeom lg(ct_geom_t g) {
     l.fwd_order = g->fwd_order;
     l.vol_yf = g->d_vol_yf;
     l.vol_zf = g->d_vol_zf;
+    l.need_yf = g->need_yf;
+    l.need_zf = g->need_zf;
     l.surf_off = g->d_off;
     l.surf_per_view = g->surf_per_view;
     l.surf_env = g->d_env;
@@ -113,6 +123,8 @@ ct_status_t check_region(ct_geom_t g, const ct_region_t &r, int64_t vb, int64_t 
         r.y0 + r.ny > h.H || r.x0 + r.nx > h.W)
         return fail(CT_E_SHAPE, "region is empty or not inside the volume");
     if (vb < 0 || ve > h.n_views || vb >= ve) return fail(CT_E_SHAPE, "view range is empty or out of range");
+    if (r.nz * r.ny * r.nx >= kMaxBufferVoxels) return fail(CT_E_RANGE, "region has >= 2^30 voxels");
+    if ((ve - vb) * h.U * h.V >= kMaxBufferRays) return fail(CT_E_RANGE, "view batch has >= 2^31 rays");
     return CT_OK;
 }
 
@@ -184,12 +196,172 @@ ct_status_t launched(hipError_t e, const char *what) {
     return CT_OK;
 }
 
-ct_status_t ensure_device(ct_geom_t g) {
+ct_status_t device_ok(ct_geom_t g) {
     int cur = -1;
     hipError_t e = hipGetDevice(&cur);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (cur != g->device) return fail(CT_E_ARG, "current HIP device differs from the handle's device");
     return CT_OK;
+}
+
+ct_status_t ensure_device(ct_geom_t g) {
+    const GeomHost &h = g->host;
+    if (h.D * h.H * h.W >= kMaxBufferVoxels)
+        return fail(CT_E_RANGE, "whole-volume calls need fewer than 2^30 voxels; use regions");
+    if (h.n_views * h.U * h.V >= kMaxBufferRays)
+        return fail(CT_E_RANGE, "whole-sinogram calls need fewer than 2^31 rays; use view batches");
+    return device_ok(g);
+}
+
+// The forward's volume copies in other axis orders, for a volume buffer of
+// nvox voxels: allocated at the first forward call, grown when a later call
+// needs more (hipFree waits for the device, so no queued launch still reads
+// the old copies).
+ct_status_t ensure_layouts(ct_geom_t g, size_t nvox) {
+    if ((!g->need_yf && !g->need_zf) || nvox <= g->layout_cap) return CT_OK;
+    if (g->d_vol_yf) (void)hipFree(g->d_vol_yf);
+    if (g->d_vol_zf) (void)hipFree(g->d_vol_zf);
+    g->d_vol_yf = g->d_vol_zf = nullptr;
+    g->layout_cap = 0;
+    const size_t bytes = nvox * sizeof(float);
+    if ((g->need_yf && hipMalloc((void **)&g->d_vol_yf, bytes) != hipSuccess) ||
+        (g->need_zf && hipMalloc((void **)&g->d_vol_zf, bytes) != hipSuccess)) {
+        (void)hipGetLastError();
+        if (g->d_vol_yf) (void)hipFree(g->d_vol_yf);
+        g->d_vol_yf = nullptr;
+        return fail(CT_E_NOMEM, "hipMalloc of a volume layout copy failed");
+    }
+    g->layout_cap = nvox;
+    return CT_OK;
+}
+
+size_t full_voxels(ct_geom_t g) { return (size_t)g->host.D * g->host.H * g->host.W; }
+
+// ---- host streaming: device staging, streams and events of one call ----
+struct Staging {
+    hipStream_t cs = nullptr, up = nullptr, down = nullptr;   // compute, host->device, device->host
+    hipEvent_t h2d[2] = {}, used[2] = {}, done[2] = {}, d2h[2] = {};
+    std::vector<void *> bufs;
+
+    hipError_t init() {
+        hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&up, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&down, hipStreamNonBlocking);
+        for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+            e = hipEventCreateWithFlags(&h2d[i], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&used[i], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&done[i], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&d2h[i], hipEventDisableTiming);
+        }
+        return e;
+    }
+    float *alloc(size_t n) {
+        void *p = nullptr;
+        if (hipMalloc(&p, n * sizeof(float)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        bufs.push_back(p);
+        return (float *)p;
+    }
+    // every stream drained, then everything released
+    hipError_t finish() {
+        hipError_t e = hipSuccess, f;
+        for (hipStream_t st : {cs, up, down})
+            if (st && (f = hipStreamSynchronize(st)) != hipSuccess && e == hipSuccess) e = f;
+        return e;
+    }
+    ~Staging() {
+        (void)finish();
+        for (void *p : bufs) (void)hipFree(p);
+        for (int i = 0; i < 2; ++i)
+            for (hipEvent_t ev : {h2d[i], used[i], done[i], d2h[i]})
+                if (ev) (void)hipEventDestroy(ev);
+        for (hipStream_t st : {cs, up, down})
+            if (st) (void)hipStreamDestroy(st);
+    }
+};
+
+// The slab axis the forward prefers: a slab face whose normal runs along the
+// detector rows' direction e_v (e_u in 2D) is crossed by the rays of one wave
+// at widely different points, which desynchronises the wave's gathers; so the
+// forward slabs along z unless e_v leans mostly on z, else along whichever of
+// y and x e_v leans on least.  The adjoint's bricks do not care: it slabs along
+// z (contiguous host copies), or y for 2D.
+int auto_axis(ct_geom_t g, bool forward) {
+    const GeomHost &h = g->host;
+    if (!forward) return h.is2d ? 1 : 0;
+    double sc[3] = {0, 0, 0};   // mean |e . axis| for z, y, x
+    for (int64_t k = 0; k < h.n_views; ++k) {
+        const double *t = g->table.data() + (size_t)k * CT_VIEW_TABLE_STRIDE + (h.is2d ? VT_EU : VT_EV);
+        const double ex = t[0] * h.sx, ey = t[1] * h.sy, ez = t[2] * h.sz;   // back to world units
+        const double n = std::sqrt(ex * ex + ey * ey + ez * ez);
+        if (n > 0) {
+            sc[0] += std::fabs(ez) / n;
+            sc[1] += std::fabs(ey) / n;
+            sc[2] += std::fabs(ex) / n;
+        }
+    }
+    for (double &v : sc) v /= (double)h.n_views;
+    if (!h.is2d && sc[0] <= 0.5) return 0;
+    return sc[2] < sc[1] ? 2 : 1;
+}
+
+// Validates a host-streaming call; returns the slab axis, thickness and batch size.
+ct_status_t check_plan(ct_geom_t g, const void *vol, const void *sino, ct_stream_plan_t plan,
+                       bool forward, int &axis, int64_t &ns, int64_t &nb) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!vol || !sino) return fail(CT_E_NULL, "vol and sino must be non-NULL");
+    if (plan.slab < 1 || plan.batch_views < 1) return fail(CT_E_ARG, "plan sizes must be >= 1");
+    if (plan.axis < -1 || plan.axis > 2 || plan.reserved != 0)
+        return fail(CT_E_ARG, "plan axis must be -1, 0, 1 or 2 and reserved 0");
+    const GeomHost &h = g->host;
+    axis = plan.axis < 0 ? auto_axis(g, forward) : plan.axis;
+    const int64_t ext[3] = {h.D, h.H, h.W};
+    ns = std::min<int64_t>(plan.slab, ext[axis]);
+    nb = std::min<int64_t>(plan.batch_views, h.n_views);
+    const int64_t slab_vox = h.D * h.H * h.W / ext[axis] * ns;
+    if (slab_vox >= kMaxBufferVoxels) return fail(CT_E_RANGE, "slab has >= 2^30 voxels");
+    if (nb * h.U * h.V >= kMaxBufferRays) return fail(CT_E_RANGE, "view batch has >= 2^31 rays");
+    ct_status_t st = check_alias({{Span{vol, vol_bytes(g)}, true}, {Span{sino, sino_bytes(g)}, true}});
+    if (st != CT_OK) return st;
+    return device_ok(g);
+}
+
+// Slab k of thickness ns along axis (0 = z, 1 = y, 2 = x), clipped to the volume.
+ct_region_t slab_region(ct_geom_t g, int axis, int64_t k, int64_t ns) {
+    const GeomHost &h = g->host;
+    ct_region_t r{0, 0, 0, h.D, h.H, h.W};
+    int64_t *lo = axis == 0 ? &r.z0 : (axis == 1 ? &r.y0 : &r.x0);
+    int64_t *n = axis == 0 ? &r.nz : (axis == 1 ? &r.ny : &r.nx);
+    *lo = k * ns;
+    *n = std::min<int64_t>(ns, *n - *lo);
+    return r;
+}
+
+// Copies a slab between the host volume (D, H, W) and its packed device buffer.
+hipError_t copy_slab(ct_geom_t g, const ct_region_t &r, float *host_vol, float *dev, bool to_device,
+                     hipStream_t s) {
+    const size_t W = (size_t)g->host.W, H = (size_t)g->host.H;
+    float *hp = host_vol + ((size_t)r.z0 * H + r.y0) * W + r.x0;
+    const size_t f = sizeof(float);
+    size_t width, rows, hpitch;
+    if (r.ny == (int64_t)H && r.nx == (int64_t)W) {   // z slab: one contiguous block
+        const size_t bytes = (size_t)r.nz * H * W * f;
+        return to_device ? hipMemcpyAsync(dev, hp, bytes, hipMemcpyHostToDevice, s)
+                         : hipMemcpyAsync(hp, dev, bytes, hipMemcpyDeviceToHost, s);
+    }
+    if (r.nx == (int64_t)W) {   // y slab: one row of ny*W per z plane
+        width = (size_t)r.ny * W * f;
+        rows = (size_t)r.nz;
+        hpitch = H * W * f;
+    } else {                    // x slab: one row of nx per (z, y)
+        width = (size_t)r.nx * f;
+        rows = (size_t)r.nz * r.ny;
+        hpitch = W * f;
+    }
+    return to_device ? hipMemcpy2DAsync(dev, width, hp, hpitch, width, rows, hipMemcpyHostToDevice, s)
+                     : hipMemcpy2DAsync(hp, hpitch, dev, width, width, rows, hipMemcpyDeviceToHost, s);
 }
 
 }  // namespace
@@ -287,19 +459,20 @@ static ct_status_t create_impl(const ct_geom_desc_t *desc, const double *offsets
         delete g;
         return hip_fail(e, "hipMemcpy of the view table");
     }
-    // volume copies in other axis orders, for the views whose gathers read them
-    bool need_y = false, need_z = false;
+    // volume copies in other axis orders, for the views whose gathers read them:
+    // whole-volume size here when the volume fits one buffer, else allocated by
+    // the first region forward at its region's size
     for (int64_t k = 0; k < h.n_views; ++k) {
         const double lay = g->table[(size_t)k * CT_VIEW_TABLE_STRIDE + VT_LAYOUT];
-        need_y = need_y || lay == 1.0;
-        need_z = need_z || lay == 2.0;
+        g->need_yf = g->need_yf || lay == 1.0;
+        g->need_zf = g->need_zf || lay == 2.0;
     }
-    const size_t vbytes = (size_t)h.D * h.H * h.W * sizeof(float);
-    if ((need_y && hipMalloc((void **)&g->d_vol_yf, vbytes) != hipSuccess) ||
-        (need_z && hipMalloc((void **)&g->d_vol_zf, vbytes) != hipSuccess)) {
-        (void)hipGetLastError();
-        free_handle(g);
-        return fail(CT_E_NOMEM, "hipMalloc of a volume layout copy failed");
+    if (h.D * h.H * h.W < kMaxBufferVoxels) {
+        st = ensure_layouts(g, full_voxels(g));
+        if (st != CT_OK) {
+            free_handle(g);
+            return st;
+        }
     }
     if (offsets) {
         // surface offsets, then the per-view footprint envelopes (synchronous)
@@ -356,6 +529,7 @@ ct_status_t ct_project(ct_geom_t g, const float *vol, float *sino, ct_stream_t s
     ct_status_t st = check_alias({{V, false}, {S, true}});
     if (st != CT_OK) return st;
     if ((st = ensure_device(g)) != CT_OK) return st;
+    if ((st = ensure_layouts(g, full_voxels(g))) != CT_OK) return st;
     return launched(launch_project(lg(g), vol, sino, (hipStream_t)stream), "ct_project launch");
 }
 
@@ -380,7 +554,8 @@ ct_status_t ct_project_region(ct_geom_t g, const float *vol_region, ct_region_t 
     const size_t sb = (size_t)(view_end - view_begin) * g->host.U * g->host.V * sizeof(float);
     st = check_alias({{Span{vol_region, vb}, false}, {Span{sino_batch, sb}, true}});
     if (st != CT_OK) return st;
-    if ((st = ensure_device(g)) != CT_OK) return st;
+    if ((st = device_ok(g)) != CT_OK) return st;
+    if ((st = ensure_layouts(g, vb / sizeof(float))) != CT_OK) return st;
     return launched(launch_project(lg_region(g, region, view_begin, view_end, accumulate != 0),
                                    vol_region, sino_batch, (hipStream_t)stream),
                     "ct_project_region launch");
@@ -397,7 +572,7 @@ ct_status_t ct_backproject_region(ct_geom_t g, const float *sino_batch, int64_t 
     const size_t sb = (size_t)(view_end - view_begin) * g->host.U * g->host.V * sizeof(float);
     st = check_alias({{Span{vol_region, vb}, true}, {Span{sino_batch, sb}, false}});
     if (st != CT_OK) return st;
-    if ((st = ensure_device(g)) != CT_OK) return st;
+    if ((st = device_ok(g)) != CT_OK) return st;
     return launched(launch_backproject(lg_region(g, region, view_begin, view_end, accumulate != 0),
                                        sino_batch, vol_region, (hipStream_t)stream),
                     "ct_backproject_region launch");
@@ -434,6 +609,7 @@ ct_status_t ct_sirt_residual(ct_geom_t g, const float *x, const float *y, const 
     ct_status_t st = check_alias({{X, false}, {Y, false}, {R, false}, {E, true}});
     if (st != CT_OK) return st;
     if ((st = ensure_device(g)) != CT_OK) return st;
+    if ((st = ensure_layouts(g, full_voxels(g))) != CT_OK) return st;
     return launched(launch_residual(lg(g), x, y, row_inv, work_sino, (hipStream_t)stream),
                     "ct_sirt_residual launch");
 }
@@ -484,6 +660,7 @@ ct_status_t ct_sirt_step_bounded(ct_geom_t g, float *x, const float *y, const fl
     if (st == CT_OK && mask) st = check_alias({{X, true}, {E, true}, {M, false}});
     if (st != CT_OK) return st;
     if ((st = ensure_device(g)) != CT_OK) return st;
+    if ((st = ensure_layouts(g, full_voxels(g))) != CT_OK) return st;
     hipError_t e = launch_residual(lg(g), x, y, row_inv, work_sino, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "ct_sirt_step_bounded residual launch");
     return launched(launch_sirt_update_bounded(lg(g), work_sino, col_inv, relax, lo, hi, mask, x,
@@ -501,6 +678,7 @@ ct_status_t ct_sirt_step(ct_geom_t g, float *x, const float *y, const float *row
     ct_status_t st = check_alias({{X, true}, {Y, false}, {R, false}, {C, false}, {E, true}});
     if (st != CT_OK) return st;
     if ((st = ensure_device(g)) != CT_OK) return st;
+    if ((st = ensure_layouts(g, full_voxels(g))) != CT_OK) return st;
     hipError_t e = launch_residual(lg(g), x, y, row_inv, work_sino, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "ct_sirt_step residual launch");
     return launched(launch_sirt_update(lg(g), work_sino, col_inv, relax, x, (hipStream_t)stream),
@@ -537,6 +715,7 @@ ct_status_t ct_cgls_init(ct_geom_t g, const float *y, const float *x, float *r, 
     ct_status_t st = check_alias({{Y, false}, {X, false}, {R, true}, {S, true}, {P, true}, {Wk, true}});
     if (st != CT_OK) return st;
     if ((st = ensure_device(g)) != CT_OK) return st;
+    if ((st = ensure_layouts(g, full_voxels(g))) != CT_OK) return st;
     double *state = (double *)work;
     return launched(launch_cgls_init(lg(g), y, x, r, s, p, state, state + kCglsStateDoubles,
                                      (hipStream_t)stream),
@@ -555,6 +734,7 @@ ct_status_t ct_cgls_step(ct_geom_t g, float *x, float *r, float *s, float *p, fl
     ct_status_t st = check_alias({{X, true}, {R, true}, {S, true}, {P, true}, {Q, true}, {Wk, true}});
     if (st != CT_OK) return st;
     if ((st = ensure_device(g)) != CT_OK) return st;
+    if ((st = ensure_layouts(g, full_voxels(g))) != CT_OK) return st;
     double *state = (double *)work;
     return launched(launch_cgls_step(lg(g), x, r, s, p, q, state, state + kCglsStateDoubles,
                                      (hipStream_t)stream),
@@ -597,6 +777,123 @@ ct_status_t ct_count_intersections(ct_geom_t g, uint32_t *per_ray, uint64_t *tot
     *total = (uint64_t)host;
     set_error("");
     return CT_OK;
+}
+
+// ---- host-streaming A^T and A ----
+
+// A^T: slabs outer, view batches inner.  Each slab accumulates the batches'
+// adjoints on the device, then goes back to the host while the next slab runs.
+// Batch k's upload waits for the kernel that last read its buffer (batch k-2);
+// slab s's first kernel waits for the download of slab s-2.
+ct_status_t ct_backproject_host(ct_geom_t g, const float *sino_host, float *vol_host,
+                                ct_stream_plan_t plan, ct_stream_t stream) {
+    int axis = 0;
+    int64_t ns = 0, nb = 0;
+    ct_status_t st = check_plan(g, vol_host, sino_host, plan, false, axis, ns, nb);
+    if (st != CT_OK) return st;
+    const GeomHost &h = g->host;
+    const int64_t ext = axis == 0 ? h.D : (axis == 1 ? h.H : h.W);
+    const int64_t n_slabs = (ext + ns - 1) / ns, n_batches = (h.n_views + nb - 1) / nb;
+    const size_t ray_per_view = (size_t)h.U * h.V;
+    const size_t slab_vox = (size_t)(h.D * h.H * h.W / ext) * ns;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);   // after the caller's queued work
+    if (e != hipSuccess) return hip_fail(e, "ct_backproject_host: caller stream");
+    Staging k;
+    if ((e = k.init()) != hipSuccess) return hip_fail(e, "ct_backproject_host: streams");
+    float *vbuf[2] = {k.alloc(slab_vox), n_slabs > 1 ? k.alloc(slab_vox) : nullptr};
+    float *sbuf[2] = {k.alloc(nb * ray_per_view), n_batches > 1 ? k.alloc(nb * ray_per_view) : nullptr};
+    if (!vbuf[0] || !sbuf[0] || (n_slabs > 1 && !vbuf[1]) || (n_batches > 1 && !sbuf[1]))
+        return fail(CT_E_NOMEM, "ct_backproject_host: device staging allocation failed");
+    auto ok = [&](hipError_t r) { if (e == hipSuccess) e = r; return e == hipSuccess; };
+    if (n_batches == 1) {   // one batch: the sinogram is uploaded once and stays
+        ok(hipMemcpyAsync(sbuf[0], sino_host, h.n_views * ray_per_view * sizeof(float),
+                          hipMemcpyHostToDevice, k.up));
+        ok(hipEventRecord(k.h2d[0], k.up));
+        ok(hipStreamWaitEvent(k.cs, k.h2d[0], 0));
+    }
+    int64_t kb = 0;
+    for (int64_t s = 0; s < n_slabs && e == hipSuccess; ++s) {
+        const ct_region_t r = slab_region(g, axis, s, ns);
+        const int vs = (int)(s & 1);
+        if (s >= 2) ok(hipStreamWaitEvent(k.cs, k.d2h[vs], 0));
+        for (int64_t b = 0; b < n_batches && e == hipSuccess; ++b, ++kb) {
+            const int64_t vb = b * nb, ve = std::min<int64_t>(h.n_views, vb + nb);
+            const int bs = n_batches == 1 ? 0 : (int)(kb & 1);
+            if (n_batches > 1) {
+                if (kb >= 2) ok(hipStreamWaitEvent(k.up, k.used[bs], 0));
+                ok(hipMemcpyAsync(sbuf[bs], sino_host + vb * ray_per_view,
+                                  (ve - vb) * ray_per_view * sizeof(float), hipMemcpyHostToDevice, k.up));
+                ok(hipEventRecord(k.h2d[bs], k.up));
+                ok(hipStreamWaitEvent(k.cs, k.h2d[bs], 0));
+            }
+            ok(launch_backproject(lg_region(g, r, vb, ve, b > 0), sbuf[bs], vbuf[vs], k.cs));
+            if (n_batches > 1) ok(hipEventRecord(k.used[bs], k.cs));
+        }
+        ok(hipEventRecord(k.done[vs], k.cs));
+        ok(hipStreamWaitEvent(k.down, k.done[vs], 0));
+        ok(copy_slab(g, r, vol_host, vbuf[vs], false, k.down));
+        ok(hipEventRecord(k.d2h[vs], k.down));
+    }
+    const hipError_t f = k.finish();
+    if (e == hipSuccess) e = f;
+    return launched(e, "ct_backproject_host");
+}
+
+// A: view batches outer, slabs inner.  Each batch accumulates the slabs'
+// projections on the device, then goes back to the host.
+ct_status_t ct_project_host(ct_geom_t g, const float *vol_host, float *sino_host, ct_stream_plan_t plan,
+                            ct_stream_t stream) {
+    int axis = 0;
+    int64_t ns = 0, nb = 0;
+    ct_status_t st = check_plan(g, vol_host, sino_host, plan, true, axis, ns, nb);
+    if (st != CT_OK) return st;
+    const GeomHost &h = g->host;
+    const int64_t ext = axis == 0 ? h.D : (axis == 1 ? h.H : h.W);
+    const int64_t n_slabs = (ext + ns - 1) / ns, n_batches = (h.n_views + nb - 1) / nb;
+    const size_t ray_per_view = (size_t)h.U * h.V;
+    const size_t slab_vox = (size_t)(h.D * h.H * h.W / ext) * ns;
+    if ((st = ensure_layouts(g, slab_vox)) != CT_OK) return st;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ct_project_host: caller stream");
+    Staging k;
+    if ((e = k.init()) != hipSuccess) return hip_fail(e, "ct_project_host: streams");
+    float *vbuf[2] = {k.alloc(slab_vox), n_slabs > 1 ? k.alloc(slab_vox) : nullptr};
+    float *sbuf[2] = {k.alloc(nb * ray_per_view), n_batches > 1 ? k.alloc(nb * ray_per_view) : nullptr};
+    if (!vbuf[0] || !sbuf[0] || (n_slabs > 1 && !vbuf[1]) || (n_batches > 1 && !sbuf[1]))
+        return fail(CT_E_NOMEM, "ct_project_host: device staging allocation failed");
+    auto ok = [&](hipError_t r) { if (e == hipSuccess) e = r; return e == hipSuccess; };
+    float *vol_src = const_cast<float *>(vol_host);   // only read: copies go host -> device
+    if (n_slabs == 1) {   // one slab: the volume is uploaded once and stays
+        ok(copy_slab(g, slab_region(g, axis, 0, ns), vol_src, vbuf[0], true, k.up));
+        ok(hipEventRecord(k.h2d[0], k.up));
+        ok(hipStreamWaitEvent(k.cs, k.h2d[0], 0));
+    }
+    int64_t ks = 0;
+    for (int64_t b = 0; b < n_batches && e == hipSuccess; ++b) {
+        const int64_t vb = b * nb, ve = std::min<int64_t>(h.n_views, vb + nb);
+        const int bs = (int)(b & 1);
+        if (b >= 2) ok(hipStreamWaitEvent(k.cs, k.d2h[bs], 0));
+        for (int64_t s = 0; s < n_slabs && e == hipSuccess; ++s, ++ks) {
+            const ct_region_t r = slab_region(g, axis, s, ns);
+            const int vs = n_slabs == 1 ? 0 : (int)(ks & 1);
+            if (n_slabs > 1) {
+                if (ks >= 2) ok(hipStreamWaitEvent(k.up, k.used[vs], 0));
+                ok(copy_slab(g, r, vol_src, vbuf[vs], true, k.up));
+                ok(hipEventRecord(k.h2d[vs], k.up));
+                ok(hipStreamWaitEvent(k.cs, k.h2d[vs], 0));
+            }
+            ok(launch_project(lg_region(g, r, vb, ve, s > 0), vbuf[vs], sbuf[bs], k.cs));
+            if (n_slabs > 1) ok(hipEventRecord(k.used[vs], k.cs));
+        }
+        ok(hipEventRecord(k.done[bs], k.cs));
+        ok(hipStreamWaitEvent(k.down, k.done[bs], 0));
+        ok(hipMemcpyAsync(sino_host + vb * ray_per_view, sbuf[bs], (ve - vb) * ray_per_view * sizeof(float),
+                          hipMemcpyDeviceToHost, k.down));
+        ok(hipEventRecord(k.d2h[bs], k.down));
+    }
+    const hipError_t f = k.finish();
+    if (e == hipSuccess) e = f;
+    return launched(e, "ct_project_host");
 }
 
 }  // extern "C"

@@ -75,8 +75,6 @@ ct_status_t validate_desc(const ct_geom_desc_t *desc, GeomHost *out, const char 
         *why = "an extent is >= 2^20";
         return CT_E_RANGE;
     }
-    if (g.D * g.H * g.W >= (int64_t(1) << 30)) { *why = "volume has >= 2^30 voxels"; return CT_E_RANGE; }
-    if (g.n_views * g.U * g.V >= (int64_t(1) << 31)) { *why = "sinogram has >= 2^31 rays"; return CT_E_RANGE; }
 
     for (int k = 0; k < 3; ++k)
         if (!std::isfinite(desc->voxel_spacing[k])) { *why = "voxel spacing not finite"; return CT_E_NONFINITE; }

@@ -1420,6 +1420,7 @@ hipError_t launch_fill(float *p, size_t n, float v, hipStream_t s) {
 static hipError_t stage_layouts(const LaunchGeom &g, const float *vol, RayArgs &a, hipStream_t s) {
     a.vol_yf = g.vol_yf;
     a.vol_zf = g.vol_zf;
+    if ((g.need_yf && !g.vol_yf) || (g.need_zf && !g.vol_zf)) return hipErrorInvalidValue;
     const size_t W = g.W, H = g.H, D = g.D;
     if (g.vol_yf) {   // (z, x, y): per z slice, transpose (y, x) -> (x, y)
         dim3 grid((unsigned)((W + 31) / 32), (unsigned)((H + 31) / 32), (unsigned)D);

@@ -24,6 +24,7 @@ struct LaunchGeom {
     float *surf_env;        // per-view footprint envelopes of the surface (device)
     float *vol_yf;         // handle-owned y-fastest volume copy, or null if no view reads it
     float *vol_zf;         // handle-owned z-fastest volume copy, or null if no view reads it
+    bool need_yf, need_zf; // some view's gathers read that copy
 };
 
 hipError_t launch_fill(float *p, size_t n, float v, hipStream_t s);

@@ -81,7 +81,10 @@ def test_validation_error_codes(L):
     assert rdp.ct_geom_validate(*_variant(cone, det_shape=(8, 0))) == rdp.CT_E_SHAPE
     assert rdp.ct_geom_validate(*_variant(fan, vol_shape=(2, 512, 512))) == rdp.CT_E_SHAPE
     assert rdp.ct_geom_validate(*_variant(fan, det_shape=(736, 2))) == rdp.CT_E_SHAPE
-    assert rdp.ct_geom_validate(*_variant(cone, vol_shape=(1024, 1024, 1024))) == rdp.CT_E_RANGE
+    # lattices beyond one buffer are valid (reached by the region and streaming calls)
+    assert rdp.ct_geom_validate(*_variant(cone, vol_shape=(1024, 1024, 1024))) == rdp.CT_OK
+    assert rdp.ct_geom_validate(*_variant(cone, vol_shape=(1 << 20, 8, 8))) == rdp.CT_E_RANGE
+    assert rdp.ct_geom_validate(*_variant(cone, det_shape=(8, 1 << 20))) == rdp.CT_E_RANGE
     # spacings
     assert rdp.ct_geom_validate(*_variant(cone, voxel_spacing=(1, -1, 1))) == rdp.CT_E_ARG
     assert rdp.ct_geom_validate(*_variant(cone, det_spacing=(0.0, 1))) == rdp.CT_E_ARG
