@@ -1,0 +1,340 @@
+"""Float64 oracle of analytical FBP / FDK (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the benchmark's
+CPU-baseline leg; the product path never imports it.  Plain numpy, float64,
+written to read like the definitions; it shares no code with the HIP library.
+
+What is computed (diffct documentation, "Differentiable analytical
+reconstruction", the "Analytical Reconstruction Helpers" and "Ramp Filter
+Options" sections of the API reference, and the FBP/FDK example pages):
+
+  1. pre-weights on the sinogram: the fan/cone cosine weight of each pixel and,
+     for short scans, Parker's weights;
+  2. a ramp filter along the detector u axis, zero-padded to pad_factor * U
+     samples and applied as a real-FFT multiplier, optionally windowed;
+  3. angular quadrature weights per view (a full fan/cone turn carries the 1/2
+     redundancy factor);
+  4. a voxel-driven, interpolating weighted backprojection (not the Siddon
+     adjoint): each voxel gathers, per view, the bilinearly interpolated
+     filtered value where its centre projects on the detector, times the
+     FDK distance weight R D / U(x)^2 (fan/cone) or 1 (parallel).
+  The transpose of step 4 scatters the same interpolation coefficients.
+
+Readings where the pages give no formula (each listed in the design notes):
+  - Ram-Lak: the band-limited ramp of Ramachandran and Lakshminarayanan sampled
+    in space (Kak and Slaney, "Principles of Computerized Tomographic Imaging",
+    ch. 3): h[0] = 1/(4 d^2), h[n] = -1/(pi n d)^2 for odd n, 0 for even n != 0,
+    taken P-periodic (n in [-P/2, P/2)); the multiplier is d * DFT_P(h).
+    Windows of the normalised frequency f = k / P in [0, 1/2]: Shepp-Logan
+    sin(pi f)/(pi f), cosine cos(pi f), Hamming 0.54 + 0.46 cos(2 pi f), Hann
+    0.5 + 0.5 cos(2 pi f).
+  - Cosine weight |(p - a).n| / |p - a| for pixel centre p, source a and unit
+    detector normal n.
+  - Angular weights: half the angular gap to the two neighbouring views,
+    periodic over the scan's period (2 pi for full fan/cone turns and for
+    redundant parallel turns, pi for parallel half turns), non-periodic
+    (one-sided at the ends) for short scans; times 1/2 for redundant full turns.
+  - FDK weight R D / U(x)^2 with U(x) = (x - a).n, D = (c - a).n and
+    R = (iso - a).n; the isocentre, when not given, is the point nearest (least
+    squares) to the lines through each source along its detector normal.
+  - Parker weights (Parker 1982) with beta the scan angle from the first view
+    and gamma the in-plane fan angle of the column, signed in the sense of
+    rotation; delta is the largest |gamma|.
+  - Interpolation treats detector samples outside [0, U-1] x [0, V-1] as 0.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+PARALLEL2D, FAN2D, CONE, PARALLEL3D = 0, 1, 2, 3
+WINDOWS = ("ram-lak", "shepp-logan", "cosine", "hamming", "hann")
+
+
+# ---------------------------------------------------------------------------
+# ramp filter
+# ---------------------------------------------------------------------------
+
+def ramlak_kernel(P: int, spacing: float) -> np.ndarray:
+    """The P-periodic band-limited ramp h[n], n = 0..P-1 (n >= P/2 stands for n - P)."""
+    n = np.arange(P)
+    n = np.where(n >= P // 2 + (P % 2), n - P, n)   # signed index in [-P/2, P/2)
+    h = np.zeros(P)
+    h[n == 0] = 1.0 / (4.0 * spacing * spacing)
+    odd = (n % 2) != 0
+    h[odd] = -1.0 / (math.pi * n[odd] * spacing) ** 2
+    return h
+
+
+def window_values(P: int, window: str) -> np.ndarray:
+    """Window at the rFFT frequencies k / P, k = 0..P//2."""
+    f = np.arange(P // 2 + 1) / P
+    if window in (None, "ram-lak"):
+        return np.ones_like(f)
+    if window == "shepp-logan":
+        return np.sinc(f)          # numpy's sinc is sin(pi f) / (pi f)
+    if window == "cosine":
+        return np.cos(math.pi * f)
+    if window == "hamming":
+        return 0.54 + 0.46 * np.cos(2 * math.pi * f)
+    if window in ("hann", "hanning"):
+        return 0.5 + 0.5 * np.cos(2 * math.pi * f)
+    raise ValueError(f"unknown window {window!r}")
+
+
+def ramp_multiplier(P: int, spacing: float, window: str = "ram-lak") -> np.ndarray:
+    """Real rFFT multiplier (length P//2 + 1) in physical units (1 / length)."""
+    h = ramlak_kernel(P, spacing)
+    M = spacing * np.fft.rfft(h).real
+    return M * window_values(P, window)
+
+
+def ramp_filter(p: np.ndarray, spacing: float, pad_factor: int = 2, window: str = "ram-lak",
+                axis: int = 1) -> np.ndarray:
+    """Filter along `axis` (zero-padded to pad_factor * N, rFFT multiplier, cropped)."""
+    p = np.moveaxis(np.asarray(p, dtype=np.float64), axis, -1)
+    N = p.shape[-1]
+    P = pad_factor * N
+    M = ramp_multiplier(P, spacing, window)
+    q = np.fft.irfft(np.fft.rfft(p, n=P, axis=-1) * M, n=P, axis=-1)[..., :N]
+    return np.moveaxis(q, -1, axis)
+
+
+# ---------------------------------------------------------------------------
+# geometry helpers
+# ---------------------------------------------------------------------------
+
+def _three_d(beam: int) -> bool:
+    return beam in (CONE, PARALLEL3D)
+
+
+def detector_normals(frames: np.ndarray, beam: int) -> np.ndarray:
+    """Unit detector normal per view, oriented from the source side to the detector."""
+    a, c, eu, ev = frames[:, 0:3], frames[:, 3:6], frames[:, 6:9], frames[:, 9:12]
+    if _three_d(beam):
+        n = np.cross(eu, ev)
+    else:
+        n = np.stack([eu[:, 1], -eu[:, 0], np.zeros(len(eu))], 1)
+    n = n / np.linalg.norm(n, axis=1, keepdims=True)
+    if beam in (FAN2D, CONE):
+        toward = np.einsum("ij,ij->i", c - a, n)
+    else:
+        toward = np.einsum("ij,ij->i", a, n)     # parallel: along the ray direction
+    return n * np.where(toward < 0, -1.0, 1.0)[:, None]
+
+
+def pixel_centres(wl) -> np.ndarray:
+    """(views, U, V, 3) world positions of the flat detector's pixel centres."""
+    fr = wl.frames
+    U, V = wl.det_shape
+    du, dv = wl.det_spacing
+    ou = (np.arange(U) - 0.5 * (U - 1)) * du
+    ov = (np.arange(V) - 0.5 * (V - 1)) * dv if _three_d(wl.beam) else np.zeros(V)
+    c, eu, ev = fr[:, 3:6], fr[:, 6:9], fr[:, 9:12]
+    return (c[:, None, None, :] + ou[None, :, None, None] * eu[:, None, None, :]
+            + ov[None, None, :, None] * ev[:, None, None, :])
+
+
+def cosine_weights(wl) -> np.ndarray:
+    """|(p - a).n| / |p - a| per pixel for fan/cone; ones for parallel beams."""
+    if wl.beam not in (FAN2D, CONE):
+        return np.ones(wl.sino_shape)
+    p = pixel_centres(wl)
+    a = wl.frames[:, None, None, 0:3]
+    n = detector_normals(wl.frames, wl.beam)[:, None, None, :]
+    d = p - a
+    return np.abs(np.sum(d * n, axis=-1)) / np.linalg.norm(d, axis=-1)
+
+
+def isocentre(wl) -> np.ndarray:
+    """Least-squares point nearest to the lines a_i + t n_i (fan/cone; origin for
+    parallel beams).  2D: in the z = 0 plane."""
+    if wl.beam not in (FAN2D, CONE):
+        return np.zeros(3)
+    a = wl.frames[:, 0:3]
+    n = detector_normals(wl.frames, wl.beam)
+    dim = 3 if wl.beam == CONE else 2
+    Asum = np.zeros((dim, dim))
+    bsum = np.zeros(dim)
+    for ai, ni in zip(a[:, :dim], n[:, :dim]):
+        Pm = np.eye(dim) - np.outer(ni, ni) / np.dot(ni, ni)
+        Asum += Pm
+        bsum += Pm @ ai
+    x = np.linalg.lstsq(Asum, bsum, rcond=None)[0]
+    out = np.zeros(3)
+    out[:dim] = x
+    return out
+
+
+def angular_weights(angles, beam: int, short_scan: bool = False, redundant=None) -> np.ndarray:
+    """Quadrature weight per view (see the module notes)."""
+    th = np.asarray(angles, dtype=np.float64)
+    n = len(th)
+    if redundant is None:
+        redundant = beam in (FAN2D, CONE) and not short_scan
+    if n == 1:
+        return np.array([math.pi if not redundant else math.pi])
+    if short_scan:
+        w = np.empty(n)
+        w[1:-1] = 0.5 * (th[2:] - th[:-2])
+        w[0] = 0.5 * (th[1] - th[0])
+        w[-1] = 0.5 * (th[-1] - th[-2])
+        w = np.abs(w)
+    else:
+        period = 2 * math.pi if (beam in (FAN2D, CONE) or redundant) else math.pi
+        sgn = 1.0 if th[-1] >= th[0] else -1.0
+        nxt = np.concatenate([th[1:], [th[0] + sgn * period]])
+        prv = np.concatenate([[th[-1] - sgn * period], th[:-1]])
+        w = np.abs(0.5 * (nxt - prv))
+    return w * (0.5 if redundant else 1.0)
+
+
+def rotation_sense(wl) -> float:
+    """+1 if the source moves counter-clockwise about z (seen from +z), else -1."""
+    a = wl.frames[:, 0:2]
+    cr = a[:-1, 0] * a[1:, 1] - a[:-1, 1] * a[1:, 0]
+    return 1.0 if cr.sum() >= 0 else -1.0
+
+
+def fan_angles(wl) -> np.ndarray:
+    """(views, U) in-plane angle between the central ray and the ray through the
+    centre of column u, positive in the sense of rotation."""
+    p = pixel_centres(wl)[:, :, 0, :]             # v at the first row: only x, y matter
+    a = wl.frames[:, None, 0:3]
+    n = detector_normals(wl.frames, wl.beam)[:, None, :]
+    d = (p - a)[..., :2]
+    d0 = np.broadcast_to(n[..., :2], d.shape)
+    cross = d0[..., 0] * d[..., 1] - d0[..., 1] * d[..., 0]
+    dot = np.sum(d0 * d, axis=-1)
+    return rotation_sense(wl) * np.arctan2(cross, dot)
+
+
+def parker(beta: np.ndarray, gamma: np.ndarray, delta: float) -> np.ndarray:
+    """Parker's short-scan weight w(beta, gamma) for a half fan angle delta."""
+    beta = np.asarray(beta, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    w = np.zeros(np.broadcast(beta, gamma).shape)
+    b = np.broadcast_to(beta, w.shape)
+    g = np.broadcast_to(gamma, w.shape)
+    r1 = (b >= 0) & (b < 2 * (delta - g))
+    r2 = (b >= 2 * (delta - g)) & (b <= math.pi - 2 * g)
+    r3 = (b > math.pi - 2 * g) & (b <= math.pi + 2 * delta)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        w = np.where(r1, np.sin(math.pi / 4 * b / (delta - g)) ** 2, w)
+        w = np.where(r2, 1.0, w)
+        w = np.where(r3, np.sin(math.pi / 4 * (math.pi + 2 * delta - b) / (delta + g)) ** 2, w)
+    return w
+
+
+def parker_weights(wl, angles) -> np.ndarray:
+    """(views, U) Parker weights of a fan/cone short scan."""
+    th = np.asarray(angles, dtype=np.float64)
+    beta = np.abs(th - th[0])
+    gam = fan_angles(wl)
+    delta = float(np.max(np.abs(gam)))
+    return parker(beta[:, None], gam, delta)
+
+
+# ---------------------------------------------------------------------------
+# filtering and the weighted backprojection
+# ---------------------------------------------------------------------------
+
+def filter_sinogram(wl, sino, angles, window="ram-lak", pad_factor=2, short_scan=False,
+                    ang_weights=None) -> np.ndarray:
+    """Steps 1-3: pre-weights, ramp filter along u, angular weights."""
+    p = np.asarray(sino, dtype=np.float64) * cosine_weights(wl)
+    if short_scan:
+        p = p * parker_weights(wl, angles)[:, :, None]
+    q = ramp_filter(p, wl.det_spacing[0], pad_factor, window, axis=1)
+    w = angular_weights(angles, wl.beam, short_scan) if ang_weights is None else \
+        np.asarray(ang_weights, dtype=np.float64)
+    return q * w[:, None, None]
+
+
+def voxel_centres(wl):
+    D, H, Wd = wl.vol_shape
+    dz, dy, dx = wl.voxel_spacing
+    x = -0.5 * Wd * dx + (np.arange(Wd) + 0.5) * dx
+    y = -0.5 * H * dy + (np.arange(H) + 0.5) * dy
+    z = -0.5 * D * dz + (np.arange(D) + 0.5) * dz if _three_d(wl.beam) else np.zeros(1)
+    return z, y, x
+
+
+def _projection(wl, view, X, iso):
+    """Detector coordinates (u, v in pixel units) and weight of the world points X (..., 3)."""
+    fr = wl.frames[view]
+    a, c, eu, ev = fr[0:3], fr[3:6], fr[6:9], fr[9:12]
+    n = detector_normals(wl.frames[view:view + 1], wl.beam)[0]
+    U, V = wl.det_shape
+    du, dv = wl.det_spacing
+    if wl.beam in (FAN2D, CONE):
+        Ux = (X - a) @ n
+        D = np.dot(c - a, n)
+        R = np.dot(iso - a, n)
+        P = a + (X - a) * (D / Ux)[..., None]
+        wgt = R * D / Ux ** 2
+    else:
+        # parallel: slide X along the ray direction onto the detector plane
+        t = ((c - X) @ n) / np.dot(a, n)
+        P = X + t[..., None] * a
+        wgt = np.ones(X.shape[:-1])
+    u = (P - c) @ eu / du + 0.5 * (U - 1)
+    v = (P - c) @ ev / dv + 0.5 * (V - 1) if _three_d(wl.beam) else np.zeros(X.shape[:-1])
+    return u, v, wgt
+
+
+def _bilinear_taps(u, v, U, V):
+    """Four (index_u, index_v, coefficient) taps; samples outside the detector are 0."""
+    iu = np.floor(u).astype(np.int64)
+    iv = np.floor(v).astype(np.int64)
+    au = u - iu
+    av = v - iv
+    taps = []
+    for su, cu in ((0, 1 - au), (1, au)):
+        for sv, cv in ((0, 1 - av), (1, av)):
+            ju, jv = iu + su, iv + sv
+            ok = (ju >= 0) & (ju < U) & (jv >= 0) & (jv < V)
+            taps.append((np.where(ok, ju, 0), np.where(ok, jv, 0), np.where(ok, cu * cv, 0.0)))
+    return taps
+
+
+def weighted_backproject(wl, q, iso=None) -> np.ndarray:
+    """Step 4: f(x) = sum_i weight_i(x) * interp(q_i, u_i(x), v_i(x))."""
+    q = np.asarray(q, dtype=np.float64)
+    iso = isocentre(wl) if iso is None else np.asarray(iso, dtype=np.float64)
+    z, y, x = voxel_centres(wl)
+    Z, Y, Xg = np.meshgrid(z, y, x, indexing="ij")
+    X = np.stack([Xg, Y, Z], axis=-1)
+    U, V = wl.det_shape
+    out = np.zeros(X.shape[:-1])
+    for i in range(wl.n_views):
+        u, v, wgt = _projection(wl, i, X, iso)
+        val = np.zeros_like(out)
+        for ju, jv, cf in _bilinear_taps(u, v, U, V):
+            val += cf * q[i, ju, jv]
+        out += wgt * val
+    return out.reshape(wl.vol_shape)
+
+
+def weighted_backproject_T(wl, vol, iso=None) -> np.ndarray:
+    """Transpose of weighted_backproject: scatter of the same coefficients."""
+    vol = np.asarray(vol, dtype=np.float64).reshape(wl.vol_shape)
+    iso = isocentre(wl) if iso is None else np.asarray(iso, dtype=np.float64)
+    z, y, x = voxel_centres(wl)
+    Z, Y, Xg = np.meshgrid(z, y, x, indexing="ij")
+    X = np.stack([Xg, Y, Z], axis=-1)
+    U, V = wl.det_shape
+    out = np.zeros(wl.sino_shape)
+    for i in range(wl.n_views):
+        u, v, wgt = _projection(wl, i, X, iso)
+        for ju, jv, cf in _bilinear_taps(u, v, U, V):
+            np.add.at(out[i], (ju.ravel(), jv.ravel()), (wgt * cf * vol).ravel())
+    return out
+
+
+def fbp(wl, sino, angles, window="ram-lak", pad_factor=2, short_scan=False, iso=None,
+        ang_weights=None) -> np.ndarray:
+    """FBP (parallel2d, fan2d) or FDK (cone): filter, then the weighted backprojection."""
+    q = filter_sinogram(wl, sino, angles, window, pad_factor, short_scan, ang_weights)
+    return weighted_backproject(wl, q, iso)

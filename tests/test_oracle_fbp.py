@@ -1,0 +1,246 @@
+"""Pins of the FBP / FDK oracle (oracle/fbp.py) against closed forms and
+invariants that do not come from the oracle itself.
+
+- The ramp filter against the closed-form ramp-filtered Gaussian (the Hilbert
+  transform of a Gaussian is a Dawson function; the ramp is (1/2 pi) d/ds H).
+- Windows: Hann and Hamming multipliers equal the Ram-Lak kernel convolved
+  with the 3-tap kernels [1/4, 1/2, 1/4] and [0.23, 0.54, 0.23]; Shepp-Logan
+  matches its classical spatial kernel -2 / (pi^2 d^2 (4 n^2 - 1)).
+- Cosine weights against D / sqrt(D^2 + u^2 + v^2) on a centred detector.
+- Angular weights: sums and uniform values for full, half and short scans.
+- Parker weights: the redundancy identity w(b, g) + w(b + pi + 2 g, -g) = 1.
+- Reconstructions of a uniform disc / ball from their exact line integrals
+  (chord lengths): parallel, fan full scan, fan short scan (Parker), and FDK on
+  the central plane, all close to the density 1; an off-centre disc too; and
+  the centroid of a small off-centre disc on half and short scans.
+- The transpose of the weighted backprojection by the dot-product identity.
+- The estimated isocentre of a shifted circular orbit.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import dawsn
+
+from oracle import fbp as F
+from ray_driven_projector_amd import workloads as W
+
+
+def test_ramp_filter_of_a_gaussian_matches_closed_form():
+    N, d, sigma = 512, 0.5, 3.0
+    s = (np.arange(N) - 0.5 * (N - 1)) * d
+    p = np.exp(-s ** 2 / (2 * sigma ** 2))[None, :]
+    x = s / (math.sqrt(2) * sigma)
+    exact = (1 - 2 * x * dawsn(x)) / (math.pi ** 1.5 * math.sqrt(2) * sigma)
+    for pad in (2, 4):
+        q = F.ramp_filter(p, d, pad_factor=pad, window="ram-lak", axis=1)[0]
+        err = np.max(np.abs(q - exact)) / np.max(np.abs(exact))
+        assert err < 1e-5, (pad, err)
+
+
+def _circ(k, P):
+    out = np.zeros(P)
+    for off, val in k.items():
+        out[off % P] += val
+    return out
+
+
+def test_hann_and_hamming_are_three_tap_smoothings():
+    P, d = 256, 0.7
+    h = F.ramlak_kernel(P, d)
+    for name, (a, b) in (("hann", (0.25, 0.5)), ("hamming", (0.23, 0.54))):
+        t = _circ({-1: a, 0: b, 1: a}, P)
+        smoothed = np.real(np.fft.ifft(np.fft.fft(h) * np.fft.fft(t)))
+        expect = d * np.fft.rfft(smoothed).real
+        got = F.ramp_multiplier(P, d, name)
+        assert np.max(np.abs(got - expect)) < 1e-12 * np.max(np.abs(expect)) + 1e-15
+
+
+def test_shepp_logan_matches_its_spatial_kernel():
+    P, d = 1024, 1.0
+    n = np.arange(P)
+    n = np.where(n >= P // 2, n - P, n)
+    hsl = -2.0 / (math.pi ** 2 * d ** 2 * (4 * n.astype(float) ** 2 - 1))
+    expect = d * np.fft.rfft(hsl).real
+    got = F.ramp_multiplier(P, d, "shepp-logan")
+    assert np.max(np.abs(got - expect)) < 2e-3 * np.max(expect)
+
+
+def test_ram_lak_multiplier_is_the_ramp_at_low_frequency():
+    P, d = 2048, 0.8
+    M = F.ramp_multiplier(P, d, "ram-lak")
+    k = np.arange(1, P // 8)
+    nu = k / (P * d)
+    # the kernel's tail beyond P/2 is cut: an error of order 1 / (pi^2 P d)
+    assert np.max(np.abs(M[k] - nu)) < 2.0 / (math.pi ** 2 * P * d)
+    assert np.max(np.abs(M[k[15:]] - nu[15:]) / nu[15:]) < 2e-3
+    # the band-limited ramp keeps a small positive DC term (no DC hole)
+    assert 0 < M[0] < 2.0 / (P * d)
+
+
+def test_cosine_weights_closed_form():
+    wl = W.tiny_workload(W.BEAM_CONE, (5, 5, 5), (9, 7), 4, 3, det_spacing=(1.3, 0.9),
+                         sid=20.0, sdd=35.0)
+    cw = F.cosine_weights(wl)
+    U, V = wl.det_shape
+    u = (np.arange(U) - 0.5 * (U - 1)) * 1.3
+    v = (np.arange(V) - 0.5 * (V - 1)) * 0.9
+    D = 35.0
+    exact = D / np.sqrt(D ** 2 + u[:, None] ** 2 + v[None, :] ** 2)
+    for i in range(wl.n_views):
+        assert np.allclose(cw[i], exact, rtol=0, atol=1e-12)
+
+
+def test_angular_weights():
+    th = W.angles(90, 2 * math.pi)
+    w = F.angular_weights(th, F.FAN2D)
+    assert np.allclose(w, math.pi / 90) and abs(w.sum() - math.pi) < 1e-12
+    th = W.angles(60, math.pi)
+    w = F.angular_weights(th, F.PARALLEL2D)
+    assert np.allclose(w, math.pi / 60)
+    w = F.angular_weights(W.angles(60, 2 * math.pi), F.PARALLEL2D, redundant=True)
+    assert np.allclose(w, math.pi / 60)
+    th = np.linspace(0, 4.0, 41)          # short scan: trapezoid, ends one-sided
+    w = F.angular_weights(th, F.FAN2D, short_scan=True)
+    assert abs(w.sum() - 4.0) < 1e-12 and abs(w[0] - 0.05) < 1e-12 and abs(w[5] - 0.1) < 1e-12
+
+
+def test_parker_redundancy_identity():
+    delta = 0.3
+    rng = np.random.default_rng(3)
+    g = rng.uniform(-delta, delta, 4000)
+    # rays seen twice: beta in [0, 2 (delta - gamma)], conjugate inside the scan
+    b = rng.uniform(0, 1, 4000) * 2 * (delta - g)
+    bc = b + math.pi + 2 * g
+    assert np.all(bc <= math.pi + 2 * delta + 1e-12)
+    tot = F.parker(b, g, delta) + F.parker(bc, -g, delta)
+    assert np.max(np.abs(tot - 1)) < 1e-9
+    # rays seen once (their conjugate lies outside the scan) weigh 1
+    b1 = 2 * (delta - g) + rng.uniform(0, 1, 4000) * (math.pi - 2 * g - 2 * (delta - g))
+    assert np.all(b1 + math.pi + 2 * g > math.pi + 2 * delta - 1e-12)
+    assert np.allclose(F.parker(b1, g, delta), 1.0)
+    b = rng.uniform(0, math.pi + 2 * delta, 4000)
+    # outside the scan the weight is 0, and it lies in [0, 1]
+    assert np.all(F.parker(np.array([-0.1, math.pi + 2 * delta + 0.1]), np.zeros(2), delta) == 0)
+    w = F.parker(b, g, delta)
+    assert np.all((w >= 0) & (w <= 1))
+
+
+# ---- reconstructions from exact line integrals ----
+
+def _chords_disc(wl, centre, radius):
+    """Exact line integrals of a uniform disc / ball (density 1) for every ray."""
+    p = F.pixel_centres(wl)
+    a = wl.frames[:, None, None, 0:3]
+    if wl.beam in (F.FAN2D, F.CONE):
+        o = np.broadcast_to(a, p.shape)
+        dvec = p - a
+    else:
+        o = p
+        dvec = np.broadcast_to(a, p.shape)
+    dvec = dvec / np.linalg.norm(dvec, axis=-1, keepdims=True)
+    rel = np.asarray(centre, float) - o
+    t = np.sum(rel * dvec, axis=-1)
+    dist2 = np.sum(rel * rel, axis=-1) - t * t
+    return 2 * np.sqrt(np.clip(radius ** 2 - dist2, 0, None))
+
+
+def _interior(wl, centre, radius, frac):
+    z, y, x = F.voxel_centres(wl)
+    Z, Y, X = np.meshgrid(z, y, x, indexing="ij")
+    r2 = (X - centre[0]) ** 2 + (Y - centre[1]) ** 2 + (Z - centre[2]) ** 2
+    return r2 < (frac * radius) ** 2
+
+
+@pytest.mark.parametrize("case", ["parallel", "fan", "fan-offcentre", "fan-short", "cone"])
+def test_uniform_disc_is_reconstructed(case):
+    if case == "parallel":
+        n = 180
+        fr = W.circular_parallel2d(n, math.pi)
+        wl = W.Workload("p", W.BEAM_PARALLEL2D, (1, 48, 48), (1, 1, 1), (128, 1), (0.5, 1), fr)
+        th = W.angles(n, math.pi)
+        centre, r, short = (0.0, 0.0, 0.0), 16.0, False
+    elif case.startswith("fan"):
+        short = case == "fan-short"
+        sid, sdd = 60.0, 100.0        # a wide fan: cosine weights down to 0.84
+        if short:
+            delta = math.atan(0.5 * 160 * 0.8 / sdd)
+            span = math.pi + 2 * delta + 0.05
+            n = 300
+            fr = W.circular_fan2d(n, sid, sdd, angular_range=span * n / (n - 1))
+            th = W.angles(n, span * n / (n - 1))
+        else:
+            n = 240
+            fr = W.circular_fan2d(n, sid, sdd)
+            th = W.angles(n, 2 * math.pi)
+        wl = W.Workload("f", W.BEAM_FAN2D, (1, 48, 48), (1, 1, 1), (160, 1), (0.8, 1), fr)
+        centre = (6.0, -4.0, 0.0) if case == "fan-offcentre" else (0.0, 0.0, 0.0)
+        r = 12.0 if case == "fan-offcentre" else 18.0
+    else:
+        n = 200
+        fr = W.helix_cone(n, 100.0, 160.0, 0.0, 1.0)
+        wl = W.Workload("c", W.BEAM_CONE, (9, 40, 40), (1, 1, 1), (96, 40), (0.8, 0.8), fr)
+        th = W.angles(n, 2 * math.pi)
+        centre, r, short = (0.0, 0.0, 0.0), 13.0, False
+    sino = _chords_disc(wl, centre, r)
+    rec = F.fbp(wl, sino, th, window="ram-lak", pad_factor=2, short_scan=short)
+    inside = _interior(wl, centre, r, 0.7)
+    outside = ~_interior(wl, centre, r, 1.3) & _interior(wl, (0, 0, 0), 28.0, 1.0)
+    mean_in = rec[inside].mean()
+    assert abs(mean_in - 1) < 0.002, (case, mean_in)
+    assert np.max(np.abs(rec[inside] - 1)) < 0.01, case
+    assert np.mean(np.abs(rec[outside])) < 0.02, case
+
+
+@pytest.mark.parametrize("case", ["parallel-half", "fan-short", "cone"])
+def test_small_disc_lands_where_it_is(case):
+    """Centroid of the reconstruction of a small off-centre disc.  Half and short
+    scans do not average a detector misregistration away: a shift of the
+    sampling position by half a bin moves the centroid by about 0.16 voxel."""
+    centre, r = (7.0, -3.0, 0.0), 5.0
+    if case == "parallel-half":
+        n = 180
+        fr = W.circular_parallel2d(n, math.pi)
+        wl = W.Workload("p", W.BEAM_PARALLEL2D, (1, 40, 40), (1, 1, 1), (112, 1), (0.5, 1), fr)
+        th, short = W.angles(n, math.pi), False
+    elif case == "fan-short":
+        sid, sdd, n = 60.0, 100.0, 300
+        delta = math.atan(0.5 * 160 * 0.8 / sdd)
+        span = (math.pi + 2 * delta + 0.05) * n / (n - 1)
+        fr = W.circular_fan2d(n, sid, sdd, angular_range=span)
+        wl = W.Workload("f", W.BEAM_FAN2D, (1, 40, 40), (1, 1, 1), (160, 1), (0.8, 1), fr)
+        th, short = W.angles(n, span), True
+    else:
+        # a ball off the orbit plane: a v misregistration moves it along z
+        centre, r, n = (4.0, -2.0, 2.0), 4.0, 120
+        fr = W.helix_cone(n, 100.0, 160.0, 0.0, 1.0)
+        wl = W.Workload("c", W.BEAM_CONE, (17, 32, 32), (1, 1, 1), (80, 48), (0.8, 0.8), fr)
+        th, short = W.angles(n, 2 * math.pi), False
+    rec = F.fbp(wl, _chords_disc(wl, centre, r), th, short_scan=short)
+    z, y, x = F.voxel_centres(wl)
+    w = rec * _interior(wl, centre, r, 1.6)
+    got = [np.sum(w * x[None, None, :]), np.sum(w * y[None, :, None]), np.sum(w * z[:, None, None])]
+    got = np.array(got) / np.sum(w)
+    assert np.max(np.abs(got - np.array(centre))) < 0.03, (case, got)
+
+
+@pytest.mark.parametrize("beam", [W.BEAM_PARALLEL2D, W.BEAM_FAN2D, W.BEAM_CONE])
+def test_weighted_backprojection_transpose_identity(beam):
+    vol = (1, 9, 11) if beam != W.BEAM_CONE else (6, 9, 11)
+    det = (17, 1) if beam != W.BEAM_CONE else (17, 13)
+    wl = W.tiny_workload(beam, vol, det, 7, 11, det_spacing=(0.9, 0.8), sid=25.0, sdd=40.0)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal(wl.sino_shape)
+    f = rng.standard_normal(wl.vol_shape)
+    lhs = np.sum(F.weighted_backproject(wl, q) * f)
+    rhs = np.sum(q * F.weighted_backproject_T(wl, f))
+    assert abs(lhs - rhs) <= 1e-12 * max(abs(lhs), 1.0)
+
+
+def test_isocentre_of_a_shifted_orbit():
+    fr = W.helix_cone(36, 50.0, 80.0, 0.0, 1.0)
+    shift = np.array([3.0, -2.0, 0.0])
+    fr[:, 0:3] += shift
+    fr[:, 3:6] += shift
+    wl = W.Workload("c", W.BEAM_CONE, (4, 8, 8), (1, 1, 1), (8, 8), (1, 1), fr)
+    assert np.allclose(F.isocentre(wl)[:2], shift[:2], atol=1e-9)
