@@ -262,6 +262,73 @@ ct_status_t ct_backproject_host(ct_geom_t g, const float *sino_host, float *vol_
 ct_status_t ct_project_host(ct_geom_t g, const float *vol_host, float *sino_host,
                             ct_stream_plan_t plan, ct_stream_t stream);
 
+/* ---- Analytical FBP / FDK (a second operator, not the Siddon pair) ----
+ * diffct documentation, "Differentiable analytical reconstruction" and the API
+ * reference's "Analytical Reconstruction Helpers" and "Ramp Filter Options":
+ * FBP (parallel2d, fan2d) and FDK (cone) on a flat detector run
+ *   1. pre-weights: the fan/cone cosine weight |(p - a).n| / |p - a| of each
+ *      pixel, and Parker's short-scan weights when short_scan is set;
+ *   2. a ramp filter along u, zero-padded to pad_factor * U samples and applied
+ *      as a real multiplier: the band-limited Ram-Lak ramp (Ramachandran and
+ *      Lakshminarayanan; Kak and Slaney ch. 3) times the chosen window of
+ *      f = k / P (Shepp-Logan sin(pi f)/(pi f), cosine cos(pi f), Hamming
+ *      0.54 + 0.46 cos(2 pi f), Hann 0.5 + 0.5 cos(2 pi f));
+ *   3. angular weights: half the gap to the neighbouring views, periodic over
+ *      2 pi (fan/cone) or pi (parallel), one-sided at the ends for short scans,
+ *      times 1/2 for full fan/cone turns; or the caller's own;
+ *   4. the voxel-driven interpolating weighted backprojection: each voxel
+ *      centre x gathers, per view, the bilinearly interpolated filtered value
+ *      where it projects, times R D / U(x)^2 (fan/cone: U(x) = (x - a).n,
+ *      D = (c - a).n, R = (iso - a).n) or 1 (parallel); samples outside the
+ *      detector are 0.  Its transpose scatters the same coefficients.
+ * It is not the ct_backproject adjoint.  ct_fbp_filter does 1-3,
+ * ct_fbp_backproject does 4, ct_fbp_run does both. */
+typedef struct ct_fbp_s *ct_fbp_t;       /* opaque, library-owned */
+
+typedef enum {
+    CT_WINDOW_RAMLAK = 0,
+    CT_WINDOW_SHEPP_LOGAN = 1,
+    CT_WINDOW_COSINE = 2,
+    CT_WINDOW_HAMMING = 3,
+    CT_WINDOW_HANN = 4
+} ct_window_t;
+
+typedef struct {
+    int32_t window;       /* ct_window_t */
+    int32_t pad_factor;   /* zero padding of each row to pad_factor * U samples, 1..16 */
+    int32_t short_scan;   /* fan/cone: Parker weights; the angles must span pi + 2 x half fan angle */
+    int32_t iso_given;    /* iso[] holds the isocentre; else the least-squares point nearest the
+                             lines through each source along its detector normal */
+    double iso[3];        /* world (x, y, z) */
+    int64_t reserved;     /* must be 0 */
+} ct_fbp_opts_t;
+
+/* Builds a plan on the current device (synchronous): validates desc (same
+ * rules as ct_geom_validate; beams parallel2d, fan2d, cone; flat detector;
+ * U <= 4096, pad_factor * U <= 16384, U >= 2 and for cone V >= 2), computes the
+ * filter, the angular and Parker weights and the per-view backprojection
+ * tables in float64, and uploads them.  angles: HOST, n_views radians (needed
+ * unless angular_weights is given, and always for short scans);
+ * angular_weights: HOST, n_views, or NULL for the rule above.
+ * Errors: CT_E_NULL, CT_E_ARG (beam, window, pad, short scan on parallel, a
+ * span too short, an isocentre that cannot be estimated), CT_E_SHAPE,
+ * CT_E_RANGE, CT_E_NONFINITE, CT_E_NOMEM, CT_E_HIP. */
+ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles,
+                          const double *angular_weights, const ct_fbp_opts_t *opts, ct_fbp_t *out);
+ct_status_t ct_fbp_destroy(ct_fbp_t f);
+/* The plan's isocentre (3 doubles) and angular weights (n_views doubles); either may be NULL. */
+ct_status_t ct_fbp_info(ct_fbp_t f, double *iso, double *angular_weights);
+
+/* filtered = steps 1-3 of sino; (views, U, V) device buffers that must not overlap. */
+ct_status_t ct_fbp_filter(ct_fbp_t f, const float *sino, float *filtered, ct_stream_t stream);
+/* vol = step 4 of filtered (overwrites every voxel). */
+ct_status_t ct_fbp_backproject(ct_fbp_t f, const float *filtered, float *vol, ct_stream_t stream);
+/* sino = transpose of step 4 applied to vol (overwrites; float atomics, so the
+ * order of additions, and the last bits, vary between runs). */
+ct_status_t ct_fbp_backproject_transpose(ct_fbp_t f, const float *vol, float *sino, ct_stream_t stream);
+/* vol = FBP/FDK of sino, with work (sinogram-sized) holding the filtered data. */
+ct_status_t ct_fbp_run(ct_fbp_t f, const float *sino, float *work, float *vol, ct_stream_t stream);
+
 /* SIRT weights (once per geometry): row_inv[i] = 1/(A 1)_i, col_inv[j] =
  * 1/(A^T 1)_j, each 0 where the sum is 0.  row_inv: (views,U,V); col_inv:
  * (D,H,W); device float32, non-overlapping. */

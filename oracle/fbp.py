@@ -317,6 +317,25 @@ def weighted_backproject(wl, q, iso=None) -> np.ndarray:
     return out.reshape(wl.vol_shape)
 
 
+def weighted_backproject_voxels(wl, q, voxel_ids, iso=None) -> np.ndarray:
+    """weighted_backproject evaluated at the given flat voxel indices only."""
+    q = np.asarray(q, dtype=np.float64)
+    iso = isocentre(wl) if iso is None else np.asarray(iso, dtype=np.float64)
+    z, y, x = voxel_centres(wl)
+    D, H, Wd = wl.vol_shape
+    ids = np.asarray(voxel_ids, dtype=np.int64)
+    X = np.stack([x[ids % Wd], y[(ids // Wd) % H], z[ids // (Wd * H)]], axis=-1)
+    U, V = wl.det_shape
+    out = np.zeros(len(ids))
+    for i in range(wl.n_views):
+        u, v, wgt = _projection(wl, i, X, iso)
+        val = np.zeros_like(out)
+        for ju, jv, cf in _bilinear_taps(u, v, U, V):
+            val += cf * q[i, ju, jv]
+        out += wgt * val
+    return out
+
+
 def weighted_backproject_T(wl, vol, iso=None) -> np.ndarray:
     """Transpose of weighted_backproject: scatter of the same coefficients."""
     vol = np.asarray(vol, dtype=np.float64).reshape(wl.vol_shape)

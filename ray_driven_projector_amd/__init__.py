@@ -31,7 +31,9 @@ CT_VIEW_TABLE_STRIDE = 48
 EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_geom_destroy",
            "ct_geom_view_table",
            "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_project_region",
-           "ct_backproject_region", "ct_project_host", "ct_backproject_host", "ct_sirt_weights",
+           "ct_backproject_region", "ct_project_host", "ct_backproject_host",
+           "ct_fbp_create", "ct_fbp_destroy", "ct_fbp_info", "ct_fbp_filter", "ct_fbp_backproject",
+           "ct_fbp_backproject_transpose", "ct_fbp_run", "ct_sirt_weights",
            "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_sirt_update_bounded",
            "ct_sirt_step_bounded", "ct_cgls_workspace_size",
            "ct_cgls_init", "ct_cgls_step", "ct_cgls_scalars", "ct_count_intersections",
@@ -89,6 +91,14 @@ def lib():
         L.ct_project_region.argtypes = [vp, vp, Region, c.c_int64, c.c_int64, vp, c.c_int, vp]
         L.ct_backproject_region.argtypes = [vp, vp, c.c_int64, c.c_int64, Region, vp, c.c_int, vp]
         L.ct_project_host.argtypes = [vp, vp, vp, StreamPlan, vp]
+        dp = P(c.c_double)
+        L.ct_fbp_create.argtypes = [vp, dp, dp, vp, vp]
+        L.ct_fbp_destroy.argtypes = [vp]
+        L.ct_fbp_info.argtypes = [vp, dp, dp]
+        L.ct_fbp_filter.argtypes = [vp, vp, vp, vp]
+        L.ct_fbp_backproject.argtypes = [vp, vp, vp, vp]
+        L.ct_fbp_backproject_transpose.argtypes = [vp, vp, vp, vp]
+        L.ct_fbp_run.argtypes = [vp, vp, vp, vp, vp]
         L.ct_backproject_host.argtypes = [vp, vp, vp, StreamPlan, vp]
         L.ct_sirt_weights.argtypes = [vp, vp, vp, vp]
         L.ct_sirt_residual.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -204,6 +214,76 @@ class Geometry:
             pass
 
 
+WINDOWS = {"ram-lak": 0, None: 0, "shepp-logan": 1, "cosine": 2, "hamming": 3, "hann": 4, "hanning": 4}
+
+
+class FbpOpts(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("pad_factor", ctypes.c_int32),
+                ("short_scan", ctypes.c_int32), ("iso_given", ctypes.c_int32),
+                ("iso", ctypes.c_double * 3), ("reserved", ctypes.c_int64)]
+
+
+class FBP:
+    """A ct_fbp_t plan: analytical FBP (parallel2d, fan2d) / FDK (cone).
+    angles: n_views radians (host); angular_weights: optional override."""
+
+    def __init__(self, beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames, angles=None,
+                 window="ram-lak", pad_factor=2, short_scan=False, iso=None, angular_weights=None):
+        d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
+        o = FbpOpts()
+        o.window = WINDOWS[window]
+        o.pad_factor = int(pad_factor)
+        o.short_scan = int(bool(short_scan))
+        o.iso_given = 0 if iso is None else 1
+        if iso is not None:
+            for k in range(3):
+                o.iso[k] = float(iso[k])
+        o.reserved = 0
+        n = fr.shape[0]
+        dp = ctypes.POINTER(ctypes.c_double)
+        self._angles = None if angles is None else np.ascontiguousarray(angles, dtype=np.float64)
+        self._aw = None if angular_weights is None else np.ascontiguousarray(angular_weights, np.float64)
+        for arr, name in ((self._angles, "angles"), (self._aw, "angular_weights")):
+            if arr is not None and arr.shape != (n,):
+                raise ValueError(f"{name} must have one value per view")
+        h = ctypes.c_void_p()
+        _check(lib().ct_fbp_create(ctypes.byref(d),
+                                   self._angles.ctypes.data_as(dp) if self._angles is not None else None,
+                                   self._aw.ctypes.data_as(dp) if self._aw is not None else None,
+                                   ctypes.byref(o), ctypes.byref(h)))
+        self._h = h
+        self.vol_shape = tuple(int(x) for x in vol_shape)
+        self.sino_shape = (n, int(det_shape[0]), int(det_shape[1]))
+
+    @classmethod
+    def from_workload(cls, wl, angles=None, **kw) -> "FBP":
+        return cls(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing, wl.frames,
+                   angles, **kw)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self):
+        """(isocentre (3,), angular weights (n_views,)) as the plan holds them."""
+        iso = np.zeros(3)
+        aw = np.zeros(self.sino_shape[0])
+        dp = ctypes.POINTER(ctypes.c_double)
+        _check(lib().ct_fbp_info(self._h, iso.ctypes.data_as(dp), aw.ctypes.data_as(dp)))
+        return iso, aw
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().ct_fbp_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):  # pragma: no cover - best effort
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -303,6 +383,34 @@ def ct_project_host(g: Geometry, vol, sino, slab, batch_views, axis="auto", stre
     _check(lib().ct_project_host(g.handle, _host_ptr(vol, g.vol_shape, "vol", False),
                                  _host_ptr(sino, g.sino_shape, "sino", True), plan, _stream(stream)))
     return sino
+
+
+def ct_fbp_filter(f: FBP, sino, filtered, stream=None):
+    """filtered = angular weight x ramp filter of the pre-weighted sinogram."""
+    _check(lib().ct_fbp_filter(f.handle, _ptr(sino, f.sino_shape, "sino"),
+                               _ptr(filtered, f.sino_shape, "filtered"), _stream(stream)))
+    return filtered
+
+
+def ct_fbp_backproject(f: FBP, filtered, vol, stream=None):
+    """vol = voxel-driven interpolating weighted backprojection of filtered."""
+    _check(lib().ct_fbp_backproject(f.handle, _ptr(filtered, f.sino_shape, "filtered"),
+                                    _ptr(vol, f.vol_shape, "vol"), _stream(stream)))
+    return vol
+
+
+def ct_fbp_backproject_transpose(f: FBP, vol, sino, stream=None):
+    """sino = transpose of the weighted backprojection applied to vol."""
+    _check(lib().ct_fbp_backproject_transpose(f.handle, _ptr(vol, f.vol_shape, "vol"),
+                                              _ptr(sino, f.sino_shape, "sino"), _stream(stream)))
+    return sino
+
+
+def ct_fbp_run(f: FBP, sino, work, vol, stream=None):
+    """vol = FBP / FDK of sino (work holds the filtered sinogram)."""
+    _check(lib().ct_fbp_run(f.handle, _ptr(sino, f.sino_shape, "sino"), _ptr(work, f.sino_shape, "work"),
+                            _ptr(vol, f.vol_shape, "vol"), _stream(stream)))
+    return vol
 
 
 def ct_backproject_atomic(g: Geometry, sino, vol, stream=None):

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libctproj.so")
-SOURCES = ["ct_abi.hip", "ct_kernels.hip", "ct_geometry.cpp"]
+SOURCES = ["ct_abi.hip", "ct_kernels.hip", "ct_fbp.hip", "ct_geometry.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

@@ -1,0 +1,809 @@
+// ct_fbp.hip -- analytical FBP (parallel2d, fan2d) and FDK (cone) on a flat
+// detector: pre-weights and ramp filter, then the voxel-driven interpolating
+// weighted backprojection, and that backprojection's transpose.
+//
+// diffct documentation, "Differentiable analytical reconstruction" and the
+// "Analytical Reconstruction Helpers" / "Ramp Filter Options" sections of its
+// API reference: cosine (and, for short scans, Parker) pre-weights, a ramp
+// filter along u zero-padded to pad_factor * U samples and applied as a real
+// multiplier, angular quadrature weights (a full fan/cone turn carries the 1/2
+// redundancy factor), and a voxel-driven interpolating backprojection that is
+// not the Siddon adjoint; its transpose scatters the same coefficients.
+//
+// Readings where the pages give no formula: the Ram-Lak filter is the
+// band-limited ramp of Ramachandran and Lakshminarayanan sampled in space
+// (Kak and Slaney, "Principles of Computerized Tomographic Imaging", ch. 3),
+// taken P-periodic; windows of f = k / P: Shepp-Logan sin(pi f)/(pi f), cosine
+// cos(pi f), Hamming 0.54 + 0.46 cos(2 pi f), Hann 0.5 + 0.5 cos(2 pi f).  The
+// FDK distance weight is R D / U(x)^2 (U(x) = (x - a).n, D = (c - a).n,
+// R = (iso - a).n).  Parker weights follow Parker (1982).  Detector samples
+// outside the detector read as 0.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "ct_internal.h"
+
+using namespace ctp;
+
+namespace {
+
+constexpr uint64_t kFbpMagic = 0x43544642'50303031ull;   // "CTFBP001"
+constexpr int kBpViews = 256;      // views whose constants one LDS batch holds
+constexpr int kBpConst = 16;       // floats per view in that batch
+
+ct_status_t ffail(ct_status_t st, const char *msg) {
+    set_error(msg);
+    return st;
+}
+
+ct_status_t fhip(hipError_t e, const char *where) {
+    char buf[400];
+    std::snprintf(buf, sizeof buf, "%s: %s", where, hipGetErrorString(e));
+    set_error(buf);
+    return CT_E_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// filter: pre-weights, circular convolution with the P-periodic filter kernel
+// (equal to the zero-padded real-FFT multiplier), angular weight
+// ---------------------------------------------------------------------------
+
+// Per view, float: D, (c - a) (3), e_u du (3), e_v dv (3), angular weight, perspective.
+constexpr int kFv = 12;
+
+struct FilterArgs {
+    const float *sino;
+    float *out;
+    const float *taps;     // 2 * U8 taps, tap j (|j| <= U8) at j + U8
+    const float *fview;    // kFv floats per view
+    const float *parker;   // n_views x U, or null
+    int U, V, n_views, U8, VT, S;   // S: LDS row stride of the tile (floats)
+    int two_d;
+};
+
+// One block filters VT rows: VT consecutive v of one view (3D), or VT
+// consecutive views (2D).  Each thread owns 8 consecutive outputs of one row
+// and keeps them in registers while it sweeps the row's samples eight at a
+// time (16 taps per sweep step cover the 8 x 8 products).
+__global__ __launch_bounds__(256) void fbp_filter_kernel(FilterArgs a) {
+    extern __shared__ float lds[];
+    float *taps = lds;                    // 2 * U8
+    float *tile = lds + 2 * a.U8;         // VT rows of S floats
+    const int U = a.U, V = a.V, U8 = a.U8, VT = a.VT, S = a.S;
+    int view0, v0;
+    if (a.two_d) {
+        view0 = blockIdx.x * VT;
+        v0 = 0;
+    } else {
+        const int nvt = (V + VT - 1) / VT;
+        view0 = blockIdx.x / nvt;
+        v0 = (blockIdx.x % nvt) * VT;
+    }
+    for (int i = threadIdx.x; i < 2 * U8; i += 256) taps[i] = a.taps[i];
+    // load the rows with their pre-weights; samples past U (or past the last
+    // row) are zero
+    for (int i = threadIdx.x; i < VT * U8; i += 256) {
+        int r, u;
+        if (a.two_d) {
+            r = i / U8;
+            u = i - r * U8;
+        } else {
+            u = i / VT;
+            r = i - u * VT;
+        }
+        const int view = a.two_d ? view0 + r : view0;
+        const int v = a.two_d ? 0 : v0 + r;
+        float val = 0.f;
+        if (u < U && view < a.n_views && v < V) {
+            const float *fv = a.fview + (size_t)view * kFv;
+            val = a.sino[((size_t)view * U + u) * V + v];
+            if (fv[11] != 0.f) {   // fan/cone: cosine weight
+                const float ou = (float)u - 0.5f * (float)(U - 1);
+                const float ov = a.two_d ? 0.f : (float)v - 0.5f * (float)(V - 1);
+                const float px = fv[1] + ou * fv[4] + ov * fv[7];
+                const float py = fv[2] + ou * fv[5] + ov * fv[8];
+                const float pz = fv[3] + ou * fv[6] + ov * fv[9];
+                val *= fabsf(fv[0]) / sqrtf(px * px + py * py + pz * pz);
+            }
+            if (a.parker) val *= a.parker[(size_t)view * U + u];
+        }
+        tile[r * S + u] = val;
+    }
+    __syncthreads();
+    const int nb = U8 / 8;   // VT * nb <= 1024: at most four tasks per thread
+    float res[4][8];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int task = threadIdx.x + 256 * it;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const int r = task / nb, n0 = (task - r * nb) * 8;
+        const float *prow = tile + r * S;
+        for (int m0 = 0; task < VT * nb && m0 < U8; m0 += 8) {
+            const float4 p0 = *(const float4 *)(prow + m0);
+            const float4 p1 = *(const float4 *)(prow + m0 + 4);
+            const float *tb = taps + (n0 - m0 - 8 + U8);   // taps n0 - m0 - 8 .. + 15
+            const float4 t0 = *(const float4 *)(tb);
+            const float4 t1 = *(const float4 *)(tb + 4);
+            const float4 t2 = *(const float4 *)(tb + 8);
+            const float4 t3 = *(const float4 *)(tb + 12);
+            const float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            const float t[16] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w,
+                                 t2.x, t2.y, t2.z, t2.w, t3.x, t3.y, t3.z, t3.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[j] = fmaf(p[i], t[j - i + 8], acc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) res[it][j] = acc[j];
+    }
+    __syncthreads();   // every read of the tile is done: reuse it for the outputs
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int task = threadIdx.x + 256 * it;
+        const int r = task / nb, n0 = (task - r * nb) * 8;
+        if (task < VT * nb) {
+            *(float4 *)(tile + r * S + n0) = make_float4(res[it][0], res[it][1], res[it][2], res[it][3]);
+            *(float4 *)(tile + r * S + n0 + 4) = make_float4(res[it][4], res[it][5], res[it][6], res[it][7]);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < VT * U8; i += 256) {
+        int r, u;
+        if (a.two_d) {
+            r = i / U8;
+            u = i - r * U8;
+        } else {
+            u = i / VT;
+            r = i - u * VT;
+        }
+        const int view = a.two_d ? view0 + r : view0;
+        const int v = a.two_d ? 0 : v0 + r;
+        if (u < U && view < a.n_views && v < V)
+            a.out[((size_t)view * U + u) * V + v] = a.fview[(size_t)view * kFv + 10] * tile[r * S + u];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// weighted backprojection B (gather) and its transpose (scatter)
+// ---------------------------------------------------------------------------
+
+// Per view, float64, in voxel-index coordinates (i, j, k) = (x, y, z) index:
+// u_h = Pu . (i, j, k) + pu, v_h likewise, w_h likewise, then
+// u = u_h / w_h, v = v_h / w_h, weight = K / w_h^2 (parallel: w_h = 1, K = 1).
+constexpr int kBpv = 16;   // Pu(3) pu Pv(3) pv Pw(3) pw K pad pad pad
+
+struct BpArgs {
+    const double *bp;
+    const float *q;      // B: filtered sinogram in; B^T: sinogram out
+    float *vol;          // B: volume out; B^T: volume in (read)
+    float *sino_out;
+    int W, H, D, U, V, n_views;
+    int nbx, nby, nbz;
+    int two_d;
+};
+
+// Block-relative constants of one view: with the tile anchor X0 and integer
+// detector anchors u0, v0 (the projection of X0, rounded down),
+//   w  = Aw + Bw . d,   u - u0 = (Au + Bu . d) / w,   v - v0 = (Av + Bv . d) / w
+// for d = X - X0 in index units; the anchors keep the float32 arithmetic on
+// small numbers.
+__device__ __forceinline__ void view_consts(const double *p, double x0, double y0, double z0, float *c) {
+    const double uh = p[0] * x0 + p[1] * y0 + p[2] * z0 + p[3];
+    const double vh = p[4] * x0 + p[5] * y0 + p[6] * z0 + p[7];
+    const double wh = p[8] * x0 + p[9] * y0 + p[10] * z0 + p[11];
+    const double u0 = wh > 0.0 ? floor(uh / wh) : 0.0;
+    const double v0 = wh > 0.0 ? floor(vh / wh) : 0.0;
+    c[0] = (float)(uh - u0 * wh);
+    c[1] = (float)(p[0] - u0 * p[8]);
+    c[2] = (float)(p[1] - u0 * p[9]);
+    c[3] = (float)(p[2] - u0 * p[10]);
+    c[4] = (float)(vh - v0 * wh);
+    c[5] = (float)(p[4] - v0 * p[8]);
+    c[6] = (float)(p[5] - v0 * p[9]);
+    c[7] = (float)(p[6] - v0 * p[10]);
+    c[8] = (float)wh;
+    c[9] = (float)p[8];
+    c[10] = (float)p[9];
+    c[11] = (float)p[10];
+    c[12] = (float)p[12];
+    c[13] = (float)fmin(fmax(u0, -1e9), 1e9);
+    c[14] = (float)fmin(fmax(v0, -1e9), 1e9);
+    c[15] = 0.f;
+}
+
+template <bool TRANSPOSE, bool TWO_D>
+__global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
+    __shared__ float cst[kBpViews * kBpConst];
+    // tile: 3D 4 x 4 x 16 voxels (x, y, z), z fastest across lanes; 2D 16 x 16 (x fastest)
+    constexpr int TX = TWO_D ? 16 : 4, TY = TWO_D ? 16 : 4, TZ = TWO_D ? 1 : 16;
+    const int b = blockIdx.x;
+    const int bx = b % a.nbx, by = (b / a.nbx) % a.nby, bz = b / (a.nbx * a.nby);
+    int lx, ly, lz;
+    if (TWO_D) {
+        lx = threadIdx.x & 15;
+        ly = threadIdx.x >> 4;
+        lz = 0;
+    } else {
+        lz = threadIdx.x & 15;
+        ly = (threadIdx.x >> 4) & 3;
+        lx = threadIdx.x >> 6;
+    }
+    const int ix = bx * TX + lx, iy = by * TY + ly, iz = bz * TZ + lz;
+    const bool inside = ix < a.W && iy < a.H && iz < a.D;
+    // anchor: the tile centre (index coordinates of voxel centres are i + 0.5
+    // in the tables' convention: they take the index itself)
+    const double X0 = bx * TX + 0.5 * (TX - 1), Y0 = by * TY + 0.5 * (TY - 1), Z0 = bz * TZ + 0.5 * (TZ - 1);
+    const float dx = (float)lx - 0.5f * (TX - 1), dy = (float)ly - 0.5f * (TY - 1),
+                dz = (float)lz - 0.5f * (TZ - 1);
+    const size_t vidx = ((size_t)iz * a.H + iy) * a.W + ix;
+    const float f = (TRANSPOSE && inside) ? a.vol[vidx] : 0.f;
+    const int U = a.U, V = a.V;
+    float acc = 0.f;
+    for (int vb = 0; vb < a.n_views; vb += kBpViews) {
+        const int nvb = min(kBpViews, a.n_views - vb);
+        __syncthreads();
+        if ((int)threadIdx.x < nvb)
+            view_consts(a.bp + (size_t)(vb + threadIdx.x) * kBpv, X0, Y0, Z0, cst + threadIdx.x * kBpConst);
+        __syncthreads();
+        if (!inside || (TRANSPOSE && f == 0.f)) continue;
+        for (int k = 0; k < nvb; ++k) {
+            const float4 c0 = *(const float4 *)(cst + k * kBpConst);
+            const float4 c1 = *(const float4 *)(cst + k * kBpConst + 4);
+            const float4 c2 = *(const float4 *)(cst + k * kBpConst + 8);
+            const float4 c3 = *(const float4 *)(cst + k * kBpConst + 12);
+            const float w = fmaf(c2.w, dz, fmaf(c2.z, dy, fmaf(c2.y, dx, c2.x)));
+            if (!(w > 0.f)) continue;   // at or behind the source
+            const float r = 1.0f / w;
+            const float nu = fmaf(c0.w, dz, fmaf(c0.z, dy, fmaf(c0.y, dx, c0.x)));
+            const float su = nu * r;
+            const float flu = floorf(su);
+            const float au = su - flu;
+            const int iu = (int)flu + (int)c3.y;
+            const float wgt = c3.x * r * r;
+            const size_t vbase = (size_t)(vb + k) * U;
+            if (TWO_D) {
+                const bool ok0 = (unsigned)iu < (unsigned)U, ok1 = (unsigned)(iu + 1) < (unsigned)U;
+                const float k0 = ok0 ? 1.f - au : 0.f, k1 = ok1 ? au : 0.f;
+                const int j0 = ok0 ? iu : 0, j1 = ok1 ? iu + 1 : 0;
+                if (TRANSPOSE) {
+                    const float g = wgt * f;
+                    if (k0 != 0.f) atomicAdd(a.sino_out + vbase + j0, g * k0);
+                    if (k1 != 0.f) atomicAdd(a.sino_out + vbase + j1, g * k1);
+                } else {
+                    const float q0 = a.q[vbase + j0], q1 = a.q[vbase + j1];
+                    acc = fmaf(wgt, fmaf(k0, q0, k1 * q1), acc);
+                }
+            } else {
+                const float nv = fmaf(c1.w, dz, fmaf(c1.z, dy, fmaf(c1.y, dx, c1.x)));
+                const float sv = nv * r;
+                const float flv = floorf(sv);
+                const float av = sv - flv;
+                const int iv = (int)flv + (int)c3.z;
+                const bool u0k = (unsigned)iu < (unsigned)U, u1k = (unsigned)(iu + 1) < (unsigned)U;
+                const bool v0k = (unsigned)iv < (unsigned)V, v1k = (unsigned)(iv + 1) < (unsigned)V;
+                const float ku0 = u0k ? 1.f - au : 0.f, ku1 = u1k ? au : 0.f;
+                const float kv0 = v0k ? 1.f - av : 0.f, kv1 = v1k ? av : 0.f;
+                const int ju0 = u0k ? iu : 0, ju1 = u1k ? iu + 1 : 0;
+                const int jv0 = v0k ? iv : 0, jv1 = v1k ? iv + 1 : 0;
+                const size_t r0 = (vbase + ju0) * V, r1 = (vbase + ju1) * V;
+                if (TRANSPOSE) {
+                    const float g = wgt * f;
+                    if (ku0 * kv0 != 0.f) atomicAdd(a.sino_out + r0 + jv0, g * ku0 * kv0);
+                    if (ku0 * kv1 != 0.f) atomicAdd(a.sino_out + r0 + jv1, g * ku0 * kv1);
+                    if (ku1 * kv0 != 0.f) atomicAdd(a.sino_out + r1 + jv0, g * ku1 * kv0);
+                    if (ku1 * kv1 != 0.f) atomicAdd(a.sino_out + r1 + jv1, g * ku1 * kv1);
+                } else {
+                    const float q00 = a.q[r0 + jv0], q01 = a.q[r0 + jv1];
+                    const float q10 = a.q[r1 + jv0], q11 = a.q[r1 + jv1];
+                    const float s0 = fmaf(kv0, q00, kv1 * q01), s1 = fmaf(kv0, q10, kv1 * q11);
+                    acc = fmaf(wgt, fmaf(ku0, s0, ku1 * s1), acc);
+                }
+            }
+        }
+    }
+    if (!TRANSPOSE && inside) a.vol[vidx] = acc;
+}
+
+__global__ void fbp_zero_kernel(float *p, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// host: the plan
+// ---------------------------------------------------------------------------
+
+struct V3 {
+    double x, y, z;
+};
+V3 operator-(V3 a, V3 b) { return {a.x - b.x, a.y - b.y, a.z - b.z}; }
+V3 operator+(V3 a, V3 b) { return {a.x + b.x, a.y + b.y, a.z + b.z}; }
+V3 operator*(double s, V3 a) { return {s * a.x, s * a.y, s * a.z}; }
+double dot(V3 a, V3 b) { return a.x * b.x + a.y * b.y + a.z * b.z; }
+V3 cross(V3 a, V3 b) { return {a.y * b.z - a.z * b.y, a.z * b.x - a.x * b.z, a.x * b.y - a.y * b.x}; }
+double norm(V3 a) { return std::sqrt(dot(a, a)); }
+
+struct ViewFrame {
+    V3 a, c, eu, ev, n;   // n: unit detector normal, from the source side toward the detector
+};
+
+// Windowed Ram-Lak multiplier M_k (k = 0..P/2) for sample spacing d.
+std::vector<double> multiplier(int P, double d, int window) {
+    std::vector<double> cosT(P);
+    for (int j = 0; j < P; ++j) cosT[j] = std::cos(2.0 * M_PI * j / P);
+    std::vector<double> h(P, 0.0);
+    for (int j = 0; j < P; ++j) {
+        const long n = j >= P / 2 + (P % 2) ? (long)j - P : j;   // signed index in [-P/2, P/2)
+        if (n == 0) h[j] = 1.0 / (4.0 * d * d);
+        else if (n % 2 != 0) h[j] = -1.0 / ((M_PI * (double)n * d) * (M_PI * (double)n * d));
+    }
+    std::vector<double> M(P / 2 + 1);
+    for (int k = 0; k <= P / 2; ++k) {
+        double s = 0.0;
+        for (int j = 0; j < P; ++j) s += h[j] * cosT[(long)k * j % P];
+        const double f = (double)k / P;
+        double w = 1.0;
+        switch (window) {
+            case CT_WINDOW_SHEPP_LOGAN: w = f == 0.0 ? 1.0 : std::sin(M_PI * f) / (M_PI * f); break;
+            case CT_WINDOW_COSINE: w = std::cos(M_PI * f); break;
+            case CT_WINDOW_HAMMING: w = 0.54 + 0.46 * std::cos(2.0 * M_PI * f); break;
+            case CT_WINDOW_HANN: w = 0.5 + 0.5 * std::cos(2.0 * M_PI * f); break;
+            default: break;
+        }
+        M[k] = d * s * w;
+    }
+    return M;
+}
+
+// Spatial taps k[n] = inverse real DFT of M (length P), for n in [-U8, U8).
+std::vector<float> filter_taps(int P, int U8, const std::vector<double> &M) {
+    std::vector<double> cosT(P);
+    for (int j = 0; j < P; ++j) cosT[j] = std::cos(2.0 * M_PI * j / P);
+    const int kmax = (P + 1) / 2 - 1;   // bins doubled by the Hermitian symmetry
+    std::vector<float> t(2 * (size_t)U8);
+    for (int i = 0; i < 2 * U8; ++i) {
+        const long n = i - U8;
+        const long nm = ((n % P) + P) % P;
+        double s = M[0];
+        for (int k = 1; k <= kmax; ++k) s += 2.0 * M[k] * cosT[(long)k * nm % P];
+        if (P % 2 == 0) s += M[P / 2] * ((nm % 2) ? -1.0 : 1.0);
+        t[i] = (float)(s / P);
+    }
+    return t;
+}
+
+bool solve(int n, double A[3][3], double b[3], double x[3]) {
+    int piv[3] = {0, 1, 2};
+    double M[3][4];
+    for (int i = 0; i < n; ++i) {
+        for (int j = 0; j < n; ++j) M[i][j] = A[i][j];
+        M[i][n] = b[i];
+    }
+    double scale = 0.0;
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < n; ++j) scale = std::max(scale, std::fabs(A[i][j]));
+    for (int c = 0; c < n; ++c) {
+        int p = c;
+        for (int r = c + 1; r < n; ++r)
+            if (std::fabs(M[r][c]) > std::fabs(M[p][c])) p = r;
+        if (!(std::fabs(M[p][c]) > 1e-9 * scale)) return false;
+        for (int j = 0; j <= n; ++j) std::swap(M[c][j], M[p][j]);
+        std::swap(piv[c], piv[p]);
+        for (int r = c + 1; r < n; ++r) {
+            const double m = M[r][c] / M[c][c];
+            for (int j = c; j <= n; ++j) M[r][j] -= m * M[c][j];
+        }
+    }
+    for (int i = n - 1; i >= 0; --i) {
+        double s = M[i][n];
+        for (int j = i + 1; j < n; ++j) s -= M[i][j] * x[j];
+        x[i] = s / M[i][i];
+    }
+    return true;
+}
+
+}  // namespace
+
+struct ct_fbp_s {
+    uint64_t magic = 0;
+    GeomHost h;
+    int device = 0;
+    int U8 = 8, VT = 1, S = 8;
+    double iso[3] = {0, 0, 0};
+    std::vector<double> ang;
+    float *d_taps = nullptr;
+    float *d_fview = nullptr;
+    float *d_parker = nullptr;
+    double *d_bp = nullptr;
+};
+
+namespace {
+
+void free_plan(ct_fbp_s *f) {
+    if (f->d_taps) (void)hipFree(f->d_taps);
+    if (f->d_fview) (void)hipFree(f->d_fview);
+    if (f->d_parker) (void)hipFree(f->d_parker);
+    if (f->d_bp) (void)hipFree(f->d_bp);
+    delete f;
+}
+
+bool valid_plan(ct_fbp_t f) { return f && f->magic == kFbpMagic; }
+
+ct_status_t plan_device(ct_fbp_t f) {
+    int cur = -1;
+    const hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fhip(e, "hipGetDevice");
+    if (cur != f->device) return ffail(CT_E_ARG, "current HIP device differs from the plan's device");
+    return CT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, const double *angular_weights,
+                          const ct_fbp_opts_t *opts, ct_fbp_t *out) {
+    if (!out) return ffail(CT_E_NULL, "output plan pointer is NULL");
+    *out = nullptr;
+    if (!opts) return ffail(CT_E_NULL, "opts is NULL");
+    GeomHost h;
+    const char *why = "";
+    ct_status_t st = validate_desc(desc, &h, &why);
+    if (st != CT_OK) return ffail(st, why);
+    if (h.beam != CT_PARALLEL2D && h.beam != CT_FAN2D && h.beam != CT_CONE)
+        return ffail(CT_E_ARG, "FBP/FDK covers parallel2d, fan2d and cone beams");
+    if (opts->window < CT_WINDOW_RAMLAK || opts->window > CT_WINDOW_HANN) return ffail(CT_E_ARG, "unknown window");
+    if (opts->pad_factor < 1 || opts->pad_factor > 16) return ffail(CT_E_ARG, "pad_factor must be in [1, 16]");
+    if (opts->reserved != 0) return ffail(CT_E_ARG, "reserved must be 0");
+    const bool persp = h.beam != CT_PARALLEL2D;
+    if (opts->short_scan && !persp) return ffail(CT_E_ARG, "short scans (Parker weights) need a fan or cone beam");
+    if (h.U < 2 || (h.beam == CT_CONE && h.V < 2)) return ffail(CT_E_SHAPE, "interpolation needs >= 2 detector bins per axis");
+    if (h.U > 4096) return ffail(CT_E_RANGE, "the filter supports U <= 4096");
+    if ((int64_t)opts->pad_factor * h.U > 16384) return ffail(CT_E_RANGE, "pad_factor * U must be <= 16384");
+    if (h.D * h.H * h.W >= (int64_t(1) << 30) || h.n_views * h.U * h.V >= (int64_t(1) << 31))
+        return ffail(CT_E_RANGE, "volume or sinogram too large for one buffer");
+    if (!angular_weights && !angles) return ffail(CT_E_NULL, "angles (or angular_weights) must be given");
+    if (opts->short_scan && !angles) return ffail(CT_E_NULL, "short scans need the angles");
+    const int64_t nv = h.n_views;
+    if (angles)
+        for (int64_t i = 0; i < nv; ++i)
+            if (!std::isfinite(angles[i])) return ffail(CT_E_NONFINITE, "angle not finite");
+    if (angular_weights)
+        for (int64_t i = 0; i < nv; ++i)
+            if (!std::isfinite(angular_weights[i])) return ffail(CT_E_NONFINITE, "angular weight not finite");
+    if (opts->iso_given)
+        for (int k = 0; k < 3; ++k)
+            if (!std::isfinite(opts->iso[k])) return ffail(CT_E_NONFINITE, "isocentre not finite");
+
+    // frames and unit normals
+    std::vector<ViewFrame> fr(nv);
+    for (int64_t i = 0; i < nv; ++i) {
+        const double *r = desc->frames + 12 * i;
+        ViewFrame &v = fr[i];
+        v.a = {r[0], r[1], r[2]};
+        v.c = {r[3], r[4], r[5]};
+        v.eu = {r[6], r[7], r[8]};
+        v.ev = {r[9], r[10], r[11]};
+        if (h.beam == CT_CONE) v.n = cross(v.eu, v.ev);
+        else v.n = {v.eu.y, -v.eu.x, 0.0};
+        v.n = (1.0 / norm(v.n)) * v.n;
+        const double toward = persp ? dot(v.c - v.a, v.n) : dot(v.a, v.n);
+        if (toward < 0) v.n = -1.0 * v.n;
+    }
+
+    ct_fbp_s *f = new (std::nothrow) ct_fbp_s();
+    if (!f) return ffail(CT_E_NOMEM, "host allocation failed");
+    f->h = h;
+    // isocentre: given, or the least-squares point nearest the lines a + t n
+    if (opts->iso_given) {
+        for (int k = 0; k < 3; ++k) f->iso[k] = opts->iso[k];
+        if (h.is2d) f->iso[2] = 0.0;
+    } else if (persp) {
+        const int dim = h.is2d ? 2 : 3;
+        double A[3][3] = {{0}}, b[3] = {0}, x[3] = {0};
+        for (const ViewFrame &v : fr) {
+            const double nn[3] = {v.n.x, v.n.y, v.n.z}, aa[3] = {v.a.x, v.a.y, v.a.z};
+            for (int i = 0; i < dim; ++i)
+                for (int j = 0; j < dim; ++j) {
+                    const double pij = (i == j ? 1.0 : 0.0) - nn[i] * nn[j];
+                    A[i][j] += pij;
+                    b[i] += pij * aa[j];
+                }
+        }
+        if (!solve(dim, A, b, x)) {
+            delete f;
+            return ffail(CT_E_ARG, "the isocentre cannot be estimated from these views; pass it");
+        }
+        for (int k = 0; k < dim; ++k) f->iso[k] = x[k];
+    }
+    // angular weights: given, or half the gaps to the neighbouring views
+    f->ang.assign(nv, 0.0);
+    const bool redundant = persp && !opts->short_scan;
+    if (angular_weights) {
+        for (int64_t i = 0; i < nv; ++i) f->ang[i] = angular_weights[i];
+    } else if (nv == 1) {
+        f->ang[0] = M_PI;
+    } else if (opts->short_scan) {
+        for (int64_t i = 0; i < nv; ++i) {
+            const double lo = angles[i > 0 ? i - 1 : 0], hi = angles[i + 1 < nv ? i + 1 : nv - 1];
+            f->ang[i] = 0.5 * std::fabs(hi - lo);
+        }
+    } else {
+        const double period = persp ? 2.0 * M_PI : M_PI;
+        const double sgn = angles[nv - 1] >= angles[0] ? 1.0 : -1.0;
+        for (int64_t i = 0; i < nv; ++i) {
+            const double nx = i + 1 < nv ? angles[i + 1] : angles[0] + sgn * period;
+            const double pv = i > 0 ? angles[i - 1] : angles[nv - 1] - sgn * period;
+            f->ang[i] = 0.5 * std::fabs(nx - pv) * (redundant ? 0.5 : 1.0);
+        }
+    }
+    const int U = (int)h.U, V = (int)h.V;
+    // Parker weights
+    std::vector<float> parker;
+    if (opts->short_scan) {
+        double rot = 0.0;
+        for (int64_t i = 0; i + 1 < nv; ++i) rot += fr[i].a.x * fr[i + 1].a.y - fr[i].a.y * fr[i + 1].a.x;
+        const double sense = rot >= 0 ? 1.0 : -1.0;
+        std::vector<double> gam((size_t)nv * U);
+        double delta = 0.0;
+        for (int64_t i = 0; i < nv; ++i)
+            for (int u = 0; u < U; ++u) {
+                const V3 p = fr[i].c + ((u - 0.5 * (U - 1)) * h.du) * fr[i].eu;
+                const V3 d = p - fr[i].a;
+                const double cr = fr[i].n.x * d.y - fr[i].n.y * d.x, dt = fr[i].n.x * d.x + fr[i].n.y * d.y;
+                const double g = sense * std::atan2(cr, dt);
+                gam[(size_t)i * U + u] = g;
+                delta = std::max(delta, std::fabs(g));
+            }
+        double span = 0.0;
+        for (int64_t i = 0; i < nv; ++i) span = std::max(span, std::fabs(angles[i] - angles[0]));
+        if (span < M_PI + 2.0 * delta - 1e-9 * (M_PI + 2.0 * delta)) {
+            delete f;
+            return ffail(CT_E_ARG, "a short scan needs an angular span of at least pi + 2 x half fan angle");
+        }
+        parker.resize((size_t)nv * U);
+        for (int64_t i = 0; i < nv; ++i) {
+            const double be = std::fabs(angles[i] - angles[0]);
+            for (int u = 0; u < U; ++u) {
+                const double g = gam[(size_t)i * U + u];
+                double w = 0.0;
+                if (be >= 0 && be < 2.0 * (delta - g)) {
+                    const double s = std::sin(M_PI / 4.0 * be / (delta - g));
+                    w = s * s;
+                } else if (be >= 2.0 * (delta - g) && be <= M_PI - 2.0 * g) {
+                    w = 1.0;
+                } else if (be > M_PI - 2.0 * g && be <= M_PI + 2.0 * delta) {
+                    const double s = std::sin(M_PI / 4.0 * (M_PI + 2.0 * delta - be) / (delta + g));
+                    w = s * s;
+                }
+                parker[(size_t)i * U + u] = (float)w;
+            }
+        }
+    }
+    // filter: taps, launch shape
+    const int P = opts->pad_factor * U;
+    f->U8 = (U + 7) / 8 * 8;
+    // rows per block: at most four tasks of 8 outputs per thread, LDS under 64 KB
+    f->VT = f->U8 <= 512 ? 16 : (f->U8 <= 1024 ? 8 : (f->U8 <= 2048 ? 2 : 1));
+    f->S = f->U8 + 4;
+    const std::vector<float> taps = filter_taps(P, f->U8, multiplier(P, h.du, opts->window));
+    std::vector<float> fview((size_t)nv * kFv, 0.f);
+    std::vector<double> bp((size_t)nv * kBpv, 0.0);
+    // voxel centre of index (i, j, k): lo + (idx + 0.5) s per axis; 2D: z = 0
+    const double sx = h.sx, sy = h.sy, sz = h.is2d ? 1.0 : h.sz;
+    const V3 lo = {-0.5 * h.W * sx + 0.5 * sx, -0.5 * h.H * sy + 0.5 * sy,
+                   h.is2d ? 0.0 : -0.5 * h.D * sz + 0.5 * sz};
+    const V3 iso = {f->iso[0], f->iso[1], f->iso[2]};
+    for (int64_t i = 0; i < nv; ++i) {
+        const ViewFrame &v = fr[i];
+        float *fv = fview.data() + i * kFv;
+        double *t = bp.data() + i * kBpv;
+        V3 Pu, Pv, Pw;
+        double pu, pv, pw, K;
+        if (persp) {
+            const double D = dot(v.c - v.a, v.n), R = dot(iso - v.a, v.n);
+            const V3 ca = v.c - v.a;
+            fv[0] = (float)D;
+            fv[1] = (float)ca.x; fv[2] = (float)ca.y; fv[3] = (float)ca.z;
+            fv[11] = 1.f;
+            // w(X) = (X - a).n ; u_h = alpha_u w + (D / du) (X - a).e_u
+            const double au = dot(v.a - v.c, v.eu) / h.du + 0.5 * (U - 1);
+            const double av = h.is2d ? 0.0 : dot(v.a - v.c, v.ev) / h.dv + 0.5 * (V - 1);
+            Pw = v.n;
+            pw = -dot(v.a, v.n);
+            Pu = au * v.n + (D / h.du) * v.eu;
+            pu = -au * dot(v.a, v.n) - (D / h.du) * dot(v.a, v.eu);
+            if (h.is2d) {
+                Pv = {0, 0, 0};
+                pv = 0.0;
+            } else {
+                Pv = av * v.n + (D / h.dv) * v.ev;
+                pv = -av * dot(v.a, v.n) - (D / h.dv) * dot(v.a, v.ev);
+            }
+            K = R * D;
+        } else {
+            fv[11] = 0.f;
+            Pw = {0, 0, 0};
+            pw = 1.0;
+            Pu = (1.0 / h.du) * v.eu;
+            pu = -dot(v.c, v.eu) / h.du + 0.5 * (U - 1);
+            Pv = {0, 0, 0};
+            pv = 0.0;
+            K = 1.0;
+        }
+        fv[4] = (float)(v.eu.x * h.du); fv[5] = (float)(v.eu.y * h.du); fv[6] = (float)(v.eu.z * h.du);
+        fv[7] = (float)(v.ev.x * h.dv); fv[8] = (float)(v.ev.y * h.dv); fv[9] = (float)(v.ev.z * h.dv);
+        fv[10] = (float)f->ang[i];
+        // to index coordinates: X = lo + idx * s
+        auto put = [&](int off, V3 P, double p) {
+            t[off + 0] = P.x * sx;
+            t[off + 1] = P.y * sy;
+            t[off + 2] = P.z * sz;
+            t[off + 3] = dot(P, lo) + p;
+        };
+        put(0, Pu, pu);
+        put(4, Pv, pv);
+        put(8, Pw, pw);
+        t[12] = K;
+    }
+    hipError_t e = hipGetDevice(&f->device);
+    if (e == hipSuccess) e = hipMalloc((void **)&f->d_taps, taps.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void **)&f->d_fview, fview.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void **)&f->d_bp, bp.size() * sizeof(double));
+    if (e == hipSuccess && !parker.empty()) e = hipMalloc((void **)&f->d_parker, parker.size() * sizeof(float));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        free_plan(f);
+        return ffail(CT_E_NOMEM, "hipMalloc of the FBP tables failed");
+    }
+    e = hipMemcpy(f->d_taps, taps.data(), taps.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(f->d_fview, fview.data(), fview.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(f->d_bp, bp.data(), bp.size() * sizeof(double), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !parker.empty())
+        e = hipMemcpy(f->d_parker, parker.data(), parker.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        free_plan(f);
+        return fhip(e, "upload of the FBP tables");
+    }
+    f->magic = kFbpMagic;
+    *out = f;
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_fbp_destroy(ct_fbp_t f) {
+    if (!f) return CT_OK;
+    if (!valid_plan(f)) return ffail(CT_E_ARG, "invalid FBP plan");
+    f->magic = 0;
+    free_plan(f);
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_fbp_info(ct_fbp_t f, double *iso, double *angular_weights) {
+    if (!valid_plan(f)) return ffail(CT_E_ARG, "invalid FBP plan");
+    if (iso)
+        for (int k = 0; k < 3; ++k) iso[k] = f->iso[k];
+    if (angular_weights) std::memcpy(angular_weights, f->ang.data(), f->ang.size() * sizeof(double));
+    set_error("");
+    return CT_OK;
+}
+
+static bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const char *x = (const char *)a, *y = (const char *)b;
+    return x < y + nb && y < x + na;
+}
+
+ct_status_t ct_fbp_filter(ct_fbp_t f, const float *sino, float *filtered, ct_stream_t stream) {
+    if (!valid_plan(f)) return ffail(CT_E_ARG, "invalid FBP plan");
+    if (!sino || !filtered) return ffail(CT_E_NULL, "sino and filtered must be non-NULL");
+    const GeomHost &h = f->h;
+    const size_t sb = (size_t)h.n_views * h.U * h.V * sizeof(float);
+    if (overlaps(sino, sb, filtered, sb)) return ffail(CT_E_ALIAS, "filtered overlaps sino");
+    ct_status_t st = plan_device(f);
+    if (st != CT_OK) return st;
+    FilterArgs a;
+    a.sino = sino;
+    a.out = filtered;
+    a.taps = f->d_taps;
+    a.fview = f->d_fview;
+    a.parker = f->d_parker;
+    a.U = (int)h.U;
+    a.V = (int)h.V;
+    a.n_views = (int)h.n_views;
+    a.U8 = f->U8;
+    a.VT = f->VT;
+    a.S = f->S;
+    a.two_d = h.is2d ? 1 : 0;
+    const unsigned blocks = h.is2d ? (unsigned)((h.n_views + f->VT - 1) / f->VT)
+                                   : (unsigned)(h.n_views * ((h.V + f->VT - 1) / f->VT));
+    const size_t lds = (2 * (size_t)f->U8 + (size_t)f->VT * f->S) * sizeof(float);
+    hipLaunchKernelGGL(fbp_filter_kernel, dim3(blocks), dim3(256), lds, (hipStream_t)stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fhip(e, "ct_fbp_filter launch");
+    set_error("");
+    return CT_OK;
+}
+
+static BpArgs bp_args(ct_fbp_t f) {
+    const GeomHost &h = f->h;
+    BpArgs a;
+    a.bp = f->d_bp;
+    a.W = (int)h.W;
+    a.H = (int)h.H;
+    a.D = (int)h.D;
+    a.U = (int)h.U;
+    a.V = (int)h.V;
+    a.n_views = (int)h.n_views;
+    a.two_d = h.is2d ? 1 : 0;
+    const int TX = h.is2d ? 16 : 4, TY = h.is2d ? 16 : 4, TZ = h.is2d ? 1 : 16;
+    a.nbx = (a.W + TX - 1) / TX;
+    a.nby = (a.H + TY - 1) / TY;
+    a.nbz = (a.D + TZ - 1) / TZ;
+    a.q = nullptr;
+    a.vol = nullptr;
+    a.sino_out = nullptr;
+    return a;
+}
+
+ct_status_t ct_fbp_backproject(ct_fbp_t f, const float *filtered, float *vol, ct_stream_t stream) {
+    if (!valid_plan(f)) return ffail(CT_E_ARG, "invalid FBP plan");
+    if (!filtered || !vol) return ffail(CT_E_NULL, "filtered and vol must be non-NULL");
+    const GeomHost &h = f->h;
+    const size_t sb = (size_t)h.n_views * h.U * h.V * sizeof(float), vb = (size_t)h.D * h.H * h.W * sizeof(float);
+    if (overlaps(filtered, sb, vol, vb)) return ffail(CT_E_ALIAS, "vol overlaps filtered");
+    ct_status_t st = plan_device(f);
+    if (st != CT_OK) return st;
+    BpArgs a = bp_args(f);
+    a.q = filtered;
+    a.vol = vol;
+    const dim3 grid((unsigned)(a.nbx * a.nby * a.nbz));
+    if (h.is2d) hipLaunchKernelGGL((fbp_bp_kernel<false, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    else hipLaunchKernelGGL((fbp_bp_kernel<false, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fhip(e, "ct_fbp_backproject launch");
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_fbp_backproject_transpose(ct_fbp_t f, const float *vol, float *sino, ct_stream_t stream) {
+    if (!valid_plan(f)) return ffail(CT_E_ARG, "invalid FBP plan");
+    if (!vol || !sino) return ffail(CT_E_NULL, "vol and sino must be non-NULL");
+    const GeomHost &h = f->h;
+    const size_t sn = (size_t)h.n_views * h.U * h.V, vb = (size_t)h.D * h.H * h.W * sizeof(float);
+    if (overlaps(sino, sn * sizeof(float), vol, vb)) return ffail(CT_E_ALIAS, "sino overlaps vol");
+    ct_status_t st = plan_device(f);
+    if (st != CT_OK) return st;
+    hipLaunchKernelGGL(fbp_zero_kernel, dim3(2048), dim3(256), 0, (hipStream_t)stream, sino, sn);
+    BpArgs a = bp_args(f);
+    a.vol = const_cast<float *>(vol);   // read only in the transpose
+    a.sino_out = sino;
+    const dim3 grid((unsigned)(a.nbx * a.nby * a.nbz));
+    if (h.is2d) hipLaunchKernelGGL((fbp_bp_kernel<true, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    else hipLaunchKernelGGL((fbp_bp_kernel<true, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fhip(e, "ct_fbp_backproject_transpose launch");
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_fbp_run(ct_fbp_t f, const float *sino, float *work, float *vol, ct_stream_t stream) {
+    if (!valid_plan(f)) return ffail(CT_E_ARG, "invalid FBP plan");
+    if (!sino || !work || !vol) return ffail(CT_E_NULL, "sino, work and vol must be non-NULL");
+    const GeomHost &h = f->h;
+    const size_t vb = (size_t)h.D * h.H * h.W * sizeof(float), sb = (size_t)h.n_views * h.U * h.V * sizeof(float);
+    if (overlaps(sino, sb, vol, vb) || overlaps(sino, sb, work, sb) || overlaps(work, sb, vol, vb))
+        return ffail(CT_E_ALIAS, "sino, work and vol must not overlap");
+    ct_status_t st = ct_fbp_filter(f, sino, work, stream);
+    if (st != CT_OK) return st;
+    return ct_fbp_backproject(f, work, vol, stream);
+}
+
+}  // extern "C"
