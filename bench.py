@@ -19,7 +19,12 @@ c5cgls time CGLS iterations (ct_cgls_step: A p with ||q||^2, r -= alpha q,
 A^T r with ||s||^2 and x += alpha p, p = s + beta p) on the same workloads
 from y = A phantom, after ct_cgls_init.  --workload c5cyl times A + A^T on C5's
 acquisition with a cylindrical detector centred on the source (radius 1500,
-the parameterized-surface path).
+the parameterized-surface path).  --workload c5fdk times FDK on C5's
+acquisition (ct_fbp_filter: cosine weights, Ram-Lak ramp filter padded to 2U,
+angular weights; ct_fbp_backproject: the interpolating weighted
+backprojection) of y = A phantom; its value is voxel-view updates per second
+(512^3 voxels x 720 views per step), and both kernels are ALU-bound, so the
+roofline is against the fp32 vector peak.
 
 Roofline: algorithmic HBM bytes of the dominant kernel per launch divided by
 its average duration (HIP events on the launch stream), against 8 TB/s.
@@ -38,11 +43,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12
+# fp32 vector peak without packed-math: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
+ALU_PEAK = 256 * 4 * 16 * 2 * 2.4e9
+# FDK backprojection flops per voxel-view: three affine forms (9 FMA = 18), a
+# reciprocal (1), u and v (2), the weight K / w^2 (2), two fractional parts (2),
+# the bilinear interpolation (3 lerps of sub + FMA = 9) and the accumulation (2)
+FDK_FLOPS_PER_UPDATE = 36
 
 
 def _kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("ct_kernels.hip", "ct_abi.hip", "ct_geometry.cpp"):
+    for f in ("ct_kernels.hip", "ct_abi.hip", "ct_geometry.cpp", "ct_fbp.hip"):
         with open(os.path.join(ROOT, "ray_driven_projector_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -91,12 +102,31 @@ def cpu_baseline(wl, n_views_sample: int):
                       f"dense sinogram, {nnz} intersections each; A {ta:.2f} s, A^T {tat:.2f} s"}
 
 
+def cpu_baseline_fdk(wl, angles, n_vox: int):
+    """Float64 oracle of the FDK backprojection on a bounded sample of voxels
+    (all views), in voxel-view updates per second."""
+    import numpy as np
+
+    from oracle import fbp as F
+
+    rng = np.random.default_rng(7)
+    ids = rng.choice(wl.n_voxels, n_vox, replace=False)
+    q = rng.standard_normal(wl.sino_shape).astype(np.float32)
+    t0 = time.perf_counter()
+    F.weighted_backproject_voxels(wl, q, ids)
+    dt = time.perf_counter() - t0
+    return {"value": n_vox * wl.n_views / dt / 1e9, "unit": "G voxel-view updates/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_vox} random voxels of the 512^3 volume, all {wl.n_views} views (numpy, "
+                      f"one thread): {dt:.2f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["c4", "c5", "c4cgls", "c5cgls", "c5cyl"], default="c4")
+    ap.add_argument("--workload", choices=["c4", "c5", "c4cgls", "c5cgls", "c5cyl", "c5fdk"], default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-views", type=int, default=16)
     ap.add_argument("--extra", action="store_true", help="also time A, A^T and atomic A^T alone")
@@ -146,7 +176,25 @@ def main():
     print(f"# nnz={nnz} rays={M} voxels={N}", file=sys.stderr, flush=True)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    if cgls:
+    fdk = args.workload == "c5fdk"
+    if fdk:
+        fdk_angles = W.angles(wl.n_views, 2 * np.pi)
+        fplan = rdp.FBP.from_workload(wl, fdk_angles, window="ram-lak", pad_factor=2)
+        work = torch.empty(g.sino_shape, device="cuda")
+        vol = torch.empty(g.vol_shape, device="cuda")
+        names = ("fbp_filter", "fbp_backproject")
+        U = wl.det_shape[0]
+        flops_per = {"fbp_filter": 2 * U * M, "fbp_backproject": FDK_FLOPS_PER_UPDATE * N * wl.n_views}
+        kern_names = {"fbp_filter": "fbp_filter_kernel",
+                      "fbp_backproject": "fbp_bp_kernel<false, false, 4>"}
+
+        def step(evs):
+            evs[0].record(stream)
+            rdp.ct_fbp_filter(fplan, y, work, stream)
+            evs[1].record(stream)
+            rdp.ct_fbp_backproject(fplan, work, vol, stream)
+            evs[2].record(stream)
+    elif cgls:
         x = torch.zeros(g.vol_shape, device="cuda")
         r = torch.empty(g.sino_shape, device="cuda")
         q = torch.empty(g.sino_shape, device="cuda")
@@ -222,8 +270,12 @@ def main():
     if cgls:
         avg.pop("none")
     dom = max(avg, key=avg.get)
-    achieved = bytes_per[dom] / (avg[dom] * 1e-3)
-    value = 2 * nnz / (ms_step * 1e-3) / 1e9
+    if fdk:
+        achieved = flops_per[dom] / (avg[dom] * 1e-3)
+        value = N * wl.n_views / (ms_step * 1e-3) / 1e9
+    else:
+        achieved = bytes_per[dom] / (avg[dom] * 1e-3)
+        value = 2 * nnz / (ms_step * 1e-3) / 1e9
 
     extra = {}
     if args.extra:
@@ -244,9 +296,10 @@ def main():
             extra[f"{name}_G_intersections_per_s"] = nnz / (np.median(ts) * 1e-3) / 1e9
 
     res = {
-        "metric": "G ray-voxel intersections/s for A and A^T; ms per SIRT iteration at 512^3",
+        "metric": ("G voxel-view updates/s of FDK at 512^3" if fdk else
+                   "G ray-voxel intersections/s for A and A^T; ms per SIRT iteration at 512^3"),
         "value": round(value, 3),
-        "unit": "G ray-voxel intersections/s",
+        "unit": "G voxel-view updates/s" if fdk else "G ray-voxel intersections/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -257,7 +310,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": (wl.name + (", one CGLS iteration (from y = A phantom)" if cgls else
+            "workload": (wl.name + (", FDK (Ram-Lak, pad 2) of y = A phantom" if fdk else
+                                    ", one CGLS iteration (from y = A phantom)" if cgls else
                                     ", one SIRT iteration (A with residual + A^T with update)"
                                     if cfg == 4 else ", A + A^T")),
             "volume": list(wl.vol_shape), "views": wl.n_views, "detector": list(wl.det_shape),
@@ -266,12 +320,17 @@ def main():
         "ms_per_sirt_iteration": round(ms_step, 3) if (cfg == 4 and not cgls) else None,
         "ms_per_cgls_iteration": round(ms_step, 3) if cgls else None,
         "kernel_ms": {k: round(v, 3) for k, v in avg.items()},
-        "roofline": {
+        "roofline": ({
+            "bound": "alu", "kernel": kern_names[dom], "achieved": round(achieved / 1e12, 2),
+            "peak": round(ALU_PEAK / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK, 4),
+            "traffic": _traffic(dom, args.workload),
+            "algorithmic_flops_per_launch": flops_per[dom],
+        } if fdk else {
             "bound": "hbm", "kernel": kern_names[dom], "achieved": round(achieved / 1e9, 1),
             "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
             "traffic": _traffic(dom, args.workload),
             "algorithmic_bytes_per_launch": bytes_per[dom],
-        },
+        }),
     }
     res.update(extra)
     if args.host_stream:
@@ -295,9 +354,12 @@ def main():
         hres["pcie_bytes"] = {"A": vb * n_bt + sb,   # axis is the library's choice
                               "AT": sb * (n_sl_a if n_bt > 1 else 1) + vb}
         res["host_stream"] = hres
+    if fdk:
+        res["kernel_ms_note"] = "fbp_filter: pre-weights + ramp + angular weights; fbp_backproject: gather"
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_views)
+        res["cpu_baseline"] = (cpu_baseline_fdk(wl, fdk_angles, 100000) if fdk else
+                               cpu_baseline(wl, args.cpu_views))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

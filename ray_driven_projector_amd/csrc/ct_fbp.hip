@@ -36,6 +36,15 @@ namespace {
 constexpr uint64_t kFbpMagic = 0x43544642'50303031ull;   // "CTFBP001"
 constexpr int kBpViews = 256;      // views whose constants one LDS batch holds
 constexpr int kBpConst = 16;       // floats per view in that batch
+constexpr int kZRun = 4;           // 3D backprojection: voxels per thread along z
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const float *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ float buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
+}
 
 ct_status_t ffail(ct_status_t st, const char *msg) {
     set_error(msg);
@@ -193,8 +202,12 @@ struct BpArgs {
 // detector anchors u0, v0 (the projection of X0, rounded down),
 //   w  = Aw + Bw . d,   u - u0 = (Au + Bu . d) / w,   v - v0 = (Av + Bv . d) / w
 // for d = X - X0 in index units; the anchors keep the float32 arithmetic on
-// small numbers.
-__device__ __forceinline__ void view_consts(const double *p, double x0, double y0, double z0, float *c) {
+// small numbers.  c[15] = 1 when the whole tile (half extents hx, hy, hz about
+// X0) lies in front of the source and projects strictly inside the detector,
+// so that every bilinear tap exists: the projection of a box is inside the
+// hull of its corners' projections.
+__device__ __forceinline__ void view_consts(const double *p, double x0, double y0, double z0, double hx,
+                                            double hy, double hz, int U, int V, bool two_d, float *c) {
     const double uh = p[0] * x0 + p[1] * y0 + p[2] * z0 + p[3];
     const double vh = p[4] * x0 + p[5] * y0 + p[6] * z0 + p[7];
     const double wh = p[8] * x0 + p[9] * y0 + p[10] * z0 + p[11];
@@ -215,14 +228,38 @@ __device__ __forceinline__ void view_consts(const double *p, double x0, double y
     c[12] = (float)p[12];
     c[13] = (float)fmin(fmax(u0, -1e9), 1e9);
     c[14] = (float)fmin(fmax(v0, -1e9), 1e9);
-    c[15] = 0.f;
+    // corners, in float32 on the block-relative constants (errors ~1e-4 bin,
+    // far inside the margin)
+    bool in = wh > 0.0;
+    const float m = 0.01f;
+    const float ulo = m - c[13], uhi = (float)(U - 1) - m - c[13];
+    const float vlo = m - c[14], vhi = (float)(V - 1) - m - c[14];
+    for (int k = 0; k < 8 && in; ++k) {
+        const float X = (k & 1) ? (float)hx : -(float)hx, Y = (k & 2) ? (float)hy : -(float)hy,
+                    Z = (k & 4) ? (float)hz : -(float)hz;
+        const float w = c[8] + c[9] * X + c[10] * Y + c[11] * Z;
+        if (!(w > 0.f)) {
+            in = false;
+            break;
+        }
+        const float u = (c[0] + c[1] * X + c[2] * Y + c[3] * Z) / w;
+        const float v = (c[4] + c[5] * X + c[6] * Y + c[7] * Z) / w;
+        in = u >= ulo && u <= uhi && (two_d || (v >= vlo && v <= vhi));
+    }
+    c[15] = in ? 1.f : 0.f;
 }
 
-template <bool TRANSPOSE, bool TWO_D>
+// One thread takes ZR voxels of a z column, 16 planes apart (the 16 lanes of
+// a row of the wave hold 16 consecutive planes, which for the usual cone
+// geometries land on neighbouring detector rows), and walks them with the
+// affine increments of w, u_h, v_h.  Views are taken in LDS batches of
+// kBpViews whose block-relative constants the first kBpViews threads compute
+// in float64.
+template <bool TRANSPOSE, bool TWO_D, int ZR>
 __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
     __shared__ float cst[kBpViews * kBpConst];
-    // tile: 3D 4 x 4 x 16 voxels (x, y, z), z fastest across lanes; 2D 16 x 16 (x fastest)
-    constexpr int TX = TWO_D ? 16 : 4, TY = TWO_D ? 16 : 4, TZ = TWO_D ? 1 : 16;
+    // tile: 3D 4 x 4 x (16 ZR) voxels (x, y, z); 2D 16 x 16
+    constexpr int TX = TWO_D ? 16 : 4, TY = TWO_D ? 16 : 4, TZ = TWO_D ? 1 : 16 * ZR;
     const int b = blockIdx.x;
     const int bx = b % a.nbx, by = (b / a.nbx) % a.nby, bz = b / (a.nbx * a.nby);
     int lx, ly, lz;
@@ -235,80 +272,129 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
         ly = (threadIdx.x >> 4) & 3;
         lx = threadIdx.x >> 6;
     }
-    const int ix = bx * TX + lx, iy = by * TY + ly, iz = bz * TZ + lz;
-    const bool inside = ix < a.W && iy < a.H && iz < a.D;
-    // anchor: the tile centre (index coordinates of voxel centres are i + 0.5
-    // in the tables' convention: they take the index itself)
+    const int ix = bx * TX + lx, iy = by * TY + ly, iz0 = bz * TZ + lz;
+    const bool col_in = ix < a.W && iy < a.H && iz0 < a.D;
     const double X0 = bx * TX + 0.5 * (TX - 1), Y0 = by * TY + 0.5 * (TY - 1), Z0 = bz * TZ + 0.5 * (TZ - 1);
     const float dx = (float)lx - 0.5f * (TX - 1), dy = (float)ly - 0.5f * (TY - 1),
                 dz = (float)lz - 0.5f * (TZ - 1);
-    const size_t vidx = ((size_t)iz * a.H + iy) * a.W + ix;
-    const float f = (TRANSPOSE && inside) ? a.vol[vidx] : 0.f;
+    const size_t plane = (size_t)a.H * a.W;
+    const size_t vidx0 = ((size_t)iz0 * a.H + iy) * a.W + ix;
+    float fz[ZR], acc[ZR];
+#pragma unroll
+    for (int r = 0; r < ZR; ++r) {
+        const bool in = col_in && iz0 + 16 * r < a.D;
+        fz[r] = (TRANSPOSE && in) ? a.vol[vidx0 + (size_t)(16 * r) * plane] : 0.f;
+        acc[r] = 0.f;
+    }
+    bool any = col_in;
+    if (TRANSPOSE) {
+        any = false;
+#pragma unroll
+        for (int r = 0; r < ZR; ++r) any = any || fz[r] != 0.f;
+    }
     const int U = a.U, V = a.V;
-    float acc = 0.f;
     for (int vb = 0; vb < a.n_views; vb += kBpViews) {
         const int nvb = min(kBpViews, a.n_views - vb);
         __syncthreads();
         if ((int)threadIdx.x < nvb)
-            view_consts(a.bp + (size_t)(vb + threadIdx.x) * kBpv, X0, Y0, Z0, cst + threadIdx.x * kBpConst);
+            view_consts(a.bp + (size_t)(vb + threadIdx.x) * kBpv, X0, Y0, Z0, 0.5 * (TX - 1), 0.5 * (TY - 1),
+                        0.5 * (TZ - 1), U, V, TWO_D, cst + threadIdx.x * kBpConst);
         __syncthreads();
-        if (!inside || (TRANSPOSE && f == 0.f)) continue;
+        if (!any) continue;
         for (int k = 0; k < nvb; ++k) {
             const float4 c0 = *(const float4 *)(cst + k * kBpConst);
             const float4 c1 = *(const float4 *)(cst + k * kBpConst + 4);
             const float4 c2 = *(const float4 *)(cst + k * kBpConst + 8);
             const float4 c3 = *(const float4 *)(cst + k * kBpConst + 12);
-            const float w = fmaf(c2.w, dz, fmaf(c2.z, dy, fmaf(c2.y, dx, c2.x)));
-            if (!(w > 0.f)) continue;   // at or behind the source
-            const float r = 1.0f / w;
-            const float nu = fmaf(c0.w, dz, fmaf(c0.z, dy, fmaf(c0.y, dx, c0.x)));
-            const float su = nu * r;
-            const float flu = floorf(su);
-            const float au = su - flu;
-            const int iu = (int)flu + (int)c3.y;
-            const float wgt = c3.x * r * r;
             const size_t vbase = (size_t)(vb + k) * U;
-            if (TWO_D) {
-                const bool ok0 = (unsigned)iu < (unsigned)U, ok1 = (unsigned)(iu + 1) < (unsigned)U;
-                const float k0 = ok0 ? 1.f - au : 0.f, k1 = ok1 ? au : 0.f;
-                const int j0 = ok0 ? iu : 0, j1 = ok1 ? iu + 1 : 0;
-                if (TRANSPOSE) {
-                    const float g = wgt * f;
-                    if (k0 != 0.f) atomicAdd(a.sino_out + vbase + j0, g * k0);
-                    if (k1 != 0.f) atomicAdd(a.sino_out + vbase + j1, g * k1);
-                } else {
-                    const float q0 = a.q[vbase + j0], q1 = a.q[vbase + j1];
-                    acc = fmaf(wgt, fmaf(k0, q0, k1 * q1), acc);
+            // this view's filtered sinogram, addressed with 32-bit offsets
+            const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + vbase * V, (uint32_t)U * V * 4u);
+            const int u0 = (int)c3.y, v0 = (int)c3.z;
+            float w = fmaf(c2.w, dz, fmaf(c2.z, dy, fmaf(c2.y, dx, c2.x)));
+            float nu = fmaf(c0.w, dz, fmaf(c0.z, dy, fmaf(c0.y, dx, c0.x)));
+            float nv = fmaf(c1.w, dz, fmaf(c1.z, dy, fmaf(c1.y, dx, c1.x)));
+            const float sw = 16.f * c2.w, su_ = 16.f * c0.w, sv_ = 16.f * c1.w;
+            const bool fast = c3.w != 0.f;   // uniform over the block
+#pragma unroll
+            for (int r = 0; r < ZR; ++r) {
+                if (r > 0) {
+                    w += sw;
+                    nu += su_;
+                    nv += sv_;
                 }
-            } else {
-                const float nv = fmaf(c1.w, dz, fmaf(c1.z, dy, fmaf(c1.y, dx, c1.x)));
-                const float sv = nv * r;
-                const float flv = floorf(sv);
-                const float av = sv - flv;
-                const int iv = (int)flv + (int)c3.z;
-                const bool u0k = (unsigned)iu < (unsigned)U, u1k = (unsigned)(iu + 1) < (unsigned)U;
-                const bool v0k = (unsigned)iv < (unsigned)V, v1k = (unsigned)(iv + 1) < (unsigned)V;
-                const float ku0 = u0k ? 1.f - au : 0.f, ku1 = u1k ? au : 0.f;
-                const float kv0 = v0k ? 1.f - av : 0.f, kv1 = v1k ? av : 0.f;
-                const int ju0 = u0k ? iu : 0, ju1 = u1k ? iu + 1 : 0;
-                const int jv0 = v0k ? iv : 0, jv1 = v1k ? iv + 1 : 0;
-                const size_t r0 = (vbase + ju0) * V, r1 = (vbase + ju1) * V;
-                if (TRANSPOSE) {
-                    const float g = wgt * f;
-                    if (ku0 * kv0 != 0.f) atomicAdd(a.sino_out + r0 + jv0, g * ku0 * kv0);
-                    if (ku0 * kv1 != 0.f) atomicAdd(a.sino_out + r0 + jv1, g * ku0 * kv1);
-                    if (ku1 * kv0 != 0.f) atomicAdd(a.sino_out + r1 + jv0, g * ku1 * kv0);
-                    if (ku1 * kv1 != 0.f) atomicAdd(a.sino_out + r1 + jv1, g * ku1 * kv1);
+                if (!fast && !(w > 0.f)) continue;   // at or behind the source
+                const float rw = 1.0f / w;
+                const float su = nu * rw;
+                const float flu = floorf(su);
+                const float au = su - flu;
+                const int iu = (int)flu + u0;
+                const float wgt = c3.x * rw * rw;
+                if (TWO_D) {
+                    bool ok0 = true, ok1 = true;
+                    if (!fast) {
+                        ok0 = (unsigned)iu < (unsigned)U;
+                        ok1 = (unsigned)(iu + 1) < (unsigned)U;
+                    }
+                    const float k0 = ok0 ? 1.f - au : 0.f, k1 = ok1 ? au : 0.f;
+                    const int j0 = ok0 ? iu : 0, j1 = ok1 ? iu + 1 : 0;
+                    if (TRANSPOSE) {
+                        const float g = wgt * fz[r];
+                        if (g != 0.f && k0 != 0.f) atomicAdd(a.sino_out + vbase + j0, g * k0);
+                        if (g != 0.f && k1 != 0.f) atomicAdd(a.sino_out + vbase + j1, g * k1);
+                    } else {
+                        const float q0 = buffer_load(rq, (uint32_t)j0 * 4u), q1 = buffer_load(rq, (uint32_t)j1 * 4u);
+                        acc[r] = fmaf(wgt, fmaf(k0, q0, k1 * q1), acc[r]);
+                    }
                 } else {
-                    const float q00 = a.q[r0 + jv0], q01 = a.q[r0 + jv1];
-                    const float q10 = a.q[r1 + jv0], q11 = a.q[r1 + jv1];
-                    const float s0 = fmaf(kv0, q00, kv1 * q01), s1 = fmaf(kv0, q10, kv1 * q11);
-                    acc = fmaf(wgt, fmaf(ku0, s0, ku1 * s1), acc);
+                    const float sv = nv * rw;
+                    const float flv = floorf(sv);
+                    const float av = sv - flv;
+                    const int iv = (int)flv + v0;
+                    if (fast && !TRANSPOSE) {
+                        // every tap exists: plain bilinear interpolation
+                        const uint32_t o = ((uint32_t)iu * V + iv) * 4u;
+                        const float q00 = buffer_load(rq, o), q01 = buffer_load(rq, o + 4u);
+                        const float q10 = buffer_load(rq, o + 4u * V), q11 = buffer_load(rq, o + 4u * V + 4u);
+                        const float s0 = fmaf(av, q01 - q00, q00), s1 = fmaf(av, q11 - q10, q10);
+                        acc[r] = fmaf(wgt, fmaf(au, s1 - s0, s0), acc[r]);
+                        continue;
+                    }
+                    bool u0k = true, u1k = true, v0k = true, v1k = true;
+                    if (!fast) {
+                        u0k = (unsigned)iu < (unsigned)U;
+                        u1k = (unsigned)(iu + 1) < (unsigned)U;
+                        v0k = (unsigned)iv < (unsigned)V;
+                        v1k = (unsigned)(iv + 1) < (unsigned)V;
+                    }
+                    const float ku0 = u0k ? 1.f - au : 0.f, ku1 = u1k ? au : 0.f;
+                    const float kv0 = v0k ? 1.f - av : 0.f, kv1 = v1k ? av : 0.f;
+                    const int ju0 = u0k ? iu : 0, ju1 = u1k ? iu + 1 : 0;
+                    const int jv0 = v0k ? iv : 0, jv1 = v1k ? iv + 1 : 0;
+                    const size_t r0 = (vbase + ju0) * V, r1 = (vbase + ju1) * V;
+                    if (TRANSPOSE) {
+                        const float g = wgt * fz[r];
+                        if (g != 0.f) {
+                            if (ku0 * kv0 != 0.f) atomicAdd(a.sino_out + r0 + jv0, g * ku0 * kv0);
+                            if (ku0 * kv1 != 0.f) atomicAdd(a.sino_out + r0 + jv1, g * ku0 * kv1);
+                            if (ku1 * kv0 != 0.f) atomicAdd(a.sino_out + r1 + jv0, g * ku1 * kv0);
+                            if (ku1 * kv1 != 0.f) atomicAdd(a.sino_out + r1 + jv1, g * ku1 * kv1);
+                        }
+                    } else {
+                        const uint32_t o0 = (uint32_t)ju0 * V * 4u, o1 = (uint32_t)ju1 * V * 4u;
+                        const float q00 = buffer_load(rq, o0 + jv0 * 4u), q01 = buffer_load(rq, o0 + jv1 * 4u);
+                        const float q10 = buffer_load(rq, o1 + jv0 * 4u), q11 = buffer_load(rq, o1 + jv1 * 4u);
+                        const float s0 = fmaf(kv0, q00, kv1 * q01), s1 = fmaf(kv0, q10, kv1 * q11);
+                        acc[r] = fmaf(wgt, fmaf(ku0, s0, ku1 * s1), acc[r]);
+                    }
                 }
             }
         }
     }
-    if (!TRANSPOSE && inside) a.vol[vidx] = acc;
+    if (!TRANSPOSE) {
+#pragma unroll
+        for (int r = 0; r < ZR; ++r)
+            if (col_in && iz0 + 16 * r < a.D) a.vol[vidx0 + (size_t)(16 * r) * plane] = acc[r];
+    }
 }
 
 __global__ void fbp_zero_kernel(float *p, size_t n) {
@@ -743,7 +829,7 @@ static BpArgs bp_args(ct_fbp_t f) {
     a.V = (int)h.V;
     a.n_views = (int)h.n_views;
     a.two_d = h.is2d ? 1 : 0;
-    const int TX = h.is2d ? 16 : 4, TY = h.is2d ? 16 : 4, TZ = h.is2d ? 1 : 16;
+    const int TX = h.is2d ? 16 : 4, TY = h.is2d ? 16 : 4, TZ = h.is2d ? 1 : 16 * kZRun;
     a.nbx = (a.W + TX - 1) / TX;
     a.nby = (a.H + TY - 1) / TY;
     a.nbz = (a.D + TZ - 1) / TZ;
@@ -765,8 +851,8 @@ ct_status_t ct_fbp_backproject(ct_fbp_t f, const float *filtered, float *vol, ct
     a.q = filtered;
     a.vol = vol;
     const dim3 grid((unsigned)(a.nbx * a.nby * a.nbz));
-    if (h.is2d) hipLaunchKernelGGL((fbp_bp_kernel<false, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
-    else hipLaunchKernelGGL((fbp_bp_kernel<false, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    if (h.is2d) hipLaunchKernelGGL((fbp_bp_kernel<false, true, 1>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    else hipLaunchKernelGGL((fbp_bp_kernel<false, false, kZRun>), grid, dim3(256), 0, (hipStream_t)stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fhip(e, "ct_fbp_backproject launch");
     set_error("");
@@ -786,8 +872,8 @@ ct_status_t ct_fbp_backproject_transpose(ct_fbp_t f, const float *vol, float *si
     a.vol = const_cast<float *>(vol);   // read only in the transpose
     a.sino_out = sino;
     const dim3 grid((unsigned)(a.nbx * a.nby * a.nbz));
-    if (h.is2d) hipLaunchKernelGGL((fbp_bp_kernel<true, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
-    else hipLaunchKernelGGL((fbp_bp_kernel<true, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    if (h.is2d) hipLaunchKernelGGL((fbp_bp_kernel<true, true, 1>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    else hipLaunchKernelGGL((fbp_bp_kernel<true, false, kZRun>), grid, dim3(256), 0, (hipStream_t)stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fhip(e, "ct_fbp_backproject_transpose launch");
     set_error("");
