@@ -23,6 +23,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -34,8 +35,8 @@ using namespace ctp;
 namespace {
 
 constexpr uint64_t kFbpMagic = 0x43544642'50303031ull;   // "CTFBP001"
-constexpr int kBpViews = 256;      // views whose constants one LDS batch holds
-constexpr int kBpConst = 16;       // floats per view in that batch
+constexpr int kBpViews = 128;      // views whose constants one LDS batch holds
+constexpr int kBpConst = 40;       // floats per view in that batch
 constexpr int kZRun = 4;           // 3D backprojection: voxels per thread along z
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const float *p, uint32_t bytes) {
@@ -179,6 +180,129 @@ __global__ __launch_bounds__(256) void fbp_filter_kernel(FilterArgs a) {
     }
 }
 
+// The same filter through FFTs, for power-of-two P <= 4096: the circular
+// convolution with the P-periodic kernel is the inverse DFT of the product of
+// the DFT and the multiplier.  Two real rows travel as the real and imaginary
+// parts of one complex row (the multiplier is real and even, so each part is
+// filtered on its own).  A block holds NPAIR complex rows in LDS: a radix-2
+// decimation-in-time transform in place (bit-reversed input, written so by the
+// load), the multiplier, then a radix-2 decimation-in-frequency inverse in
+// place (natural input, bit-reversed output, read so by the store).
+struct FftArgs {
+    const float *sino;
+    float *out;
+    const float2 *tw;      // exp(-2 pi i t / P), t < P / 2
+    const float *mul;      // multiplier M_k, k = 0..P/2
+    const float *fview;
+    const float *parker;
+    int U, V, n_views, P, L, npair;
+    int two_d;
+};
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+
+__global__ __launch_bounds__(256) void fbp_fft_filter_kernel(FftArgs a) {
+    extern __shared__ float2 sh[];
+    const int P = a.P, L = a.L, NP = a.npair, C = 2 * NP, U = a.U, V = a.V;
+    float2 *x = sh;                   // NP rows of P complex
+    float2 *tw = sh + NP * P;         // P / 2
+    float *mul = (float *)(tw + P / 2);   // P / 2 + 1
+    int view0, v0;
+    if (a.two_d) {
+        view0 = blockIdx.x * C;
+        v0 = 0;
+    } else {
+        const int nvt = (V + C - 1) / C;
+        view0 = blockIdx.x / nvt;
+        v0 = (blockIdx.x % nvt) * C;
+    }
+    for (int i = threadIdx.x; i < P / 2; i += 256) tw[i] = a.tw[i];
+    for (int i = threadIdx.x; i <= P / 2; i += 256) mul[i] = a.mul[i];
+    float *xf = (float *)x;
+    for (int i = threadIdx.x; i < C * P; i += 256) {
+        int c, u;
+        if (a.two_d) {
+            c = i / P;
+            u = i - c * P;
+        } else {
+            u = i / C;
+            c = i - u * C;
+        }
+        const int view = a.two_d ? view0 + c : view0;
+        const int v = a.two_d ? 0 : v0 + c;
+        float val = 0.f;
+        if (u < U && view < a.n_views && v < V) {
+            const float *fv = a.fview + (size_t)view * kFv;
+            val = a.sino[((size_t)view * U + u) * V + v];
+            if (fv[11] != 0.f) {
+                const float ou = (float)u - 0.5f * (float)(U - 1);
+                const float ov = a.two_d ? 0.f : (float)v - 0.5f * (float)(V - 1);
+                const float px = fv[1] + ou * fv[4] + ov * fv[7];
+                const float py = fv[2] + ou * fv[5] + ov * fv[8];
+                const float pz = fv[3] + ou * fv[6] + ov * fv[9];
+                val *= fabsf(fv[0]) / sqrtf(px * px + py * py + pz * pz);
+            }
+            if (a.parker) val *= a.parker[(size_t)view * U + u];
+        }
+        const int br = (int)(__builtin_bitreverse32((uint32_t)u) >> (32 - L));
+        xf[2 * ((c >> 1) * P + br) + (c & 1)] = val;
+    }
+    __syncthreads();
+    const int nbf = NP * (P / 2);
+    for (int st = 1; st <= L; ++st) {   // forward, decimation in time
+        const int half = 1 << (st - 1);
+        for (int b = threadIdx.x; b < nbf; b += 256) {
+            const int pr = b >> (L - 1), bb = b & (P / 2 - 1);
+            const int j = bb & (half - 1);
+            const int i0 = pr * P + ((bb >> (st - 1)) << st) + j, i1 = i0 + half;
+            const float2 t = cmul(tw[j << (L - st)], x[i1]);
+            const float2 u0 = x[i0];
+            x[i0] = make_float2(u0.x + t.x, u0.y + t.y);
+            x[i1] = make_float2(u0.x - t.x, u0.y - t.y);
+        }
+        __syncthreads();
+    }
+    for (int i = threadIdx.x; i < NP * P; i += 256) {
+        const int k = i & (P - 1);
+        const float m = mul[k <= P / 2 ? k : P - k];
+        x[i] = make_float2(x[i].x * m, x[i].y * m);
+    }
+    __syncthreads();
+    for (int st = L; st >= 1; --st) {   // inverse, decimation in frequency
+        const int half = 1 << (st - 1);
+        for (int b = threadIdx.x; b < nbf; b += 256) {
+            const int pr = b >> (L - 1), bb = b & (P / 2 - 1);
+            const int j = bb & (half - 1);
+            const int i0 = pr * P + ((bb >> (st - 1)) << st) + j, i1 = i0 + half;
+            const float2 p0 = x[i0], p1 = x[i1];
+            const float2 w = tw[j << (L - st)];
+            x[i0] = make_float2(p0.x + p1.x, p0.y + p1.y);
+            x[i1] = cmul(make_float2(p0.x - p1.x, p0.y - p1.y), make_float2(w.x, -w.y));
+        }
+        __syncthreads();
+    }
+    const float inv = 1.0f / (float)P;
+    for (int i = threadIdx.x; i < C * P; i += 256) {
+        int c, u;
+        if (a.two_d) {
+            c = i / P;
+            u = i - c * P;
+        } else {
+            u = i / C;
+            c = i - u * C;
+        }
+        const int view = a.two_d ? view0 + c : view0;
+        const int v = a.two_d ? 0 : v0 + c;
+        if (u < U && view < a.n_views && v < V) {
+            const int br = (int)(__builtin_bitreverse32((uint32_t)u) >> (32 - L));
+            a.out[((size_t)view * U + u) * V + v] =
+                a.fview[(size_t)view * kFv + 10] * inv * xf[2 * ((c >> 1) * P + br) + (c & 1)];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // weighted backprojection B (gather) and its transpose (scatter)
 // ---------------------------------------------------------------------------
@@ -198,68 +322,81 @@ struct BpArgs {
     int two_d;
 };
 
-// Block-relative constants of one view: with the tile anchor X0 and integer
-// detector anchors u0, v0 (the projection of X0, rounded down),
-//   w  = Aw + Bw . d,   u - u0 = (Au + Bu . d) / w,   v - v0 = (Av + Bv . d) / w
-// for d = X - X0 in index units; the anchors keep the float32 arithmetic on
-// small numbers.  c[15] = 1 when the whole tile (half extents hx, hy, hz about
-// X0) lies in front of the source and projects strictly inside the detector,
-// so that every bilinear tap exists: the projection of a box is inside the
-// hull of its corners' projections.
-__device__ __forceinline__ void view_consts(const double *p, double x0, double y0, double z0, double hx,
-                                            double hy, double hz, int U, int V, bool two_d, float *c) {
-    const double uh = p[0] * x0 + p[1] * y0 + p[2] * z0 + p[3];
-    const double vh = p[4] * x0 + p[5] * y0 + p[6] * z0 + p[7];
-    const double wh = p[8] * x0 + p[9] * y0 + p[10] * z0 + p[11];
-    const double u0 = wh > 0.0 ? floor(uh / wh) : 0.0;
-    const double v0 = wh > 0.0 ? floor(vh / wh) : 0.0;
-    c[0] = (float)(uh - u0 * wh);
-    c[1] = (float)(p[0] - u0 * p[8]);
-    c[2] = (float)(p[1] - u0 * p[9]);
-    c[3] = (float)(p[2] - u0 * p[10]);
-    c[4] = (float)(vh - v0 * wh);
-    c[5] = (float)(p[4] - v0 * p[8]);
-    c[6] = (float)(p[5] - v0 * p[9]);
-    c[7] = (float)(p[6] - v0 * p[10]);
-    c[8] = (float)wh;
-    c[9] = (float)p[8];
-    c[10] = (float)p[9];
-    c[11] = (float)p[10];
-    c[12] = (float)p[12];
-    c[13] = (float)fmin(fmax(u0, -1e9), 1e9);
-    c[14] = (float)fmin(fmax(v0, -1e9), 1e9);
-    // corners, in float32 on the block-relative constants (errors ~1e-4 bin,
-    // far inside the margin)
-    bool in = wh > 0.0;
-    const float m = 0.01f;
-    const float ulo = m - c[13], uhi = (float)(U - 1) - m - c[13];
-    const float vlo = m - c[14], vhi = (float)(V - 1) - m - c[14];
+// Block-relative constants of one view, for a tile of ZR sub-blocks stacked
+// along z (sub-block r centred at X_r = (x0, y0, zc0 + 16 r)).  For a voxel at
+// X_r + d (d the same offset in every sub-block):
+//   w = Aw_r + Pw . d,   u - u0_r = (Au_r + Pu . d - u0_r Pw . d) / w,   v likewise
+// with the integer anchors u0_r, v0_r (the projection of X_r, rounded down)
+// and Au_r = u_h(X_r) - u0_r w_h(X_r), computed in float64: the float32
+// arithmetic then only meets numbers of the size of a sub-block's footprint.
+// Layout: Pu(3) Pv(3) Pw(3) 1 fast 0 | Au[4] | Av[4] | Aw[4] | u0[4] | v0[4]
+// | u0[4] | v0[4] (the last two as int bits).  Every P and A is scaled by
+// 1 / sqrt(K), which leaves u and v unchanged and makes the weight K / w^2
+// the square of the reciprocal of the scaled w.
+// fast = 1 when the whole tile (half extents hx, hy, hz about its centre
+// (x0, y0, zt)) lies in front of the source and projects strictly inside the
+// detector, so every bilinear tap exists: the projection of a box lies inside
+// the hull of its corners' projections.
+template <int ZR>
+__device__ __forceinline__ void view_consts(const double *p, double x0, double y0, double zc0, double zt,
+                                            double hx, double hy, double hz, int U, int V, bool two_d,
+                                            float *c) {
+    const double sk = 1.0 / sqrt(p[12]);   // K > 0 (checked when the plan is made)
+    for (int k = 0; k < 3; ++k) {
+        c[k] = (float)(sk * p[k]);
+        c[3 + k] = (float)(sk * p[4 + k]);
+        c[6 + k] = (float)(sk * p[8 + k]);
+    }
+    c[9] = 1.f;
+    c[11] = 0.f;
+#pragma unroll 1
+    for (int r = 0; r < 4; ++r) {
+        const double z = zc0 + 16.0 * (r < ZR ? r : 0);
+        const double uh = p[0] * x0 + p[1] * y0 + p[2] * z + p[3];
+        const double vh = p[4] * x0 + p[5] * y0 + p[6] * z + p[7];
+        const double wh = p[8] * x0 + p[9] * y0 + p[10] * z + p[11];
+        const double u0 = wh > 0.0 ? fmin(fmax(floor(uh / wh), -1e9), 1e9) : 0.0;
+        const double v0 = wh > 0.0 ? fmin(fmax(floor(vh / wh), -1e9), 1e9) : 0.0;
+        c[12 + r] = (float)(sk * (uh - u0 * wh));
+        c[16 + r] = (float)(sk * (vh - v0 * wh));
+        c[20 + r] = (float)(sk * wh);
+        c[24 + r] = (float)u0;
+        c[28 + r] = (float)v0;
+        c[32 + r] = __int_as_float((int)u0);
+        c[36 + r] = __int_as_float((int)v0);
+    }
+    bool in = true;
+#pragma unroll 1
     for (int k = 0; k < 8 && in; ++k) {
-        const float X = (k & 1) ? (float)hx : -(float)hx, Y = (k & 2) ? (float)hy : -(float)hy,
-                    Z = (k & 4) ? (float)hz : -(float)hz;
-        const float w = c[8] + c[9] * X + c[10] * Y + c[11] * Z;
+        const double X = x0 + ((k & 1) ? hx : -hx), Y = y0 + ((k & 2) ? hy : -hy), Z = zt + ((k & 4) ? hz : -hz);
+        const float w = (float)(p[8] * X + p[9] * Y + p[10] * Z + p[11]);
         if (!(w > 0.f)) {
             in = false;
             break;
         }
-        const float u = (c[0] + c[1] * X + c[2] * Y + c[3] * Z) / w;
-        const float v = (c[4] + c[5] * X + c[6] * Y + c[7] * Z) / w;
-        in = u >= ulo && u <= uhi && (two_d || (v >= vlo && v <= vhi));
+        // float32 corners (errors ~1e-4 bin, far inside the 0.01 margin)
+        const float u = (float)(p[0] * X + p[1] * Y + p[2] * Z + p[3]) / w;
+        const float v = (float)(p[4] * X + p[5] * Y + p[6] * Z + p[7]) / w;
+        in = u >= 0.01f && u <= (float)(U - 1) - 0.01f &&
+             (two_d || (v >= 0.01f && v <= (float)(V - 1) - 0.01f));
     }
-    c[15] = in ? 1.f : 0.f;
+    c[10] = in ? 1.f : 0.f;
 }
 
 // One thread takes ZR voxels of a z column, 16 planes apart (the 16 lanes of
 // a row of the wave hold 16 consecutive planes, which for the usual cone
-// geometries land on neighbouring detector rows), and walks them with the
-// affine increments of w, u_h, v_h.  Views are taken in LDS batches of
-// kBpViews whose block-relative constants the first kBpViews threads compute
-// in float64.
+// geometries land on neighbouring detector rows).  Views are taken in LDS
+// batches of kBpViews whose block-relative constants the first kBpViews
+// threads compute.
 template <bool TRANSPOSE, bool TWO_D, int ZR>
 __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
     __shared__ float cst[kBpViews * kBpConst];
     // tile: 3D 4 x 4 x (16 ZR) voxels (x, y, z); 2D 16 x 16
     constexpr int TX = TWO_D ? 16 : 4, TY = TWO_D ? 16 : 4, TZ = TWO_D ? 1 : 16 * ZR;
+    // Tiles in launch order (x fastest): the blocks resident at one time, on
+    // every XCD, cover one band of z and so read the same detector rows per
+    // view.  (Giving each XCD a contiguous range of tiles instead spreads the
+    // XCDs over eight bands of z and measured 27% slower at 512^3.)
     const int b = blockIdx.x;
     const int bx = b % a.nbx, by = (b / a.nbx) % a.nby, bz = b / (a.nbx * a.nby);
     int lx, ly, lz;
@@ -274,9 +411,11 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
     }
     const int ix = bx * TX + lx, iy = by * TY + ly, iz0 = bz * TZ + lz;
     const bool col_in = ix < a.W && iy < a.H && iz0 < a.D;
-    const double X0 = bx * TX + 0.5 * (TX - 1), Y0 = by * TY + 0.5 * (TY - 1), Z0 = bz * TZ + 0.5 * (TZ - 1);
+    const double X0 = bx * TX + 0.5 * (TX - 1), Y0 = by * TY + 0.5 * (TY - 1);
+    const double ZC0 = bz * TZ + (TWO_D ? 0.0 : 7.5);          // centre of sub-block 0
+    const double ZT = bz * TZ + 0.5 * (TZ - 1);                // centre of the tile
     const float dx = (float)lx - 0.5f * (TX - 1), dy = (float)ly - 0.5f * (TY - 1),
-                dz = (float)lz - 0.5f * (TZ - 1);
+                dz = TWO_D ? 0.f : (float)lz - 7.5f;
     const size_t plane = (size_t)a.H * a.W;
     const size_t vidx0 = ((size_t)iz0 * a.H + iy) * a.W + ix;
     float fz[ZR], acc[ZR];
@@ -297,38 +436,65 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
         const int nvb = min(kBpViews, a.n_views - vb);
         __syncthreads();
         if ((int)threadIdx.x < nvb)
-            view_consts(a.bp + (size_t)(vb + threadIdx.x) * kBpv, X0, Y0, Z0, 0.5 * (TX - 1), 0.5 * (TY - 1),
-                        0.5 * (TZ - 1), U, V, TWO_D, cst + threadIdx.x * kBpConst);
+            view_consts<ZR>(a.bp + (size_t)(vb + threadIdx.x) * kBpv, X0, Y0, ZC0, ZT, 0.5 * (TX - 1),
+                            0.5 * (TY - 1), 0.5 * (TZ - 1), U, V, TWO_D, cst + threadIdx.x * kBpConst);
         __syncthreads();
         if (!any) continue;
         for (int k = 0; k < nvb; ++k) {
-            const float4 c0 = *(const float4 *)(cst + k * kBpConst);
-            const float4 c1 = *(const float4 *)(cst + k * kBpConst + 4);
-            const float4 c2 = *(const float4 *)(cst + k * kBpConst + 8);
-            const float4 c3 = *(const float4 *)(cst + k * kBpConst + 12);
+            const float *ck = cst + k * kBpConst;
+            const float4 c0 = *(const float4 *)(ck);        // Pu.x Pu.y Pu.z Pv.x
+            const float4 c1 = *(const float4 *)(ck + 4);    // Pv.y Pv.z Pw.x Pw.y
+            const float4 c2 = *(const float4 *)(ck + 8);    // Pw.z K fast 0
+            const float4 au4 = *(const float4 *)(ck + 12);
+            const float4 av4 = *(const float4 *)(ck + 16);
+            const float4 aw4 = *(const float4 *)(ck + 20);
+            const float4 u04 = *(const float4 *)(ck + 24);
+            const float4 v04 = *(const float4 *)(ck + 28);
+            const float Au[4] = {au4.x, au4.y, au4.z, au4.w}, Av[4] = {av4.x, av4.y, av4.z, av4.w};
+            const float Aw[4] = {aw4.x, aw4.y, aw4.z, aw4.w};
+            const float U0[4] = {u04.x, u04.y, u04.z, u04.w}, V0[4] = {v04.x, v04.y, v04.z, v04.w};
+            const float pud = fmaf(c0.z, dz, fmaf(c0.y, dy, c0.x * dx));
+            const float pvd = fmaf(c1.y, dz, fmaf(c1.x, dy, c0.w * dx));
+            const float pwd = fmaf(c2.x, dz, fmaf(c1.w, dy, c1.z * dx));
+            const float K = c2.y;   // 1: the weight is folded into the scaled w
+            // uniform over the block: a scalar branch
+            const bool fast = __builtin_amdgcn_readfirstlane(c2.z != 0.f ? 1 : 0) != 0;
             const size_t vbase = (size_t)(vb + k) * U;
             // this view's filtered sinogram, addressed with 32-bit offsets
             const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + vbase * V, (uint32_t)U * V * 4u);
-            const int u0 = (int)c3.y, v0 = (int)c3.z;
-            float w = fmaf(c2.w, dz, fmaf(c2.z, dy, fmaf(c2.y, dx, c2.x)));
-            float nu = fmaf(c0.w, dz, fmaf(c0.z, dy, fmaf(c0.y, dx, c0.x)));
-            float nv = fmaf(c1.w, dz, fmaf(c1.z, dy, fmaf(c1.y, dx, c1.x)));
-            const float sw = 16.f * c2.w, su_ = 16.f * c0.w, sv_ = 16.f * c1.w;
-            const bool fast = c3.w != 0.f;   // uniform over the block
+            if (!TWO_D && !TRANSPOSE && fast) {
+                // every voxel of the tile is in front of the source and every
+                // bilinear tap exists
+                const int4 iu4 = *(const int4 *)(ck + 32);
+                const int4 iv4 = *(const int4 *)(ck + 36);
+                const int IU[4] = {iu4.x, iu4.y, iu4.z, iu4.w}, IV[4] = {iv4.x, iv4.y, iv4.z, iv4.w};
+#pragma unroll
+                for (int r = 0; r < ZR; ++r) {
+                    const float rw = __builtin_amdgcn_rcpf(Aw[r] + pwd);
+                    const float su = fmaf(-U0[r], pwd, Au[r] + pud) * rw;
+                    const float sv = fmaf(-V0[r], pwd, Av[r] + pvd) * rw;
+                    const float flu = floorf(su), flv = floorf(sv);
+                    const float au = su - flu, av = sv - flv;
+                    // u, v < 2^20: 24-bit multiplies run at the full rate
+                    const uint32_t o =
+                        (__umul24((uint32_t)((int)flu + IU[r]), (uint32_t)V) + (uint32_t)((int)flv + IV[r])) * 4u;
+                    const float q00 = buffer_load(rq, o), q01 = buffer_load(rq, o + 4u);
+                    const float q10 = buffer_load(rq, o + 4u * V), q11 = buffer_load(rq, o + 4u * V + 4u);
+                    const float s0 = fmaf(av, q01 - q00, q00), s1 = fmaf(av, q11 - q10, q10);
+                    acc[r] = fmaf(rw * rw, fmaf(au, s1 - s0, s0), acc[r]);
+                }
+                continue;
+            }
 #pragma unroll
             for (int r = 0; r < ZR; ++r) {
-                if (r > 0) {
-                    w += sw;
-                    nu += su_;
-                    nv += sv_;
-                }
+                const float w = Aw[r] + pwd;
                 if (!fast && !(w > 0.f)) continue;   // at or behind the source
-                const float rw = 1.0f / w;
-                const float su = nu * rw;
+                const float rw = __builtin_amdgcn_rcpf(w);
+                const float su = fmaf(-U0[r], pwd, Au[r] + pud) * rw;
                 const float flu = floorf(su);
                 const float au = su - flu;
-                const int iu = (int)flu + u0;
-                const float wgt = c3.x * rw * rw;
+                const int iu = (int)flu + (int)U0[r];
+                const float wgt = K * rw * rw;
                 if (TWO_D) {
                     bool ok0 = true, ok1 = true;
                     if (!fast) {
@@ -346,19 +512,10 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
                         acc[r] = fmaf(wgt, fmaf(k0, q0, k1 * q1), acc[r]);
                     }
                 } else {
-                    const float sv = nv * rw;
+                    const float sv = fmaf(-V0[r], pwd, Av[r] + pvd) * rw;
                     const float flv = floorf(sv);
                     const float av = sv - flv;
-                    const int iv = (int)flv + v0;
-                    if (fast && !TRANSPOSE) {
-                        // every tap exists: plain bilinear interpolation
-                        const uint32_t o = ((uint32_t)iu * V + iv) * 4u;
-                        const float q00 = buffer_load(rq, o), q01 = buffer_load(rq, o + 4u);
-                        const float q10 = buffer_load(rq, o + 4u * V), q11 = buffer_load(rq, o + 4u * V + 4u);
-                        const float s0 = fmaf(av, q01 - q00, q00), s1 = fmaf(av, q11 - q10, q10);
-                        acc[r] = fmaf(wgt, fmaf(au, s1 - s0, s0), acc[r]);
-                        continue;
-                    }
+                    const int iv = (int)flv + (int)V0[r];
                     bool u0k = true, u1k = true, v0k = true, v1k = true;
                     if (!fast) {
                         u0k = (unsigned)iu < (unsigned)U;
@@ -505,6 +662,9 @@ struct ct_fbp_s {
     double iso[3] = {0, 0, 0};
     std::vector<double> ang;
     float *d_taps = nullptr;
+    int P = 0, L = 0, npair = 0;   // FFT filter: P a power of two <= 4096, else 0
+    float2 *d_tw = nullptr;
+    float *d_mul = nullptr;
     float *d_fview = nullptr;
     float *d_parker = nullptr;
     double *d_bp = nullptr;
@@ -514,6 +674,8 @@ namespace {
 
 void free_plan(ct_fbp_s *f) {
     if (f->d_taps) (void)hipFree(f->d_taps);
+    if (f->d_tw) (void)hipFree(f->d_tw);
+    if (f->d_mul) (void)hipFree(f->d_mul);
     if (f->d_fview) (void)hipFree(f->d_fview);
     if (f->d_parker) (void)hipFree(f->d_parker);
     if (f->d_bp) (void)hipFree(f->d_bp);
@@ -521,6 +683,12 @@ void free_plan(ct_fbp_s *f) {
 }
 
 bool valid_plan(ct_fbp_t f) { return f && f->magic == kFbpMagic; }
+
+// CTPROJ_FBP_DIRECT=1 keeps the filter on the direct convolution (for comparisons).
+bool fft_disabled() {
+    const char *e = std::getenv("CTPROJ_FBP_DIRECT");
+    return e && e[0] == '1';
+}
 
 ct_status_t plan_device(ct_fbp_t f) {
     int cur = -1;
@@ -679,7 +847,22 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     // rows per block: at most four tasks of 8 outputs per thread, LDS under 64 KB
     f->VT = f->U8 <= 512 ? 16 : (f->U8 <= 1024 ? 8 : (f->U8 <= 2048 ? 2 : 1));
     f->S = f->U8 + 4;
-    const std::vector<float> taps = filter_taps(P, f->U8, multiplier(P, h.du, opts->window));
+    const std::vector<double> mult = multiplier(P, h.du, opts->window);
+    const std::vector<float> taps = filter_taps(P, f->U8, mult);
+    // FFT path: P a power of two in [64, 4096]
+    std::vector<float2> twf;
+    std::vector<float> mulf;
+    if ((P & (P - 1)) == 0 && P >= 64 && P <= 4096) {
+        f->P = P;
+        f->L = 0;
+        while ((1 << f->L) < P) ++f->L;
+        f->npair = std::max(1, std::min(8, 4096 / P));
+        twf.resize(P / 2);
+        for (int t = 0; t < P / 2; ++t)
+            twf[t] = make_float2((float)std::cos(2.0 * M_PI * t / P), (float)-std::sin(2.0 * M_PI * t / P));
+        mulf.resize(P / 2 + 1);
+        for (int k = 0; k <= P / 2; ++k) mulf[k] = (float)mult[k];
+    }
     std::vector<float> fview((size_t)nv * kFv, 0.f);
     std::vector<double> bp((size_t)nv * kBpv, 0.0);
     // voxel centre of index (i, j, k): lo + (idx + 0.5) s per axis; 2D: z = 0
@@ -695,6 +878,10 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
         double pu, pv, pw, K;
         if (persp) {
             const double D = dot(v.c - v.a, v.n), R = dot(iso - v.a, v.n);
+            if (!(R > 0.0)) {
+                delete f;
+                return ffail(CT_E_ARG, "the isocentre must lie in front of every source");
+            }
             const V3 ca = v.c - v.a;
             fv[0] = (float)D;
             fv[1] = (float)ca.x; fv[2] = (float)ca.y; fv[3] = (float)ca.z;
@@ -744,6 +931,8 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     if (e == hipSuccess) e = hipMalloc((void **)&f->d_fview, fview.size() * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void **)&f->d_bp, bp.size() * sizeof(double));
     if (e == hipSuccess && !parker.empty()) e = hipMalloc((void **)&f->d_parker, parker.size() * sizeof(float));
+    if (e == hipSuccess && f->P) e = hipMalloc((void **)&f->d_tw, twf.size() * sizeof(float2));
+    if (e == hipSuccess && f->P) e = hipMalloc((void **)&f->d_mul, mulf.size() * sizeof(float));
     if (e != hipSuccess) {
         (void)hipGetLastError();
         free_plan(f);
@@ -754,6 +943,8 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     if (e == hipSuccess) e = hipMemcpy(f->d_bp, bp.data(), bp.size() * sizeof(double), hipMemcpyHostToDevice);
     if (e == hipSuccess && !parker.empty())
         e = hipMemcpy(f->d_parker, parker.data(), parker.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess && f->P) e = hipMemcpy(f->d_tw, twf.data(), twf.size() * sizeof(float2), hipMemcpyHostToDevice);
+    if (e == hipSuccess && f->P) e = hipMemcpy(f->d_mul, mulf.data(), mulf.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         free_plan(f);
         return fhip(e, "upload of the FBP tables");
@@ -795,6 +986,32 @@ ct_status_t ct_fbp_filter(ct_fbp_t f, const float *sino, float *filtered, ct_str
     if (overlaps(sino, sb, filtered, sb)) return ffail(CT_E_ALIAS, "filtered overlaps sino");
     ct_status_t st = plan_device(f);
     if (st != CT_OK) return st;
+    if (f->P && !fft_disabled()) {
+        FftArgs b;
+        b.sino = sino;
+        b.out = filtered;
+        b.tw = f->d_tw;
+        b.mul = f->d_mul;
+        b.fview = f->d_fview;
+        b.parker = f->d_parker;
+        b.U = (int)h.U;
+        b.V = (int)h.V;
+        b.n_views = (int)h.n_views;
+        b.P = f->P;
+        b.L = f->L;
+        b.npair = f->npair;
+        b.two_d = h.is2d ? 1 : 0;
+        const int C = 2 * f->npair;
+        const unsigned blocks = h.is2d ? (unsigned)((h.n_views + C - 1) / C)
+                                       : (unsigned)(h.n_views * ((h.V + C - 1) / C));
+        const size_t lds = (size_t)f->npair * f->P * sizeof(float2) + (size_t)(f->P / 2) * sizeof(float2) +
+                           (size_t)(f->P / 2 + 1) * sizeof(float);
+        hipLaunchKernelGGL(fbp_fft_filter_kernel, dim3(blocks), dim3(256), lds, (hipStream_t)stream, b);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fhip(e, "ct_fbp_filter launch");
+        set_error("");
+        return CT_OK;
+    }
     FilterArgs a;
     a.sino = sino;
     a.out = filtered;

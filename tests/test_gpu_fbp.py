@@ -67,6 +67,10 @@ CASES = {
     "fan-short": short_fan,
     "cone": cone_wl,
     "cone-jittered-aniso": lambda: cone_wl(jitter=0.4, spacing=(1.2, 0.9, 1.0)),
+    # power-of-two padded rows take the FFT filter
+    "parallel-pow2": lambda: par_wl(U=64),
+    "fan-pow2": lambda: fan_wl(U=128),
+    "cone-pow2": lambda: cone_wl(det=(64, 37)),
 }
 
 
@@ -80,6 +84,8 @@ def plan(wl, th, **kw):
 def test_filter_matches_oracle(name, window, pad):
     wl, th = CASES[name]()
     short = name == "fan-short"
+    if "pow2" in name and pad == 3:
+        pad = 2
     f = plan(wl, th, window=window, pad_factor=pad, short_scan=short)
     iso, aw = f.info()
     assert np.allclose(iso, F.isocentre(wl), atol=1e-9)
@@ -141,6 +147,22 @@ def test_pipeline_matches_oracle(name):
     e = rel_l2(host(vol), ref)
     say(f"{name}: FBP/FDK rel_l2 {e:.2e}")
     assert e <= TOL
+
+
+@pytest.mark.parametrize("name", ["cone-pow2", "fan-pow2"])
+def test_fft_and_direct_filters_agree(name, monkeypatch):
+    wl, th = CASES[name]()
+    f = plan(wl, th, window="shepp-logan", pad_factor=2)
+    sino = dev(np.random.default_rng(6).uniform(0, 1, wl.sino_shape))
+    a = torch.empty(wl.sino_shape, device="cuda")
+    b = torch.empty(wl.sino_shape, device="cuda")
+    rdp.ct_fbp_filter(f, sino, a)
+    monkeypatch.setenv("CTPROJ_FBP_DIRECT", "1")
+    rdp.ct_fbp_filter(f, sino, b)
+    monkeypatch.delenv("CTPROJ_FBP_DIRECT")
+    e = rel_l2(host(a), host(b))
+    say(f"{name}: FFT vs direct filter {e:.2e}")
+    assert e <= 2e-6
 
 
 def test_given_isocentre_and_angular_weights():
