@@ -393,12 +393,20 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
     __shared__ float cst[kBpViews * kBpConst];
     // tile: 3D 4 x 4 x (16 ZR) voxels (x, y, z); 2D 16 x 16
     constexpr int TX = TWO_D ? 16 : 4, TY = TWO_D ? 16 : 4, TZ = TWO_D ? 1 : 16 * ZR;
-    // Tiles in launch order (x fastest): the blocks resident at one time, on
-    // every XCD, cover one band of z and so read the same detector rows per
-    // view.  (Giving each XCD a contiguous range of tiles instead spreads the
-    // XCDs over eight bands of z and measured 27% slower at 512^3.)
-    const int b = blockIdx.x;
-    const int bx = b % a.nbx, by = (b / a.nbx) % a.nby, bz = b / (a.nbx * a.nby);
+    // Tile order: z bands outermost, so the blocks resident at one time, on
+    // every XCD, read the same detector rows per view; within a band, squares
+    // of 8 x 8 tiles, so they also read a narrow range of detector columns
+    // (512^3 cone: 105 ms in plain order, 98 / 96 / 99 ms with squares of
+    // 16 / 8 / 4 tiles).
+    // (Giving each XCD a contiguous range of tiles instead spreads the XCDs over
+    // eight bands of z and measured 27% slower at 512^3.)
+    constexpr int ST = 8;
+    const int b = blockIdx.x, nxy = a.nbx * a.nby;
+    const int bz = b / nxy, rem = b - bz * nxy;
+    const int sy = rem / (ST * a.nbx), rows_in = min(ST, a.nby - sy * ST), r2 = rem - sy * ST * a.nbx;
+    const int sx = r2 / (ST * rows_in), cols_in = min(ST, a.nbx - sx * ST), r3 = r2 - sx * ST * rows_in;
+    const int ty = r3 / cols_in;
+    const int bx = sx * ST + (r3 - ty * cols_in), by = sy * ST + ty;
     int lx, ly, lz;
     if (TWO_D) {
         lx = threadIdx.x & 15;
