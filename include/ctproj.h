@@ -184,6 +184,27 @@ ct_status_t ct_backproject(ct_geom_t g, const float *sino, float *vol, ct_stream
  * documentation notes for its atomic adjoint in "Example results"). */
 ct_status_t ct_backproject_atomic(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream);
 
+/* ---- Ordered subsets (SART) ----
+ * The ASTRA guide lists SART with MinConstraint / MaxConstraint /
+ * ReconstructionMask.  Read here as ordered-subset SIRT: the views are taken in
+ * subsets [view_begin, view_end) one after another, and each subset applies the
+ * bounded, masked SIRT step of its own rays,
+ *   x <- clip(x + relax * C_s * A_s^T R_s (y_s - A_s x), lo, hi) where mask != 0,
+ * with R_s = 1 / (A_s 1) (the subset's rows of R) and C_s = 1 / (A_s^T 1) (0 where
+ * the sums are 0).  One view per subset is SART; the whole range is SIRT.
+ * ct_sirt_weights_views: row_inv_batch (view_end - view_begin, U, V) and
+ * col_inv (D, H, W) for the subset.  ct_sirt_step_views: y_batch, row_inv_batch
+ * and work_batch hold the subset's views; lo = -inf, hi = +inf and mask = NULL
+ * give the plain step.  Device buffers, asynchronous on stream.  Errors as for
+ * ct_sirt_step_bounded, plus CT_E_SHAPE for an empty or out-of-range view range
+ * (checked first). */
+ct_status_t ct_sirt_weights_views(ct_geom_t g, int64_t view_begin, int64_t view_end,
+                                  float *row_inv_batch, float *col_inv, ct_stream_t stream);
+ct_status_t ct_sirt_step_views(ct_geom_t g, int64_t view_begin, int64_t view_end, float *x,
+                               const float *y_batch, const float *row_inv_batch,
+                               const float *col_inv, float relax, float lo, float hi,
+                               const uint8_t *mask, float *work_batch, ct_stream_t stream);
+
 /* ---- Regions and view batches (chunked execution) ----
  * The diffct documentation ("Large Volumes and Chunked Execution" > "Resident
  * layouts and accumulation") splits large problems into volume tiles and view

@@ -33,7 +33,8 @@ EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_g
            "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_project_region",
            "ct_backproject_region", "ct_project_host", "ct_backproject_host",
            "ct_fbp_create", "ct_fbp_destroy", "ct_fbp_info", "ct_fbp_filter", "ct_fbp_backproject",
-           "ct_fbp_backproject_transpose", "ct_fbp_run", "ct_sirt_weights",
+           "ct_fbp_backproject_transpose", "ct_fbp_run", "ct_sirt_weights_views", "ct_sirt_step_views",
+           "ct_sirt_weights",
            "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_sirt_update_bounded",
            "ct_sirt_step_bounded", "ct_cgls_workspace_size",
            "ct_cgls_init", "ct_cgls_step", "ct_cgls_scalars", "ct_count_intersections",
@@ -101,6 +102,9 @@ def lib():
         L.ct_fbp_run.argtypes = [vp, vp, vp, vp, vp]
         L.ct_backproject_host.argtypes = [vp, vp, vp, StreamPlan, vp]
         L.ct_sirt_weights.argtypes = [vp, vp, vp, vp]
+        L.ct_sirt_weights_views.argtypes = [vp, c.c_int64, c.c_int64, vp, vp, vp]
+        L.ct_sirt_step_views.argtypes = [vp, c.c_int64, c.c_int64, vp, vp, vp, vp, c.c_float, c.c_float,
+                                         c.c_float, vp, vp, vp]
         L.ct_sirt_residual.argtypes = [vp, vp, vp, vp, vp, vp]
         L.ct_sirt_update.argtypes = [vp, vp, vp, c.c_float, vp, vp]
         L.ct_sirt_step.argtypes = [vp, vp, vp, vp, vp, c.c_float, vp, vp]
@@ -474,6 +478,29 @@ def ct_sirt_step_bounded(g: Geometry, x, y, row_inv, col_inv, relax, lo, hi, mas
                                       _ptr(col_inv, g.vol_shape, "col_inv"), float(relax), float(lo),
                                       float(hi), _mask_ptr(g, mask),
                                       _ptr(work_sino, g.sino_shape, "work_sino"), _stream(stream)))
+    return x
+
+
+def ct_sirt_weights_views(g: Geometry, view_begin, view_end, row_inv_batch, col_inv, stream=None):
+    """R and C of the views [view_begin, view_end) (one ordered subset)."""
+    vb, ve = int(view_begin), int(view_end)
+    bshape = (ve - vb,) + g.sino_shape[1:]
+    _check(lib().ct_sirt_weights_views(g.handle, vb, ve, _ptr(row_inv_batch, bshape, "row_inv_batch"),
+                                       _ptr(col_inv, g.vol_shape, "col_inv"), _stream(stream)))
+    return row_inv_batch, col_inv
+
+
+def ct_sirt_step_views(g: Geometry, view_begin, view_end, x, y_batch, row_inv_batch, col_inv, relax=1.0,
+                       lo=-float("inf"), hi=float("inf"), mask=None, work_batch=None, stream=None):
+    """One ordered-subset (SART) step on the views [view_begin, view_end)."""
+    vb, ve = int(view_begin), int(view_end)
+    bshape = (ve - vb,) + g.sino_shape[1:]
+    _check(lib().ct_sirt_step_views(g.handle, vb, ve, _ptr(x, g.vol_shape, "x"),
+                                    _ptr(y_batch, bshape, "y_batch"),
+                                    _ptr(row_inv_batch, bshape, "row_inv_batch"),
+                                    _ptr(col_inv, g.vol_shape, "col_inv"), float(relax), float(lo),
+                                    float(hi), _mask_ptr(g, mask), _ptr(work_batch, bshape, "work_batch"),
+                                    _stream(stream)))
     return x
 
 

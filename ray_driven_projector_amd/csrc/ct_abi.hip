@@ -645,6 +645,52 @@ ct_status_t ct_sirt_update_bounded(ct_geom_t g, const float *work_sino, const fl
                     "ct_sirt_update_bounded launch");
 }
 
+// ---- ordered subsets (SART): the SIRT weights and step on a range of views ----
+
+ct_status_t ct_sirt_weights_views(ct_geom_t g, int64_t view_begin, int64_t view_end, float *row_inv,
+                                  float *col_inv, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    const GeomHost &h = g->host;
+    const ct_region_t all{0, 0, 0, h.D, h.H, h.W};
+    ct_status_t st = check_region(g, all, view_begin, view_end);
+    if (st != CT_OK) return st;
+    if (!row_inv || !col_inv) return fail(CT_E_NULL, "row_inv and col_inv must be non-NULL");
+    const size_t sb = (size_t)(view_end - view_begin) * h.U * h.V * sizeof(float);
+    st = check_alias({{Span{row_inv, sb}, true}, {Span{col_inv, vol_bytes(g)}, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    const LaunchGeom l = lg_region(g, all, view_begin, view_end, false);
+    hipError_t e = launch_rowinv(l, row_inv, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ct_sirt_weights_views row launch");
+    return launched(launch_colinv(l, col_inv, (hipStream_t)stream), "ct_sirt_weights_views column launch");
+}
+
+ct_status_t ct_sirt_step_views(ct_geom_t g, int64_t view_begin, int64_t view_end, float *x, const float *y,
+                               const float *row_inv, const float *col_inv, float relax, float lo, float hi,
+                               const uint8_t *mask, float *work, ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    const GeomHost &h = g->host;
+    const ct_region_t all{0, 0, 0, h.D, h.H, h.W};
+    ct_status_t st = check_region(g, all, view_begin, view_end);
+    if (st != CT_OK) return st;
+    if (!x || !y || !row_inv || !col_inv || !work) return fail(CT_E_NULL, "a buffer pointer is NULL");
+    if (!std::isfinite(relax)) return fail(CT_E_ARG, "relax must be finite");
+    if (std::isnan(lo) || std::isnan(hi) || !(lo <= hi)) return fail(CT_E_ARG, "bounds must satisfy lo <= hi");
+    const size_t sb = (size_t)(view_end - view_begin) * h.U * h.V * sizeof(float);
+    const size_t nvox = vol_bytes(g) / sizeof(float);
+    Span X{x, vol_bytes(g)}, Y{y, sb}, R{row_inv, sb}, C{col_inv, vol_bytes(g)}, E{work, sb}, M{mask, nvox};
+    st = check_alias({{X, true}, {Y, false}, {R, false}, {C, false}, {E, true}});
+    if (st == CT_OK && mask) st = check_alias({{X, true}, {E, true}, {M, false}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    if ((st = ensure_layouts(g, full_voxels(g))) != CT_OK) return st;
+    const LaunchGeom l = lg_region(g, all, view_begin, view_end, false);
+    hipError_t e = launch_residual(l, x, y, row_inv, work, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ct_sirt_step_views residual launch");
+    return launched(launch_sirt_update_bounded(l, work, col_inv, relax, lo, hi, mask, x, (hipStream_t)stream),
+                    "ct_sirt_step_views update launch");
+}
+
 ct_status_t ct_sirt_step_bounded(ct_geom_t g, float *x, const float *y, const float *row_inv,
                                  const float *col_inv, float relax, float lo, float hi,
                                  const uint8_t *mask, float *work_sino, ct_stream_t stream) {

@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
             const float *ck = cst + k * kBpConst;
             const float4 c0 = *(const float4 *)(ck);        // Pu.x Pu.y Pu.z Pv.x
             const float4 c1 = *(const float4 *)(ck + 4);    // Pv.y Pv.z Pw.x Pw.y
-            const float4 c2 = *(const float4 *)(ck + 8);    // Pw.z K fast 0
+            const float4 c2 = *(const float4 *)(ck + 8);    // Pw.z 1 fast 0
             const float4 au4 = *(const float4 *)(ck + 12);
             const float4 av4 = *(const float4 *)(ck + 16);
             const float4 aw4 = *(const float4 *)(ck + 20);
@@ -464,7 +464,6 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
             const float pud = fmaf(c0.z, dz, fmaf(c0.y, dy, c0.x * dx));
             const float pvd = fmaf(c1.y, dz, fmaf(c1.x, dy, c0.w * dx));
             const float pwd = fmaf(c2.x, dz, fmaf(c1.w, dy, c1.z * dx));
-            const float K = c2.y;   // 1: the weight is folded into the scaled w
             // uniform over the block: a scalar branch
             const bool fast = __builtin_amdgcn_readfirstlane(c2.z != 0.f ? 1 : 0) != 0;
             const size_t vbase = (size_t)(vb + k) * U;
@@ -502,7 +501,7 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
                 const float flu = floorf(su);
                 const float au = su - flu;
                 const int iu = (int)flu + (int)U0[r];
-                const float wgt = K * rw * rw;
+                const float wgt = rw * rw;   // K / w^2: K is folded into the scaled w
                 if (TWO_D) {
                     bool ok0 = true, ok1 = true;
                     if (!fast) {
