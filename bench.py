@@ -24,7 +24,9 @@ acquisition (ct_fbp_filter: cosine weights, Ram-Lak ramp filter padded to 2U,
 angular weights; ct_fbp_backproject: the interpolating weighted
 backprojection) of y = A phantom; its value is voxel-view updates per second
 (512^3 voxels x 720 views per step), and both kernels are ALU-bound, so the
-roofline is against the fp32 vector peak.
+roofline is against the fp32 vector peak.  --workload c1 / c2 / c3 time A + A^T
+(dense seeded A^T input) on the small configurations (2D parallel 64^2, 2D fan
+512^2, helical cone 128^3), whose throughput is reported for completeness.
 
 Roofline: algorithmic HBM bytes of the dominant kernel per launch divided by
 its average duration (HIP events on the launch stream), against 8 TB/s.
@@ -126,7 +128,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["c4", "c5", "c4cgls", "c5cgls", "c5cyl", "c5fdk"], default="c4")
+    ap.add_argument("--workload", choices=["c1", "c2", "c3", "c4", "c5", "c4cgls", "c5cgls", "c5cyl", "c5fdk"],
+                    default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-views", type=int, default=16)
     ap.add_argument("--extra", action="store_true", help="also time A, A^T and atomic A^T alone")
@@ -159,7 +162,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cfg = 4 if args.workload.startswith("c4") else 5
+    cfg = int(args.workload[1])
     cgls = args.workload.endswith("cgls")
     wl = W.make_workload(cfg)
     if args.workload == "c5cyl":
@@ -240,8 +243,10 @@ def main():
         names = ("project", "backproject")
         bytes_per = {"project": 4 * nnz + 4 * M, "backproject": 4 * nnz + 4 * M + 4 * N}
         sf = "true" if wl.offsets is not None else "false"
-        kern_names = {"project": f"ray_kernel<0, false, {sf}>",
-                      "backproject": f"brick_kernel<16, 16, 32, 512, 0, {sf}>"}
+        two_d = wl.beam in (W.BEAM_PARALLEL2D, W.BEAM_FAN2D)
+        kern_names = {"project": f"ray_kernel<0, {'true' if two_d else 'false'}, {sf}>",
+                      "backproject": (f"brick_kernel<64, 64, 1, 256, 0, {sf}>" if two_d else
+                                      f"brick_kernel<16, 16, 32, 512, 0, {sf}>")}
 
         def step(evs):
             evs[0].record(stream)

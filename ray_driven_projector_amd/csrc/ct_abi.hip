@@ -40,6 +40,7 @@ struct ct_geom_s {
     unsigned long long *d_total = nullptr;  // device counter for ct_count_intersections
     int device = 0;
     int brick_shape = 5;                // adjoint bricks of 16 x 16 x 32
+    int brick2d = 2;                    // 2D adjoint bricks of 16 x 16
     int fwd_order = 5;                  // forward block order: 2 x 2 tile groups, views inside
     float *d_vol_yf = nullptr;          // y-fastest volume copy read by some views' gathers
     float *d_vol_zf = nullptr;          // z-fastest volume copy read by some views' gathers
@@ -88,6 +89,7 @@ LaunchGeom lg(ct_geom_t g) {
     l.spz = g->host.sz;
     l.two_d = g->host.is2d;
     l.brick_shape = g->brick_shape;
+    l.brick2d = g->brick2d;
     l.fwd_order = g->fwd_order;
     l.vol_yf = g->d_vol_yf;
     l.vol_zf = g->d_vol_zf;
@@ -165,6 +167,14 @@ ct_status_t check_alias(std::initializer_list<Arg> args) {
 // Defaults measured on 512^3 cone and parallel3d workloads: 16 x 16 x 32 bricks,
 // forward order 5 (groups of 2 x 2 pixel tiles, every view of a group in turn).
 void choose_tiles(ct_geom_s *g) {
+    // 2D: 16 x 16 bricks (C2, 512^2 fan, 360 views: A^T 1.17 ms with 64 x 64,
+    // 0.50 with 32 x 32, 0.44 with 16 x 16 -- small 2D volumes need many bricks
+    // to fill the chip); CTPROJ_BRICK2D (0..2) overrides
+    g->brick2d = 2;
+    if (const char *e = std::getenv("CTPROJ_BRICK2D")) {
+        const int v = std::atoi(e);
+        if (v >= 0 && v <= 2) g->brick2d = v;
+    }
     g->brick_shape = 5;
     if (const char *e = std::getenv("CTPROJ_BRICK")) {
         const int v = std::atoi(e);

@@ -1511,7 +1511,9 @@ static hipError_t launch_brick_args(const LaunchGeom &g, BrickArgs a, hipStream_
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
     if (g.two_d) {
-        launch_brick_shape<64, 64, 1, 256, MODE>(a, g, s);
+        if (g.brick2d == 1) launch_brick_shape<32, 32, 1, 256, MODE>(a, g, s);
+        else if (g.brick2d == 2) launch_brick_shape<16, 16, 1, 256, MODE>(a, g, s);
+        else launch_brick_shape<64, 64, 1, 256, MODE>(a, g, s);
     } else if (g.brick_shape == 1) {
         launch_brick_shape<32, 32, 16, 1024, MODE>(a, g, s);
     } else if (g.brick_shape == 2) {
@@ -1584,7 +1586,7 @@ size_t cgls_ray_blocks(const LaunchGeom &g) { return (size_t)ray_args(g).n_block
 
 size_t cgls_brick_blocks(const LaunchGeom &g) {
     int bx = 16, by = 16, bz = 16;
-    if (g.two_d) { bx = 64; by = 64; bz = 1; }
+    if (g.two_d) { bx = by = g.brick2d == 1 ? 32 : (g.brick2d == 2 ? 16 : 64); bz = 1; }
     else if (g.brick_shape == 1) { bx = 32; by = 32; bz = 16; }
     else if (g.brick_shape == 2) { bx = 32; by = 16; bz = 16; }
     else if (g.brick_shape == 3) { bx = 32; by = 16; bz = 32; }
