@@ -156,12 +156,23 @@ def main():
         from ray_driven_projector_amd import build as b
         b.build()
     torch.cuda.set_device(0)
-    if args.copy_calibration:
-        src = torch.ones(1 << 28, device="cuda")
-        dst = torch.empty_like(src)
+    # the box's device-copy bandwidth (1 GiB read + 1 GiB written), the second
+    # yardstick for the roofline fraction; with --copy-calibration it is also
+    # the reference kernel for the HBM counters
+    src = torch.ones(1 << 28, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    copy_ms = []
+    for _ in range(1 if args.copy_calibration else 5):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
         dst.copy_(src)
+        c1.record()
         torch.cuda.synchronize()
-        del src, dst
+        copy_ms.append(c0.elapsed_time(c1))
+    copy_bw = 2 * (1 << 30) / (float(np.median(copy_ms)) * 1e-3)
+    del src, dst
     cfg = int(args.workload[1])
     cgls = args.workload.endswith("cgls")
     wl = W.make_workload(cfg)
@@ -335,6 +346,7 @@ def main():
             "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
             "traffic": _traffic(dom, args.workload),
             "algorithmic_bytes_per_launch": bytes_per[dom],
+            "copy_bw": round(copy_bw / 1e9, 1), "frac_vs_copy": round(achieved / copy_bw, 4),
         }),
     }
     res.update(extra)
