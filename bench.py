@@ -142,8 +142,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py: this build targets one GPU; the multi-GPU sharding of the path is "
-              "described in DESIGN.md and not run. Use --gpus 1.", file=sys.stderr)
+        print("bench.py: runs on one GPU; several GPUs (views or space sharding) are not "
+              "implemented. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

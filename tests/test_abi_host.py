@@ -131,6 +131,63 @@ def test_compute_calls_reject_bad_handles_before_any_launch(L):
     assert L.ct_count_intersections(None, nul, ctypes.byref(total), None) == rdp.CT_E_ARG
     assert L.ct_geom_destroy(None) == rdp.CT_OK
     assert L.ct_geom_create(None, None) == rdp.CT_E_NULL
+    r = rdp.Region(0, 0, 0, 1, 1, 1)
+    assert L.ct_project_region(None, one, r, 0, 1, one, 0, None) == rdp.CT_E_ARG
+    assert L.ct_backproject_region(None, one, 0, 1, r, one, 0, None) == rdp.CT_E_ARG
+    plan = rdp.StreamPlan(1, 1, -1, 0)
+    assert L.ct_project_host(None, one, one, plan, None) == rdp.CT_E_ARG
+    assert L.ct_backproject_host(None, one, one, plan, None) == rdp.CT_E_ARG
+    assert L.ct_sirt_weights_views(None, 0, 1, one, one, None) == rdp.CT_E_ARG
+    assert L.ct_sirt_step_views(None, 0, 1, one, one, one, one, 1.0, 0.0, 1.0, None, one, None) == rdp.CT_E_ARG
+    assert L.ct_fbp_filter(None, one, one, None) == rdp.CT_E_ARG
+    assert L.ct_fbp_backproject(None, one, one, None) == rdp.CT_E_ARG
+    assert L.ct_fbp_backproject_transpose(None, one, one, None) == rdp.CT_E_ARG
+    assert L.ct_fbp_run(None, one, one, one, None) == rdp.CT_E_ARG
+    assert L.ct_fbp_info(None, None, None) == rdp.CT_E_ARG
+    assert L.ct_fbp_destroy(None) == rdp.CT_OK
+
+
+def test_fbp_plan_arguments_are_checked_on_the_host(L):
+    """ct_fbp_create rejects bad options before it touches the device."""
+    import math
+    cone = W.make_workload(3, scale=8, n_views=12)
+    d, fr = rdp.make_desc(*_args(cone))
+    th = np.ascontiguousarray(W.angles(12, 2 * math.pi))
+    dp = ctypes.POINTER(ctypes.c_double)
+    out = ctypes.c_void_p()
+
+    def create(desc=d, angles=th, **kw):
+        o = rdp.FbpOpts()
+        o.window, o.pad_factor, o.short_scan, o.iso_given, o.reserved = 0, 2, 0, 0, 0
+        for k, v in kw.items():
+            setattr(o, k, v)
+        a = angles.ctypes.data_as(dp) if angles is not None else None
+        return L.ct_fbp_create(ctypes.byref(desc), a, None, ctypes.byref(o), ctypes.byref(out))
+
+    assert create(window=5) == rdp.CT_E_ARG
+    assert create(pad_factor=0) == rdp.CT_E_ARG
+    assert create(pad_factor=17) == rdp.CT_E_ARG
+    assert create(reserved=1) == rdp.CT_E_ARG
+    assert create(angles=None) == rdp.CT_E_NULL
+    bad = th.copy()
+    bad[2] = math.inf
+    assert create(angles=bad) == rdp.CT_E_NONFINITE
+    p3 = W.make_workload(4, scale=32, n_views=4)
+    d3, fr3 = rdp.make_desc(*_args(p3))
+    assert create(desc=d3, angles=np.ascontiguousarray(th[:4])) == rdp.CT_E_ARG   # parallel3d
+    par = W.make_workload(1, scale=2)
+    dp2, fr2 = rdp.make_desc(*_args(par))
+    assert create(desc=dp2, angles=np.ascontiguousarray(W.angles(90, math.pi)), short_scan=1) == rdp.CT_E_ARG
+    assert L.ct_fbp_create(ctypes.byref(d), th.ctypes.data_as(dp), None, None, ctypes.byref(out)) == rdp.CT_E_NULL
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
 
 
 def _pixel(frames, k, u, v, U, V, du, dv, is2d):
