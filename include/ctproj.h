@@ -331,6 +331,11 @@ typedef struct {
  * tables in float64, and uploads them.  angles: HOST, n_views radians (needed
  * unless angular_weights is given, and always for short scans);
  * angular_weights: HOST, n_views, or NULL for the rule above.
+ * A cone-beam plan also owns device staging for the backprojection: the
+ * filtered sinogram of one batch of nb <= 128 views in pair-interleaved form
+ * (8 nb U V bytes; the views are split into equal batches).  Backprojections
+ * with one plan therefore share it: calls of ct_fbp_backproject or ct_fbp_run
+ * with the same plan on different streams must not overlap in time.
  * Errors: CT_E_NULL, CT_E_ARG (beam, window, pad, short scan on parallel, a
  * span too short, an isocentre that cannot be estimated), CT_E_SHAPE,
  * CT_E_RANGE, CT_E_NONFINITE, CT_E_NOMEM, CT_E_HIP. */
@@ -342,7 +347,10 @@ ct_status_t ct_fbp_info(ct_fbp_t f, double *iso, double *angular_weights);
 
 /* filtered = steps 1-3 of sino; (views, U, V) device buffers that must not overlap. */
 ct_status_t ct_fbp_filter(ct_fbp_t f, const float *sino, float *filtered, ct_stream_t stream);
-/* vol = step 4 of filtered (overwrites every voxel). */
+/* vol = step 4 of filtered (overwrites every voxel).  Cone: per batch of views,
+ * the plan's staging receives the batch pair-interleaved, (q[u][v], q[u+1][v])
+ * per pixel, so that one 16-byte load fetches the four bilinear taps; the first
+ * batch writes vol, the later ones add to it. */
 ct_status_t ct_fbp_backproject(ct_fbp_t f, const float *filtered, float *vol, ct_stream_t stream);
 /* sino = transpose of step 4 applied to vol (overwrites; float atomics, so the
  * order of additions, and the last bits, vary between runs). */

@@ -47,6 +47,19 @@ __device__ __forceinline__ float buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t 
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
 }
 
+// Four consecutive floats at byte offset off (one 16-byte load).
+__device__ __forceinline__ float4 buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return make_float4(buffer_load(r, off), buffer_load(r, off + 4u), buffer_load(r, off + 8u),
+                       buffer_load(r, off + 12u));
+}
+
+// floor(x) as an integer in one instruction (|x| < 2^31).
+__device__ __forceinline__ int floor_i32(float x) {
+    int r;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 ct_status_t ffail(ct_status_t st, const char *msg) {
     set_error(msg);
     return st;
@@ -314,13 +327,29 @@ constexpr int kBpv = 16;   // Pu(3) pu Pv(3) pv Pw(3) pw K pad pad pad
 
 struct BpArgs {
     const double *bp;
-    const float *q;      // B: filtered sinogram in; B^T: sinogram out
+    const float *q;      // B (2D): filtered sinogram in
+    const float2 *pairs; // B (3D): views [view0, view1) of the filtered sinogram, pair-interleaved
     float *vol;          // B: volume out; B^T: volume in (read)
-    float *sino_out;
+    float *sino_out;     // B^T: sinogram out
     int W, H, D, U, V, n_views;
+    int view0, view1;    // the views this launch takes
+    int accumulate;      // B: add to vol instead of overwriting it
     int nbx, nby, nbz;
     int two_d;
 };
+
+// Pair interleaving of views [v0, v0 + n) of a (views, U, V) sinogram:
+// out[view][u][v] = (q[view][u][v], q[view][u + 1][v]), with q[view][U][v] = 0.
+// The four bilinear taps at (u, v), (u + 1, v), (u, v + 1), (u + 1, v + 1) are
+// then 16 consecutive bytes, which one load fetches.
+__global__ __launch_bounds__(256) void fbp_pair_kernel(const float *__restrict__ q, float2 *__restrict__ out,
+                                                       int U, int V, size_t n) {
+    const size_t uv = (size_t)U * V;
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const size_t r = i % uv;   // u * V + v within the view
+        out[i] = make_float2(q[i], r + V < uv ? q[i + V] : 0.f);
+    }
+}
 
 // Block-relative constants of one view, for a tile of ZR sub-blocks stacked
 // along z (sub-block r centred at X_r = (x0, y0, zc0 + 16 r)).  For a voxel at
@@ -330,7 +359,9 @@ struct BpArgs {
 // and Au_r = u_h(X_r) - u0_r w_h(X_r), computed in float64: the float32
 // arithmetic then only meets numbers of the size of a sub-block's footprint.
 // Layout: Pu(3) Pv(3) Pw(3) 1 fast 0 | Au[4] | Av[4] | Aw[4] | u0[4] | v0[4]
-// | u0[4] | v0[4] (the last two as int bits).  Every P and A is scaled by
+// | o0[4] | 0[4], o0 = 8 (u0 V + v0) the byte offset of the anchor pixel in the
+// view's pair-interleaved sinogram (int bits; used only where the tile is
+// inside the detector, so it is in range there).  Every P and A is scaled by
 // 1 / sqrt(K), which leaves u and v unchanged and makes the weight K / w^2
 // the square of the reciprocal of the scaled w.
 // fast = 1 when the whole tile (half extents hx, hy, hz about its centre
@@ -362,8 +393,8 @@ __device__ __forceinline__ void view_consts(const double *p, double x0, double y
         c[20 + r] = (float)(sk * wh);
         c[24 + r] = (float)u0;
         c[28 + r] = (float)v0;
-        c[32 + r] = __int_as_float((int)u0);
-        c[36 + r] = __int_as_float((int)v0);
+        c[32 + r] = __uint_as_float((uint32_t)((int64_t)u0 * V + (int64_t)v0) * 8u);
+        c[36 + r] = 0.f;
     }
     bool in = true;
 #pragma unroll 1
@@ -440,8 +471,8 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
         for (int r = 0; r < ZR; ++r) any = any || fz[r] != 0.f;
     }
     const int U = a.U, V = a.V;
-    for (int vb = 0; vb < a.n_views; vb += kBpViews) {
-        const int nvb = min(kBpViews, a.n_views - vb);
+    for (int vb = a.view0; vb < a.view1; vb += kBpViews) {
+        const int nvb = min(kBpViews, a.view1 - vb);
         __syncthreads();
         if ((int)threadIdx.x < nvb)
             view_consts<ZR>(a.bp + (size_t)(vb + threadIdx.x) * kBpv, X0, Y0, ZC0, ZT, 0.5 * (TX - 1),
@@ -467,28 +498,30 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
             // uniform over the block: a scalar branch
             const bool fast = __builtin_amdgcn_readfirstlane(c2.z != 0.f ? 1 : 0) != 0;
             const size_t vbase = (size_t)(vb + k) * U;
-            // this view's filtered sinogram, addressed with 32-bit offsets
-            const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + vbase * V, (uint32_t)U * V * 4u);
+            // this view's filtered sinogram (3D B: pair-interleaved), addressed
+            // with 32-bit offsets
+            const __amdgpu_buffer_rsrc_t rq =
+                (!TWO_D && !TRANSPOSE)
+                    ? buffer_rsrc((const float *)(a.pairs + (size_t)(vb + k - a.view0) * U * V), (uint32_t)U * V * 8u)
+                    : buffer_rsrc(a.q + vbase * V, (uint32_t)U * V * 4u);
             if (!TWO_D && !TRANSPOSE && fast) {
                 // every voxel of the tile is in front of the source and every
                 // bilinear tap exists
-                const int4 iu4 = *(const int4 *)(ck + 32);
-                const int4 iv4 = *(const int4 *)(ck + 36);
-                const int IU[4] = {iu4.x, iu4.y, iu4.z, iu4.w}, IV[4] = {iv4.x, iv4.y, iv4.z, iv4.w};
+                const int4 o4 = *(const int4 *)(ck + 32);
+                const int O0[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
                 for (int r = 0; r < ZR; ++r) {
                     const float rw = __builtin_amdgcn_rcpf(Aw[r] + pwd);
                     const float su = fmaf(-U0[r], pwd, Au[r] + pud) * rw;
                     const float sv = fmaf(-V0[r], pwd, Av[r] + pvd) * rw;
-                    const float flu = floorf(su), flv = floorf(sv);
-                    const float au = su - flu, av = sv - flv;
-                    // u, v < 2^20: 24-bit multiplies run at the full rate
-                    const uint32_t o =
-                        (__umul24((uint32_t)((int)flu + IU[r]), (uint32_t)V) + (uint32_t)((int)flv + IV[r])) * 4u;
-                    const float q00 = buffer_load(rq, o), q01 = buffer_load(rq, o + 4u);
-                    const float q10 = buffer_load(rq, o + 4u * V), q11 = buffer_load(rq, o + 4u * V + 4u);
-                    const float s0 = fmaf(av, q01 - q00, q00), s1 = fmaf(av, q11 - q10, q10);
-                    acc[r] = fmaf(rw * rw, fmaf(au, s1 - s0, s0), acc[r]);
+                    // offsets from the anchor pixel: small signed integers, so a
+                    // 24-bit multiply-add forms the byte offset
+                    const float au = __builtin_amdgcn_fractf(su), av = __builtin_amdgcn_fractf(sv);
+                    const uint32_t o = (uint32_t)(__mul24(floor_i32(su), 8 * V) + (floor_i32(sv) * 8 + O0[r]));
+                    // q(u, v), q(u + 1, v), q(u, v + 1), q(u + 1, v + 1) in one load
+                    const float4 t = buffer_load4(rq, o);
+                    const float s0 = fmaf(au, t.y - t.x, t.x), s1 = fmaf(au, t.w - t.z, t.z);
+                    acc[r] = fmaf(rw * rw, fmaf(av, s1 - s0, s0), acc[r]);
                 }
                 continue;
             }
@@ -544,9 +577,10 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
                             if (ku1 * kv1 != 0.f) atomicAdd(a.sino_out + r1 + jv1, g * ku1 * kv1);
                         }
                     } else {
-                        const uint32_t o0 = (uint32_t)ju0 * V * 4u, o1 = (uint32_t)ju1 * V * 4u;
-                        const float q00 = buffer_load(rq, o0 + jv0 * 4u), q01 = buffer_load(rq, o0 + jv1 * 4u);
-                        const float q10 = buffer_load(rq, o1 + jv0 * 4u), q11 = buffer_load(rq, o1 + jv1 * 4u);
+                        // the first float of each pair is the pixel itself
+                        const uint32_t o0 = (uint32_t)ju0 * V * 8u, o1 = (uint32_t)ju1 * V * 8u;
+                        const float q00 = buffer_load(rq, o0 + jv0 * 8u), q01 = buffer_load(rq, o0 + jv1 * 8u);
+                        const float q10 = buffer_load(rq, o1 + jv0 * 8u), q11 = buffer_load(rq, o1 + jv1 * 8u);
                         const float s0 = fmaf(kv0, q00, kv1 * q01), s1 = fmaf(kv0, q10, kv1 * q11);
                         acc[r] = fmaf(wgt, fmaf(ku0, s0, ku1 * s1), acc[r]);
                     }
@@ -557,7 +591,10 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
     if (!TRANSPOSE) {
 #pragma unroll
         for (int r = 0; r < ZR; ++r)
-            if (col_in && iz0 + 16 * r < a.D) a.vol[vidx0 + (size_t)(16 * r) * plane] = acc[r];
+            if (col_in && iz0 + 16 * r < a.D) {
+                float *o = a.vol + vidx0 + (size_t)(16 * r) * plane;
+                *o = a.accumulate ? *o + acc[r] : acc[r];
+            }
     }
 }
 
@@ -675,6 +712,9 @@ struct ct_fbp_s {
     float *d_fview = nullptr;
     float *d_parker = nullptr;
     double *d_bp = nullptr;
+    // 3D backprojection: the pair-interleaved copy of one batch of views
+    float2 *d_pairs = nullptr;
+    int pair_views = 0;
 };
 
 namespace {
@@ -686,6 +726,7 @@ void free_plan(ct_fbp_s *f) {
     if (f->d_fview) (void)hipFree(f->d_fview);
     if (f->d_parker) (void)hipFree(f->d_parker);
     if (f->d_bp) (void)hipFree(f->d_bp);
+    if (f->d_pairs) (void)hipFree(f->d_pairs);
     delete f;
 }
 
@@ -728,7 +769,8 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     if (h.U < 2 || (h.beam == CT_CONE && h.V < 2)) return ffail(CT_E_SHAPE, "interpolation needs >= 2 detector bins per axis");
     if (h.U > 4096) return ffail(CT_E_RANGE, "the filter supports U <= 4096");
     if ((int64_t)opts->pad_factor * h.U > 16384) return ffail(CT_E_RANGE, "pad_factor * U must be <= 16384");
-    if (h.D * h.H * h.W >= (int64_t(1) << 30) || h.n_views * h.U * h.V >= (int64_t(1) << 31))
+    if (h.D * h.H * h.W >= (int64_t(1) << 30) || h.n_views * h.U * h.V >= (int64_t(1) << 31) ||
+        h.U * h.V >= (int64_t(1) << 30))
         return ffail(CT_E_RANGE, "volume or sinogram too large for one buffer");
     if (!angular_weights && !angles) return ffail(CT_E_NULL, "angles (or angular_weights) must be given");
     if (opts->short_scan && !angles) return ffail(CT_E_NULL, "short scans need the angles");
@@ -940,6 +982,12 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     if (e == hipSuccess && !parker.empty()) e = hipMalloc((void **)&f->d_parker, parker.size() * sizeof(float));
     if (e == hipSuccess && f->P) e = hipMalloc((void **)&f->d_tw, twf.size() * sizeof(float2));
     if (e == hipSuccess && f->P) e = hipMalloc((void **)&f->d_mul, mulf.size() * sizeof(float));
+    if (!h.is2d) {
+        // equal batches of at most kBpViews views
+        const int64_t nb = (h.n_views + kBpViews - 1) / kBpViews;
+        f->pair_views = (int)((h.n_views + nb - 1) / nb);
+        if (e == hipSuccess) e = hipMalloc((void **)&f->d_pairs, (size_t)f->pair_views * h.U * h.V * sizeof(float2));
+    }
     if (e != hipSuccess) {
         (void)hipGetLastError();
         free_plan(f);
@@ -1058,8 +1106,12 @@ static BpArgs bp_args(ct_fbp_t f) {
     a.nby = (a.H + TY - 1) / TY;
     a.nbz = (a.D + TZ - 1) / TZ;
     a.q = nullptr;
+    a.pairs = nullptr;
     a.vol = nullptr;
     a.sino_out = nullptr;
+    a.view0 = 0;
+    a.view1 = a.n_views;
+    a.accumulate = 0;
     return a;
 }
 
@@ -1075,8 +1127,24 @@ ct_status_t ct_fbp_backproject(ct_fbp_t f, const float *filtered, float *vol, ct
     a.q = filtered;
     a.vol = vol;
     const dim3 grid((unsigned)(a.nbx * a.nby * a.nbz));
-    if (h.is2d) hipLaunchKernelGGL((fbp_bp_kernel<false, true, 1>), grid, dim3(256), 0, (hipStream_t)stream, a);
-    else hipLaunchKernelGGL((fbp_bp_kernel<false, false, kZRun>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    if (h.is2d) {
+        hipLaunchKernelGGL((fbp_bp_kernel<false, true, 1>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    } else {
+        // batches of views: pair-interleave the batch, then gather from it
+        // (the first batch writes the volume, the others add to it)
+        const size_t per_view = (size_t)h.U * h.V;
+        for (int v0 = 0; v0 < (int)h.n_views; v0 += f->pair_views) {
+            const int v1 = (int)std::min<int64_t>(h.n_views, (int64_t)v0 + f->pair_views);
+            const size_t n = (size_t)(v1 - v0) * per_view;
+            hipLaunchKernelGGL(fbp_pair_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 65536)), dim3(256),
+                               0, (hipStream_t)stream, filtered + (size_t)v0 * per_view, f->d_pairs, a.U, a.V, n);
+            a.pairs = f->d_pairs;
+            a.view0 = v0;
+            a.view1 = v1;
+            a.accumulate = v0 > 0 ? 1 : 0;
+            hipLaunchKernelGGL((fbp_bp_kernel<false, false, kZRun>), grid, dim3(256), 0, (hipStream_t)stream, a);
+        }
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fhip(e, "ct_fbp_backproject launch");
     set_error("");

@@ -72,6 +72,13 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 __device__ __forceinline__ float uni(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
+// The opposite: hold a value in a vector register.  A loop that selects among
+// wave-uniform operands with a per-lane mask needs them in vector registers
+// (one scalar operand per instruction); held there, the copies stay out of the loop.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x) {
+    asm("" : "+v"(x));
+    return x;
+}
 
 // Non-negative float64 to fixed point, saturating.
 __device__ __forceinline__ uint32_t fix64(double x) {
@@ -927,6 +934,58 @@ __device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long 
 // once, outside the ray loop.  TWO_D: single-slice bricks of a 2D geometry,
 // whose rays lie in the slice (z is neither clipped nor walked).  S = walk units
 // per length unit; yscale = power-of-two fixed-point scale of the ray values.
+// Everything of a brick walk that depends on the ray direction alone (for
+// parallel rays: once per view and brick).  Components below 2^-40 of the
+// largest count as zero; the test is taken over the wave, so waves without any
+// such component (nearly all of them) skip the special clip.  Negative
+// directions are mirrored about the brick centre, so every axis walks upwards.
+struct DirPlan {
+    float axx, ayy, azz;      // |direction|
+    float ix, iy, iz;         // 1 / |direction| (approximate reciprocal)
+    float LS;                 // walk units per unit of the ray parameter
+    float qfx, qfy, qfz;      // crossing spacing per axis, in walk units
+    uint32_t qx, qy, qz;      // the same in fixed point, saturating
+    uint32_t stx, sty, stz;   // LDS byte strides of a step along each axis
+    bool nx, ny, nz;          // mirrored axes
+    bool slow;                // some lane of the wave has a zero component
+};
+
+template <int LSY, int LSZ, bool TWO_D>
+__device__ __forceinline__ DirPlan dir_plan(float dx, float dy, float dz, float spx, float spy, float spz,
+                                            float S) {
+    DirPlan p;
+    if (TWO_D) dz = 0.f;
+    const float dm = fmaxf(fabsf(dx), fmaxf(fabsf(dy), fabsf(dz))) * 0x1p-40f;
+    const float amin = TWO_D ? fminf(fabsf(dx), fabsf(dy)) : fminf(fabsf(dx), fminf(fabsf(dy), fabsf(dz)));
+    p.slow = __builtin_amdgcn_ballot_w64(amin < dm) != 0;   // wave-uniform
+    if (p.slow) {
+        if (fabsf(dx) < dm) dx = 0.f;
+        if (fabsf(dy) < dm) dy = 0.f;
+        if (!TWO_D && fabsf(dz) < dm) dz = 0.f;
+    }
+    p.nx = dx < 0.f;
+    p.ny = dy < 0.f;
+    p.nz = dz < 0.f;
+    p.axx = fabsf(dx);
+    p.ayy = fabsf(dy);
+    p.azz = fabsf(dz);
+    p.ix = __builtin_amdgcn_rcpf(p.axx);
+    p.iy = __builtin_amdgcn_rcpf(p.ayy);
+    p.iz = TWO_D ? 0.f : __builtin_amdgcn_rcpf(p.azz);
+    const float px = dx * spx, py = dy * spy, pz = dz * spz;
+    p.LS = __builtin_amdgcn_sqrtf(px * px + py * py + pz * pz) * S;
+    p.qfx = p.LS * p.ix;
+    p.qfy = p.LS * p.iy;
+    p.qfz = p.LS * p.iz;
+    p.qx = sat_u32(p.qfx);
+    p.qy = sat_u32(p.qfy);
+    p.qz = TWO_D ? 0xFFFFFFFFu : sat_u32(p.qfz);
+    p.stx = p.nx ? (uint32_t)-8 : 8u;
+    p.sty = p.ny ? (uint32_t)(-8 * LSY) : (uint32_t)(8 * LSY);
+    p.stz = TWO_D ? 0u : (p.nz ? (uint32_t)(-8 * LSZ) : (uint32_t)(8 * LSZ));
+    return p;
+}
+
 template <int LSY, int LSZ, int MODE, bool PERSP, bool TWO_D, bool SURF>
 __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw, int view,
                                            const Footprint &f, int lane, int x0, int y0, int z0,
@@ -975,6 +1034,25 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     const float DSx = uni((float)vw[qs_ + 0]), DSy = uni((float)vw[qs_ + 1]);
     const float DSz = uni((float)vw[qs_ + 2]);
     const float tv0 = uni((float)(vw[VT_TMIN] - tb)), tv1 = uni((float)(vw[VT_TMAX] - tb));
+    // parallel rays: one direction plan for the footprint, and the anchor
+    // coefficients of the origin mirrored with it (a sign change is exact)
+    constexpr bool SHARED_DIR = !PERSP && !SURF;
+    DirPlan dp0{};
+    float mA0x = A0x, mA0y = A0y, mA0z = A0z, mAfx = Afx, mAfy = Afy, mAfz = Afz, mAsx = Asx, mAsy = Asy,
+          mAsz = Asz;
+    if (SHARED_DIR) {
+        dp0 = dir_plan<LSY, LSZ, TWO_D>(Dx, Dy, Dz, spx, spy, spz, S);
+        // wave-uniform: keep the plan in scalar registers
+        dp0.axx = uni(dp0.axx); dp0.ayy = uni(dp0.ayy); dp0.azz = uni(dp0.azz);
+        dp0.ix = uni(dp0.ix); dp0.iy = uni(dp0.iy); dp0.iz = uni(dp0.iz);
+        dp0.LS = uni(dp0.LS);
+        dp0.qfx = uni(dp0.qfx); dp0.qfy = uni(dp0.qfy); dp0.qfz = uni(dp0.qfz);
+        dp0.qx = (uint32_t)uni((int)dp0.qx); dp0.qy = (uint32_t)uni((int)dp0.qy);
+        dp0.qz = (uint32_t)uni((int)dp0.qz);
+        if (dp0.nx) { mA0x = -A0x; mAfx = -Afx; mAsx = -Asx; }
+        if (dp0.ny) { mA0y = -A0y; mAfy = -Afy; mAsy = -Asy; }
+        if (dp0.nz) { mA0z = -A0z; mAfz = -Afz; mAsz = -Asz; }
+    }
     const float *ysrc = a.sino + ((size_t)view * a.U + u0) * a.V + v0;
     const uint32_t yfs = ufast ? a.V : 1, yss = ufast ? 1 : a.V;   // sinogram strides, fast / slow
 
@@ -1024,74 +1102,66 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
             if (SURF) { o0n = ob[3 * yo]; o1n = ob[3 * yo + 1]; o2n = ob[3 * yo + 2]; }
         }
         if (yv == 0.f) continue;
-        float ox, oy, oz, dx, dy, dz, t0, t1;
-        if (SURF) {
-            // surface pixel: the ray from the table, re-expressed in float64 around
-            // the plane through the brick centre parallel to the flat detector
-            // (any parameter near the plane will do: the origin is then formed in
-            // float64 exactly on the ray for that parameter, so the crossing
-            // parameter itself is computed in float32)
-            const double px = sCx + o0 * sUx + o1 * sVx + o2 * sNx;
-            const double py = sCy + o0 * sUy + o1 * sVy + o2 * sNy;
-            const double pz = sCz + o0 * sUz + o1 * sVz + o2 * sNz;
-            double rdx, rdy, rdz, bx_, by_, bz_;   // direction; origin relative to the brick centre
-            if (PERSP) {
-                rdx = px; rdy = py; rdz = pz;
-                bx_ = vw[VT_O00 + 0] - cbx; by_ = vw[VT_O00 + 1] - cby; bz_ = vw[VT_O00 + 2] - cbz;
-            } else {
-                rdx = sDx; rdy = sDy; rdz = sDz;
-                bx_ = px - cbx; by_ = py - cby; bz_ = pz - cbz;
-            }
-            const float num = -((float)bx_ * fnx + (float)by_ * fny + (float)bz_ * fnz);
-            const float den = (float)rdx * fnx + (float)rdy * fny + (float)rdz * fnz;
-            const double tr = (double)(num * __builtin_amdgcn_rcpf(den));
-            ox = (float)fma(tr, rdx, bx_);
-            oy = (float)fma(tr, rdy, by_);
-            oz = TWO_D ? A0z : (float)fma(tr, rdz, bz_);
-            dx = (float)rdx;
-            dy = (float)rdy;
-            dz = TWO_D ? 0.f : (float)rdz;
-            t0 = (float)(vw[VT_TMIN] - tr);
-            t1 = (float)(vw[VT_TMAX] - tr);
-        } else {
-            ox = fmaf(cs, Asx, fmaf(cf, Afx, A0x));
-            oy = fmaf(cs, Asy, fmaf(cf, Afy, A0y));
-            oz = TWO_D ? A0z : fmaf(cs, Asz, fmaf(cf, Afz, A0z));
-            dx = Dx; dy = Dy; dz = Dz;
-            if (PERSP) {
-                dx = fmaf(cs, DSx, fmaf(cf, DFx, Dx));
-                dy = fmaf(cs, DSy, fmaf(cf, DFy, Dy));
-                if (!TWO_D) dz = fmaf(cs, DSz, fmaf(cf, DFz, Dz));
-            }
-            if (TWO_D) dz = 0.f;
+        float mx, my, mz, t0, t1;   // origin relative to the brick centre, mirrored
+        DirPlan dp;
+        if (SHARED_DIR) {
+            dp = dp0;
+            mx = fmaf(cs, mAsx, fmaf(cf, mAfx, mA0x));
+            my = fmaf(cs, mAsy, fmaf(cf, mAfy, mA0y));
+            mz = TWO_D ? mA0z : fmaf(cs, mAsz, fmaf(cf, mAfz, mA0z));
             t0 = tv0;
             t1 = tv1;
+        } else {
+            float ox, oy, oz, dx, dy, dz;
+            if (SURF) {
+                // surface pixel: the ray from the table, re-expressed in float64 around
+                // the plane through the brick centre parallel to the flat detector
+                // (any parameter near the plane will do: the origin is then formed in
+                // float64 exactly on the ray for that parameter, so the crossing
+                // parameter itself is computed in float32)
+                const double px = sCx + o0 * sUx + o1 * sVx + o2 * sNx;
+                const double py = sCy + o0 * sUy + o1 * sVy + o2 * sNy;
+                const double pz = sCz + o0 * sUz + o1 * sVz + o2 * sNz;
+                double rdx, rdy, rdz, bx_, by_, bz_;   // direction; origin relative to the brick centre
+                if (PERSP) {
+                    rdx = px; rdy = py; rdz = pz;
+                    bx_ = vw[VT_O00 + 0] - cbx; by_ = vw[VT_O00 + 1] - cby; bz_ = vw[VT_O00 + 2] - cbz;
+                } else {
+                    rdx = sDx; rdy = sDy; rdz = sDz;
+                    bx_ = px - cbx; by_ = py - cby; bz_ = pz - cbz;
+                }
+                const float num = -((float)bx_ * fnx + (float)by_ * fny + (float)bz_ * fnz);
+                const float den = (float)rdx * fnx + (float)rdy * fny + (float)rdz * fnz;
+                const double tr = (double)(num * __builtin_amdgcn_rcpf(den));
+                ox = (float)fma(tr, rdx, bx_);
+                oy = (float)fma(tr, rdy, by_);
+                oz = TWO_D ? A0z : (float)fma(tr, rdz, bz_);
+                dx = (float)rdx;
+                dy = (float)rdy;
+                dz = TWO_D ? 0.f : (float)rdz;
+                t0 = (float)(vw[VT_TMIN] - tr);
+                t1 = (float)(vw[VT_TMAX] - tr);
+            } else {
+                ox = fmaf(cs, Asx, fmaf(cf, Afx, A0x));
+                oy = fmaf(cs, Asy, fmaf(cf, Afy, A0y));
+                oz = TWO_D ? A0z : fmaf(cs, Asz, fmaf(cf, Afz, A0z));
+                dx = fmaf(cs, DSx, fmaf(cf, DFx, Dx));
+                dy = fmaf(cs, DSy, fmaf(cf, DFy, Dy));
+                dz = TWO_D ? 0.f : fmaf(cs, DSz, fmaf(cf, DFz, Dz));
+                t0 = tv0;
+                t1 = tv1;
+            }
+            dp = dir_plan<LSY, LSZ, TWO_D>(dx, dy, dz, spx, spy, spz, S);
+            mx = dp.nx ? -ox : ox;
+            my = dp.ny ? -oy : oy;
+            mz = dp.nz ? -oz : oz;
         }
-        // Components below 2^-40 of the largest count as zero.  Waves without
-        // any (nearly all of them) take the short clip below.
-        const float dm = fmaxf(fabsf(dx), fmaxf(fabsf(dy), fabsf(dz))) * 0x1p-40f;
-        const float amin = TWO_D ? fminf(fabsf(dx), fabsf(dy))
-                                 : fminf(fabsf(dx), fminf(fabsf(dy), fabsf(dz)));
-        const bool slow = __builtin_amdgcn_ballot_w64(amin < dm) != 0;   // wave-uniform
-        if (slow) {
-            if (fabsf(dx) < dm) dx = 0.f;
-            if (fabsf(dy) < dm) dy = 0.f;
-            if (!TWO_D && fabsf(dz) < dm) dz = 0.f;
-        }
-        // mirror negative directions about the brick centre: walk every axis upwards
-        const bool nx = dx < 0.f, ny = dy < 0.f, nz = dz < 0.f;
-        const float mx = nx ? -ox : ox, axx = fabsf(dx);
-        const float my = ny ? -oy : oy, ayy = fabsf(dy);
-        const float mz = nz ? -oz : oz, azz = fabsf(dz);
-        const float ix = __builtin_amdgcn_rcpf(axx);
-        const float iy = __builtin_amdgcn_rcpf(ayy);
-        const float iz = TWO_D ? 0.f : __builtin_amdgcn_rcpf(azz);
         // slab clip: lo = (-h - m) / a, hi = (h - m) / a
-        float cx = mx, cy = my, cz = mz, cix = ix, ciy = iy, ciz = iz;
-        if (slow) {
-            bclip_zero(mx, axx, hx, cx, cix);
-            bclip_zero(my, ayy, hy, cy, ciy);
-            if (!TWO_D) bclip_zero(mz, azz, hz, cz, ciz);
+        float cx = mx, cy = my, cz = mz, cix = dp.ix, ciy = dp.iy, ciz = dp.iz;
+        if (dp.slow) {
+            bclip_zero(mx, dp.axx, hx, cx, cix);
+            bclip_zero(my, dp.ayy, hy, cy, ciy);
+            if (!TWO_D) bclip_zero(mz, dp.azz, hz, cz, ciz);
         }
         const float lox = (-hx - cx) * cix, hix = fmaf(fex, cix, lox);
         const float loy = (-hy - cy) * ciy, hiy = fmaf(fey, ciy, loy);
@@ -1100,30 +1170,27 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         const float tin = fmaxf(fmaxf(fmaxf(lox, loy), loz), t0);
         const float tout = fminf(fminf(fminf(hix, hiy), hiz), t1);
         if (!(tin < tout)) continue;
-        const float px = dx * spx, py = dy * spy, pz = dz * spz;
-        const float LS = __builtin_amdgcn_sqrtf(px * px + py * py + pz * pz) * S;
-        const float qfx = LS * ix, qfy = LS * iy, qfz = LS * iz;
         IWalk w;
-        w.qx = sat_u32(qfx);
-        w.qy = sat_u32(qfy);
-        w.qz = TWO_D ? 0xFFFFFFFFu : sat_u32(qfz);
+        w.qx = dp.qx;
+        w.qy = dp.qy;
+        w.qz = dp.qz;
         float fcx, fcy, fcz = 0.f;
         uint32_t farx, fary, farz = 0xFFFFFFFFu;
-        baxis(mx, axx, tin, hx, fex - 1.f, qfx, w.qx, fcx, w.lx, farx);
-        baxis(my, ayy, tin, hy, fey - 1.f, qfy, w.qy, fcy, w.ly, fary);
-        if (!TWO_D) baxis(mz, azz, tin, hz, fez - 1.f, qfz, w.qz, fcz, w.lz, farz);
+        baxis(mx, dp.axx, tin, hx, fex - 1.f, dp.qfx, w.qx, fcx, w.lx, farx);
+        baxis(my, dp.ayy, tin, hy, fey - 1.f, dp.qfy, w.qy, fcy, w.ly, fary);
+        if (!TWO_D) baxis(mz, dp.azz, tin, hz, fez - 1.f, dp.qfz, w.qz, fcz, w.lz, farz);
         else w.lz = 0xFFFFFFFFu;
         // the walk ends at the ray's own end (a segment may stop inside the
         // brick) or at the first far-face crossing, whichever comes first
-        w.lend = min(sat_u32((tout - tin) * LS), min(min(farx, fary), farz));
+        w.lend = min(sat_u32((tout - tin) * dp.LS), min(min(farx, fary), farz));
         // back to real cell indices (exact small integers in float) and strides
-        const float rcx = nx ? fex - 1.f - fcx : fcx;
-        const float rcy = ny ? fey - 1.f - fcy : fcy;
-        const float rcz = nz ? fez - 1.f - fcz : fcz;
+        const float rcx = dp.nx ? fex - 1.f - fcx : fcx;
+        const float rcy = dp.ny ? fey - 1.f - fcy : fcy;
+        const float rcz = dp.nz ? fez - 1.f - fcz : fcz;
         w.idx = (uint32_t)fmaf(rcz, (float)(8 * LSZ), fmaf(rcy, (float)(8 * LSY), rcx * 8.f));
-        w.stx = nx ? (uint32_t)-8 : 8u;
-        w.sty = ny ? (uint32_t)(-8 * LSY) : (uint32_t)(8 * LSY);
-        w.stz = TWO_D ? 0u : (nz ? (uint32_t)(-8 * LSZ) : (uint32_t)(8 * LSZ));
+        w.stx = in_vgpr(dp.stx);
+        w.sty = in_vgpr(dp.sty);
+        w.stz = in_vgpr(dp.stz);
         const int Y = (int)rintf(__builtin_amdgcn_fmed3f(yv * yscale, -8388607.f, 8388607.f));
         iwalk_scatter_fix(w, acc, Y);
     }
