@@ -26,6 +26,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "ct_internal.h"
@@ -338,16 +339,25 @@ struct BpArgs {
     int two_d;
 };
 
-// Pair interleaving of views [v0, v0 + n) of a (views, U, V) sinogram:
-// out[view][u][v] = (q[view][u][v], q[view][u + 1][v]), with q[view][U][v] = 0.
-// The four bilinear taps at (u, v), (u + 1, v), (u, v + 1), (u + 1, v + 1) are
-// then 16 consecutive bytes, which one load fetches.
+// Pair interleaving of nv views of a (views, U, V) sinogram, with a border
+// of zeros: per view (U + 1) x (V + 2) pairs,
+//   out[view][u + 1][v + 1] = (q[view][u][v], q[view][u + 1][v]),  u in [-1, U - 1], v in [-1, V],
+// q being 0 outside the detector.  The four bilinear taps at (u, v), (u + 1, v),
+// (u, v + 1), (u + 1, v + 1) are then the 16 bytes at out[view][u + 1][v + 1],
+// one load, for every -1 <= u <= U - 1 and -1 <= v <= V - 1; taps off the
+// detector read the zeros.
 __global__ __launch_bounds__(256) void fbp_pair_kernel(const float *__restrict__ q, float2 *__restrict__ out,
-                                                       int U, int V, size_t n) {
-    const size_t uv = (size_t)U * V;
+                                                       int U, int V, size_t nv) {
+    const int Vp = V + 2;
+    const size_t per = (size_t)(U + 1) * Vp, n = nv * per;
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const size_t r = i % uv;   // u * V + v within the view
-        out[i] = make_float2(q[i], r + V < uv ? q[i + V] : 0.f);
+        const size_t view = i / per;
+        const int r = (int)(i - view * per);
+        const int u = r / Vp - 1, v = r % Vp - 1;   // u in [-1, U - 1], v in [-1, V]
+        const float *qv = q + view * U * V;
+        const bool vin = v >= 0 && v < V;
+        out[i] = make_float2(vin && u >= 0 ? qv[(size_t)u * V + v] : 0.f,
+                             vin && u + 1 < U ? qv[(size_t)(u + 1) * V + v] : 0.f);
     }
 }
 
@@ -359,19 +369,19 @@ __global__ __launch_bounds__(256) void fbp_pair_kernel(const float *__restrict__
 // and Au_r = u_h(X_r) - u0_r w_h(X_r), computed in float64: the float32
 // arithmetic then only meets numbers of the size of a sub-block's footprint.
 // Layout: Pu(3) Pv(3) Pw(3) 1 fast 0 | Au[4] | Av[4] | Aw[4] | u0[4] | v0[4]
-// | o0[4] | 0[4], o0 = 8 (u0 V + v0) the byte offset of the anchor pixel in the
-// view's pair-interleaved sinogram (int bits; used only where the tile is
-// inside the detector, so it is in range there).  Every P and A is scaled by
+// | o0[4] | 0[4], o0 = 8 ((u0 + 1)(V + 2) + v0 + 1) the byte offset of the
+// anchor pixel in the view's padded pair-interleaved sinogram (int bits; used
+// only for offsets that are in range).  Every P and A is scaled by
 // 1 / sqrt(K), which leaves u and v unchanged and makes the weight K / w^2
 // the square of the reciprocal of the scaled w.
 // fast = 1 when the whole tile (half extents hx, hy, hz about its centre
-// (x0, y0, zt)) lies in front of the source and projects strictly inside the
-// detector, so every bilinear tap exists: the projection of a box lies inside
-// the hull of its corners' projections.
+// (x0, y0, zt)) lies in front of the source and projects inside the detector
+// (padded: inside the zero border), so every bilinear tap exists: the
+// projection of a box lies inside the hull of its corners' projections.
 template <int ZR>
 __device__ __forceinline__ void view_consts(const double *p, double x0, double y0, double zc0, double zt,
                                             double hx, double hy, double hz, int U, int V, bool two_d,
-                                            float *c) {
+                                            bool padded, float *c) {
     const double sk = 1.0 / sqrt(p[12]);   // K > 0 (checked when the plan is made)
     for (int k = 0; k < 3; ++k) {
         c[k] = (float)(sk * p[k]);
@@ -393,7 +403,7 @@ __device__ __forceinline__ void view_consts(const double *p, double x0, double y
         c[20 + r] = (float)(sk * wh);
         c[24 + r] = (float)u0;
         c[28 + r] = (float)v0;
-        c[32 + r] = __uint_as_float((uint32_t)((int64_t)u0 * V + (int64_t)v0) * 8u);
+        c[32 + r] = __uint_as_float((uint32_t)((int64_t)(u0 + 1) * (V + 2) + (int64_t)(v0 + 1)) * 8u);
         c[36 + r] = 0.f;
     }
     bool in = true;
@@ -405,11 +415,16 @@ __device__ __forceinline__ void view_consts(const double *p, double x0, double y
             in = false;
             break;
         }
-        // float32 corners (errors ~1e-4 bin, far inside the 0.01 margin)
+        // float32 corners (errors ~1e-4 bin, far inside the 0.01 margin).
+        // Plain layout: both taps on the detector; padded pairs: floor(u) in
+        // [-1, U - 1] and floor(v) in [-1, V - 1] (the border holds the zeros)
         const float u = (float)(p[0] * X + p[1] * Y + p[2] * Z + p[3]) / w;
         const float v = (float)(p[4] * X + p[5] * Y + p[6] * Z + p[7]) / w;
-        in = u >= 0.01f && u <= (float)(U - 1) - 0.01f &&
-             (two_d || (v >= 0.01f && v <= (float)(V - 1) - 0.01f));
+        if (padded)
+            in = u >= -0.99f && u <= (float)U - 0.01f && v >= -0.99f && v <= (float)V - 0.01f;
+        else
+            in = u >= 0.01f && u <= (float)(U - 1) - 0.01f &&
+                 (two_d || (v >= 0.01f && v <= (float)(V - 1) - 0.01f));
     }
     c[10] = in ? 1.f : 0.f;
 }
@@ -471,120 +486,166 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
         for (int r = 0; r < ZR; ++r) any = any || fz[r] != 0.f;
     }
     const int U = a.U, V = a.V;
+    // One view's contribution to the thread's voxels.  fast_tag: the tile lies
+    // in front of the source and projects inside the detector (no bounds checks).
+    auto one_view = [&](int vb, int k, auto fast_tag) {
+        const float *ck = cst + k * kBpConst;
+        const float4 c0 = *(const float4 *)(ck);        // Pu.x Pu.y Pu.z Pv.x
+        const float4 c1 = *(const float4 *)(ck + 4);    // Pv.y Pv.z Pw.x Pw.y
+        const float4 c2 = *(const float4 *)(ck + 8);    // Pw.z 1 fast 0
+        const float4 au4 = *(const float4 *)(ck + 12);
+        const float4 av4 = *(const float4 *)(ck + 16);
+        const float4 aw4 = *(const float4 *)(ck + 20);
+        const float4 u04 = *(const float4 *)(ck + 24);
+        const float4 v04 = *(const float4 *)(ck + 28);
+        const float Au[4] = {au4.x, au4.y, au4.z, au4.w}, Av[4] = {av4.x, av4.y, av4.z, av4.w};
+        const float Aw[4] = {aw4.x, aw4.y, aw4.z, aw4.w};
+        const float U0[4] = {u04.x, u04.y, u04.z, u04.w}, V0[4] = {v04.x, v04.y, v04.z, v04.w};
+        const float pud = fmaf(c0.z, dz, fmaf(c0.y, dy, c0.x * dx));
+        const float pvd = fmaf(c1.y, dz, fmaf(c1.x, dy, c0.w * dx));
+        const float pwd = fmaf(c2.x, dz, fmaf(c1.w, dy, c1.z * dx));
+        constexpr bool fast = decltype(fast_tag)::value;
+        const size_t vbase = (size_t)(vb + k) * U;
+        if constexpr (!TWO_D && !TRANSPOSE) {
+            // 3D gather from the view's padded pair-interleaved copy
+            const uint32_t pv = (uint32_t)(U + 1) * (uint32_t)(V + 2) * 8u;
+            const __amdgpu_buffer_rsrc_t rq =
+                buffer_rsrc((const float *)(a.pairs + (size_t)(vb + k - a.view0) * (U + 1) * (V + 2)), pv);
+            const int4 o4 = *(const int4 *)(ck + 32);
+            const int O0[4] = {o4.x, o4.y, o4.z, o4.w};
+            const int row = 8 * (V + 2);
+#pragma unroll
+            for (int r = 0; r < ZR; ++r) {
+                const float w = Aw[r] + pwd;
+                const float rw = __builtin_amdgcn_rcpf(w);
+                const float su = fmaf(-U0[r], pwd, Au[r] + pud) * rw;
+                const float sv = fmaf(-V0[r], pwd, Av[r] + pvd) * rw;
+                // offsets from the anchor pixel: small signed integers, so a
+                // 24-bit multiply-add forms the byte offset
+                const float au = __builtin_amdgcn_fractf(su), av = __builtin_amdgcn_fractf(sv);
+                uint32_t o = (uint32_t)(__mul24(floor_i32(su), row) + (floor_i32(sv) * 8 + O0[r]));
+                // outside the fast tiles: voxels at or behind the source, or whose
+                // taps fall beyond the zero border, add nothing (and read a safe
+                // address); near the border a rounding of the test reads zeros
+                bool in = true;
+                if constexpr (!fast) {
+                    const float fu = su + U0[r], fv = sv + V0[r];
+                    in = w > 0.f && fu >= -1.f && fu < (float)U && fv >= -1.f && fv < (float)V;
+                    o = in ? o : 0u;
+                }
+                // q(u, v), q(u + 1, v), q(u, v + 1), q(u + 1, v + 1) in one load
+                const float4 t = buffer_load4(rq, o);
+                const float s0 = fmaf(au, t.y - t.x, t.x), s1 = fmaf(au, t.w - t.z, t.z);
+                const float nacc = fmaf(rw * rw, fmaf(av, s1 - s0, s0), acc[r]);
+                acc[r] = in ? nacc : acc[r];
+            }
+            return;
+        }
+        // this view's filtered sinogram, addressed with 32-bit offsets
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + vbase * V, (uint32_t)U * V * 4u);
+#pragma unroll
+        for (int r = 0; r < ZR; ++r) {
+            const float w = Aw[r] + pwd;
+            if (!fast && !(w > 0.f)) continue;   // at or behind the source
+            const float rw = __builtin_amdgcn_rcpf(w);
+            const float su = fmaf(-U0[r], pwd, Au[r] + pud) * rw;
+            const float flu = floorf(su);
+            const float au = su - flu;
+            const int iu = (int)flu + (int)U0[r];
+            const float wgt = rw * rw;   // K / w^2: K is folded into the scaled w
+            if (TWO_D) {
+                bool ok0 = true, ok1 = true;
+                if (!fast) {
+                    ok0 = (unsigned)iu < (unsigned)U;
+                    ok1 = (unsigned)(iu + 1) < (unsigned)U;
+                }
+                const float k0 = ok0 ? 1.f - au : 0.f, k1 = ok1 ? au : 0.f;
+                const int j0 = ok0 ? iu : 0, j1 = ok1 ? iu + 1 : 0;
+                if (TRANSPOSE) {
+                    const float g = wgt * fz[r];
+                    if (g != 0.f && k0 != 0.f) atomicAdd(a.sino_out + vbase + j0, g * k0);
+                    if (g != 0.f && k1 != 0.f) atomicAdd(a.sino_out + vbase + j1, g * k1);
+                } else {
+                    const float q0 = buffer_load(rq, (uint32_t)j0 * 4u), q1 = buffer_load(rq, (uint32_t)j1 * 4u);
+                    acc[r] = fmaf(wgt, fmaf(k0, q0, k1 * q1), acc[r]);
+                }
+            } else {
+                const float sv = fmaf(-V0[r], pwd, Av[r] + pvd) * rw;
+                const float flv = floorf(sv);
+                const float av = sv - flv;
+                const int iv = (int)flv + (int)V0[r];
+                bool u0k = true, u1k = true, v0k = true, v1k = true;
+                if (!fast) {
+                    u0k = (unsigned)iu < (unsigned)U;
+                    u1k = (unsigned)(iu + 1) < (unsigned)U;
+                    v0k = (unsigned)iv < (unsigned)V;
+                    v1k = (unsigned)(iv + 1) < (unsigned)V;
+                }
+                const float ku0 = u0k ? 1.f - au : 0.f, ku1 = u1k ? au : 0.f;
+                const float kv0 = v0k ? 1.f - av : 0.f, kv1 = v1k ? av : 0.f;
+                const int ju0 = u0k ? iu : 0, ju1 = u1k ? iu + 1 : 0;
+                const int jv0 = v0k ? iv : 0, jv1 = v1k ? iv + 1 : 0;
+                const size_t r0 = (vbase + ju0) * V, r1 = (vbase + ju1) * V;
+                if (TRANSPOSE) {
+                    const float g = wgt * fz[r];
+                    if (g != 0.f) {
+                        if (ku0 * kv0 != 0.f) atomicAdd(a.sino_out + r0 + jv0, g * ku0 * kv0);
+                        if (ku0 * kv1 != 0.f) atomicAdd(a.sino_out + r0 + jv1, g * ku0 * kv1);
+                        if (ku1 * kv0 != 0.f) atomicAdd(a.sino_out + r1 + jv0, g * ku1 * kv0);
+                        if (ku1 * kv1 != 0.f) atomicAdd(a.sino_out + r1 + jv1, g * ku1 * kv1);
+                    }
+                } else {
+                    const uint32_t o0 = (uint32_t)ju0 * V * 4u, o1 = (uint32_t)ju1 * V * 4u;
+                    const float q00 = buffer_load(rq, o0 + jv0 * 4u), q01 = buffer_load(rq, o0 + jv1 * 4u);
+                    const float q10 = buffer_load(rq, o1 + jv0 * 4u), q11 = buffer_load(rq, o1 + jv1 * 4u);
+                    const float s0 = fmaf(kv0, q00, kv1 * q01), s1 = fmaf(kv0, q10, kv1 * q11);
+                    acc[r] = fmaf(wgt, fmaf(ku0, s0, ku1 * s1), acc[r]);
+                }
+            }
+        }
+    };
+    __shared__ unsigned char vorder[kBpViews];   // 3D B: the batch's views, fast ones first
+    __shared__ int vfast;
     for (int vb = a.view0; vb < a.view1; vb += kBpViews) {
         const int nvb = min(kBpViews, a.view1 - vb);
         __syncthreads();
         if ((int)threadIdx.x < nvb)
             view_consts<ZR>(a.bp + (size_t)(vb + threadIdx.x) * kBpv, X0, Y0, ZC0, ZT, 0.5 * (TX - 1),
-                            0.5 * (TY - 1), 0.5 * (TZ - 1), U, V, TWO_D, cst + threadIdx.x * kBpConst);
+                            0.5 * (TY - 1), 0.5 * (TZ - 1), U, V, TWO_D, !TWO_D && !TRANSPOSE,
+                            cst + threadIdx.x * kBpConst);
         __syncthreads();
-        if (!any) continue;
-        for (int k = 0; k < nvb; ++k) {
-            const float *ck = cst + k * kBpConst;
-            const float4 c0 = *(const float4 *)(ck);        // Pu.x Pu.y Pu.z Pv.x
-            const float4 c1 = *(const float4 *)(ck + 4);    // Pv.y Pv.z Pw.x Pw.y
-            const float4 c2 = *(const float4 *)(ck + 8);    // Pw.z 1 fast 0
-            const float4 au4 = *(const float4 *)(ck + 12);
-            const float4 av4 = *(const float4 *)(ck + 16);
-            const float4 aw4 = *(const float4 *)(ck + 20);
-            const float4 u04 = *(const float4 *)(ck + 24);
-            const float4 v04 = *(const float4 *)(ck + 28);
-            const float Au[4] = {au4.x, au4.y, au4.z, au4.w}, Av[4] = {av4.x, av4.y, av4.z, av4.w};
-            const float Aw[4] = {aw4.x, aw4.y, aw4.z, aw4.w};
-            const float U0[4] = {u04.x, u04.y, u04.z, u04.w}, V0[4] = {v04.x, v04.y, v04.z, v04.w};
-            const float pud = fmaf(c0.z, dz, fmaf(c0.y, dy, c0.x * dx));
-            const float pvd = fmaf(c1.y, dz, fmaf(c1.x, dy, c0.w * dx));
-            const float pwd = fmaf(c2.x, dz, fmaf(c1.w, dy, c1.z * dx));
-            // uniform over the block: a scalar branch
-            const bool fast = __builtin_amdgcn_readfirstlane(c2.z != 0.f ? 1 : 0) != 0;
-            const size_t vbase = (size_t)(vb + k) * U;
-            // this view's filtered sinogram (3D B: pair-interleaved), addressed
-            // with 32-bit offsets
-            const __amdgpu_buffer_rsrc_t rq =
-                (!TWO_D && !TRANSPOSE)
-                    ? buffer_rsrc((const float *)(a.pairs + (size_t)(vb + k - a.view0) * U * V), (uint32_t)U * V * 8u)
-                    : buffer_rsrc(a.q + vbase * V, (uint32_t)U * V * 4u);
-            if (!TWO_D && !TRANSPOSE && fast) {
-                // every voxel of the tile is in front of the source and every
-                // bilinear tap exists
-                const int4 o4 = *(const int4 *)(ck + 32);
-                const int O0[4] = {o4.x, o4.y, o4.z, o4.w};
-#pragma unroll
-                for (int r = 0; r < ZR; ++r) {
-                    const float rw = __builtin_amdgcn_rcpf(Aw[r] + pwd);
-                    const float su = fmaf(-U0[r], pwd, Au[r] + pud) * rw;
-                    const float sv = fmaf(-V0[r], pwd, Av[r] + pvd) * rw;
-                    // offsets from the anchor pixel: small signed integers, so a
-                    // 24-bit multiply-add forms the byte offset
-                    const float au = __builtin_amdgcn_fractf(su), av = __builtin_amdgcn_fractf(sv);
-                    const uint32_t o = (uint32_t)(__mul24(floor_i32(su), 8 * V) + (floor_i32(sv) * 8 + O0[r]));
-                    // q(u, v), q(u + 1, v), q(u, v + 1), q(u + 1, v + 1) in one load
-                    const float4 t = buffer_load4(rq, o);
-                    const float s0 = fmaf(au, t.y - t.x, t.x), s1 = fmaf(au, t.w - t.z, t.z);
-                    acc[r] = fmaf(rw * rw, fmaf(av, s1 - s0, s0), acc[r]);
-                }
-                continue;
+        if constexpr (!TWO_D && !TRANSPOSE) {
+            // order the batch: views whose fast flag is set first (each lane of
+            // wave 0 ranks views l and l + 64 with ballots), so the two loops
+            // below carry no per-view branch
+            if (threadIdx.x < 64) {
+                const int l = threadIdx.x;
+                const bool in0 = l < nvb, in1 = l + 64 < nvb;
+                const bool f0 = in0 && cst[l * kBpConst + 10] != 0.f;
+                const bool f1 = in1 && cst[(l + 64) * kBpConst + 10] != 0.f;
+                const uint64_t bf0 = __ballot(f0), bf1 = __ballot(f1);
+                const uint64_t bs0 = __ballot(in0 && !f0), bs1 = __ballot(in1 && !f1);
+                const uint64_t below = (1ull << l) - 1ull;
+                const int nf0 = __popcll(bf0), nf = nf0 + __popcll(bf1), ns0 = __popcll(bs0);
+                if (f0) vorder[__popcll(bf0 & below)] = (unsigned char)l;
+                if (f1) vorder[nf0 + __popcll(bf1 & below)] = (unsigned char)(l + 64);
+                if (in0 && !f0) vorder[nf + __popcll(bs0 & below)] = (unsigned char)l;
+                if (in1 && !f1) vorder[nf + ns0 + __popcll(bs1 & below)] = (unsigned char)(l + 64);
+                if (l == 0) vfast = nf;
             }
-#pragma unroll
-            for (int r = 0; r < ZR; ++r) {
-                const float w = Aw[r] + pwd;
-                if (!fast && !(w > 0.f)) continue;   // at or behind the source
-                const float rw = __builtin_amdgcn_rcpf(w);
-                const float su = fmaf(-U0[r], pwd, Au[r] + pud) * rw;
-                const float flu = floorf(su);
-                const float au = su - flu;
-                const int iu = (int)flu + (int)U0[r];
-                const float wgt = rw * rw;   // K / w^2: K is folded into the scaled w
-                if (TWO_D) {
-                    bool ok0 = true, ok1 = true;
-                    if (!fast) {
-                        ok0 = (unsigned)iu < (unsigned)U;
-                        ok1 = (unsigned)(iu + 1) < (unsigned)U;
-                    }
-                    const float k0 = ok0 ? 1.f - au : 0.f, k1 = ok1 ? au : 0.f;
-                    const int j0 = ok0 ? iu : 0, j1 = ok1 ? iu + 1 : 0;
-                    if (TRANSPOSE) {
-                        const float g = wgt * fz[r];
-                        if (g != 0.f && k0 != 0.f) atomicAdd(a.sino_out + vbase + j0, g * k0);
-                        if (g != 0.f && k1 != 0.f) atomicAdd(a.sino_out + vbase + j1, g * k1);
-                    } else {
-                        const float q0 = buffer_load(rq, (uint32_t)j0 * 4u), q1 = buffer_load(rq, (uint32_t)j1 * 4u);
-                        acc[r] = fmaf(wgt, fmaf(k0, q0, k1 * q1), acc[r]);
-                    }
-                } else {
-                    const float sv = fmaf(-V0[r], pwd, Av[r] + pvd) * rw;
-                    const float flv = floorf(sv);
-                    const float av = sv - flv;
-                    const int iv = (int)flv + (int)V0[r];
-                    bool u0k = true, u1k = true, v0k = true, v1k = true;
-                    if (!fast) {
-                        u0k = (unsigned)iu < (unsigned)U;
-                        u1k = (unsigned)(iu + 1) < (unsigned)U;
-                        v0k = (unsigned)iv < (unsigned)V;
-                        v1k = (unsigned)(iv + 1) < (unsigned)V;
-                    }
-                    const float ku0 = u0k ? 1.f - au : 0.f, ku1 = u1k ? au : 0.f;
-                    const float kv0 = v0k ? 1.f - av : 0.f, kv1 = v1k ? av : 0.f;
-                    const int ju0 = u0k ? iu : 0, ju1 = u1k ? iu + 1 : 0;
-                    const int jv0 = v0k ? iv : 0, jv1 = v1k ? iv + 1 : 0;
-                    const size_t r0 = (vbase + ju0) * V, r1 = (vbase + ju1) * V;
-                    if (TRANSPOSE) {
-                        const float g = wgt * fz[r];
-                        if (g != 0.f) {
-                            if (ku0 * kv0 != 0.f) atomicAdd(a.sino_out + r0 + jv0, g * ku0 * kv0);
-                            if (ku0 * kv1 != 0.f) atomicAdd(a.sino_out + r0 + jv1, g * ku0 * kv1);
-                            if (ku1 * kv0 != 0.f) atomicAdd(a.sino_out + r1 + jv0, g * ku1 * kv0);
-                            if (ku1 * kv1 != 0.f) atomicAdd(a.sino_out + r1 + jv1, g * ku1 * kv1);
-                        }
-                    } else {
-                        // the first float of each pair is the pixel itself
-                        const uint32_t o0 = (uint32_t)ju0 * V * 8u, o1 = (uint32_t)ju1 * V * 8u;
-                        const float q00 = buffer_load(rq, o0 + jv0 * 8u), q01 = buffer_load(rq, o0 + jv1 * 8u);
-                        const float q10 = buffer_load(rq, o1 + jv0 * 8u), q11 = buffer_load(rq, o1 + jv1 * 8u);
-                        const float s0 = fmaf(kv0, q00, kv1 * q01), s1 = fmaf(kv0, q10, kv1 * q11);
-                        acc[r] = fmaf(wgt, fmaf(ku0, s0, ku1 * s1), acc[r]);
-                    }
-                }
+            __syncthreads();
+            if (!any) continue;
+            const int nf = vfast;
+            for (int i = 0; i < nf; ++i) one_view(vb, vorder[i], std::true_type{});
+            for (int i = nf; i < nvb; ++i) one_view(vb, vorder[i], std::false_type{});
+        } else {
+            if (!any) continue;
+            for (int k = 0; k < nvb; ++k) {
+                // uniform over the block: a scalar branch
+                if (__builtin_amdgcn_readfirstlane(cst[k * kBpConst + 10] != 0.f ? 1 : 0) != 0)
+                    one_view(vb, k, std::true_type{});
+                else
+                    one_view(vb, k, std::false_type{});
             }
         }
     }
@@ -986,7 +1047,8 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
         // equal batches of at most kBpViews views
         const int64_t nb = (h.n_views + kBpViews - 1) / kBpViews;
         f->pair_views = (int)((h.n_views + nb - 1) / nb);
-        if (e == hipSuccess) e = hipMalloc((void **)&f->d_pairs, (size_t)f->pair_views * h.U * h.V * sizeof(float2));
+        if (e == hipSuccess)
+            e = hipMalloc((void **)&f->d_pairs, (size_t)f->pair_views * (h.U + 1) * (h.V + 2) * sizeof(float2));
     }
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -1132,12 +1194,13 @@ ct_status_t ct_fbp_backproject(ct_fbp_t f, const float *filtered, float *vol, ct
     } else {
         // batches of views: pair-interleave the batch, then gather from it
         // (the first batch writes the volume, the others add to it)
-        const size_t per_view = (size_t)h.U * h.V;
+        const size_t per_view = (size_t)h.U * h.V, per_pairs = (size_t)(h.U + 1) * (h.V + 2);
         for (int v0 = 0; v0 < (int)h.n_views; v0 += f->pair_views) {
             const int v1 = (int)std::min<int64_t>(h.n_views, (int64_t)v0 + f->pair_views);
-            const size_t n = (size_t)(v1 - v0) * per_view;
+            const size_t n = (size_t)(v1 - v0) * per_pairs;
             hipLaunchKernelGGL(fbp_pair_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 65536)), dim3(256),
-                               0, (hipStream_t)stream, filtered + (size_t)v0 * per_view, f->d_pairs, a.U, a.V, n);
+                               0, (hipStream_t)stream, filtered + (size_t)v0 * per_view, f->d_pairs, a.U, a.V,
+                               (size_t)(v1 - v0));
             a.pairs = f->d_pairs;
             a.view0 = v0;
             a.view1 = v1;

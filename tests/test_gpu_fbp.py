@@ -67,6 +67,8 @@ CASES = {
     "fan-short": short_fan,
     "cone": cone_wl,
     "cone-jittered-aniso": lambda: cone_wl(jitter=0.4, spacing=(1.2, 0.9, 1.0)),
+    # more views than one backprojection batch holds: batches of 86, 86, 85
+    "cone-257-views": lambda: cone_wl(n=257, det=(31, 23), vol=(12, 17, 19)),
     # power-of-two padded rows take the FFT filter
     "parallel-pow2": lambda: par_wl(U=64),
     "fan-pow2": lambda: fan_wl(U=128),
