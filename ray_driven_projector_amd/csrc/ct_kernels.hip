@@ -1056,16 +1056,21 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     const float *ysrc = a.sino + ((size_t)view * a.U + u0) * a.V + v0;
     const uint32_t yfs = ufast ? a.V : 1, yss = ufast ? 1 : a.V;   // sinogram strides, fast / slow
 
-    // footprint position of ray r (fast and slow offsets ff, fs from the anchor,
-    // sinogram offset yo from (u0, v0)), advanced by 64 rays per round
+    // Ray r of the footprint is pixel lf = r mod nf of slow row srow(r / nf).
+    // Parallel rays take the rows from the centre outwards, so the 64 rays of a
+    // round lie at similar distances from the brick's projected centre and walk
+    // similar lengths through it (fewer idle lanes than in row order; for
+    // fan/cone footprints the gain does not pay for the index arithmetic).
+    // (lk, lf) advance by 64 rays per round; yo is the sinogram offset of the
+    // ray from (u0, v0).
     const int step_slow = 64 / nf, step_fast = 64 - step_slow * nf;
-    const uint32_t yo_step = step_fast * yfs + step_slow * yss, yo_wrap = yss - nf * yfs;
+    const int hs = (nrays / nf) >> 1;
+    const auto srow = [hs](int k) {
+        return PERSP ? k : hs + ((k & 1) ? -((k + 1) >> 1) : (k >> 1));
+    };
     const float af = (float)(ufast ? cu : cv), as_ = (float)(ufast ? cv : cu);
-    const float fnf = (float)nf, fend = fnf - af;
-    const float fstep_fast = (float)step_fast, fstep_slow = (float)step_slow;
-    const int ls = lane / nf, lf = lane - ls * nf;
-    float ff = (float)lf - af, fs = (float)ls - as_;
-    uint32_t yo = lf * yfs + ls * yss;
+    int lk = lane / nf, lf = lane - lk * nf;
+    uint32_t yo = lf * yfs + srow(lk) * yss;
     float ynext = 1.f;
     if (MODE != BM_COLINV && lane < nrays) ynext = ysrc[yo];
     // surface: the frame in registers, and each ray's offsets fetched one round
@@ -1088,11 +1093,11 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         if (lane < nrays) { o0n = ob[3 * yo]; o1n = ob[3 * yo + 1]; o2n = ob[3 * yo + 2]; }
     }
     for (int r = lane; r < nrays; r += 64) {
-        const float cf = ff, cs = fs;
-        ff += fstep_fast;
-        fs += fstep_slow;
-        yo += yo_step;
-        if (ff >= fend) { ff -= fnf; fs += 1.f; yo += yo_wrap; }
+        const float cf = (float)lf - af, cs = (float)srow(lk) - as_;
+        lf += step_fast;
+        lk += step_slow;
+        if (lf >= nf) { lf -= nf; lk += 1; }
+        yo = lf * yfs + srow(lk) * yss;
         // take this ray's prefetched values before issuing the next ray's loads, so
         // the wait covers only loads issued a round earlier
         const float yv = ynext;
