@@ -44,6 +44,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const float *p, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// Workgroups are dispatched to the 8 XCDs in turn (block i to XCD i mod 8),
+// and each XCD has its own L2.  Logical block ids remapped so that XCD x runs
+// one contiguous range: neighbouring blocks, which share cache lines of the
+// sinogram rows, then share an L2.
+__device__ __forceinline__ int xcd_block(int hw, int nblocks) {
+    constexpr int kXcd = 8;
+    const int q = nblocks / kXcd, r = nblocks % kXcd;
+    const int x = hw % kXcd, k = hw / kXcd;
+    return x * q + min(x, r) + k;
+}
+
 __device__ __forceinline__ float buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
 }
@@ -102,12 +113,13 @@ __global__ __launch_bounds__(256) void fbp_filter_kernel(FilterArgs a) {
     const int U = a.U, V = a.V, U8 = a.U8, VT = a.VT, S = a.S;
     int view0, v0;
     if (a.two_d) {
-        view0 = blockIdx.x * VT;
+        view0 = xcd_block(blockIdx.x, gridDim.x) * VT;
         v0 = 0;
     } else {
         const int nvt = (V + VT - 1) / VT;
-        view0 = blockIdx.x / nvt;
-        v0 = (blockIdx.x % nvt) * VT;
+        const int b = xcd_block(blockIdx.x, gridDim.x);
+        view0 = b / nvt;
+        v0 = (b % nvt) * VT;
     }
     for (int i = threadIdx.x; i < 2 * U8; i += 256) taps[i] = a.taps[i];
     // load the rows with their pre-weights; samples past U (or past the last
@@ -225,12 +237,13 @@ __global__ __launch_bounds__(256) void fbp_fft_filter_kernel(FftArgs a) {
     float *mul = (float *)(tw + P / 2);   // P / 2 + 1
     int view0, v0;
     if (a.two_d) {
-        view0 = blockIdx.x * C;
+        view0 = xcd_block(blockIdx.x, gridDim.x) * C;
         v0 = 0;
     } else {
         const int nvt = (V + C - 1) / C;
-        view0 = blockIdx.x / nvt;
-        v0 = (blockIdx.x % nvt) * C;
+        const int b = xcd_block(blockIdx.x, gridDim.x);
+        view0 = b / nvt;
+        v0 = (b % nvt) * C;
     }
     for (int i = threadIdx.x; i < P / 2; i += 256) tw[i] = a.tw[i];
     for (int i = threadIdx.x; i <= P / 2; i += 256) mul[i] = a.mul[i];
@@ -264,17 +277,41 @@ __global__ __launch_bounds__(256) void fbp_fft_filter_kernel(FftArgs a) {
         xf[2 * ((c >> 1) * P + br) + (c & 1)] = val;
     }
     __syncthreads();
-    const int nbf = NP * (P / 2);
-    for (int st = 1; st <= L; ++st) {   // forward, decimation in time
-        const int half = 1 << (st - 1);
-        for (int b = threadIdx.x; b < nbf; b += 256) {
-            const int pr = b >> (L - 1), bb = b & (P / 2 - 1);
-            const int j = bb & (half - 1);
-            const int i0 = pr * P + ((bb >> (st - 1)) << st) + j, i1 = i0 + half;
-            const float2 t = cmul(tw[j << (L - st)], x[i1]);
-            const float2 u0 = x[i0];
-            x[i0] = make_float2(u0.x + t.x, u0.y + t.y);
-            x[i1] = make_float2(u0.x - t.x, u0.y - t.y);
+    // Forward, decimation in time, two stages per pass: stages s and s + 1
+    // touch the four elements i, i + h, i + 2h, i + 3h (h = 2^(s-1)) of a group
+    // of 4h and no others, so a thread takes them through both stages in
+    // registers (half the LDS traffic and barriers of one stage per pass).
+    // An odd count of stages starts with one single stage.
+    const int nbf = NP * (P / 2), nq = NP * (P / 4);
+    int st = 1;
+    if (L & 1) {
+        for (int b = threadIdx.x; b < nbf; b += 256) {   // stage 1: h = 1, twiddle 1
+            const float2 u0 = x[2 * b], u1 = x[2 * b + 1];
+            x[2 * b] = make_float2(u0.x + u1.x, u0.y + u1.y);
+            x[2 * b + 1] = make_float2(u0.x - u1.x, u0.y - u1.y);
+        }
+        __syncthreads();
+        st = 2;
+    }
+    for (; st < L; st += 2) {
+        const int h = 1 << (st - 1);
+        for (int b = threadIdx.x; b < nq; b += 256) {
+            const int pr = b >> (L - 2), bb = b & (P / 4 - 1);
+            const int j = bb & (h - 1);
+            const int i0 = pr * P + ((bb >> (st - 1)) << (st + 1)) + j;
+            const float2 w1 = tw[j << (L - st)];
+            const float2 w2a = tw[j << (L - st - 1)], w2b = tw[(j + h) << (L - st - 1)];
+            const float2 x0 = x[i0], x1 = x[i0 + h], x2 = x[i0 + 2 * h], x3 = x[i0 + 3 * h];
+            float2 t = cmul(w1, x1);
+            const float2 y0 = make_float2(x0.x + t.x, x0.y + t.y), y1 = make_float2(x0.x - t.x, x0.y - t.y);
+            t = cmul(w1, x3);
+            const float2 y2 = make_float2(x2.x + t.x, x2.y + t.y), y3 = make_float2(x2.x - t.x, x2.y - t.y);
+            t = cmul(w2a, y2);
+            x[i0] = make_float2(y0.x + t.x, y0.y + t.y);
+            x[i0 + 2 * h] = make_float2(y0.x - t.x, y0.y - t.y);
+            t = cmul(w2b, y3);
+            x[i0 + h] = make_float2(y1.x + t.x, y1.y + t.y);
+            x[i0 + 3 * h] = make_float2(y1.x - t.x, y1.y - t.y);
         }
         __syncthreads();
     }
@@ -284,16 +321,33 @@ __global__ __launch_bounds__(256) void fbp_fft_filter_kernel(FftArgs a) {
         x[i] = make_float2(x[i].x * m, x[i].y * m);
     }
     __syncthreads();
-    for (int st = L; st >= 1; --st) {   // inverse, decimation in frequency
-        const int half = 1 << (st - 1);
-        for (int b = threadIdx.x; b < nbf; b += 256) {
-            const int pr = b >> (L - 1), bb = b & (P / 2 - 1);
-            const int j = bb & (half - 1);
-            const int i0 = pr * P + ((bb >> (st - 1)) << st) + j, i1 = i0 + half;
-            const float2 p0 = x[i0], p1 = x[i1];
-            const float2 w = tw[j << (L - st)];
-            x[i0] = make_float2(p0.x + p1.x, p0.y + p1.y);
-            x[i1] = cmul(make_float2(p0.x - p1.x, p0.y - p1.y), make_float2(w.x, -w.y));
+    // Inverse, decimation in frequency, stages L down to 1, two per pass:
+    // stages s and s - 1 touch i, i + h, i + 2h, i + 3h (h = 2^(s-2)); an odd
+    // count ends with the single stage 1.
+    for (st = L; st >= 2; st -= 2) {
+        const int h = 1 << (st - 2);
+        for (int b = threadIdx.x; b < nq; b += 256) {
+            const int pr = b >> (L - 2), bb = b & (P / 4 - 1);
+            const int j = bb & (h - 1);
+            const int i0 = pr * P + ((bb >> (st - 2)) << st) + j;
+            const float2 wa = tw[j << (L - st)], wb = tw[(j + h) << (L - st)], wc = tw[j << (L - st + 1)];
+            const float2 x0 = x[i0], x1 = x[i0 + h], x2 = x[i0 + 2 * h], x3 = x[i0 + 3 * h];
+            const float2 y0 = make_float2(x0.x + x2.x, x0.y + x2.y);
+            const float2 y2 = cmul(make_float2(x0.x - x2.x, x0.y - x2.y), make_float2(wa.x, -wa.y));
+            const float2 y1 = make_float2(x1.x + x3.x, x1.y + x3.y);
+            const float2 y3 = cmul(make_float2(x1.x - x3.x, x1.y - x3.y), make_float2(wb.x, -wb.y));
+            x[i0] = make_float2(y0.x + y1.x, y0.y + y1.y);
+            x[i0 + h] = cmul(make_float2(y0.x - y1.x, y0.y - y1.y), make_float2(wc.x, -wc.y));
+            x[i0 + 2 * h] = make_float2(y2.x + y3.x, y2.y + y3.y);
+            x[i0 + 3 * h] = cmul(make_float2(y2.x - y3.x, y2.y - y3.y), make_float2(wc.x, -wc.y));
+        }
+        __syncthreads();
+    }
+    if (st == 1) {
+        for (int b = threadIdx.x; b < nbf; b += 256) {   // stage 1: h = 1, twiddle 1
+            const float2 p0 = x[2 * b], p1 = x[2 * b + 1];
+            x[2 * b] = make_float2(p0.x + p1.x, p0.y + p1.y);
+            x[2 * b + 1] = make_float2(p0.x - p1.x, p0.y - p1.y);
         }
         __syncthreads();
     }
