@@ -1070,7 +1070,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     };
     const float af = (float)(ufast ? cu : cv), as_ = (float)(ufast ? cv : cu);
     int lk = lane / nf, lf = lane - lk * nf;
-    uint32_t yo = lf * yfs + srow(lk) * yss;
+    uint32_t yo = __umul24(lf, yfs) + __umul24(srow(lk), yss);   // offsets < 2^24, products < 2^31
     float ynext = 1.f;
     if (MODE != BM_COLINV && lane < nrays) ynext = ysrc[yo];
     // surface: the frame in registers, and each ray's offsets fetched one round
@@ -1097,7 +1097,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         lf += step_fast;
         lk += step_slow;
         if (lf >= nf) { lf -= nf; lk += 1; }
-        yo = lf * yfs + srow(lk) * yss;
+        yo = __umul24(lf, yfs) + __umul24(srow(lk), yss);
         // take this ray's prefetched values before issuing the next ray's loads, so
         // the wait covers only loads issued a round earlier
         const float yv = ynext;
