@@ -199,8 +199,11 @@ def main():
         names = ("fbp_filter", "fbp_backproject")
         U = wl.det_shape[0]
         flops_per = {"fbp_filter": 2 * U * M, "fbp_backproject": FDK_FLOPS_PER_UPDATE * N * wl.n_views}
-        kern_names = {"fbp_filter": "fbp_filter_kernel",
-                      "fbp_backproject": "fbp_bp_kernel<false, false, 4>"}
+        # ct_fbp_backproject gathers in equal batches of at most 128 views, one
+        # launch each (after a pair-interleaving copy of the batch)
+        n_batch = -(-wl.n_views // 128)
+        kern_names = {"fbp_filter": "fbp_fft_filter_kernel",
+                      "fbp_backproject": f"fbp_bp_kernel<false, false, 4> ({n_batch} launches per call)"}
 
         def step(evs):
             evs[0].record(stream)
@@ -340,7 +343,8 @@ def main():
             "bound": "alu", "kernel": kern_names[dom], "achieved": round(achieved / 1e12, 2),
             "peak": round(ALU_PEAK / 1e12, 1), "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK, 4),
             "traffic": _traffic(dom, args.workload),
-            "algorithmic_flops_per_launch": flops_per[dom],
+            "algorithmic_flops_per_launch": flops_per[dom] // (n_batch if dom == "fbp_backproject" else 1),
+            "launches_per_call": n_batch if dom == "fbp_backproject" else 1,
         } if fdk else {
             "bound": "hbm", "kernel": kern_names[dom], "achieved": round(achieved / 1e9, 1),
             "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved / HBM_PEAK, 4),
