@@ -333,7 +333,8 @@ typedef struct {
  * angular_weights: HOST, n_views, or NULL for the rule above.
  * A cone-beam plan also owns device staging for the backprojection: the
  * filtered sinogram of one batch of nb <= 128 views in pair-interleaved form
- * (8 nb U V bytes; the views are split into equal batches).  Backprojections
+ * with a border of zeros (8 nb (U + 1)(V + 2) bytes; the views are split into
+ * equal batches).  Backprojections
  * with one plan therefore share it: calls of ct_fbp_backproject or ct_fbp_run
  * with the same plan on different streams must not overlap in time.
  * Errors: CT_E_NULL, CT_E_ARG (beam, window, pad, short scan on parallel, a
@@ -349,8 +350,8 @@ ct_status_t ct_fbp_info(ct_fbp_t f, double *iso, double *angular_weights);
 ct_status_t ct_fbp_filter(ct_fbp_t f, const float *sino, float *filtered, ct_stream_t stream);
 /* vol = step 4 of filtered (overwrites every voxel).  Cone: per batch of views,
  * the plan's staging receives the batch pair-interleaved, (q[u][v], q[u+1][v])
- * per pixel, so that one 16-byte load fetches the four bilinear taps; the first
- * batch writes vol, the later ones add to it. */
+ * per pixel inside a border of zeros, so that one 16-byte load fetches the four
+ * bilinear taps; the first batch writes vol, the later ones add to it. */
 ct_status_t ct_fbp_backproject(ct_fbp_t f, const float *filtered, float *vol, ct_stream_t stream);
 /* sino = transpose of step 4 applied to vol (overwrites; float atomics, so the
  * order of additions, and the last bits, vary between runs). */
