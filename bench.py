@@ -36,6 +36,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -53,11 +54,19 @@ ALU_PEAK = 256 * 4 * 16 * 2 * 2.4e9
 FDK_FLOPS_PER_UPDATE = 36
 
 
+KERNEL_SOURCES = ("ct_kernels.hip", "ct_abi.hip", "ct_geometry.cpp", "ct_fbp.hip", "ct_launch.h", "ct_internal.h")
+
+
 def _kernel_source_hash() -> str:
+    """Hash of the library's code with comments and blank space removed, so
+    that counter summaries stay valid across edits that change no code."""
     h = hashlib.sha256()
-    for f in ("ct_kernels.hip", "ct_abi.hip", "ct_geometry.cpp", "ct_fbp.hip"):
-        with open(os.path.join(ROOT, "ray_driven_projector_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ray_driven_projector_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

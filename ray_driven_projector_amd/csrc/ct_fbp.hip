@@ -541,7 +541,9 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
     }
     const int U = a.U, V = a.V;
     // One view's contribution to the thread's voxels.  fast_tag: the tile lies
-    // in front of the source and projects inside the detector (no bounds checks).
+    // in front of the source and every tap of its voxels exists (on the
+    // detector, or for the 3D gather within the staging's zero border), so no
+    // voxel needs a test.
     auto one_view = [&](int vb, int k, auto fast_tag) {
         const float *ck = cst + k * kBpConst;
         const float4 c0 = *(const float4 *)(ck);        // Pu.x Pu.y Pu.z Pv.x
