@@ -928,12 +928,6 @@ __device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long 
     if (lc < lend) lds_add(lds, idx, mul24_64(lend - lc, Y));
 }
 
-// Walk every ray of one view's footprint through the brick.  PERSP: fan/cone
-// rays (direction per ray); otherwise parallel rays, whose direction and all
-// that is derived from it are the same for the whole footprint and computed
-// once, outside the ray loop.  TWO_D: single-slice bricks of a 2D geometry,
-// whose rays lie in the slice (z is neither clipped nor walked).  S = walk units
-// per length unit; yscale = power-of-two fixed-point scale of the ray values.
 // Everything of a brick walk that depends on the ray direction alone (for
 // parallel rays: once per view and brick).  Components below 2^-40 of the
 // largest count as zero; the test is taken over the wave, so waves without any
@@ -986,6 +980,12 @@ __device__ __forceinline__ DirPlan dir_plan(float dx, float dy, float dz, float 
     return p;
 }
 
+// Walk every ray of one view's footprint through the brick.  PERSP: fan/cone
+// rays (direction per ray); otherwise parallel rays, whose direction and all
+// that is derived from it are the same for the whole footprint and computed
+// once, outside the ray loop.  TWO_D: single-slice bricks of a 2D geometry,
+// whose rays lie in the slice (z is neither clipped nor walked).  S = walk units
+// per length unit; yscale = power-of-two fixed-point scale of the ray values.
 template <int LSY, int LSZ, int MODE, bool PERSP, bool TWO_D, bool SURF>
 __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw, int view,
                                            const Footprint &f, int lane, int x0, int y0, int z0,
