@@ -301,7 +301,9 @@ ct_status_t ct_project_host(ct_geom_t g, const float *vol_host, float *sino_host
  *      centre x gathers, per view, the bilinearly interpolated filtered value
  *      where it projects, times R D / U(x)^2 (fan/cone: U(x) = (x - a).n,
  *      D = (c - a).n, R = (iso - a).n) or 1 (parallel); samples outside the
- *      detector are 0.  Its transpose scatters the same coefficients.
+ *      detector are 0, and a voxel at or behind the source (U(x) <= 0) lies
+ *      on no ray of that view and gathers nothing from it.  Its transpose
+ *      scatters the same coefficients.
  * It is not the ct_backproject adjoint.  ct_fbp_filter does 1-3,
  * ct_fbp_backproject does 4, ct_fbp_run does both. */
 typedef struct ct_fbp_s *ct_fbp_t;       /* opaque, library-owned */

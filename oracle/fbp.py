@@ -41,6 +41,9 @@ Readings where the pages give no formula (each listed in the design notes):
     and gamma the in-plane fan angle of the column, signed in the sense of
     rotation; delta is the largest |gamma|.
   - Interpolation treats detector samples outside [0, U-1] x [0, V-1] as 0.
+  - Fan/cone: a point at or behind the source (U(x) <= 0) lies on no ray of
+    that view (the rays run from the source towards the detector) and gathers
+    nothing from it.
 """
 from __future__ import annotations
 
@@ -272,8 +275,10 @@ def _projection(wl, view, X, iso):
         Ux = (X - a) @ n
         D = np.dot(c - a, n)
         R = np.dot(iso - a, n)
-        P = a + (X - a) * (D / Ux)[..., None]
-        wgt = R * D / Ux ** 2
+        front = Ux > 0
+        Us = np.where(front, Ux, 1.0)            # points on no ray: any finite stand-in
+        P = a + (X - a) * (D / Us)[..., None]
+        wgt = np.where(front, R * D / Us ** 2, 0.0)
     else:
         # parallel: slide X along the ray direction onto the detector plane
         t = ((c - X) @ n) / np.dot(a, n)

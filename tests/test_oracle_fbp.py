@@ -237,6 +237,37 @@ def test_weighted_backprojection_transpose_identity(beam):
     assert abs(lhs - rhs) <= 1e-12 * max(abs(lhs), 1.0)
 
 
+@pytest.mark.parametrize("beam", [W.BEAM_FAN2D, W.BEAM_CONE])
+def test_points_behind_the_source_gather_nothing(beam):
+    # one view, source at the origin looking along +x: the half-space x <= 0
+    # lies on no ray, and a point in front gets the distance weight R D / U^2
+    fr = np.zeros((1, 12))
+    fr[0, 3:6] = [40.0, 0.0, 0.0]                      # detector centre
+    fr[0, 6:9] = [0.0, 1.0, 0.0]                       # e_u
+    fr[0, 9:12] = [0.0, 0.0, 1.0]                      # e_v
+    three_d = beam == W.BEAM_CONE
+    wl = W.Workload("v", beam, (5 if three_d else 1, 7, 9), (1, 1, 1),
+                    (31, 21 if three_d else 1), (2.0, 2.0), fr)
+    z, y, x = F.voxel_centres(wl)                      # x spans -4 .. 4
+    q = np.ones(wl.sino_shape)
+    iso = np.array([20.0, 0.0, 0.0])
+    got = F.weighted_backproject(wl, q, iso=iso)
+    behind = np.broadcast_to(x[None, None, :] <= 0, got.shape)
+    assert np.all(got[behind] == 0.0)
+    # in front, where every tap is on the detector (all ones), the value is
+    # R D / U^2 with U = x
+    Xc = np.broadcast_to(x[None, None, :], got.shape)
+    Yc = np.broadcast_to(y[None, :, None], got.shape)
+    Zc = np.broadcast_to(z[:, None, None], got.shape)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        inside = (~behind) & (np.abs(Yc * 40.0 / Xc) <= 26.0)
+        if three_d:
+            inside &= np.abs(Zc * 40.0 / Xc) <= 16.0
+        expect = 20.0 * 40.0 / Xc ** 2
+    assert inside.sum() >= 8
+    assert np.allclose(got[inside], expect[inside], rtol=1e-12)
+
+
 def test_isocentre_of_a_shifted_orbit():
     fr = W.helix_cone(36, 50.0, 80.0, 0.0, 1.0)
     shift = np.array([3.0, -2.0, 0.0])
