@@ -597,7 +597,7 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
             }
             return;
         }
-        // this view's filtered sinogram, addressed with 32-bit offsets
+        // 2D gather: this view's filtered sinogram, addressed with 32-bit offsets
         const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(a.q + vbase * V, (uint32_t)U * V * 4u);
 #pragma unroll
         for (int r = 0; r < ZR; ++r) {
@@ -626,6 +626,7 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
                     acc[r] = fmaf(wgt, fmaf(k0, q0, k1 * q1), acc[r]);
                 }
             } else {
+                // 3D reaches here for the transpose only (the gather returned above)
                 const float sv = fmaf(-V0[r], pwd, Av[r] + pvd) * rw;
                 const float flv = floorf(sv);
                 const float av = sv - flv;
@@ -642,20 +643,12 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
                 const int ju0 = u0k ? iu : 0, ju1 = u1k ? iu + 1 : 0;
                 const int jv0 = v0k ? iv : 0, jv1 = v1k ? iv + 1 : 0;
                 const size_t r0 = (vbase + ju0) * V, r1 = (vbase + ju1) * V;
-                if (TRANSPOSE) {
-                    const float g = wgt * fz[r];
-                    if (g != 0.f) {
-                        if (ku0 * kv0 != 0.f) atomicAdd(a.sino_out + r0 + jv0, g * ku0 * kv0);
-                        if (ku0 * kv1 != 0.f) atomicAdd(a.sino_out + r0 + jv1, g * ku0 * kv1);
-                        if (ku1 * kv0 != 0.f) atomicAdd(a.sino_out + r1 + jv0, g * ku1 * kv0);
-                        if (ku1 * kv1 != 0.f) atomicAdd(a.sino_out + r1 + jv1, g * ku1 * kv1);
-                    }
-                } else {
-                    const uint32_t o0 = (uint32_t)ju0 * V * 4u, o1 = (uint32_t)ju1 * V * 4u;
-                    const float q00 = buffer_load(rq, o0 + jv0 * 4u), q01 = buffer_load(rq, o0 + jv1 * 4u);
-                    const float q10 = buffer_load(rq, o1 + jv0 * 4u), q11 = buffer_load(rq, o1 + jv1 * 4u);
-                    const float s0 = fmaf(kv0, q00, kv1 * q01), s1 = fmaf(kv0, q10, kv1 * q11);
-                    acc[r] = fmaf(wgt, fmaf(ku0, s0, ku1 * s1), acc[r]);
+                const float g = wgt * fz[r];
+                if (g != 0.f) {
+                    if (ku0 * kv0 != 0.f) atomicAdd(a.sino_out + r0 + jv0, g * ku0 * kv0);
+                    if (ku0 * kv1 != 0.f) atomicAdd(a.sino_out + r0 + jv1, g * ku0 * kv1);
+                    if (ku1 * kv0 != 0.f) atomicAdd(a.sino_out + r1 + jv0, g * ku1 * kv0);
+                    if (ku1 * kv1 != 0.f) atomicAdd(a.sino_out + r1 + jv1, g * ku1 * kv1);
                 }
             }
         }
