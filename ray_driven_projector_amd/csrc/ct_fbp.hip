@@ -72,6 +72,14 @@ __device__ __forceinline__ int floor_i32(float x) {
     return r;
 }
 
+// a * b + c with a and b signed 24-bit, in one instruction (the compiler
+// otherwise splits it around a three-operand add).
+__device__ __forceinline__ int mad_i24(int a, int b, int c) {
+    int r;
+    asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 ct_status_t ffail(ct_status_t st, const char *msg) {
     set_error(msg);
     return st;
@@ -418,10 +426,11 @@ __global__ __launch_bounds__(256) void fbp_pair_kernel(const float *__restrict__
 // Block-relative constants of one view, for a tile of ZR sub-blocks stacked
 // along z (sub-block r centred at X_r = (x0, y0, zc0 + 16 r)).  For a voxel at
 // X_r + d (d the same offset in every sub-block):
-//   w = Aw_r + Pw . d,   u - u0_r = (Au_r + Pu . d - u0_r Pw . d) / w,   v likewise
-// with the integer anchors u0_r, v0_r (the projection of X_r, rounded down)
-// and Au_r = u_h(X_r) - u0_r w_h(X_r), computed in float64: the float32
-// arithmetic then only meets numbers of the size of a sub-block's footprint.
+//   w = Aw_r + Pw . d,   u - u0 = (Au_r + Pu . d - u0 Pw . d) / w,   v likewise
+// with integer anchors: v0_r the projection of X_r rounded down, and one u0
+// for the whole tile (u barely moves along z); Au_r = u_h(X_r) - u0 w_h(X_r),
+// computed in float64: the float32 arithmetic then only meets numbers of the
+// size of a sub-block's footprint.  (The u0 slots repeat the tile's anchor.)
 // Layout: Pu(3) Pv(3) Pw(3) 1 fast 0 | Au[4] | Av[4] | Aw[4] | u0[4] | v0[4]
 // | o0[4] | 0[4], o0 = 8 ((u0 + 1)(V + 2) + v0 + 1) the byte offset of the
 // anchor pixel in the view's padded pair-interleaved sinogram (int bits; used
@@ -444,13 +453,25 @@ __device__ __forceinline__ void view_consts(const double *p, double x0, double y
     }
     c[9] = 1.f;
     c[11] = 0.f;
+    // one u anchor for the tile, from the sub-block farthest in front of the
+    // source (u hardly changes along z: the tile's u range is a few bins)
+    double ubest = 0.0, wbest = 0.0;
+#pragma unroll 1
+    for (int r = 0; r < ZR; ++r) {
+        const double z = zc0 + 16.0 * r;
+        const double wh = p[8] * x0 + p[9] * y0 + p[10] * z + p[11];
+        if (wh > wbest) {
+            wbest = wh;
+            ubest = p[0] * x0 + p[1] * y0 + p[2] * z + p[3];
+        }
+    }
+    const double u0 = wbest > 0.0 ? fmin(fmax(floor(ubest / wbest), -1e9), 1e9) : 0.0;
 #pragma unroll 1
     for (int r = 0; r < 4; ++r) {
         const double z = zc0 + 16.0 * (r < ZR ? r : 0);
         const double uh = p[0] * x0 + p[1] * y0 + p[2] * z + p[3];
         const double vh = p[4] * x0 + p[5] * y0 + p[6] * z + p[7];
         const double wh = p[8] * x0 + p[9] * y0 + p[10] * z + p[11];
-        const double u0 = wh > 0.0 ? fmin(fmax(floor(uh / wh), -1e9), 1e9) : 0.0;
         const double v0 = wh > 0.0 ? fmin(fmax(floor(vh / wh), -1e9), 1e9) : 0.0;
         c[12 + r] = (float)(sk * (uh - u0 * wh));
         c[16 + r] = (float)(sk * (vh - v0 * wh));
@@ -570,16 +591,17 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
             const int4 o4 = *(const int4 *)(ck + 32);
             const int O0[4] = {o4.x, o4.y, o4.z, o4.w};
             const int row = 8 * (V + 2);
+            const float pud0 = fmaf(-U0[0], pwd, pud);   // the tile's one u anchor
 #pragma unroll
             for (int r = 0; r < ZR; ++r) {
                 const float w = Aw[r] + pwd;
                 const float rw = __builtin_amdgcn_rcpf(w);
-                const float su = fmaf(-U0[r], pwd, Au[r] + pud) * rw;
+                const float su = (Au[r] + pud0) * rw;
                 const float sv = fmaf(-V0[r], pwd, Av[r] + pvd) * rw;
                 // offsets from the anchor pixel: small signed integers, so a
                 // 24-bit multiply-add forms the byte offset
                 const float au = __builtin_amdgcn_fractf(su), av = __builtin_amdgcn_fractf(sv);
-                uint32_t o = (uint32_t)(__mul24(floor_i32(su), row) + (floor_i32(sv) * 8 + O0[r]));
+                uint32_t o = (uint32_t)mad_i24(floor_i32(su), row, floor_i32(sv) * 8 + O0[r]);
                 // outside the fast tiles: voxels at or behind the source, or whose
                 // taps fall beyond the zero border, add nothing (and read a safe
                 // address); near the border a rounding of the test reads zeros
