@@ -428,7 +428,9 @@ __device__ __forceinline__ float iwalk_gather(const IWalk &w, __amdgpu_buffer_rs
         acc = fmaf((float)s2.seg, v2, acc);
         v0 = load_f32(rs, idx);
         acc = fmaf((float)s3.seg, v3, acc);
-        if (s0.last || s1.last || s2.last || s3.last) break;
+        // the next crossing never moves backwards, so once one step has reached
+        // the end every later one has: the fourth step's test covers all four
+        if (s3.last) break;
     }
     return acc;
 }
