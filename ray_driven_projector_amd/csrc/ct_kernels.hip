@@ -342,24 +342,39 @@ __global__ __launch_bounds__(256) void surface_env_kernel(const double *views, S
     }
 }
 
-// First index i in [0, n) with a[i] >= x (n if none); a non-decreasing,
-// wave-uniform arguments.
-__device__ __forceinline__ int first_ge(const float *a, int n, float x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] >= x) hi = mid; else lo = mid + 1;
+// First index i in [0, n) with a[i] >= x (GT: a[i] > x), n if none; a
+// non-decreasing, wave-uniform arguments, called by the whole wave.  A 64-way
+// search: every lane probes the start of one of 64 chunks and a ballot picks
+// the chunk holding the first hit, so n <= 4096 takes two rounds of loads
+// (a binary search would take twelve dependent ones).
+template <bool GT>
+__device__ __forceinline__ int first_hit(const float *a, int n, float x, int lane) {
+    int lo = 0, len = n;   // the first hit lies in [lo, lo + len], lo + len meaning none
+    while (len > 64) {
+        const int step = (len + 63) >> 6;
+        const int i = lo + lane * step;
+        const bool in = i < lo + len;
+        const float ai = a[in ? i : 0];   // n >= 1: index 0 is always there
+        const uint64_t hit = __ballot(in && (GT ? ai > x : ai >= x));
+        const int nprobe = (len + step - 1) / step;   // lanes that probed
+        if (hit == 0ull) {
+            const int last = lo + (nprobe - 1) * step;   // every probe missed
+            len = lo + len - (last + 1);
+            lo = last + 1;
+        } else {
+            const int L = __ffsll((unsigned long long)hit) - 1;
+            const int hi = lo + L * step;                // a hit; the one before missed
+            const int nlo = L == 0 ? lo : lo + (L - 1) * step + 1;
+            len = hi - nlo;
+            lo = nlo;
+            if (len == 0) return lo;
+        }
     }
-    return lo;
-}
-// First index i in [0, n) with a[i] > x (n if none).
-__device__ __forceinline__ int first_gt(const float *a, int n, float x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] > x) hi = mid; else lo = mid + 1;
-    }
-    return lo;
+    const int i = lo + lane;
+    const bool in = lane < len;
+    const float ai = a[in ? i : 0];
+    const uint64_t hit = __ballot(in && (GT ? ai > x : ai >= x));
+    return hit == 0ull ? lo + len : lo + __ffsll((unsigned long long)hit) - 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -847,15 +862,15 @@ __device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int 
         // detector surface: the pixel ranges whose flat-plane crossings can fall in
         // the box (monotone envelopes; a margin for their float32 rounding)
         const float m = 1e-2f;
-        f.u0 = first_ge(env + U, U, umin - m);
-        f.u1 = first_gt(env, U, umax + m) - 1;
+        f.u0 = first_hit<false>(env + U, U, umin - m, lane);
+        f.u1 = first_hit<true>(env, U, umax + m, lane) - 1;
         f.v0 = V;
         f.v1 = -1;
         if (f.u0 <= f.u1) {
             for (int t = f.u0 / kEnvTile; t <= f.u1 / kEnvTile; ++t) {
                 const float *r = env + 2 * U + (size_t)t * 2 * V;
-                f.v0 = min(f.v0, first_ge(r + V, V, vmin - m));
-                f.v1 = max(f.v1, first_gt(r, V, vmax + m) - 1);
+                f.v0 = min(f.v0, first_hit<false>(r + V, V, vmin - m, lane));
+                f.v1 = max(f.v1, first_hit<true>(r, V, vmax + m, lane) - 1);
             }
         }
     } else {
@@ -878,6 +893,7 @@ __device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int 
 // order of the adds.  Float atomic adds in LDS run some 30x slower than integer
 // ones on this chip, hence the integer accumulator.
 constexpr float kPieceUnits = 8323072.f;   // 2^23 - 2^16
+constexpr int kFpCache = 1024;             // brick kernel: views whose footprints LDS keeps
 __device__ __forceinline__ unsigned long long mul24_64(uint32_t len, int y) {
     const int a = (int)(len << 8) >> 8, b = (y << 8) >> 8;   // 24-bit operands
     return (unsigned long long)((long long)a * (long long)b);
@@ -1215,6 +1231,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     constexpr int NWAVES = NT / 64;
     __shared__ unsigned long long acc[LN];
     __shared__ float wave_max[NWAVES];
+    // footprints found in pass 1, reused by pass 2 (u1 < u0: the view misses
+    // the brick); for up to kFpCache views on detectors below 2^16 pixels a
+    // side, and only where the LDS still holds the workgroups of 4 waves per SIMD
+    constexpr bool FPC = (LN * 8 + kFpCache * 8 + 1024) * (1024 / NT) <= 160 * 1024;
+    __shared__ ushort4 fpc[FPC ? kFpCache : 1];
     for (int i = threadIdx.x; i < LN; i += NT) acc[i] = 0ull;
 
     const int blk = xcd_remap(blockIdx.x, a.n_blocks);
@@ -1242,14 +1263,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
 
     // ---- pass 1: largest |y| over the rays that can meet this brick ----
     float ymax = 1.f;
+    const bool cache = FPC && MODE != BM_COLINV && a.n_views <= kFpCache && a.U < 65536 && a.V < 65536;
     if (MODE != BM_COLINV) {
         float m = 0.f;
         for (int view = wv; view < a.n_views; view += NWAVES) {
             const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
             Footprint f;
-            if (!brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
-                                 a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f))
-                continue;
+            const bool seen = brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
+                                              a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f);
+            if (cache && lane == 0)
+                fpc[view] = seen ? make_ushort4((unsigned short)f.u0, (unsigned short)f.u1,
+                                                (unsigned short)f.v0, (unsigned short)f.v1)
+                                 : make_ushort4(1, 0, 0, 0);
+            if (!seen) continue;
             const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
             const float *ysrc = a.sino + ((size_t)view * a.U + f.u0) * a.V + f.v0;
             const int step_slow = 64 / nfv, step_fast = 64 - step_slow * nfv;
@@ -1281,9 +1307,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     for (int view = wv; view < a.n_views; view += NWAVES) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
         Footprint f;
-        if (!brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
-                             a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f))
+        if (cache) {
+            const ushort4 c = fpc[view];   // written by this wave in pass 1
+            f.u0 = uni((int)c.x);
+            f.u1 = uni((int)c.y);
+            f.v0 = uni((int)c.z);
+            f.v1 = uni((int)c.w);
+            if (f.u1 < f.u0) continue;
+        } else if (!brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
+                                    a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f)) {
             continue;
+        }
         if (vw[VT_PERSP] != 0.0)
             brick_rays<LSY, LSZ, MODE, true, TWO_D, SURF>(a, vw, view, f, lane, x0, y0, z0, ex, ey,
                                                           ez, cbx, cby, cbz, S, yscale, acc);
