@@ -96,6 +96,20 @@ def test_tiny_grids_match_brute_force(beam, seed):
         assert np.max(np.abs(gb.ravel() - ref_b)) <= 1e-5 * max(1.0, np.abs(ref_b).max())
 
 
+@pytest.mark.parametrize("beam", [W.BEAM_CONE, W.BEAM_PARALLEL3D])
+def test_adjoint_beyond_the_footprint_cache(beam):
+    # 1100 views: more than the brick kernel keeps footprints for (1024), so
+    # pass 2 recomputes them; the adjoint and the SIRT update still match
+    wl = _tiny(beam, 77 + beam, vol=(9, 10, 11), det=(12, 9), views=1100,
+               jitter=0.3 if beam == W.BEAM_CONE else 0.0)
+    p = Pair(wl)
+    rng = np.random.default_rng(8)
+    y = rng.uniform(0, 1, wl.sino_shape).astype(np.float32)
+    e = rel_l2(p.AT(y), oracle.backproject(p.og, y))
+    say(f"{W.BEAM_NAMES[beam]} with 1100 views: A^T rel_l2 {e:.2e}")
+    assert e <= TOL
+
+
 @pytest.mark.parametrize("beam", [W.BEAM_CONE, W.BEAM_PARALLEL3D, W.BEAM_FAN2D])
 def test_several_tiles_with_ragged_tails(beam):
     # volume not a multiple of the 16^3 (2D: 64^2) bricks, detector not a
