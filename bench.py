@@ -22,14 +22,17 @@ acquisition with a cylindrical detector centred on the source (radius 1500,
 the parameterized-surface path).  --workload c5fdk times FDK on C5's
 acquisition (ct_fbp_filter: cosine weights, Ram-Lak ramp filter padded to 2U,
 angular weights; ct_fbp_backproject: the interpolating weighted
-backprojection) of y = A phantom; its value is voxel-view updates per second
-(512^3 voxels x 720 views per step), and both kernels are ALU-bound, so the
-roofline is against the fp32 vector peak.  --workload c1 / c2 / c3 time A + A^T
+backprojection, six launches of 120 views, each after a pair-interleaving
+copy of its views) of y = A phantom; its value is voxel-view updates per second
+(512^3 voxels x 720 views per step), and the backprojection is bound by
+instruction issue, so its roofline is against the fp32 vector peak, per launch.  --workload c1 / c2 / c3 time A + A^T
 (dense seeded A^T input) on the small configurations (2D parallel 64^2, 2D fan
 512^2, helical cone 128^3), whose throughput is reported for completeness.
 
 Roofline: algorithmic HBM bytes of the dominant kernel per launch divided by
-its average duration (HIP events on the launch stream), against 8 TB/s.
+its average duration (HIP events on the launch stream), against 8 TB/s;
+"traffic" is the HBM bytes per launch from committed rocprofv3 counter runs
+(profiles/traffic_*.json) when they were taken on the current kernel code.
 CPU baseline: the float64 oracle on a bounded sample of views, same unit.
 """
 from __future__ import annotations
