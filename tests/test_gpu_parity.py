@@ -402,6 +402,32 @@ def test_sirt_step_c4_matches_composition():
 # edge cases
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("beam", [W.BEAM_CONE, W.BEAM_PARALLEL3D, W.BEAM_FAN2D])
+def test_zero_gradient_at_the_calibrated_point(beam):
+    # The gradient of 1/2 ||A x - y||^2 is A^T (A x - y) (diffct docs,
+    # "Differentiable analytical reconstruction"); at y = A x it vanishes.  The
+    # forward is deterministic, so on the GPU the residual is exactly zero, and
+    # a SIRT step (and CGLS's r = y - A x) leave the calibrated x unchanged.
+    wl = _tiny(beam, 91 + beam, vol=(12, 13, 14), det=(17, 15), views=24,
+               jitter=0.3 if beam >= 2 else 0.0)
+    p = Pair(wl)
+    x = dev(np.random.default_rng(12).uniform(0, 1, wl.vol_shape))
+    y = torch.empty(p.g.sino_shape, device="cuda")
+    rdp.ct_project(p.g, x, y)
+    work = torch.empty(p.g.sino_shape, device="cuda")
+    ones = torch.ones(p.g.sino_shape, device="cuda")
+    rdp.ct_sirt_residual(p.g, x, y, ones, work)
+    assert torch.count_nonzero(work).item() == 0
+    r, c = torch.empty(p.g.sino_shape, device="cuda"), torch.empty(p.g.vol_shape, device="cuda")
+    rdp.ct_sirt_weights(p.g, r, c)
+    x2 = x.clone()
+    rdp.ct_sirt_step(p.g, x2, y, r, c, 1.0, work)
+    assert torch.equal(x2, x)
+    g = torch.empty(p.g.vol_shape, device="cuda")
+    rdp.ct_backproject(p.g, work, g)
+    assert torch.count_nonzero(g).item() == 0
+
+
 def test_all_rays_miss():
     wl = W.tiny_workload(W.BEAM_PARALLEL3D, (8, 8, 8), (6, 5), 4, 3)
     wl.frames[:, 3:6] += np.array([500.0, 0, 0])  # detector far to the side, rays along ~z
