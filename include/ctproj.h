@@ -335,8 +335,8 @@ typedef struct {
  * angular_weights: HOST, n_views, or NULL for the rule above.
  * A cone-beam plan also owns device staging for the backprojection: the
  * filtered sinogram of one batch of nb <= 128 views in pair-interleaved form
- * with a border of zeros (8 nb (U + 1)(V + 2) bytes; the views are split into
- * equal batches).  Backprojections
+ * with a border of zeros (8 nb (U + 1)(V + 2) bytes, at most 4 GiB unless one
+ * view alone needs more; the views are split into equal batches).  Backprojections
  * with one plan therefore share it: calls of ct_fbp_backproject or ct_fbp_run
  * with the same plan on different streams must not overlap in time.
  * Errors: CT_E_NULL, CT_E_ARG (beam, window, pad, short scan on parallel, a

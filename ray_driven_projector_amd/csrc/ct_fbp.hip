@@ -39,6 +39,7 @@ constexpr uint64_t kFbpMagic = 0x43544642'50303031ull;   // "CTFBP001"
 constexpr int kBpViews = 128;      // views whose constants one LDS batch holds
 constexpr int kBpConst = 40;       // floats per view in that batch
 constexpr int kZRun = 4;           // 3D backprojection: voxels per thread along z
+constexpr int64_t kStagingBytes = int64_t(4) << 30;   // cone backprojection staging cap
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const float *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), (short)0, (int)bytes, 0x00020000);
@@ -1115,8 +1116,11 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     if (e == hipSuccess && f->P) e = hipMalloc((void **)&f->d_tw, twf.size() * sizeof(float2));
     if (e == hipSuccess && f->P) e = hipMalloc((void **)&f->d_mul, mulf.size() * sizeof(float));
     if (!h.is2d) {
-        // equal batches of at most kBpViews views
-        const int64_t nb = (h.n_views + kBpViews - 1) / kBpViews;
+        // equal batches of at most kBpViews views, and of at most kStagingBytes
+        // of staging (large detectors take smaller batches)
+        const int64_t per_view = (h.U + 1) * (h.V + 2) * (int64_t)sizeof(float2);
+        const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(kBpViews, kStagingBytes / per_view));
+        const int64_t nb = (h.n_views + cap - 1) / cap;
         f->pair_views = (int)((h.n_views + nb - 1) / nb);
         if (e == hipSuccess)
             e = hipMalloc((void **)&f->d_pairs, (size_t)f->pair_views * (h.U + 1) * (h.V + 2) * sizeof(float2));
