@@ -20,8 +20,8 @@
 // the volume or the brick, whatever the rounding of the set-up.
 //
 // Precision.  The forward gather sets each ray up in float64 and re-bases the walk
-// every kChunk cells of the major axis, so every piece length is resolved to
-// better than 1e-5 of a cell.  The brick adjoint sets each ray up in float32 in
+// every 64 (fan/cone) or 128 (parallel) cells of the major axis, so every piece
+// length is resolved to better than 1e-5 of a cell.  The brick adjoint sets each ray up in float32 in
 // brick-local coordinates (positions within tens of voxels) and sums exact
 // integer products, so its result does not depend on the order of the adds.
 // The atomic adjoint keeps a float64 walk.
@@ -455,7 +455,9 @@ __device__ __forceinline__ float iwalk_gather(const IWalk &w, __amdgpu_buffer_rs
 // ---------------------------------------------------------------------------
 
 // Cells of the major axis covered by one chunk of the walk.
-constexpr int kChunk = 64;
+// 128 for parallel rays; fan/cone rays of one wave differ more in length, and
+// their last chunks leave more lanes idle when a chunk is long, so they take 64.
+constexpr int kChunkLog2Parallel = 7, kChunkLog2Persp = 6;
 
 // Cells of one axis for a chunk of the ray.  On the major axis the chunk's first
 // cell and cell count are known exactly; a chunk after the first starts on a
@@ -491,12 +493,12 @@ __device__ __forceinline__ void fix_axis(double d, double L, double S, int ncr, 
 }
 
 // Line integral of the ray o + t d, t in [tin, tout] (inside the box), with the
-// walk re-based every kChunk cells of the major axis.
+// walk re-based every 2^clog2 cells of the major axis (2^31 walk units per chunk).
 __device__ __forceinline__ float project_ray(double ox, double oy, double oz, double dx, double dy,
                                              double dz, double tin, double tout, int nx, int ny,
                                              int nz, double spx, double spy, double spz,
                                              uint32_t ex, uint32_t ey, uint32_t ez,
-                                             __amdgpu_buffer_rsrc_t rs) {
+                                             __amdgpu_buffer_rsrc_t rs, int clog2) {
     const double px = dx * spx, py = dy * spy, pz = dz * spz;
     const double L = sqrt(px * px + py * py + pz * pz);
     const double ax = fabs(dx), ay = fabs(dy), az = fabs(dz);
@@ -511,14 +513,15 @@ __device__ __forceinline__ float project_ray(double ox, double oy, double oz, do
     cin = min(max(cin, 0), nM - 1);
     cout = min(max(cout, 0), nM - 1);
     const int ncell = max((cout - cin) * sgn, 0) + 1;
-    const int nch = (ncell + kChunk - 1) / kChunk;
+    const int chunk = 1 << clog2;
+    const int nch = (ncell + chunk - 1) >> clog2;
     // (ex, ey, ez): element strides of x, y, z in the volume copy being read
     const uint32_t sx = ex * 4u, sy = ey * 4u, sz = ez * 4u;
     float total = 0.f;
     double ta = tin;
     for (int ch = 0; ch < nch; ++ch) {
-        const int first = cin + sgn * ch * kChunk;
-        const int cells = min(kChunk, ncell - ch * kChunk);
+        const int first = cin + sgn * (ch << clog2);
+        const int cells = min(chunk, ncell - (ch << clog2));
         double tb = tout;
         if (ch != nch - 1) {
             const int P = sgn > 0 ? first + cells : first - cells + 1;
@@ -530,17 +533,17 @@ __device__ __forceinline__ float project_ray(double ox, double oy, double oz, do
         chunk_axis(oy, dy, ta, tb, ny, M == 1, first, cells, ch == 0, cy, nyc, ddy);
         chunk_axis(oz, dz, ta, tb, nz, M == 2, first, cells, ch == 0, cz, nzc, ddz);
         const double chord = (tb - ta) * L;
-        const double S = 0x1p30 / chord;   // walk units per length unit
+        const double S = 0x1p31 / chord;   // walk units per length unit
         IWalk w;
         w.idx = (uint32_t)cx * sx + (uint32_t)cy * sy + (uint32_t)cz * sz;
         w.stx = dx > 0.0 ? sx : 0u - sx;
         w.sty = dy > 0.0 ? sy : 0u - sy;
         w.stz = dz > 0.0 ? sz : 0u - sz;
-        w.lend = 1u << 30;
+        w.lend = 1u << 31;
         fix_axis(dx, L, S, nxc, ddx, w.lx, w.qx, w.lend);
         fix_axis(dy, L, S, nyc, ddy, w.ly, w.qy, w.lend);
         fix_axis(dz, L, S, nzc, ddz, w.lz, w.qz, w.lend);
-        total = fmaf(iwalk_gather(w, rs), (float)(chord * 0x1p-30), total);
+        total = fmaf(iwalk_gather(w, rs), (float)(chord * 0x1p-31), total);
         ta = tb;
     }
     return total;
@@ -665,7 +668,8 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
                 const uint32_t ez = layout == 0 ? W * H : (layout == 1 ? W * H : 1u);
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, a.vol_bytes);
                 acc = project_ray(ox, oy, oz, dx, dy, dz, tin, tout, a.W, a.H, a.D, a.spx, a.spy,
-                                  a.spz, ex, ey, ez, rs);
+                                  a.spz, ex, ey, ez, rs,
+                                  vw[VT_PERSP] != 0.0 ? kChunkLog2Persp : kChunkLog2Parallel);
             }
             if (MODE == RM_PROJECT || MODE == RM_PROJECT_SQ) {
                 if (MODE == RM_PROJECT && a.accumulate) acc += a.out[ray];
