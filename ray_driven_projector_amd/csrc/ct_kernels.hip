@@ -403,16 +403,19 @@ __device__ __forceinline__ GStep gstep(const IWalk &w, uint32_t &idx, uint32_t &
     const uint32_t qx = w.qx, qy = w.qy, qz = w.qz, sx = w.stx, sy = w.sty, sz = w.stz;
     const uint32_t tmin = umin3(lx, ly, lz);
     const uint32_t tn = min(tmin, w.lend);
-    const bool bx = lx == tmin;
-    const bool by = !bx && ly == tmin;
-    const bool bz = !bx && !by;
+    // the step masks are combined as wave masks, on the scalar unit
+    const uint64_t mx = __builtin_amdgcn_ballot_w64(lx == tmin);
+    const uint64_t my = __builtin_amdgcn_ballot_w64(ly == tmin) & ~mx;
+    const bool bx = __builtin_amdgcn_inverse_ballot_w64(mx);
+    const bool by = __builtin_amdgcn_inverse_ballot_w64(my);
+    const bool bxy = __builtin_amdgcn_inverse_ballot_w64(mx | my);
     const uint32_t nx = __builtin_elementwise_add_sat(lx, qx);
     const uint32_t ny = __builtin_elementwise_add_sat(ly, qy);
     const uint32_t nz = __builtin_elementwise_add_sat(lz, qz);
     const uint32_t syz = by ? sy : sz;
     lx = bx ? nx : lx;
     ly = by ? ny : ly;
-    lz = bz ? nz : lz;
+    lz = bxy ? lz : nz;
     idx += bx ? sx : syz;
     GStep g{tn - lc, tmin >= w.lend};
     lc = tn;
@@ -914,16 +917,19 @@ __device__ __forceinline__ void lds_add(unsigned long long *lds, uint32_t byte_o
 __device__ __forceinline__ void sadvance(uint32_t qx, uint32_t qy, uint32_t qz, uint32_t sx,
                                          uint32_t sy, uint32_t sz, uint32_t t, uint32_t &idx,
                                          uint32_t &lx, uint32_t &ly, uint32_t &lz) {
-    const bool bx = lx == t;
-    const bool by = !bx && ly == t;
-    const bool bz = !bx && !by;
+    // the step masks are combined as wave masks, on the scalar unit
+    const uint64_t mx = __builtin_amdgcn_ballot_w64(lx == t);
+    const uint64_t my = __builtin_amdgcn_ballot_w64(ly == t) & ~mx;
+    const bool bx = __builtin_amdgcn_inverse_ballot_w64(mx);
+    const bool by = __builtin_amdgcn_inverse_ballot_w64(my);
+    const bool bxy = __builtin_amdgcn_inverse_ballot_w64(mx | my);
     const uint32_t nx = __builtin_elementwise_add_sat(lx, qx);
     const uint32_t ny = __builtin_elementwise_add_sat(ly, qy);
     const uint32_t nz = __builtin_elementwise_add_sat(lz, qz);
     const uint32_t syz = by ? sy : sz;   // values, not field addresses: no table in memory
     lx = bx ? nx : lx;
     ly = by ? ny : ly;
-    lz = bz ? nz : lz;
+    lz = bxy ? lz : nz;
     idx += bx ? sx : syz;
 }
 // Two pieces per iteration with one exit test: the loop is entered only while the
