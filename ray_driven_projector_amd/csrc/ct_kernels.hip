@@ -1008,6 +1008,34 @@ __device__ __forceinline__ DirPlan dir_plan(float dx, float dy, float dz, float 
     return p;
 }
 
+// The same for a direction already mirrored to positive components, none of
+// them near zero (the caller has shown both for every ray of the footprint);
+// signs and strides are then the caller's, once per footprint.
+template <bool TWO_D>
+__device__ __forceinline__ DirPlan dir_plan_pos(float ax, float ay, float az, float spx, float spy,
+                                                float spz, float S) {
+    DirPlan p;
+    if (TWO_D) az = 0.f;
+    p.slow = false;
+    p.nx = p.ny = p.nz = false;
+    p.axx = ax;
+    p.ayy = ay;
+    p.azz = az;
+    p.ix = __builtin_amdgcn_rcpf(ax);
+    p.iy = __builtin_amdgcn_rcpf(ay);
+    p.iz = TWO_D ? 0.f : __builtin_amdgcn_rcpf(az);
+    const float px = ax * spx, py = ay * spy, pz = az * spz;
+    p.LS = __builtin_amdgcn_sqrtf(px * px + py * py + pz * pz) * S;
+    p.qfx = p.LS * p.ix;
+    p.qfy = p.LS * p.iy;
+    p.qfz = p.LS * p.iz;
+    p.qx = sat_u32(p.qfx);
+    p.qy = sat_u32(p.qfy);
+    p.qz = TWO_D ? 0xFFFFFFFFu : sat_u32(p.qfz);
+    p.stx = p.sty = p.stz = 0u;
+    return p;
+}
+
 // Walk every ray of one view's footprint through the brick.  PERSP: fan/cone
 // rays (direction per ray); otherwise parallel rays, whose direction and all
 // that is derived from it are the same for the whole footprint and computed
@@ -1097,6 +1125,57 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         return PERSP ? k : hs + ((k & 1) ? -((k + 1) >> 1) : (k >> 1));
     };
     const float af = (float)(ufast ? cu : cv), as_ = (float)(ufast ? cv : cu);
+    // Fan/cone rays on a flat detector: each direction component is affine in
+    // the ray's (fast, slow) pixel offsets, so over the footprint it takes its
+    // extremes at the four corners.  Where every component keeps one sign at
+    // the corners with a margin (2^-20 of the largest sum of term magnitudes,
+    // far above the rounding of the per-ray sums, about 2^-23 of it, and above
+    // the direction plan's near-zero threshold), the footprint is walked with
+    // its coefficients mirrored once to positive directions: the signs, the
+    // mirroring and the strides are then settled per footprint, not per ray.
+    // Mirroring negates operands, which is exact, so the walks are unchanged.
+    bool fsign = false;
+    float mDx = Dx, mDy = Dy, mDz = Dz, mDFx = DFx, mDFy = DFy, mDFz = DFz, mDSx = DSx, mDSy = DSy,
+          mDSz = DSz;
+    float kx = 8.f, ky = (float)(8 * LSY), kz = (float)(8 * LSZ), k0 = 0.f;
+    uint32_t fstx = 0, fsty = 0, fstz = 0;
+    if (PERSP && !SURF && nrays > 0) {
+        const int nrow = nrays / nf;
+        const float f0 = -af, f1 = (float)(nf - 1) - af, s0 = -as_, s1 = (float)(nrow - 1) - as_;
+        const float fm = fmaxf(fabsf(f0), fabsf(f1)), sm = fmaxf(fabsf(s0), fabsf(s1));
+        const float Tx = fabsf(Dx) + fm * fabsf(DFx) + sm * fabsf(DSx);
+        const float Ty = fabsf(Dy) + fm * fabsf(DFy) + sm * fabsf(DSy);
+        const float Tz = TWO_D ? 0.f : fabsf(Dz) + fm * fabsf(DFz) + sm * fabsf(DSz);
+        const float thr = 0x1p-20f * fmaxf(Tx, fmaxf(Ty, Tz));
+        const auto sgn = [&](float D, float DF, float DS) {
+            const float c00 = fmaf(s0, DS, fmaf(f0, DF, D)), c10 = fmaf(s0, DS, fmaf(f1, DF, D));
+            const float c01 = fmaf(s1, DS, fmaf(f0, DF, D)), c11 = fmaf(s1, DS, fmaf(f1, DF, D));
+            const float lo = fminf(fminf(c00, c10), fminf(c01, c11));
+            const float hi = fmaxf(fmaxf(c00, c10), fmaxf(c01, c11));
+            return lo > thr ? 1.f : (hi < -thr ? -1.f : 0.f);
+        };
+        const float sgx = sgn(Dx, DFx, DSx), sgy = sgn(Dy, DFy, DSy);
+        const float sgz = TWO_D ? 1.f : sgn(Dz, DFz, DSz);
+        fsign = sgx != 0.f && sgy != 0.f && sgz != 0.f;
+        if (fsign) {
+            mDx = sgx * Dx; mDFx = sgx * DFx; mDSx = sgx * DSx;
+            mDy = sgy * Dy; mDFy = sgy * DFy; mDSy = sgy * DSy;
+            mDz = sgz * Dz; mDFz = sgz * DFz; mDSz = sgz * DSz;
+            mA0x = sgx * A0x; mAfx = sgx * Afx; mAsx = sgx * Asx;
+            mA0y = sgy * A0y; mAfy = sgy * Afy; mAsy = sgy * Asy;
+            mA0z = sgz * A0z; mAfz = sgz * Afz; mAsz = sgz * Asz;
+            // cell offset from the mirrored cell indices: c for a positive
+            // axis, e - 1 - c for a mirrored one
+            kx = 8.f * sgx;
+            ky = (float)(8 * LSY) * sgy;
+            kz = (float)(8 * LSZ) * sgz;
+            k0 = (sgx < 0.f ? 8.f * (fex - 1.f) : 0.f) + (sgy < 0.f ? (float)(8 * LSY) * (fey - 1.f) : 0.f) +
+                 (sgz < 0.f ? (float)(8 * LSZ) * (fez - 1.f) : 0.f);
+            fstx = in_vgpr(sgx < 0.f ? (uint32_t)-8 : 8u);
+            fsty = in_vgpr(sgy < 0.f ? (uint32_t)(-8 * LSY) : (uint32_t)(8 * LSY));
+            fstz = in_vgpr(TWO_D ? 0u : (sgz < 0.f ? (uint32_t)(-8 * LSZ) : (uint32_t)(8 * LSZ)));
+        }
+    }
     int lk = lane / nf, lf = lane - lk * nf;
     uint32_t yo = __umul24(lf, yfs) + __umul24(srow(lk), yss);   // offsets < 2^24, products < 2^31
     float ynext = 1.f;
@@ -1120,6 +1199,8 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
                                (size_t)u0 * a.V + v0);
         if (lane < nrays) { o0n = ob[3 * yo]; o1n = ob[3 * yo + 1]; o2n = ob[3 * yo + 2]; }
     }
+    const auto walk_rays = [&](auto fs_tag) {
+    constexpr bool FS = decltype(fs_tag)::value;   // mirrored fan/cone footprint
     for (int r = lane; r < nrays; r += 64) {
         const float cf = (float)lf - af, cs = (float)srow(lk) - as_;
         lf += step_fast;
@@ -1142,6 +1223,14 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
             mx = fmaf(cs, mAsx, fmaf(cf, mAfx, mA0x));
             my = fmaf(cs, mAsy, fmaf(cf, mAfy, mA0y));
             mz = TWO_D ? mA0z : fmaf(cs, mAsz, fmaf(cf, mAfz, mA0z));
+            t0 = tv0;
+            t1 = tv1;
+        } else if (FS) {
+            mx = fmaf(cs, mAsx, fmaf(cf, mAfx, mA0x));
+            my = fmaf(cs, mAsy, fmaf(cf, mAfy, mA0y));
+            mz = TWO_D ? mA0z : fmaf(cs, mAsz, fmaf(cf, mAfz, mA0z));
+            dp = dir_plan_pos<TWO_D>(fmaf(cs, mDSx, fmaf(cf, mDFx, mDx)), fmaf(cs, mDSy, fmaf(cf, mDFy, mDy)),
+                                     fmaf(cs, mDSz, fmaf(cf, mDFz, mDz)), spx, spy, spz, S);
             t0 = tv0;
             t1 = tv1;
         } else {
@@ -1191,7 +1280,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         }
         // slab clip: lo = (-h - m) / a, hi = (h - m) / a
         float cx = mx, cy = my, cz = mz, cix = dp.ix, ciy = dp.iy, ciz = dp.iz;
-        if (dp.slow) {
+        if (!FS && dp.slow) {
             bclip_zero(mx, dp.axx, hx, cx, cix);
             bclip_zero(my, dp.ayy, hy, cy, ciy);
             if (!TWO_D) bclip_zero(mz, dp.azz, hz, cz, ciz);
@@ -1217,15 +1306,29 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         // brick) or at the first far-face crossing, whichever comes first
         w.lend = min(sat_u32((tout - tin) * dp.LS), min(min(farx, fary), farz));
         // back to real cell indices (exact small integers in float) and strides
-        const float rcx = dp.nx ? fex - 1.f - fcx : fcx;
-        const float rcy = dp.ny ? fey - 1.f - fcy : fcy;
-        const float rcz = dp.nz ? fez - 1.f - fcz : fcz;
-        w.idx = (uint32_t)fmaf(rcz, (float)(8 * LSZ), fmaf(rcy, (float)(8 * LSY), rcx * 8.f));
-        w.stx = in_vgpr(dp.stx);
-        w.sty = in_vgpr(dp.sty);
-        w.stz = in_vgpr(dp.stz);
+        if (FS) {
+            w.idx = (uint32_t)fmaf(fcz, kz, fmaf(fcy, ky, fmaf(fcx, kx, k0)));
+            w.stx = fstx;
+            w.sty = fsty;
+            w.stz = fstz;
+        } else {
+            const float rcx = dp.nx ? fex - 1.f - fcx : fcx;
+            const float rcy = dp.ny ? fey - 1.f - fcy : fcy;
+            const float rcz = dp.nz ? fez - 1.f - fcz : fcz;
+            w.idx = (uint32_t)fmaf(rcz, (float)(8 * LSZ), fmaf(rcy, (float)(8 * LSY), rcx * 8.f));
+            w.stx = in_vgpr(dp.stx);
+            w.sty = in_vgpr(dp.sty);
+            w.stz = in_vgpr(dp.stz);
+        }
         const int Y = (int)rintf(__builtin_amdgcn_fmed3f(yv * yscale, -8388607.f, 8388607.f));
         iwalk_scatter_fix(w, acc, Y);
+    }
+    };
+    if constexpr (PERSP && !SURF) {
+        if (fsign) walk_rays(std::true_type{});
+        else walk_rays(std::false_type{});
+    } else {
+        walk_rays(std::false_type{});
     }
 }
 
