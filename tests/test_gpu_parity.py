@@ -456,6 +456,34 @@ def test_rays_on_lattice_planes_follow_half_open_cells():
     assert rel_l2(p.AT(y, atomic=True), ob) <= TOL
 
 
+@pytest.mark.parametrize("beam", [W.BEAM_FAN2D, W.BEAM_CONE])
+@pytest.mark.parametrize("n", [23, 24])
+def test_fan_cone_rays_with_zero_direction_components(beam, n):
+    # four views exactly along the axes (frames rounded, so cos and sin are 0 or
+    # +-1) and an odd, centred detector: the central rays have direction
+    # components that are exactly zero.  Footprints that straddle an axis plane
+    # take the per-ray sign handling and the near-zero clip, the others the
+    # footprint-wide mirroring; an even volume puts the central rays on lattice
+    # planes (half-open cells).
+    if beam == W.BEAM_CONE:
+        fr = np.round(W.helix_cone(4, 40.0, 70.0, 0.0), 12)
+        vol, det = (n, n, n), (31, 29)
+    else:
+        fr = np.round(W.circular_fan2d(4, 40.0, 70.0), 12)
+        vol, det = (1, n, n), (31, 1)
+    assert np.all((fr == 0.0) | (np.abs(fr) >= 1.0))
+    wl = W.Workload(f"axis views {n}", beam, vol, (1.0, 1.0, 1.0), det, (1.0, 1.0), fr)
+    say("axis views", W.BEAM_NAMES[beam], n)
+    p = Pair(wl)
+    rng = np.random.default_rng(11 + n)
+    x = rng.uniform(0, 1, wl.vol_shape).astype(np.float32)
+    y = rng.uniform(0, 1, wl.sino_shape).astype(np.float32)
+    assert rel_l2(p.A(x), oracle.project(p.og, x)) <= TOL
+    ob = oracle.backproject(p.og, y)
+    assert rel_l2(p.AT(y), ob) <= TOL
+    assert rel_l2(p.AT(y, atomic=True), ob) <= TOL
+
+
 @pytest.mark.parametrize("where", ["source_inside", "detector_inside"])
 def test_cone_segment_ends_inside_volume(where):
     fr = W.helix_cone(9, 30.0, 50.0, 0.0)
