@@ -341,7 +341,8 @@ typedef struct {
  * with the same plan on different streams must not overlap in time.
  * Errors: CT_E_NULL, CT_E_ARG (beam, window, pad, short scan on parallel, a
  * span too short, an isocentre that cannot be estimated), CT_E_SHAPE,
- * CT_E_RANGE, CT_E_NONFINITE, CT_E_NOMEM, CT_E_HIP. */
+ * CT_E_RANGE (also a cone detector with (U + 1)(V + 2) >= 2^29, whose one-view
+ * staging would pass 32-bit byte offsets), CT_E_NONFINITE, CT_E_NOMEM, CT_E_HIP. */
 ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles,
                           const double *angular_weights, const ct_fbp_opts_t *opts, ct_fbp_t *out);
 ct_status_t ct_fbp_destroy(ct_fbp_t f);

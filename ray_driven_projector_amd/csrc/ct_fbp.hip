@@ -905,6 +905,9 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     if (h.D * h.H * h.W >= (int64_t(1) << 30) || h.n_views * h.U * h.V >= (int64_t(1) << 31) ||
         h.U * h.V >= (int64_t(1) << 30))
         return ffail(CT_E_RANGE, "volume or sinogram too large for one buffer");
+    // cone staging: one view's (U + 1)(V + 2) 8-byte pairs take 32-bit byte offsets
+    if (h.beam == CT_CONE && (h.U + 1) * (h.V + 2) >= (int64_t(1) << 29))
+        return ffail(CT_E_RANGE, "cone detector too large: (U + 1)(V + 2) must be < 2^29");
     if (!angular_weights && !angles) return ffail(CT_E_NULL, "angles (or angular_weights) must be given");
     if (opts->short_scan && !angles) return ffail(CT_E_NULL, "short scans need the angles");
     const int64_t nv = h.n_views;
