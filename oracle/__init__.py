@@ -27,13 +27,22 @@ _SRC = os.path.join(_HERE, "ct_oracle.c")
 _LIB = os.path.join(_HERE, "libctoracle.so")
 
 
+# plain gcc, IEEE float64: no contraction into fused multiply-adds, no fast math
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
+
+
+def compile_library(src: str, out: str, extra=()) -> str:
+    """Compile one oracle C source into a shared library at `out`."""
+    cmd = ["gcc", *CFLAGS, *extra, "-I", _HERE, "-o", out + ".tmp", src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build(force: bool = True) -> str:
-    """Compile ct_oracle.c into libctoracle.so (plain gcc, IEEE float64)."""
+    """Compile ct_oracle.c into libctoracle.so."""
     if force or not os.path.exists(_LIB):
-        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-               "-fPIC", "-shared", "-pthread", "-o", _LIB + ".tmp", _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(_LIB + ".tmp", _LIB)
+        compile_library(_SRC, _LIB)
     return _LIB
 
 
@@ -55,27 +64,32 @@ class _Ray(ctypes.Structure):
 _lib = None
 
 
+def bind(L):
+    """Declare the C signatures on a loaded copy of the oracle library."""
+    P = ctypes.POINTER
+    dp = P(ctypes.c_double)
+    ip = P(ctypes.c_int64)
+    L.ora_ray_of.argtypes = [P(_Geom), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P(_Ray)]
+    L.ora_box_chord.argtypes = [P(_Ray), dp, dp]
+    L.ora_box_chord.restype = ctypes.c_double
+    L.ora_trace.argtypes = [P(_Geom), P(_Ray), dp, ip, ip]
+    L.ora_trace.restype = ctypes.c_double
+    L.ora_project.argtypes = [P(_Geom), dp, dp, ctypes.c_int, ip, ip]
+    L.ora_project_rays.argtypes = [P(_Geom), dp, ip, ctypes.c_int64, dp, ip, ctypes.c_int]
+    L.ora_backproject.argtypes = [P(_Geom), dp, dp, ctypes.c_int]
+    L.ora_brute_matrix.argtypes = [P(_Geom), dp]
+    L.ora_column_dot.argtypes = [P(_Geom), ctypes.c_int64, dp, ctypes.c_int]
+    L.ora_column_dot.restype = ctypes.c_double
+    L.ora_row_chords.argtypes = [P(_Geom), dp, ctypes.c_int]
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
-        L = ctypes.CDLL(_LIB)
-        P = ctypes.POINTER
-        dp = P(ctypes.c_double)
-        ip = P(ctypes.c_int64)
-        L.ora_ray_of.argtypes = [P(_Geom), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P(_Ray)]
-        L.ora_box_chord.argtypes = [P(_Ray), dp, dp]
-        L.ora_box_chord.restype = ctypes.c_double
-        L.ora_trace.argtypes = [P(_Geom), P(_Ray), dp, ip, ip]
-        L.ora_trace.restype = ctypes.c_double
-        L.ora_project.argtypes = [P(_Geom), dp, dp, ctypes.c_int, ip, ip]
-        L.ora_project_rays.argtypes = [P(_Geom), dp, ip, ctypes.c_int64, dp, ip, ctypes.c_int]
-        L.ora_backproject.argtypes = [P(_Geom), dp, dp, ctypes.c_int]
-        L.ora_brute_matrix.argtypes = [P(_Geom), dp]
-        L.ora_column_dot.argtypes = [P(_Geom), ctypes.c_int64, dp, ctypes.c_int]
-        L.ora_column_dot.restype = ctypes.c_double
-        _lib = L
+        _lib = bind(ctypes.CDLL(_LIB))
     return _lib
 
 
@@ -177,6 +191,13 @@ def backproject(g: Geometry, sino, nthreads: int | None = None) -> np.ndarray:
     y = _as64(sino).reshape(g.sino_shape)
     out = np.zeros(g.vol_shape, dtype=np.float64)
     lib().ora_backproject(ctypes.byref(g._g), _dptr(y), _dptr(out), nthreads or default_threads())
+    return out
+
+
+def row_chords(g: Geometry, nthreads: int | None = None) -> np.ndarray:
+    """Per ray, the chord of the whole volume box: the row sums A 1 in closed form."""
+    out = np.zeros(g.sino_shape, dtype=np.float64)
+    lib().ora_row_chords(ctypes.byref(g._g), _dptr(out), nthreads or default_threads())
     return out
 
 

@@ -314,6 +314,36 @@ int ora_project_rays(const ora_geom *g, const double *vol, const int64_t *ray_id
     return 0;
 }
 
+typedef struct {
+    const ora_geom *g;
+    double *out;
+} chord_ctx;
+
+static void chord_views(void *p, int64_t v0, int64_t v1, int tid)
+{
+    chord_ctx *c = (chord_ctx *)p;
+    const ora_geom *g = c->g;
+    int64_t n[3];
+    double s[3], lo[3], hi[3];
+    (void)tid;
+    lattice(g, n, s, lo, hi);
+    for (int64_t view = v0; view < v1; ++view)
+        for (int64_t u = 0; u < g->nu; ++u)
+            for (int64_t v = 0; v < g->nv; ++v) {
+                ora_ray r;
+                ora_ray_of(g, view, u, v, &r);
+                c->out[(view * g->nu + u) * g->nv + v] = ora_box_chord(&r, lo, hi);
+            }
+}
+
+int ora_row_chords(const ora_geom *g, double *out, int nthreads)
+{
+    chord_ctx c;
+    c.g = g; c.out = out;
+    run_parallel(nthreads, g->n_views, chord_views, &c);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* adjoint: merged plane-crossing lists (Siddon's alpha sets)           */
 /* ------------------------------------------------------------------ */

@@ -78,6 +78,11 @@ int ora_project_rays(const ora_geom *g, const double *vol, const int64_t *ray_id
  * skipped. */
 int ora_backproject(const ora_geom *g, const double *sino, double *vol, int nthreads);
 
+/* Row sums of A in closed form: for every ray, the length of its chord through
+ * the whole volume box (slab method), out[(view * nu + u) * nv + v].  Equals
+ * A 1 up to rounding, without walking the cells.  Returns 0. */
+int ora_row_chords(const ora_geom *g, double *out, int nthreads);
+
 /* Dense matrix A (n_rays x n_voxels) by per-cell chords: tiny grids only. */
 int ora_brute_matrix(const ora_geom *g, double *A);
 

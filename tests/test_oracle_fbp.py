@@ -275,3 +275,72 @@ def test_isocentre_of_a_shifted_orbit():
     fr[:, 3:6] += shift
     wl = W.Workload("c", W.BEAM_CONE, (4, 8, 8), (1, 1, 1), (8, 8), (1, 1), fr)
     assert np.allclose(F.isocentre(wl)[:2], shift[:2], atol=1e-9)
+
+
+# ---- the sampled-voxel gather and the cosine window ----
+
+@pytest.mark.parametrize("beam", [W.BEAM_PARALLEL2D, W.BEAM_FAN2D, W.BEAM_CONE])
+def test_weighted_backproject_voxels_is_the_whole_gather_at_those_voxels(beam):
+    """weighted_backproject_voxels over every voxel id, shuffled, returns the
+    whole gather's values at those ids (id = (z * H + y) * W + x); anisotropic
+    voxels and a detector that does not cover the volume (taps off the
+    detector, voxels seen by no view) are included."""
+    vol = (1, 9, 11) if beam != W.BEAM_CONE else (6, 9, 11)
+    det = (13, 1) if beam != W.BEAM_CONE else (13, 7)
+    wl = W.tiny_workload(beam, vol, det, 7, 19, det_spacing=(0.9, 0.8), sid=25.0, sdd=40.0)
+    wl = W.Workload(wl.name, wl.beam, wl.vol_shape, (1.3, 0.7, 1.1), wl.det_shape, wl.det_spacing,
+                    wl.frames)
+    q = np.random.default_rng(beam).standard_normal(wl.sino_shape)
+    full = F.weighted_backproject(wl, q)
+    ids = np.random.default_rng(2).permutation(int(np.prod(wl.vol_shape)))
+    got = F.weighted_backproject_voxels(wl, q, ids)
+    np.testing.assert_allclose(got, full.ravel()[ids], rtol=1e-13, atol=1e-13)
+    # one voxel by hand: the coefficient of q[i, u, v] is the voxel's entry of the
+    # transpose applied to a unit sinogram
+    j = int(ids[0])
+    e = np.zeros(wl.sino_shape)
+    i, u, v = 3, wl.det_shape[0] // 2, wl.det_shape[1] // 2
+    e[i, u, v] = 1.0
+    col = F.weighted_backproject_T(wl, np.eye(1, int(np.prod(wl.vol_shape)), j).reshape(wl.vol_shape))
+    assert abs(F.weighted_backproject_voxels(wl, e, [j])[0] - col[i, u, v]) < 1e-13
+
+
+def test_cosine_window_is_the_ramp_averaged_at_half_samples():
+    """The cosine window multiplies the spectrum by cos(pi k / P), i.e. it
+    averages the filter's impulse response shifted by +1/2 and -1/2 sample.
+    The band-limited ramp of bandwidth 1/(2d) has the closed-form impulse
+    response h(t) = sin(pi t/d) / (2 pi d t) + (cos(pi t/d) - 1) / (2 pi^2 t^2)
+    (whose samples at t = n d are the Ram-Lak taps), so the cosine-windowed
+    taps are (h((n - 1/2) d) + h((n + 1/2) d)) / 2, up to the P-periodic
+    truncation of the kernel (an error of order 1 / (pi^2 d^2 P))."""
+    P, d = 4096, 0.8
+
+    def h(t):
+        return np.sin(math.pi * t / d) / (2 * math.pi * d * t) + (np.cos(math.pi * t / d) - 1) / (
+            2 * math.pi ** 2 * t ** 2)
+
+    n = np.arange(-40, 41)
+    expect = 0.5 * (h((n - 0.5) * d) + h((n + 0.5) * d))
+    M = F.ramp_multiplier(P, d, "cosine")
+    taps = np.fft.irfft(M, n=P) / d
+    got = taps[n % P]
+    scale = 1.0 / (4 * d * d)                 # the ramp's peak tap
+    assert np.max(np.abs(got - expect)) < 2.0 / (math.pi ** 2 * d * d * P) + 1e-12 * scale
+    # the closed form reproduces the Ram-Lak taps at the samples themselves
+    m = np.arange(1, 40)
+    ramlak = F.ramlak_kernel(P, d)
+    assert np.allclose(h(m * d), ramlak[m], rtol=0, atol=1e-15 * scale)
+    # unit gain at DC, zero at Nyquist, non-negative in between
+    w = M / F.ramp_multiplier(P, d, "ram-lak")
+    assert abs(w[0] - 1) < 1e-12 and abs(w[-1]) < 1e-12 and np.all(w >= -1e-15)
+
+
+def test_cosine_window_squared_is_hann():
+    """cos^2(pi f) = (1 + cos 2 pi f) / 2: the cosine multiplier squared is the
+    Hann multiplier (pinned above by its 3-tap smoothing) times Ram-Lak's."""
+    for P, d in ((256, 0.7), (1000, 1.3)):
+        Mc = F.ramp_multiplier(P, d, "cosine")
+        Mh = F.ramp_multiplier(P, d, "hann")
+        Mr = F.ramp_multiplier(P, d, "ram-lak")
+        assert np.max(np.abs(Mc * Mc - Mh * Mr)) < 1e-12 * np.max(Mr) ** 2
+        assert np.all(Mc >= 0)

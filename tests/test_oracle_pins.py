@@ -478,3 +478,77 @@ def test_source_centred_cylinder_geometry(two_d):
                 dn, du_ = d @ n, d @ eu
                 assert abs(math.hypot(dn, du_) - sdd) < 1e-9
                 assert abs(math.atan2(du_, dn) - up / sdd) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# selected rays, per-ray counts and closed-form row sums
+# ---------------------------------------------------------------------------
+
+def _with_cylinder(wl):
+    two_d = wl.beam in (W.BEAM_PARALLEL2D, W.BEAM_FAN2D)
+    off = W.cylinder_offsets(wl.det_shape, wl.det_spacing, 40.0, two_d=two_d)
+    return W.with_surface(wl, off, "cylinder")
+
+
+@pytest.mark.parametrize("surface", [False, True])
+@pytest.mark.parametrize("beam", ALL_BEAMS)
+def test_project_rays_is_project_at_those_rays(beam, surface):
+    """oracle.project_rays over every ray id, in a shuffled order, returns the
+    whole projection's values at those ids (the id is (view * U + u) * V + v),
+    and its per-ray intersection counts are the nonzeros of each row of the
+    brute-force matrix and add up to the whole projection's count."""
+    wl = _tiny(beam, 41, vol=(5, 6, 7), det=(9, 5), views=6)
+    if surface:
+        wl = _with_cylinder(wl)
+    g = oracle.Geometry.from_workload(wl)
+    x = np.random.default_rng(beam + 10 * surface).uniform(0.1, 1.0, wl.vol_shape)
+    full, nnz, _ = oracle.project(g, x, with_counts=True)
+    ids = np.random.default_rng(7).permutation(g.n_rays)
+    vals, cnt = oracle.project_rays(g, x, ids, with_counts=True)
+    np.testing.assert_array_equal(vals, full.ravel()[ids])
+    assert int(cnt.sum()) == nnz
+    A = oracle.brute_matrix(g)
+    np.testing.assert_array_equal(cnt, (A > 0).sum(axis=1)[ids])
+    # the values are the rows of the matrix applied to x
+    np.testing.assert_allclose(vals, (A @ x.ravel())[ids], rtol=1e-12, atol=1e-12)
+    # a strided subset with repeats
+    sub = np.concatenate([ids[::5], ids[:3]])
+    np.testing.assert_array_equal(oracle.project_rays(g, x, sub), full.ravel()[sub])
+
+
+def test_project_rays_on_a_workload_sample():
+    """The same on C2's acquisition (512^2 fan beam): 2 000 sampled rays."""
+    wl = W.make_workload(2)
+    g = oracle.Geometry.from_workload(wl)
+    x = W.make_phantom(wl)
+    full, nnz, _ = oracle.project(g, x, with_counts=True)
+    ids = np.random.default_rng(3).choice(g.n_rays, 2000, replace=False)
+    vals, cnt = oracle.project_rays(g, x, ids, with_counts=True)
+    np.testing.assert_array_equal(vals, full.ravel()[ids])
+    all_vals, all_cnt = oracle.project_rays(g, np.zeros(wl.vol_shape), np.arange(g.n_rays),
+                                            with_counts=True)
+    assert int(all_cnt.sum()) == nnz and not np.any(all_vals)
+    np.testing.assert_array_equal(cnt, all_cnt[ids])
+
+
+@pytest.mark.parametrize("surface", [False, True])
+@pytest.mark.parametrize("beam", ALL_BEAMS)
+def test_row_chords_are_the_row_sums(beam, surface):
+    """oracle.row_chords: the brute-force matrix's row sums, and per ray the
+    face-rectangle chord of the whole volume box."""
+    wl = _tiny(beam, 43, vol=(4, 6, 5), det=(8, 5), views=5)
+    if surface:
+        wl = _with_cylinder(wl)
+    g = oracle.Geometry.from_workload(wl)
+    rc = oracle.row_chords(g)
+    A = oracle.brute_matrix(g)
+    np.testing.assert_allclose(rc.ravel(), A.sum(axis=1), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rc, oracle.project(g, np.ones(wl.vol_shape)), rtol=1e-12, atol=1e-12)
+    d, h, w = wl.vol_shape
+    dz, dy, dx = wl.voxel_spacing
+    hi = 0.5 * np.array([w * dx, h * dy, d * dz])
+    for view in range(wl.n_views):
+        for u in range(0, wl.det_shape[0], 3):
+            o, dvec, tmin, tmax = g.ray(view, u, 0)
+            ref = face_chord(o, dvec, tmin, tmax, -hi, hi)
+            assert abs(rc[view, u, 0] - ref) <= 1e-12 * max(1.0, ref)
