@@ -161,6 +161,21 @@ ct_status_t ct_geom_destroy(ct_geom_t g);
 #define CT_VIEW_TABLE_STRIDE 48
 ct_status_t ct_geom_view_table(ct_geom_t g, const ct_geom_desc_t *desc, double *out);
 
+/* Range of the adjoint's fixed-point accumulation, for inspection (host only,
+ * no device work; with g == NULL it is computed from desc, surface != 0 for a
+ * parameterized detector).  *rays_bound receives a bound on the (ray, voxel)
+ * pairs one voxel can collect over all views: per view, the pixel centres in
+ * the voxel's image on a flat detector, (e_u + 1)(e_v + 1) for an image of
+ * e_u x e_v pixels (fan/cone: magnified at the volume corner nearest the
+ * source plane; a volume reaching that plane, or a surface detector: U V).
+ * Each pair adds less than 2^46 units, and the 64-bit sums are kept below
+ * 2^62: *shift receives the right shift applied to every term, 0 unless
+ * *rays_bound >= 2^16 (then ceil(log2(*rays_bound)) - 16).  Each ray still
+ * keeps its own 24 significant bits, so the shift costs no precision beyond
+ * one accumulator unit per term. */
+ct_status_t ct_geom_adjoint_range(ct_geom_t g, const ct_geom_desc_t *desc, int surface, double *rays_bound,
+                                  int32_t *shift);
+
 /* Forward projection A: sino[view][u][v] = sum_j a_ij vol[j].
  * vol: device (D,H,W) float32; sino: device (views,U,V) float32.
  * Every ray is written, missed rays as 0 (diffct "Large Volumes and Chunked
@@ -171,12 +186,18 @@ ct_status_t ct_project(ct_geom_t g, const float *vol, float *sino, ct_stream_t s
 
 /* Matched adjoint A^T: vol[j] = sum_i a_ij sino[i]; every voxel is overwritten.
  * Volume bricks accumulate their rays in on-chip memory (LDS) and are each
- * written once, with no global atomics.  Each term is an exact product of a
- * fixed-point piece length and a fixed-point ray value, summed in 64-bit
- * integers, so the result is bit-for-bit the same on every run (unlike an
- * adjoint built on float atomics: the diffct documentation notes run-to-run
- * differences of its atomic adjoint in "Example results").  sino must hold
- * finite values; sino and vol must not overlap. */
+ * written once, with no global atomics.  Each term is a product of a
+ * fixed-point piece length (2^-23 of a voxel diagonal) and the ray value in
+ * fixed point, summed in 64-bit integers, so the result is bit-for-bit the
+ * same on every run (unlike an adjoint built on float atomics: the diffct
+ * documentation notes run-to-run differences of its atomic adjoint in
+ * "Example results").  Range: each ray value keeps 24 significant bits
+ * whatever the other rays of its brick hold (rays far below the brick's
+ * largest are stored as a mantissa whose products are shifted down), so per
+ * voxel the error stays near float32's 2^-24 of sum_i |a_ij y_i|; rays below
+ * 2^-46 of the largest ray crossing the same 16 x 16 x 32 brick add nothing.
+ * The sums cannot overflow (ct_geom_adjoint_range).  sino must hold finite
+ * values; sino and vol must not overlap. */
 ct_status_t ct_backproject(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream);
 
 /* The same A^T by one lane per ray with global float atomics (a measured

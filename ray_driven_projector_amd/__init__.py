@@ -29,7 +29,7 @@ CT_VIEW_TABLE_STRIDE = 48
 
 # every symbol declared in include/ctproj.h
 EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_geom_destroy",
-           "ct_geom_view_table",
+           "ct_geom_view_table", "ct_geom_adjoint_range",
            "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_project_region",
            "ct_backproject_region", "ct_project_host", "ct_backproject_host",
            "ct_fbp_create", "ct_fbp_destroy", "ct_fbp_info", "ct_fbp_filter", "ct_fbp_backproject",
@@ -86,6 +86,7 @@ def lib():
         L.ct_geom_create_surface.argtypes = [P(GeomDesc), P(c.c_double), c.c_int, P(vp)]
         L.ct_geom_destroy.argtypes = [vp]
         L.ct_geom_view_table.argtypes = [vp, P(GeomDesc), P(c.c_double)]
+        L.ct_geom_adjoint_range.argtypes = [vp, P(GeomDesc), c.c_int, P(c.c_double), P(c.c_int32)]
         L.ct_project.argtypes = [vp, vp, vp, vp]
         L.ct_backproject.argtypes = [vp, vp, vp, vp]
         L.ct_backproject_atomic.argtypes = [vp, vp, vp, vp]
@@ -163,6 +164,22 @@ def ct_geom_view_table(beam, vol_shape, voxel_spacing, det_shape, det_spacing, f
     _check(lib().ct_geom_view_table(None, ctypes.byref(d),
                                     out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
     return out
+
+
+def ct_geom_adjoint_range(beam=None, vol_shape=None, voxel_spacing=None, det_shape=None, det_spacing=None,
+                          frames=None, surface=False, geometry=None):
+    """(rays_bound, shift) of the adjoint's fixed-point range: from a handle
+    (geometry=) or computed on the host from the description."""
+    bound = ctypes.c_double(0.0)
+    shift = ctypes.c_int32(0)
+    if geometry is not None:
+        _check(lib().ct_geom_adjoint_range(geometry.handle, None, int(surface), ctypes.byref(bound),
+                                           ctypes.byref(shift)))
+    else:
+        d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
+        _check(lib().ct_geom_adjoint_range(None, ctypes.byref(d), int(surface), ctypes.byref(bound),
+                                           ctypes.byref(shift)))
+    return float(bound.value), int(shift.value)
 
 
 def last_error() -> str:

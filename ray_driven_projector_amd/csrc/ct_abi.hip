@@ -39,9 +39,8 @@ struct ct_geom_s {
     double *d_views = nullptr;          // device view table
     unsigned long long *d_total = nullptr;  // device counter for ct_count_intersections
     int device = 0;
-    int brick_shape = 5;                // adjoint bricks of 16 x 16 x 32
-    int brick2d = 2;                    // 2D adjoint bricks of 16 x 16
-    int fwd_order = 5;                  // forward block order: 2 x 2 tile groups, views inside
+    double rays_bound = 0.0;            // brick adjoint: (ray, voxel) pairs a voxel can collect
+    int yshift = 0;                     // brick adjoint: right shift of every term (range bound)
     float *d_vol_yf = nullptr;          // y-fastest volume copy read by some views' gathers
     float *d_vol_zf = nullptr;          // z-fastest volume copy read by some views' gathers
     bool need_yf = false, need_zf = false;  // some view reads that copy
@@ -88,9 +87,8 @@ LaunchGeom lg(ct_geom_t g) {
     l.spy = g->host.sy;
     l.spz = g->host.sz;
     l.two_d = g->host.is2d;
-    l.brick_shape = g->brick_shape;
-    l.brick2d = g->brick2d;
-    l.fwd_order = g->fwd_order;
+    l.persp = g->host.beam == CT_FAN2D || g->host.beam == CT_CONE;
+    l.yshift = g->yshift;
     l.vol_yf = g->d_vol_yf;
     l.vol_zf = g->d_vol_zf;
     l.need_yf = g->need_yf;
@@ -158,46 +156,6 @@ ct_status_t check_alias(std::initializer_list<Arg> args) {
             if ((v[i].output || v[j].output) && overlap(v[i].span, v[j].span))
                 return fail(CT_E_ALIAS, "an output buffer overlaps another buffer of the call");
     return CT_OK;
-}
-
-// Launch shapes.  CTPROJ_BRICK (0..6) overrides the adjoint brick shape,
-// CTPROJ_FWD_ORDER (0..7) the forward block order, and
-// CTPROJ_FWD_LAYOUT=x keeps every forward gather on the caller's x-fastest volume;
-// both only change the work decomposition (used for tuning comparisons).
-// Defaults measured on 512^3 cone and parallel3d workloads: 16 x 16 x 32 bricks,
-// forward order 5 (groups of 2 x 2 pixel tiles, every view of a group in turn).
-void choose_tiles(ct_geom_s *g) {
-    // 2D: 16 x 16 bricks (C2, 512^2 fan, 360 views: A^T 1.17 ms with 64 x 64,
-    // 0.50 with 32 x 32, 0.44 with 16 x 16 -- small 2D volumes need many bricks
-    // to fill the chip); CTPROJ_BRICK2D (0..2) overrides
-    g->brick2d = 2;
-    if (const char *e = std::getenv("CTPROJ_BRICK2D")) {
-        const int v = std::atoi(e);
-        if (v >= 0 && v <= 2) g->brick2d = v;
-    }
-    g->brick_shape = 5;
-    if (const char *e = std::getenv("CTPROJ_BRICK")) {
-        const int v = std::atoi(e);
-        if (v >= 0 && v <= 6) g->brick_shape = v;
-    }
-    g->fwd_order = 5;
-    if (const char *e = std::getenv("CTPROJ_FWD_ORDER")) {
-        const int v = std::atoi(e);
-        if (v >= 0 && v <= 7) g->fwd_order = v;
-    }
-    const char *lay = std::getenv("CTPROJ_FWD_LAYOUT");
-    if (lay && lay[0] == 'x') {
-        for (int64_t k = 0; k < g->host.n_views; ++k) {
-            double *t = g->table.data() + k * CT_VIEW_TABLE_STRIDE;
-            const double su[3] = {t[VT_OU] + t[VT_DU], t[VT_OU + 1] + t[VT_DU + 1], t[VT_OU + 2] + t[VT_DU + 2]};
-            const double sv[3] = {t[VT_OV] + t[VT_DV], t[VT_OV + 1] + t[VT_DV + 1], t[VT_OV + 2] + t[VT_DV + 2]};
-            const double nu = std::sqrt(su[0] * su[0] + su[1] * su[1] + su[2] * su[2]);
-            const double nv = std::sqrt(sv[0] * sv[0] + sv[1] * sv[1] + sv[2] * sv[2]);
-            const double au = nu > 0 ? std::fabs(su[0]) / nu : 0.0, av = nv > 0 ? std::fabs(sv[0]) / nv : 0.0;
-            t[VT_LAYOUT] = 0.0;
-            t[VT_PATCH] = (g->host.is2d || au >= av) ? 0.0 : 1.0;
-        }
-    }
 }
 
 ct_status_t launched(hipError_t e, const char *what) {
@@ -407,6 +365,33 @@ ct_status_t ct_geom_view_table(ct_geom_t g, const ct_geom_desc_t *desc, double *
     return CT_OK;
 }
 
+ct_status_t ct_geom_adjoint_range(ct_geom_t g, const ct_geom_desc_t *desc, int surface, double *rays_bound,
+                                  int32_t *shift) {
+    if (!rays_bound || !shift) return fail(CT_E_NULL, "output pointer is NULL");
+    if (g) {
+        if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+        *rays_bound = g->rays_bound;
+        *shift = g->yshift;
+        set_error("");
+        return CT_OK;
+    }
+    GeomHost h;
+    const char *why = "";
+    ct_status_t st = validate_desc(desc, &h, &why);
+    if (st != CT_OK) return fail(st, why);
+    std::vector<double> table;
+    try {
+        table.assign((size_t)h.n_views * CT_VIEW_TABLE_STRIDE, 0.0);
+    } catch (...) {
+        return fail(CT_E_NOMEM, "host allocation failed");
+    }
+    build_view_table(desc, h, table.data());
+    *rays_bound = adjoint_rays_bound(h, table.data(), surface != 0);
+    *shift = adjoint_term_shift(*rays_bound);
+    set_error("");
+    return CT_OK;
+}
+
 static void free_handle(ct_geom_s *g) {
     if (g->d_views) (void)hipFree(g->d_views);
     if (g->d_total) (void)hipFree(g->d_total);
@@ -442,7 +427,8 @@ static ct_status_t create_impl(const ct_geom_desc_t *desc, const double *offsets
         return fail(CT_E_NOMEM, "host allocation failed");
     }
     build_view_table(desc, h, g->table.data());
-    choose_tiles(g);
+    g->rays_bound = adjoint_rays_bound(h, g->table.data(), offsets != nullptr);
+    g->yshift = adjoint_term_shift(g->rays_bound);
     hipError_t e = hipGetDevice(&g->device);
     if (e != hipSuccess) {
         delete g;

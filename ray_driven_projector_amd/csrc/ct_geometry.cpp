@@ -268,4 +268,69 @@ void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *tab
     choose_layouts(g, table);
 }
 
+// Range of the brick adjoint's 64-bit accumulator.  Each (ray, voxel) pair adds
+// at most one voxel chord times the largest ray value: below 2^46 in the
+// accumulator's units (both factors are under 2^23).  The rays of one view that
+// cross one voxel are those whose pixel centres fall in the voxel's image on
+// the detector: at most (e_u + 1)(e_v + 1) for an image of extent e_u x e_v
+// pixels.  Parallel beams: e_u = sum_a |d beta / d X_a| (the second row of
+// MINV; voxel-coordinate axes are one voxel long).  Fan/cone: u = beta/alpha,
+// d u / d X_a = (MINV1_a - u MINV0_a) / alpha with 0 <= u <= U - 1 wherever a
+// pixel centre lies, and alpha is smallest at a corner of the volume box (it
+// is affine in X); a box reaching the source plane (alpha <= 0) may be
+// crossed by every ray of the view.  A detector surface has no such image
+// bound: every pixel counts.  The sum over the views times 2^46 must stay
+// below 2^62 (one bit of margin under the sign); each doubling beyond that
+// costs one bit of right shift on every term.
+double adjoint_rays_bound(const GeomHost &g, const double *table, bool surface) {
+    const double all = double(g.U) * double(g.V);
+    double total = 0.0;
+    for (int64_t k = 0; k < g.n_views; ++k) {
+        const double *t = table + k * CT_VIEW_TABLE_STRIDE;
+        const double *M = t + VT_MINV;
+        double count = all;
+        if (!surface) {
+            double eu = 0.0, ev = 0.0;
+            bool bounded = true;
+            if (t[VT_PERSP] != 0.0) {
+                double amin = INFINITY;
+                for (int c = 0; c < 8; ++c) {
+                    const double X[3] = {(c & 1) ? double(g.W) : 0.0, (c & 2) ? double(g.H) : 0.0,
+                                         (c & 4) ? double(g.D) : 0.0};
+                    double al = 0.0;
+                    for (int a = 0; a < 3; ++a) al += M[a] * (X[a] - t[VT_O00 + a]);
+                    amin = std::fmin(amin, al);
+                }
+                bounded = amin > 1e-9;
+                if (bounded) {
+                    for (int a = 0; a < 3; ++a) {
+                        eu += std::fabs(M[3 + a]) + double(g.U - 1) * std::fabs(M[a]);
+                        ev += std::fabs(M[6 + a]) + double(g.V - 1) * std::fabs(M[a]);
+                    }
+                    eu /= amin;
+                    ev /= amin;
+                }
+            } else {
+                for (int a = 0; a < 3; ++a) {
+                    eu += std::fabs(M[3 + a]);
+                    ev += std::fabs(M[6 + a]);
+                }
+            }
+            if (bounded) {
+                const double nu = std::fmin(double(g.U), eu + 1.0);
+                const double nv = g.is2d ? 1.0 : std::fmin(double(g.V), ev + 1.0);
+                count = nu * nv;
+            }
+        }
+        total += count;
+    }
+    return total;
+}
+
+int adjoint_term_shift(double rays_bound) {
+    int h = 0;
+    while (h < 40 && rays_bound >= std::ldexp(1.0, 16 + h)) ++h;
+    return h;
+}
+
 }  // namespace ctp

@@ -74,6 +74,12 @@ struct GeomHost {
 ct_status_t validate_desc(const ct_geom_desc_t *desc, GeomHost *out, const char **why);
 void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *table);
 
+// Brick adjoint range: a bound on the (ray, voxel) pairs a voxel can collect
+// over all views, and the right shift its terms need so the 64-bit sums stay
+// below 2^62 (ct_geometry.cpp).
+double adjoint_rays_bound(const GeomHost &g, const double *table, bool surface);
+int adjoint_term_shift(double rays_bound);
+
 void set_error(const char *msg);
 
 }  // namespace ctp

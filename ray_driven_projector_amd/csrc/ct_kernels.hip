@@ -580,16 +580,14 @@ struct RayArgs {
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
     int n_utiles, n_vtiles, n_blocks;
-    int order;                 // block order: 0 band/view/u-tile, 1 band/u-tile/view,
-                               // 2 band/view-group of 8/u-tile/view
     uint32_t vol_bytes;
 };
 
 // Tiles: a 256-thread block takes 16 x 16 pixels of one view; each wave takes a
 // 16 x 4 (or 4 x 16) patch whose 16-wide side runs along the detector axis that
 // the view's volume copy stores contiguously, so the 64 rays of a wave read few
-// cache lines per step.  2D: 256 consecutive u per block.  Block order (default
-// 5): groups of 2 v-bands x 2 u-tiles, and inside a group every view in turn, so
+// cache lines per step.  2D: 256 consecutive u per block.  Block order: groups
+// of 2 v-bands x 2 u-tiles, and inside a group every view in turn, so
 // the blocks an XCD runs together trace the same few pixel tiles through
 // neighbouring views; their rays cross the same voxels at nearly the same time
 // and the gathers hit in L2 (this order cut the 512^3 forward times by a
@@ -598,38 +596,19 @@ struct RayArgs {
 template <int MODE, bool TWO_D, bool SURF>
 __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
     const int blk = xcd_remap(blockIdx.x, a.n_blocks);
-    int ut, view, band;
-    if (a.order == 1 || a.order >= 3) {
-        // groups of TB bands x TU u-tiles; within a group: view, then band, then
-        // u-tile (the last group of each kind may be short)
-        const int TU = a.order == 3 || a.order == 5 ? 2 : (a.order == 6 ? 4 : 1);
-        const int TB = a.order == 4 || a.order == 5 ? 2 : (a.order == 7 ? 4 : 1);
-        const int bg = blk / (a.n_views * a.n_utiles * TB);
-        int r = blk - bg * (a.n_views * a.n_utiles * TB);
-        const int tb = min(TB, a.n_vtiles - bg * TB);
-        const int ug = r / (a.n_views * TU * tb);
-        r -= ug * (a.n_views * TU * tb);
-        const int tu = min(TU, a.n_utiles - ug * TU);
-        view = r / (tu * tb);
-        r -= view * (tu * tb);
-        band = bg * TB + r / tu;
-        ut = ug * TU + r % tu;
-    } else if (a.order == 2) {
-        // views in groups of 8 (the last group may be short)
-        const int per_band = a.n_views * a.n_utiles;
-        band = blk / per_band;
-        int r = blk - band * per_band;
-        const int grp = r / (8 * a.n_utiles);
-        const int g0 = grp * 8, gn = min(8, a.n_views - g0);
-        r -= grp * 8 * a.n_utiles;
-        ut = r / gn;
-        view = g0 + (r - ut * gn);
-    } else {
-        ut = blk % a.n_utiles;
-        const int rest = blk / a.n_utiles;
-        view = rest % a.n_views;
-        band = rest / a.n_views;
-    }
+    // groups of 2 v-bands x 2 u-tiles; within a group: view, then band, then
+    // u-tile (the last group of each kind may be short)
+    constexpr int TU = 2, TB = 2;
+    const int bg = blk / (a.n_views * a.n_utiles * TB);
+    int r = blk - bg * (a.n_views * a.n_utiles * TB);
+    const int tb = min(TB, a.n_vtiles - bg * TB);
+    const int ug = r / (a.n_views * TU * tb);
+    r -= ug * (a.n_views * TU * tb);
+    const int tu = min(TU, a.n_utiles - ug * TU);
+    const int view = r / (tu * tb);
+    r -= view * (tu * tb);
+    const int band = bg * TB + r / tu;
+    const int ut = ug * TU + r % tu;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int u, v;
     if (TWO_D) {
@@ -772,21 +751,11 @@ struct BrickArgs {
     const float *env;         // surface: per-view footprint envelopes
     int offx, offy, offz;     // voxel index of the volume buffer's first voxel (a region)
     int accumulate;           // BM_BACKPROJECT: add to the volume instead of writing it
+    int yshift;               // every term shifted right by this many bits (range bound)
     int W, H, D, U, V, n_views;
     double spx, spy, spz;
     int nbx, nby, nbz, n_blocks;
 };
-
-// Slab clip of an axis the ray does not move along (a = 0), in brick-centred
-// coordinates: the ray is inside for every t iff -h <= o < h.  Replaces (o, 1/a)
-// by stand-ins for which the general formulas lo = (-h - o)/a, hi = lo + 2h/a
-// give an unbounded interval (inside) or an empty one (outside).
-__device__ __forceinline__ void bclip_zero(float o, float a, float h, float &co, float &cinv) {
-    if (a == 0.f) {
-        co = (o >= -h && o < h) ? 0.f : -h - 1.f;
-        cinv = 1e35f;
-    }
-}
 
 // Non-negative float32 to fixed point with the convert's own saturation
 // (values from 2^32 up and INF give 0xFFFFFFFF, negative values 0).
@@ -899,6 +868,16 @@ __device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int 
 // (v_mul_i32_i24 / v_mul_hi_i32_i24) and the integer sums do not depend on the
 // order of the adds.  Float atomic adds in LDS run some 30x slower than integer
 // ones on this chip, hence the integer accumulator.
+//
+// Range.  The accumulator's unit is set per brick by its largest |y|.  A ray
+// far below that keeps its own 24 significant bits: Y is its mantissa scaled
+// up by 2^k and each product is shifted right by k before the add (SHIFT
+// walks), so its terms carry float32-like relative precision (the shift drops
+// less than one accumulator unit, about 2^-45 of the brick's largest term).
+// Rays within 2^6 of the largest use the plain walk (at least 17 bits).  A
+// geometry whose per-voxel sum could pass 2^63 (many views of voxels much
+// larger than the pixels, or a source near the volume) shifts every term by
+// the host-computed a.yshift as well.
 constexpr float kPieceUnits = 8323072.f;   // 2^23 - 2^16
 constexpr int kFpCache = 1024;             // brick kernel: views whose footprints LDS keeps
 __device__ __forceinline__ unsigned long long mul24_64(uint32_t len, int y) {
@@ -936,24 +915,30 @@ __device__ __forceinline__ void sadvance(uint32_t qx, uint32_t qy, uint32_t qz, 
 // next event t lies before l_end, so the first piece of an iteration is whole;
 // the second is cut at l_end.  A cell is only written before a crossing at or
 // past l_end has been taken, so every offset stays inside the brick.
-__device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long long *lds, int Y) {
+template <bool SHIFT>
+__device__ __forceinline__ unsigned long long term(uint32_t len, int Y, int sh) {
+    const unsigned long long p = mul24_64(len, Y);
+    return SHIFT ? (unsigned long long)((long long)p >> sh) : p;
+}
+template <bool SHIFT>
+__device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long long *lds, int Y, int sh) {
     const uint32_t qx = w.qx, qy = w.qy, qz = w.qz, sx = w.stx, sy = w.sty, sz = w.stz;
     const uint32_t lend = w.lend;
     uint32_t idx = w.idx;
     uint32_t lx = w.lx, ly = w.ly, lz = w.lz;
     uint32_t lc = 0, t = umin3(lx, ly, lz);
     while (t < lend) {
-        lds_add(lds, idx, mul24_64(t - lc, Y));
+        lds_add(lds, idx, term<SHIFT>(t - lc, Y, sh));
         sadvance(qx, qy, qz, sx, sy, sz, t, idx, lx, ly, lz);
         lc = t;
         t = umin3(lx, ly, lz);
         const uint32_t tn = min(t, lend);
-        lds_add(lds, idx, mul24_64(tn - lc, Y));
+        lds_add(lds, idx, term<SHIFT>(tn - lc, Y, sh));
         sadvance(qx, qy, qz, sx, sy, sz, t, idx, lx, ly, lz);
         lc = tn;
         t = umin3(lx, ly, lz);
     }
-    if (lc < lend) lds_add(lds, idx, mul24_64(lend - lc, Y));
+    if (lc < lend) lds_add(lds, idx, term<SHIFT>(lend - lc, Y, sh));
 }
 
 // Everything of a brick walk that depends on the ray direction alone (for
@@ -1278,16 +1263,23 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
             my = dp.ny ? -oy : oy;
             mz = dp.nz ? -oz : oz;
         }
-        // slab clip: lo = (-h - m) / a, hi = (h - m) / a
-        float cx = mx, cy = my, cz = mz, cix = dp.ix, ciy = dp.iy, ciz = dp.iz;
+        // slab clip: lo = (-h - m) / a, hi = (h - m) / a; an axis the ray does
+        // not move along holds it for every t iff -h <= m < h
+        float cx = -hx - mx, cy = -hy - my, cz = -hz - mz, cix = dp.ix, ciy = dp.iy, ciz = dp.iz;
         if (!FS && dp.slow) {
-            bclip_zero(mx, dp.axx, hx, cx, cix);
-            bclip_zero(my, dp.ayy, hy, cy, ciy);
-            if (!TWO_D) bclip_zero(mz, dp.azz, hz, cz, ciz);
+            const auto zero_axis = [](float a, float m, float h, float &c, float &ci) {
+                if (a == 0.f) {
+                    c = (-h <= m && m < h) ? -h : 1.f;   // lo -> -inf / +inf
+                    ci = 1e35f;
+                }
+            };
+            zero_axis(dp.axx, mx, hx, cx, cix);
+            zero_axis(dp.ayy, my, hy, cy, ciy);
+            if (!TWO_D) zero_axis(dp.azz, mz, hz, cz, ciz);
         }
-        const float lox = (-hx - cx) * cix, hix = fmaf(fex, cix, lox);
-        const float loy = (-hy - cy) * ciy, hiy = fmaf(fey, ciy, loy);
-        const float loz = TWO_D ? -3e38f : (-hz - cz) * ciz;
+        const float lox = cx * cix, hix = fmaf(fex, cix, lox);
+        const float loy = cy * ciy, hiy = fmaf(fey, ciy, loy);
+        const float loz = TWO_D ? -3e38f : cz * ciz;
         const float hiz = TWO_D ? 3e38f : fmaf(fez, ciz, loz);
         const float tin = fmaxf(fmaxf(fmaxf(lox, loy), loz), t0);
         const float tout = fminf(fminf(fminf(hix, hiy), hiz), t1);
@@ -1320,8 +1312,19 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
             w.sty = in_vgpr(dp.sty);
             w.stz = in_vgpr(dp.stz);
         }
-        const int Y = (int)rintf(__builtin_amdgcn_fmed3f(yv * yscale, -8388607.f, 8388607.f));
-        iwalk_scatter_fix(w, acc, Y);
+        // the ray value in fixed point: rays within 2^6 of the brick's largest as
+        // they are (|Y| >= 2^17), smaller ones (and all rays when the geometry
+        // asks for a shift) as a 24-bit mantissa with the product shifted back
+        const float Yf = yv * yscale;   // |Yf| < 2^23
+        const bool mant = a.yshift != 0 || fabsf(Yf) < 0x1p17f;
+        if (__builtin_amdgcn_ballot_w64(mant)) {
+            const int up = mant ? 23 - __builtin_amdgcn_frexp_expf(Yf) : 0;
+            const int sh = up + a.yshift;
+            const int Y = (int)rintf(__builtin_amdgcn_fmed3f(ldexpf(Yf, up), -8388607.f, 8388607.f));
+            if (sh <= 46) iwalk_scatter_fix<true>(w, acc, Y, sh);   // else every term is below one unit
+        } else {
+            iwalk_scatter_fix<false>(w, acc, (int)rintf(__builtin_amdgcn_fmed3f(Yf, -8388607.f, 8388607.f)), 0);
+        }
     }
     };
     if constexpr (PERSP && !SURF) {
@@ -1335,7 +1338,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
 // Two 512-thread workgroups (or four of 256, one of 1024) share a CU through
 // their LDS, i.e. 4 waves per SIMD; the register budget is held to that.
 // SURF: parameterized detector surface (per-pixel rays from the offsets table).
-template <int BX, int BY, int BZ, int NT, int MODE, bool SURF>
+template <int BX, int BY, int BZ, int NT, int MODE, bool SURF, bool PERSP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void brick_kernel(
     BrickArgs a) {
     constexpr int LSY = BX + 1;           // padded LDS strides (elements): rays of a
@@ -1431,15 +1434,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
                                     a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f)) {
             continue;
         }
-        if (vw[VT_PERSP] != 0.0)
-            brick_rays<LSY, LSZ, MODE, true, TWO_D, SURF>(a, vw, view, f, lane, x0, y0, z0, ex, ey,
-                                                          ez, cbx, cby, cbz, S, yscale, acc);
-        else
-            brick_rays<LSY, LSZ, MODE, false, TWO_D, SURF>(a, vw, view, f, lane, x0, y0, z0, ex, ey,
-                                                           ez, cbx, cby, cbz, S, yscale, acc);
+        // PERSP: every view of the geometry is fan/cone (else parallel)
+        brick_rays<LSY, LSZ, MODE, PERSP, TWO_D, SURF>(a, vw, view, f, lane, x0, y0, z0, ex, ey, ez, cbx, cby,
+                                                       cbz, S, yscale, acc);
     }
     __syncthreads();
-    const double inv_scale = 1.0 / ((double)S * (double)yscale);
+    const double inv_scale = ldexp(1.0, a.yshift) / ((double)S * (double)yscale);
     const float alpha = (MODE == BM_CGLS && a.x_upd) ? (float)a.state[CS_ALPHA] : 0.f;
     double sq = 0.0;
     for (int i = threadIdx.x; i < BX * BY * BZ; i += NT) {
@@ -1597,7 +1597,6 @@ __global__ __launch_bounds__(256) void cgls_update_p_kernel(float *__restrict__ 
 
 static RayArgs ray_args(const LaunchGeom &g) {
     RayArgs a{};
-    a.order = g.fwd_order;
     a.offx = g.offx; a.offy = g.offy; a.offz = g.offz;
     a.accumulate = g.accumulate;
     a.surf = Surface{g.surf_off, g.surf_per_view};
@@ -1714,12 +1713,14 @@ static void launch_brick_shape(BrickArgs &a, const LaunchGeom &g, hipStream_t s)
     a.nby = (g.H + BY - 1) / BY;
     a.nbz = (g.D + BZ - 1) / BZ;
     a.n_blocks = a.nbx * a.nby * a.nbz;
-    if (a.surf.off)
-        hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, true>), dim3(a.n_blocks), dim3(NT), 0, s,
-                           a);
-    else
-        hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, false>), dim3(a.n_blocks), dim3(NT), 0,
-                           s, a);
+    const dim3 grid(a.n_blocks), block(NT);
+    if (a.surf.off) {
+        if (g.persp) hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, true, false>), grid, block, 0, s, a);
+    } else {
+        if (g.persp) hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, false, false>), grid, block, 0, s, a);
+    }
 }
 
 template <int MODE>
@@ -1731,25 +1732,10 @@ static hipError_t launch_brick_args(const LaunchGeom &g, BrickArgs a, hipStream_
     a.env = g.surf_env;
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
-    if (g.two_d) {
-        if (g.brick2d == 1) launch_brick_shape<32, 32, 1, 256, MODE>(a, g, s);
-        else if (g.brick2d == 2) launch_brick_shape<16, 16, 1, 256, MODE>(a, g, s);
-        else launch_brick_shape<64, 64, 1, 256, MODE>(a, g, s);
-    } else if (g.brick_shape == 1) {
-        launch_brick_shape<32, 32, 16, 1024, MODE>(a, g, s);
-    } else if (g.brick_shape == 2) {
-        launch_brick_shape<32, 16, 16, 512, MODE>(a, g, s);
-    } else if (g.brick_shape == 3) {
-        launch_brick_shape<32, 16, 32, 1024, MODE>(a, g, s);
-    } else if (g.brick_shape == 4) {
-        launch_brick_shape<32, 32, 8, 512, MODE>(a, g, s);
-    } else if (g.brick_shape == 5) {
-        launch_brick_shape<16, 16, 32, 512, MODE>(a, g, s);
-    } else if (g.brick_shape == 6) {
-        launch_brick_shape<16, 16, 64, 1024, MODE>(a, g, s);
-    } else {
-        launch_brick_shape<16, 16, 16, 256, MODE>(a, g, s);
-    }
+    a.yshift = g.yshift;
+    // 3D: bricks of 16 x 16 x 32 voxels, 512 threads; 2D: 16 x 16, 256 threads
+    if (g.two_d) launch_brick_shape<16, 16, 1, 256, MODE>(a, g, s);
+    else launch_brick_shape<16, 16, 32, 512, MODE>(a, g, s);
     return hipGetLastError();
 }
 
@@ -1806,14 +1792,7 @@ hipError_t launch_surface_env(const LaunchGeom &g, unsigned long long *bad, hipS
 size_t cgls_ray_blocks(const LaunchGeom &g) { return (size_t)ray_args(g).n_blocks; }
 
 size_t cgls_brick_blocks(const LaunchGeom &g) {
-    int bx = 16, by = 16, bz = 16;
-    if (g.two_d) { bx = by = g.brick2d == 1 ? 32 : (g.brick2d == 2 ? 16 : 64); bz = 1; }
-    else if (g.brick_shape == 1) { bx = 32; by = 32; bz = 16; }
-    else if (g.brick_shape == 2) { bx = 32; by = 16; bz = 16; }
-    else if (g.brick_shape == 3) { bx = 32; by = 16; bz = 32; }
-    else if (g.brick_shape == 4) { bx = 32; by = 32; bz = 8; }
-    else if (g.brick_shape == 5) { bx = 16; by = 16; bz = 32; }
-    else if (g.brick_shape == 6) { bx = 16; by = 16; bz = 64; }
+    const int bx = 16, by = 16, bz = g.two_d ? 1 : 32;
     return (size_t)((g.W + bx - 1) / bx) * ((g.H + by - 1) / by) * ((g.D + bz - 1) / bz);
 }
 

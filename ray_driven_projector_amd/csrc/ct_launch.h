@@ -13,11 +13,9 @@ struct LaunchGeom {
     int W, H, D, U, V, n_views;
     double spx, spy, spz;  // voxel spacing (x, y, z)
     bool two_d;
-    int brick_shape;       // adjoint brick: 0 = 16^3, 1 = 32x32x16, 2 = 32x16x16,
-                           // 3 = 32x16x32, 4 = 32x32x8, 5 = 16x16x32, 6 = 16x16x64
-                           // (x by y by z)
-    int brick2d;           // 2D adjoint brick: 0 = 64 x 64, 1 = 32 x 32, 2 = 16 x 16
-    int fwd_order;         // forward block order (see RayArgs::order)
+    bool persp;            // fan/cone beam (rays from a source), else parallel
+    int yshift;            // brick adjoint: every fixed-point term is shifted right by
+                           // this many bits (0 unless the geometry's term bound needs it)
     int offx, offy, offz;  // region launches: voxel index of the buffer's first voxel
     int accumulate;        // region launches: add to the output instead of writing it
     const double *surf_off; // detector surface offsets (device float64), or null: flat

@@ -239,3 +239,51 @@ def test_view_table_rays_pass_through_pixels(L, config):
             N = t[20:23]
             assert abs(np.dot(N, t[3:6] + t[12:15])) < 1e-9
             assert abs(np.dot(N, t[6:9] + t[15:18])) < 1e-9
+
+
+# ---- the adjoint's fixed-point range bound ----
+
+@pytest.mark.parametrize("beam", [W.BEAM_PARALLEL2D, W.BEAM_FAN2D, W.BEAM_CONE, W.BEAM_PARALLEL3D])
+@pytest.mark.parametrize("spacing", [1.0, 3.0])
+def test_adjoint_range_bound_covers_the_rays_through_each_voxel(L, beam, spacing):
+    """The host bound on the (ray, voxel) pairs a voxel can collect is at least
+    the true count from the oracle's brute-force matrix: per view the most
+    rays crossing any one voxel, summed over the views (which bounds every
+    voxel's own sum)."""
+    import oracle
+    vol = (5, 6, 7) if beam >= 2 else (1, 6, 7)
+    det = (23, 17) if beam >= 2 else (23, 1)
+    wl = W.tiny_workload(beam, vol, det, 6, 13 + beam, voxel_spacing=(spacing,) * 3,
+                         det_spacing=(0.7, 0.6), sid=40.0, sdd=70.0, jitter=0.3 if beam >= 2 else 0.0)
+    A = oracle.brute_matrix(oracle.Geometry.from_workload(wl))
+    per_view = (A > 0).reshape(wl.n_views, -1, A.shape[1]).sum(axis=1)   # (views, voxels)
+    need = per_view.max(axis=1).sum()
+    bound, shift = rdp.ct_geom_adjoint_range(*_args(wl))
+    assert bound >= need, (bound, need)
+    assert bound <= wl.n_rays and shift == 0
+    # a detector surface is bounded by its pixel count
+    bs, _ = rdp.ct_geom_adjoint_range(*_args(wl), surface=True)
+    assert bs == wl.n_rays
+
+
+def test_adjoint_range_shift_rule(L):
+    """shift = 0 below 2^16 pairs, else ceil(log2(bound)) - 16: coarse voxels
+    seen by many views through a fine detector need it."""
+    fr = W.circular_parallel2d(30000)
+    bound, shift = rdp.ct_geom_adjoint_range(W.BEAM_PARALLEL2D, (1, 16, 16), (1.0, 8.0, 8.0), (200, 1),
+                                            (0.75, 1.0), fr)
+    # each voxel's image is at most 8 sqrt(2) / 0.75 pixels wide: about 16 rays a view
+    assert 30000 * 8.0 / 0.75 <= bound <= 30000 * (8.0 * math.sqrt(2) / 0.75 + 1) + 1e-6
+    assert shift == math.ceil(math.log2(bound)) - 16 == 3
+    few = fr[:100]
+    b2, s2 = rdp.ct_geom_adjoint_range(W.BEAM_PARALLEL2D, (1, 16, 16), (1.0, 8.0, 8.0), (200, 1),
+                                       (0.75, 1.0), few)
+    assert b2 < 2 ** 16 and s2 == 0
+    # a cone source inside the volume: every ray of the view may cross one voxel
+    wl = W.tiny_workload(W.BEAM_CONE, (8, 8, 8), (40, 30), 4, 3, sid=2.0, sdd=30.0)
+    b3, _ = rdp.ct_geom_adjoint_range(*_args(wl))
+    assert b3 == wl.n_rays
+    # the five workloads need no shift; the same geometries with surfaces do
+    for c in (1, 2, 3, 4, 5):
+        w = W.make_workload(c)
+        assert rdp.ct_geom_adjoint_range(*_args(w))[1] == 0
