@@ -447,6 +447,21 @@ ct_status_t ct_cgls_init(ct_geom_t g, const float *y, const float *x, float *r, 
 ct_status_t ct_cgls_step(ct_geom_t g, float *x, float *r, float *s, float *p, float *q, void *work,
                          ct_stream_t stream);
 
+/* One CGLS iteration that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The same kernels and results as ct_cgls_step, bit
+ * for bit; the per-block partial sums live in a fixed 32 MiB array in the
+ * library's device memory (one per GPU, held until the process ends) instead
+ * of the caller's workspace.  state: the first 256 bytes of a workspace that
+ * ct_cgls_init filled (the scalars), device memory, 8-byte aligned, read and
+ * updated in place.  Geometries whose largest launch has more than 2^22
+ * blocks (see ct_cgls_workspace_size: its bytes / 8 - 32) are rejected with
+ * CT_E_RANGE before any launch.  All calls on one GPU share the array, so
+ * calls that overlap in time on one GPU (different streams or threads) race;
+ * the first call on a device looks the array up there. */
+ct_status_t ct_cgls_step_noalloc(ct_geom_t g, float *x, float *r, float *s, float *p, float *q, double *state,
+                                 ct_stream_t stream);
+
 /* Copy the scalars to the host (synchronises the stream): out[0] = gamma =
  * ||A^T r||^2, out[1] = alpha and out[2] = beta of the last step, out[3] =
  * ||q||^2 of the last step, out[4] = ||r||^2. */

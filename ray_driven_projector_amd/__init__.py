@@ -37,7 +37,7 @@ EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_g
            "ct_sirt_weights",
            "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_sirt_update_bounded",
            "ct_sirt_step_bounded", "ct_cgls_workspace_size",
-           "ct_cgls_init", "ct_cgls_step", "ct_cgls_scalars", "ct_count_intersections",
+           "ct_cgls_init", "ct_cgls_step", "ct_cgls_step_noalloc", "ct_cgls_scalars", "ct_count_intersections",
            "ct_last_error", "ct_version"]
 
 
@@ -115,6 +115,7 @@ def lib():
         L.ct_cgls_workspace_size.argtypes = [vp, P(c.c_size_t)]
         L.ct_cgls_init.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.ct_cgls_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        L.ct_cgls_step_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.ct_cgls_scalars.argtypes = [vp, vp, P(c.c_double), vp]
         L.ct_count_intersections.argtypes = [vp, vp, P(c.c_uint64), vp]
         for name in EXPORTS[:-2]:
@@ -549,6 +550,21 @@ def ct_cgls_step(g: Geometry, x, r, s, p, q, work, stream=None):
     _check(lib().ct_cgls_step(g.handle, _ptr(x, g.vol_shape, "x"), _ptr(r, g.sino_shape, "r"),
                               _ptr(s, g.vol_shape, "s"), _ptr(p, g.vol_shape, "p"),
                               _ptr(q, g.sino_shape, "q"), _work_ptr(g, work), _stream(stream)))
+
+
+def ct_cgls_step_noalloc(g: Geometry, x, r, s, p, q, state, stream=None):
+    """One CGLS iteration with the partial sums in the library's static device
+    scratch; state: a device tensor whose first 256 bytes hold the scalars
+    (e.g. the workspace ct_cgls_init filled)."""
+    import torch
+    if not isinstance(state, torch.Tensor) or not state.is_cuda or not state.is_contiguous():
+        raise ValueError("state must be a contiguous device tensor")
+    if state.numel() * state.element_size() < 256:
+        raise ValueError("state must hold at least 256 bytes")
+    _check(lib().ct_cgls_step_noalloc(g.handle, _ptr(x, g.vol_shape, "x"), _ptr(r, g.sino_shape, "r"),
+                                      _ptr(s, g.vol_shape, "s"), _ptr(p, g.vol_shape, "p"),
+                                      _ptr(q, g.sino_shape, "q"), ctypes.c_void_p(state.data_ptr()),
+                                      _stream(stream)))
 
 
 def ct_cgls_scalars(g: Geometry, work, stream=None) -> dict:

@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -781,6 +782,59 @@ ct_status_t ct_cgls_step(ct_geom_t g, float *x, float *r, float *s, float *p, fl
     return launched(launch_cgls_step(lg(g), x, r, s, p, q, state, state + kCglsStateDoubles,
                                      (hipStream_t)stream),
                     "ct_cgls_step launch");
+}
+
+// ---- CGLS step without device allocation ----
+// The per-block float64 partial sums of a CGLS step held in a fixed array of
+// the library's own device memory, for callers that cannot allocate (graph
+// capture, serving loops).  Each GPU the library runs on holds its own copy
+// until the process ends; its address on a device comes from
+// hipGetSymbolAddress on that device (the array's name is only a host-side
+// stand-in).  Every partial a finalize reads is written by the launch before
+// it, so nothing needs clearing between calls.
+constexpr size_t kStaticPartials = size_t(1) << 22;   // 4 Mi doubles, 32 MiB per device
+static __device__ __align__(256) double scratch[kStaticPartials];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on `device` (the current device).
+ct_status_t static_scratch(int device, double **out) {
+    if (device < 0 || device >= kMaxDevices) return fail(CT_E_RANGE, "device index beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the CGLS scratch");
+        g_scratch_ptr[device] = (double *)ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return CT_OK;
+}
+}  // namespace
+
+ct_status_t ct_cgls_step_noalloc(ct_geom_t g, float *x, float *r, float *s, float *p, float *q, double *state,
+                                 ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!x || !r || !s || !p || !q || !state) return fail(CT_E_NULL, "a buffer pointer is NULL");
+    if (((uintptr_t)state & 7u) != 0) return fail(CT_E_ARG, "state must be 8-byte aligned");
+    Span X{x, vol_bytes(g)}, R{r, sino_bytes(g)}, S{s, vol_bytes(g)}, P{p, vol_bytes(g)},
+        Q{q, sino_bytes(g)}, St{state, kCglsStateDoubles * sizeof(double)};
+    ct_status_t st = check_alias({{X, true}, {R, true}, {S, true}, {P, true}, {Q, true}, {St, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    const size_t need = cgls_partials(g);
+    if (need > kStaticPartials)
+        return fail(CT_E_RANGE, "geometry needs more CGLS partial sums than the 4 Mi-double static scratch "
+                                "holds; use ct_cgls_step with a workspace");
+    if ((g->need_yf || g->need_zf) && g->layout_cap < full_voxels(g))
+        return fail(CT_E_RANGE, "the handle holds no whole-volume layout copies");
+    double *partial = nullptr;
+    if ((st = static_scratch(g->device, &partial)) != CT_OK) return st;
+    return launched(launch_cgls_step(lg(g), x, r, s, p, q, state, partial, (hipStream_t)stream),
+                    "ct_cgls_step_noalloc launch");
 }
 
 ct_status_t ct_cgls_scalars(ct_geom_t g, const void *work, double *out, ct_stream_t stream) {
