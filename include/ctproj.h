@@ -45,8 +45,10 @@
  *     along y or z (ct_geom_create allocates only those some view needs).  The
  *     forward calls (ct_project, ct_project_region, ct_sirt_residual,
  *     ct_sirt_step*, ct_cgls_*) write these copies, so such calls on one handle
- *     must not overlap in time; use one handle per stream for concurrent
- *     forward projections.  All other calls only read the handle.
+ *     must not overlap in time: they are serialised conveniences.  For
+ *     concurrent forward projections with one handle, ct_project_ws takes the
+ *     copies in caller workspace and only reads the handle, as every other
+ *     call does.
  *   - Every compute call is asynchronous and ordered on the caller's stream
  *     (a hipStream_t passed as void*; NULL is the legacy default stream).
  *   - Compute calls allocate nothing: all device memory they touch is the
@@ -183,6 +185,26 @@ ct_status_t ct_geom_adjoint_range(ct_geom_t g, const ct_geom_desc_t *desc, int s
  * each ray, including missed rays).  vol and sino must not overlap; vol must
  * hold finite values (a non-finite voxel may spread to rays that pass near it). */
 ct_status_t ct_project(ct_geom_t g, const float *vol, float *sino, ct_stream_t stream);
+
+/* The same forward projection with the volume copies in caller memory, so the
+ * handle is only read: calls with one handle may run concurrently on
+ * different streams as long as each has its own work buffer (the handle is
+ * then immutable after create, as the library's other read-only calls treat
+ * it).  ct_project is the serialised convenience that keeps the copies in the
+ * handle.  work: DEVICE memory of at least ct_forward_workspace_size bytes,
+ * 256-byte aligned, caller-owned scratch (overwritten; it may be NULL when
+ * that size is 0, i.e. every view gathers from the caller's x-fastest
+ * volume); it must not overlap vol or sino.  Same results as ct_project, bit
+ * for bit. */
+ct_status_t ct_project_ws(ct_geom_t g, const float *vol, float *sino, void *work, size_t work_bytes,
+                          ct_stream_t stream);
+
+/* Bytes of ct_project_ws workspace: one volume-sized float32 copy, rounded up
+ * to 256 bytes, per axis order other than x-fastest that some view's gathers
+ * use (y- and/or z-fastest; 0 for 2D beams and for geometries whose views all
+ * gather along x).  From a handle, or with g == NULL computed on the host from
+ * desc (no device work). */
+ct_status_t ct_forward_workspace_size(ct_geom_t g, const ct_geom_desc_t *desc, size_t *bytes);
 
 /* Matched adjoint A^T: vol[j] = sum_i a_ij sino[i]; every voxel is overwritten.
  * Volume bricks accumulate their rays in on-chip memory (LDS) and are each

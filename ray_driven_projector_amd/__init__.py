@@ -30,7 +30,8 @@ CT_VIEW_TABLE_STRIDE = 48
 # every symbol declared in include/ctproj.h
 EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_geom_destroy",
            "ct_geom_view_table", "ct_geom_adjoint_range",
-           "ct_project", "ct_backproject", "ct_backproject_atomic", "ct_project_region",
+           "ct_project", "ct_project_ws", "ct_forward_workspace_size", "ct_backproject",
+           "ct_backproject_atomic", "ct_project_region",
            "ct_backproject_region", "ct_project_host", "ct_backproject_host",
            "ct_fbp_create", "ct_fbp_destroy", "ct_fbp_info", "ct_fbp_filter", "ct_fbp_backproject",
            "ct_fbp_backproject_transpose", "ct_fbp_run", "ct_sirt_weights_views", "ct_sirt_step_views",
@@ -88,6 +89,8 @@ def lib():
         L.ct_geom_view_table.argtypes = [vp, P(GeomDesc), P(c.c_double)]
         L.ct_geom_adjoint_range.argtypes = [vp, P(GeomDesc), c.c_int, P(c.c_double), P(c.c_int32)]
         L.ct_project.argtypes = [vp, vp, vp, vp]
+        L.ct_project_ws.argtypes = [vp, vp, vp, vp, c.c_size_t, vp]
+        L.ct_forward_workspace_size.argtypes = [vp, P(GeomDesc), P(c.c_size_t)]
         L.ct_backproject.argtypes = [vp, vp, vp, vp]
         L.ct_backproject_atomic.argtypes = [vp, vp, vp, vp]
         L.ct_project_region.argtypes = [vp, vp, Region, c.c_int64, c.c_int64, vp, c.c_int, vp]
@@ -333,6 +336,33 @@ def ct_project(g: Geometry, vol, sino, stream=None):
     _check(lib().ct_project(g.handle, _ptr(vol, g.vol_shape, "vol"),
                             _ptr(sino, g.sino_shape, "sino"), _stream(stream)))
     return sino
+
+
+def ct_forward_workspace_size(g: Geometry = None, desc_args=None) -> int:
+    """Bytes of ct_project_ws workspace, from a handle or (desc_args: beam,
+    vol_shape, voxel_spacing, det_shape, det_spacing, frames) on the host."""
+    n = ctypes.c_size_t(0)
+    if g is not None:
+        _check(lib().ct_forward_workspace_size(g.handle, None, ctypes.byref(n)))
+    else:
+        d, fr = make_desc(*desc_args)
+        _check(lib().ct_forward_workspace_size(None, ctypes.byref(d), ctypes.byref(n)))
+    return int(n.value)
+
+
+def ct_project_ws(g: Geometry, vol, sino, work, stream=None):
+    """Forward projection with the volume copies in `work` (a device tensor of
+    at least ct_forward_workspace_size(g) bytes, 256-byte aligned, or None when
+    that size is 0); the handle is only read."""
+    if work is None:
+        ptr, nb = None, 0
+    else:
+        import torch
+        if not isinstance(work, torch.Tensor) or not work.is_cuda or not work.is_contiguous():
+            raise ValueError("work must be a contiguous device tensor")
+        ptr, nb = ctypes.c_void_p(work.data_ptr()), work.numel() * work.element_size()
+    _check(lib().ct_project_ws(g.handle, _ptr(vol, g.vol_shape, "vol"), _ptr(sino, g.sino_shape, "sino"), ptr,
+                               nb, _stream(stream)))
 
 
 def ct_backproject(g: Geometry, sino, vol, stream=None):

@@ -530,6 +530,64 @@ ct_status_t ct_project(ct_geom_t g, const float *vol, float *sino, ct_stream_t s
     return launched(launch_project(lg(g), vol, sino, (hipStream_t)stream), "ct_project launch");
 }
 
+// Workspace of ct_project_ws: the y-fastest copy (if a view gathers from it)
+// then the z-fastest one, each volume-sized and 256-byte aligned.
+static size_t layout_copy_bytes(size_t nvox) { return (nvox * sizeof(float) + 255) & ~size_t(255); }
+
+static size_t forward_workspace(bool yf, bool zf, size_t nvox) {
+    return (size_t)(yf ? 1 : 0) * layout_copy_bytes(nvox) + (size_t)(zf ? 1 : 0) * layout_copy_bytes(nvox);
+}
+
+ct_status_t ct_forward_workspace_size(ct_geom_t g, const ct_geom_desc_t *desc, size_t *bytes) {
+    if (!bytes) return fail(CT_E_NULL, "bytes must be non-NULL");
+    if (g) {
+        if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+        *bytes = forward_workspace(g->need_yf, g->need_zf, full_voxels(g));
+        set_error("");
+        return CT_OK;
+    }
+    GeomHost h;
+    const char *why = "";
+    ct_status_t st = validate_desc(desc, &h, &why);
+    if (st != CT_OK) return fail(st, why);
+    std::vector<double> table;
+    try {
+        table.assign((size_t)h.n_views * CT_VIEW_TABLE_STRIDE, 0.0);
+    } catch (...) {
+        return fail(CT_E_NOMEM, "host allocation failed");
+    }
+    build_view_table(desc, h, table.data());
+    bool yf = false, zf = false;
+    for (int64_t k = 0; k < h.n_views; ++k) {
+        const double lay = table[(size_t)k * CT_VIEW_TABLE_STRIDE + VT_LAYOUT];
+        yf = yf || lay == 1.0;
+        zf = zf || lay == 2.0;
+    }
+    *bytes = forward_workspace(yf, zf, (size_t)h.D * h.H * h.W);
+    set_error("");
+    return CT_OK;
+}
+
+ct_status_t ct_project_ws(ct_geom_t g, const float *vol, float *sino, void *work, size_t work_bytes,
+                          ct_stream_t stream) {
+    if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+    if (!vol || !sino) return fail(CT_E_NULL, "vol and sino must be non-NULL");
+    const size_t need = forward_workspace(g->need_yf, g->need_zf, full_voxels(g));
+    if (need > 0 && !work) return fail(CT_E_NULL, "work must be non-NULL (ct_forward_workspace_size > 0)");
+    if (work_bytes < need) return fail(CT_E_ARG, "work_bytes is below ct_forward_workspace_size");
+    if (((uintptr_t)work & 255u) != 0) return fail(CT_E_ARG, "work must be 256-byte aligned");
+    Span V{vol, vol_bytes(g)}, S{sino, sino_bytes(g)}, Wk{work, need};
+    ct_status_t st = need > 0 ? check_alias({{V, false}, {S, true}, {Wk, true}})
+                              : check_alias({{V, false}, {S, true}});
+    if (st != CT_OK) return st;
+    if ((st = ensure_device(g)) != CT_OK) return st;
+    LaunchGeom l = lg(g);
+    char *w = (char *)work;
+    l.vol_yf = g->need_yf ? (float *)w : nullptr;
+    l.vol_zf = g->need_zf ? (float *)(w + (g->need_yf ? layout_copy_bytes(full_voxels(g)) : 0)) : nullptr;
+    return launched(launch_project(l, vol, sino, (hipStream_t)stream), "ct_project_ws launch");
+}
+
 ct_status_t ct_backproject(ct_geom_t g, const float *sino, float *vol, ct_stream_t stream) {
     if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
     if (!vol || !sino) return fail(CT_E_NULL, "vol and sino must be non-NULL");
