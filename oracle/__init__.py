@@ -275,6 +275,26 @@ def sirt(g: Geometry, y, x0=None, n_iter: int = 1, relax: float = 1.0,
 # with alpha = 0 when q = 0 and beta = 0 when gamma = 0.
 # ----------------------------------------------------------------------------
 
+def cgls_step(g: Geometry, x, r, s, p, gamma: float, nthreads: int | None = None) -> dict:
+    """One CGLS iteration from the state (x, r, s, p, gamma): returns the new
+    x, r, s, p, the q = A p it used, and alpha, beta, gamma, qq = ||q||^2,
+    rr = ||r||^2 (after the step)."""
+    x = _as64(x).reshape(g.vol_shape)
+    r = _as64(r).reshape(g.sino_shape)
+    p = _as64(p).reshape(g.vol_shape)
+    q = project(g, p, nthreads)
+    qq = float(np.sum(q * q))
+    alpha = gamma / qq if qq > 0 else 0.0
+    x = x + alpha * p
+    r = r - alpha * q
+    s = backproject(g, r, nthreads)
+    gnew = float(np.sum(s * s))
+    beta = gnew / gamma if gamma > 0 else 0.0
+    p = s + beta * p
+    return {"x": x, "r": r, "s": s, "p": p, "q": q, "alpha": alpha, "beta": beta, "gamma": gnew,
+            "qq": qq, "rr": float(np.sum(r * r))}
+
+
 def cgls(g: Geometry, y, x0=None, n_iter: int = 1, nthreads: int | None = None):
     """Returns (x, hist): hist holds per iteration alpha, beta, gamma (after the
     step), qq = ||q||^2 and rr = ||r||^2 (after the step), plus the start's
@@ -288,17 +308,8 @@ def cgls(g: Geometry, y, x0=None, n_iter: int = 1, nthreads: int | None = None):
     hist = {"gamma0": gamma, "rr0": float(np.sum(r * r)),
             "alpha": [], "beta": [], "gamma": [], "qq": [], "rr": []}
     for _ in range(n_iter):
-        q = project(g, p, nthreads)
-        qq = float(np.sum(q * q))
-        alpha = gamma / qq if qq > 0 else 0.0
-        x = x + alpha * p
-        r = r - alpha * q
-        s = backproject(g, r, nthreads)
-        gnew = float(np.sum(s * s))
-        beta = gnew / gamma if gamma > 0 else 0.0
-        p = s + beta * p
-        gamma = gnew
-        for k, v in (("alpha", alpha), ("beta", beta), ("gamma", gamma), ("qq", qq),
-                     ("rr", float(np.sum(r * r)))):
-            hist[k].append(v)
+        st = cgls_step(g, x, r, s, p, gamma, nthreads)
+        x, r, s, p, gamma = st["x"], st["r"], st["s"], st["p"], st["gamma"]
+        for k in ("alpha", "beta", "gamma", "qq", "rr"):
+            hist[k].append(st[k])
     return x, hist

@@ -252,3 +252,44 @@ def test_cgls_full_size_first_step(config):
     rr1 = sc0["rr"] - alpha * sc0["gamma"]
     say(f"C{config} CGLS ||r1||^2 {sc['rr']:.6e} recurrence {rr1:.6e}")
     assert abs(sc["rr"] - rr1) <= 1e-4 * sc0["rr"]
+
+
+def _step_local(wl, y, steps, x0=None):
+    """Each GPU step against one oracle step from the GPU's own state: the
+    oracle reads the GPU's (x, r, s, p, gamma) after step k and takes step k+1;
+    the GPU's state after step k+1 must match it to 1e-5.  No amplification
+    across steps enters this bar, only the rounding of one step."""
+    gc = GpuCgls(wl, y, x0)
+    og = oracle.Geometry.from_workload(wl)
+    worst = 0.0
+    for k in range(steps):
+        x, r, s, p = host(gc.x), host(gc.r), host(gc.s), host(gc.p)
+        gamma = gc.scalars()["gamma"]
+        ref = oracle.cgls_step(og, x, r, s, p, gamma)
+        gc.step()
+        sc = gc.scalars()
+        errs = {n: rel(host(getattr(gc, n)), ref[n]) for n in ("x", "r", "s", "p", "q")}
+        errs.update({n: abs(sc[n] - ref[n]) / max(abs(ref[n]), 1e-300) for n in SCALARS})
+        say(f"{wl.name} step {k + 1}: " + ", ".join(f"{n} {v:.1e}" for n, v in errs.items()))
+        for n, v in errs.items():
+            assert v <= 1e-5, (k + 1, n, v)
+        worst = max(worst, max(errs.values()))
+    return worst
+
+
+@pytest.mark.parametrize("beam", [W.BEAM_PARALLEL2D, W.BEAM_FAN2D, W.BEAM_CONE, W.BEAM_PARALLEL3D])
+def test_step_local_parity_tiny(beam):
+    wl = _tiny(beam, 60 + beam)
+    rng = np.random.default_rng(beam)
+    y = rng.uniform(0, 1, wl.sino_shape).astype(np.float32)
+    _step_local(wl, y, 6)
+    x0 = rng.uniform(0, 1, wl.vol_shape).astype(np.float32)
+    _step_local(wl, y, 3, x0=x0)
+
+
+@pytest.mark.parametrize("config", [2, 3])
+def test_step_local_parity_c2_c3(config):
+    wl = W.make_workload(config)
+    og = oracle.Geometry.from_workload(wl)
+    y = oracle.project(og, W.make_phantom(wl)).astype(np.float32)
+    _step_local(wl, y, 6 if config == 2 else 3)
