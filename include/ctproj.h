@@ -10,8 +10,9 @@
  *          pixel, no detector-area integration: "Trajectories and Geometry" >
  *          "Parameterized detector surfaces").
  *   A^T  : its matched adjoint (backprojection), the exact transpose of A
- *          (diffct documentation, Projector.backproject: "Apply the matched
- *          adjoint"; Quickstart: "matched adjoint A^T", "not an inverse").
+ *          (diffct documentation: Projector.backproject applies the matched
+ *          adjoint; the Quickstart pairs A with it and notes that it does not
+ *          invert A).
  *   SIRT : x <- x + relax * C A^T R (y - A x) with R = 1/(A 1) per ray and
  *          C = 1/(A^T 1) per voxel, each 0 where the sum is 0 (the pages name
  *          a SIRT solver -- diffct "API Reference" > "Numerical Solvers",
@@ -29,8 +30,8 @@
  *       det_center + (u - (U-1)/2) du det_u + (v - (V-1)/2) dv det_v.
  *   - fan/cone rays are the segment from the source to the pixel centre;
  *     parallel and parallel3d rays are infinite lines through the pixel
- *     (Projector class reference: "its infinite ray lines pass through
- *     detector pixels").
+ *     (the Projector class reference describes parallel3d rays as unbounded
+ *     lines through the detector pixels).
  *   - Voxels are half-open boxes [lo + k s, lo + (k+1) s): a ray lying exactly
  *     on a lattice plane belongs to the higher-index cell.
  *
@@ -385,7 +386,9 @@ typedef struct {
  * Errors: CT_E_NULL, CT_E_ARG (beam, window, pad, short scan on parallel, a
  * span too short, an isocentre that cannot be estimated), CT_E_SHAPE,
  * CT_E_RANGE (also a cone detector with (U + 1)(V + 2) >= 2^29, whose one-view
- * staging would pass 32-bit byte offsets), CT_E_NONFINITE, CT_E_NOMEM, CT_E_HIP. */
+ * staging would pass 32-bit byte offsets, or with V + 2 >= 2^20, whose row
+ * stride would pass the gather's 24-bit offset arithmetic), CT_E_NONFINITE,
+ * CT_E_NOMEM, CT_E_HIP. */
 ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles,
                           const double *angular_weights, const ct_fbp_opts_t *opts, ct_fbp_t *out);
 ct_status_t ct_fbp_destroy(ct_fbp_t f);

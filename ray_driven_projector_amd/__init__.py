@@ -605,7 +605,10 @@ def ct_cgls_scalars(g: Geometry, work, stream=None) -> dict:
 
 
 def ct_count_intersections(g: Geometry, per_ray=None, stream=None) -> int:
-    """Number of (ray, voxel) pairs with positive float32 length (syncs the stream)."""
+    """Number of (ray, voxel) pairs the traversal visits: per ray the lattice-plane
+    crossings inside the volume plus one, from float64 entry and exit cells
+    (equal to the pairs of positive length except where a ray crosses two planes
+    at exactly the same point).  Syncs the stream."""
     import torch
     total = ctypes.c_uint64(0)
     p = ctypes.c_void_p(0)

@@ -908,6 +908,10 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     // cone staging: one view's (U + 1)(V + 2) 8-byte pairs take 32-bit byte offsets
     if (h.beam == CT_CONE && (h.U + 1) * (h.V + 2) >= (int64_t(1) << 29))
         return ffail(CT_E_RANGE, "cone detector too large: (U + 1)(V + 2) must be < 2^29");
+    // the gather forms its byte offsets with a signed 24-bit multiply-add whose
+    // row operand is 8 (V + 2)
+    if (h.beam == CT_CONE && h.V + 2 >= (int64_t(1) << 20))
+        return ffail(CT_E_RANGE, "cone detector too large: V + 2 must be < 2^20");
     if (!angular_weights && !angles) return ffail(CT_E_NULL, "angles (or angular_weights) must be given");
     if (opts->short_scan && !angles) return ffail(CT_E_NULL, "short scans need the angles");
     const int64_t nv = h.n_views;

@@ -179,6 +179,14 @@ def test_fbp_plan_arguments_are_checked_on_the_host(L):
     dp2, fr2 = rdp.make_desc(*_args(par))
     assert create(desc=dp2, angles=np.ascontiguousarray(W.angles(90, math.pi)), short_scan=1) == rdp.CT_E_ARG
     assert L.ct_fbp_create(ctypes.byref(d), th.ctypes.data_as(dp), None, None, ctypes.byref(out)) == rdp.CT_E_NULL
+    # a cone detector of 500 x (2^20 - 1): (U + 1)(V + 2) < 2^29, but the row
+    # stride 8 (V + 2) passes the gather's signed 24-bit offset arithmetic
+    tall = W.Workload("tall", W.BEAM_CONE, (4, 4, 4), (1.0, 1.0, 1.0), (500, (1 << 20) - 1), (1.0, 1e-5),
+                      W.helix_cone(2, 100.0, 150.0, 0.0, 1.0))
+    assert (500 + 1) * ((1 << 20) + 1) < 1 << 29
+    dt, frt = rdp.make_desc(*_args(tall))
+    assert create(desc=dt, angles=np.ascontiguousarray(W.angles(2, 2 * math.pi))) == rdp.CT_E_RANGE
+    assert "2^20" in rdp.last_error()
 
 
 def test_bench_refuses_several_gpus():
