@@ -44,6 +44,24 @@ Readings where the pages give no formula (each listed in the design notes):
   - Fan/cone: a point at or behind the source (U(x) <= 0) lies on no ray of
     that view (the rays run from the source towards the detector) and gathers
     nothing from it.
+  - Overrides (same page, the paragraph on the complete APIs): a caller's
+    projection weights take the place of the cosine weight of step 1 (Parker's
+    weights, when asked for, still multiply); a caller's filter response, of
+    length pad_factor * U // 2 + 1 in physical units, takes the place of the
+    windowed multiplier of step 2.
+
+Helical approximation (same page, "Helical approximation"): the rows are
+filtered once (steps 1-2, no angular weight), and each axial slice s is then
+gathered as in step 4 with its own per-view weights w[s, i].  Reading of the
+window: the source crosses the slice centre z_s at the angle theta_c(s), found
+by linear interpolation of the (source z, unwrapped angle) samples; the slice
+integrates over the full turn [theta_c - pi, theta_c + pi] with the 1/2
+redundancy factor, by the trapezoidal rule on the sampled angles, i.e.
+w[s, i] = 1/2 * integral over the window of the hat function of sample i (the
+piecewise-linear interpolation basis on the angles).  The hats sum to 1 on the
+scanned range, so each slice's weights sum to pi.  A slice whose centre lies
+outside the source's z range, or whose window leaves the scanned angles, is
+rejected.
 """
 from __future__ import annotations
 
@@ -94,12 +112,19 @@ def ramp_multiplier(P: int, spacing: float, window: str = "ram-lak") -> np.ndarr
 
 
 def ramp_filter(p: np.ndarray, spacing: float, pad_factor: int = 2, window: str = "ram-lak",
-                axis: int = 1) -> np.ndarray:
-    """Filter along `axis` (zero-padded to pad_factor * N, rFFT multiplier, cropped)."""
+                axis: int = 1, response=None) -> np.ndarray:
+    """Filter along `axis` (zero-padded to pad_factor * N, rFFT multiplier, cropped).
+    response: the caller's multiplier (length pad_factor * N // 2 + 1), in place
+    of the windowed ramp."""
     p = np.moveaxis(np.asarray(p, dtype=np.float64), axis, -1)
     N = p.shape[-1]
     P = pad_factor * N
-    M = ramp_multiplier(P, spacing, window)
+    if response is None:
+        M = ramp_multiplier(P, spacing, window)
+    else:
+        M = np.asarray(response, dtype=np.float64)
+        if M.shape != (P // 2 + 1,):
+            raise ValueError(f"filter response must have pad_factor * U // 2 + 1 = {P // 2 + 1} values")
     q = np.fft.irfft(np.fft.rfft(p, n=P, axis=-1) * M, n=P, axis=-1)[..., :N]
     return np.moveaxis(q, -1, axis)
 
@@ -244,12 +269,21 @@ def parker_weights(wl, angles) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def filter_sinogram(wl, sino, angles, window="ram-lak", pad_factor=2, short_scan=False,
-                    ang_weights=None) -> np.ndarray:
-    """Steps 1-3: pre-weights, ramp filter along u, angular weights."""
-    p = np.asarray(sino, dtype=np.float64) * cosine_weights(wl)
+                    ang_weights=None, projection_weights=None, filter_response=None) -> np.ndarray:
+    """Steps 1-3: pre-weights, ramp filter along u, angular weights.
+    projection_weights ((U, V) or (views, U, V)) replace the cosine weight;
+    filter_response replaces the windowed multiplier."""
+    if projection_weights is None:
+        pre = cosine_weights(wl)
+    else:
+        pw = np.asarray(projection_weights, dtype=np.float64)
+        if pw.shape not in (tuple(wl.det_shape), tuple(wl.sino_shape)):
+            raise ValueError("projection weights must have shape (U, V) or (views, U, V)")
+        pre = np.broadcast_to(pw, wl.sino_shape)
+    p = np.asarray(sino, dtype=np.float64) * pre
     if short_scan:
         p = p * parker_weights(wl, angles)[:, :, None]
-    q = ramp_filter(p, wl.det_spacing[0], pad_factor, window, axis=1)
+    q = ramp_filter(p, wl.det_spacing[0], pad_factor, window, axis=1, response=filter_response)
     w = angular_weights(angles, wl.beam, short_scan) if ang_weights is None else \
         np.asarray(ang_weights, dtype=np.float64)
     return q * w[:, None, None]
@@ -358,7 +392,125 @@ def weighted_backproject_T(wl, vol, iso=None) -> np.ndarray:
 
 
 def fbp(wl, sino, angles, window="ram-lak", pad_factor=2, short_scan=False, iso=None,
-        ang_weights=None) -> np.ndarray:
+        ang_weights=None, projection_weights=None, filter_response=None) -> np.ndarray:
     """FBP (parallel2d, fan2d) or FDK (cone): filter, then the weighted backprojection."""
-    q = filter_sinogram(wl, sino, angles, window, pad_factor, short_scan, ang_weights)
+    q = filter_sinogram(wl, sino, angles, window, pad_factor, short_scan, ang_weights,
+                        projection_weights, filter_response)
     return weighted_backproject(wl, q, iso)
+
+
+# ---------------------------------------------------------------------------
+# helical approximation
+# ---------------------------------------------------------------------------
+
+def _hat_integral(t, i, lo, hi) -> float:
+    """Integral over [lo, hi] of the hat function of node i on the increasing nodes t."""
+    total = 0.0
+    if i > 0:                                   # rising side, 0 at t[i-1] to 1 at t[i]
+        a, b = max(lo, t[i - 1]), min(hi, t[i])
+        if b > a:
+            L = t[i] - t[i - 1]
+            total += ((b - t[i - 1]) ** 2 - (a - t[i - 1]) ** 2) / (2 * L)
+    if i < len(t) - 1:                          # falling side, 1 at t[i] to 0 at t[i+1]
+        a, b = max(lo, t[i]), min(hi, t[i + 1])
+        if b > a:
+            L = t[i + 1] - t[i]
+            total += ((t[i + 1] - a) ** 2 - (t[i + 1] - b) ** 2) / (2 * L)
+    return total
+
+
+def helical_window_centres(wl, angles) -> np.ndarray:
+    """theta_c per slice: the unwrapped angle at which the source crosses the
+    slice centre, by linear interpolation of the (source z, angle) samples."""
+    th = np.asarray(angles, dtype=np.float64)
+    zs = wl.frames[:, 2]
+    if wl.beam != CONE:
+        raise ValueError("the helical approximation is a cone-beam method")
+    if len(th) != wl.n_views or len(th) < 2:
+        raise ValueError("one unwrapped angle per view, at least two views")
+    dth, dz = np.diff(th), np.diff(zs)
+    if not (np.all(dth > 0) or np.all(dth < 0)):
+        raise ValueError("the unwrapped angles must be strictly monotone")
+    if not (np.all(dz > 0) or np.all(dz < 0)):
+        raise ValueError("the source z must be strictly monotone")
+    sz = 1.0 if dz[0] > 0 else -1.0
+    z_c = voxel_centres(wl)[0]
+    out = np.empty(len(z_c))
+    for s, zc in enumerate(z_c):
+        key = sz * zs
+        if not (key[0] <= sz * zc <= key[-1]):
+            raise ValueError(f"slice {s} (z = {zc}) lies outside the source's z range")
+        k = min(int(np.searchsorted(key, sz * zc, side="right")) - 1, len(th) - 2)
+        f = (zc - zs[k]) / (zs[k + 1] - zs[k])
+        out[s] = th[k] + f * (th[k + 1] - th[k])
+    return out
+
+
+def helical_view_weights(wl, angles) -> np.ndarray:
+    """(D, views) per-slice weights: half the integral of each sample's hat
+    function over the full turn centred at the slice's theta_c."""
+    th = np.asarray(angles, dtype=np.float64)
+    centres = helical_window_centres(wl, angles)
+    sa = 1.0 if th[-1] > th[0] else -1.0
+    t = sa * th                                # increasing
+    tol = 1e-9 * (1.0 + np.max(np.abs(t)))
+    w = np.zeros((len(centres), len(th)))
+    for s, tc in enumerate(sa * centres):
+        lo, hi = tc - math.pi, tc + math.pi
+        if lo < t[0] - tol or hi > t[-1] + tol:
+            raise ValueError(f"slice {s}: the full turn about its crossing angle leaves the scan")
+        lo, hi = max(lo, t[0]), min(hi, t[-1])
+        for i in range(len(t)):
+            w[s, i] = 0.5 * _hat_integral(t, i, lo, hi)
+    return w
+
+
+def helical_weighted_backproject(wl, q, weights, iso=None) -> np.ndarray:
+    """Step 4 with per-slice view weights: f_s(x) = sum_i w[s, i] * weight_i(x) *
+    interp(q_i, u_i(x), v_i(x)) for the voxels x of slice s."""
+    q = np.asarray(q, dtype=np.float64)
+    wts = np.asarray(weights, dtype=np.float64)
+    if wts.shape != (wl.vol_shape[0], wl.n_views):
+        raise ValueError("weights must have shape (D, views)")
+    iso = isocentre(wl) if iso is None else np.asarray(iso, dtype=np.float64)
+    z, y, x = voxel_centres(wl)
+    Z, Y, Xg = np.meshgrid(z, y, x, indexing="ij")
+    X = np.stack([Xg, Y, Z], axis=-1)
+    U, V = wl.det_shape
+    out = np.zeros(X.shape[:-1])
+    for i in range(wl.n_views):
+        u, v, wgt = _projection(wl, i, X, iso)
+        val = np.zeros_like(out)
+        for ju, jv, cf in _bilinear_taps(u, v, U, V):
+            val += cf * q[i, ju, jv]
+        out += wts[:, i][:, None, None] * wgt * val
+    return out
+
+
+def helical_weighted_backproject_T(wl, vol, weights, iso=None) -> np.ndarray:
+    """Transpose of helical_weighted_backproject."""
+    vol = np.asarray(vol, dtype=np.float64).reshape(wl.vol_shape)
+    wts = np.asarray(weights, dtype=np.float64)
+    if wts.shape != (wl.vol_shape[0], wl.n_views):
+        raise ValueError("weights must have shape (D, views)")
+    iso = isocentre(wl) if iso is None else np.asarray(iso, dtype=np.float64)
+    z, y, x = voxel_centres(wl)
+    Z, Y, Xg = np.meshgrid(z, y, x, indexing="ij")
+    X = np.stack([Xg, Y, Z], axis=-1)
+    U, V = wl.det_shape
+    out = np.zeros(wl.sino_shape)
+    for i in range(wl.n_views):
+        u, v, wgt = _projection(wl, i, X, iso)
+        g = wts[:, i][:, None, None] * wgt * vol
+        for ju, jv, cf in _bilinear_taps(u, v, U, V):
+            np.add.at(out[i], (ju.ravel(), jv.ravel()), (cf * g).ravel())
+    return out
+
+
+def helical_fdk(wl, sino, angles, window="ram-lak", pad_factor=2, iso=None, projection_weights=None,
+                filter_response=None) -> np.ndarray:
+    """Filter the rows once (no angular weight), then gather each slice with its
+    helical view weights."""
+    q = filter_sinogram(wl, sino, angles, window, pad_factor, False, np.ones(wl.n_views),
+                        projection_weights, filter_response)
+    return helical_weighted_backproject(wl, q, helical_view_weights(wl, angles), iso)

@@ -13,7 +13,9 @@ parameters, the half-open cell rule, the lattice origin, the adjoint's piece
 midpoint and its last piece, ray-id decoding of the sampled-ray forward, the
 surface normal, the row-chord layout, the brute-force cell boxes, SIRT and
 CGLS recurrences, the ramp filter's taps and windows, the FDK weights,
-interpolation and sampled-voxel decoding.
+interpolation and sampled-voxel decoding; the filter-response and
+projection-weight overrides; the helical window's width, redundancy half,
+quadrature, crossing angle and per-slice indexing.
 
 Equivalent mutations (changes that cannot alter any result) are not listed:
 for instance the start-cell rule of an axis at its entry face, where the
@@ -37,6 +39,7 @@ PY_SRC = {"oracle": os.path.join(ROOT, "oracle", "__init__.py"),
 
 PINS = os.path.join("tests", "test_oracle_pins.py")
 FBP_PINS = os.path.join("tests", "test_oracle_fbp.py")
+EXT_PINS = os.path.join("tests", "test_oracle_fbp_ext.py")
 # the two sampled-line-integral pins take most of the pin file's time; every
 # mutant below is caught without them
 FAST = "not sampled_line_integral"
@@ -106,8 +109,7 @@ MUTANTS = [
      "return 0.46 + 0.54 * np.cos(2 * math.pi * f)", FBP_PINS),
     ("Hann as cosine", "oracle.fbp", "return 0.5 + 0.5 * np.cos(2 * math.pi * f)",
      "return np.cos(math.pi * f)", FBP_PINS),
-    ("no cosine pre-weight", "oracle.fbp", "p = np.asarray(sino, dtype=np.float64) * cosine_weights(wl)",
-     "p = np.asarray(sino, dtype=np.float64)", FBP_PINS),
+    ("no cosine pre-weight", "oracle.fbp", "pre = cosine_weights(wl)", "pre = np.ones(wl.sino_shape)", FBP_PINS),
     ("Parker fan angle sign", "oracle.fbp", "return rotation_sense(wl) * np.arctan2(cross, dot)",
      "return -rotation_sense(wl) * np.arctan2(cross, dot)", FBP_PINS),
     ("angular weights without the redundancy half", "oracle.fbp",
@@ -124,8 +126,30 @@ MUTANTS = [
     ("sampled voxels: x and y decoded swapped", "oracle.fbp",
      "X = np.stack([x[ids % Wd], y[(ids // Wd) % H], z[ids // (Wd * H)]], axis=-1)",
      "X = np.stack([x[(ids // H) % Wd], y[ids % H], z[ids // (Wd * H)]], axis=-1)", FBP_PINS),
-    ("scatter index u/v swapped", "oracle.fbp", "np.add.at(out[i], (ju.ravel(), jv.ravel())",
-     "np.add.at(out[i], (jv.ravel() % U, ju.ravel() % V)", FBP_PINS),
+    ("scatter index u/v swapped", "oracle.fbp", "np.add.at(out[i], (ju.ravel(), jv.ravel()), (wgt * cf * vol)",
+     "np.add.at(out[i], (jv.ravel() % U, ju.ravel() % V), (wgt * cf * vol)", FBP_PINS),
+    ("filter response ignored", "oracle.fbp", "M = np.asarray(response, dtype=np.float64)",
+     "M = ramp_multiplier(P, spacing, window)", EXT_PINS),
+    ("projection weights ignored", "oracle.fbp", "pre = np.broadcast_to(pw, wl.sino_shape)",
+     "pre = cosine_weights(wl)", EXT_PINS),
+    ("helical window of half a turn", "oracle.fbp", "lo, hi = tc - math.pi, tc + math.pi",
+     "lo, hi = tc - math.pi / 2, tc + math.pi / 2", EXT_PINS),
+    ("helical weights without the redundancy half", "oracle.fbp",
+     "w[s, i] = 0.5 * _hat_integral(t, i, lo, hi)", "w[s, i] = _hat_integral(t, i, lo, hi)", EXT_PINS),
+    ("hat integral, rising side over L", "oracle.fbp",
+     "total += ((b - t[i - 1]) ** 2 - (a - t[i - 1]) ** 2) / (2 * L)",
+     "total += ((b - t[i - 1]) ** 2 - (a - t[i - 1]) ** 2) / L", EXT_PINS),
+    ("crossing angle of the sample below", "oracle.fbp", "out[s] = th[k] + f * (th[k + 1] - th[k])",
+     "out[s] = th[k]", EXT_PINS),
+    ("crossing fraction from the upper sample", "oracle.fbp", "f = (zc - zs[k]) / (zs[k + 1] - zs[k])",
+     "f = (zs[k + 1] - zc) / (zs[k + 1] - zs[k])", EXT_PINS),
+    ("slice weights of the mirrored slice", "oracle.fbp", "out += wts[:, i][:, None, None] * wgt * val",
+     "out += wts[::-1, i][:, None, None] * wgt * val", EXT_PINS),
+    ("helical scatter drops the slice weights", "oracle.fbp", "g = wts[:, i][:, None, None] * wgt * vol",
+     "g = wgt * vol", EXT_PINS),
+    ("helical FDK keeps the angular weights", "oracle.fbp",
+     "q = filter_sinogram(wl, sino, angles, window, pad_factor, False, np.ones(wl.n_views),",
+     "q = filter_sinogram(wl, sino, angles, window, pad_factor, False, None,", EXT_PINS),
 ]
 
 
@@ -167,7 +191,7 @@ def _run_mutant(tmp, idx, name, target, old, new, pins):
 def test_every_mutant_fails_a_pin(tmp_path):
     # the unmutated oracle passes the same selection (a control run)
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "tests.mutant_plugin", "-m", "not gpu",
-                        "-k", FAST, PINS, FBP_PINS], cwd=ROOT, capture_output=True, text=True, timeout=600)
+                        "-k", FAST, PINS, FBP_PINS, EXT_PINS], cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:]
     with ThreadPoolExecutor(max_workers=min(8, oracle.default_threads())) as ex:
         results = list(ex.map(lambda a: _run_mutant(str(tmp_path), *a),
