@@ -395,6 +395,67 @@ ct_status_t ct_fbp_destroy(ct_fbp_t f);
 /* The plan's isocentre (3 doubles) and angular weights (n_views doubles); either may be NULL. */
 ct_status_t ct_fbp_info(ct_fbp_t f, double *iso, double *angular_weights);
 
+/* Overrides of the filter stage and per-slice view weights (diffct
+ * documentation, "Differentiable analytical reconstruction": the paragraph on
+ * the complete APIs, and "Helical approximation").  Every pointer is HOST
+ * memory read during ct_fbp_create_ext only; NULL keeps the default.
+ *   filter_response: pad_factor * U / 2 + 1 real multipliers M_k (k = 0..P/2,
+ *     P = pad_factor * U) in physical units, used in place of the windowed
+ *     Ram-Lak multiplier of step 2 (opts->window is then ignored);
+ *   projection_weights: pre-weights used in place of the cosine weight of
+ *     step 1 (Parker's weights, when short_scan is set, still multiply);
+ *     U * V values (index u * V + v) shared by every view, or, when
+ *     projection_weights_per_view is 1, n_views * U * V values (view-major);
+ *   slice_weights (cone only): D * n_views values, w[s * n_views + i] the
+ *     weight of view i for the voxels of axial slice s (z index s).  Step 3
+ *     then applies no angular weight and step 4 multiplies view i's
+ *     contribution to a voxel of slice s by w[s][i]; the transpose scatters
+ *     with the same factors.  ct_helical_view_weights computes the helical
+ *     approximation's weights; any others may be passed.  Not combinable
+ *     with angular_weights or short_scan.  Views whose weights are 0 for a
+ *     whole band of 64 slices are skipped there.
+ * reserved fields must be 0. */
+typedef struct {
+    const double *filter_response;
+    const double *projection_weights;
+    const double *slice_weights;
+    int32_t projection_weights_per_view;   /* 0: U * V shared values; 1: n_views * U * V */
+    int32_t direct_filter;    /* 1: step 2 always by direct circular convolution with the
+                                 P-periodic kernel; 0: through FFTs when P is a power of
+                                 two in [64, 4096] (the same filter either way) */
+    int64_t reserved[4];
+} ct_fbp_ext_t;
+
+/* ct_fbp_create with the overrides above (ext NULL: exactly ct_fbp_create).
+ * With slice_weights, angles may be NULL, and ct_fbp_info reports angular
+ * weights of 1.  Errors: those of ct_fbp_create, and CT_E_ARG (slice weights
+ * on a non-cone beam or with angular_weights / short_scan, a per-view or
+ * direct-filter flag other than 0 or 1, nonzero reserved fields), CT_E_NONFINITE (a non-finite
+ * override value). */
+ct_status_t ct_fbp_create_ext(const ct_geom_desc_t *desc, const double *angles,
+                              const double *angular_weights, const ct_fbp_opts_t *opts,
+                              const ct_fbp_ext_t *ext, ct_fbp_t *out);
+
+/* Per-slice view weights of the helical approximation (same page, "Helical
+ * approximation"): the rows are filtered once, and each axial slice is
+ * reconstructed from the full turn of views centred where the source crosses
+ * it, with the half redundancy factor.  Computed on the host in float64:
+ *   theta_c(s) = the unwrapped angle at which the source z (frames' a_z)
+ *     reaches the slice centre z_s (voxel-centre z), by linear interpolation
+ *     between the two samples around it;
+ *   w[s][i] = 1/2 * integral over [theta_c - pi, theta_c + pi] of the hat
+ *     function of view i (the piecewise-linear interpolation basis on the
+ *     angles), so that each slice's weights sum to pi.
+ * desc: a cone geometry (validated as by ct_geom_validate) with n_views >= 2;
+ * angles: HOST, n_views unwrapped radians, strictly monotone; the source z
+ * must be strictly monotone too.  weights: HOST, D * n_views doubles
+ * (slice-major), written on success only.
+ * Errors: CT_E_NULL, CT_E_ARG (beam not cone, fewer than 2 views, angles or
+ * source z not strictly monotone), CT_E_NONFINITE, CT_E_RANGE (a slice centre
+ * outside the source's z range, or a slice whose full turn leaves the
+ * scanned angles: incomplete windows are rejected). */
+ct_status_t ct_helical_view_weights(const ct_geom_desc_t *desc, const double *angles, double *weights);
+
 /* filtered = steps 1-3 of sino; (views, U, V) device buffers that must not overlap. */
 ct_status_t ct_fbp_filter(ct_fbp_t f, const float *sino, float *filtered, ct_stream_t stream);
 /* vol = step 4 of filtered (overwrites every voxel).  Cone: per batch of views,

@@ -33,7 +33,7 @@ EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_g
            "ct_project", "ct_project_ws", "ct_forward_workspace_size", "ct_backproject",
            "ct_backproject_atomic", "ct_project_region",
            "ct_backproject_region", "ct_project_host", "ct_backproject_host",
-           "ct_fbp_create", "ct_fbp_destroy", "ct_fbp_info", "ct_fbp_filter", "ct_fbp_backproject",
+           "ct_fbp_create", "ct_fbp_create_ext", "ct_helical_view_weights", "ct_fbp_destroy", "ct_fbp_info", "ct_fbp_filter", "ct_fbp_backproject",
            "ct_fbp_backproject_transpose", "ct_fbp_run", "ct_sirt_weights_views", "ct_sirt_step_views",
            "ct_sirt_weights",
            "ct_sirt_residual", "ct_sirt_update", "ct_sirt_step", "ct_sirt_update_bounded",
@@ -98,6 +98,8 @@ def lib():
         L.ct_project_host.argtypes = [vp, vp, vp, StreamPlan, vp]
         dp = P(c.c_double)
         L.ct_fbp_create.argtypes = [vp, dp, dp, vp, vp]
+        L.ct_fbp_create_ext.argtypes = [vp, dp, dp, vp, vp, vp]
+        L.ct_helical_view_weights.argtypes = [vp, dp, dp]
         L.ct_fbp_destroy.argtypes = [vp]
         L.ct_fbp_info.argtypes = [vp, dp, dp]
         L.ct_fbp_filter.argtypes = [vp, vp, vp, vp]
@@ -248,12 +250,36 @@ class FbpOpts(ctypes.Structure):
                 ("iso", ctypes.c_double * 3), ("reserved", ctypes.c_int64)]
 
 
+class FbpExt(ctypes.Structure):
+    _fields_ = [("filter_response", ctypes.POINTER(ctypes.c_double)),
+                ("projection_weights", ctypes.POINTER(ctypes.c_double)),
+                ("slice_weights", ctypes.POINTER(ctypes.c_double)),
+                ("projection_weights_per_view", ctypes.c_int32), ("direct_filter", ctypes.c_int32),
+                ("reserved", ctypes.c_int64 * 4)]
+
+
+def ct_helical_view_weights(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames, angles):
+    """(D, n_views) per-slice weights of the helical approximation (host, float64)."""
+    d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
+    th = np.ascontiguousarray(angles, dtype=np.float64)
+    if th.shape != (fr.shape[0],):
+        raise ValueError("angles must have one value per view")
+    out = np.zeros((int(vol_shape[0]), fr.shape[0]))
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(lib().ct_helical_view_weights(ctypes.byref(d), th.ctypes.data_as(dp), out.ctypes.data_as(dp)))
+    return out
+
+
 class FBP:
     """A ct_fbp_t plan: analytical FBP (parallel2d, fan2d) / FDK (cone).
-    angles: n_views radians (host); angular_weights: optional override."""
+    angles: n_views radians (host); angular_weights: optional override.
+    filter_response (pad_factor * U // 2 + 1), projection_weights ((U, V) or
+    (views, U, V)) and slice_weights ((D, views), cone) are the overrides of
+    ct_fbp_create_ext; direct_filter keeps step 2 on the direct convolution."""
 
     def __init__(self, beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames, angles=None,
-                 window="ram-lak", pad_factor=2, short_scan=False, iso=None, angular_weights=None):
+                 window="ram-lak", pad_factor=2, short_scan=False, iso=None, angular_weights=None,
+                 filter_response=None, projection_weights=None, slice_weights=None, direct_filter=False):
         d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
         o = FbpOpts()
         o.window = WINDOWS[window]
@@ -271,11 +297,35 @@ class FBP:
         for arr, name in ((self._angles, "angles"), (self._aw, "angular_weights")):
             if arr is not None and arr.shape != (n,):
                 raise ValueError(f"{name} must have one value per view")
+        U, V = int(det_shape[0]), int(det_shape[1])
+        x = FbpExt()
+        x.direct_filter = int(bool(direct_filter))
+        self._ext = []
+        if filter_response is not None:
+            r = np.ascontiguousarray(filter_response, dtype=np.float64)
+            if r.shape != (int(pad_factor) * U // 2 + 1,):
+                raise ValueError("filter_response must have pad_factor * U // 2 + 1 values")
+            x.filter_response = r.ctypes.data_as(dp)
+            self._ext.append(r)
+        if projection_weights is not None:
+            pw = np.ascontiguousarray(projection_weights, dtype=np.float64)
+            if pw.shape not in ((U, V), (n, U, V)):
+                raise ValueError("projection_weights must have shape (U, V) or (views, U, V)")
+            x.projection_weights = pw.ctypes.data_as(dp)
+            x.projection_weights_per_view = 1 if pw.ndim == 3 else 0
+            self._ext.append(pw)
+        if slice_weights is not None:
+            sw = np.ascontiguousarray(slice_weights, dtype=np.float64)
+            if sw.shape != (int(vol_shape[0]), n):
+                raise ValueError("slice_weights must have shape (D, views)")
+            x.slice_weights = sw.ctypes.data_as(dp)
+            self._ext.append(sw)
         h = ctypes.c_void_p()
-        _check(lib().ct_fbp_create(ctypes.byref(d),
-                                   self._angles.ctypes.data_as(dp) if self._angles is not None else None,
-                                   self._aw.ctypes.data_as(dp) if self._aw is not None else None,
-                                   ctypes.byref(o), ctypes.byref(h)))
+        _check(lib().ct_fbp_create_ext(ctypes.byref(d),
+                                       self._angles.ctypes.data_as(dp) if self._angles is not None else None,
+                                       self._aw.ctypes.data_as(dp) if self._aw is not None else None,
+                                       ctypes.byref(o), ctypes.byref(x), ctypes.byref(h)))
+        self._ext = None
         self._h = h
         self.vol_shape = tuple(int(x) for x in vol_shape)
         self.sino_shape = (n, int(det_shape[0]), int(det_shape[1]))
@@ -284,6 +334,15 @@ class FBP:
     def from_workload(cls, wl, angles=None, **kw) -> "FBP":
         return cls(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing, wl.frames,
                    angles, **kw)
+
+    @classmethod
+    def helical_from_workload(cls, wl, angles, **kw) -> "FBP":
+        """Helical FDK plan: the slice weights of ct_helical_view_weights for
+        these unwrapped angles (or kw["slice_weights"], the caller's own)."""
+        if kw.get("slice_weights") is None:
+            kw["slice_weights"] = ct_helical_view_weights(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape,
+                                                          wl.det_spacing, wl.frames, angles)
+        return cls.from_workload(wl, None, **kw)
 
     @property
     def handle(self):

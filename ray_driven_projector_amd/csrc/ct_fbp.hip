@@ -18,6 +18,12 @@
 // FDK distance weight is R D / U(x)^2 (U(x) = (x - a).n, D = (c - a).n,
 // R = (iso - a).n).  Parker weights follow Parker (1982).  Detector samples
 // outside the detector read as 0.
+//
+// Overrides and the helical approximation (same page, the paragraph on the
+// complete APIs and "Helical approximation"): a caller's filter response and
+// pre-weights stand in for the windowed ramp and the cosine weight, and
+// per-slice view weights (the helical full-turn windows, or the caller's) take
+// the place of the angular weights inside the gather.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -107,6 +113,8 @@ struct FilterArgs {
     const float *taps;     // 2 * U8 taps, tap j (|j| <= U8) at j + U8
     const float *fview;    // kFv floats per view
     const float *parker;   // n_views x U, or null
+    const float *pw;       // pre-weights replacing the cosine weight (index view * pw_stride + u V + v), or null
+    size_t pw_stride;      // 0 (one U x V array for every view) or U V
     int U, V, n_views, U8, VT, S;   // S: LDS row stride of the tile (floats)
     int two_d;
 };
@@ -148,7 +156,9 @@ __global__ __launch_bounds__(256) void fbp_filter_kernel(FilterArgs a) {
         if (u < U && view < a.n_views && v < V) {
             const float *fv = a.fview + (size_t)view * kFv;
             val = a.sino[((size_t)view * U + u) * V + v];
-            if (fv[11] != 0.f) {   // fan/cone: cosine weight
+            if (a.pw) {   // the caller's pre-weights
+                val *= a.pw[(size_t)view * a.pw_stride + (size_t)u * V + v];
+            } else if (fv[11] != 0.f) {   // fan/cone: cosine weight
                 const float ou = (float)u - 0.5f * (float)(U - 1);
                 const float ov = a.two_d ? 0.f : (float)v - 0.5f * (float)(V - 1);
                 const float px = fv[1] + ou * fv[4] + ov * fv[7];
@@ -230,6 +240,8 @@ struct FftArgs {
     const float *mul;      // multiplier M_k, k = 0..P/2
     const float *fview;
     const float *parker;
+    const float *pw;
+    size_t pw_stride;
     int U, V, n_views, P, L, npair;
     int two_d;
 };
@@ -272,7 +284,9 @@ __global__ __launch_bounds__(256) void fbp_fft_filter_kernel(FftArgs a) {
         if (u < U && view < a.n_views && v < V) {
             const float *fv = a.fview + (size_t)view * kFv;
             val = a.sino[((size_t)view * U + u) * V + v];
-            if (fv[11] != 0.f) {
+            if (a.pw) {   // the caller's pre-weights
+                val *= a.pw[(size_t)view * a.pw_stride + (size_t)u * V + v];
+            } else if (fv[11] != 0.f) {
                 const float ou = (float)u - 0.5f * (float)(U - 1);
                 const float ov = a.two_d ? 0.f : (float)v - 0.5f * (float)(V - 1);
                 const float px = fv[1] + ou * fv[4] + ov * fv[7];
@@ -398,6 +412,8 @@ struct BpArgs {
     int W, H, D, U, V, n_views;
     int view0, view1;    // the views this launch takes
     int accumulate;      // B: add to vol instead of overwriting it
+    const float *zw;     // per-slice view weights, zw[view * D + z] (3D with slice weights), else null
+    const int2 *zrange;  // per band of TZ slices: the views [x, y) with a nonzero weight there
     int nbx, nby, nbz;
     int two_d;
 };
@@ -509,9 +525,12 @@ __device__ __forceinline__ void view_consts(const double *p, double x0, double y
 // a row of the wave hold 16 consecutive planes, which for the usual cone
 // geometries land on neighbouring detector rows).  Views are taken in LDS
 // batches of kBpViews whose block-relative constants the first kBpViews
-// threads compute.
-template <bool TRANSPOSE, bool TWO_D, int ZR>
+// threads compute.  SLICEW (3D): each view's term for a voxel of slice z also
+// carries the weight zw[view][z] (16 lanes read 16 consecutive floats of the
+// view's row), and a block takes only the views of its band's range.
+template <bool TRANSPOSE, bool TWO_D, int ZR, bool SLICEW = false>
 __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
+    static_assert(!(SLICEW && TWO_D), "slice weights are for 3D volumes");
     __shared__ float cst[kBpViews * kBpConst];
     // tile: 3D 4 x 4 x (16 ZR) voxels (x, y, z); 2D 16 x 16
     constexpr int TX = TWO_D ? 16 : 4, TY = TWO_D ? 16 : 4, TZ = TWO_D ? 1 : 16 * ZR;
@@ -584,6 +603,16 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
         const float pwd = fmaf(c2.x, dz, fmaf(c1.w, dy, c1.z * dx));
         constexpr bool fast = decltype(fast_tag)::value;
         const size_t vbase = (size_t)(vb + k) * U;
+        // slice weights of the thread's voxels (a voxel past the last slice,
+        // which is neither read nor written, takes the last slice's)
+        float wz[ZR];
+#pragma unroll
+        for (int r = 0; r < ZR; ++r) wz[r] = 1.f;
+        if constexpr (SLICEW) {
+            const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(a.zw + (size_t)(vb + k) * a.D, (uint32_t)a.D * 4u);
+#pragma unroll
+            for (int r = 0; r < ZR; ++r) wz[r] = buffer_load(rz, (uint32_t)min(iz0 + 16 * r, a.D - 1) * 4u);
+        }
         if constexpr (!TWO_D && !TRANSPOSE) {
             // 3D gather from the view's padded pair-interleaved copy
             const uint32_t pv = (uint32_t)(U + 1) * (uint32_t)(V + 2) * 8u;
@@ -615,7 +644,8 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
                 // q(u, v), q(u + 1, v), q(u, v + 1), q(u + 1, v + 1) in one load
                 const float4 t = buffer_load4(rq, o);
                 const float s0 = fmaf(au, t.y - t.x, t.x), s1 = fmaf(au, t.w - t.z, t.z);
-                const float nacc = fmaf(rw * rw, fmaf(av, s1 - s0, s0), acc[r]);
+                const float wq = SLICEW ? rw * rw * wz[r] : rw * rw;
+                const float nacc = fmaf(wq, fmaf(av, s1 - s0, s0), acc[r]);
                 acc[r] = in ? nacc : acc[r];
             }
             return;
@@ -666,7 +696,7 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
                 const int ju0 = u0k ? iu : 0, ju1 = u1k ? iu + 1 : 0;
                 const int jv0 = v0k ? iv : 0, jv1 = v1k ? iv + 1 : 0;
                 const size_t r0 = (vbase + ju0) * V, r1 = (vbase + ju1) * V;
-                const float g = wgt * fz[r];
+                const float g = SLICEW ? wgt * wz[r] * fz[r] : wgt * fz[r];
                 if (g != 0.f) {
                     if (ku0 * kv0 != 0.f) atomicAdd(a.sino_out + r0 + jv0, g * ku0 * kv0);
                     if (ku0 * kv1 != 0.f) atomicAdd(a.sino_out + r0 + jv1, g * ku0 * kv1);
@@ -678,8 +708,14 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
     };
     __shared__ unsigned char vorder[kBpViews];   // 3D B: the batch's views, fast ones first
     __shared__ int vfast;
-    for (int vb = a.view0; vb < a.view1; vb += kBpViews) {
-        const int nvb = min(kBpViews, a.view1 - vb);
+    int vlo = a.view0, vhi = a.view1;
+    if constexpr (SLICEW) {
+        const int2 zr = a.zrange[bz];
+        vlo = max(vlo, zr.x);
+        vhi = min(vhi, zr.y);
+    }
+    for (int vb = vlo; vb < vhi; vb += kBpViews) {
+        const int nvb = min(kBpViews, vhi - vb);
         __syncthreads();
         if ((int)threadIdx.x < nvb)
             view_consts<ZR>(a.bp + (size_t)(vb + threadIdx.x) * kBpv, X0, Y0, ZC0, ZT, 0.5 * (TX - 1),
@@ -721,7 +757,8 @@ __global__ __launch_bounds__(256) void fbp_bp_kernel(BpArgs a) {
             }
         }
     }
-    if (!TRANSPOSE) {
+    // (a later batch of views that adds nothing to this band leaves it alone)
+    if (!TRANSPOSE && !(SLICEW && a.accumulate && vlo >= vhi)) {
 #pragma unroll
         for (int r = 0; r < ZR; ++r)
             if (col_in && iz0 + 16 * r < a.D) {
@@ -848,6 +885,11 @@ struct ct_fbp_s {
     // 3D backprojection: the pair-interleaved copy of one batch of views
     float2 *d_pairs = nullptr;
     int pair_views = 0;
+    bool direct = false;          // step 2 by direct convolution even where the FFT path applies
+    float *d_pw = nullptr;        // the caller's pre-weights, or null
+    size_t pw_stride = 0;
+    float *d_zw = nullptr;        // slice weights, [view][z], or null
+    int2 *d_zrange = nullptr;     // per band of 16 kZRun slices: views with a nonzero weight
 };
 
 namespace {
@@ -860,16 +902,13 @@ void free_plan(ct_fbp_s *f) {
     if (f->d_parker) (void)hipFree(f->d_parker);
     if (f->d_bp) (void)hipFree(f->d_bp);
     if (f->d_pairs) (void)hipFree(f->d_pairs);
+    if (f->d_pw) (void)hipFree(f->d_pw);
+    if (f->d_zw) (void)hipFree(f->d_zw);
+    if (f->d_zrange) (void)hipFree(f->d_zrange);
     delete f;
 }
 
 bool valid_plan(ct_fbp_t f) { return f && f->magic == kFbpMagic; }
-
-// CTPROJ_FBP_DIRECT=1 keeps the filter on the direct convolution (for comparisons).
-bool fft_disabled() {
-    const char *e = std::getenv("CTPROJ_FBP_DIRECT");
-    return e && e[0] == '1';
-}
 
 ct_status_t plan_device(ct_fbp_t f) {
     int cur = -1;
@@ -885,9 +924,22 @@ extern "C" {
 
 ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, const double *angular_weights,
                           const ct_fbp_opts_t *opts, ct_fbp_t *out) {
+    return ct_fbp_create_ext(desc, angles, angular_weights, opts, nullptr, out);
+}
+
+ct_status_t ct_fbp_create_ext(const ct_geom_desc_t *desc, const double *angles, const double *angular_weights,
+                              const ct_fbp_opts_t *opts, const ct_fbp_ext_t *ext_in, ct_fbp_t *out) {
     if (!out) return ffail(CT_E_NULL, "output plan pointer is NULL");
     *out = nullptr;
     if (!opts) return ffail(CT_E_NULL, "opts is NULL");
+    ct_fbp_ext_t ext{};
+    if (ext_in) ext = *ext_in;
+    for (int k = 0; k < 4; ++k)
+        if (ext.reserved[k] != 0) return ffail(CT_E_ARG, "ext reserved fields must be 0");
+    if (ext.projection_weights_per_view != 0 && ext.projection_weights_per_view != 1)
+        return ffail(CT_E_ARG, "projection_weights_per_view must be 0 or 1");
+    if (ext.direct_filter != 0 && ext.direct_filter != 1) return ffail(CT_E_ARG, "direct_filter must be 0 or 1");
+    const bool slicew = ext.slice_weights != nullptr;
     GeomHost h;
     const char *why = "";
     ct_status_t st = validate_desc(desc, &h, &why);
@@ -900,6 +952,9 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     const bool persp = h.beam != CT_PARALLEL2D;
     if (opts->short_scan && !persp) return ffail(CT_E_ARG, "short scans (Parker weights) need a fan or cone beam");
     if (h.U < 2 || (h.beam == CT_CONE && h.V < 2)) return ffail(CT_E_SHAPE, "interpolation needs >= 2 detector bins per axis");
+    if (slicew && h.beam != CT_CONE) return ffail(CT_E_ARG, "slice weights are for cone beams");
+    if (slicew && (angular_weights || opts->short_scan))
+        return ffail(CT_E_ARG, "slice weights replace the angular weights; no angular_weights or short_scan with them");
     if (h.U > 4096) return ffail(CT_E_RANGE, "the filter supports U <= 4096");
     if ((int64_t)opts->pad_factor * h.U > 16384) return ffail(CT_E_RANGE, "pad_factor * U must be <= 16384");
     if (h.D * h.H * h.W >= (int64_t(1) << 30) || h.n_views * h.U * h.V >= (int64_t(1) << 31) ||
@@ -912,7 +967,8 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     // row operand is 8 (V + 2)
     if (h.beam == CT_CONE && h.V + 2 >= (int64_t(1) << 20))
         return ffail(CT_E_RANGE, "cone detector too large: V + 2 must be < 2^20");
-    if (!angular_weights && !angles) return ffail(CT_E_NULL, "angles (or angular_weights) must be given");
+    if (!angular_weights && !angles && !slicew)
+        return ffail(CT_E_NULL, "angles (or angular_weights, or slice weights) must be given");
     if (opts->short_scan && !angles) return ffail(CT_E_NULL, "short scans need the angles");
     const int64_t nv = h.n_views;
     if (angles)
@@ -924,6 +980,19 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     if (opts->iso_given)
         for (int k = 0; k < 3; ++k)
             if (!std::isfinite(opts->iso[k])) return ffail(CT_E_NONFINITE, "isocentre not finite");
+    const int64_t n_resp = (int64_t)opts->pad_factor * h.U / 2 + 1;
+    const int64_t n_pw = (ext.projection_weights_per_view ? nv : 1) * h.U * h.V;
+    const int64_t n_sw = h.D * nv;
+    auto all_finite = [](const double *p, int64_t n) {
+        for (int64_t i = 0; i < n; ++i)
+            if (!std::isfinite(p[i])) return false;
+        return true;
+    };
+    if (ext.filter_response && !all_finite(ext.filter_response, n_resp))
+        return ffail(CT_E_NONFINITE, "filter response not finite");
+    if (ext.projection_weights && !all_finite(ext.projection_weights, n_pw))
+        return ffail(CT_E_NONFINITE, "projection weight not finite");
+    if (slicew && !all_finite(ext.slice_weights, n_sw)) return ffail(CT_E_NONFINITE, "slice weight not finite");
 
     // frames and unit normals
     std::vector<ViewFrame> fr(nv);
@@ -969,7 +1038,9 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     // angular weights: given, or half the gaps to the neighbouring views
     f->ang.assign(nv, 0.0);
     const bool redundant = persp && !opts->short_scan;
-    if (angular_weights) {
+    if (slicew) {
+        f->ang.assign(nv, 1.0);   // the slice weights carry the quadrature
+    } else if (angular_weights) {
         for (int64_t i = 0; i < nv; ++i) f->ang[i] = angular_weights[i];
     } else if (nv == 1) {
         f->ang[0] = M_PI;
@@ -1036,7 +1107,9 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     // rows per block: at most four tasks of 8 outputs per thread, LDS under 64 KB
     f->VT = f->U8 <= 512 ? 16 : (f->U8 <= 1024 ? 8 : (f->U8 <= 2048 ? 2 : 1));
     f->S = f->U8 + 4;
-    const std::vector<double> mult = multiplier(P, h.du, opts->window);
+    const std::vector<double> mult = ext.filter_response
+                                         ? std::vector<double>(ext.filter_response, ext.filter_response + n_resp)
+                                         : multiplier(P, h.du, opts->window);
     const std::vector<float> taps = filter_taps(P, f->U8, mult);
     // FFT path: P a power of two in [64, 4096]
     std::vector<float2> twf;
@@ -1122,6 +1195,35 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
     if (e == hipSuccess && !parker.empty()) e = hipMalloc((void **)&f->d_parker, parker.size() * sizeof(float));
     if (e == hipSuccess && f->P) e = hipMalloc((void **)&f->d_tw, twf.size() * sizeof(float2));
     if (e == hipSuccess && f->P) e = hipMalloc((void **)&f->d_mul, mulf.size() * sizeof(float));
+    // overrides: pre-weights as float; slice weights transposed to [view][z], and
+    // per band of 16 kZRun slices the range of views with a nonzero weight there
+    std::vector<float> pwf, zwf;
+    std::vector<int2> zr;
+    if (ext.projection_weights) {
+        pwf.assign(ext.projection_weights, ext.projection_weights + n_pw);
+        f->pw_stride = ext.projection_weights_per_view ? (size_t)(h.U * h.V) : 0;
+        if (e == hipSuccess) e = hipMalloc((void **)&f->d_pw, pwf.size() * sizeof(float));
+    }
+    if (slicew) {
+        const int64_t D = h.D, TZ = 16 * kZRun, nbz = (D + TZ - 1) / TZ;
+        zwf.resize((size_t)(nv * D));
+        zr.assign((size_t)nbz, make_int2(0, 0));
+        for (int64_t b = 0; b < nbz; ++b) {
+            int64_t lo = nv, hi = 0;
+            for (int64_t z = b * TZ; z < std::min(D, (b + 1) * TZ); ++z)
+                for (int64_t i = 0; i < nv; ++i)
+                    if (ext.slice_weights[z * nv + i] != 0.0) {
+                        lo = std::min(lo, i);
+                        hi = std::max(hi, i + 1);
+                    }
+            if (lo < hi) zr[(size_t)b] = make_int2((int)lo, (int)hi);
+        }
+        for (int64_t z = 0; z < D; ++z)
+            for (int64_t i = 0; i < nv; ++i) zwf[(size_t)(i * D + z)] = (float)ext.slice_weights[z * nv + i];
+        if (e == hipSuccess) e = hipMalloc((void **)&f->d_zw, zwf.size() * sizeof(float));
+        if (e == hipSuccess) e = hipMalloc((void **)&f->d_zrange, zr.size() * sizeof(int2));
+    }
+    f->direct = ext.direct_filter != 0;
     if (!h.is2d) {
         // equal batches of at most kBpViews views, and of at most kStagingBytes
         // of staging (large detectors take smaller batches)
@@ -1144,6 +1246,10 @@ ct_status_t ct_fbp_create(const ct_geom_desc_t *desc, const double *angles, cons
         e = hipMemcpy(f->d_parker, parker.data(), parker.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess && f->P) e = hipMemcpy(f->d_tw, twf.data(), twf.size() * sizeof(float2), hipMemcpyHostToDevice);
     if (e == hipSuccess && f->P) e = hipMemcpy(f->d_mul, mulf.data(), mulf.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess && f->d_pw) e = hipMemcpy(f->d_pw, pwf.data(), pwf.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess && f->d_zw) e = hipMemcpy(f->d_zw, zwf.data(), zwf.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess && f->d_zrange)
+        e = hipMemcpy(f->d_zrange, zr.data(), zr.size() * sizeof(int2), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         free_plan(f);
         return fhip(e, "upload of the FBP tables");
@@ -1185,7 +1291,7 @@ ct_status_t ct_fbp_filter(ct_fbp_t f, const float *sino, float *filtered, ct_str
     if (overlaps(sino, sb, filtered, sb)) return ffail(CT_E_ALIAS, "filtered overlaps sino");
     ct_status_t st = plan_device(f);
     if (st != CT_OK) return st;
-    if (f->P && !fft_disabled()) {
+    if (f->P && !f->direct) {
         FftArgs b;
         b.sino = sino;
         b.out = filtered;
@@ -1193,6 +1299,8 @@ ct_status_t ct_fbp_filter(ct_fbp_t f, const float *sino, float *filtered, ct_str
         b.mul = f->d_mul;
         b.fview = f->d_fview;
         b.parker = f->d_parker;
+        b.pw = f->d_pw;
+        b.pw_stride = f->pw_stride;
         b.U = (int)h.U;
         b.V = (int)h.V;
         b.n_views = (int)h.n_views;
@@ -1217,6 +1325,8 @@ ct_status_t ct_fbp_filter(ct_fbp_t f, const float *sino, float *filtered, ct_str
     a.taps = f->d_taps;
     a.fview = f->d_fview;
     a.parker = f->d_parker;
+    a.pw = f->d_pw;
+    a.pw_stride = f->pw_stride;
     a.U = (int)h.U;
     a.V = (int)h.V;
     a.n_views = (int)h.n_views;
@@ -1256,6 +1366,8 @@ static BpArgs bp_args(ct_fbp_t f) {
     a.view0 = 0;
     a.view1 = a.n_views;
     a.accumulate = 0;
+    a.zw = f->d_zw;
+    a.zrange = f->d_zrange;
     return a;
 }
 
@@ -1287,7 +1399,11 @@ ct_status_t ct_fbp_backproject(ct_fbp_t f, const float *filtered, float *vol, ct
             a.view0 = v0;
             a.view1 = v1;
             a.accumulate = v0 > 0 ? 1 : 0;
-            hipLaunchKernelGGL((fbp_bp_kernel<false, false, kZRun>), grid, dim3(256), 0, (hipStream_t)stream, a);
+            if (f->d_zw)
+                hipLaunchKernelGGL((fbp_bp_kernel<false, false, kZRun, true>), grid, dim3(256), 0,
+                                   (hipStream_t)stream, a);
+            else
+                hipLaunchKernelGGL((fbp_bp_kernel<false, false, kZRun>), grid, dim3(256), 0, (hipStream_t)stream, a);
         }
     }
     const hipError_t e = hipGetLastError();
@@ -1310,6 +1426,8 @@ ct_status_t ct_fbp_backproject_transpose(ct_fbp_t f, const float *vol, float *si
     a.sino_out = sino;
     const dim3 grid((unsigned)(a.nbx * a.nby * a.nbz));
     if (h.is2d) hipLaunchKernelGGL((fbp_bp_kernel<true, true, 1>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    else if (f->d_zw)
+        hipLaunchKernelGGL((fbp_bp_kernel<true, false, kZRun, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
     else hipLaunchKernelGGL((fbp_bp_kernel<true, false, kZRun>), grid, dim3(256), 0, (hipStream_t)stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fhip(e, "ct_fbp_backproject_transpose launch");
@@ -1327,6 +1445,77 @@ ct_status_t ct_fbp_run(ct_fbp_t f, const float *sino, float *work, float *vol, c
     ct_status_t st = ct_fbp_filter(f, sino, work, stream);
     if (st != CT_OK) return st;
     return ct_fbp_backproject(f, work, vol, stream);
+}
+
+// Helical approximation: per slice, the full turn centred at the angle where
+// the source crosses the slice centre, integrated by the trapezoidal rule on the
+// sampled angles (the hat functions of the linear interpolation), times 1/2.
+ct_status_t ct_helical_view_weights(const ct_geom_desc_t *desc, const double *angles, double *weights) {
+    if (!angles || !weights) return ffail(CT_E_NULL, "angles and weights must be non-NULL");
+    GeomHost h;
+    const char *why = "";
+    const ct_status_t st = validate_desc(desc, &h, &why);
+    if (st != CT_OK) return ffail(st, why);
+    if (h.beam != CT_CONE) return ffail(CT_E_ARG, "the helical approximation is a cone-beam method");
+    const int64_t nv = h.n_views, D = h.D;
+    if (nv < 2) return ffail(CT_E_ARG, "the helical weights need at least two views");
+    for (int64_t i = 0; i < nv; ++i)
+        if (!std::isfinite(angles[i])) return ffail(CT_E_NONFINITE, "angle not finite");
+    // work in increasing t = sa * angle and increasing key = sz * source z
+    const double sa = angles[nv - 1] > angles[0] ? 1.0 : -1.0;
+    const double sz = desc->frames[12 * (nv - 1) + 2] > desc->frames[2] ? 1.0 : -1.0;
+    std::vector<double> t((size_t)nv), zs((size_t)nv);
+    for (int64_t i = 0; i < nv; ++i) {
+        t[(size_t)i] = sa * angles[i];
+        zs[(size_t)i] = desc->frames[12 * i + 2];
+    }
+    for (int64_t i = 1; i < nv; ++i) {
+        if (!(t[(size_t)i] > t[(size_t)i - 1])) return ffail(CT_E_ARG, "the unwrapped angles must be strictly monotone");
+        if (!(sz * zs[(size_t)i] > sz * zs[(size_t)i - 1]))
+            return ffail(CT_E_ARG, "the source z must be strictly monotone");
+    }
+    const double tol = 1e-9 * (1.0 + std::max(std::fabs(t[0]), std::fabs(t[(size_t)nv - 1])));
+    std::vector<double> w((size_t)(D * nv), 0.0);
+    char msg[160];
+    for (int64_t s = 0; s < D; ++s) {
+        const double zc = -0.5 * (double)D * h.sz + ((double)s + 0.5) * h.sz;
+        const double key = sz * zc;
+        if (key < sz * zs[0] || key > sz * zs[(size_t)nv - 1]) {
+            std::snprintf(msg, sizeof msg, "slice %lld (z = %g) lies outside the source's z range", (long long)s, zc);
+            return ffail(CT_E_RANGE, msg);
+        }
+        int64_t lo = 0, hi = nv - 1;   // the last sample at or below the slice, at most nv - 2
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) / 2;
+            if (sz * zs[(size_t)mid] <= key) lo = mid;
+            else hi = mid;
+        }
+        const double fz = (zc - zs[(size_t)lo]) / (zs[(size_t)lo + 1] - zs[(size_t)lo]);
+        const double tc = t[(size_t)lo] + fz * (t[(size_t)lo + 1] - t[(size_t)lo]);
+        double a = tc - M_PI, b = tc + M_PI;
+        if (a < t[0] - tol || b > t[(size_t)nv - 1] + tol) {
+            std::snprintf(msg, sizeof msg, "slice %lld: the full turn about its crossing angle leaves the scan",
+                          (long long)s);
+            return ffail(CT_E_RANGE, msg);
+        }
+        a = std::max(a, t[0]);
+        b = std::min(b, t[(size_t)nv - 1]);
+        for (int64_t i = 0; i < nv; ++i) {
+            double acc = 0.0;
+            if (i > 0) {   // rising side: (x - t[i-1]) / L over [l, r]
+                const double tp = t[(size_t)i - 1], l = std::max(a, tp), r = std::min(b, t[(size_t)i]);
+                if (r > l) acc += (r - l) * ((r - tp) + (l - tp)) / (2.0 * (t[(size_t)i] - tp));
+            }
+            if (i + 1 < nv) {   // falling side: (t[i+1] - x) / L over [l, r]
+                const double tn = t[(size_t)i + 1], l = std::max(a, t[(size_t)i]), r = std::min(b, tn);
+                if (r > l) acc += (r - l) * ((tn - l) + (tn - r)) / (2.0 * (tn - t[(size_t)i]));
+            }
+            w[(size_t)(s * nv + i)] = 0.5 * acc;
+        }
+    }
+    std::memcpy(weights, w.data(), w.size() * sizeof(double));
+    set_error("");
+    return CT_OK;
 }
 
 }  // extern "C"

@@ -295,3 +295,100 @@ def test_adjoint_range_shift_rule(L):
     for c in (1, 2, 3, 4, 5):
         w = W.make_workload(c)
         assert rdp.ct_geom_adjoint_range(*_args(w))[1] == 0
+
+
+def test_fbp_ext_arguments_are_checked_on_the_host(L):
+    """ct_fbp_create_ext rejects bad overrides before it touches the device."""
+    cone = W.make_workload(3, scale=8, n_views=12)
+    d, fr = rdp.make_desc(*_args(cone))
+    th = np.ascontiguousarray(W.angles(12, 2 * math.pi))
+    dp = ctypes.POINTER(ctypes.c_double)
+    out = ctypes.c_void_p()
+    D, n = cone.vol_shape[0], cone.n_views
+    U, V = cone.det_shape
+    sw = np.ascontiguousarray(np.full((D, n), math.pi / n))
+
+    def create(desc=d, angles=th, aw=None, short_scan=0, **kw):
+        o = rdp.FbpOpts()
+        o.window, o.pad_factor, o.short_scan, o.iso_given, o.reserved = 0, 2, short_scan, 0, 0
+        x = rdp.FbpExt()
+        keep = []
+        for k, v in kw.items():
+            if isinstance(v, np.ndarray):
+                v = np.ascontiguousarray(v, dtype=np.float64)
+                keep.append(v)
+                setattr(x, k, v.ctypes.data_as(dp))
+            elif k == "reserved":
+                x.reserved[0] = v
+            else:
+                setattr(x, k, v)
+        a = angles.ctypes.data_as(dp) if angles is not None else None
+        w = aw.ctypes.data_as(dp) if aw is not None else None
+        return L.ct_fbp_create_ext(ctypes.byref(desc), a, w, ctypes.byref(o), ctypes.byref(x), ctypes.byref(out))
+
+    assert create(reserved=1) == rdp.CT_E_ARG
+    assert create(projection_weights_per_view=2) == rdp.CT_E_ARG
+    assert create(direct_filter=3) == rdp.CT_E_ARG
+    bad = np.ones(2 * U // 2 + 1)
+    bad[3] = math.nan
+    assert create(filter_response=bad) == rdp.CT_E_NONFINITE
+    badw = np.ones((U, V))
+    badw[1, 2] = math.inf
+    assert create(projection_weights=badw) == rdp.CT_E_NONFINITE
+    bads = sw.copy()
+    bads[0, 0] = math.nan
+    assert create(slice_weights=bads) == rdp.CT_E_NONFINITE
+    assert create(slice_weights=sw, aw=np.ones(n)) == rdp.CT_E_ARG
+    assert create(slice_weights=sw, short_scan=1) == rdp.CT_E_ARG
+    fan = W.Workload("f", W.BEAM_FAN2D, (1, 16, 16), (1, 1, 1), (40, 1), (1, 1), W.circular_fan2d(12, 60.0, 100.0))
+    df, frf = rdp.make_desc(*_args(fan))
+    assert create(desc=df, slice_weights=np.ones((1, 12))) == rdp.CT_E_ARG
+    assert "cone" in rdp.last_error()
+
+
+def _helix_wl(N=36, turns=3, per_view_z=1.0, D=9, dz=1.0, start=0.0):
+    n = N * turns
+    fr = W.helix_cone(n, 80.0, 130.0, per_view_z * n, turns)
+    th = start + W.angles(n, 2 * math.pi * turns)
+    c, s = np.cos(th), np.sin(th)
+    fr[:, 0], fr[:, 1] = 80.0 * c, 80.0 * s
+    fr[:, 3], fr[:, 4] = -50.0 * c, -50.0 * s
+    fr[:, 6], fr[:, 7] = s, -c
+    return W.Workload("h", W.BEAM_CONE, (D, 16, 16), (dz, 1, 1), (40, 24), (1.0, 1.0), fr), th
+
+
+def test_helical_view_weights_match_the_oracle(L):
+    from oracle import fbp as F
+    rng = np.random.default_rng(3)
+    cases = [_helix_wl(), _helix_wl(D=8), _helix_wl(N=50, D=13, dz=0.7, start=0.3)]
+    wl, th = _helix_wl(N=40, D=11)
+    th = th + rng.uniform(-0.3, 0.3, len(th)) * (2 * math.pi / 40)
+    wl.frames[:, 2] = -(wl.frames[:, 2] + rng.uniform(-0.2, 0.2, len(th)))
+    cases.append((wl, -th))     # descending angles, falling source, jittered
+    for wl, th in cases:
+        got = rdp.ct_helical_view_weights(*_args(wl), th)
+        want = F.helical_view_weights(wl, th)
+        assert np.allclose(got, want, rtol=0, atol=1e-12), np.abs(got - want).max()
+        assert np.allclose(got.sum(axis=1), math.pi, rtol=0, atol=1e-12)
+
+
+def test_helical_view_weights_reject_what_the_oracle_rejects(L):
+    from oracle import fbp as F
+    wl, th = _helix_wl()
+    cases = [(W.Workload("h", W.BEAM_CONE, (80, 16, 16), (1, 1, 1), wl.det_shape, wl.det_spacing, wl.frames), th,
+              rdp.CT_E_RANGE),
+             (W.Workload("h", W.BEAM_CONE, (120, 16, 16), (1, 1, 1), wl.det_shape, wl.det_spacing, wl.frames), th,
+              rdp.CT_E_RANGE)]
+    flat = wl.frames.copy()
+    flat[5, 2] = flat[4, 2]
+    cases.append((W.Workload("h", W.BEAM_CONE, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing, flat),
+                  th, rdp.CT_E_ARG))
+    bad = th.copy()
+    bad[3] = bad[2]
+    cases.append((wl, bad, rdp.CT_E_ARG))
+    for w, t, code in cases:
+        with pytest.raises(ValueError):
+            F.helical_view_weights(w, t)
+        with pytest.raises(rdp.CtError) as e:
+            rdp.ct_helical_view_weights(*_args(w), t)
+        assert e.value.status == code, (e.value, code)
