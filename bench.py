@@ -441,7 +441,7 @@ def single_run(args, rdp, W, torch, np):
         flops = FDK_FLOPS_PER_UPDATE * N * wl.n_views // n_batch
         achieved = flops / (ms[1] / n_batch * 1e-3)
         c = counters("c5fdk/fbp_backproject")
-        res["roofline"] = {"bound": "alu", "kernel": f"fbp_bp_kernel<false, false, 4> ({n_batch} launches per call)",
+        res["roofline"] = {"bound": "alu", "kernel": f"fbp_bp_kernel<false, false, 4, false> ({n_batch} launches per call)",
                            "achieved": round(achieved / 1e12, 2), "peak": round(ALU_PEAK / 1e12, 1),
                            "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK, 4),
                            "traffic": c.get("hbm_bytes") if c else None,

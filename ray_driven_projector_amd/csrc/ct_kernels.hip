@@ -422,6 +422,41 @@ __device__ __forceinline__ GStep gstep(const IWalk &w, uint32_t &idx, uint32_t &
     return g;
 }
 
+// The same walk for a ray that never crosses the planes of one axis (that
+// direction component is 0: the third axis's next crossing stays at 0xFFFFFFFF
+// and never is the minimum): the two live axes a and b, in x, y, z order, so
+// ties step a first as the three-axis step does, and the pieces and cells are
+// the same.
+struct IWalk2 {
+    uint32_t idx, sa, sb, la, lb, qa, qb, lend;
+};
+__device__ __forceinline__ IWalk2 live_axes(const IWalk &w, int dead) {
+    IWalk2 v;
+    v.idx = w.idx;
+    v.lend = w.lend;
+    v.la = dead == 0 ? w.ly : w.lx;
+    v.qa = dead == 0 ? w.qy : w.qx;
+    v.sa = dead == 0 ? w.sty : w.stx;
+    v.lb = dead == 2 ? w.ly : w.lz;
+    v.qb = dead == 2 ? w.qy : w.qz;
+    v.sb = dead == 2 ? w.sty : w.stz;
+    return v;
+}
+__device__ __forceinline__ GStep gstep2(const IWalk2 &w, uint32_t &idx, uint32_t &lc, uint32_t &la,
+                                        uint32_t &lb) {
+    const uint32_t tmin = min(la, lb);
+    const uint32_t tn = min(tmin, w.lend);
+    const bool ba = la == tmin;
+    const uint32_t na = __builtin_elementwise_add_sat(la, w.qa);
+    const uint32_t nb = __builtin_elementwise_add_sat(lb, w.qb);
+    la = ba ? na : la;
+    lb = ba ? lb : nb;
+    idx += ba ? w.sa : w.sb;
+    GStep g{tn - lc, tmin >= w.lend};
+    lc = tn;
+    return g;
+}
+
 // Sum of length * value over the walk, in walk units.  The cell offsets do not
 // depend on the loaded values, so the walk runs ahead of the arithmetic: each
 // iteration generates four pieces and has their four gathers in flight before
@@ -448,6 +483,28 @@ __device__ __forceinline__ float iwalk_gather(const IWalk &w, __amdgpu_buffer_rs
         acc = fmaf((float)s3.seg, v3, acc);
         // the next crossing never moves backwards, so once one step has reached
         // the end every later one has: the fourth step's test covers all four
+        if (s3.last) break;
+    }
+    return acc;
+}
+__device__ __forceinline__ float iwalk_gather2(const IWalk2 &w, __amdgpu_buffer_rsrc_t rs) {
+    uint32_t idx = w.idx;
+    uint32_t lc = 0, la = w.la, lb = w.lb;
+    float acc = 0.f;
+    float v0 = load_f32(rs, idx);
+    for (;;) {
+        const GStep s0 = gstep2(w, idx, lc, la, lb);
+        const float v1 = load_f32(rs, idx);
+        const GStep s1 = gstep2(w, idx, lc, la, lb);
+        const float v2 = load_f32(rs, idx);
+        const GStep s2 = gstep2(w, idx, lc, la, lb);
+        const float v3 = load_f32(rs, idx);
+        const GStep s3 = gstep2(w, idx, lc, la, lb);
+        acc = fmaf((float)s0.seg, v0, acc);
+        acc = fmaf((float)s1.seg, v1, acc);
+        acc = fmaf((float)s2.seg, v2, acc);
+        v0 = load_f32(rs, idx);
+        acc = fmaf((float)s3.seg, v3, acc);
         if (s3.last) break;
     }
     return acc;
@@ -520,6 +577,11 @@ __device__ __forceinline__ float project_ray(double ox, double oy, double oz, do
     const int nch = (ncell + chunk - 1) >> clog2;
     // (ex, ey, ez): element strides of x, y, z in the volume copy being read
     const uint32_t sx = ex * 4u, sy = ey * 4u, sz = ez * 4u;
+    // an axis the ray never crosses (parallel tilt series, 2D beams): when every
+    // ray of the wave has the same one, the two-axis walk
+    const int dead = dx == 0.0 ? 0 : (dy == 0.0 ? 1 : (dz == 0.0 ? 2 : 3));
+    const int dead0 = __builtin_amdgcn_readfirstlane(dead);
+    const bool two_axis = dead0 < 3 && __builtin_amdgcn_ballot_w64(dead != dead0) == 0;
     float total = 0.f;
     double ta = tin;
     for (int ch = 0; ch < nch; ++ch) {
@@ -546,7 +608,8 @@ __device__ __forceinline__ float project_ray(double ox, double oy, double oz, do
         fix_axis(dx, L, S, nxc, ddx, w.lx, w.qx, w.lend);
         fix_axis(dy, L, S, nyc, ddy, w.ly, w.qy, w.lend);
         fix_axis(dz, L, S, nzc, ddz, w.lz, w.qz, w.lend);
-        total = fmaf(iwalk_gather(w, rs), (float)(chord * 0x1p-31), total);
+        const float sum = two_axis ? iwalk_gather2(live_axes(w, dead0), rs) : iwalk_gather(w, rs);
+        total = fmaf(sum, (float)(chord * 0x1p-31), total);
         ta = tb;
     }
     return total;
@@ -941,6 +1004,35 @@ __device__ __forceinline__ void iwalk_scatter_fix(const IWalk &w, unsigned long 
     if (lc < lend) lds_add(lds, idx, term<SHIFT>(lend - lc, Y, sh));
 }
 
+// The two-axis walk (one direction component 0; see live_axes): the same
+// pieces and cells as the three-axis walk.
+template <bool SHIFT>
+__device__ __forceinline__ void iwalk2_scatter_fix(const IWalk2 &w, unsigned long long *lds, int Y, int sh) {
+    const uint32_t qa = w.qa, qb = w.qb, sa = w.sa, sb = w.sb, lend = w.lend;
+    uint32_t idx = w.idx, la = w.la, lb = w.lb;
+    uint32_t lc = 0, t = min(la, lb);
+    const auto advance = [&]() {
+        const bool ba = la == t;
+        const uint32_t na = __builtin_elementwise_add_sat(la, qa);
+        const uint32_t nb = __builtin_elementwise_add_sat(lb, qb);
+        la = ba ? na : la;
+        lb = ba ? lb : nb;
+        idx += ba ? sa : sb;
+    };
+    while (t < lend) {
+        lds_add(lds, idx, term<SHIFT>(t - lc, Y, sh));
+        advance();
+        lc = t;
+        t = min(la, lb);
+        const uint32_t tn = min(t, lend);
+        lds_add(lds, idx, term<SHIFT>(tn - lc, Y, sh));
+        advance();
+        lc = tn;
+        t = min(la, lb);
+    }
+    if (lc < lend) lds_add(lds, idx, term<SHIFT>(lend - lc, Y, sh));
+}
+
 // Everything of a brick walk that depends on the ray direction alone (for
 // parallel rays: once per view and brick).  Components below 2^-40 of the
 // largest count as zero; the test is taken over the wave, so waves without any
@@ -1079,6 +1171,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     // coefficients of the origin mirrored with it (a sign change is exact)
     constexpr bool SHARED_DIR = !PERSP && !SURF;
     DirPlan dp0{};
+    int dead = TWO_D ? 2 : 3;   // an axis no ray of the footprint crosses (3: none)
     float mA0x = A0x, mA0y = A0y, mA0z = A0z, mAfx = Afx, mAfy = Afy, mAfz = Afz, mAsx = Asx, mAsy = Asy,
           mAsz = Asz;
     if (SHARED_DIR) {
@@ -1093,6 +1186,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         if (dp0.nx) { mA0x = -A0x; mAfx = -Afx; mAsx = -Asx; }
         if (dp0.ny) { mA0y = -A0y; mAfy = -Afy; mAsy = -Asy; }
         if (dp0.nz) { mA0z = -A0z; mAfz = -Afz; mAsz = -Asz; }
+        if (!TWO_D) dead = uni(dp0.axx == 0.f ? 0 : (dp0.ayy == 0.f ? 1 : (dp0.azz == 0.f ? 2 : 3)));
     }
     const float *ysrc = a.sino + ((size_t)view * a.U + u0) * a.V + v0;
     const uint32_t yfs = ufast ? a.V : 1, yss = ufast ? 1 : a.V;   // sinogram strides, fast / slow
@@ -1321,9 +1415,14 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
             const int up = mant ? 23 - __builtin_amdgcn_frexp_expf(Yf) : 0;
             const int sh = up + a.yshift;
             const int Y = (int)rintf(__builtin_amdgcn_fmed3f(ldexpf(Yf, up), -8388607.f, 8388607.f));
-            if (sh <= 46) iwalk_scatter_fix<true>(w, acc, Y, sh);   // else every term is below one unit
+            if (sh <= 46) {   // else every term is below one unit
+                if (dead < 3) iwalk2_scatter_fix<true>(live_axes(w, dead), acc, Y, sh);
+                else iwalk_scatter_fix<true>(w, acc, Y, sh);
+            }
         } else {
-            iwalk_scatter_fix<false>(w, acc, (int)rintf(__builtin_amdgcn_fmed3f(Yf, -8388607.f, 8388607.f)), 0);
+            const int Y = (int)rintf(__builtin_amdgcn_fmed3f(Yf, -8388607.f, 8388607.f));
+            if (dead < 3) iwalk2_scatter_fix<false>(live_axes(w, dead), acc, Y, 0);
+            else iwalk_scatter_fix<false>(w, acc, Y, 0);
         }
     }
     };
