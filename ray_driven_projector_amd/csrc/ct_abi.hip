@@ -45,6 +45,7 @@ struct ct_geom_s {
     float *d_vol_yf = nullptr;          // y-fastest volume copy read by some views' gathers
     float *d_vol_zf = nullptr;          // z-fastest volume copy read by some views' gathers
     bool need_yf = false, need_zf = false;  // some view reads that copy
+    bool packet = false;                // every view has a packet axis (flat detector)
     size_t layout_cap = 0;              // voxels the copies hold (allocated on first use)
     double *d_off = nullptr;            // detector surface offsets (float64), or null: flat
     int surf_per_view = 0;
@@ -94,6 +95,7 @@ LaunchGeom lg(ct_geom_t g) {
     l.vol_zf = g->d_vol_zf;
     l.need_yf = g->need_yf;
     l.need_zf = g->need_zf;
+    l.packet = g->packet && !g->d_off;
     l.surf_off = g->d_off;
     l.surf_per_view = g->surf_per_view;
     l.surf_env = g->d_env;
@@ -459,10 +461,12 @@ static ct_status_t create_impl(const ct_geom_desc_t *desc, const double *offsets
     // volume copies in other axis orders, for the views whose gathers read them:
     // whole-volume size here when the volume fits one buffer, else allocated by
     // the first region forward at its region's size
+    g->packet = !offsets;
     for (int64_t k = 0; k < h.n_views; ++k) {
         const double lay = g->table[(size_t)k * CT_VIEW_TABLE_STRIDE + VT_LAYOUT];
         g->need_yf = g->need_yf || lay == 1.0;
         g->need_zf = g->need_zf || lay == 2.0;
+        g->packet = g->packet && g->table[(size_t)k * CT_VIEW_TABLE_STRIDE + VT_PACKET] >= 0.0;
     }
     if (h.D * h.H * h.W < kMaxBufferVoxels) {
         st = ensure_layouts(g, full_voxels(g));

@@ -264,6 +264,28 @@ void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *tab
         put(t + VT_EU, to_vox_vec(eu));
         put(t + VT_EV, to_vox_vec(ev));
         put(t + VT_EN, to_vox_vec(n));
+        // packets: u's (or v's) pixel step runs along one axis alone, whose
+        // direction component is below 2^-40 of the largest (the gathers take
+        // it as 0): rays one step apart along that detector axis differ only in
+        // a coordinate they never cross
+        t[VT_PACKET] = -1.0;
+        if (parallel && !g.is2d) {
+            const double dd[3] = {D00.x, D00.y, D00.z};
+            const double dm = std::max(std::fabs(dd[0]), std::max(std::fabs(dd[1]), std::fabs(dd[2]))) * 0x1p-40;
+            const double su[3] = {OU.x, OU.y, OU.z}, sv[3] = {OV.x, OV.y, OV.z};
+            // the pixel step runs along one axis alone, which the rays do not cross
+            auto along = [&](const double *st) {
+                int k = -1, n = 0;
+                for (int i = 0; i < 3; ++i)
+                    if (st[i] != 0.0) {
+                        k = i;
+                        ++n;
+                    }
+                return n == 1 && std::fabs(dd[k]) < dm;
+            };
+            if (along(su)) t[VT_PACKET] = 0.0;
+            else if (along(sv)) t[VT_PACKET] = 1.0;
+        }
     }
     choose_layouts(g, table);
 }

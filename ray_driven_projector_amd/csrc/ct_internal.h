@@ -53,7 +53,10 @@ enum ViewSlot : int {
     VT_EU = 38,     // e_u, e_v and the normal n as voxel-coordinate vectors (e / s):
     VT_EV = 41,     // a surface pixel with local offsets (o_u, o_v, o_n) sits at
     VT_EN = 44,     // C + o_u EU + o_v EV + o_n EN
-    VT_END = 47
+    VT_PACKET = 47, // parallel view whose rays never cross one axis d, and whose pixel
+                    // step along u (0) or v (1) runs along d alone: rays one step apart
+                    // along that detector axis share their walk (-1: no such axis)
+    VT_END = 48
 };
 static_assert(VT_END <= CT_VIEW_TABLE_STRIDE, "view table overflow");
 

@@ -457,6 +457,8 @@ __device__ __forceinline__ GStep gstep2(const IWalk2 &w, uint32_t &idx, uint32_t
     return g;
 }
 
+constexpr int kPacket = 4;   // rays per packet (forward and brick adjoint)
+
 // Sum of length * value over the walk, in walk units.  The cell offsets do not
 // depend on the loaded values, so the walk runs ahead of the arithmetic: each
 // iteration generates four pieces and has their four gathers in flight before
@@ -508,6 +510,45 @@ __device__ __forceinline__ float iwalk_gather2(const IWalk2 &w, __amdgpu_buffer_
         if (s3.last) break;
     }
     return acc;
+}
+
+// The two-axis gather for a packet of K rays that share the walk: at every
+// piece one gather per ray (ray j's cell is off[j] bytes from the walk's) and
+// one sum per ray, each formed exactly as iwalk_gather2 forms it.  CONSEC:
+// the rays' cells are consecutive words (off[j] = 4 j), read by one
+// K-word load.
+template <int K, bool CONSEC>
+__device__ __forceinline__ void iwalk_gather2_packet(const IWalk2 &w, __amdgpu_buffer_rsrc_t rs,
+                                                     const uint32_t (&off)[K], float (&acc)[K]) {
+    uint32_t idx = w.idx;
+    uint32_t lc = 0, la = w.la, lb = w.lb;
+    float v0[K], v1[K], v2[K], v3[K];
+    const auto gather = [&](float (&v)[K]) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = load_f32(rs, idx + (CONSEC ? 4u * j : off[j]));
+    };
+#pragma unroll
+    for (int j = 0; j < K; ++j) acc[j] = 0.f;
+    gather(v0);
+    for (;;) {
+        const GStep s0 = gstep2(w, idx, lc, la, lb);
+        gather(v1);
+        const GStep s1 = gstep2(w, idx, lc, la, lb);
+        gather(v2);
+        const GStep s2 = gstep2(w, idx, lc, la, lb);
+        gather(v3);
+        const GStep s3 = gstep2(w, idx, lc, la, lb);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            acc[j] = fmaf((float)s0.seg, v0[j], acc[j]);
+            acc[j] = fmaf((float)s1.seg, v1[j], acc[j]);
+            acc[j] = fmaf((float)s2.seg, v2[j], acc[j]);
+        }
+        gather(v0);
+#pragma unroll
+        for (int j = 0; j < K; ++j) acc[j] = fmaf((float)s3.seg, v3[j], acc[j]);
+        if (s3.last) break;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -768,6 +809,159 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
         if (lane == 0) wsum[wv] = q;
         __syncthreads();
         if (threadIdx.x == 0) a.partial[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    }
+}
+
+// Forward in packets (flat detector; every view parallel with a packet axis P,
+// VT_PACKET): the rays of one row along P differ only in their coordinate on
+// the axis d they never cross, so they walk the same cells of the other two
+// axes.  A thread takes kPacket consecutive pixels along P: one clip and one
+// walk, and at every piece one gather per ray from its own cell of d.  Each
+// ray's sum is formed exactly as ray_kernel forms it (same clip, chunks,
+// pieces and order of additions).  Tiles: a block takes 64 pixels along P x 16
+// across (a wave 16 packets x 4 rows); blocks run tile by tile, each tile
+// through every view in turn.  RM_PROJECT and RM_RESIDUAL.
+template <int MODE>
+__global__ __launch_bounds__(256) void ray_packet_kernel(RayArgs a) {
+    constexpr int K = kPacket;
+    const int blk = xcd_remap(blockIdx.x, a.n_blocks);
+    const int view = blk % a.n_views, tile = blk / a.n_views;
+    const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
+    const bool pu = vw[VT_PACKET] == 0.0;   // packets along u (else v)
+    const int NP = pu ? a.U : a.V, NQ = pu ? a.V : a.U;
+    const int ntp = (NP + 63) / 64, ntq = (NQ + 15) / 16;
+    if (tile >= ntp * ntq) return;
+    const int tp = tile % ntp, tq = tile / ntp;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int p0 = tp * 64 + (lane & 15) * K, q = tq * 16 + wv * 4 + (lane >> 4);
+    if (p0 >= NP || q >= NQ) return;
+    const int kk = min(K, NP - p0);
+    const int u0 = pu ? p0 : q, v0 = pu ? q : p0;
+    double ox, oy, oz, dx, dy, dz;
+    pixel_ray(vw, Surface{nullptr, 0}, view, u0, v0, a.U, a.V, ox, oy, oz, dx, dy, dz);
+    ox -= a.offx;
+    oy -= a.offy;
+    oz -= a.offz;
+    // the clip of clip_ray, without the untraversed axis (tested per ray)
+    const double dm = fmax(fabs(dx), fmax(fabs(dy), fabs(dz))) * 0x1p-40;
+    if (fabs(dx) < dm) dx = 0.0;
+    if (fabs(dy) < dm) dy = 0.0;
+    if (fabs(dz) < dm) dz = 0.0;
+    // d: the axis the packet's pixel step runs along (the rays do not cross it)
+    const int ps = pu ? VT_OU : VT_OV;
+    const int d = vw[ps + 0] != 0.0 ? 0 : (vw[ps + 1] != 0.0 ? 1 : 2);
+    double tin = vw[VT_TMIN], tout = vw[VT_TMAX];
+    bool hit = true;
+    if (d != 0) clip_axis(ox, dx, (double)a.W, tin, tout, hit);
+    if (d != 1) clip_axis(oy, dy, (double)a.H, tin, tout, hit);
+    if (d != 2) clip_axis(oz, dz, (double)a.D, tin, tout, hit);
+    hit = hit && tout > tin;
+    // per ray: its coordinate on d (as pixel_ray forms it), slab test and cell
+    const int layout = (int)vw[VT_LAYOUT];
+    const uint32_t W = a.W, H = a.H, D = a.D;
+    const uint32_t ex = layout == 0 ? 1u : (layout == 1 ? H : H * D);
+    const uint32_t ey = layout == 0 ? W : (layout == 1 ? 1u : D);
+    const uint32_t ez = layout == 0 ? W * H : (layout == 1 ? W * H : 1u);
+    const uint32_t sd = 4u * (d == 0 ? ex : (d == 1 ? ey : ez));
+    const int nd = d == 0 ? a.W : (d == 1 ? a.H : a.D);
+    bool in[K];
+    int cd[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        double rx = ox, ry = oy, rz = oz, qx, qy, qz;
+        if (j > 0) {
+            pixel_ray(vw, Surface{nullptr, 0}, view, u0 + (pu ? j : 0), v0 + (pu ? 0 : j), a.U, a.V, rx, ry, rz, qx,
+                      qy, qz);
+            rx -= a.offx;
+            ry -= a.offy;
+            rz -= a.offz;
+        }
+        const double od = d == 0 ? rx : (d == 1 ? ry : rz);
+        in[j] = j < kk && od >= 0.0 && od < (double)nd;
+        cd[j] = min(max((int)floor(od), 0), nd - 1);
+    }
+    float tot[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) tot[j] = 0.f;
+    if (hit) {
+        const float *src = layout == 0 ? a.vol : (layout == 1 ? a.vol_yf : a.vol_zf);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, a.vol_bytes);
+        uint32_t off[K];
+        bool consec = sd == 4u;   // the rays' cells are consecutive words
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            off[j] = (uint32_t)(cd[j] - cd[0]) * sd;
+            consec = consec && (!in[j] || cd[j] == cd[0] + j);
+        }
+        const bool vec = __builtin_amdgcn_ballot_w64(!consec) == 0;
+        // project_ray's chunked walk for the live axes; the untraversed axis
+        // only places the cells
+        const double px = dx * a.spx, py = dy * a.spy, pz = dz * a.spz;
+        const double L = sqrt(px * px + py * py + pz * pz);
+        const double ax_ = fabs(dx), ay_ = fabs(dy), az_ = fabs(dz);
+        const int M = (ax_ >= ay_ && ax_ >= az_) ? 0 : (ay_ >= az_ ? 1 : 2);
+        const double oM = M == 0 ? ox : (M == 1 ? oy : oz);
+        const double dM = M == 0 ? dx : (M == 1 ? dy : dz);
+        const int nM = M == 0 ? a.W : (M == 1 ? a.H : a.D);
+        const double eM = fma(tin, dM, oM), xM = fma(tout, dM, oM);
+        const int sgn = dM > 0.0 ? 1 : -1;
+        int cin = sgn > 0 ? (int)floor(eM) : (int)ceil(eM) - 1;
+        int cout = sgn > 0 ? (int)ceil(xM) - 1 : (int)floor(xM);
+        cin = min(max(cin, 0), nM - 1);
+        cout = min(max(cout, 0), nM - 1);
+        const int ncell = max((cout - cin) * sgn, 0) + 1;
+        constexpr int clog2 = kChunkLog2Parallel;
+        const int chunk = 1 << clog2;
+        const int nch = (ncell + chunk - 1) >> clog2;
+        const uint32_t sx = ex * 4u, sy = ey * 4u, sz = ez * 4u;
+        double ta = tin;
+        for (int ch = 0; ch < nch; ++ch) {
+            const int first = cin + sgn * (ch << clog2);
+            const int cells = min(chunk, ncell - (ch << clog2));
+            double tb = tout;
+            if (ch != nch - 1) {
+                const int P = sgn > 0 ? first + cells : first - cells + 1;
+                tb = ((double)P - oM) / dM;
+            }
+            int cx, cy, cz, nxc, nyc, nzc;
+            double ddx, ddy, ddz;
+            chunk_axis(ox, dx, ta, tb, a.W, M == 0, first, cells, ch == 0, cx, nxc, ddx);
+            chunk_axis(oy, dy, ta, tb, a.H, M == 1, first, cells, ch == 0, cy, nyc, ddy);
+            chunk_axis(oz, dz, ta, tb, a.D, M == 2, first, cells, ch == 0, cz, nzc, ddz);
+            if (d == 0) cx = cd[0];
+            else if (d == 1) cy = cd[0];
+            else cz = cd[0];
+            const double chord = (tb - ta) * L;
+            const double S = 0x1p31 / chord;
+            IWalk w;
+            w.idx = (uint32_t)cx * sx + (uint32_t)cy * sy + (uint32_t)cz * sz;
+            w.stx = dx > 0.0 ? sx : 0u - sx;
+            w.sty = dy > 0.0 ? sy : 0u - sy;
+            w.stz = dz > 0.0 ? sz : 0u - sz;
+            w.lend = 1u << 31;
+            fix_axis(dx, L, S, nxc, ddx, w.lx, w.qx, w.lend);
+            fix_axis(dy, L, S, nyc, ddy, w.ly, w.qy, w.lend);
+            fix_axis(dz, L, S, nzc, ddz, w.lz, w.qz, w.lend);
+            float sum[K];
+            if (vec) iwalk_gather2_packet<K, true>(live_axes(w, d), rs, off, sum);
+            else iwalk_gather2_packet<K, false>(live_axes(w, d), rs, off, sum);
+            const float cs = (float)(chord * 0x1p-31);
+#pragma unroll
+            for (int j = 0; j < K; ++j) tot[j] = fmaf(sum[j], cs, tot[j]);
+            ta = tb;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        if (j >= kk) break;
+        const int u = u0 + (pu ? j : 0), v = v0 + (pu ? 0 : j);
+        const size_t ray = ((size_t)view * a.U + u) * a.V + v;
+        const float acc = in[j] ? tot[j] : 0.f;
+        if (MODE == RM_PROJECT) {
+            a.out[ray] = a.accumulate ? acc + a.out[ray] : acc;
+        } else {
+            a.out[ray] = a.rinv[ray] * (a.sino[ray] - acc);
+        }
     }
 }
 
@@ -1033,6 +1227,42 @@ __device__ __forceinline__ void iwalk2_scatter_fix(const IWalk2 &w, unsigned lon
     if (lc < lend) lds_add(lds, idx, term<SHIFT>(lend - lc, Y, sh));
 }
 
+// A packet of K rays that share their walk (parallel rays one detector step
+// apart along the axis none of them crosses): the live-axis walk once, and at
+// every piece one term per ray into its own cell of the untraversed axis
+// (off[j], from the walk's cell).  A ray without a value there has Y = 0.
+template <bool SHIFT, int K>
+__device__ __forceinline__ void iwalk2_scatter_packet(const IWalk2 &w, unsigned long long *lds, const int (&Y)[K],
+                                                      const int (&sh)[K], const uint32_t (&off)[K]) {
+    const uint32_t qa = w.qa, qb = w.qb, sa = w.sa, sb = w.sb, lend = w.lend;
+    uint32_t idx = w.idx, la = w.la, lb = w.lb;
+    uint32_t lc = 0, t = min(la, lb);
+    const auto put = [&](uint32_t len) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) lds_add(lds, idx + off[j], term<SHIFT>(len, Y[j], sh[j]));
+    };
+    const auto advance = [&]() {
+        const bool ba = la == t;
+        const uint32_t na = __builtin_elementwise_add_sat(la, qa);
+        const uint32_t nb = __builtin_elementwise_add_sat(lb, qb);
+        la = ba ? na : la;
+        lb = ba ? lb : nb;
+        idx += ba ? sa : sb;
+    };
+    while (t < lend) {
+        put(t - lc);
+        advance();
+        lc = t;
+        t = min(la, lb);
+        const uint32_t tn = min(t, lend);
+        put(tn - lc);
+        advance();
+        lc = tn;
+        t = min(la, lb);
+    }
+    if (lc < lend) put(lend - lc);
+}
+
 // Everything of a brick walk that depends on the ray direction alone (for
 // parallel rays: once per view and brick).  Components below 2^-40 of the
 // largest count as zero; the test is taken over the wave, so waves without any
@@ -1278,7 +1508,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
                                (size_t)u0 * a.V + v0);
         if (lane < nrays) { o0n = ob[3 * yo]; o1n = ob[3 * yo + 1]; o2n = ob[3 * yo + 2]; }
     }
-    const auto walk_rays = [&](auto fs_tag) {
+    const auto walk_rays = [&](auto fs_tag) __attribute__((always_inline)) {
     constexpr bool FS = decltype(fs_tag)::value;   // mirrored fan/cone footprint
     for (int r = lane; r < nrays; r += 64) {
         const float cf = (float)lf - af, cs = (float)srow(lk) - as_;
@@ -1426,8 +1656,118 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         }
     }
     };
+    // Parallel rays with an untraversed axis d whose footprint's fast pixel
+    // step runs along d alone: the rays of a row differ only in their d
+    // coordinate, so they have the same walk through the other two axes.  A
+    // lane then takes a packet of kPacket consecutive rays of a row: one
+    // set-up and one walk, one term per ray (a ray outside the brick's d slab,
+    // or past the row's end, gets Y = 0).  The arithmetic is that of the ray
+    // path above, term by term, so the sums are the same.
+    const auto walk_packets = [&]() __attribute__((always_inline)) {
+        constexpr int K = kPacket;
+        // slots: live axes a < b (x, y, z order), untraversed axis d (values
+        // picked by value, so no reference is selected)
+        const int d = dead;
+        const auto A = [d](auto x, auto y, auto z) { return d == 0 ? y : x; };
+        const auto B = [d](auto x, auto y, auto z) { return d == 2 ? y : z; };
+        const auto Dd = [d](auto x, auto y, auto z) { return d == 0 ? x : (d == 1 ? y : z); };
+        const float ha = A(hx, hy, hz), hb = B(hx, hy, hz), hd = Dd(hx, hy, hz);
+        const float ea = A(fex, fey, fez), eb = B(fex, fey, fez), ed = Dd(fex, fey, fez);
+        const float A0a = A(mA0x, mA0y, mA0z), A0b = B(mA0x, mA0y, mA0z), A0d = Dd(mA0x, mA0y, mA0z);
+        const float Asa = A(mAsx, mAsy, mAsz), Asb = B(mAsx, mAsy, mAsz), Asd = Dd(mAsx, mAsy, mAsz);
+        const float Afd = Dd(mAfx, mAfy, mAfz);
+        const float ia = A(dp0.ix, dp0.iy, dp0.iz), ib = B(dp0.ix, dp0.iy, dp0.iz);
+        const float aa = A(dp0.axx, dp0.ayy, dp0.azz), ab = B(dp0.axx, dp0.ayy, dp0.azz);
+        const float qfa = A(dp0.qfx, dp0.qfy, dp0.qfz), qfb = B(dp0.qfx, dp0.qfy, dp0.qfz);
+        const uint32_t qa = A(dp0.qx, dp0.qy, dp0.qz), qb = B(dp0.qx, dp0.qy, dp0.qz);
+        const bool na = A(dp0.nx, dp0.ny, dp0.nz), nb = B(dp0.nx, dp0.ny, dp0.nz), nd = Dd(dp0.nx, dp0.ny, dp0.nz);
+        constexpr uint32_t SX = 8u, SY = 8u * LSY, SZ = 8u * LSZ;   // LDS byte strides
+        const uint32_t Sa = A(SX, SY, SZ), Sb = B(SX, SY, SZ), Sd = Dd(SX, SY, SZ);
+        const uint32_t sta = in_vgpr(na ? 0u - Sa : Sa), stb = in_vgpr(nb ? 0u - Sb : Sb);
+        const float LS = dp0.LS;
+        const int nrow = nrays / nf, np = (nf + K - 1) / K, npk = nrow * np;
+        const int pstep_slow = 64 / np, pstep_fast = 64 - pstep_slow * np;
+        int prow = lane / np, pp = lane - prow * np;
+        for (int r = lane; r < npk; r += 64) {
+            const int lf0 = pp * K, row = srow(prow);
+            const int kk = min(K, nf - lf0);
+            pp += pstep_fast;
+            prow += pstep_slow;
+            if (pp >= np) { pp -= np; prow += 1; }
+            const float cs = (float)row - as_, cf0 = (float)lf0 - af;
+            const uint32_t yo = __umul24(lf0, yfs) + __umul24(row, yss);
+            float yv[K];
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                yv[j] = j < kk ? (MODE == BM_COLINV ? 1.f : ysrc[yo + j * yfs]) : 0.f;
+            // the live axes: shared by the packet (their fast-step terms are 0)
+            const float ma = fmaf(cs, Asa, A0a), mb = fmaf(cs, Asb, A0b);
+            const float loa = (-ha - ma) * ia, hia = fmaf(ea, ia, loa);
+            const float lob = (-hb - mb) * ib, hib = fmaf(eb, ib, lob);
+            const float tin = fmaxf(fmaxf(loa, lob), tv0);
+            const float tout = fminf(fminf(hia, hib), tv1);
+            if (!(tin < tout)) continue;
+            IWalk2 w;
+            float fca, fcb;
+            uint32_t fara, farb;
+            baxis(ma, aa, tin, ha, ea - 1.f, qfa, qa, fca, w.la, fara);
+            baxis(mb, ab, tin, hb, eb - 1.f, qfb, qb, fcb, w.lb, farb);
+            w.qa = qa;
+            w.qb = qb;
+            w.sa = sta;
+            w.sb = stb;
+            w.lend = min(sat_u32((tout - tin) * LS), min(fara, farb));
+            const float rca = na ? ea - 1.f - fca : fca, rcb = nb ? eb - 1.f - fcb : fcb;
+            w.idx = (uint32_t)rca * Sa + (uint32_t)rcb * Sb;
+            // per ray: its cell of the untraversed axis and its fixed-point value
+            float Yf[K];
+            uint32_t off[K];
+            bool mant_any = false;
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const float md = fmaf(cs, Asd, fmaf(cf0 + (float)j, Afd, A0d));
+                const bool in = -hd <= md && md < hd;
+                const float fcd = __builtin_amdgcn_fmed3f(floorf(md + hd), 0.f, ed - 1.f);
+                off[j] = (uint32_t)(nd ? ed - 1.f - fcd : fcd) * Sd;
+                Yf[j] = in ? yv[j] * yscale : 0.f;   // |Yf| < 2^23
+                mant_any = mant_any || (Yf[j] != 0.f && (a.yshift != 0 || fabsf(Yf[j]) < 0x1p17f));
+            }
+            bool some = false;
+#pragma unroll
+            for (int j = 0; j < K; ++j) some = some || Yf[j] != 0.f;
+            if (!some) continue;
+            int Y[K], sh[K];
+            if (__builtin_amdgcn_ballot_w64(mant_any)) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    const bool mant = a.yshift != 0 || fabsf(Yf[j]) < 0x1p17f;
+                    const int up = mant ? 23 - __builtin_amdgcn_frexp_expf(Yf[j]) : 0;
+                    sh[j] = up + a.yshift;
+                    const int Yv = (int)rintf(__builtin_amdgcn_fmed3f(ldexpf(Yf[j], up), -8388607.f, 8388607.f));
+                    Y[j] = sh[j] <= 46 ? Yv : 0;   // else every term is below one unit
+                    sh[j] = min(sh[j], 46);
+                }
+                iwalk2_scatter_packet<true, K>(w, acc, Y, sh, off);
+            } else {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    Y[j] = (int)rintf(__builtin_amdgcn_fmed3f(Yf[j], -8388607.f, 8388607.f));
+                    sh[j] = 0;
+                }
+                iwalk2_scatter_packet<false, K>(w, acc, Y, sh, off);
+            }
+        }
+    };
     if constexpr (PERSP && !SURF) {
         if (fsign) walk_rays(std::true_type{});
+        else walk_rays(std::false_type{});
+    } else if constexpr (SHARED_DIR && !TWO_D) {
+        // exactly one untraversed axis, and the fast pixel step along it alone
+        const bool pk = dead == 0   ? (mAfy == 0.f && mAfz == 0.f && dp0.ayy != 0.f && dp0.azz != 0.f)
+                        : dead == 1 ? (mAfx == 0.f && mAfz == 0.f && dp0.axx != 0.f && dp0.azz != 0.f)
+                        : dead == 2 ? (mAfx == 0.f && mAfy == 0.f && dp0.axx != 0.f && dp0.ayy != 0.f)
+                                    : false;
+        if (pk) walk_packets();
         else walk_rays(std::false_type{});
     } else {
         walk_rays(std::false_type{});
@@ -1716,6 +2056,14 @@ static RayArgs ray_args(const LaunchGeom &g) {
 
 template <int MODE>
 static hipError_t launch_ray(const LaunchGeom &g, RayArgs a, hipStream_t s) {
+    if ((MODE == RM_PROJECT || MODE == RM_RESIDUAL) && g.packet && !g.two_d && !a.surf.off) {
+        // tiles of 64 x 16 pixels, the long side along each view's packet axis
+        const int tu = ((g.U + 63) / 64) * ((g.V + 15) / 16), tv = ((g.V + 63) / 64) * ((g.U + 15) / 16);
+        a.n_blocks = g.n_views * std::max(tu, tv);
+        hipLaunchKernelGGL((ray_packet_kernel<MODE == RM_PROJECT ? RM_PROJECT : RM_RESIDUAL>), dim3(a.n_blocks),
+                           dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     const dim3 grid(a.n_blocks), block(256);
     if (g.two_d) {
         if (a.surf.off) hipLaunchKernelGGL((ray_kernel<MODE, true, true>), grid, block, 0, s, a);

@@ -24,6 +24,8 @@ struct LaunchGeom {
     float *vol_yf;         // handle-owned y-fastest volume copy, or null if no view reads it
     float *vol_zf;         // handle-owned z-fastest volume copy, or null if no view reads it
     bool need_yf, need_zf; // some view's gathers read that copy
+    bool packet;           // flat detector and every view has a packet axis (VT_PACKET >= 0):
+                           // the forward takes rays in packets
 };
 
 hipError_t launch_fill(float *p, size_t n, float v, hipStream_t s);
