@@ -43,6 +43,13 @@ Default run (one JSON line):
 --workload c1|c2|c3|c4|c5 times A + A^T of one workload (c4: the SIRT step);
 c4cgls / c5cgls time CGLS iterations, c5cyl A + A^T with a cylindrical
 detector, c5fdk the FDK (filter + interpolating backprojection).
+
+--ingest-counters WL=DIR ... (no GPU) reads rocprofv3 --pmc CSV output (one
+directory per workload, holding the passes' *_counter_collection.csv files),
+takes each hot kernel's last dispatch (the timed step), scales FETCH_SIZE and
+WRITE_SIZE by what they read for the --copy-calibration copy, and writes
+profiles/counters.json (keyed to the current device code) and a Markdown
+table beside it.
 """
 from __future__ import annotations
 
@@ -100,6 +107,104 @@ def counters(key: str):
         return d["entries"].get(key)
     except (OSError, ValueError, KeyError):
         return None
+
+
+# kernel-name patterns of the hot kernels and the role each plays
+ROLES = (("ray_kernel<0,", "project"), ("ray_kernel<1,", "sirt_residual"), ("ray_kernel<4,", "backproject_atomic"),
+         ("ray_kernel<5,", "cgls_project"), ("brick_kernel<", "backproject"), ("fbp_bp_kernel<", "fbp_backproject"),
+         ("fbp_fft_filter_kernel", "fbp_filter"), ("fbp_filter_kernel", "fbp_filter"))
+BRICK_MODES = {"0": "backproject", "1": "sirt_update", "2": "colinv", "3": "cgls_adjoint"}
+COPY_BYTES = 1 << 30   # the --copy-calibration copy reads and writes 1 GiB
+
+
+def kernel_role(name: str):
+    for pat, role in ROLES:
+        if pat in name:
+            if role == "backproject":   # brick_kernel<BX, BY, BZ, NT, MODE, SURF, PERSP>
+                args = name.split("brick_kernel<", 1)[1].split(">", 1)[0].split(",")
+                return BRICK_MODES.get(args[4].strip())
+            return role
+    return None
+
+
+def ingest_counters(specs, out_path=COUNTERS):
+    """Write profiles/counters.json (and counters.md) from rocprofv3 --pmc runs."""
+    import csv
+    import glob
+    entries, notes = {}, []
+    for spec in specs:
+        wl, d = spec.split("=", 1)
+        disp = {}
+        for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            run = os.path.basename(path)
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    k = (run, int(r["Dispatch_Id"]))
+                    e = disp.setdefault(k, {"name": r["Kernel_Name"], "c": {},
+                                            "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                    e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        # the calibration copy: the largest FETCH_SIZE / WRITE_SIZE among the copy kernels
+        fscale = wscale = None
+        for (run, _), e in disp.items():
+            if "copy" not in e["name"].lower():
+                continue
+            if "FETCH_SIZE" in e["c"] and e["c"]["FETCH_SIZE"] * 1024 > COPY_BYTES / 2:
+                fscale = COPY_BYTES / (e["c"]["FETCH_SIZE"] * 1024)
+            if "WRITE_SIZE" in e["c"] and e["c"]["WRITE_SIZE"] * 1024 > COPY_BYTES / 2:
+                wscale = COPY_BYTES / (e["c"]["WRITE_SIZE"] * 1024)
+        notes.append(f"{wl}: FETCH_SIZE x{fscale if fscale is None else round(fscale, 3)}, "
+                     f"WRITE_SIZE x{wscale if wscale is None else round(wscale, 3)}")
+        last = {}
+        for (run, did), e in sorted(disp.items()):
+            role = kernel_role(e["name"])
+            if role:
+                last.setdefault(role, {})
+                last[role][run] = e          # the last dispatch of each run
+        for role, runs in last.items():
+            c, names = {}, set()
+            for e in runs.values():
+                c.update(e["c"])
+                names.add(e["name"])
+            ent = {"kernel": sorted(names)[0]}
+            if "SQ_INSTS_VALU" in c:
+                ent["valu_insts"] = c["SQ_INSTS_VALU"]
+            for k, v in (("SQ_INSTS_LDS", "lds_insts"), ("SQ_INSTS_SALU", "salu_insts"), ("SQ_WAVES", "waves"),
+                         ("SQ_INSTS_VMEM_RD", "vmem_rd_insts"), ("SQ_LDS_BANK_CONFLICT", "lds_bank_conflict")):
+                if k in c:
+                    ent[v] = c[k]
+            if "GRBM_GUI_ACTIVE" in c:
+                cyc = c["GRBM_GUI_ACTIVE"] / 8          # the counter sums the 8 XCDs
+                ent["cycles"] = cyc
+                if "SQ_INSTS_VALU" in c:
+                    ent["valu_busy"] = round(c["SQ_INSTS_VALU"] * 4 / (1024 * cyc), 3)
+            if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c:
+                ent["l2_hit"] = round(c["TCC_HIT_sum"] / max(1.0, c["TCC_HIT_sum"] + c["TCC_MISS_sum"]), 3)
+            if "FETCH_SIZE" in c and fscale:
+                ent["fetch_bytes"] = int(c["FETCH_SIZE"] * 1024 * fscale)
+            if "WRITE_SIZE" in c and wscale:
+                ent["write_bytes"] = int(c["WRITE_SIZE"] * 1024 * wscale)
+            if "fetch_bytes" in ent and "write_bytes" in ent:
+                ent["hbm_bytes"] = ent["fetch_bytes"] + ent["write_bytes"]
+            entries[f"{wl}/{role}"] = ent
+    doc = {"code_object": code_object_hash(), "scales": notes, "entries": entries}
+    with open(out_path, "w") as f:
+        json.dump(doc, f, indent=1, sort_keys=True)
+    md = os.path.splitext(out_path)[0] + ".md"
+    with open(md, "w") as f:
+        f.write("# rocprofv3 counters of the hot kernels (generated by bench.py --ingest-counters)\n\n")
+        f.write(f"Device code object: {doc['code_object']} (SHA-256 of libctproj.so's .hip_fatbin, first 16 hex).\n")
+        f.write("Calibration (1 GiB device copy): " + "; ".join(notes) + ".\n\n")
+        f.write("| key | kernel | VALU instr (wave) | VALU busy | LDS instr | cycles (M) | L2 hit | HBM fetch GB | "
+                "HBM write GB |\n|---|---|---|---|---|---|---|---|---|\n")
+        for k in sorted(entries):
+            e = entries[k]
+            g = lambda x, fmt: (fmt.format(e[x]) if x in e else "")
+            f.write(f"| {k} | `{e['kernel'].split('(')[0].replace('void ', '')}` | {g('valu_insts', '{:.3e}')} | "
+                    f"{g('valu_busy', '{}')} | {g('lds_insts', '{:.3e}')} | "
+                    f"{(format(e['cycles'] / 1e6, '.1f') if 'cycles' in e else '')} | {g('l2_hit', '{}')} | "
+                    f"{(format(e['fetch_bytes'] / 1e9, '.2f') if 'fetch_bytes' in e else '')} | "
+                    f"{(format(e['write_bytes'] / 1e9, '.2f') if 'write_bytes' in e else '')} |\n")
+    print(f"wrote {out_path} and {md}: {len(entries)} entries", flush=True)
 
 
 def golden_nnz(wl, config: int):
@@ -506,7 +611,12 @@ def main():
                          "(PCIe-inclusive; reported apart from value)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (the reference kernel for HBM counters)")
+    ap.add_argument("--ingest-counters", nargs="+", metavar="WL=DIR",
+                    help="write profiles/counters.json from rocprofv3 --pmc output directories (no GPU)")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
