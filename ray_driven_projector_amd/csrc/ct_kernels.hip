@@ -458,6 +458,7 @@ __device__ __forceinline__ GStep gstep2(const IWalk2 &w, uint32_t &idx, uint32_t
 }
 
 constexpr int kPacket = 4;   // rays per packet (forward and brick adjoint)
+constexpr int kPacketTileGroup = 1;     // forward packet tiles per block group (1: every view per tile)
 
 // Sum of length * value over the walk, in walk units.  The cell offsets do not
 // depend on the loaded values, so the walk runs ahead of the arithmetic: each
@@ -825,7 +826,11 @@ template <int MODE>
 __global__ __launch_bounds__(256) void ray_packet_kernel(RayArgs a) {
     constexpr int K = kPacket;
     const int blk = xcd_remap(blockIdx.x, a.n_blocks);
-    const int view = blk % a.n_views, tile = blk / a.n_views;
+    // groups of kPacketTileGroup consecutive tiles; inside a group every view
+    // in turn, the group's tiles innermost
+    constexpr int G = kPacketTileGroup;
+    const int grp = blk / (a.n_views * G), rg = blk - grp * (a.n_views * G);
+    const int view = rg / G, tile = grp * G + (rg - (rg / G) * G);
     const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
     const bool pu = vw[VT_PACKET] == 0.0;   // packets along u (else v)
     const int NP = pu ? a.U : a.V, NQ = pu ? a.V : a.U;
@@ -2059,7 +2064,8 @@ static hipError_t launch_ray(const LaunchGeom &g, RayArgs a, hipStream_t s) {
     if ((MODE == RM_PROJECT || MODE == RM_RESIDUAL) && g.packet && !g.two_d && !a.surf.off) {
         // tiles of 64 x 16 pixels, the long side along each view's packet axis
         const int tu = ((g.U + 63) / 64) * ((g.V + 15) / 16), tv = ((g.V + 63) / 64) * ((g.U + 15) / 16);
-        a.n_blocks = g.n_views * std::max(tu, tv);
+        const int G = kPacketTileGroup;
+        a.n_blocks = g.n_views * ((std::max(tu, tv) + G - 1) / G) * G;
         hipLaunchKernelGGL((ray_packet_kernel<MODE == RM_PROJECT ? RM_PROJECT : RM_RESIDUAL>), dim3(a.n_blocks),
                            dim3(256), 0, s, a);
         return hipGetLastError();
