@@ -111,6 +111,7 @@ def counters(key: str):
 
 # kernel-name patterns of the hot kernels and the role each plays
 ROLES = (("ray_kernel<0,", "project"), ("ray_kernel<1,", "sirt_residual"), ("ray_kernel<4,", "backproject_atomic"),
+         ("ray_packet_kernel<0>", "project"), ("ray_packet_kernel<1>", "sirt_residual"),
          ("ray_kernel<5,", "cgls_project"), ("brick_kernel<", "backproject"), ("fbp_bp_kernel<", "fbp_backproject"),
          ("fbp_fft_filter_kernel", "fbp_filter"), ("fbp_filter_kernel", "fbp_filter"))
 BRICK_MODES = {"0": "backproject", "1": "sirt_update", "2": "colinv", "3": "cgls_adjoint"}
@@ -199,7 +200,8 @@ def ingest_counters(specs, out_path=COUNTERS):
         for k in sorted(entries):
             e = entries[k]
             g = lambda x, fmt: (fmt.format(e[x]) if x in e else "")
-            f.write(f"| {k} | `{e['kernel'].split('(')[0].replace('void ', '')}` | {g('valu_insts', '{:.3e}')} | "
+            name = e["kernel"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            f.write(f"| {k} | `{name}` | {g('valu_insts', '{:.3e}')} | "
                     f"{g('valu_busy', '{}')} | {g('lds_insts', '{:.3e}')} | "
                     f"{(format(e['cycles'] / 1e6, '.1f') if 'cycles' in e else '')} | {g('l2_hit', '{}')} | "
                     f"{(format(e['fetch_bytes'] / 1e9, '.2f') if 'fetch_bytes' in e else '')} | "

@@ -458,7 +458,16 @@ __device__ __forceinline__ GStep gstep2(const IWalk2 &w, uint32_t &idx, uint32_t
 }
 
 constexpr int kPacket = 4;   // rays per packet (forward and brick adjoint)
-constexpr int kPacketTileGroup = 1;     // forward packet tiles per block group (1: every view per tile)
+// Forward packet blocks (measured on the 512^3 dual-axis SIRT residual):
+// 16 waves, each 8 packets along P (one 128-byte line of the volume copy's
+// contiguous axis) x 8 rows, so a block takes a tile of 32 x 128 pixels, and
+// one tile runs through every view in turn.  12.1 ms with 256-thread blocks
+// of 64 x 16 pixels; 9.1 with 1024-thread 64 x 64; 8.9 with 32 x 128; 20.3
+// with 16 x 256 (half lines); grouping 2 / 4 tiles per view: 10.7 / 12.9.
+constexpr int kPacketTileGroup = 1;
+constexpr int kPacketWaves = 16;
+constexpr int kPacketLanesP = 8;
+constexpr int kPacketTP = kPacketLanesP * kPacket, kPacketTQ = (64 / kPacketLanesP) * kPacketWaves;   // tile
 
 // Sum of length * value over the walk, in walk units.  The cell offsets do not
 // depend on the loaded values, so the walk runs ahead of the arithmetic: each
@@ -819,11 +828,11 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
 // axes.  A thread takes kPacket consecutive pixels along P: one clip and one
 // walk, and at every piece one gather per ray from its own cell of d.  Each
 // ray's sum is formed exactly as ray_kernel forms it (same clip, chunks,
-// pieces and order of additions).  Tiles: a block takes 64 pixels along P x 16
-// across (a wave 16 packets x 4 rows); blocks run tile by tile, each tile
-// through every view in turn.  RM_PROJECT and RM_RESIDUAL.
+// pieces and order of additions).  Tiles: a block takes kPacketTP pixels
+// along P x kPacketTQ across; blocks run tile by tile, each tile through every
+// view in turn.  RM_PROJECT and RM_RESIDUAL.
 template <int MODE>
-__global__ __launch_bounds__(256) void ray_packet_kernel(RayArgs a) {
+__global__ __launch_bounds__(64 * kPacketWaves) void ray_packet_kernel(RayArgs a) {
     constexpr int K = kPacket;
     const int blk = xcd_remap(blockIdx.x, a.n_blocks);
     // groups of kPacketTileGroup consecutive tiles; inside a group every view
@@ -833,12 +842,13 @@ __global__ __launch_bounds__(256) void ray_packet_kernel(RayArgs a) {
     const int view = rg / G, tile = grp * G + (rg - (rg / G) * G);
     const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
     const bool pu = vw[VT_PACKET] == 0.0;   // packets along u (else v)
+    constexpr int TP = kPacketTP, TQ = kPacketTQ, RQ = 64 / kPacketLanesP;
     const int NP = pu ? a.U : a.V, NQ = pu ? a.V : a.U;
-    const int ntp = (NP + 63) / 64, ntq = (NQ + 15) / 16;
+    const int ntp = (NP + TP - 1) / TP, ntq = (NQ + TQ - 1) / TQ;
     if (tile >= ntp * ntq) return;
     const int tp = tile % ntp, tq = tile / ntp;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int p0 = tp * 64 + (lane & 15) * K, q = tq * 16 + wv * 4 + (lane >> 4);
+    const int p0 = tp * TP + (lane % kPacketLanesP) * K, q = tq * TQ + wv * RQ + lane / kPacketLanesP;
     if (p0 >= NP || q >= NQ) return;
     const int kk = min(K, NP - p0);
     const int u0 = pu ? p0 : q, v0 = pu ? q : p0;
@@ -2062,12 +2072,13 @@ static RayArgs ray_args(const LaunchGeom &g) {
 template <int MODE>
 static hipError_t launch_ray(const LaunchGeom &g, RayArgs a, hipStream_t s) {
     if ((MODE == RM_PROJECT || MODE == RM_RESIDUAL) && g.packet && !g.two_d && !a.surf.off) {
-        // tiles of 64 x 16 pixels, the long side along each view's packet axis
-        const int tu = ((g.U + 63) / 64) * ((g.V + 15) / 16), tv = ((g.V + 63) / 64) * ((g.U + 15) / 16);
+        // tiles of kPacketTP x kPacketTQ pixels, the first along each view's packet axis
+        constexpr int TP = kPacketTP, TQ = kPacketTQ;
+        const int tu = ((g.U + TP - 1) / TP) * ((g.V + TQ - 1) / TQ), tv = ((g.V + TP - 1) / TP) * ((g.U + TQ - 1) / TQ);
         const int G = kPacketTileGroup;
         a.n_blocks = g.n_views * ((std::max(tu, tv) + G - 1) / G) * G;
         hipLaunchKernelGGL((ray_packet_kernel<MODE == RM_PROJECT ? RM_PROJECT : RM_RESIDUAL>), dim3(a.n_blocks),
-                           dim3(256), 0, s, a);
+                           dim3(64 * kPacketWaves), 0, s, a);
         return hipGetLastError();
     }
     const dim3 grid(a.n_blocks), block(256);
