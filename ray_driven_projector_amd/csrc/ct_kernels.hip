@@ -1246,7 +1246,9 @@ __device__ __forceinline__ void iwalk2_scatter_fix(const IWalk2 &w, unsigned lon
 // apart along the axis none of them crosses): the live-axis walk once, and at
 // every piece one term per ray into its own cell of the untraversed axis
 // (off[j], from the walk's cell).  A ray without a value there has Y = 0.
-template <bool SHIFT, int K>
+// SD > 0: the rays' cells are consecutive along the untraversed axis, whose
+// LDS byte stride is SD: off[j] = j SD, an immediate offset of the add.
+template <bool SHIFT, int K, uint32_t SD>
 __device__ __forceinline__ void iwalk2_scatter_packet(const IWalk2 &w, unsigned long long *lds, const int (&Y)[K],
                                                       const int (&sh)[K], const uint32_t (&off)[K]) {
     const uint32_t qa = w.qa, qb = w.qb, sa = w.sa, sb = w.sb, lend = w.lend;
@@ -1254,7 +1256,14 @@ __device__ __forceinline__ void iwalk2_scatter_packet(const IWalk2 &w, unsigned 
     uint32_t lc = 0, t = min(la, lb);
     const auto put = [&](uint32_t len) {
 #pragma unroll
-        for (int j = 0; j < K; ++j) lds_add(lds, idx + off[j], term<SHIFT>(len, Y[j], sh[j]));
+        for (int j = 0; j < K; ++j) {
+            if constexpr (SD > 0) {
+                unsigned long long *cell = (unsigned long long *)((char *)lds + idx) + j * (SD / 8);
+                atomicAdd(cell, term<SHIFT>(len, Y[j], sh[j]));
+            } else {
+                lds_add(lds, idx + off[j], term<SHIFT>(len, Y[j], sh[j]));
+            }
+        }
     };
     const auto advance = [&]() {
         const bool ba = la == t;
@@ -1747,10 +1756,28 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
                 Yf[j] = in ? yv[j] * yscale : 0.f;   // |Yf| < 2^23
                 mant_any = mant_any || (Yf[j] != 0.f && (a.yshift != 0 || fabsf(Yf[j]) < 0x1p17f));
             }
-            bool some = false;
+            bool some = false, consec = true;
 #pragma unroll
-            for (int j = 0; j < K; ++j) some = some || Yf[j] != 0.f;
+            for (int j = 0; j < K; ++j) {
+                some = some || Yf[j] != 0.f;
+                consec = consec && off[j] == off[0] + j * Sd;
+            }
             if (!some) continue;
+            // consecutive cells (every ray's, also those without a value):
+            // the walk's cell takes ray 0's, the others are immediate offsets
+            const bool cw = __builtin_amdgcn_ballot_w64(!consec) == 0;
+            if (cw) {
+                w.idx += off[0];
+#pragma unroll
+                for (int j = 0; j < K; ++j) off[j] = 0u;
+            }
+            const auto walk = [&](auto shift_tag, const int(&Y)[K], const int(&sh)[K]) {
+                constexpr bool SH = decltype(shift_tag)::value;
+                if (cw && d == 0) iwalk2_scatter_packet<SH, K, SX>(w, acc, Y, sh, off);
+                else if (cw && d == 1) iwalk2_scatter_packet<SH, K, SY>(w, acc, Y, sh, off);
+                else if (cw) iwalk2_scatter_packet<SH, K, SZ>(w, acc, Y, sh, off);
+                else iwalk2_scatter_packet<SH, K, 0>(w, acc, Y, sh, off);
+            };
             int Y[K], sh[K];
             if (__builtin_amdgcn_ballot_w64(mant_any)) {
 #pragma unroll
@@ -1762,14 +1789,14 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
                     Y[j] = sh[j] <= 46 ? Yv : 0;   // else every term is below one unit
                     sh[j] = min(sh[j], 46);
                 }
-                iwalk2_scatter_packet<true, K>(w, acc, Y, sh, off);
+                walk(std::true_type{}, Y, sh);
             } else {
 #pragma unroll
                 for (int j = 0; j < K; ++j) {
                     Y[j] = (int)rintf(__builtin_amdgcn_fmed3f(Yf[j], -8388607.f, 8388607.f));
                     sh[j] = 0;
                 }
-                iwalk2_scatter_packet<false, K>(w, acc, Y, sh, off);
+                walk(std::false_type{}, Y, sh);
             }
         }
     };
