@@ -26,14 +26,17 @@ Default run (one JSON line):
   ALU one: algorithmic lane operations per launch over the launch's duration
   against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s (one
   wave64 VALU instruction per SIMD every 4 cycles; packed math does not apply
-  to this integer and compare work).  The algorithmic work is 12 lane
-  operations per intersection: the cell-walk bookkeeping of a Siddon step
-  (minimum of the next crossings, the compares, the index and position
-  updates, the loop test) plus the length and the multiply-add, 10 to 14 by
-  the model the bound was derived from; the kernels spend more (the measured
-  figure, from committed counters, is given beside it).  The effective-HBM
-  view (4 bytes per intersection against 8 TB/s, most of them served by the
-  caches) is kept as "effective_hbm_frac".
+  to this integer and compare work).  The algorithmic work per intersection
+  is that of the walk that runs: a Siddon step is 10 lane operations of
+  bookkeeping and length (minimum of the next crossings, the compares, the
+  index and position updates, the loop test, the length) plus 2 for the
+  multiply-add, 12 in all (10 to 14 by the model the bound was derived
+  from); where four rays share one walk (parallel views with an untraversed
+  axis whose pixel step runs along it, as on the dual-axis workload) the 10
+  are shared, 10 / 4 + 2 = 4.5.  The kernels spend more (the measured figure,
+  from committed counters, is given beside it).  The effective-HBM view (4
+  bytes per intersection against 8 TB/s, most of them served by the caches)
+  is kept as "effective_hbm_frac".
 - "traffic" and the measured VALU instructions come from rocprofv3 counter
   runs committed in profiles/counters.json; they are reported only while the
   library's device code object is the one they were taken on (its SHA-256).
@@ -67,8 +70,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12
 # VALU issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane operations per second
 VALU_PEAK = 256 * 4 * 16 * 2.4e9
-# algorithmic lane operations per ray-voxel intersection (see the module notes)
-OPS_PER_INTERSECTION = 12
+# algorithmic lane operations per ray-voxel intersection (see the module notes):
+# walk bookkeeping and length, shared by the rays of a packet, plus the
+# multiply-add of each ray
+WALK_OPS, RAY_OPS, PACKET = 10, 2, 4
+OPS_PER_INTERSECTION = WALK_OPS + RAY_OPS
+OPS_PACKET = WALK_OPS / PACKET + RAY_OPS
 # fp32 vector peak without packed math, for the FDK gather: VALU_PEAK x 2 (FMA)
 ALU_PEAK = 2 * VALU_PEAK
 # FDK backprojection flops per voxel-view: three affine forms (9 FMA = 18), a
@@ -116,6 +123,12 @@ ROLES = (("ray_kernel<0,", "project"), ("ray_kernel<1,", "sirt_residual"), ("ray
          ("fbp_fft_filter_kernel", "fbp_filter"), ("fbp_filter_kernel", "fbp_filter"))
 BRICK_MODES = {"0": "backproject", "1": "sirt_update", "2": "colinv", "3": "cgls_adjoint"}
 COPY_BYTES = 1 << 30   # the --copy-calibration copy reads and writes 1 GiB
+# the rocprofv3 --pmc passes the counters come from: (output name, counters, extra bench flag)
+PMC_PASSES = (("sq", "SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVES SQ_INSTS_VMEM_RD SQ_LDS_BANK_CONFLICT "
+               "GRBM_GUI_ACTIVE", ""),
+              ("tcc", "TCC_HIT_sum TCC_MISS_sum", ""),
+              ("fetch", "FETCH_SIZE", " --copy-calibration"),
+              ("write", "WRITE_SIZE", " --copy-calibration"))
 
 
 def kernel_role(name: str):
@@ -206,6 +219,16 @@ def ingest_counters(specs, out_path=COUNTERS):
                     f"{(format(e['cycles'] / 1e6, '.1f') if 'cycles' in e else '')} | {g('l2_hit', '{}')} | "
                     f"{(format(e['fetch_bytes'] / 1e9, '.2f') if 'fetch_bytes' in e else '')} | "
                     f"{(format(e['write_bytes'] / 1e9, '.2f') if 'write_bytes' in e else '')} |\n")
+        f.write("\nEach workload `<wl>` takes four passes of one step each (`--extra` on the parallel workload adds "
+                "the SIRT, weight and atomic-adjoint kernels), from /tmp, `<repo>` the repository root:\n\n")
+        for out, pmc, cal in PMC_PASSES:
+            f.write(f"    rocprofv3 --pmc {pmc} --output-format csv -d <repo>/gpurun_out/cnt/<wl> -o {out} -- "
+                    f"python3 <repo>/bench.py --workload <wl> --steps 1 --warmup 0 --no-cpu-baseline [--extra]{cal}\n")
+        f.write("\nthen `python3 bench.py --ingest-counters " +
+                " ".join(f"{s.split('=', 1)[0]}=gpurun_out/cnt/{s.split('=', 1)[0]}" for s in specs) + "`.\n"
+                "VALU busy = SQ_INSTS_VALU x 4 cycles / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); "
+                "HBM bytes = FETCH_SIZE / WRITE_SIZE in KiB x the calibration factor, which makes the counter read "
+                "1 GiB for a 1 GiB device-to-device copy in the same run.\n")
     print(f"wrote {out_path} and {md}: {len(entries)} entries", flush=True)
 
 
@@ -222,14 +245,24 @@ def golden_nnz(wl, config: int):
     return int(e["nnz"]) if e.get("frames_sha256") == sha else None
 
 
-def alu_roofline(kernel: str, nnz: int, ms: float, key: str):
-    ops = OPS_PER_INTERSECTION * nnz
+def packet_views(wl) -> bool:
+    """Every view of the workload runs in packets (parallel, flat, a detector
+    axis along an untraversed volume axis: the view table's packet slot)."""
+    import ray_driven_projector_amd as rdp
+    t = rdp.ct_geom_view_table(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing,
+                               wl.frames)
+    return bool((t[:, 47] >= 0).all()) and getattr(wl, "offsets", None) is None
+
+
+def alu_roofline(kernel: str, nnz: int, ms: float, key: str, packets: bool = False):
+    per = OPS_PACKET if packets else OPS_PER_INTERSECTION
+    ops = int(per * nnz)
     achieved = ops / (ms * 1e-3)
     c = counters(key)
     out = {"bound": "alu", "kernel": kernel, "achieved": round(achieved / 1e12, 2),
            "peak": round(VALU_PEAK / 1e12, 2), "unit": "T lane-ops/s", "frac": round(achieved / VALU_PEAK, 4),
            "traffic": None, "algorithmic_ops_per_launch": ops,
-           "ops_per_intersection": OPS_PER_INTERSECTION,
+           "ops_per_intersection": per,
            "effective_hbm_frac": round(4 * nnz / (ms * 1e-3) / HBM_PEAK, 4)}
     if c:
         out["traffic"] = c.get("hbm_bytes")
@@ -312,13 +345,16 @@ class Timer:
         return ts[len(ts) // 2]
 
 
-def kernel_names(wl, W):
+def kernel_names(wl, W, mode=0):
+    """(forward, adjoint) kernel names; mode 0: A and A^T, 1: the SIRT pair."""
     two_d = wl.beam in (W.BEAM_PARALLEL2D, W.BEAM_FAN2D)
     persp = wl.beam in (W.BEAM_FAN2D, W.BEAM_CONE)
     sf = "true" if getattr(wl, "offsets", None) is not None else "false"
     shape = "16, 16, 1, 256" if two_d else "16, 16, 32, 512"
-    return (f"ray_kernel<0, {'true' if two_d else 'false'}, {sf}>",
-            f"brick_kernel<{shape}, 0, {sf}, {'true' if persp else 'false'}>")
+    fwd = (f"ray_packet_kernel<{mode}>" if packet_views(wl) else
+           f"ray_kernel<{mode}, {'true' if two_d else 'false'}, {sf}>")
+    return fwd, f"brick_kernel<{shape}, {mode}, {sf}, {'true' if persp else 'false'}> (packets of {PACKET})" \
+        if packet_views(wl) else f"brick_kernel<{shape}, {mode}, {sf}, {'true' if persp else 'false'}>"
 
 
 def config_pair(cfg, rdp, W, torch, stream, timer):
@@ -337,13 +373,14 @@ def config_pair(cfg, rdp, W, torch, stream, timer):
     ms_at = timer.median_ms(lambda: rdp.ct_backproject(g, y, vol, stream))
     n = nnz if nnz is not None else gpu_nnz
     ka, kat = kernel_names(wl, W)
+    pk = packet_views(wl)
     out = {"workload": wl.name, "nnz": n, "nnz_source": "oracle" if nnz is not None else "gpu count",
            "gpu_count_matches": gpu_nnz == n,
            "A_ms": round(ms_a, 4), "AT_ms": round(ms_at, 4),
            "A_G_intersections_per_s": round(n / (ms_a * 1e-3) / 1e9, 1),
            "AT_G_intersections_per_s": round(n / (ms_at * 1e-3) / 1e9, 1),
-           "A_roofline": alu_roofline(ka, n, ms_a, f"c{cfg}/project"),
-           "AT_roofline": alu_roofline(kat, n, ms_at, f"c{cfg}/backproject")}
+           "A_roofline": alu_roofline(ka, n, ms_a, f"c{cfg}/project", pk),
+           "AT_roofline": alu_roofline(kat, n, ms_at, f"c{cfg}/backproject", pk)}
     del g, x, y, sino, vol
     torch.cuda.empty_cache()
     return out
@@ -394,8 +431,9 @@ def default_run(args, rdp, W, torch, np):
     ms_upd = float(np.mean([e[1].elapsed_time(e[2]) for e in all_evs]))
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = 2 * nnz / (ms_step * 1e-3) / 1e9
-    kernels = {"sirt_residual": ("ray_kernel<1, false, false>", ms_res),
-               "sirt_update": ("brick_kernel<16, 16, 32, 512, 1, false, false>", ms_upd)}
+    pk = packet_views(wl)
+    kres, kupd = kernel_names(wl, W, 1)
+    kernels = {"sirt_residual": (kres, ms_res), "sirt_update": (kupd, ms_upd)}
     dom = max(kernels, key=lambda k: kernels[k][1])
     res = {
         "metric": "G ray-voxel intersections/s for A and A^T; ms per SIRT iteration at 512^3",
@@ -410,8 +448,8 @@ def default_run(args, rdp, W, torch, np):
                    "intersections_per_pass": nnz, "rays": M, "voxels": N},
         "ms_per_sirt_iteration": round(ms_step, 3),
         "kernel_ms": {k: round(v[1], 3) for k, v in kernels.items()},
-        "roofline": alu_roofline(kernels[dom][0], nnz, kernels[dom][1], f"c4/{dom}"),
-        "roofline_other": {k: alu_roofline(v[0], nnz, v[1], f"c4/{k}") for k, v in kernels.items() if k != dom},
+        "roofline": alu_roofline(kernels[dom][0], nnz, kernels[dom][1], f"c4/{dom}", pk),
+        "roofline_other": {k: alu_roofline(v[0], nnz, v[1], f"c4/{k}", pk) for k, v in kernels.items() if k != dom},
     }
     del g, x_true, y, rinv, cinv, x, work
     torch.cuda.empty_cache()
@@ -488,7 +526,7 @@ def single_run(args, rdp, W, torch, np):
         x = torch.zeros(g.vol_shape, device="cuda")
         work = torch.empty(g.sino_shape, device="cuda")
         names = ("sirt_residual", "sirt_update")
-        ka, kat = "ray_kernel<1, false, false>", "brick_kernel<16, 16, 32, 512, 1, false, false>"
+        ka, kat = kernel_names(wl, W, 1)
 
         def step(evs):
             evs[0].record(stream)
@@ -559,7 +597,8 @@ def single_run(args, rdp, W, torch, np):
     else:
         dom = 0 if ms[0] >= ms[1] else 1
         kern = (ka, kat)[dom]
-        res["roofline"] = alu_roofline(kern, nnz, ms[dom], f"c{cfg}/{names[dom]}")
+        res["roofline"] = alu_roofline(kern, nnz, ms[dom], f"c{cfg}/{names[dom]}",
+                                       packet_views(wl) and args.workload != "c5cyl")
         if cfg == 4:
             res["ms_per_sirt_iteration"] = round(ms_step, 3)
     if args.extra:
