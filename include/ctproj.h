@@ -50,6 +50,14 @@
  *     concurrent forward projections with one handle, ct_project_ws takes the
  *     copies in caller workspace and only reads the handle, as every other
  *     call does.
+ *   - When the volume fits one buffer, the detector sides are below 2^16 and
+ *     the table fits 4 GiB, the handle also holds the adjoint's record table:
+ *     64 bytes per (brick, view) pair (bricks of 16 x 16 x 32 voxels, 16 x 16
+ *     in 2D), the footprint of the brick on that view's detector and its anchor
+ *     ray, built at creation and only read afterwards (512^3 with 720 views:
+ *     755 MB).  Adjoint calls over the whole volume read it; region calls
+ *     whose boxes are not the whole volume, and handles without the table,
+ *     compute the same values in the kernel (the same bits).
  *   - Every compute call is asynchronous and ordered on the caller's stream
  *     (a hipStream_t passed as void*; NULL is the legacy default stream).
  *   - Compute calls allocate nothing: all device memory they touch is the
@@ -133,7 +141,8 @@ typedef struct {
 ct_status_t ct_geom_validate(const ct_geom_desc_t *desc);
 
 /* Validate, precompute the per-view float64 ray table, allocate and upload it
- * to the current HIP device (synchronous).  *out receives the handle. */
+ * to the current HIP device, and build the adjoint's record table there when it
+ * fits (synchronous).  *out receives the handle. */
 ct_status_t ct_geom_create(const ct_geom_desc_t *desc, ct_geom_t *out);
 
 /* Create a geometry whose detector is a parameterized surface (diffct

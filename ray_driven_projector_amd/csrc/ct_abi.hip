@@ -50,6 +50,8 @@ struct ct_geom_s {
     double *d_off = nullptr;            // detector surface offsets (float64), or null: flat
     int surf_per_view = 0;
     float *d_env = nullptr;             // per-view footprint envelopes of the surface
+    void *d_brick_rec = nullptr;        // brick adjoint: per-(brick, view) footprints and anchors of
+                                        // the whole volume (read-only after creation), or null
 };
 
 namespace {
@@ -61,6 +63,10 @@ constexpr uint64_t kMagic = 0x43545052'4F4A3031ull;  // "CTPROJ01"
 // Larger lattices are reached through the region and host-streaming calls.
 constexpr int64_t kMaxBufferVoxels = int64_t(1) << 30;
 constexpr int64_t kMaxBufferRays = int64_t(1) << 31;
+// The brick adjoint's record table (64 bytes per brick and view) is built at
+// creation when it fits this budget and the detector sides fit 16 bits; else the
+// kernel computes footprints and anchors itself.
+constexpr size_t kMaxBrickRecordBytes = size_t(4) << 30;
 
 ct_status_t fail(ct_status_t st, const char *msg) {
     set_error(msg);
@@ -99,6 +105,9 @@ LaunchGeom lg(ct_geom_t g) {
     l.surf_off = g->d_off;
     l.surf_per_view = g->surf_per_view;
     l.surf_env = g->d_env;
+    l.brick_rec = g->d_brick_rec;
+    l.rec_stride = (int)g->host.n_views;
+    l.rec_view0 = 0;
     return l;
 }
 
@@ -115,6 +124,11 @@ LaunchGeom lg_region(ct_geom_t g, const ct_region_t &r, int64_t vb, int64_t ve, 
     l.accumulate = accumulate ? 1 : 0;
     l.views = g->d_views + (size_t)vb * CT_VIEW_TABLE_STRIDE;
     l.n_views = (int)(ve - vb);
+    // the record table holds the whole volume's bricks: regions compute their own
+    const bool whole = r.x0 == 0 && r.y0 == 0 && r.z0 == 0 && r.nx == g->host.W && r.ny == g->host.H &&
+                       r.nz == g->host.D;
+    if (whole) l.rec_view0 = (int)vb;
+    else l.brick_rec = nullptr;
     if (g->d_off && g->surf_per_view) l.surf_off = g->d_off + (size_t)vb * g->host.U * g->host.V * 3;
     if (g->d_env) l.surf_env = g->d_env + (size_t)vb * surface_env_floats((int)g->host.U, (int)g->host.V);
     return l;
@@ -402,6 +416,7 @@ static void free_handle(ct_geom_s *g) {
     if (g->d_vol_zf) (void)hipFree(g->d_vol_zf);
     if (g->d_off) (void)hipFree(g->d_off);
     if (g->d_env) (void)hipFree(g->d_env);
+    if (g->d_brick_rec) (void)hipFree(g->d_brick_rec);
     delete g;
 }
 
@@ -497,6 +512,25 @@ static ct_status_t create_impl(const ct_geom_desc_t *desc, const double *offsets
         if (bad) {
             free_handle(g);
             return fail(CT_E_FRAME, "a surface pixel is not in front of the source");
+        }
+    }
+    // the brick adjoint's record table (synchronous); without it the kernel
+    // computes the same footprints and anchors itself
+    if (h.D * h.H * h.W < kMaxBufferVoxels && h.U < 65536 && h.V < 65536) {
+        const LaunchGeom l = lg(g);
+        const size_t bytes = brick_record_count(l) * brick_record_bytes();
+        if (bytes <= kMaxBrickRecordBytes) {
+            if (hipMalloc(&g->d_brick_rec, bytes) != hipSuccess) {
+                (void)hipGetLastError();
+                g->d_brick_rec = nullptr;   // the kernel computes them
+            } else {
+                e = launch_brick_records(l, g->d_brick_rec, nullptr);
+                if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+                if (e != hipSuccess) {
+                    free_handle(g);
+                    return hip_fail(e, "brick record table");
+                }
+            }
         }
     }
     *out = g;

@@ -1005,6 +1005,7 @@ __global__ __launch_bounds__(64 * kPacketWaves) void ray_packet_kernel(RayArgs a
 // x += alpha p (alpha read from the CGLS state) and p = s (the start).
 enum BrickMode : int { BM_BACKPROJECT = 0, BM_SIRT_UPDATE = 1, BM_COLINV = 2, BM_CGLS = 3 };
 
+struct BrickRec;
 struct BrickArgs {
     const double *views;
     const float *sino;        // BM_BACKPROJECT, BM_SIRT_UPDATE
@@ -1022,6 +1023,11 @@ struct BrickArgs {
     Surface surf;             // detector surface (off == null: flat)
     const float *env;         // surface: per-view footprint envelopes
     int offx, offy, offz;     // voxel index of the volume buffer's first voxel (a region)
+    const BrickRec *rec;      // per-(brick, view) records of this launch's bricks, or null:
+                              // record of brick b, view k at rec[b * rec_stride + k]
+    int rec_stride;
+    int y_vec4;               // the sinogram's rows are 16-byte aligned (V % 4 == 0, aligned base):
+                              // pass 1 reads them four values at a time
     int accumulate;           // BM_BACKPROJECT: add to the volume instead of writing it
     int yshift;               // every term shifted right by this many bits (range bound)
     int W, H, D, U, V, n_views;
@@ -1066,25 +1072,30 @@ __device__ __forceinline__ double block_sum(double v, double *wsum) {
 }
 
 // Footprint of the brick [x0, x0+ex) x [y0, y0+ey) x [z0, z0+ez) on the detector of
-// one view: the bounding box of its 8 projected corners (lane & 7 projects corner
-// lane & 7; lanes reduce in groups of 8).  Returns false if no pixel can see it.
+// one view: the bounding box of its 8 projected corners.  Returns false if no pixel
+// can see it.  Two forms give the same box: the wave form (lane & 7 projects
+// corner lane & 7, lanes reduce in groups of 8; the surface envelopes are searched
+// by the whole wave) and the lane form (one lane projects all 8 corners and
+// searches alone), which builds the per-(brick, view) record table.
 struct Footprint {
     int u0, u1, v0, v1;
 };
-__device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int x0, int y0, int z0,
-                                                int ex, int ey, int ez, int U, int V, bool two_d,
-                                                const float *env, Footprint &f) {
-    const int c = lane & 7;
+// View-table reads through the constant address space: wave-uniform reads
+// become scalar loads (the table is never written while a kernel runs).
+typedef const __attribute__((address_space(4))) double *ConstViewPtr;
+__device__ __forceinline__ double vt(const double *vw, int i) { return ((ConstViewPtr)vw)[i]; }
+// Corner c (bit 0: x, bit 1: y, bit 2: z far side) on the detector, in pixel units;
+// bad: the corner lies at or behind the source.
+__device__ __forceinline__ void corner_uv(const double *vw, int c, int x0, int y0, int z0, int ex, int ey,
+                                          int ez, bool persp, float &cu, float &cvv, int &bad) {
     const double X = (c & 1) ? x0 + ex : x0;
     const double Y = (c & 2) ? y0 + ey : y0;
     const double Z = (c & 4) ? z0 + ez : z0;
-    const double rx = X - vw[VT_O00 + 0], ry = Y - vw[VT_O00 + 1], rz = Z - vw[VT_O00 + 2];
-    const double al = vw[VT_MINV + 0] * rx + vw[VT_MINV + 1] * ry + vw[VT_MINV + 2] * rz;
-    const double be = vw[VT_MINV + 3] * rx + vw[VT_MINV + 4] * ry + vw[VT_MINV + 5] * rz;
-    const double ga = vw[VT_MINV + 6] * rx + vw[VT_MINV + 7] * ry + vw[VT_MINV + 8] * rz;
-    const bool persp = vw[VT_PERSP] != 0.0;
-    float cu, cvv;
-    int bad = 0;
+    const double rx = X - vt(vw, VT_O00 + 0), ry = Y - vt(vw, VT_O00 + 1), rz = Z - vt(vw, VT_O00 + 2);
+    const double al = vt(vw, VT_MINV + 0) * rx + vt(vw, VT_MINV + 1) * ry + vt(vw, VT_MINV + 2) * rz;
+    const double be = vt(vw, VT_MINV + 3) * rx + vt(vw, VT_MINV + 4) * ry + vt(vw, VT_MINV + 5) * rz;
+    const double ga = vt(vw, VT_MINV + 6) * rx + vt(vw, VT_MINV + 7) * ry + vt(vw, VT_MINV + 8) * rz;
+    bad = 0;
     if (persp) {
         // a corner at or behind the source: every pixel may see the brick
         bad = !(al > 1e-9);
@@ -1094,31 +1105,47 @@ __device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int 
         cu = (float)be;
         cvv = (float)ga;
     }
-    float umin = cu, umax = cu, vmin = cvv, vmax = cvv;
-    for (int off = 1; off < 8; off <<= 1) {
-        umin = fminf(umin, __shfl_xor(umin, off));
-        umax = fmaxf(umax, __shfl_xor(umax, off));
-        vmin = fminf(vmin, __shfl_xor(vmin, off));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-        bad |= __shfl_xor(bad, off);
+}
+// First index i in [0, n) with a[i] >= x (GT: a[i] > x), n if none; a
+// non-decreasing.  One lane alone (binary search): the same index as first_hit.
+template <bool GT>
+__device__ __forceinline__ int first_hit_lane(const float *a, int n, float x) {
+    int lo = 0, hi = n;   // the first hit lies in [lo, hi]
+    while (lo < hi) {
+        const int mid = lo + ((hi - lo) >> 1);
+        const bool hit = GT ? a[mid] > x : a[mid] >= x;
+        hi = hit ? mid : hi;
+        lo = hit ? lo : mid + 1;
     }
-    umin = uni(umin); umax = uni(umax); vmin = uni(vmin); vmax = uni(vmax);
-    bad = uni(bad);
+    return lo;
+}
+// The pixel box from the corners' extremes (wave-uniform in the wave form).
+template <bool WAVE>
+__device__ __forceinline__ bool footprint_box(float umin, float umax, float vmin, float vmax, int bad, int U,
+                                              int V, bool two_d, const float *env, int lane, Footprint &f) {
+    const auto hit_lo = [&](const float *a, int n, float x) {
+        if constexpr (WAVE) return first_hit<false>(a, n, x, lane);
+        else return first_hit_lane<false>(a, n, x);
+    };
+    const auto hit_hi = [&](const float *a, int n, float x) {
+        if constexpr (WAVE) return first_hit<true>(a, n, x, lane);
+        else return first_hit_lane<true>(a, n, x);
+    };
     if (bad) {
         f.u0 = 0; f.u1 = U - 1; f.v0 = 0; f.v1 = V - 1;
     } else if (env) {
         // detector surface: the pixel ranges whose flat-plane crossings can fall in
         // the box (monotone envelopes; a margin for their float32 rounding)
         const float m = 1e-2f;
-        f.u0 = first_hit<false>(env + U, U, umin - m, lane);
-        f.u1 = first_hit<true>(env, U, umax + m, lane) - 1;
+        f.u0 = hit_lo(env + U, U, umin - m);
+        f.u1 = hit_hi(env, U, umax + m) - 1;
         f.v0 = V;
         f.v1 = -1;
         if (f.u0 <= f.u1) {
             for (int t = f.u0 / kEnvTile; t <= f.u1 / kEnvTile; ++t) {
                 const float *r = env + 2 * U + (size_t)t * 2 * V;
-                f.v0 = min(f.v0, first_hit<false>(r + V, V, vmin - m, lane));
-                f.v1 = max(f.v1, first_hit<true>(r, V, vmax + m, lane) - 1);
+                f.v0 = min(f.v0, hit_lo(r + V, V, vmin - m));
+                f.v1 = max(f.v1, hit_hi(r, V, vmax + m) - 1);
             }
         }
     } else {
@@ -1132,6 +1159,109 @@ __device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int 
     }
     if (two_d) { f.v0 = 0; f.v1 = 0; }
     return f.u0 <= f.u1 && f.v0 <= f.v1;
+}
+__device__ __forceinline__ bool brick_footprint(const double *vw, int lane, int x0, int y0, int z0,
+                                                int ex, int ey, int ez, int U, int V, bool two_d,
+                                                const float *env, Footprint &f) {
+    const bool persp = vt(vw, VT_PERSP) != 0.0;
+    float cu, cvv;
+    int bad;
+    corner_uv(vw, lane & 7, x0, y0, z0, ex, ey, ez, persp, cu, cvv, bad);
+    float umin = cu, umax = cu, vmin = cvv, vmax = cvv;
+    for (int off = 1; off < 8; off <<= 1) {
+        umin = fminf(umin, __shfl_xor(umin, off));
+        umax = fmaxf(umax, __shfl_xor(umax, off));
+        vmin = fminf(vmin, __shfl_xor(vmin, off));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+        bad |= __shfl_xor(bad, off);
+    }
+    umin = uni(umin); umax = uni(umax); vmin = uni(vmin); vmax = uni(vmax);
+    bad = uni(bad);
+    return footprint_box<true>(umin, umax, vmin, vmax, bad, U, V, two_d, env, lane, f);
+}
+__device__ __forceinline__ bool brick_footprint_lane(const double *vw, int x0, int y0, int z0, int ex, int ey,
+                                                     int ez, int U, int V, bool two_d, const float *env,
+                                                     Footprint &f) {
+    const bool persp = vw[VT_PERSP] != 0.0;
+    float umin = 3e38f, umax = -3e38f, vmin = 3e38f, vmax = -3e38f;
+    int bad = 0;
+    for (int c = 0; c < 8; ++c) {
+        float cu, cvv;
+        int b;
+        corner_uv(vw, c, x0, y0, z0, ex, ey, ez, persp, cu, cvv, b);
+        umin = fminf(umin, cu); umax = fmaxf(umax, cu);
+        vmin = fminf(vmin, cvv); vmax = fmaxf(vmax, cvv);
+        bad |= b;
+    }
+    return footprint_box<false>(umin, umax, vmin, vmax, bad, U, V, two_d, env, 0, f);
+}
+
+// The ray of a footprint's centre pixel (u0 + nfu/2, v0 + nfv/2), re-expressed
+// around the plane through the brick centre parallel to the detector: for a flat
+// detector, the point where pixel (u, v) meets that plane is affine in (u, v), so
+// per ray it is formed in float32 from this anchor plus small integer offsets and
+// positions stay within tens of voxels.  Positions are relative to the brick
+// centre; "fast" is the footprint's fast pixel axis (u when the view's wave patch
+// runs along u).  Computed in float64, rounded once.
+struct Anchor {
+    float A0x, A0y, A0z;   // anchor point on the plane, relative to the brick centre
+    float Afx, Afy, Afz;   // its step per fast pixel
+    float Asx, Asy, Asz;   // its step per slow pixel
+    float Dx, Dy, Dz;      // direction of the centre pixel's ray
+    float tv0, tv1;        // the ray's parameter range, relative to the plane crossing
+};
+__device__ __forceinline__ Anchor make_anchor(const double *vw, const Footprint &f, double cbx, double cby,
+                                              double cbz, bool ufast) {
+    const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1;
+    const double fu0 = f.u0 + nfu / 2, fv0 = f.v0 + nfv / 2;
+    const double nx_ = vt(vw, VT_N + 0), ny_ = vt(vw, VT_N + 1), nz_ = vt(vw, VT_N + 2);
+    const double aox = vt(vw, VT_O00 + 0) + fu0 * vt(vw, VT_OU + 0) + fv0 * vt(vw, VT_OV + 0);
+    const double aoy = vt(vw, VT_O00 + 1) + fu0 * vt(vw, VT_OU + 1) + fv0 * vt(vw, VT_OV + 1);
+    const double aoz = vt(vw, VT_O00 + 2) + fu0 * vt(vw, VT_OU + 2) + fv0 * vt(vw, VT_OV + 2);
+    const double adx = vt(vw, VT_D00 + 0) + fu0 * vt(vw, VT_DU + 0) + fv0 * vt(vw, VT_DV + 0);
+    const double ady = vt(vw, VT_D00 + 1) + fu0 * vt(vw, VT_DU + 1) + fv0 * vt(vw, VT_DV + 1);
+    const double adz = vt(vw, VT_D00 + 2) + fu0 * vt(vw, VT_DU + 2) + fv0 * vt(vw, VT_DV + 2);
+    // Dir . N is the same for every pixel of a flat detector
+    const double tb = ((cbx - aox) * nx_ + (cby - aoy) * ny_ + (cbz - aoz) * nz_) /
+                      (adx * nx_ + ady * ny_ + adz * nz_);
+    const int pf = ufast ? VT_OU : VT_OV, ps = ufast ? VT_OV : VT_OU;
+    const int qf_ = ufast ? VT_DU : VT_DV, qs_ = ufast ? VT_DV : VT_DU;
+    Anchor an;
+    an.A0x = (float)(aox + tb * adx - cbx);
+    an.A0y = (float)(aoy + tb * ady - cby);
+    an.A0z = (float)(aoz + tb * adz - cbz);
+    an.Afx = (float)(vt(vw, pf + 0) + tb * vt(vw, qf_ + 0));
+    an.Afy = (float)(vt(vw, pf + 1) + tb * vt(vw, qf_ + 1));
+    an.Afz = (float)(vt(vw, pf + 2) + tb * vt(vw, qf_ + 2));
+    an.Asx = (float)(vt(vw, ps + 0) + tb * vt(vw, qs_ + 0));
+    an.Asy = (float)(vt(vw, ps + 1) + tb * vt(vw, qs_ + 1));
+    an.Asz = (float)(vt(vw, ps + 2) + tb * vt(vw, qs_ + 2));
+    an.Dx = (float)adx;
+    an.Dy = (float)ady;
+    an.Dz = (float)adz;
+    an.tv0 = (float)(vt(vw, VT_TMIN) - tb);
+    an.tv1 = (float)(vt(vw, VT_TMAX) - tb);
+    return an;
+}
+
+// One (brick, view) pair of the record table: the footprint (u1 < u0: the view
+// does not see the brick) and the anchor.  64 bytes, read by scalar loads.
+struct BrickRec {
+    uint32_t fu;   // u0 | u1 << 16
+    uint32_t fv;   // v0 | v1 << 16
+    Anchor an;
+};
+static_assert(sizeof(BrickRec) == 64, "brick record layout");
+typedef const __attribute__((address_space(4))) BrickRec *ConstRecPtr;
+// a record's anchor, field by field (scalar loads)
+__device__ __forceinline__ Anchor rec_anchor(ConstRecPtr r) {
+    Anchor an;
+    an.A0x = r->an.A0x; an.A0y = r->an.A0y; an.A0z = r->an.A0z;
+    an.Afx = r->an.Afx; an.Afy = r->an.Afy; an.Afz = r->an.Afz;
+    an.Asx = r->an.Asx; an.Asy = r->an.Asy; an.Asz = r->an.Asz;
+    an.Dx = r->an.Dx; an.Dy = r->an.Dy; an.Dz = r->an.Dz;
+    an.tv0 = r->an.tv0; an.tv1 = r->an.tv1;
+    return an;
 }
 
 // LDS scatter into 64-bit fixed point: lds[cell] += length * Y for every piece,
@@ -1375,8 +1505,8 @@ __device__ __forceinline__ DirPlan dir_plan_pos(float ax, float ay, float az, fl
 // per length unit; yscale = power-of-two fixed-point scale of the ray values.
 template <int LSY, int LSZ, int MODE, bool PERSP, bool TWO_D, bool SURF>
 __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw, int view,
-                                           const Footprint &f, int lane, int x0, int y0, int z0,
-                                           int ex, int ey, int ez, double cbx, double cby,
+                                           const Footprint &f, const Anchor &an, int lane, int x0, int y0,
+                                           int z0, int ex, int ey, int ez, double cbx, double cby,
                                            double cbz, float S, float yscale,
                                            unsigned long long *acc) {
     const float fex = (float)ex, fey = (float)ey, fez = (float)ez;
@@ -1384,43 +1514,23 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
     const int u0 = f.u0, v0 = f.v0;
     const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
-    const bool ufast = !TWO_D && vw[VT_PATCH] == 0.0;
+    const bool ufast = !TWO_D && vt(vw, VT_PATCH) == 0.0;
     const int nf = ufast ? nfu : nfv;
 
-    // ---- per (view, brick) ray parametrisation, anchored at the footprint's
-    // centre pixel (u0 + cu, v0 + cv), so pixel offsets stay within half the
-    // footprint; positions are relative to the brick centre ----
+    // ---- the footprint's anchor (centre pixel u0 + cu, v0 + cv; pixel offsets
+    // stay within half the footprint) and the per-pixel direction steps ----
     const int cu = nfu / 2, cv = nfv / 2;
-    const double nx_ = vw[VT_N + 0], ny_ = vw[VT_N + 1], nz_ = vw[VT_N + 2];
-    const float fnx = (float)nx_, fny = (float)ny_, fnz = (float)nz_;
-    const double fu0 = u0 + cu, fv0 = v0 + cv;
-    const double aox = vw[VT_O00 + 0] + fu0 * vw[VT_OU + 0] + fv0 * vw[VT_OV + 0];
-    const double aoy = vw[VT_O00 + 1] + fu0 * vw[VT_OU + 1] + fv0 * vw[VT_OV + 1];
-    const double aoz = vw[VT_O00 + 2] + fu0 * vw[VT_OU + 2] + fv0 * vw[VT_OV + 2];
-    const double adx = vw[VT_D00 + 0] + fu0 * vw[VT_DU + 0] + fv0 * vw[VT_DV + 0];
-    const double ady = vw[VT_D00 + 1] + fu0 * vw[VT_DU + 1] + fv0 * vw[VT_DV + 1];
-    const double adz = vw[VT_D00 + 2] + fu0 * vw[VT_DU + 2] + fv0 * vw[VT_DV + 2];
-    // Dir . N is the same for every pixel of a flat detector
-    const double tb = ((cbx - aox) * nx_ + (cby - aoy) * ny_ + (cbz - aoz) * nz_) /
-                      (adx * nx_ + ady * ny_ + adz * nz_);
-    // per-pixel steps along the footprint's fast (f) and slow (s) axes
-    const int pf = ufast ? VT_OU : VT_OV, ps = ufast ? VT_OV : VT_OU;
+    const float fnx = (float)vt(vw, VT_N + 0), fny = (float)vt(vw, VT_N + 1), fnz = (float)vt(vw, VT_N + 2);
     const int qf_ = ufast ? VT_DU : VT_DV, qs_ = ufast ? VT_DV : VT_DU;
-    const float A0x = uni((float)(aox + tb * adx - cbx));
-    const float A0y = uni((float)(aoy + tb * ady - cby));
-    const float A0z = uni((float)(aoz + tb * adz - cbz));
-    const float Afx = uni((float)(vw[pf + 0] + tb * vw[qf_ + 0]));
-    const float Afy = uni((float)(vw[pf + 1] + tb * vw[qf_ + 1]));
-    const float Afz = uni((float)(vw[pf + 2] + tb * vw[qf_ + 2]));
-    const float Asx = uni((float)(vw[ps + 0] + tb * vw[qs_ + 0]));
-    const float Asy = uni((float)(vw[ps + 1] + tb * vw[qs_ + 1]));
-    const float Asz = uni((float)(vw[ps + 2] + tb * vw[qs_ + 2]));
-    const float Dx = uni((float)adx), Dy = uni((float)ady), Dz = uni((float)adz);
-    const float DFx = uni((float)vw[qf_ + 0]), DFy = uni((float)vw[qf_ + 1]);
-    const float DFz = uni((float)vw[qf_ + 2]);
-    const float DSx = uni((float)vw[qs_ + 0]), DSy = uni((float)vw[qs_ + 1]);
-    const float DSz = uni((float)vw[qs_ + 2]);
-    const float tv0 = uni((float)(vw[VT_TMIN] - tb)), tv1 = uni((float)(vw[VT_TMAX] - tb));
+    const float A0x = uni(an.A0x), A0y = uni(an.A0y), A0z = uni(an.A0z);
+    const float Afx = uni(an.Afx), Afy = uni(an.Afy), Afz = uni(an.Afz);
+    const float Asx = uni(an.Asx), Asy = uni(an.Asy), Asz = uni(an.Asz);
+    const float Dx = uni(an.Dx), Dy = uni(an.Dy), Dz = uni(an.Dz);
+    const float DFx = uni((float)vt(vw, qf_ + 0)), DFy = uni((float)vt(vw, qf_ + 1));
+    const float DFz = uni((float)vt(vw, qf_ + 2));
+    const float DSx = uni((float)vt(vw, qs_ + 0)), DSy = uni((float)vt(vw, qs_ + 1));
+    const float DSz = uni((float)vt(vw, qs_ + 2));
+    const float tv0 = uni(an.tv0), tv1 = uni(an.tv1);
     // parallel rays: one direction plan for the footprint, and the anchor
     // coefficients of the origin mirrored with it (a sign change is exact)
     constexpr bool SHARED_DIR = !PERSP && !SURF;
@@ -1520,13 +1630,13 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     const double *ob = nullptr;
     double o0n = 0, o1n = 0, o2n = 0;
     if (SURF) {
-        sCx = vw[VT_C + 0]; sCy = vw[VT_C + 1]; sCz = vw[VT_C + 2];
-        sUx = vw[VT_EU + 0]; sUy = vw[VT_EU + 1]; sUz = vw[VT_EU + 2];
-        sVx = vw[VT_EV + 0]; sVy = vw[VT_EV + 1]; sVz = vw[VT_EV + 2];
-        sNx = vw[VT_EN + 0]; sNy = vw[VT_EN + 1]; sNz = vw[VT_EN + 2];
-        sDx = vw[VT_D00 + 0]; sDy = vw[VT_D00 + 1]; sDz = vw[VT_D00 + 2];
+        sCx = vt(vw, VT_C + 0); sCy = vt(vw, VT_C + 1); sCz = vt(vw, VT_C + 2);
+        sUx = vt(vw, VT_EU + 0); sUy = vt(vw, VT_EU + 1); sUz = vt(vw, VT_EU + 2);
+        sVx = vt(vw, VT_EV + 0); sVy = vt(vw, VT_EV + 1); sVz = vt(vw, VT_EV + 2);
+        sNx = vt(vw, VT_EN + 0); sNy = vt(vw, VT_EN + 1); sNz = vt(vw, VT_EN + 2);
+        sDx = vt(vw, VT_D00 + 0); sDy = vt(vw, VT_D00 + 1); sDz = vt(vw, VT_D00 + 2);
         if (PERSP) {   // offsets relative to the source: P - S = (C - S) + o . E
-            sCx -= vw[VT_O00 + 0]; sCy -= vw[VT_O00 + 1]; sCz -= vw[VT_O00 + 2];
+            sCx -= vt(vw, VT_O00 + 0); sCy -= vt(vw, VT_O00 + 1); sCz -= vt(vw, VT_O00 + 2);
         }
         ob = a.surf.off + 3 * ((a.surf.per_view ? (size_t)view * a.U * a.V : 0) +
                                (size_t)u0 * a.V + v0);
@@ -1580,7 +1690,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
                 double rdx, rdy, rdz, bx_, by_, bz_;   // direction; origin relative to the brick centre
                 if (PERSP) {
                     rdx = px; rdy = py; rdz = pz;
-                    bx_ = vw[VT_O00 + 0] - cbx; by_ = vw[VT_O00 + 1] - cby; bz_ = vw[VT_O00 + 2] - cbz;
+                    bx_ = vt(vw, VT_O00 + 0) - cbx; by_ = vt(vw, VT_O00 + 1) - cby; bz_ = vt(vw, VT_O00 + 2) - cbz;
                 } else {
                     rdx = sDx; rdy = sDy; rdz = sDz;
                     bx_ = px - cbx; by_ = py - cby; bz_ = pz - cbz;
@@ -1594,8 +1704,8 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
                 dx = (float)rdx;
                 dy = (float)rdy;
                 dz = TWO_D ? 0.f : (float)rdz;
-                t0 = (float)(vw[VT_TMIN] - tr);
-                t1 = (float)(vw[VT_TMAX] - tr);
+                t0 = (float)(vt(vw, VT_TMIN) - tr);
+                t1 = (float)(vt(vw, VT_TMAX) - tr);
             } else {
                 ox = fmaf(cs, Asx, fmaf(cf, Afx, A0x));
                 oy = fmaf(cs, Asy, fmaf(cf, Afy, A0y));
@@ -1819,7 +1929,8 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
 // Two 512-thread workgroups (or four of 256, one of 1024) share a CU through
 // their LDS, i.e. 4 waves per SIMD; the register budget is held to that.
 // SURF: parameterized detector surface (per-pixel rays from the offsets table).
-template <int BX, int BY, int BZ, int NT, int MODE, bool SURF, bool PERSP>
+// REC: footprints and anchors come from the launch's record table (a.rec).
+template <int BX, int BY, int BZ, int NT, int MODE, bool SURF, bool PERSP, bool REC>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void brick_kernel(
     BrickArgs a) {
     constexpr int LSY = BX + 1;           // padded LDS strides (elements): rays of a
@@ -1831,7 +1942,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     // footprints found in pass 1, reused by pass 2 (u1 < u0: the view misses
     // the brick); for up to kFpCache views on detectors below 2^16 pixels a
     // side, and only where the LDS still holds the workgroups of 4 waves per SIMD
-    constexpr bool FPC = (LN * 8 + kFpCache * 8 + 1024) * (1024 / NT) <= 160 * 1024;
+    constexpr bool FPC = !REC && (LN * 8 + kFpCache * 8 + 1024) * (1024 / NT) <= 160 * 1024;
     __shared__ ushort4 fpc[FPC ? kFpCache : 1];
     for (int i = threadIdx.x; i < LN; i += NT) acc[i] = 0ull;
 
@@ -1859,29 +1970,64 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
 
     // ---- pass 1: largest |y| over the rays that can meet this brick ----
+    // Footprints come from the record table when the launch has one, else they
+    // are computed here and kept in LDS for pass 2.
+    const ConstRecPtr rec = REC ? (ConstRecPtr)a.rec + (size_t)blk * a.rec_stride : nullptr;
     float ymax = 1.f;
-    const bool cache = FPC && MODE != BM_COLINV && a.n_views <= kFpCache && a.U < 65536 && a.V < 65536;
+    const bool cache = !REC && FPC && MODE != BM_COLINV && a.n_views <= kFpCache && a.U < 65536 && a.V < 65536;
+    const auto rec_footprint = [&](int view, Footprint &f) {
+        const uint32_t fu = rec[view].fu, fv = rec[view].fv;
+        f.u0 = uni((int)(fu & 0xFFFFu));
+        f.u1 = uni((int)(fu >> 16));
+        f.v0 = uni((int)(fv & 0xFFFFu));
+        f.v1 = uni((int)(fv >> 16));
+        return f.u0 <= f.u1;
+    };
     if (MODE != BM_COLINV) {
         float m = 0.f;
         for (int view = wv; view < a.n_views; view += NWAVES) {
             const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
             Footprint f;
-            const bool seen = brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
-                                              a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f);
-            if (cache && lane == 0)
-                fpc[view] = seen ? make_ushort4((unsigned short)f.u0, (unsigned short)f.u1,
-                                                (unsigned short)f.v0, (unsigned short)f.v1)
-                                 : make_ushort4(1, 0, 0, 0);
+            bool seen;
+            if constexpr (REC) {
+                seen = rec_footprint(view, f);
+            } else {
+                seen = brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
+                                       a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f);
+                if (cache && lane == 0)
+                    fpc[view] = seen ? make_ushort4((unsigned short)f.u0, (unsigned short)f.u1,
+                                                    (unsigned short)f.v0, (unsigned short)f.v1)
+                                     : make_ushort4(1, 0, 0, 0);
+            }
             if (!seen) continue;
-            const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
-            const float *ysrc = a.sino + ((size_t)view * a.U + f.u0) * a.V + f.v0;
-            const int step_slow = 64 / nfv, step_fast = 64 - step_slow * nfv;
-            int iu = lane / nfv, iv = lane - (lane / nfv) * nfv;
-            for (int r = lane; r < nrays; r += 64) {
-                m = fmaxf(m, fabsf(ysrc[(size_t)iu * a.V + iv]));
-                iv += step_fast;
-                iu += step_slow;
-                if (iv >= nfv) { iv -= nfv; iu += 1; }
+            const int nfu = f.u1 - f.u0 + 1;
+            if (a.y_vec4) {
+                // aligned groups of four pixels of each footprint row: the groups at
+                // the row's ends may hold pixels beyond the footprint, which only
+                // raise the maximum (the scale stays valid, a little coarser)
+                const int g0 = f.v0 >> 2, ng = (f.v1 >> 2) - g0 + 1, n = nfu * ng;
+                const float4 *ysrc = (const float4 *)(a.sino + ((size_t)view * a.U + f.u0) * a.V) + g0;
+                const int rowg = a.V >> 2;
+                const int step_slow = 64 / ng, step_fast = 64 - step_slow * ng;
+                int iu = lane / ng, ig = lane - (lane / ng) * ng;
+                for (int r = lane; r < n; r += 64) {
+                    const float4 q = ysrc[iu * rowg + ig];
+                    m = fmaxf(m, fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
+                    ig += step_fast;
+                    iu += step_slow;
+                    if (ig >= ng) { ig -= ng; iu += 1; }
+                }
+            } else {
+                const int nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
+                const float *ysrc = a.sino + ((size_t)view * a.U + f.u0) * a.V + f.v0;
+                const int step_slow = 64 / nfv, step_fast = 64 - step_slow * nfv;
+                int iu = lane / nfv, iv = lane - (lane / nfv) * nfv;
+                for (int r = lane; r < nrays; r += 64) {
+                    m = fmaxf(m, fabsf(ysrc[(size_t)iu * a.V + iv]));
+                    iv += step_fast;
+                    iu += step_slow;
+                    if (iv >= nfv) { iv -= nfv; iu += 1; }
+                }
             }
         }
         for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -1904,20 +2050,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     for (int view = wv; view < a.n_views; view += NWAVES) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
         Footprint f;
-        if (cache) {
-            const ushort4 c = fpc[view];   // written by this wave in pass 1
-            f.u0 = uni((int)c.x);
-            f.u1 = uni((int)c.y);
-            f.v0 = uni((int)c.z);
-            f.v1 = uni((int)c.w);
-            if (f.u1 < f.u0) continue;
-        } else if (!brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
-                                    a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f)) {
-            continue;
+        Anchor an;
+        if constexpr (REC) {
+            if (!rec_footprint(view, f)) continue;
+            an = rec_anchor(rec + view);
+        } else {
+            if (cache) {
+                const ushort4 c = fpc[view];   // written by this wave in pass 1
+                f.u0 = uni((int)c.x);
+                f.u1 = uni((int)c.y);
+                f.v0 = uni((int)c.z);
+                f.v1 = uni((int)c.w);
+                if (f.u1 < f.u0) continue;
+            } else if (!brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
+                                        a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f)) {
+                continue;
+            }
+            an = make_anchor(vw, f, cbx, cby, cbz, !TWO_D && vt(vw, VT_PATCH) == 0.0);
         }
         // PERSP: every view of the geometry is fan/cone (else parallel)
-        brick_rays<LSY, LSZ, MODE, PERSP, TWO_D, SURF>(a, vw, view, f, lane, x0, y0, z0, ex, ey, ez, cbx, cby,
-                                                       cbz, S, yscale, acc);
+        brick_rays<LSY, LSZ, MODE, PERSP, TWO_D, SURF>(a, vw, view, f, an, lane, x0, y0, z0, ex, ey, ez, cbx,
+                                                       cby, cbz, S, yscale, acc);
     }
     __syncthreads();
     const double inv_scale = ldexp(1.0, a.yshift) / ((double)S * (double)yscale);
@@ -1953,6 +2106,37 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
         const double t = block_sum<NT>(sq, wsq);
         if (threadIdx.x == 0) a.partial[blockIdx.x] = t;
     }
+}
+
+// The record table of a whole-volume brick launch: for every (brick, view) pair,
+// one lane computes the footprint (lane form) and the anchor exactly as the brick
+// kernel would, so launches that read the table give the same bits as launches
+// that compute them.  Pairs are brick-major (all views of brick 0 first).
+template <int BX, int BY, int BZ>
+__global__ __launch_bounds__(256) void brick_rec_kernel(const double *views, int n_views, int W, int H, int D,
+                                                        int U, int V, const float *env, int nbx, int nby,
+                                                        size_t n_pairs, BrickRec *out) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_pairs) return;
+    const int b = (int)(i / (size_t)n_views), view = (int)(i - (size_t)b * n_views);
+    const int bxi = b % nbx, byi = (b / nbx) % nby, bzi = b / (nbx * nby);
+    const int x0 = bxi * BX, y0 = byi * BY, z0 = bzi * BZ;
+    const int ex = min(BX, W - x0), ey = min(BY, H - y0), ez = min(BZ, D - z0);
+    const double cbx = x0 + 0.5 * ex, cby = y0 + 0.5 * ey, cbz = z0 + 0.5 * ez;
+    const double *vw = views + (size_t)view * CT_VIEW_TABLE_STRIDE;
+    constexpr bool TWO_D = BZ == 1;
+    Footprint f;
+    BrickRec r{};
+    if (brick_footprint_lane(vw, x0, y0, z0, ex, ey, ez, U, V, TWO_D,
+                             env ? env + (size_t)view * env_size(U, V) : nullptr, f)) {
+        r.fu = (uint32_t)f.u0 | (uint32_t)f.u1 << 16;
+        r.fv = (uint32_t)f.v0 | (uint32_t)f.v1 << 16;
+        r.an = make_anchor(vw, f, cbx, cby, cbz, !TWO_D && vt(vw, VT_PATCH) == 0.0);
+    } else {
+        r.fu = 1u;   // u0 = 1 > u1 = 0: unseen
+        r.fv = 0u;
+    }
+    out[i] = r;
 }
 
 // out[a + b*tb + o*to] = in[a*sa + b + o*so]: one 32 x 32 tile of a 2D transpose
@@ -2205,18 +2389,54 @@ static void launch_brick_shape(BrickArgs &a, const LaunchGeom &g, hipStream_t s)
     a.nbz = (g.D + BZ - 1) / BZ;
     a.n_blocks = a.nbx * a.nby * a.nbz;
     const dim3 grid(a.n_blocks), block(NT);
+    const auto go = [&](auto surf, auto persp) {
+        constexpr bool SF = decltype(surf)::value, PS = decltype(persp)::value;
+        if (a.rec) hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, SF, PS, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, SF, PS, false>), grid, block, 0, s, a);
+    };
     if (a.surf.off) {
-        if (g.persp) hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, true, false>), grid, block, 0, s, a);
+        if (g.persp) go(std::true_type{}, std::true_type{});
+        else go(std::true_type{}, std::false_type{});
     } else {
-        if (g.persp) hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, false, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((brick_kernel<BX, BY, BZ, NT, MODE, false, false>), grid, block, 0, s, a);
+        if (g.persp) go(std::false_type{}, std::true_type{});
+        else go(std::false_type{}, std::false_type{});
     }
+}
+
+static void brick_shape(const LaunchGeom &g, int &bx, int &by, int &bz) {
+    bx = 16;
+    by = 16;
+    bz = g.two_d ? 1 : 32;
+}
+
+size_t brick_record_count(const LaunchGeom &g) {
+    int bx, by, bz;
+    brick_shape(g, bx, by, bz);
+    return (size_t)((g.W + bx - 1) / bx) * ((g.H + by - 1) / by) * ((g.D + bz - 1) / bz) * (size_t)g.n_views;
+}
+size_t brick_record_bytes() { return sizeof(BrickRec); }
+
+hipError_t launch_brick_records(const LaunchGeom &g, void *out, hipStream_t s) {
+    int bx, by, bz;
+    brick_shape(g, bx, by, bz);
+    const size_t n = brick_record_count(g);
+    const int nbx = (g.W + bx - 1) / bx, nby = (g.H + by - 1) / by;
+    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    if (g.two_d)
+        hipLaunchKernelGGL((brick_rec_kernel<16, 16, 1>), grid, block, 0, s, g.views, g.n_views, g.W, g.H, g.D,
+                           g.U, g.V, g.surf_env, nbx, nby, n, (BrickRec *)out);
+    else
+        hipLaunchKernelGGL((brick_rec_kernel<16, 16, 32>), grid, block, 0, s, g.views, g.n_views, g.W, g.H,
+                           g.D, g.U, g.V, g.surf_env, nbx, nby, n, (BrickRec *)out);
+    return hipGetLastError();
 }
 
 template <int MODE>
 static hipError_t launch_brick_args(const LaunchGeom &g, BrickArgs a, hipStream_t s) {
     a.views = g.views;
+    a.rec = g.brick_rec ? (const BrickRec *)g.brick_rec + g.rec_view0 : nullptr;
+    a.rec_stride = g.rec_stride;
+    a.y_vec4 = (g.V % 4 == 0 && ((uintptr_t)a.sino & 15u) == 0) ? 1 : 0;
     a.offx = g.offx; a.offy = g.offy; a.offz = g.offz;
     a.accumulate = g.accumulate;
     a.surf = Surface{g.surf_off, g.surf_per_view};
@@ -2283,7 +2503,8 @@ hipError_t launch_surface_env(const LaunchGeom &g, unsigned long long *bad, hipS
 size_t cgls_ray_blocks(const LaunchGeom &g) { return (size_t)ray_args(g).n_blocks; }
 
 size_t cgls_brick_blocks(const LaunchGeom &g) {
-    const int bx = 16, by = 16, bz = g.two_d ? 1 : 32;
+    int bx, by, bz;
+    brick_shape(g, bx, by, bz);
     return (size_t)((g.W + bx - 1) / bx) * ((g.H + by - 1) / by) * ((g.D + bz - 1) / bz);
 }
 

@@ -26,6 +26,10 @@ struct LaunchGeom {
     bool need_yf, need_zf; // some view's gathers read that copy
     bool packet;           // flat detector and every view has a packet axis (VT_PACKET >= 0):
                            // the forward takes rays in packets
+    const void *brick_rec; // brick adjoint: the handle's per-(brick, view) record table, or null
+                           // (launches whose bricks are not the whole volume's compute them)
+    int rec_stride;        // views per brick in the table
+    int rec_view0;         // table view of the launch's first view
 };
 
 hipError_t launch_fill(float *p, size_t n, float v, hipStream_t s);
@@ -41,6 +45,12 @@ hipError_t launch_backproject(const LaunchGeom &g, const float *sino, float *vol
 hipError_t launch_sirt_update(const LaunchGeom &g, const float *e, const float *cinv, float relax,
                               float *x, hipStream_t s);
 hipError_t launch_colinv(const LaunchGeom &g, float *cinv, hipStream_t s);
+// The brick adjoint's per-(brick, view) record table of a whole-volume launch:
+// brick_record_count(g) records of brick_record_bytes() each (footprint and
+// anchor of every pair), built once at geometry creation.
+size_t brick_record_count(const LaunchGeom &g);
+size_t brick_record_bytes();
+hipError_t launch_brick_records(const LaunchGeom &g, void *out, hipStream_t s);
 // Per-view footprint envelopes of a detector surface (once, at geometry creation).
 // bad (device) receives nonzero if a fan/cone surface pixel is not in front of
 // the source.
