@@ -1985,12 +1985,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     };
     if (MODE != BM_COLINV) {
         float m = 0.f;
+        // the next view's footprint words are fetched one view ahead
+        uint32_t nxu = 1u, nxv = 0u;
+        if (REC && wv < a.n_views) { nxu = rec[wv].fu; nxv = rec[wv].fv; }
         for (int view = wv; view < a.n_views; view += NWAVES) {
             const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
             Footprint f;
             bool seen;
             if constexpr (REC) {
-                seen = rec_footprint(view, f);
+                const uint32_t fu = nxu, fv = nxv;
+                if (view + NWAVES < a.n_views) { nxu = rec[view + NWAVES].fu; nxv = rec[view + NWAVES].fv; }
+                f.u0 = uni((int)(fu & 0xFFFFu));
+                f.u1 = uni((int)(fu >> 16));
+                f.v0 = uni((int)(fv & 0xFFFFu));
+                f.v1 = uni((int)(fv >> 16));
+                seen = f.u0 <= f.u1;
             } else {
                 seen = brick_footprint(vw, lane, gx0, gy0, gz0, ex, ey, ez, a.U, a.V, two_d,
                                        a.env ? a.env + (size_t)view * env_size(a.U, a.V) : nullptr, f);
@@ -2010,12 +2019,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
                 const int rowg = a.V >> 2;
                 const int step_slow = 64 / ng, step_fast = 64 - step_slow * ng;
                 int iu = lane / ng, ig = lane - (lane / ng) * ng;
-                for (int r = lane; r < n; r += 64) {
-                    const float4 q = ysrc[iu * rowg + ig];
-                    m = fmaxf(m, fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
-                    ig += step_fast;
-                    iu += step_slow;
-                    if (ig >= ng) { ig -= ng; iu += 1; }
+                // four independent loads in flight per round; a lane past the end
+                // reloads the footprint's first group, which leaves the maximum as is
+                for (int r = lane; r < n; r += 256) {
+                    float4 q[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        q[k] = ysrc[r + 64 * k < n ? iu * rowg + ig : 0];
+                        ig += step_fast;
+                        iu += step_slow;
+                        if (ig >= ng) { ig -= ng; iu += 1; }
+                    }
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        m = fmaxf(m, fmaxf(fmaxf(fabsf(q[k].x), fabsf(q[k].y)), fmaxf(fabsf(q[k].z), fabsf(q[k].w))));
                 }
             } else {
                 const int nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
