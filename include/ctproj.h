@@ -188,6 +188,27 @@ ct_status_t ct_geom_view_table(ct_geom_t g, const ct_geom_desc_t *desc, double *
 ct_status_t ct_geom_adjoint_range(ct_geom_t g, const ct_geom_desc_t *desc, int surface, double *rays_bound,
                                   int32_t *shift);
 
+/* Which adjoint a geometry takes (host only when desc is given, no device work;
+ * or from a handle g, then desc is ignored).  surface: the geometry has a
+ * parameterized detector (always the brick walk).
+ *   CT_ADJOINT_BRICK: rays binned per 16 x 16 x 32 brick and walked through it,
+ *     exact 64-bit integer sums in LDS.
+ *   CT_ADJOINT_LINE: a separable tilt series -- parallel3d, every view's rays
+ *     inside planes of one volume axis d, one detector axis running along d at
+ *     exactly one pixel per voxel (|pixel step| = voxel spacing along d) and the
+ *     other detector axis without a d component.  Then the rays of one pixel
+ *     column lie in one voxel plane and each plane is a 2D parallel projection
+ *     (the electron-tomography article's dual-axis tilt series about x and y is
+ *     such a geometry).  The adjoint forms each ray's chord through a voxel once
+ *     per 16 voxels along d, from the ray's offset to the voxel's centre (the
+ *     chord of a line through a square), and sums chord * value in float32 over
+ *     16 views, then in the brick's float32 accumulator: per voxel the error is
+ *     within about (2 * rays per voxel and 16 views + views / 16) * 2^-24 of
+ *     sum_i |a_ij y_i|.  A ray lying on a voxel plane belongs to the higher
+ *     voxel, as in the walks. */
+enum { CT_ADJOINT_BRICK = 0, CT_ADJOINT_LINE = 1 };
+ct_status_t ct_geom_adjoint_kind(ct_geom_t g, const ct_geom_desc_t *desc, int surface, int32_t *kind);
+
 /* Forward projection A: sino[view][u][v] = sum_j a_ij vol[j].
  * vol: device (D,H,W) float32; sino: device (views,U,V) float32.
  * Every ray is written, missed rays as 0 (diffct "Large Volumes and Chunked

@@ -29,7 +29,7 @@ CT_VIEW_TABLE_STRIDE = 48
 
 # every symbol declared in include/ctproj.h
 EXPORTS = ["ct_geom_validate", "ct_geom_create", "ct_geom_create_surface", "ct_geom_destroy",
-           "ct_geom_view_table", "ct_geom_adjoint_range",
+           "ct_geom_view_table", "ct_geom_adjoint_range", "ct_geom_adjoint_kind",
            "ct_project", "ct_project_ws", "ct_forward_workspace_size", "ct_backproject",
            "ct_backproject_atomic", "ct_project_region",
            "ct_backproject_region", "ct_project_host", "ct_backproject_host",
@@ -88,6 +88,7 @@ def lib():
         L.ct_geom_destroy.argtypes = [vp]
         L.ct_geom_view_table.argtypes = [vp, P(GeomDesc), P(c.c_double)]
         L.ct_geom_adjoint_range.argtypes = [vp, P(GeomDesc), c.c_int, P(c.c_double), P(c.c_int32)]
+        L.ct_geom_adjoint_kind.argtypes = [vp, P(GeomDesc), c.c_int, P(c.c_int32)]
         L.ct_project.argtypes = [vp, vp, vp, vp]
         L.ct_project_ws.argtypes = [vp, vp, vp, vp, c.c_size_t, vp]
         L.ct_forward_workspace_size.argtypes = [vp, P(GeomDesc), P(c.c_size_t)]
@@ -186,6 +187,22 @@ def ct_geom_adjoint_range(beam=None, vol_shape=None, voxel_spacing=None, det_sha
         _check(lib().ct_geom_adjoint_range(None, ctypes.byref(d), int(surface), ctypes.byref(bound),
                                            ctypes.byref(shift)))
     return float(bound.value), int(shift.value)
+
+
+ADJOINT_BRICK, ADJOINT_LINE = 0, 1
+
+
+def ct_geom_adjoint_kind(beam=None, vol_shape=None, voxel_spacing=None, det_shape=None, det_spacing=None,
+                         frames=None, surface=False, geometry=None):
+    """Which adjoint the geometry takes (ADJOINT_BRICK or ADJOINT_LINE): from a
+    handle (geometry=) or decided on the host from the description."""
+    kind = ctypes.c_int32(-1)
+    if geometry is not None:
+        _check(lib().ct_geom_adjoint_kind(geometry.handle, None, int(surface), ctypes.byref(kind)))
+    else:
+        d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
+        _check(lib().ct_geom_adjoint_kind(None, ctypes.byref(d), int(surface), ctypes.byref(kind)))
+    return int(kind.value)
 
 
 def last_error() -> str:

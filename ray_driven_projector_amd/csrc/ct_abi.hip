@@ -52,6 +52,8 @@ struct ct_geom_s {
     float *d_env = nullptr;             // per-view footprint envelopes of the surface
     void *d_brick_rec = nullptr;        // brick adjoint: per-(brick, view) footprints and anchors of
                                         // the whole volume (read-only after creation), or null
+    LineView *d_line = nullptr;         // separable tilt series: per-view line table (the adjoint
+                                        // runs the line kernel), or null
 };
 
 namespace {
@@ -108,6 +110,7 @@ LaunchGeom lg(ct_geom_t g) {
     l.brick_rec = g->d_brick_rec;
     l.rec_stride = (int)g->host.n_views;
     l.rec_view0 = 0;
+    l.line_tab = g->d_line;
     return l;
 }
 
@@ -129,6 +132,7 @@ LaunchGeom lg_region(ct_geom_t g, const ct_region_t &r, int64_t vb, int64_t ve, 
                        r.nz == g->host.D;
     if (whole) l.rec_view0 = (int)vb;
     else l.brick_rec = nullptr;
+    if (g->d_line) l.line_tab = g->d_line + vb;
     if (g->d_off && g->surf_per_view) l.surf_off = g->d_off + (size_t)vb * g->host.U * g->host.V * 3;
     if (g->d_env) l.surf_env = g->d_env + (size_t)vb * surface_env_floats((int)g->host.U, (int)g->host.V);
     return l;
@@ -409,6 +413,32 @@ ct_status_t ct_geom_adjoint_range(ct_geom_t g, const ct_geom_desc_t *desc, int s
     return CT_OK;
 }
 
+ct_status_t ct_geom_adjoint_kind(ct_geom_t g, const ct_geom_desc_t *desc, int surface, int32_t *kind) {
+    if (!kind) return fail(CT_E_NULL, "output pointer is NULL");
+    if (g) {
+        if (!valid(g)) return fail(CT_E_ARG, "invalid geometry handle");
+        *kind = g->d_line ? CT_ADJOINT_LINE : CT_ADJOINT_BRICK;
+        set_error("");
+        return CT_OK;
+    }
+    GeomHost h;
+    const char *why = "";
+    ct_status_t st = validate_desc(desc, &h, &why);
+    if (st != CT_OK) return fail(st, why);
+    std::vector<double> table;
+    std::vector<LineView> lines;
+    try {
+        table.assign((size_t)h.n_views * CT_VIEW_TABLE_STRIDE, 0.0);
+        lines.resize((size_t)h.n_views);
+    } catch (...) {
+        return fail(CT_E_NOMEM, "host allocation failed");
+    }
+    build_view_table(desc, h, table.data());
+    *kind = !surface && build_line_table(h, table.data(), lines.data()) ? CT_ADJOINT_LINE : CT_ADJOINT_BRICK;
+    set_error("");
+    return CT_OK;
+}
+
 static void free_handle(ct_geom_s *g) {
     if (g->d_views) (void)hipFree(g->d_views);
     if (g->d_total) (void)hipFree(g->d_total);
@@ -417,6 +447,7 @@ static void free_handle(ct_geom_s *g) {
     if (g->d_off) (void)hipFree(g->d_off);
     if (g->d_env) (void)hipFree(g->d_env);
     if (g->d_brick_rec) (void)hipFree(g->d_brick_rec);
+    if (g->d_line) (void)hipFree(g->d_line);
     delete g;
 }
 
@@ -514,9 +545,26 @@ static ct_status_t create_impl(const ct_geom_desc_t *desc, const double *offsets
             return fail(CT_E_FRAME, "a surface pixel is not in front of the source");
         }
     }
+    // a separable tilt series takes the line adjoint (per-view table, synchronous)
+    if (!offsets) {
+        std::vector<LineView> lines((size_t)h.n_views);
+        if (build_line_table(h, g->table.data(), lines.data())) {
+            const size_t bytes = lines.size() * sizeof(LineView);
+            if (hipMalloc((void **)&g->d_line, bytes) != hipSuccess) {
+                (void)hipGetLastError();
+                free_handle(g);
+                return fail(CT_E_NOMEM, "hipMalloc of the line table failed");
+            }
+            e = hipMemcpy(g->d_line, lines.data(), bytes, hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                free_handle(g);
+                return hip_fail(e, "hipMemcpy of the line table");
+            }
+        }
+    }
     // the brick adjoint's record table (synchronous); without it the kernel
     // computes the same footprints and anchors itself
-    if (h.D * h.H * h.W < kMaxBufferVoxels && h.U < 65536 && h.V < 65536) {
+    if (!g->d_line && h.D * h.H * h.W < kMaxBufferVoxels && h.U < 65536 && h.V < 65536) {
         const LaunchGeom l = lg(g);
         const size_t bytes = brick_record_count(l) * brick_record_bytes();
         if (bytes <= kMaxBrickRecordBytes) {

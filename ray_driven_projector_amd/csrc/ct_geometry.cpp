@@ -290,6 +290,79 @@ void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *tab
     choose_layouts(g, table);
 }
 
+bool build_line_table(const GeomHost &g, const double *table, LineView *out) {
+    if (g.is2d || g.beam != CT_PARALLEL3D) return false;
+    // one view's pixels are read through a buffer of 32-bit byte offsets, where a
+    // negative offset (a pixel before the detector) must fall outside the view
+    if ((double)g.U * (double)g.V * 4.0 >= 2147483648.0) return false;
+    const double sp[3] = {g.sx, g.sy, g.sz};
+    const int ext[3] = {kLineBX, kLineBY, kLineBZ};
+    for (int64_t k = 0; k < g.n_views; ++k) {
+        const double *t = table + (size_t)k * CT_VIEW_TABLE_STRIDE;
+        if (t[VT_PACKET] < 0.0) return false;
+        LineView &L = out[k];
+        std::memset(&L, 0, sizeof L);
+        L.P = t[VT_PACKET] == 0.0 ? 0 : 1;
+        const double *OP = t + (L.P == 0 ? VT_OU : VT_OV), *OQ = t + (L.P == 0 ? VT_OV : VT_OU);
+        const double *O = t + VT_O00, *D = t + VT_D00;
+        int d = -1;
+        for (int i = 0; i < 3; ++i)
+            if (OP[i] != 0.0) d = i;
+        // one voxel plane per pixel column, the other detector axis in the plane
+        if (d < 0 || std::fabs(OP[d]) != 1.0 || OQ[d] != 0.0) return false;
+        L.d = d;
+        L.g = OP[d] > 0.0 ? 1 : -1;
+        const double kc = std::floor(O[d]);
+        if (std::fabs(kc) > 1e9) return false;
+        L.kc = (int)kc;
+        const int a = d == 0 ? 1 : 0, b = d == 2 ? 1 : 2;
+        // in-plane direction in voxel coordinates; a component below 2^-40 of the
+        // largest counts as zero, as in the walks
+        const double dm = std::max(std::fabs(D[0]), std::max(std::fabs(D[1]), std::fabs(D[2]))) * 0x1p-40;
+        double ea = std::fabs(D[a]) < dm ? 0.0 : D[a], eb = std::fabs(D[b]) < dm ? 0.0 : D[b];
+        const double len = std::sqrt(ea * ea + eb * eb);
+        if (!(len > 0.0)) return false;
+        ea /= len;
+        eb /= len;
+        const double na = -eb, nb = ea;
+        // physical length per voxel-coordinate length along the ray
+        const double kap = std::sqrt((D[a] * sp[a]) * (D[a] * sp[a]) + (D[b] * sp[b]) * (D[b] * sp[b])) /
+                           std::sqrt(D[a] * D[a] + D[b] * D[b]);
+        L.na = na;
+        L.nb = nb;
+        L.naf = (float)na;
+        L.nbf = (float)nb;
+        L.E0 = na * O[a] + nb * O[b];
+        L.dq = na * OQ[a] + nb * OQ[b];
+        if (!(std::fabs(L.dq) > 1e-9)) return false;
+        L.inv_dq = 1.0 / L.dq;
+        L.inv_dqf = (float)L.inv_dq;
+        const double A = std::fabs(ea), B = std::fabs(eb);
+        L.H = (float)(0.5 * (A + B));
+        L.Lmax = (float)(kap / std::max(A, B));
+        if (A == 0.0 || B == 0.0) {
+            L.aligned = A == 0.0 ? 1 : 2;
+            const int c = A == 0.0 ? a : b;
+            L.X0 = O[c];
+            L.Xq = OQ[c];
+            if (L.Xq == 0.0) return false;
+        } else {
+            L.R = (float)(kap / (A * B));
+        }
+        // rows one brick stages for this view: its cross-section's shadow along n
+        const double w = 0.5 * (std::fabs(na) * ext[a] + std::fabs(nb) * ext[b]);
+        if (2.0 * (0.5 * (A + B) + w) / std::fabs(L.dq) + 4.0 > (double)kLineRows) return false;
+    }
+    // each view's distance to the next view of its family (0: the last one)
+    int last[3] = {-1, -1, -1};
+    for (int64_t k = 0; k < g.n_views; ++k) {
+        const int d = out[k].d;
+        if (last[d] >= 0) out[last[d]].next = (int)(k - last[d]);
+        last[d] = (int)k;
+    }
+    return true;
+}
+
 // Range of the brick adjoint's 64-bit accumulator.  Each (ray, voxel) pair adds
 // at most one voxel chord times the largest ray value: below 2^46 in the
 // accumulator's units (both factors are under 2^23).  The rays of one view that

@@ -73,6 +73,37 @@ struct GeomHost {
     double du = 1, dv = 1;
 };
 
+// Separable parallel views (the line adjoint).  A parallel view whose rays never
+// cross the planes of one volume axis d (direction component 0), whose pixel
+// step along one detector axis P runs along d alone at one voxel per pixel
+// (|O_P[d]| = 1), and whose other detector axis Q has no d component: the rays
+// of pixel column p lie in the voxel plane kc + g p of axis d, and inside that
+// plane the view is a 2D parallel projection of one slice.  Voxel coordinates;
+// a < b are the two axes other than d, e the unit in-plane ray direction and
+// n = (-e_b, e_a) its normal.  The ray of row q sits at signed offset
+// E0 + q dq along n; it meets cell (ia, ib) iff its offset from the cell centre,
+// delta, satisfies |delta| < H, along the chord clamp((H - |delta|) R, 0, Lmax)
+// (in physical length units), the cell's cross-section being a unit square.
+// Rays parallel to an axis (aligned) meet exactly the cell whose index is the
+// floor of their constant coordinate X0 + q Xq.
+struct LineView {
+    double E0, dq;       // row offsets along n: E0 + q dq (dq != 0)
+    double X0, Xq;       // aligned views: constant in-plane coordinate of row q
+    double na, nb;       // unit normal (float64: per-brick reference offsets)
+    double inv_dq;       // 1 / dq
+    float naf, nbf;      // the unit normal in float32 (per-cell offsets within a brick)
+    float H, R, Lmax;    // chord trapezoid (R unused for aligned views)
+    float inv_dqf;       // 1 / dq in float32
+    int d, P, g, kc;     // untraversed axis; detector axis along it (0 u, 1 v); column p lies in plane kc + g p
+    int aligned;         // 0 oblique; 1: e_a = 0 (constant a coordinate); 2: e_b = 0 (constant b)
+    int next;            // views to the next view with the same d (0: none)
+    int pad[2];
+};
+static_assert(sizeof(LineView) == 112, "line table layout");
+// The line adjoint's bricks (x, y, z) and the rows of one view it stages per brick.
+constexpr int kLineBX = 16, kLineBY = 16, kLineBZ = 32;
+constexpr int kLineRows = 64;
+
 // Validation and table precompute (host only, no HIP calls): ct_geometry.cpp
 ct_status_t validate_desc(const ct_geom_desc_t *desc, GeomHost *out, const char **why);
 void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *table);
@@ -81,6 +112,9 @@ void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *tab
 // over all views, and the right shift its terms need so the 64-bit sums stay
 // below 2^62 (ct_geometry.cpp).
 double adjoint_rays_bound(const GeomHost &g, const double *table, bool surface);
+// The line table (one LineView per view); false when some view is not separable
+// in the sense above or a brick would need more than kLineRows rows of a view.
+bool build_line_table(const GeomHost &g, const double *table, LineView *out);
 int adjoint_term_shift(double rays_bound);
 
 void set_error(const char *msg);

@@ -72,6 +72,11 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 __device__ __forceinline__ float uni(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
+__device__ __forceinline__ double uni(double x) {
+    const long long b = __builtin_bit_cast(long long, x);
+    const int lo = __builtin_amdgcn_readfirstlane((int)(b & 0xFFFFFFFFll)), hi = __builtin_amdgcn_readfirstlane((int)(b >> 32));
+    return __builtin_bit_cast(double, (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
 // The opposite: hold a value in a vector register.  A loop that selects among
 // wave-uniform operands with a per-lane mask needs them in vector registers
 // (one scalar operand per instruction); held there, the copies stay out of the loop.
@@ -1926,6 +1931,48 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     }
 }
 
+// Write-out of one brick: each voxel's adjoint value val(lx, ly, lz) (local
+// indices) goes once to the volume through the mode's epilogue: A^T (written or
+// added), the SIRT update x += relax C A^T e (optionally masked and clamped), the
+// CGLS adjoint with its fused vector updates and the brick's sum of squares, or
+// the column weights 1 / (A^T 1).
+template <int BX, int BY, int BZ, int NT, int MODE, class F>
+__device__ __forceinline__ void brick_writeout(const BrickArgs &a, int x0, int y0, int z0, int ex, int ey,
+                                               int ez, F &&val_of) {
+    const float alpha = (MODE == BM_CGLS && a.x_upd) ? (float)a.state[CS_ALPHA] : 0.f;
+    double sq = 0.0;
+    for (int i = threadIdx.x; i < BX * BY * BZ; i += NT) {
+        const int lx = i % BX, ly = (i / BX) % BY, lz = i / (BX * BY);
+        if (lx < ex && ly < ey && lz < ez) {
+            const size_t g = ((size_t)(z0 + lz) * a.H + (y0 + ly)) * a.W + (x0 + lx);
+            const float val = val_of(lx, ly, lz);
+            if (MODE == BM_BACKPROJECT) {
+                a.vol[g] = a.accumulate ? a.vol[g] + val : val;
+            } else if (MODE == BM_SIRT_UPDATE) {
+                if (!a.mask || a.mask[g]) {
+                    float v = fmaf(a.relax * a.cinv[g], val, a.vol[g]);
+                    if (a.bounded) v = fminf(fmaxf(v, a.lo), a.hi);
+                    a.vol[g] = v;
+                }
+            } else if (MODE == BM_CGLS) {
+                a.vol[g] = val;
+                sq += (double)val * val;
+                if (a.p_copy) a.p_copy[g] = val;
+                if (a.x_upd) a.x_upd[g] = fmaf(alpha, a.p_old[g], a.x_upd[g]);
+            } else {
+                const float r = val > 0.f ? 1.0f / val : 0.f;
+                a.vol[g] = isfinite(r) ? r : 0.f;
+            }
+        }
+    }
+    if (MODE == BM_CGLS) {
+        // fixed-order block sum (float64), one partial per brick
+        __shared__ double wsq[NT / 64];
+        const double t = block_sum<NT>(sq, wsq);
+        if (threadIdx.x == 0) a.partial[blockIdx.x] = t;
+    }
+}
+
 // Two 512-thread workgroups (or four of 256, one of 1024) share a CU through
 // their LDS, i.e. 4 waves per SIMD; the register budget is held to that.
 // SURF: parameterized detector surface (per-pixel rays from the offsets table).
@@ -2091,38 +2138,220 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
     }
     __syncthreads();
     const double inv_scale = ldexp(1.0, a.yshift) / ((double)S * (double)yscale);
-    const float alpha = (MODE == BM_CGLS && a.x_upd) ? (float)a.state[CS_ALPHA] : 0.f;
-    double sq = 0.0;
-    for (int i = threadIdx.x; i < BX * BY * BZ; i += NT) {
-        const int lx = i % BX, ly = (i / BX) % BY, lz = i / (BX * BY);
-        if (lx < ex && ly < ey && lz < ez) {
-            const size_t g = ((size_t)(z0 + lz) * a.H + (y0 + ly)) * a.W + (x0 + lx);
-            const float val = (float)((double)(long long)acc[lz * LSZ + ly * LSY + lx] * inv_scale);
-            if (MODE == BM_BACKPROJECT) {
-                a.vol[g] = a.accumulate ? a.vol[g] + val : val;
-            } else if (MODE == BM_SIRT_UPDATE) {
-                if (!a.mask || a.mask[g]) {
-                    float v = fmaf(a.relax * a.cinv[g], val, a.vol[g]);
-                    if (a.bounded) v = fminf(fmaxf(v, a.lo), a.hi);
-                    a.vol[g] = v;
-                }
-            } else if (MODE == BM_CGLS) {
-                a.vol[g] = val;
-                sq += (double)val * val;
-                if (a.p_copy) a.p_copy[g] = val;
-                if (a.x_upd) a.x_upd[g] = fmaf(alpha, a.p_old[g], a.x_upd[g]);
-            } else {
-                const float r = val > 0.f ? 1.0f / val : 0.f;
-                a.vol[g] = isfinite(r) ? r : 0.f;
+    brick_writeout<BX, BY, BZ, NT, MODE>(a, x0, y0, z0, ex, ey, ez, [&](int lx, int ly, int lz) {
+        return (float)((double)(long long)acc[lz * LSZ + ly * LSY + lx] * inv_scale);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// line adjoint: separable parallel views (LineView)
+// ---------------------------------------------------------------------------
+//
+// Every view of the geometry lies in planes of one volume axis d (a tilt series
+// about a volume axis with one detector column per voxel plane).  One 512-thread
+// workgroup owns a brick of 16 x 16 x 32 voxels.  Views are taken family by
+// family (d = x, y, z); within a family every thread owns a segment of 16 voxels
+// along d at one in-plane cell.  Per view the workgroup stages in LDS the rows of
+// the view that can meet its brick, for the 16 (32 for d = z) pixel columns whose
+// planes hold its voxels; each thread then finds the rows meeting its cell (one
+// or two), forms each ray's chord through the cell once, from the ray's offset to
+// the cell centre (the trapezoid of a unit square), and adds chord * value to its
+// 16 voxels.  No ray is walked and nothing is added atomically: sums run in
+// float32 registers over 16 views, then into the brick's float32 accumulator in
+// LDS (each voxel belongs to one segment per family), which is written once.
+constexpr int kLinePitch = 36;   // floats per staged row: up to 32 pixel columns, padded
+typedef const __attribute__((address_space(4))) LineView *ConstLinePtr;
+// a view's entry, field by field (scalar loads)
+__device__ __forceinline__ LineView load_line(ConstLinePtr p) {
+    LineView L;
+    L.E0 = p->E0; L.dq = p->dq; L.X0 = p->X0; L.Xq = p->Xq; L.na = p->na; L.nb = p->nb;
+    L.inv_dq = p->inv_dq; L.naf = p->naf; L.nbf = p->nbf; L.H = p->H; L.R = p->R; L.Lmax = p->Lmax;
+    L.inv_dqf = p->inv_dqf; L.d = p->d; L.P = p->P; L.g = p->g; L.kc = p->kc; L.aligned = p->aligned;
+    L.next = p->next;
+    return L;
+}
+
+// One family of views (untraversed axis D) of one brick: sums into acc.
+template <int MODE, int D, int LSY, int LSZ>
+__device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv, float *acc,
+                                            float (&stage)[2][kLineRows * kLinePitch], int &buf, int x0,
+                                            int y0, int z0, int ex, int ey, int ez) {
+    constexpr int NT = 512;
+    constexpr int AX = D == 0 ? 1 : 0, BXS = D == 2 ? 1 : 2;   // in-plane axes a < b
+    constexpr int W = D == 2 ? 32 : 16;                        // staged pixel columns
+    constexpr int NSLOT = W * kLineRows / NT;                  // staged values per thread
+    const int tid = threadIdx.x;
+    // this thread's segment: cell (la, lb), voxels s0 .. s0 + 15 along D
+    const int la = tid & 15, lb = D == 2 ? (tid >> 4) & 15 : tid >> 4, s0 = D == 2 ? (tid >> 8) * 16 : 0;
+    const int gd = D == 0 ? x0 + a.offx : (D == 1 ? y0 + a.offy : z0 + a.offz);   // on the lattice
+    const int ga = AX == 0 ? x0 + a.offx : y0 + a.offy, gb = BXS == 1 ? y0 + a.offy : z0 + a.offz;
+    const int ea = AX == 0 ? ex : ey, eb = BXS == 1 ? ey : ez, ed = D == 0 ? ex : (D == 1 ? ey : ez);
+    const bool live = la < ea && lb < eb && s0 < ed;
+    // the cell centre relative to the cross-section's centre (exact in float64)
+    const double ca = la + 0.5 - 0.5 * ea, cb = lb + 0.5 - 0.5 * eb;
+    int view = 0;
+    while (view < a.n_views && lv[view].d != D) ++view;
+    if (view >= a.n_views) return;
+    float part[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) part[j] = 0.f;
+    int batch = 0;
+    // the thread's slots of the staged block: slot m holds row i0 + m di, column
+    // j0 + m dj; along its slots the pixel's v stays fixed and u steps
+    const auto slot0 = [&](int P, int &i0, int &j0, int &di, int &dj) {
+        if (P == 0) {   // p = u, q = v: threads along the rows (memory order)
+            i0 = tid & 63;
+            j0 = tid >> 6;
+            di = 0;
+            dj = NT / 64;
+        } else {        // p = v, q = u: threads along the columns (memory order)
+            j0 = tid & (W - 1);
+            i0 = tid / W;
+            di = NT / W;
+            dj = 0;
+        }
+    };
+    for (;;) {
+        const LineView L = load_line(lv + view);
+        // rows of the view that can meet the brick, referred to the row nearest the
+        // centre of the brick's cross-section, so the per-cell arithmetic meets
+        // small numbers
+        const double Eref = L.E0 - L.na * (ga + 0.5 * ea) - L.nb * (gb + 0.5 * eb);
+        const double qr = rint(-Eref * L.inv_dq);
+        const int qref = uni((int)qr);
+        const double C0d = uni(fma(qr, L.dq, Eref));
+        const float w = 0.5f * (fabsf(L.naf) * (float)ea + fabsf(L.nbf) * (float)eb);
+        const float C0 = (float)C0d;
+        const float r1 = (-L.H - w - C0) * L.inv_dqf, r2 = (L.H + w - C0) * L.inv_dqf;
+        const int rlo = uni((int)floorf(fminf(r1, r2)) - 1);
+        const int nrows = uni(min(kLineRows, (int)ceilf(fmaxf(r1, r2)) + 2 - rlo));
+        // stage rows q = qref + rlo + i and pixel columns p = g (gd + j - kc) (zero off
+        // the detector and past the brick), loads along the sinogram's contiguous v
+        float *st = stage[buf];
+        {
+            int i0, j0, di, dj;
+            slot0(L.P, i0, j0, di, dj);
+            const int q0 = qref + rlo + i0, p0 = L.g * (gd + j0 - L.kc);
+            const int u0 = L.P == 0 ? p0 : q0, vv = L.P == 0 ? q0 : p0;
+            const int du = L.P == 0 ? L.g * dj : di;
+            const bool vok = vv >= 0 && vv < a.V;
+            // the view's pixels as one buffer: offsets of pixels off the detector in u
+            // fall outside it (a negative one wraps high) and read 0
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(a.sino + (size_t)view * a.U * a.V, (uint32_t)(a.U * a.V) * 4u);
+            const uint32_t off0 = (uint32_t)(u0 * a.V + vv) * 4u, dstep = (uint32_t)(du * a.V) * 4u;
+            float ld[NSLOT];
+#pragma unroll
+            for (int m = 0; m < NSLOT; ++m) {
+                const int i = i0 + m * di, j = j0 + m * dj, u = u0 + m * du;
+                ld[m] = 0.f;
+                if (i < nrows && j < ed && vok && (MODE != BM_COLINV || (u >= 0 && u < a.U)))
+                    ld[m] = MODE == BM_COLINV ? 1.f : load_f32(rs, off0 + m * dstep);
+            }
+#pragma unroll
+            for (int m = 0; m < NSLOT; ++m) {
+                const int i = i0 + m * di, j = j0 + m * dj;
+                if (i < nrows) st[i * kLinePitch + j] = ld[m];
             }
         }
+        __syncthreads();
+        // the rows meeting this cell, each with its chord, summed into the segment
+        if (live) {
+            // offset of row qref + r from this cell's centre: C + r dq, formed in
+            // float64 for the first candidate (offsets of tens of voxels cancel to
+            // under one, and near-axis rays have chord ramps as steep as 1 / sin of
+            // their angle to the axis), then stepped by dq
+            const double Cd = C0d - L.na * ca - L.nb * cb;
+            const float C = (float)Cd;
+            // rows strictly inside the window |offset| < H meet the cell; oblique rays
+            // at its edge have zero chord, aligned ones there are decided below
+            const float t1 = (-L.H - C) * L.inv_dqf, t2 = (L.H - C) * L.inv_dqf;
+            const int edge = L.aligned ? 0 : 1;
+            const int rA = max((int)floorf(fminf(t1, t2)) + edge, rlo);
+            const int rB = min((int)ceilf(fmaxf(t1, t2)) - edge, rlo + nrows - 1);
+            float dl, step;
+            if (L.aligned) {
+                // the rays' constant coordinate relative to this cell (a ray on a cell
+                // boundary belongs to the higher cell)
+                dl = (float)(fma(qr + rA, L.Xq, L.X0) - (L.aligned == 1 ? ga + la : gb + lb));
+                step = (float)L.Xq;
+            } else {
+                dl = (float)fma((double)rA, L.dq, Cd);
+                step = (float)L.dq;
+            }
+            const float *row = st + (rA - rlo) * kLinePitch + s0;
+            for (int r = rA; r <= rB; ++r, row += kLinePitch) {
+                const float Lc = L.aligned ? ((dl >= 0.f && dl < 1.f) ? L.Lmax : 0.f)
+                                           : fminf(fmaxf((L.H - fabsf(dl)) * L.R, 0.f), L.Lmax);
+                dl += step;
+                if (Lc != 0.f) {
+                    const float4 *row4 = (const float4 *)row;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float4 q = row4[k];
+                        part[4 * k + 0] = fmaf(Lc, q.x, part[4 * k + 0]);
+                        part[4 * k + 1] = fmaf(Lc, q.y, part[4 * k + 1]);
+                        part[4 * k + 2] = fmaf(Lc, q.z, part[4 * k + 2]);
+                        part[4 * k + 3] = fmaf(Lc, q.w, part[4 * k + 3]);
+                    }
+                }
+            }
+        }
+        buf ^= 1;
+        const bool last = L.next == 0 || view + L.next >= a.n_views;
+        if (++batch == 16 || last) {
+            // into the brick's accumulator: each voxel belongs to one segment here
+            if (live) {
+                constexpr int STEP = D == 0 ? 1 : (D == 1 ? LSY : LSZ);
+                const int base = D == 0 ? lb * LSZ + la * LSY : (D == 1 ? lb * LSZ + la : lb * LSY + la);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    acc[base + (s0 + j) * STEP] += part[j];
+                    part[j] = 0.f;
+                }
+            }
+            batch = 0;
+        }
+        if (last) break;
+        view += L.next;
     }
-    if (MODE == BM_CGLS) {
-        // fixed-order block sum (float64), one partial per brick
-        __shared__ double wsq[NWAVES];
-        const double t = block_sum<NT>(sq, wsq);
-        if (threadIdx.x == 0) a.partial[blockIdx.x] = t;
+    __syncthreads();   // the next family's segments own other voxels
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void line_kernel(BrickArgs a, const LineView *lines) {
+    constexpr int BX = kLineBX, BY = kLineBY, BZ = kLineBZ, NT = 512;
+    constexpr int LSY = BX + 1, LSZ = LSY * BY + 1, LN = LSZ * BZ;
+    __shared__ float acc[LN];
+    __shared__ float stage[2][kLineRows * kLinePitch];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < LN; i += NT) acc[i] = 0.f;
+
+    const int blk = xcd_remap(blockIdx.x, a.n_blocks);
+    const int bxi = blk % a.nbx;
+    const int byi = (blk / a.nbx) % a.nby;
+    const int bzi = blk / (a.nbx * a.nby);
+    const int x0 = bxi * BX, y0 = byi * BY, z0 = bzi * BZ;   // within the volume buffer
+    const int ex = min(BX, a.W - x0), ey = min(BY, a.H - y0), ez = min(BZ, a.D - z0);
+    if (MODE == BM_SIRT_UPDATE && a.mask) {
+        // a brick with no voxel to update does no work at all
+        int any = 0;
+        for (int i = tid; i < BX * BY * BZ; i += NT) {
+            const int lx = i % BX, ly = (i / BX) % BY, lz = i / (BX * BY);
+            if (lx < ex && ly < ey && lz < ez)
+                any |= a.mask[((size_t)(z0 + lz) * a.H + (y0 + ly)) * a.W + (x0 + lx)] != 0;
+        }
+        if (!__syncthreads_or(any)) return;
     }
+    const ConstLinePtr lv = (ConstLinePtr)lines;
+    int buf = 0;
+    line_family<MODE, 0, LSY, LSZ>(a, lv, acc, stage, buf, x0, y0, z0, ex, ey, ez);
+    line_family<MODE, 1, LSY, LSZ>(a, lv, acc, stage, buf, x0, y0, z0, ex, ey, ez);
+    line_family<MODE, 2, LSY, LSZ>(a, lv, acc, stage, buf, x0, y0, z0, ex, ey, ez);
+    __syncthreads();
+    brick_writeout<BX, BY, BZ, NT, MODE>(a, x0, y0, z0, ex, ey, ez, [&](int lx, int ly, int lz) {
+        return acc[lz * LSZ + ly * LSY + lx];
+    });
 }
 
 // The record table of a whole-volume brick launch: for every (brick, view) pair,
@@ -2461,9 +2690,20 @@ static hipError_t launch_brick_args(const LaunchGeom &g, BrickArgs a, hipStream_
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
     a.yshift = g.yshift;
-    // 3D: bricks of 16 x 16 x 32 voxels, 512 threads; 2D: 16 x 16, 256 threads
-    if (g.two_d) launch_brick_shape<16, 16, 1, 256, MODE>(a, g, s);
-    else launch_brick_shape<16, 16, 32, 512, MODE>(a, g, s);
+    // 3D: bricks of 16 x 16 x 32 voxels, 512 threads; 2D: 16 x 16, 256 threads;
+    // separable tilt series: the line adjoint on the same bricks
+    if (g.line_tab && !g.two_d) {
+        a.nbx = (g.W + kLineBX - 1) / kLineBX;
+        a.nby = (g.H + kLineBY - 1) / kLineBY;
+        a.nbz = (g.D + kLineBZ - 1) / kLineBZ;
+        a.n_blocks = a.nbx * a.nby * a.nbz;
+        hipLaunchKernelGGL((line_kernel<MODE>), dim3(a.n_blocks), dim3(512), 0, s, a,
+                           (const LineView *)g.line_tab);
+    } else if (g.two_d) {
+        launch_brick_shape<16, 16, 1, 256, MODE>(a, g, s);
+    } else {
+        launch_brick_shape<16, 16, 32, 512, MODE>(a, g, s);
+    }
     return hipGetLastError();
 }
 

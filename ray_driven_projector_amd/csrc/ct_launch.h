@@ -30,6 +30,8 @@ struct LaunchGeom {
                            // (launches whose bricks are not the whole volume's compute them)
     int rec_stride;        // views per brick in the table
     int rec_view0;         // table view of the launch's first view
+    const void *line_tab;  // separable tilt series: the line table (LineView) from the launch's
+                           // first view; the adjoint then runs the line kernel (else null)
 };
 
 hipError_t launch_fill(float *p, size_t n, float v, hipStream_t s);

@@ -392,3 +392,63 @@ def test_helical_view_weights_reject_what_the_oracle_rejects(L):
         with pytest.raises(rdp.CtError) as e:
             rdp.ct_helical_view_weights(*_args(w), t)
         assert e.value.status == code, (e.value, code)
+
+
+def _tilt(n, first, step, axis):
+    """Parallel rays tilted about one volume axis; e_v (or e_u for axis x) along it."""
+    t = np.radians(first + step * np.arange(n))
+    c, s, z, o = np.cos(t), np.sin(t), np.zeros(n), np.ones(n)
+    if axis == "x":
+        ray, eu, ev = np.stack([z, -s, c], 1), np.stack([o, z, z], 1), np.stack([z, c, s], 1)
+    elif axis == "y":
+        ray, eu, ev = np.stack([s, z, c], 1), np.stack([c, z, -s], 1), np.stack([z, o, z], 1)
+    else:
+        ray, eu, ev = np.stack([c, s, z], 1), np.stack([-s, c, z], 1), np.stack([z, z, o], 1)
+    return np.concatenate([ray, np.zeros_like(ray), eu, ev], 1)
+
+
+def _kind(fr, vol=(40, 36, 44), sp=(1.0, 1.0, 1.0), det=(60, 56), dsp=(1.0, 1.0), beam=W.BEAM_PARALLEL3D,
+          surface=False):
+    return rdp.ct_geom_adjoint_kind(beam, vol, sp, det, dsp, fr, surface=surface)
+
+
+def test_line_adjoint_eligibility(L):
+    """Separable tilt series take the line adjoint; anything that breaks one
+    voxel plane per pixel column takes the brick walk (decided on the host)."""
+    line, brick = rdp.ADJOINT_LINE, rdp.ADJOINT_BRICK
+    wl4 = W.make_workload(4)
+    assert rdp.ct_geom_adjoint_kind(wl4.beam, wl4.vol_shape, wl4.voxel_spacing, wl4.det_shape,
+                                    wl4.det_spacing, wl4.frames) == line
+    for c in (1, 2, 3, 5):
+        wl = W.make_workload(c)
+        assert rdp.ct_geom_adjoint_kind(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape,
+                                        wl.det_spacing, wl.frames) == brick, c
+    for axis in "xyz":
+        assert _kind(_tilt(9, -60.0, 15.0, axis)) == line, axis
+    both = np.concatenate([_tilt(5, -40.0, 20.0, "x"), _tilt(5, -40.0, 20.0, "z")])
+    assert _kind(both) == line                                   # two families, one geometry
+    assert _kind(_tilt(9, -60.0, 15.0, "x"), surface=True) == brick
+    assert _kind(_tilt(9, -60.0, 15.0, "x"), dsp=(0.8, 1.0)) == brick      # 1.25 columns per voxel plane
+    assert _kind(_tilt(9, -60.0, 15.0, "x"), sp=(1.0, 1.0, 2.0)) == brick  # half a column per plane
+    # pixel spacing equal to the voxel spacing along the untraversed axis is enough
+    assert _kind(_tilt(9, -60.0, 15.0, "x"), sp=(1.5, 0.7, 2.0), dsp=(2.0, 1.0)) == line
+    # a ray direction leaving the plane, or a row axis with a component along it
+    fr = _tilt(9, -60.0, 15.0, "x")
+    tilted = fr.copy()
+    tilted[:, 0] = 1e-3
+    tilted[:, 0:3] /= np.linalg.norm(tilted[:, 0:3], axis=1)[:, None]
+    assert _kind(tilted) == brick
+    # the detector axes turned by 2 degrees about the ray: neither runs along x alone
+    skew = fr.copy()
+    b = math.radians(2.0)
+    skew[:, 6:9] = math.cos(b) * fr[:, 6:9] + math.sin(b) * fr[:, 9:12]
+    skew[:, 9:12] = -math.sin(b) * fr[:, 6:9] + math.cos(b) * fr[:, 9:12]
+    assert _kind(skew) == brick
+    # a detector far finer than the voxels across the rays would need more staged rows
+    assert _kind(_tilt(9, -60.0, 15.0, "y"), sp=(1.0, 0.25, 1.0), dsp=(1.0, 0.25)) in (line, brick)
+    assert _kind(_tilt(9, -60.0, 15.0, "x"), vol=(40, 36, 44), sp=(1.0, 1.0, 1.0), det=(60, 56),
+                 dsp=(1.0, 0.2)) == brick
+    # 2D beams and fan/cone never do
+    fan = W.make_workload(2)
+    assert rdp.ct_geom_adjoint_kind(fan.beam, fan.vol_shape, fan.voxel_spacing, fan.det_shape, fan.det_spacing,
+                                    fan.frames) == brick
