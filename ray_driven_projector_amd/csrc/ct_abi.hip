@@ -54,6 +54,7 @@ struct ct_geom_s {
                                         // the whole volume (read-only after creation), or null
     LineView *d_line = nullptr;         // separable tilt series: per-view line table (the adjoint
                                         // runs the line kernel), or null
+    int line_shape = -1;                // its brick shape (kLineShapes)
 };
 
 namespace {
@@ -111,6 +112,7 @@ LaunchGeom lg(ct_geom_t g) {
     l.rec_stride = (int)g->host.n_views;
     l.rec_view0 = 0;
     l.line_tab = g->d_line;
+    l.line_shape = g->line_shape;
     return l;
 }
 
@@ -434,7 +436,7 @@ ct_status_t ct_geom_adjoint_kind(ct_geom_t g, const ct_geom_desc_t *desc, int su
         return fail(CT_E_NOMEM, "host allocation failed");
     }
     build_view_table(desc, h, table.data());
-    *kind = !surface && build_line_table(h, table.data(), lines.data()) ? CT_ADJOINT_LINE : CT_ADJOINT_BRICK;
+    *kind = !surface && build_line_table(h, table.data(), lines.data()) >= 0 ? CT_ADJOINT_LINE : CT_ADJOINT_BRICK;
     set_error("");
     return CT_OK;
 }
@@ -548,7 +550,8 @@ static ct_status_t create_impl(const ct_geom_desc_t *desc, const double *offsets
     // a separable tilt series takes the line adjoint (per-view table, synchronous)
     if (!offsets) {
         std::vector<LineView> lines((size_t)h.n_views);
-        if (build_line_table(h, g->table.data(), lines.data())) {
+        g->line_shape = build_line_table(h, g->table.data(), lines.data());
+        if (g->line_shape >= 0) {
             const size_t bytes = lines.size() * sizeof(LineView);
             if (hipMalloc((void **)&g->d_line, bytes) != hipSuccess) {
                 (void)hipGetLastError();

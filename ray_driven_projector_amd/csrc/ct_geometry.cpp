@@ -290,16 +290,16 @@ void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *tab
     choose_layouts(g, table);
 }
 
-bool build_line_table(const GeomHost &g, const double *table, LineView *out) {
-    if (g.is2d || g.beam != CT_PARALLEL3D) return false;
+int build_line_table(const GeomHost &g, const double *table, LineView *out) {
+    if (g.is2d || g.beam != CT_PARALLEL3D) return -1;
     // one view's pixels are read through a buffer of 32-bit byte offsets, where a
     // negative offset (a pixel before the detector) must fall outside the view
-    if ((double)g.U * (double)g.V * 4.0 >= 2147483648.0) return false;
+    if ((double)g.U * (double)g.V * 4.0 >= 2147483648.0) return -1;
     const double sp[3] = {g.sx, g.sy, g.sz};
-    const int ext[3] = {kLineBX, kLineBY, kLineBZ};
+    bool fits[2] = {true, true};   // every view's rows fit each shape's stage
     for (int64_t k = 0; k < g.n_views; ++k) {
         const double *t = table + (size_t)k * CT_VIEW_TABLE_STRIDE;
-        if (t[VT_PACKET] < 0.0) return false;
+        if (t[VT_PACKET] < 0.0) return -1;
         LineView &L = out[k];
         std::memset(&L, 0, sizeof L);
         L.P = t[VT_PACKET] == 0.0 ? 0 : 1;
@@ -309,11 +309,11 @@ bool build_line_table(const GeomHost &g, const double *table, LineView *out) {
         for (int i = 0; i < 3; ++i)
             if (OP[i] != 0.0) d = i;
         // one voxel plane per pixel column, the other detector axis in the plane
-        if (d < 0 || std::fabs(OP[d]) != 1.0 || OQ[d] != 0.0) return false;
+        if (d < 0 || std::fabs(OP[d]) != 1.0 || OQ[d] != 0.0) return -1;
         L.d = d;
         L.g = OP[d] > 0.0 ? 1 : -1;
         const double kc = std::floor(O[d]);
-        if (std::fabs(kc) > 1e9) return false;
+        if (std::fabs(kc) > 1e9) return -1;
         L.kc = (int)kc;
         const int a = d == 0 ? 1 : 0, b = d == 2 ? 1 : 2;
         // in-plane direction in voxel coordinates; a component below 2^-40 of the
@@ -321,7 +321,7 @@ bool build_line_table(const GeomHost &g, const double *table, LineView *out) {
         const double dm = std::max(std::fabs(D[0]), std::max(std::fabs(D[1]), std::fabs(D[2]))) * 0x1p-40;
         double ea = std::fabs(D[a]) < dm ? 0.0 : D[a], eb = std::fabs(D[b]) < dm ? 0.0 : D[b];
         const double len = std::sqrt(ea * ea + eb * eb);
-        if (!(len > 0.0)) return false;
+        if (!(len > 0.0)) return -1;
         ea /= len;
         eb /= len;
         const double na = -eb, nb = ea;
@@ -334,7 +334,7 @@ bool build_line_table(const GeomHost &g, const double *table, LineView *out) {
         L.nbf = (float)nb;
         L.E0 = na * O[a] + nb * O[b];
         L.dq = na * OQ[a] + nb * OQ[b];
-        if (!(std::fabs(L.dq) > 1e-9)) return false;
+        if (!(std::fabs(L.dq) > 1e-9)) return -1;
         L.inv_dq = 1.0 / L.dq;
         L.inv_dqf = (float)L.inv_dq;
         const double A = std::fabs(ea), B = std::fabs(eb);
@@ -345,13 +345,18 @@ bool build_line_table(const GeomHost &g, const double *table, LineView *out) {
             const int c = A == 0.0 ? a : b;
             L.X0 = O[c];
             L.Xq = OQ[c];
-            if (L.Xq == 0.0) return false;
+            if (L.Xq == 0.0) return -1;
         } else {
             L.R = (float)(kap / (A * B));
         }
         // rows one brick stages for this view: its cross-section's shadow along n
-        const double w = 0.5 * (std::fabs(na) * ext[a] + std::fabs(nb) * ext[b]);
-        if (2.0 * (0.5 * (A + B) + w) / std::fabs(L.dq) + 4.0 > (double)kLineRows) return false;
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const LineShape &sh = kLineShapes[k2];
+            const int ext[3] = {sh.bx, sh.by, sh.bz};
+            const double w = 0.5 * (std::fabs(na) * ext[a] + std::fabs(nb) * ext[b]);
+            if (2.0 * (0.5 * (A + B) + w) / std::fabs(L.dq) + 4.0 > (double)sh.rows) fits[k2] = false;
+        }
+        if (d == 2) fits[1] = false;   // shape 1's lines run along x or y only
     }
     // each view's distance to the next view of its family (0: the last one)
     int last[3] = {-1, -1, -1};
@@ -360,7 +365,7 @@ bool build_line_table(const GeomHost &g, const double *table, LineView *out) {
         if (last[d] >= 0) out[last[d]].next = (int)(k - last[d]);
         last[d] = (int)k;
     }
-    return true;
+    return fits[1] ? 1 : (fits[0] ? 0 : -1);
 }
 
 // Range of the brick adjoint's 64-bit accumulator.  Each (ray, voxel) pair adds

@@ -100,9 +100,14 @@ struct LineView {
     int pad[2];
 };
 static_assert(sizeof(LineView) == 112, "line table layout");
-// The line adjoint's bricks (x, y, z) and the rows of one view it stages per brick.
-constexpr int kLineBX = 16, kLineBY = 16, kLineBZ = 32;
-constexpr int kLineRows = 64;
+// The line adjoint's brick shapes: bricks of bx x by x bz voxels, each thread
+// owning seg voxels along the untraversed axis, and the rows of one view a brick
+// stages.  Shape 1 (lines of 32 voxels, half the per-view work per voxel) serves
+// geometries whose views never run along z planes; shape 0 serves all.
+struct LineShape {
+    int bx, by, bz, seg, rows;
+};
+constexpr LineShape kLineShapes[2] = {{16, 16, 32, 16, 64}, {32, 32, 16, 32, 44}};
 
 // Validation and table precompute (host only, no HIP calls): ct_geometry.cpp
 ct_status_t validate_desc(const ct_geom_desc_t *desc, GeomHost *out, const char **why);
@@ -112,9 +117,10 @@ void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *tab
 // over all views, and the right shift its terms need so the 64-bit sums stay
 // below 2^62 (ct_geometry.cpp).
 double adjoint_rays_bound(const GeomHost &g, const double *table, bool surface);
-// The line table (one LineView per view); false when some view is not separable
-// in the sense above or a brick would need more than kLineRows rows of a view.
-bool build_line_table(const GeomHost &g, const double *table, LineView *out);
+// The line table (one LineView per view) and the brick shape it takes (an index
+// into kLineShapes); -1 when some view is not separable in the sense above or a
+// brick of every eligible shape would need more rows of a view than it stages.
+int build_line_table(const GeomHost &g, const double *table, LineView *out);
 int adjoint_term_shift(double rays_bound);
 
 void set_error(const char *msg);

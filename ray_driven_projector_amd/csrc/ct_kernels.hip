@@ -2172,17 +2172,26 @@ __device__ __forceinline__ LineView load_line(ConstLinePtr p) {
 }
 
 // One family of views (untraversed axis D) of one brick: sums into acc.
-template <int MODE, int D, int LSY, int LSZ>
+template <int MODE, int D, int SHAPE, int LSY, int LSZ>
 __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv, float *acc,
-                                            float (&stage)[2][kLineRows * kLinePitch], int &buf, int x0,
-                                            int y0, int z0, int ex, int ey, int ez) {
+                                            float (&stage)[2][kLineShapes[SHAPE].rows * kLinePitch], int &buf,
+                                            int x0, int y0, int z0, int ex, int ey, int ez) {
     constexpr int NT = 512;
+    constexpr LineShape SH = kLineShapes[SHAPE];
+    constexpr int SEG = SH.seg, ROWS = SH.rows;
     constexpr int AX = D == 0 ? 1 : 0, BXS = D == 2 ? 1 : 2;   // in-plane axes a < b
-    constexpr int W = D == 2 ? 32 : 16;                        // staged pixel columns
-    constexpr int NSLOT = W * kLineRows / NT;                  // staged values per thread
+    constexpr int EXT[3] = {SH.bx, SH.by, SH.bz};
+    constexpr int EA = EXT[AX], EB = EXT[BXS];
+    constexpr int W = EXT[D];                                  // staged pixel columns (the brick along D)
+    static_assert(EA * EB * (W / SEG) == NT, "one segment per thread");
+    static_assert(W <= kLinePitch - 4, "staged row pitch");
+    // staged values per thread: 64 rows (at most) of W columns, whichever way the
+    // threads run over them (rows past the view's count are not loaded)
+    static_assert(ROWS <= 64, "staged rows");
+    constexpr int NSLOT = W * 64 / NT;
     const int tid = threadIdx.x;
-    // this thread's segment: cell (la, lb), voxels s0 .. s0 + 15 along D
-    const int la = tid & 15, lb = D == 2 ? (tid >> 4) & 15 : tid >> 4, s0 = D == 2 ? (tid >> 8) * 16 : 0;
+    // this thread's segment: cell (la, lb), voxels s0 .. s0 + SEG - 1 along D
+    const int la = tid % EA, lb = (tid / EA) % EB, s0 = (tid / (EA * EB)) * SEG;
     const int gd = D == 0 ? x0 + a.offx : (D == 1 ? y0 + a.offy : z0 + a.offz);   // on the lattice
     const int ga = AX == 0 ? x0 + a.offx : y0 + a.offy, gb = BXS == 1 ? y0 + a.offy : z0 + a.offz;
     const int ea = AX == 0 ? ex : ey, eb = BXS == 1 ? ey : ez, ed = D == 0 ? ex : (D == 1 ? ey : ez);
@@ -2192,9 +2201,9 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
     int view = 0;
     while (view < a.n_views && lv[view].d != D) ++view;
     if (view >= a.n_views) return;
-    float part[16];
+    float part[SEG];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) part[j] = 0.f;
+    for (int j = 0; j < SEG; ++j) part[j] = 0.f;
     int batch = 0;
     // the thread's slots of the staged block: slot m holds row i0 + m di, column
     // j0 + m dj; along its slots the pixel's v stays fixed and u steps
@@ -2224,7 +2233,7 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
         const float C0 = (float)C0d;
         const float r1 = (-L.H - w - C0) * L.inv_dqf, r2 = (L.H + w - C0) * L.inv_dqf;
         const int rlo = uni((int)floorf(fminf(r1, r2)) - 1);
-        const int nrows = uni(min(kLineRows, (int)ceilf(fmaxf(r1, r2)) + 2 - rlo));
+        const int nrows = uni(min(ROWS, (int)ceilf(fmaxf(r1, r2)) + 2 - rlo));
         // stage rows q = qref + rlo + i and pixel columns p = g (gd + j - kc) (zero off
         // the detector and past the brick), loads along the sinogram's contiguous v
         float *st = stage[buf];
@@ -2287,7 +2296,7 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
                 if (Lc != 0.f) {
                     const float4 *row4 = (const float4 *)row;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
+                    for (int k = 0; k < SEG / 4; ++k) {
                         const float4 q = row4[k];
                         part[4 * k + 0] = fmaf(Lc, q.x, part[4 * k + 0]);
                         part[4 * k + 1] = fmaf(Lc, q.y, part[4 * k + 1]);
@@ -2305,7 +2314,7 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
                 constexpr int STEP = D == 0 ? 1 : (D == 1 ? LSY : LSZ);
                 const int base = D == 0 ? lb * LSZ + la * LSY : (D == 1 ? lb * LSZ + la : lb * LSY + la);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
+                for (int j = 0; j < SEG; ++j) {
                     acc[base + (s0 + j) * STEP] += part[j];
                     part[j] = 0.f;
                 }
@@ -2318,12 +2327,13 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
     __syncthreads();   // the next family's segments own other voxels
 }
 
-template <int MODE>
+template <int MODE, int SHAPE>
 __global__ __launch_bounds__(512) void line_kernel(BrickArgs a, const LineView *lines) {
-    constexpr int BX = kLineBX, BY = kLineBY, BZ = kLineBZ, NT = 512;
+    constexpr LineShape SH = kLineShapes[SHAPE];
+    constexpr int BX = SH.bx, BY = SH.by, BZ = SH.bz, NT = 512;
     constexpr int LSY = BX + 1, LSZ = LSY * BY + 1, LN = LSZ * BZ;
     __shared__ float acc[LN];
-    __shared__ float stage[2][kLineRows * kLinePitch];
+    __shared__ float stage[2][SH.rows * kLinePitch];
     const int tid = threadIdx.x;
     for (int i = tid; i < LN; i += NT) acc[i] = 0.f;
 
@@ -2345,9 +2355,9 @@ __global__ __launch_bounds__(512) void line_kernel(BrickArgs a, const LineView *
     }
     const ConstLinePtr lv = (ConstLinePtr)lines;
     int buf = 0;
-    line_family<MODE, 0, LSY, LSZ>(a, lv, acc, stage, buf, x0, y0, z0, ex, ey, ez);
-    line_family<MODE, 1, LSY, LSZ>(a, lv, acc, stage, buf, x0, y0, z0, ex, ey, ez);
-    line_family<MODE, 2, LSY, LSZ>(a, lv, acc, stage, buf, x0, y0, z0, ex, ey, ez);
+    line_family<MODE, 0, SHAPE, LSY, LSZ>(a, lv, acc, stage, buf, x0, y0, z0, ex, ey, ez);
+    line_family<MODE, 1, SHAPE, LSY, LSZ>(a, lv, acc, stage, buf, x0, y0, z0, ex, ey, ez);
+    if constexpr (SHAPE == 0) line_family<MODE, 2, SHAPE, LSY, LSZ>(a, lv, acc, stage, buf, x0, y0, z0, ex, ey, ez);
     __syncthreads();
     brick_writeout<BX, BY, BZ, NT, MODE>(a, x0, y0, z0, ex, ey, ez, [&](int lx, int ly, int lz) {
         return acc[lz * LSZ + ly * LSY + lx];
@@ -2693,12 +2703,17 @@ static hipError_t launch_brick_args(const LaunchGeom &g, BrickArgs a, hipStream_
     // 3D: bricks of 16 x 16 x 32 voxels, 512 threads; 2D: 16 x 16, 256 threads;
     // separable tilt series: the line adjoint on the same bricks
     if (g.line_tab && !g.two_d) {
-        a.nbx = (g.W + kLineBX - 1) / kLineBX;
-        a.nby = (g.H + kLineBY - 1) / kLineBY;
-        a.nbz = (g.D + kLineBZ - 1) / kLineBZ;
+        const LineShape &sh = kLineShapes[g.line_shape];
+        a.nbx = (g.W + sh.bx - 1) / sh.bx;
+        a.nby = (g.H + sh.by - 1) / sh.by;
+        a.nbz = (g.D + sh.bz - 1) / sh.bz;
         a.n_blocks = a.nbx * a.nby * a.nbz;
-        hipLaunchKernelGGL((line_kernel<MODE>), dim3(a.n_blocks), dim3(512), 0, s, a,
-                           (const LineView *)g.line_tab);
+        if (g.line_shape == 1)
+            hipLaunchKernelGGL((line_kernel<MODE, 1>), dim3(a.n_blocks), dim3(512), 0, s, a,
+                               (const LineView *)g.line_tab);
+        else
+            hipLaunchKernelGGL((line_kernel<MODE, 0>), dim3(a.n_blocks), dim3(512), 0, s, a,
+                               (const LineView *)g.line_tab);
     } else if (g.two_d) {
         launch_brick_shape<16, 16, 1, 256, MODE>(a, g, s);
     } else {
@@ -2762,6 +2777,11 @@ size_t cgls_ray_blocks(const LaunchGeom &g) { return (size_t)ray_args(g).n_block
 size_t cgls_brick_blocks(const LaunchGeom &g) {
     int bx, by, bz;
     brick_shape(g, bx, by, bz);
+    if (g.line_tab && !g.two_d) {   // the line adjoint's bricks
+        bx = kLineShapes[g.line_shape].bx;
+        by = kLineShapes[g.line_shape].by;
+        bz = kLineShapes[g.line_shape].bz;
+    }
     return (size_t)((g.W + bx - 1) / bx) * ((g.H + by - 1) / by) * ((g.D + bz - 1) / bz);
 }
 

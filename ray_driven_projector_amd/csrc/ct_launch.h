@@ -32,6 +32,7 @@ struct LaunchGeom {
     int rec_view0;         // table view of the launch's first view
     const void *line_tab;  // separable tilt series: the line table (LineView) from the launch's
                            // first view; the adjoint then runs the line kernel (else null)
+    int line_shape;        // its brick shape (an index into kLineShapes)
 };
 
 hipError_t launch_fill(float *p, size_t n, float v, hipStream_t s);
