@@ -2208,11 +2208,12 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
     // the thread's slots of the staged block: slot m holds row i0 + m di, column
     // j0 + m dj; along its slots the pixel's v stays fixed and u steps
     const auto slot0 = [&](int P, int &i0, int &j0, int &di, int &dj) {
-        if (P == 0) {   // p = u, q = v: threads along the rows (memory order)
+        if (P == 0) {   // p = u, q = v: threads along the rows (memory order), NSLOT
+                        // consecutive columns each
             i0 = tid & 63;
-            j0 = tid >> 6;
+            j0 = (tid >> 6) * NSLOT;
             di = 0;
-            dj = NT / 64;
+            dj = 1;
         } else {        // p = v, q = u: threads along the columns (memory order)
             j0 = tid & (W - 1);
             i0 = tid / W;
@@ -2249,18 +2250,33 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(a.sino + (size_t)view * a.U * a.V, (uint32_t)(a.U * a.V) * 4u);
             const uint32_t off0 = (uint32_t)(u0 * a.V + vv) * 4u, dstep = (uint32_t)(du * a.V) * 4u;
+            // Columns past the brick are loaded too (they only reach voxels that are
+            // never written out), and so are rows past the view's count (never read);
+            // a row off the detector in v reads nothing, through an offset past the
+            // buffer.
             float ld[NSLOT];
 #pragma unroll
             for (int m = 0; m < NSLOT; ++m) {
-                const int i = i0 + m * di, j = j0 + m * dj, u = u0 + m * du;
-                ld[m] = 0.f;
-                if (i < nrows && j < ed && vok && (MODE != BM_COLINV || (u >= 0 && u < a.U)))
-                    ld[m] = MODE == BM_COLINV ? 1.f : load_f32(rs, off0 + m * dstep);
+                const int u = u0 + m * du;
+                if (MODE == BM_COLINV)
+                    ld[m] = (vok && u >= 0 && u < a.U) ? 1.f : 0.f;
+                else
+                    ld[m] = load_f32(rs, vok ? off0 + m * dstep : 0x80000000u);
             }
+            if (L.P == 0) {   // a row's NSLOT consecutive columns: one store
+                if (i0 < nrows) {
+                    float *dst = st + i0 * kLinePitch + j0;
+                    if constexpr (NSLOT == 4)
+                        *(float4 *)dst = make_float4(ld[0], ld[1], ld[2], ld[3]);
+                    else
+                        *(float2 *)dst = make_float2(ld[0], ld[1]);
+                }
+            } else {
 #pragma unroll
-            for (int m = 0; m < NSLOT; ++m) {
-                const int i = i0 + m * di, j = j0 + m * dj;
-                if (i < nrows) st[i * kLinePitch + j] = ld[m];
+                for (int m = 0; m < NSLOT; ++m) {
+                    const int i = i0 + m * di;
+                    if (i < nrows) st[i * kLinePitch + j0] = ld[m];
+                }
             }
         }
         __syncthreads();
@@ -2293,16 +2309,15 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
                 const float Lc = L.aligned ? ((dl >= 0.f && dl < 1.f) ? L.Lmax : 0.f)
                                            : fminf(fmaxf((L.H - fabsf(dl)) * L.R, 0.f), L.Lmax);
                 dl += step;
-                if (Lc != 0.f) {
-                    const float4 *row4 = (const float4 *)row;
+                // (a zero chord, an aligned ray on the cell's far edge, adds nothing)
+                const float4 *row4 = (const float4 *)row;
 #pragma unroll
-                    for (int k = 0; k < SEG / 4; ++k) {
-                        const float4 q = row4[k];
-                        part[4 * k + 0] = fmaf(Lc, q.x, part[4 * k + 0]);
-                        part[4 * k + 1] = fmaf(Lc, q.y, part[4 * k + 1]);
-                        part[4 * k + 2] = fmaf(Lc, q.z, part[4 * k + 2]);
-                        part[4 * k + 3] = fmaf(Lc, q.w, part[4 * k + 3]);
-                    }
+                for (int k = 0; k < SEG / 4; ++k) {
+                    const float4 q = row4[k];
+                    part[4 * k + 0] = fmaf(Lc, q.x, part[4 * k + 0]);
+                    part[4 * k + 1] = fmaf(Lc, q.y, part[4 * k + 1]);
+                    part[4 * k + 2] = fmaf(Lc, q.z, part[4 * k + 2]);
+                    part[4 * k + 3] = fmaf(Lc, q.w, part[4 * k + 3]);
                 }
             }
         }
