@@ -33,8 +33,13 @@ Default run (one JSON line):
   multiply-add, 12 in all (10 to 14 by the model the bound was derived
   from); where four rays share one walk (parallel views with an untraversed
   axis whose pixel step runs along it, as on the dual-axis workload) the 10
-  are shared, 10 / 4 + 2 = 4.5.  The kernels spend more (the measured figure,
-  from committed counters, is given beside it).  The effective-HBM view (4
+  are shared, 10 / 4 + 2 = 4.5.  Where the adjoint runs as the line kernel
+  (every view's rays lie in planes of one volume axis, as on the dual-axis
+  workload) no ray is walked: a ray's chord through an in-plane cell is formed
+  once (6 lane operations: offset, distance to the window edge, slope, the two
+  clamps, the step to the next row) and shared by the 32 voxels of the thread's
+  line through that cell, so 6 / 32 + 2.  The kernels spend more (the measured
+  figure, from committed counters, is given beside it).  The effective-HBM view (4
   bytes per intersection against 8 TB/s, most of them served by the caches)
   is kept as "effective_hbm_frac".
 - "traffic" and the measured VALU instructions come from rocprofv3 counter
@@ -76,6 +81,9 @@ VALU_PEAK = 256 * 4 * 16 * 2.4e9
 WALK_OPS, RAY_OPS, PACKET = 10, 2, 4
 OPS_PER_INTERSECTION = WALK_OPS + RAY_OPS
 OPS_PACKET = WALK_OPS / PACKET + RAY_OPS
+# line adjoint: one chord per (ray, in-plane cell), shared along a 32-voxel line
+CHORD_OPS, LINE_SEG = 6, 32
+OPS_LINE = CHORD_OPS / LINE_SEG + RAY_OPS
 # fp32 vector peak without packed math, for the FDK gather: VALU_PEAK x 2 (FMA)
 ALU_PEAK = 2 * VALU_PEAK
 # FDK backprojection flops per voxel-view: three affine forms (9 FMA = 18), a
@@ -119,7 +127,8 @@ def counters(key: str):
 # kernel-name patterns of the hot kernels and the role each plays
 ROLES = (("ray_kernel<0,", "project"), ("ray_kernel<1,", "sirt_residual"), ("ray_kernel<4,", "backproject_atomic"),
          ("ray_packet_kernel<0>", "project"), ("ray_packet_kernel<1>", "sirt_residual"),
-         ("ray_kernel<5,", "cgls_project"), ("brick_kernel<", "backproject"), ("fbp_bp_kernel<", "fbp_backproject"),
+         ("ray_kernel<5,", "cgls_project"), ("brick_kernel<", "backproject"), ("line_kernel<", "backproject"),
+         ("fbp_bp_kernel<", "fbp_backproject"),
          ("fbp_fft_filter_kernel", "fbp_filter"), ("fbp_filter_kernel", "fbp_filter"))
 BRICK_MODES = {"0": "backproject", "1": "sirt_update", "2": "colinv", "3": "cgls_adjoint"}
 COPY_BYTES = 1 << 30   # the --copy-calibration copy reads and writes 1 GiB
@@ -134,9 +143,12 @@ PMC_PASSES = (("sq", "SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVES SQ_INSTS
 def kernel_role(name: str):
     for pat, role in ROLES:
         if pat in name:
-            if role == "backproject":   # brick_kernel<BX, BY, BZ, NT, MODE, SURF, PERSP>
+            if role == "backproject" and pat == "brick_kernel<":   # <BX, BY, BZ, NT, MODE, SURF, PERSP, REC>
                 args = name.split("brick_kernel<", 1)[1].split(">", 1)[0].split(",")
                 return BRICK_MODES.get(args[4].strip())
+            if role == "backproject":   # line_kernel<MODE, SHAPE>
+                args = name.split("line_kernel<", 1)[1].split(">", 1)[0].split(",")
+                return BRICK_MODES.get(args[0].strip())
             return role
     return None
 
@@ -254,8 +266,17 @@ def packet_views(wl) -> bool:
     return bool((t[:, 47] >= 0).all()) and getattr(wl, "offsets", None) is None
 
 
-def alu_roofline(kernel: str, nnz: int, ms: float, key: str, packets: bool = False):
-    per = OPS_PACKET if packets else OPS_PER_INTERSECTION
+def line_adjoint(wl) -> bool:
+    """The workload's adjoint runs as the line kernel (decided by the library
+    from the geometry description)."""
+    import ray_driven_projector_amd as rdp
+    return rdp.ct_geom_adjoint_kind(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing,
+                                    wl.frames, surface=getattr(wl, "offsets", None) is not None) \
+        == rdp.ADJOINT_LINE
+
+
+def alu_roofline(kernel: str, nnz: int, ms: float, key: str, packets: bool = False, line: bool = False):
+    per = OPS_LINE if line else (OPS_PACKET if packets else OPS_PER_INTERSECTION)
     ops = int(per * nnz)
     achieved = ops / (ms * 1e-3)
     c = counters(key)
@@ -353,6 +374,8 @@ def kernel_names(wl, W, mode=0):
     shape = "16, 16, 1, 256" if two_d else "16, 16, 32, 512"
     fwd = (f"ray_packet_kernel<{mode}>" if packet_views(wl) else
            f"ray_kernel<{mode}, {'true' if two_d else 'false'}, {sf}>")
+    if line_adjoint(wl):
+        return fwd, f"line_kernel<{mode}, shape> (line adjoint)"
     return fwd, f"brick_kernel<{shape}, {mode}, {sf}, {'true' if persp else 'false'}> (packets of {PACKET})" \
         if packet_views(wl) else f"brick_kernel<{shape}, {mode}, {sf}, {'true' if persp else 'false'}>"
 
@@ -380,7 +403,7 @@ def config_pair(cfg, rdp, W, torch, stream, timer):
            "A_G_intersections_per_s": round(n / (ms_a * 1e-3) / 1e9, 1),
            "AT_G_intersections_per_s": round(n / (ms_at * 1e-3) / 1e9, 1),
            "A_roofline": alu_roofline(ka, n, ms_a, f"c{cfg}/project", pk),
-           "AT_roofline": alu_roofline(kat, n, ms_at, f"c{cfg}/backproject", pk)}
+           "AT_roofline": alu_roofline(kat, n, ms_at, f"c{cfg}/backproject", pk, line_adjoint(wl))}
     del g, x, y, sino, vol
     torch.cuda.empty_cache()
     return out
@@ -448,8 +471,10 @@ def default_run(args, rdp, W, torch, np):
                    "intersections_per_pass": nnz, "rays": M, "voxels": N},
         "ms_per_sirt_iteration": round(ms_step, 3),
         "kernel_ms": {k: round(v[1], 3) for k, v in kernels.items()},
-        "roofline": alu_roofline(kernels[dom][0], nnz, kernels[dom][1], f"c4/{dom}", pk),
-        "roofline_other": {k: alu_roofline(v[0], nnz, v[1], f"c4/{k}", pk) for k, v in kernels.items() if k != dom},
+        "roofline": alu_roofline(kernels[dom][0], nnz, kernels[dom][1], f"c4/{dom}", pk,
+                                 line_adjoint(wl) and dom == "sirt_update"),
+        "roofline_other": {k: alu_roofline(v[0], nnz, v[1], f"c4/{k}", pk, line_adjoint(wl) and k == "sirt_update")
+                           for k, v in kernels.items() if k != dom},
     }
     del g, x_true, y, rinv, cinv, x, work
     torch.cuda.empty_cache()
@@ -598,7 +623,8 @@ def single_run(args, rdp, W, torch, np):
         dom = 0 if ms[0] >= ms[1] else 1
         kern = (ka, kat)[dom]
         res["roofline"] = alu_roofline(kern, nnz, ms[dom], f"c{cfg}/{names[dom]}",
-                                       packet_views(wl) and args.workload != "c5cyl")
+                                       packet_views(wl) and args.workload != "c5cyl",
+                                       dom == 1 and line_adjoint(wl))
         if cfg == 4:
             res["ms_per_sirt_iteration"] = round(ms_step, 3)
     if args.extra:

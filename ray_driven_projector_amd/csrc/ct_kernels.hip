@@ -2249,7 +2249,9 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
             // fall outside it (a negative one wraps high) and read 0
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(a.sino + (size_t)view * a.U * a.V, (uint32_t)(a.U * a.V) * 4u);
-            const uint32_t off0 = (uint32_t)(u0 * a.V + vv) * 4u, dstep = (uint32_t)(du * a.V) * 4u;
+            // (24-bit products: the line table takes detectors under 2^22 pixels a side)
+            const uint32_t off0 = (uint32_t)(__mul24(u0, a.V) + vv) * 4u;
+            const uint32_t dstep = (uint32_t)uni(du * a.V * 4);
             // Columns past the brick are loaded too (they only reach voxels that are
             // never written out), and so are rows past the view's count (never read);
             // a row off the detector in v reads nothing, through an offset past the
