@@ -2149,16 +2149,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
 //
 // Every view of the geometry lies in planes of one volume axis d (a tilt series
 // about a volume axis with one detector column per voxel plane).  One 512-thread
-// workgroup owns a brick of 16 x 16 x 32 voxels.  Views are taken family by
-// family (d = x, y, z); within a family every thread owns a segment of 16 voxels
-// along d at one in-plane cell.  Per view the workgroup stages in LDS the rows of
-// the view that can meet its brick, for the 16 (32 for d = z) pixel columns whose
-// planes hold its voxels; each thread then finds the rows meeting its cell (one
-// or two), forms each ray's chord through the cell once, from the ray's offset to
-// the cell centre (the trapezoid of a unit square), and adds chord * value to its
-// 16 voxels.  No ray is walked and nothing is added atomically: sums run in
-// float32 registers over 16 views, then into the brick's float32 accumulator in
-// LDS (each voxel belongs to one segment per family), which is written once.
+// workgroup owns a brick (kLineShapes: 32 x 32 x 16 voxels with lines of 32 when
+// no view's planes are z planes, else 16 x 16 x 32 with lines of 16).  Views are
+// taken family by family (d = x, y, z); within a family every thread owns a
+// segment (line) of voxels along d at one in-plane cell.  Per view the workgroup
+// stages in LDS the rows of the view that can meet its brick, for the pixel
+// columns whose planes hold its voxels; each thread then finds the rows meeting
+// its cell (one or two), forms each ray's chord through the cell once, from the
+// ray's offset to the cell centre (the trapezoid of a unit square), and adds
+// chord * value to the voxels of its line.  No ray is walked and nothing is
+// added atomically: sums run in float32 registers over 16 views, then into the
+// brick's float32 accumulator in LDS (each voxel belongs to one line per family),
+// which is written once.
 constexpr int kLinePitch = 36;   // floats per staged row: up to 32 pixel columns, padded
 typedef const __attribute__((address_space(4))) LineView *ConstLinePtr;
 // a view's entry, field by field (scalar loads)
