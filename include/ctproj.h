@@ -199,7 +199,7 @@ ct_status_t ct_geom_adjoint_range(ct_geom_t g, const ct_geom_desc_t *desc, int s
  *     other detector axis without a d component.  Then the rays of one pixel
  *     column lie in one voxel plane and each plane is a 2D parallel projection
  *     (the electron-tomography article's dual-axis tilt series about x and y is
- *     such a geometry), with detector sides under 2^22 pixels.  The adjoint
+ *     such a geometry).  The adjoint
  *     forms each ray's chord through a voxel once per line of 32 voxels along d
  *     (16 when some views' planes are z planes, or a view's rows are too dense
  *     for a 32 x 32 x 16 brick to stage them), from the ray's offset to the

@@ -295,7 +295,6 @@ int build_line_table(const GeomHost &g, const double *table, LineView *out) {
     // one view's pixels are read through a buffer of 32-bit byte offsets, where a
     // negative offset (a pixel before the detector) must fall outside the view
     if ((double)g.U * (double)g.V * 4.0 >= 2147483648.0) return -1;
-    if (g.U >= (1 << 22) || g.V >= (1 << 22)) return -1;   // the kernel's 24-bit pixel offsets
     const double sp[3] = {g.sx, g.sy, g.sz};
     bool fits[2] = {true, true};   // every view's rows fit each shape's stage
     for (int64_t k = 0; k < g.n_views; ++k) {

@@ -2251,7 +2251,7 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
             // fall outside it (a negative one wraps high) and read 0
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(a.sino + (size_t)view * a.U * a.V, (uint32_t)(a.U * a.V) * 4u);
-            // (24-bit products: the line table takes detectors under 2^22 pixels a side)
+            // (24-bit products: validated detector sides are under 2^20 pixels)
             const uint32_t off0 = (uint32_t)(__mul24(u0, a.V) + vv) * 4u;
             const uint32_t dstep = (uint32_t)uni(du * a.V * 4);
             // Columns past the brick are loaded too (they only reach voxels that are
