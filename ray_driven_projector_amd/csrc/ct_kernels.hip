@@ -2223,67 +2223,96 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
             dj = 0;
         }
     };
-    for (;;) {
-        const LineView L = load_line(lv + view);
-        // rows of the view that can meet the brick, referred to the row nearest the
-        // centre of the brick's cross-section, so the per-cell arithmetic meets
-        // small numbers
-        const double Eref = L.E0 - L.na * (ga + 0.5 * ea) - L.nb * (gb + 0.5 * eb);
-        const double qr = rint(-Eref * L.inv_dq);
-        const int qref = uni((int)qr);
-        const double C0d = uni(fma(qr, L.dq, Eref));
-        const float w = 0.5f * (fabsf(L.naf) * (float)ea + fabsf(L.nbf) * (float)eb);
-        const float C0 = (float)C0d;
-        const float r1 = (-L.H - w - C0) * L.inv_dqf, r2 = (L.H + w - C0) * L.inv_dqf;
-        const int rlo = uni((int)floorf(fminf(r1, r2)) - 1);
-        const int nrows = uni(min(ROWS, (int)ceilf(fmaxf(r1, r2)) + 2 - rlo));
-        // stage rows q = qref + rlo + i and pixel columns p = g (gd + j - kc) (zero off
-        // the detector and past the brick), loads along the sinogram's contiguous v
-        float *st = stage[buf];
-        {
-            int i0, j0, di, dj;
-            slot0(L.P, i0, j0, di, dj);
-            const int q0 = qref + rlo + i0, p0 = L.g * (gd + j0 - L.kc);
-            const int u0 = L.P == 0 ? p0 : q0, vv = L.P == 0 ? q0 : p0;
-            const int du = L.P == 0 ? L.g * dj : di;
-            const bool vok = vv >= 0 && vv < a.V;
-            // the view's pixels as one buffer: offsets of pixels off the detector in u
-            // fall outside it (a negative one wraps high) and read 0
-            const __amdgpu_buffer_rsrc_t rs =
-                make_rsrc(a.sino + (size_t)view * a.U * a.V, (uint32_t)(a.U * a.V) * 4u);
-            // (24-bit products: validated detector sides are under 2^20 pixels)
-            const uint32_t off0 = (uint32_t)(__mul24(u0, a.V) + vv) * 4u;
-            const uint32_t dstep = (uint32_t)uni(du * a.V * 4);
-            // Columns past the brick are loaded too (they only reach voxels that are
-            // never written out), and so are rows past the view's count (never read);
-            // a row off the detector in v reads nothing, through an offset past the
-            // buffer.
-            float ld[NSLOT];
+    // A view's per-brick quantities (wave-uniform): the rows of the view that can
+    // meet the brick, referred to the row nearest the centre of the brick's
+    // cross-section, so the per-cell arithmetic meets small numbers.
+    struct Head {
+        LineView L;
+        double qr, C0d;
+        int qref, rlo, nrows;
+    };
+    const auto head = [&](int v, Head &h) __attribute__((always_inline)) {
+        h.L = load_line(lv + v);
+        const double Eref = h.L.E0 - h.L.na * (ga + 0.5 * ea) - h.L.nb * (gb + 0.5 * eb);
+        h.qr = rint(-Eref * h.L.inv_dq);
+        h.qref = uni((int)h.qr);
+        h.C0d = uni(fma(h.qr, h.L.dq, Eref));
+        const float w = 0.5f * (fabsf(h.L.naf) * (float)ea + fabsf(h.L.nbf) * (float)eb);
+        const float C0 = (float)h.C0d;
+        const float r1 = (-h.L.H - w - C0) * h.L.inv_dqf, r2 = (h.L.H + w - C0) * h.L.inv_dqf;
+        h.rlo = uni((int)floorf(fminf(r1, r2)) - 1);
+        h.nrows = uni(min(ROWS, (int)ceilf(fmaxf(r1, r2)) + 2 - h.rlo));
+    };
+    // This thread's values of a view's staged block (rows q = qref + rlo + i, pixel
+    // columns p = g (gd + j - kc), zero off the detector), loaded along the
+    // sinogram's contiguous v.  Columns past the brick are loaded too (they only
+    // reach voxels that are never written out), and so are rows past the view's
+    // count (never stored); a row off the detector in v reads nothing, through an
+    // offset past the buffer.
+    const auto fetch = [&](int v, const Head &h, float (&ld)[NSLOT]) __attribute__((always_inline)) {
+        int i0, j0, di, dj;
+        slot0(h.L.P, i0, j0, di, dj);
+        const int q0 = h.qref + h.rlo + i0, p0 = h.L.g * (gd + j0 - h.L.kc);
+        const int u0 = h.L.P == 0 ? p0 : q0, vv = h.L.P == 0 ? q0 : p0;
+        const int du = h.L.P == 0 ? h.L.g * dj : di;
+        const bool vok = vv >= 0 && vv < a.V;
+        // the view's pixels as one buffer: offsets of pixels off the detector in u
+        // fall outside it (a negative one wraps high) and read 0
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(a.sino + (size_t)v * a.U * a.V, (uint32_t)(a.U * a.V) * 4u);
+        // (24-bit products: validated detector sides are under 2^20 pixels)
+        const uint32_t off0 = (uint32_t)(__mul24(u0, a.V) + vv) * 4u;
+        const uint32_t dstep = (uint32_t)uni(du * a.V * 4);
+#pragma unroll
+        for (int m = 0; m < NSLOT; ++m) {
+            const int u = u0 + m * du;
+            if (MODE == BM_COLINV)
+                ld[m] = (vok && u >= 0 && u < a.U) ? 1.f : 0.f;
+            else
+                ld[m] = load_f32(rs, vok ? off0 + m * dstep : 0x80000000u);
+        }
+    };
+    const auto stash = [&](const Head &h, const float (&ld)[NSLOT], float *st) __attribute__((always_inline)) {
+        int i0, j0, di, dj;
+        slot0(h.L.P, i0, j0, di, dj);
+        if (h.L.P == 0) {   // a row's NSLOT consecutive columns: one store
+            if (i0 < h.nrows) {
+                float *dst = st + i0 * kLinePitch + j0;
+                if constexpr (NSLOT == 4)
+                    *(float4 *)dst = make_float4(ld[0], ld[1], ld[2], ld[3]);
+                else
+                    *(float2 *)dst = make_float2(ld[0], ld[1]);
+            }
+        } else {
 #pragma unroll
             for (int m = 0; m < NSLOT; ++m) {
-                const int u = u0 + m * du;
-                if (MODE == BM_COLINV)
-                    ld[m] = (vok && u >= 0 && u < a.U) ? 1.f : 0.f;
-                else
-                    ld[m] = load_f32(rs, vok ? off0 + m * dstep : 0x80000000u);
-            }
-            if (L.P == 0) {   // a row's NSLOT consecutive columns: one store
-                if (i0 < nrows) {
-                    float *dst = st + i0 * kLinePitch + j0;
-                    if constexpr (NSLOT == 4)
-                        *(float4 *)dst = make_float4(ld[0], ld[1], ld[2], ld[3]);
-                    else
-                        *(float2 *)dst = make_float2(ld[0], ld[1]);
-                }
-            } else {
-#pragma unroll
-                for (int m = 0; m < NSLOT; ++m) {
-                    const int i = i0 + m * di;
-                    if (i < nrows) st[i * kLinePitch + j0] = ld[m];
-                }
+                const int i = i0 + m * di;
+                if (i < h.nrows) st[i * kLinePitch + j0] = ld[m];
             }
         }
+    };
+    // Software pipeline: a view's block is loaded into registers while the
+    // workgroup sums the view before it, and stored to the other staging buffer
+    // at the top of its own turn; one barrier per view.
+    Head h;
+    float ld[NSLOT];
+    head(view, h);
+    fetch(view, h, ld);
+    for (;;) {
+        stash(h, ld, stage[buf]);
+        const bool last = h.L.next == 0 || view + h.L.next >= a.n_views;
+        const int nview = view + h.L.next;
+        Head hn;
+        float ldn[NSLOT];
+        if (!last) {
+            head(nview, hn);
+            fetch(nview, hn, ldn);
+        }
         __syncthreads();
+        const float *st = stage[buf];
+        const LineView &L = h.L;
+        const int rlo = h.rlo, nrows = h.nrows;
+        const double qr = h.qr, C0d = h.C0d;
         // the rows meeting this cell, each with its chord, summed into the segment
         if (live) {
             // offset of row qref + r from this cell's centre: C + r dq, formed in
@@ -2326,7 +2355,6 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
             }
         }
         buf ^= 1;
-        const bool last = L.next == 0 || view + L.next >= a.n_views;
         if (++batch == 16 || last) {
             // into the brick's accumulator: each voxel belongs to one segment here
             if (live) {
@@ -2341,7 +2369,10 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
             batch = 0;
         }
         if (last) break;
-        view += L.next;
+        view = nview;
+        h = hn;
+#pragma unroll
+        for (int m = 0; m < NSLOT; ++m) ld[m] = ldn[m];
     }
     __syncthreads();   // the next family's segments own other voxels
 }
