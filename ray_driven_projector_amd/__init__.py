@@ -165,7 +165,7 @@ def ct_geom_validate(beam, vol_shape, voxel_spacing, det_shape, det_spacing, fra
 
 
 def ct_geom_view_table(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames):
-    """Host-computed per-view ray table (n_views x 40 float64)."""
+    """Host-computed per-view ray table (n_views x CT_VIEW_TABLE_STRIDE float64)."""
     d, fr = make_desc(beam, vol_shape, voxel_spacing, det_shape, det_spacing, frames)
     out = np.zeros((fr.shape[0], CT_VIEW_TABLE_STRIDE), dtype=np.float64)
     _check(lib().ct_geom_view_table(None, ctypes.byref(d),

@@ -835,7 +835,8 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
 // ray's sum is formed exactly as ray_kernel forms it (same clip, chunks,
 // pieces and order of additions).  Tiles: a block takes kPacketTP pixels
 // along P x kPacketTQ across; blocks run tile by tile, each tile through every
-// view in turn.  RM_PROJECT and RM_RESIDUAL.
+// view in turn.  RM_PROJECT, RM_RESIDUAL, and the CGLS forms RM_PROJECT_SQ and
+// RM_CGLS_R0 with their fixed-order block sums of squares (one partial per block).
 template <int MODE>
 __global__ __launch_bounds__(64 * kPacketWaves) void ray_packet_kernel(RayArgs a) {
     constexpr int K = kPacket;
@@ -850,11 +851,13 @@ __global__ __launch_bounds__(64 * kPacketWaves) void ray_packet_kernel(RayArgs a
     constexpr int TP = kPacketTP, TQ = kPacketTQ, RQ = 64 / kPacketLanesP;
     const int NP = pu ? a.U : a.V, NQ = pu ? a.V : a.U;
     const int ntp = (NP + TP - 1) / TP, ntq = (NQ + TQ - 1) / TQ;
-    if (tile >= ntp * ntq) return;
+    const bool tile_ok = tile < ntp * ntq;   // (a block past the last tile only writes its partial)
     const int tp = tile % ntp, tq = tile / ntp;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int p0 = tp * TP + (lane % kPacketLanesP) * K, q = tq * TQ + wv * RQ + lane / kPacketLanesP;
-    if (p0 >= NP || q >= NQ) return;
+    constexpr bool SQ = MODE == RM_PROJECT_SQ || MODE == RM_CGLS_R0;
+    double my_sq = 0.0;
+    if (tile_ok && p0 < NP && q < NQ) {
     const int kk = min(K, NP - p0);
     const int u0 = pu ? p0 : q, v0 = pu ? q : p0;
     double ox, oy, oz, dx, dy, dz;
@@ -979,8 +982,29 @@ __global__ __launch_bounds__(64 * kPacketWaves) void ray_packet_kernel(RayArgs a
         const float acc = in[j] ? tot[j] : 0.f;
         if (MODE == RM_PROJECT) {
             a.out[ray] = a.accumulate ? acc + a.out[ray] : acc;
+        } else if (MODE == RM_PROJECT_SQ) {
+            a.out[ray] = acc;
+            my_sq += (double)acc * acc;
+        } else if (MODE == RM_CGLS_R0) {
+            const float r = a.sino[ray] - acc;
+            a.out[ray] = r;
+            my_sq += (double)r * r;
         } else {
             a.out[ray] = a.rinv[ray] * (a.sino[ray] - acc);
+        }
+    }
+    }
+    if constexpr (SQ) {
+        // fixed-order block sum (float64), one partial per block
+        __shared__ double wsum[kPacketWaves];
+        double t = my_sq;
+        for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+        if (lane == 0) wsum[wv] = t;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double b = 0.0;
+            for (int k = 0; k < kPacketWaves; ++k) b += wsum[k];
+            a.partial[blockIdx.x] = b;
         }
     }
 }
@@ -2586,15 +2610,25 @@ static RayArgs ray_args(const LaunchGeom &g) {
     return a;
 }
 
+// The forward kinds the packet kernel serves, and the geometries it serves them on.
+constexpr bool packet_mode(int mode) {
+    return mode == RM_PROJECT || mode == RM_RESIDUAL || mode == RM_PROJECT_SQ || mode == RM_CGLS_R0;
+}
+static bool packet_geom(const LaunchGeom &g) { return g.packet && !g.two_d && !g.surf_off; }
+// Blocks of a packet launch: tiles of kPacketTP x kPacketTQ pixels, the first
+// along each view's packet axis, for every view.
+static int packet_blocks(const LaunchGeom &g) {
+    constexpr int TP = kPacketTP, TQ = kPacketTQ;
+    const int tu = ((g.U + TP - 1) / TP) * ((g.V + TQ - 1) / TQ), tv = ((g.V + TP - 1) / TP) * ((g.U + TQ - 1) / TQ);
+    const int G = kPacketTileGroup;
+    return g.n_views * ((std::max(tu, tv) + G - 1) / G) * G;
+}
+
 template <int MODE>
 static hipError_t launch_ray(const LaunchGeom &g, RayArgs a, hipStream_t s) {
-    if ((MODE == RM_PROJECT || MODE == RM_RESIDUAL) && g.packet && !g.two_d && !a.surf.off) {
-        // tiles of kPacketTP x kPacketTQ pixels, the first along each view's packet axis
-        constexpr int TP = kPacketTP, TQ = kPacketTQ;
-        const int tu = ((g.U + TP - 1) / TP) * ((g.V + TQ - 1) / TQ), tv = ((g.V + TP - 1) / TP) * ((g.U + TQ - 1) / TQ);
-        const int G = kPacketTileGroup;
-        a.n_blocks = g.n_views * ((std::max(tu, tv) + G - 1) / G) * G;
-        hipLaunchKernelGGL((ray_packet_kernel<MODE == RM_PROJECT ? RM_PROJECT : RM_RESIDUAL>), dim3(a.n_blocks),
+    if (packet_mode(MODE) && packet_geom(g)) {
+        a.n_blocks = packet_blocks(g);
+        hipLaunchKernelGGL((ray_packet_kernel<packet_mode(MODE) ? MODE : RM_PROJECT>), dim3(a.n_blocks),
                            dim3(64 * kPacketWaves), 0, s, a);
         return hipGetLastError();
     }
@@ -2822,7 +2856,10 @@ hipError_t launch_surface_env(const LaunchGeom &g, unsigned long long *bad, hipS
 
 // ---- CGLS ----
 
-size_t cgls_ray_blocks(const LaunchGeom &g) { return (size_t)ray_args(g).n_blocks; }
+// partials of the CGLS forward (RM_PROJECT_SQ, RM_CGLS_R0): one per block of the launch
+size_t cgls_ray_blocks(const LaunchGeom &g) {
+    return packet_geom(g) ? (size_t)packet_blocks(g) : (size_t)ray_args(g).n_blocks;
+}
 
 size_t cgls_brick_blocks(const LaunchGeom &g) {
     int bx, by, bz;
@@ -2853,7 +2890,7 @@ hipError_t launch_cgls_init(const LaunchGeom &g, const float *y, const float *x,
     ra.out = r;
     ra.partial = partial;
     if ((e = launch_ray<RM_CGLS_R0>(g, ra, s)) != hipSuccess) return e;
-    if ((e = cgls_finalize(partial, (size_t)ra.n_blocks, state, CO_RR, s)) != hipSuccess) return e;
+    if ((e = cgls_finalize(partial, cgls_ray_blocks(g), state, CO_RR, s)) != hipSuccess) return e;
     // s = A^T r, p = s, gamma = ||s||^2
     BrickArgs b{};
     b.sino = r;
@@ -2875,7 +2912,7 @@ hipError_t launch_cgls_step(const LaunchGeom &g, float *x, float *r, float *sv, 
     ra.out = q;
     ra.partial = partial;
     if ((e = launch_ray<RM_PROJECT_SQ>(g, ra, s)) != hipSuccess) return e;
-    if ((e = cgls_finalize(partial, (size_t)ra.n_blocks, state, CO_ALPHA, s)) != hipSuccess) return e;
+    if ((e = cgls_finalize(partial, cgls_ray_blocks(g), state, CO_ALPHA, s)) != hipSuccess) return e;
     // r -= alpha q, rr = ||r||^2
     const size_t m = (size_t)g.n_views * g.U * g.V;
     const bool vr = aligned16(r) && aligned16(q);

@@ -287,6 +287,52 @@ def test_step_local_parity_tiny(beam):
     _step_local(wl, y, 3, x0=x0)
 
 
+def _untraversed_plane_distance(wl):
+    """Smallest distance (in cells) from a ray to a lattice plane of an axis the
+    ray never crosses, over every ray with such an axis (rays exactly in such a
+    plane are ties, where rounding decides between two valid cells)."""
+    D, H, Wd = wl.vol_shape
+    dz, dy, dx = wl.voxel_spacing
+    n, sp = np.array([Wd, H, D], float), np.array([dx, dy, dz])
+    lo = -0.5 * n * sp
+    U, V = wl.det_shape
+    su, sv = wl.det_spacing
+    fr = np.asarray(wl.frames, np.float64)
+    ou = (np.arange(U) - 0.5 * (U - 1)) * su
+    ov = (np.arange(V) - 0.5 * (V - 1)) * sv
+    best = np.inf
+    for ray, c, eu, ev in zip(fr[:, 0:3], fr[:, 3:6], fr[:, 6:9], fr[:, 9:12]):
+        for k in np.nonzero(ray == 0.0)[0]:
+            p = c[k] + ou[:, None] * eu[k] + ov[None, :] * ev[k]
+            q = (p - lo[k]) / sp[k]
+            best = min(best, float(np.abs(q - np.rint(q)).min()))
+    return best
+
+
+def test_step_local_parity_packets():
+    # Dual-axis parallel views: every ray lies in planes of x or y and a detector
+    # axis runs along that axis alone, so the CGLS forward (A p with ||q||^2, and
+    # the start r = y - A x) runs in packets of rays that share their walk, and so
+    # does the brick adjoint (anisotropic voxels keep it off the line adjoint).  A
+    # 46 x 38 detector leaves ragged packet tiles; the tilts avoid 0 and the
+    # spacings keep every ray clear of the planes it runs along.
+    fr = W.dual_axis_parallel3d(6, -61.0, 130.0 / 6)
+    wl = W.Workload("packets parallel3d", W.BEAM_PARALLEL3D, (20, 24, 28), (1.0, 0.93, 1.07), (46, 38),
+                    (1.0, 1.0), fr, 0)
+    for ray, eu, ev in zip(fr[:, 0:3], fr[:, 6:9], fr[:, 9:12]):
+        d = int(np.argmin(np.abs(ray)))
+        assert ray[d] == 0.0
+        assert any(np.count_nonzero(e) == 1 and e[d] != 0.0 for e in (eu, ev))
+    assert _untraversed_plane_distance(wl) > 1e-3
+    assert rdp.ct_geom_adjoint_kind(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing,
+                                    wl.frames) == rdp.ADJOINT_BRICK
+    rng = np.random.default_rng(71)
+    y = rng.uniform(0, 1, wl.sino_shape).astype(np.float32)
+    _step_local(wl, y, 4)
+    x0 = rng.uniform(0, 1, wl.vol_shape).astype(np.float32)
+    _step_local(wl, y, 2, x0=x0)
+
+
 @pytest.mark.parametrize("config", [2, 3])
 def test_step_local_parity_c2_c3(config):
     wl = W.make_workload(config)

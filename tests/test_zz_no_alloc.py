@@ -60,9 +60,10 @@ def test_noalloc_step_matches_the_workspace_step_on_two_geometries():
 
 
 def test_noalloc_step_rejects_geometries_beyond_the_scratch():
-    # a 2048 x 2048 detector with 257 views: 128 x 128 x 257 > 2^22 forward blocks
-    fr = W.dual_axis_parallel3d(129, -60.0, 120.0 / 129)[:257]
-    g = rdp.Geometry(W.BEAM_PARALLEL3D, (8, 8, 8), (1.0, 1.0, 1.0), (2048, 2048), (0.01, 0.01), fr)
+    # cone views (one ray per lane, no packets) on a 2048 x 2048 detector with 257
+    # views: 128 x 128 x 257 > 2^22 forward blocks
+    fr = W.helix_cone(257, 40.0, 80.0)
+    g = rdp.Geometry(W.BEAM_CONE, (8, 8, 8), (1.0, 1.0, 1.0), (2048, 2048), (0.01, 0.01), fr)
     assert rdp.ct_cgls_workspace_size(g) // 8 - 32 > 2 ** 22
     # the check comes before any launch: far-apart stand-in addresses never read
     base = 1 << 46
