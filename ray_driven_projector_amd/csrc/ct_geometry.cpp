@@ -290,6 +290,14 @@ void build_view_table(const ct_geom_desc_t *desc, const GeomHost &g, double *tab
     choose_layouts(g, table);
 }
 
+// A pixel's coordinate on an axis its ray never crosses, settled on a lattice
+// plane when within 2^-30 cell of it: a ray in a plane belongs to the cell above
+// (the kernels decide these cells the same way).
+static double settle_on_plane(double o) {
+    const double r = std::nearbyint(o);
+    return std::fabs(o - r) < 0x1p-30 ? r : o;
+}
+
 int build_line_table(const GeomHost &g, const double *table, LineView *out) {
     if (g.is2d || g.beam != CT_PARALLEL3D) return -1;
     // one view's pixels are read through a buffer of 32-bit byte offsets, where a
@@ -312,7 +320,7 @@ int build_line_table(const GeomHost &g, const double *table, LineView *out) {
         if (d < 0 || std::fabs(OP[d]) != 1.0 || OQ[d] != 0.0) return -1;
         L.d = d;
         L.g = OP[d] > 0.0 ? 1 : -1;
-        const double kc = std::floor(O[d]);
+        const double kc = std::floor(settle_on_plane(O[d]));
         if (std::fabs(kc) > 1e9) return -1;
         L.kc = (int)kc;
         const int a = d == 0 ? 1 : 0, b = d == 2 ? 1 : 2;

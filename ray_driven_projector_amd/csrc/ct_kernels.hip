@@ -141,16 +141,28 @@ __device__ __forceinline__ void axis_cells(double o, double d, double tin, doubl
     dist = d > 0.0 ? (double)(ce + 1) - e : (d < 0.0 ? e - (double)ce : 0.0);
 }
 
+// The coordinate (in cells) of a ray on an axis it never crosses.  A ray lying
+// in a lattice plane belongs to the cell above it; the frames' arithmetic puts
+// such a ray a few ulps either side of the plane, so a coordinate within 2^-30
+// cell of a plane is taken to lie on it.  Every path (forward, packets, both
+// adjoints, counts) decides these cells from this value, so A and A^T agree on
+// such rays.
+__device__ __forceinline__ double on_plane(double o) {
+    const double r = rint(o);
+    return fabs(o - r) < 0x1p-30 ? r : o;
+}
+
 // Drop direction components below 2^-40 of the largest (they move the ray by
 // less than 1e-12 of its length along that axis: the ray is then parallel to
-// those planes), and clip to the volume box.  Returns false on a miss.
-__device__ __forceinline__ bool clip_ray(double ox, double oy, double oz, double &dx, double &dy,
+// those planes), settle the origin on those axes (on_plane), and clip to the
+// volume box.  Returns false on a miss.
+__device__ __forceinline__ bool clip_ray(double &ox, double &oy, double &oz, double &dx, double &dy,
                                          double &dz, double tmin, double tmax, int nx, int ny,
                                          int nz, double &tin, double &tout) {
     const double dm = fmax(fabs(dx), fmax(fabs(dy), fabs(dz))) * 0x1p-40;
-    if (fabs(dx) < dm) dx = 0.0;
-    if (fabs(dy) < dm) dy = 0.0;
-    if (fabs(dz) < dm) dz = 0.0;
+    if (fabs(dx) < dm) { dx = 0.0; ox = on_plane(ox); }
+    if (fabs(dy) < dm) { dy = 0.0; oy = on_plane(oy); }
+    if (fabs(dz) < dm) { dz = 0.0; oz = on_plane(oz); }
     tin = tmin;
     tout = tmax;
     bool hit = true;
@@ -249,6 +261,13 @@ __device__ __forceinline__ void surface_point(const double *vw, const Surface &s
     pz = vw[VT_C + 2] + ou * vw[VT_EU + 2] + ov * vw[VT_EV + 2] + on * vw[VT_EN + 2];
 }
 
+// Coordinate k of the origin of flat-detector pixel (u, v), in voxel
+// coordinates: one fixed sequence of two fused multiply-adds, so every kernel
+// that needs it gets the same bits.
+__device__ __forceinline__ double pixel_origin(const double *vw, int k, int u, int v) {
+    return fma((double)v, vw[VT_OV + k], fma((double)u, vw[VT_OU + k], vw[VT_O00 + k]));
+}
+
 // Ray of pixel (u, v): origin and direction in voxel coordinates (flat detector:
 // the affine table; surface: the source or the pixel's surface point).
 __device__ __forceinline__ void pixel_ray(const double *vw, const Surface &sf, int view, int u, int v,
@@ -256,9 +275,9 @@ __device__ __forceinline__ void pixel_ray(const double *vw, const Surface &sf, i
                                           double &dx, double &dy, double &dz) {
     if (!sf.off) {
         const double fu = (double)u, fv = (double)v;
-        ox = vw[VT_O00 + 0] + fu * vw[VT_OU + 0] + fv * vw[VT_OV + 0];
-        oy = vw[VT_O00 + 1] + fu * vw[VT_OU + 1] + fv * vw[VT_OV + 1];
-        oz = vw[VT_O00 + 2] + fu * vw[VT_OU + 2] + fv * vw[VT_OV + 2];
+        ox = pixel_origin(vw, 0, u, v);
+        oy = pixel_origin(vw, 1, u, v);
+        oz = pixel_origin(vw, 2, u, v);
         dx = vw[VT_D00 + 0] + fu * vw[VT_DU + 0] + fv * vw[VT_DV + 0];
         dy = vw[VT_D00 + 1] + fu * vw[VT_DU + 1] + fv * vw[VT_DV + 1];
         dz = vw[VT_D00 + 2] + fu * vw[VT_DU + 2] + fv * vw[VT_DV + 2];
@@ -867,9 +886,9 @@ __global__ __launch_bounds__(64 * kPacketWaves) void ray_packet_kernel(RayArgs a
     oz -= a.offz;
     // the clip of clip_ray, without the untraversed axis (tested per ray)
     const double dm = fmax(fabs(dx), fmax(fabs(dy), fabs(dz))) * 0x1p-40;
-    if (fabs(dx) < dm) dx = 0.0;
-    if (fabs(dy) < dm) dy = 0.0;
-    if (fabs(dz) < dm) dz = 0.0;
+    if (fabs(dx) < dm) { dx = 0.0; ox = on_plane(ox); }
+    if (fabs(dy) < dm) { dy = 0.0; oy = on_plane(oy); }
+    if (fabs(dz) < dm) { dz = 0.0; oz = on_plane(oz); }
     // d: the axis the packet's pixel step runs along (the rays do not cross it)
     const int ps = pu ? VT_OU : VT_OV;
     const int d = vw[ps + 0] != 0.0 ? 0 : (vw[ps + 1] != 0.0 ? 1 : 2);
@@ -899,7 +918,7 @@ __global__ __launch_bounds__(64 * kPacketWaves) void ray_packet_kernel(RayArgs a
             ry -= a.offy;
             rz -= a.offz;
         }
-        const double od = d == 0 ? rx : (d == 1 ? ry : rz);
+        const double od = on_plane(d == 0 ? rx : (d == 1 ? ry : rz));
         in[j] = j < kk && od >= 0.0 && od < (double)nd;
         cd[j] = min(max((int)floor(od), 0), nd - 1);
     }
@@ -1542,6 +1561,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     const float hx = 0.5f * fex, hy = 0.5f * fey, hz = 0.5f * fez;
     const float spx = (float)a.spx, spy = (float)a.spy, spz = (float)a.spz;
     const int u0 = f.u0, v0 = f.v0;
+    const int gx0 = x0 + a.offx, gy0 = y0 + a.offy, gz0 = z0 + a.offz;   // the brick's first cell on the lattice
     const int nfu = f.u1 - f.u0 + 1, nfv = f.v1 - f.v0 + 1, nrays = nfu * nfv;
     const bool ufast = !TWO_D && vt(vw, VT_PATCH) == 0.0;
     const int nf = ufast ? nfu : nfv;
@@ -1675,6 +1695,7 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
     constexpr bool FS = decltype(fs_tag)::value;   // mirrored fan/cone footprint
     for (int r = lane; r < nrays; r += 64) {
         const float cf = (float)lf - af, cs = (float)srow(lk) - as_;
+        const int pu = ufast ? u0 + lf : u0 + srow(lk), pv = ufast ? v0 + srow(lk) : v0 + lf;   // its pixel
         lf += step_fast;
         lk += step_slow;
         if (lf >= nf) { lf -= nf; lk += 1; }
@@ -1754,15 +1775,33 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         // not move along holds it for every t iff -h <= m < h
         float cx = -hx - mx, cy = -hy - my, cz = -hz - mz, cix = dp.ix, ciy = dp.iy, ciz = dp.iz;
         if (!FS && dp.slow) {
-            const auto zero_axis = [](float a, float m, float h, float &c, float &ci) {
-                if (a == 0.f) {
-                    c = (-h <= m && m < h) ? -h : 1.f;   // lo -> -inf / +inf
+            // On an axis the ray does not move along, its cell comes from its
+            // float64 origin as the forward forms it (pixel_origin / pixel_ray,
+            // on_plane), so both sides agree on rays that lie in a lattice plane;
+            // the ray's float32 coordinate there is moved to that cell's centre.
+            const auto zero_axis = [&](int k, float ad, int g0, int e, float h, float &m, float &c,
+                                       float &ci) __attribute__((always_inline)) {
+                if (ad == 0.f) {
+                    double o;
+                    if constexpr (SURF) {
+                        double p[3], q[3];
+                        pixel_ray(vw, a.surf, view, pu, pv, a.U, a.V, p[0], p[1], p[2], q[0], q[1], q[2]);
+                        o = p[k];
+                    } else if constexpr (PERSP) {
+                        o = vt(vw, VT_O00 + k);   // the source (pixel_origin of every pixel)
+                    } else {
+                        o = pixel_origin(vw, k, pu, pv);
+                    }
+                    const double l = on_plane(o) - (double)g0;
+                    const bool in = l >= 0.0 && l < (double)e;
+                    m = in ? (float)floor(l) + 0.5f - h : 0.f;
+                    c = in ? -h : 1.f;   // lo -> -inf / +inf
                     ci = 1e35f;
                 }
             };
-            zero_axis(dp.axx, mx, hx, cx, cix);
-            zero_axis(dp.ayy, my, hy, cy, ciy);
-            if (!TWO_D) zero_axis(dp.azz, mz, hz, cz, ciz);
+            zero_axis(0, dp.axx, gx0, ex, hx, mx, cx, cix);
+            zero_axis(1, dp.ayy, gy0, ey, hy, my, cy, ciy);
+            if (!TWO_D) zero_axis(2, dp.azz, gz0, ez, hz, mz, cz, ciz);
         }
         const float lox = cx * cix, hix = fmaf(fex, cix, lox);
         const float loy = cy * ciy, hiy = fmaf(fey, ciy, loy);
@@ -1834,11 +1873,11 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
         const auto A = [d](auto x, auto y, auto z) { return d == 0 ? y : x; };
         const auto B = [d](auto x, auto y, auto z) { return d == 2 ? y : z; };
         const auto Dd = [d](auto x, auto y, auto z) { return d == 0 ? x : (d == 1 ? y : z); };
-        const float ha = A(hx, hy, hz), hb = B(hx, hy, hz), hd = Dd(hx, hy, hz);
+        const float ha = A(hx, hy, hz), hb = B(hx, hy, hz);
         const float ea = A(fex, fey, fez), eb = B(fex, fey, fez), ed = Dd(fex, fey, fez);
-        const float A0a = A(mA0x, mA0y, mA0z), A0b = B(mA0x, mA0y, mA0z), A0d = Dd(mA0x, mA0y, mA0z);
-        const float Asa = A(mAsx, mAsy, mAsz), Asb = B(mAsx, mAsy, mAsz), Asd = Dd(mAsx, mAsy, mAsz);
-        const float Afd = Dd(mAfx, mAfy, mAfz);
+        const int ied = Dd(ex, ey, ez), gd0 = Dd(gx0, gy0, gz0);
+        const float A0a = A(mA0x, mA0y, mA0z), A0b = B(mA0x, mA0y, mA0z);
+        const float Asa = A(mAsx, mAsy, mAsz), Asb = B(mAsx, mAsy, mAsz);
         const float ia = A(dp0.ix, dp0.iy, dp0.iz), ib = B(dp0.ix, dp0.iy, dp0.iz);
         const float aa = A(dp0.axx, dp0.ayy, dp0.azz), ab = B(dp0.axx, dp0.ayy, dp0.azz);
         const float qfa = A(dp0.qfx, dp0.qfy, dp0.qfz), qfb = B(dp0.qfx, dp0.qfy, dp0.qfz);
@@ -1888,9 +1927,13 @@ __device__ __forceinline__ void brick_rays(const BrickArgs &a, const double *vw,
             bool mant_any = false;
 #pragma unroll
             for (int j = 0; j < K; ++j) {
-                const float md = fmaf(cs, Asd, fmaf(cf0 + (float)j, Afd, A0d));
-                const bool in = -hd <= md && md < hd;
-                const float fcd = __builtin_amdgcn_fmed3f(floorf(md + hd), 0.f, ed - 1.f);
+                // the cell on d from the ray's float64 origin as the forward forms it
+                // (pixel_origin, on_plane), so both sides agree on rays in a lattice plane
+                const int pf = lf0 + j;
+                const double ld = on_plane(pixel_origin(vw, d, ufast ? u0 + pf : u0 + row, ufast ? v0 + row : v0 + pf)) -
+                                  (double)gd0;
+                const bool in = ld >= 0.0 && ld < (double)ied;
+                const float fcd = in ? (float)floor(ld) : 0.f;
                 off[j] = (uint32_t)(nd ? ed - 1.f - fcd : fcd) * Sd;
                 Yf[j] = in ? yv[j] * yscale : 0.f;   // |Yf| < 2^23
                 mant_any = mant_any || (Yf[j] != 0.f && (a.yshift != 0 || fabsf(Yf[j]) < 0x1p17f));
@@ -2351,21 +2394,25 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
             const int edge = L.aligned ? 0 : 1;
             const int rA = max((int)floorf(fminf(t1, t2)) + edge, rlo);
             const int rB = min((int)ceilf(fmaxf(t1, t2)) - edge, rlo + nrows - 1);
-            float dl, step;
-            if (L.aligned) {
-                // the rays' constant coordinate relative to this cell (a ray on a cell
-                // boundary belongs to the higher cell)
-                dl = (float)(fma(qr + rA, L.Xq, L.X0) - (L.aligned == 1 ? ga + la : gb + lb));
-                step = (float)L.Xq;
-            } else {
+            float dl = 0.f, step = 0.f;
+            const double cell = L.aligned == 1 ? ga + la : gb + lb;
+            if (!L.aligned) {
                 dl = (float)fma((double)rA, L.dq, Cd);
                 step = (float)L.dq;
             }
             const float *row = st + (rA - rlo) * kLinePitch + s0;
             for (int r = rA; r <= rB; ++r, row += kLinePitch) {
-                const float Lc = L.aligned ? ((dl >= 0.f && dl < 1.f) ? L.Lmax : 0.f)
-                                           : fminf(fmaxf((L.H - fabsf(dl)) * L.R, 0.f), L.Lmax);
-                dl += step;
+                float Lc;
+                if (L.aligned) {
+                    // the rays' constant coordinate relative to this cell, per row in
+                    // float64 and settled on the lattice planes (on_plane): a ray in a
+                    // cell's lower plane belongs to that cell
+                    const double x = on_plane(fma(qr + r, L.Xq, L.X0)) - cell;
+                    Lc = (x >= 0.0 && x < 1.0) ? L.Lmax : 0.f;
+                } else {
+                    Lc = fminf(fmaxf((L.H - fabsf(dl)) * L.R, 0.f), L.Lmax);
+                    dl += step;
+                }
                 // (a zero chord, an aligned ray on the cell's far edge, adds nothing)
                 const float4 *row4 = (const float4 *)row;
 #pragma unroll

@@ -17,6 +17,7 @@ import pytest
 
 import oracle
 import ray_driven_projector_amd as rdp
+from geom_checks import untraversed_plane_distance
 from ray_driven_projector_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -287,28 +288,6 @@ def test_step_local_parity_tiny(beam):
     _step_local(wl, y, 3, x0=x0)
 
 
-def _untraversed_plane_distance(wl):
-    """Smallest distance (in cells) from a ray to a lattice plane of an axis the
-    ray never crosses, over every ray with such an axis (rays exactly in such a
-    plane are ties, where rounding decides between two valid cells)."""
-    D, H, Wd = wl.vol_shape
-    dz, dy, dx = wl.voxel_spacing
-    n, sp = np.array([Wd, H, D], float), np.array([dx, dy, dz])
-    lo = -0.5 * n * sp
-    U, V = wl.det_shape
-    su, sv = wl.det_spacing
-    fr = np.asarray(wl.frames, np.float64)
-    ou = (np.arange(U) - 0.5 * (U - 1)) * su
-    ov = (np.arange(V) - 0.5 * (V - 1)) * sv
-    best = np.inf
-    for ray, c, eu, ev in zip(fr[:, 0:3], fr[:, 3:6], fr[:, 6:9], fr[:, 9:12]):
-        for k in np.nonzero(ray == 0.0)[0]:
-            p = c[k] + ou[:, None] * eu[k] + ov[None, :] * ev[k]
-            q = (p - lo[k]) / sp[k]
-            best = min(best, float(np.abs(q - np.rint(q)).min()))
-    return best
-
-
 def test_step_local_parity_packets():
     # Dual-axis parallel views: every ray lies in planes of x or y and a detector
     # axis runs along that axis alone, so the CGLS forward (A p with ||q||^2, and
@@ -323,7 +302,7 @@ def test_step_local_parity_packets():
         d = int(np.argmin(np.abs(ray)))
         assert ray[d] == 0.0
         assert any(np.count_nonzero(e) == 1 and e[d] != 0.0 for e in (eu, ev))
-    assert _untraversed_plane_distance(wl) > 1e-3
+    assert untraversed_plane_distance(wl) > 1e-3
     assert rdp.ct_geom_adjoint_kind(wl.beam, wl.vol_shape, wl.voxel_spacing, wl.det_shape, wl.det_spacing,
                                     wl.frames) == rdp.ADJOINT_BRICK
     rng = np.random.default_rng(71)
