@@ -33,7 +33,13 @@
  *     (the Projector class reference describes parallel3d rays as unbounded
  *     lines through the detector pixels).
  *   - Voxels are half-open boxes [lo + k s, lo + (k+1) s): a ray lying exactly
- *     on a lattice plane belongs to the higher-index cell.
+ *     on a lattice plane belongs to the higher-index cell.  On an axis a ray
+ *     never crosses (its direction component is 0, or below 2^-40 of the
+ *     largest), its coordinate comes from one float64 evaluation of the pixel
+ *     origin and counts as on a plane when within 2^-30 cell of it, in the
+ *     forward, both adjoints and the intersection count alike, so A and A^T
+ *     agree on such rays (pixel centres on planes arise, e.g., from an odd
+ *     detector over an even volume at equal pitch).
  *
  * Ownership and threading:
  *   - Every float* argument of the compute calls is a DEVICE pointer owned by
