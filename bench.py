@@ -6,7 +6,8 @@ Default run (one JSON line):
 - The timed step is one SIRT iteration on the 512^3 parallel3d dual-axis
   workload (280 views, 512 x 512 detector): the forward projection with the
   residual epilogue (ct_sirt_residual) and the brick-binned adjoint with the
-  update epilogue (ct_sirt_update), every hot-path kernel of the iteration.
+  update epilogue (ct_sirt_update; the line adjoint on this tilt series),
+  every hot-path kernel of the iteration.
   The SIRT weights are computed once before timing; inputs live in HBM before
   the timed region starts.  value = ray-voxel intersections per second over
   the step (each intersection is visited once by A and once by A^T: 2 nnz per
@@ -20,10 +21,10 @@ Default run (one JSON line):
   roofline fraction.  nnz is the oracle's exact count
   (tests/golden/nnz_configs.json, checked against the frames and the GPU's
   own count).
-- "roofline": the dominant kernel of the step.  Both Siddon kernels are
-  bound by VALU instruction issue (the rocprofv3 counters put their VALU busy
-  at about 1.0 while they fetch under 1 TB/s from HBM), so the roofline is the
-  ALU one: algorithmic lane operations per launch over the launch's duration
+- "roofline": the dominant kernel of the step.  The projector kernels are
+  bound by instruction issue and latency, not by HBM (the rocprofv3 counters
+  put the VALU busy at 0.6-1.0 while they fetch 1-2.5 TB/s from HBM), so the
+  roofline is the ALU one: algorithmic lane operations per launch over the launch's duration
   against 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s (one
   wave64 VALU instruction per SIMD every 4 cycles; packed math does not apply
   to this integer and compare work).  The algorithmic work per intersection
@@ -45,6 +46,8 @@ Default run (one JSON line):
 - "traffic" and the measured VALU instructions come from rocprofv3 counter
   runs committed in profiles/counters.json; they are reported only while the
   library's device code object is the one they were taken on (its SHA-256).
+- "solvers": one CGLS iteration on C4 and on C5 (from y = A phantom) and the
+  FDK (Ram-Lak, pad 2) of C5's acquisition, in ms, timed the same way.
 - "cpu_baseline": the float64 oracle on a bounded sample of views of the same
   workload (A, then A^T of a dense sinogram), same unit.
 
@@ -409,6 +412,45 @@ def config_pair(cfg, rdp, W, torch, stream, timer):
     return out
 
 
+def solver_lines(rdp, W, torch, np, stream, timer):
+    """The solvers around the projector pair, timed beside the SIRT step: one
+    CGLS iteration on C4 and on C5 (from y = A phantom, median of the timed
+    steps after two warm-up steps), and the FDK (Ram-Lak, pad 2) of C5's
+    acquisition (filter + backprojection)."""
+    out = {}
+    for cfg, reps in ((4, 7), (5, 3)):
+        wl = W.make_workload(cfg)
+        g = rdp.Geometry.from_workload(wl)
+        y = torch.empty(g.sino_shape, device="cuda")
+        rdp.ct_project(g, torch.from_numpy(W.make_phantom(wl)).cuda(), y, stream)
+        x = torch.zeros(g.vol_shape, device="cuda")
+        r = torch.empty(g.sino_shape, device="cuda")
+        q = torch.empty(g.sino_shape, device="cuda")
+        s_ = torch.empty(g.vol_shape, device="cuda")
+        p_ = torch.empty(g.vol_shape, device="cuda")
+        work = torch.empty(rdp.ct_cgls_workspace_size(g), dtype=torch.uint8, device="cuda")
+        rdp.ct_cgls_init(g, y, x, r, s_, p_, work, stream)
+        ms = timer.median_ms(lambda: rdp.ct_cgls_step(g, x, r, s_, p_, q, work, stream), warmup=2, reps=reps)
+        out[f"c{cfg}_cgls_ms_per_iteration"] = round(ms, 3)
+        del x, r, q, s_, p_, work
+        if cfg == 5:
+            angles = W.angles(wl.n_views, 2 * np.pi)
+            fplan = rdp.FBP.from_workload(wl, angles, window="ram-lak", pad_factor=2)
+            filt = torch.empty(g.sino_shape, device="cuda")
+            vol = torch.empty(g.vol_shape, device="cuda")
+
+            def fdk():
+                rdp.ct_fbp_filter(fplan, y, filt, stream)
+                rdp.ct_fbp_backproject(fplan, filt, vol, stream)
+            ms = timer.median_ms(fdk, warmup=1, reps=3)
+            out["c5_fdk_ms"] = round(ms, 3)
+            out["c5_fdk_G_voxel_view_updates_per_s"] = round(wl.n_voxels * wl.n_views / (ms * 1e-3) / 1e9, 1)
+            del fplan, filt, vol
+        del g, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def default_run(args, rdp, W, torch, np):
     stream = torch.cuda.current_stream()
     timer = Timer(torch, stream)
@@ -483,6 +525,8 @@ def default_run(args, rdp, W, torch, np):
         say(f"config C{cfg}: A and A^T")
         configs[f"c{cfg}"] = config_pair(cfg, rdp, W, torch, stream, timer)
     res["configs"] = configs
+    say("solvers: CGLS on C4 and C5, FDK on C5")
+    res["solvers"] = solver_lines(rdp, W, torch, np, stream, timer)
     res["device_code"] = code_object_hash()
     if not args.no_cpu_baseline:
         say("cpu baseline (oracle) ...")
