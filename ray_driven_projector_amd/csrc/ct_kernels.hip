@@ -483,13 +483,15 @@ __device__ __forceinline__ GStep gstep2(const IWalk2 &w, uint32_t &idx, uint32_t
 
 constexpr int kPacket = 4;   // rays per packet (forward and brick adjoint)
 // Forward packet blocks (measured on the 512^3 dual-axis SIRT residual):
-// 16 waves, each 8 packets along P (one 128-byte line of the volume copy's
-// contiguous axis) x 8 rows, so a block takes a tile of 32 x 128 pixels, and
-// one tile runs through every view in turn.  12.1 ms with 256-thread blocks
-// of 64 x 16 pixels; 9.1 with 1024-thread 64 x 64; 8.9 with 32 x 128; 20.3
-// with 16 x 256 (half lines); grouping 2 / 4 tiles per view: 10.7 / 12.9.
+// 8 waves, each 8 packets along P (one 128-byte line of the volume copy's
+// contiguous axis) x 8 rows, so a block takes a tile of 32 x 64 pixels, and
+// one tile runs through every view in turn.  8.57 ms; 8.81 with 1024-thread
+// blocks of 32 x 128 (one block per CU at 96 VGPRs), 10.6 with 256-thread
+// 32 x 32; earlier shapes 12.1 ms with 256-thread 64 x 16, 9.1 with 1024-thread
+// 64 x 64, 20.3 with 16 x 256 (half lines); grouping 2 / 4 tiles per view
+// 10.7 / 12.9.
 constexpr int kPacketTileGroup = 1;
-constexpr int kPacketWaves = 16;
+constexpr int kPacketWaves = 8;
 constexpr int kPacketLanesP = 8;
 constexpr int kPacketTP = kPacketLanesP * kPacket, kPacketTQ = (64 / kPacketLanesP) * kPacketWaves;   // tile
 
