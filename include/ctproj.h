@@ -210,9 +210,9 @@ ct_status_t ct_geom_adjoint_range(ct_geom_t g, const ct_geom_desc_t *desc, int s
  *     (16 when some views' planes are z planes, or a view's rows are too dense
  *     for a 32 x 32 x 16 brick to stage them), from the ray's offset to the
  *     voxel's centre (the chord of a line through a square), and sums chord *
- *     value in float32 over 16 views, then in the brick's float32 accumulator:
- *     per voxel the error is within about (2 * rays per voxel and 16 views +
- *     views / 16) * 2^-24 of sum_i |a_ij y_i|.  A ray lying on a voxel plane
+ *     value in float32 over 32 views, then in the brick's float32 accumulator:
+ *     per voxel the error is within about (2 * rays per voxel and 32 views +
+ *     views / 32) * 2^-24 of sum_i |a_ij y_i|.  A ray lying on a voxel plane
  *     belongs to the higher voxel, as in the walks. */
 enum { CT_ADJOINT_BRICK = 0, CT_ADJOINT_LINE = 1 };
 ct_status_t ct_geom_adjoint_kind(ct_geom_t g, const ct_geom_desc_t *desc, int surface, int32_t *kind);

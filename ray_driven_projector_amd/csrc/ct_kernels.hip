@@ -2227,7 +2227,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void br
 // its cell (one or two), forms each ray's chord through the cell once, from the
 // ray's offset to the cell centre (the trapezoid of a unit square), and adds
 // chord * value to the voxels of its line.  No ray is walked and nothing is
-// added atomically: sums run in float32 registers over 16 views, then into the
+// added atomically: sums run in float32 registers over 32 views, then into the
 // brick's float32 accumulator in LDS (each voxel belongs to one line per family),
 // which is written once.
 constexpr int kLinePitch = 36;   // floats per staged row: up to 32 pixel columns, padded
@@ -2428,7 +2428,7 @@ __device__ __forceinline__ void line_family(const BrickArgs &a, ConstLinePtr lv,
             }
         }
         buf ^= 1;
-        if (++batch == 16 || last) {
+        if (++batch == 32 || last) {
             // into the brick's accumulator: each voxel belongs to one segment here
             if (live) {
                 constexpr int STEP = D == 0 ? 1 : (D == 1 ? LSY : LSZ);
