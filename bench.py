@@ -235,12 +235,12 @@ def ingest_counters(specs, out_path=COUNTERS):
                     f"{(format(e['fetch_bytes'] / 1e9, '.2f') if 'fetch_bytes' in e else '')} | "
                     f"{(format(e['write_bytes'] / 1e9, '.2f') if 'write_bytes' in e else '')} |\n")
         f.write("\nEach workload `<wl>` takes four passes of one step each (`--extra` on the parallel workload adds "
-                "the SIRT, weight and atomic-adjoint kernels), from /tmp, `<repo>` the repository root:\n\n")
+                "the SIRT, weight and atomic-adjoint kernels), from /tmp, `<repo>` the repository root, `<out>` any output folder:\n\n")
         for out, pmc, cal in PMC_PASSES:
-            f.write(f"    rocprofv3 --pmc {pmc} --output-format csv -d <repo>/gpurun_out/cnt/<wl> -o {out} -- "
+            f.write(f"    rocprofv3 --pmc {pmc} --output-format csv -d <out>/<wl> -o {out} -- "
                     f"python3 <repo>/bench.py --workload <wl> --steps 1 --warmup 0 --no-cpu-baseline [--extra]{cal}\n")
         f.write("\nthen `python3 bench.py --ingest-counters " +
-                " ".join(f"{s.split('=', 1)[0]}=gpurun_out/cnt/{s.split('=', 1)[0]}" for s in specs) + "`.\n"
+                " ".join(f"{s.split('=', 1)[0]}=<out>/{s.split('=', 1)[0]}" for s in specs) + "`.\n"
                 "VALU busy = SQ_INSTS_VALU x 4 cycles / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); "
                 "HBM bytes = FETCH_SIZE / WRITE_SIZE in KiB x the calibration factor, which makes the counter read "
                 "1 GiB for a 1 GiB device-to-device copy in the same run.\n")
