@@ -631,11 +631,15 @@ __device__ __forceinline__ void fix_axis(double d, double L, double S, int ncr, 
 
 // Line integral of the ray o + t d, t in [tin, tout] (inside the box), with the
 // walk re-based every 2^clog2 cells of the major axis (2^31 walk units per chunk).
+// nparts > 1: only chunks part, part + nparts, ...; a chunk's start is then its
+// first plane's parameter, the same expression that ends the chunk before it, so
+// every chunk's pieces are those of the whole walk.
 __device__ __forceinline__ float project_ray(double ox, double oy, double oz, double dx, double dy,
                                              double dz, double tin, double tout, int nx, int ny,
                                              int nz, double spx, double spy, double spz,
                                              uint32_t ex, uint32_t ey, uint32_t ez,
-                                             __amdgpu_buffer_rsrc_t rs, int clog2) {
+                                             __amdgpu_buffer_rsrc_t rs, int clog2, int part = 0,
+                                             int nparts = 1) {
     const double px = dx * spx, py = dy * spy, pz = dz * spz;
     const double L = sqrt(px * px + py * py + pz * pz);
     const double ax = fabs(dx), ay = fabs(dy), az = fabs(dz);
@@ -661,8 +665,9 @@ __device__ __forceinline__ float project_ray(double ox, double oy, double oz, do
     const bool two_axis = dead0 < 3 && __builtin_amdgcn_ballot_w64(dead != dead0) == 0;
     float total = 0.f;
     double ta = tin;
-    for (int ch = 0; ch < nch; ++ch) {
+    for (int ch = part; ch < nch; ch += nparts) {
         const int first = cin + sgn * (ch << clog2);
+        if (nparts > 1 && ch != 0) ta = ((double)(sgn > 0 ? first : first + 1) - oM) / dM;
         const int cells = min(chunk, ncell - (ch << clog2));
         double tb = tout;
         if (ch != nch - 1) {
@@ -726,7 +731,11 @@ struct RayArgs {
 // Tiles: a 256-thread block takes 16 x 16 pixels of one view; each wave takes a
 // 16 x 4 (or 4 x 16) patch whose 16-wide side runs along the detector axis that
 // the view's volume copy stores contiguously, so the 64 rays of a wave read few
-// cache lines per step.  2D: 256 consecutive u per block.  Block order: groups
+// cache lines per step.  2D: 64 consecutive u per block; the forward modes give
+// each ray four lanes, which take every fourth chunk of its walk and sum their
+// parts in a fixed order (a 2D sinogram has too few rays to keep the SIMDs busy
+// with one lane each: the gathers' latency went unhidden), and the other modes
+// use the first wave only.  Block order: groups
 // of 2 v-bands x 2 u-tiles, and inside a group every view in turn, so
 // the blocks an XCD runs together trace the same few pixel tiles through
 // neighbouring views; their rays cross the same voxels at nearly the same time
@@ -750,9 +759,15 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
     const int band = bg * TB + r / tu;
     const int ut = ug * TU + r % tu;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    constexpr bool kFwd = MODE == RM_PROJECT || MODE == RM_RESIDUAL || MODE == RM_PROJECT_SQ ||
+                          MODE == RM_CGLS_R0;
+    constexpr bool SPLIT = TWO_D && kFwd;   // four lanes per ray
     int u, v;
-    if (TWO_D) {
-        u = ut * 256 + threadIdx.x;
+    if (SPLIT) {
+        u = ut * 64 + (threadIdx.x >> 2);
+        v = 0;
+    } else if (TWO_D) {
+        u = threadIdx.x < 64 ? ut * 64 + threadIdx.x : a.U;   // first wave only
         v = 0;
     } else {
         const double *vw0 = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
@@ -765,9 +780,10 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
         }
     }
     const bool active = (u < a.U) && (v < a.V);
+    // the lane that writes a ray's result (the whole group agrees on active and on
+    // the clip, so the exchanges below stay inside active lanes)
+    const bool writer = !SPLIT || (threadIdx.x & 3) == 0;
     uint32_t my_count = 0;
-    constexpr bool kFwd = MODE == RM_PROJECT || MODE == RM_RESIDUAL || MODE == RM_PROJECT_SQ ||
-                          MODE == RM_CGLS_R0;
     double my_sq = 0.0;
     if (active) {
         const double *vw = a.views + (size_t)view * CT_VIEW_TABLE_STRIDE;
@@ -791,18 +807,25 @@ __global__ __launch_bounds__(256) void ray_kernel(RayArgs a) {
                 const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, a.vol_bytes);
                 acc = project_ray(ox, oy, oz, dx, dy, dz, tin, tout, a.W, a.H, a.D, a.spx, a.spy,
                                   a.spz, ex, ey, ez, rs,
-                                  vw[VT_PERSP] != 0.0 ? kChunkLog2Persp : kChunkLog2Parallel);
+                                  vw[VT_PERSP] != 0.0 ? kChunkLog2Persp : kChunkLog2Parallel,
+                                  SPLIT ? (int)(threadIdx.x & 3) : 0, SPLIT ? 4 : 1);
             }
-            if (MODE == RM_PROJECT || MODE == RM_PROJECT_SQ) {
-                if (MODE == RM_PROJECT && a.accumulate) acc += a.out[ray];
-                a.out[ray] = acc;
-                if (MODE == RM_PROJECT_SQ) my_sq = (double)acc * acc;
-            } else if (MODE == RM_CGLS_R0) {
-                const float r = a.sino[ray] - acc;
-                a.out[ray] = r;
-                my_sq = (double)r * r;
-            } else {
-                a.out[ray] = a.rinv[ray] * (a.sino[ray] - acc);
+            if (SPLIT) {   // (part 0 + part 1) + (part 2 + part 3), the same on every lane
+                acc += __shfl_xor(acc, 1);
+                acc += __shfl_xor(acc, 2);
+            }
+            if (writer) {
+                if (MODE == RM_PROJECT || MODE == RM_PROJECT_SQ) {
+                    if (MODE == RM_PROJECT && a.accumulate) acc += a.out[ray];
+                    a.out[ray] = acc;
+                    if (MODE == RM_PROJECT_SQ) my_sq = (double)acc * acc;
+                } else if (MODE == RM_CGLS_R0) {
+                    const float r = a.sino[ray] - acc;
+                    a.out[ray] = r;
+                    my_sq = (double)r * r;
+                } else {
+                    a.out[ray] = a.rinv[ray] * (a.sino[ray] - acc);
+                }
             }
         } else {
             DWalk w;
@@ -2648,7 +2671,7 @@ static RayArgs ray_args(const LaunchGeom &g) {
     a.W = g.W; a.H = g.H; a.D = g.D; a.U = g.U; a.V = g.V; a.n_views = g.n_views;
     a.spx = g.spx; a.spy = g.spy; a.spz = g.spz;
     if (g.two_d) {
-        a.n_utiles = (g.U + 255) / 256;
+        a.n_utiles = (g.U + 63) / 64;
         a.n_vtiles = 1;
     } else {
         a.n_utiles = (g.U + 15) / 16;
